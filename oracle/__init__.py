@@ -1,0 +1,202 @@
+"""fp64 CPU oracle for the 2-D TM Maxwell FDTD propagator (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``, never by the product package.
+It shares no code with the GPU path; both consume the seeded arrays of
+``tm_maxwell_fdtd_amd.inputs`` (the oracle receives the float32-rounded
+values widened back to float64, see ``inputs.as_f32``).
+
+The arithmetic lives in ``tm_oracle.c`` (plain C, fp64, OpenMP over rows);
+this module only marshals arrays.  Every function's definition and the
+page passages it follows are documented in that file.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tm_oracle.c")
+_LIB = os.path.join(_HERE, "liborac.so")
+
+_ll = ctypes.c_longlong
+_dp = ctypes.POINTER(ctypes.c_double)
+_lp = ctypes.POINTER(ctypes.c_longlong)
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [
+        ("order", ctypes.c_int),
+        ("periodic", ctypes.c_int),
+        ("n_shots", _ll), ("ny", _ll), ("nx", _ll),
+        ("pml_y0", _ll), ("pml_y1", _ll), ("pml_x0", _ll), ("pml_x1", _ll),
+        ("rdy", ctypes.c_double), ("rdx", ctypes.c_double),
+        ("n_src", _ll), ("n_rec", _ll),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/liborac.so``."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.orc_forward.restype = ctypes.c_int
+        L.orc_forward.argtypes = [ctypes.POINTER(Geom), _dp, _dp, _dp, _dp, _ll, _dp, _lp, _lp,
+                                  _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ll, _ll]
+        L.orc_adjoint.restype = ctypes.c_int
+        L.orc_adjoint.argtypes = [ctypes.POINTER(Geom), _dp, _dp, _dp, _dp, _ll, _lp, _lp, _ll,
+                                  _dp, _dp, _dp, _dp, _dp, _dp]
+        L.orc_shot_sum.restype = None
+        L.orc_shot_sum.argtypes = [_ll, _ll, _dp, _dp]
+        L.orc_coefficients.restype = ctypes.c_int
+        L.orc_coefficients.argtypes = [ctypes.c_int, _dp]
+        _lib = L
+    return _lib
+
+
+def _d(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.cast(None, _dp)
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(_dp)
+
+
+def _l(a: np.ndarray):
+    assert a.dtype == np.int64 and a.flags.c_contiguous
+    return a.ctypes.data_as(_lp)
+
+
+def _c64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def geom(wl, periodic: bool = False) -> Geom:
+    return Geom(order=wl.order, periodic=int(periodic), n_shots=wl.n_shots, ny=wl.ny, nx=wl.nx,
+                pml_y0=wl.pml_y0, pml_y1=wl.pml_y1, pml_x0=wl.pml_x0, pml_x1=wl.pml_x1,
+                rdy=1.0 / wl.dy, rdx=1.0 / wl.dx, n_src=wl.n_src, n_rec=wl.n_rec)
+
+
+def coefficients(order: int) -> np.ndarray:
+    c = np.zeros(4)
+    n = lib().orc_coefficients(order, _d(c))
+    if n < 0:
+        raise ValueError(f"order {order} not supported")
+    return c[:n]
+
+
+class State:
+    """Forward state of all shots: fields and the four CPML memories."""
+
+    def __init__(self, n_shots, ny, nx):
+        shape = (n_shots, ny, nx)
+        self.E = np.zeros(shape)
+        self.Hx = np.zeros(shape)
+        self.Hz = np.zeros(shape)
+        self.psi_ez = np.zeros(shape)
+        self.psi_ex = np.zeros(shape)
+        self.psi_hxz = np.zeros(shape)
+        self.psi_hzx = np.zeros(shape)
+
+    def copy(self):
+        out = State.__new__(State)
+        for k, v in self.__dict__.items():
+            setattr(out, k, v.copy())
+        return out
+
+
+def forward(wl, t0: int = 0, t1: Optional[int] = None, state: Optional[State] = None,
+            store: bool = False, periodic: bool = False, ca=None, cb=None, cq=None, f=None):
+    """Run forward steps t0..t1-1.  Returns (records, state, snapshots).
+
+    ``records`` is [nt][S][n_rec] (rows outside [t0, t1) are zero);
+    ``snapshots`` is None or a pair (Ey^n, curlH^n) of [nt][S][ny_i][nx_i].
+    ``ca``/``cb``/``cq``/``f`` override the workload's arrays.
+    """
+    t1 = wl.nt if t1 is None else t1
+    g = geom(wl, periodic)
+    st = State(wl.n_shots, wl.ny, wl.nx) if state is None else state
+    r = np.zeros((wl.nt, wl.n_shots, wl.n_rec))
+    snaps = None
+    if store:
+        nyi, nxi = wl.pml_y1 - wl.pml_y0, wl.pml_x1 - wl.pml_x0
+        snaps = (np.zeros((wl.nt, wl.n_shots, nyi, nxi)), np.zeros((wl.nt, wl.n_shots, nyi, nxi)))
+    ca = _c64(wl.ca if ca is None else ca)
+    cb = _c64(wl.cb if cb is None else cb)
+    cq = _c64(wl.cq if cq is None else cq)
+    f = _c64(wl.f if f is None else f)
+    cpml = _c64(wl.cpml)
+    src = np.ascontiguousarray(wl.src, dtype=np.int64)
+    rec = np.ascontiguousarray(wl.rec, dtype=np.int64)
+    rc = lib().orc_forward(ctypes.byref(g), _d(ca), _d(cb), _d(cq), _d(cpml), cpml.shape[1],
+                           _d(f), _l(src), _l(rec), _d(st.E), _d(st.Hx), _d(st.Hz),
+                           _d(st.psi_ez), _d(st.psi_ex), _d(st.psi_hxz), _d(st.psi_hzx),
+                           _d(r), _d(snaps[0] if snaps else None), _d(snaps[1] if snaps else None),
+                           t0, t1)
+    if rc != 0:
+        raise RuntimeError(f"orc_forward failed ({rc})")
+    return r, st, snaps
+
+
+def adjoint(wl, grad_r: np.ndarray, snaps=None, ca=None, cb=None, cq=None, want_grad_f=True):
+    """Exact adjoint.  Returns (grad_f [nt][S][n_src], gca [S][ny][nx], gcb [S][ny][nx])."""
+    g = geom(wl)
+    grad_r = _c64(grad_r)
+    assert grad_r.shape == (wl.nt, wl.n_shots, wl.n_rec)
+    grad_f = np.zeros((wl.nt, wl.n_shots, wl.n_src)) if want_grad_f else None
+    gca = np.zeros((wl.n_shots, wl.ny, wl.nx))
+    gcb = np.zeros((wl.n_shots, wl.ny, wl.nx))
+    ca = _c64(wl.ca if ca is None else ca)
+    cb = _c64(wl.cb if cb is None else cb)
+    cq = _c64(wl.cq if cq is None else cq)
+    cpml = _c64(wl.cpml)
+    src = np.ascontiguousarray(wl.src, dtype=np.int64)
+    rec = np.ascontiguousarray(wl.rec, dtype=np.int64)
+    se = _c64(snaps[0]) if snaps is not None else None
+    sc = _c64(snaps[1]) if snaps is not None else None
+    rc = lib().orc_adjoint(ctypes.byref(g), _d(ca), _d(cb), _d(cq), _d(cpml), cpml.shape[1],
+                           _l(src), _l(rec), wl.nt, _d(grad_r), _d(grad_f), _d(se), _d(sc),
+                           _d(gca), _d(gcb))
+    if rc != 0:
+        raise RuntimeError(f"orc_adjoint failed ({rc})")
+    return grad_f, gca, gcb
+
+
+def shot_sum(grad_shot: np.ndarray) -> np.ndarray:
+    gs = _c64(grad_shot)
+    out = np.zeros(gs.shape[1:])
+    lib().orc_shot_sum(gs.shape[0], int(np.prod(gs.shape[1:])), _d(gs), _d(out))
+    return out
+
+
+def misfit_and_gradient(wl, observed=None):
+    """J = 1/2 ||r - d||^2 (d = 0 when ``observed`` is None) and its gradients.
+
+    Returns dict with records, J, grad_f, per-shot gca/gcb and the shot sums.
+    """
+    r, _, snaps = forward(wl, store=True)
+    resid = r if observed is None else r - observed
+    J = 0.5 * float(np.sum(resid * resid))
+    grad_f, gca, gcb = adjoint(wl, resid, snaps)
+    return dict(records=r, J=J, grad_f=grad_f, gca_shot=gca, gcb_shot=gcb,
+                gca=shot_sum(gca), gcb=shot_sum(gcb), residual=resid)
