@@ -1,0 +1,168 @@
+/*
+ * tm_fdtd.h -- C ABI of the MI355X (gfx950) 2-D TM Maxwell FDTD propagator
+ * with its exact discrete adjoint and the model gradients dJ/dCa, dJ/dCb.
+ *
+ * Source of the method: tide-GPR 0.0.9, tide/csrc/maxwell.cu (the header
+ * comment's discrete equations, the kernels forward_kernel_h/_e, the
+ * storing variants, add_sources_ey, record_receivers_ey,
+ * add_adjoint_sources_ey, record_adjoint_at_sources, combine_grad and the
+ * host launchers forward, forward_with_storage and backward).
+ *
+ * Grid and index conventions (all per shot, row-major, x fastest):
+ *   ny x nx padded grid, P = order / 2, flat cell index y * nx + x.
+ *   Ey is updated on P <= y <= ny-P, P <= x <= nx-P;
+ *   Hx on P <= y <= ny-P-1, P <= x <= nx-P (the point y + 1/2 stored at y);
+ *   Hz on P <= y <= ny-P,   P <= x <= nx-P-1 (the point x + 1/2 stored at x).
+ *   The interior window [pml_y0, pml_y1) x [pml_x0, pml_x1) is the region
+ *   without CPML; E derivatives are CPML-filtered outside it, H derivatives
+ *   outside [pml_y0, pml_y1 - 1) (resp. x), as in the page's kernels.
+ *   Gradients are accumulated on the interior window only.
+ *
+ * One step n (forward_kernel_h, forward_kernel_e, add_sources_ey,
+ * record_receivers_ey, in that order):
+ *   Hx -= Cq * filt(Dz^h Ey);  Hz += Cq * filt(Dx^h Ey)
+ *   Ey  = Ca * Ey + Cb * (filt(Dx Hz) - filt(Dz Hx))
+ *   Ey[src] += f[n];  r[n] = Ey[rec]
+ * with filt(d) = d / kappa + m, m <- b m + a d on the CPML bands.
+ *
+ * Memory ownership: every array argument of tm_forward, tm_adjoint,
+ * tm_grad and tm_courant is a device pointer owned by the caller.  The
+ * workspace is caller-allocated device memory of at least
+ * tm_workspace_bytes() bytes; it holds the wavefields, the band-only CPML
+ * memories, the snapshot store (or checkpoints and a replay segment) and
+ * small tables.  A plan owns host memory only.  Every call is asynchronous
+ * on ``stream`` (a hipStream_t; NULL = the null stream) unless stated.
+ *
+ * Errors: argument errors are detected on the host before any launch and
+ * returned as a tm_status; nothing is printed and nothing aborts.
+ */
+#ifndef TM_FDTD_H
+#define TM_FDTD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tm_status {
+    TM_OK = 0,
+    TM_EINVAL = 1,      /* invalid descriptor, pointer, size or index          */
+    TM_EUNSTABLE = 2,   /* Courant number of the model above 1                 */
+    TM_ENOMEM = 3,      /* workspace too small, or plan over the HBM budget    */
+    TM_EHIP = 4,        /* a HIP runtime call or kernel launch failed          */
+    TM_ESTATE = 5,      /* call sequence: e.g. adjoint without a storing forward */
+    TM_ENONFINITE = 6   /* non-finite value detected                           */
+} tm_status;
+
+typedef enum tm_snap {
+    TM_SNAP_F32 = 0,    /* snapshots stored as float32                          */
+    TM_SNAP_BF16 = 1    /* snapshots stored as bfloat16, round-to-nearest-even  */
+} tm_snap;
+
+/* tm_forward flags */
+#define TM_FWD_STORE 1  /* keep what tm_adjoint needs: snapshots, or checkpoints */
+#define TM_FWD_CHECK 2  /* check the Courant number before stepping (synchronises) */
+
+typedef struct tm_desc {
+    int32_t order;          /* spatial order: 2, 4 or 8                         */
+    int32_t snap;           /* tm_snap                                          */
+    int64_t n_shots;        /* shots S sharing one model                        */
+    int64_t ny, nx;         /* padded grid; ny * nx < 2^31                      */
+    int64_t pml_y0, pml_y1; /* interior window rows [pml_y0, pml_y1)            */
+    int64_t pml_x0, pml_x1; /* interior window columns [pml_x0, pml_x1)         */
+    double dy, dx;          /* grid spacing in metres (kernels use 1/dy, 1/dx)  */
+    int64_t nt;             /* time steps                                       */
+    int64_t n_src, n_rec;   /* sources and receivers per shot (may be 0)        */
+    int64_t ckpt_every;     /* 0: store every step; K > 0: checkpoint the state
+                               every K steps and replay segments in tm_adjoint  */
+    uint64_t hbm_budget;    /* bytes the workspace may use; 0 = unlimited       */
+} tm_desc;
+
+typedef struct tm_plan tm_plan;
+
+/*
+ * Validate a problem and build a plan (host only, no HIP call).
+ *   cpml: host float32 [12][max(ny, nx)]: ay, by, ky, ayh, byh, kyh (first
+ *         ny entries used) then ax, bx, kx, axh, bxh, kxh (first nx used);
+ *         the integer-grid arrays filter E-update derivatives, the half-grid
+ *         ones H-update derivatives.  kappa must be nonzero on the bands.
+ *   src:  host int64 [S][n_src] flat cell indices y*nx+x (may be NULL when
+ *         n_src == 0); rec: host int64 [S][n_rec].  A negative index means
+ *         "no source/receiver"; any other index must be an Ey cell.  Several
+ *         sources (receivers) of one shot may share a cell: they add up.
+ * Returns TM_EINVAL on an inconsistent descriptor (order not in {2,4,8},
+ * grid too small, window outside [P, n-P], empty window, ny*nx >= 2^31,
+ * bad indices, ckpt_every < 0), TM_ENOMEM when the workspace would exceed
+ * hbm_budget.  The plan copies everything it needs.
+ */
+tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const int64_t* src,
+                         const int64_t* rec, tm_plan** out);
+
+void tm_plan_destroy(tm_plan* plan);
+
+/* Bytes of device workspace the plan needs (host only). */
+tm_status tm_workspace_bytes(const tm_plan* plan, uint64_t* bytes);
+
+/*
+ * Courant number sqrt(max(Cb*Cq)) * sum|c_k| * sqrt(1/dx^2 + 1/dy^2) of a
+ * model; the scheme is stable when it is at most 1.  cb, cq: device
+ * float32 [ny][nx].  Uses the workspace's scratch area and synchronises
+ * ``stream``.
+ */
+tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb,
+                     const float* cq, void* stream, double* courant);
+
+/*
+ * Forward propagation of all shots over steps [t0, t1), 0 <= t0 < t1 <= nt.
+ * t0 == 0 starts from zero fields; t0 > 0 continues the state a previous
+ * call on the same workspace left at step t0 (else TM_ESTATE).
+ *   ca, cb, cq: device float32 [ny][nx] update coefficients.
+ *   f: device float32 [nt][S][n_src] source amplitudes, added to Ey after
+ *      the E update of step n (required when n_src > 0).
+ *   r: device float32 [nt][S][n_rec]; rows t0..t1-1 receive Ey at the
+ *      receivers after the injection of the same step (0 for a negative
+ *      index).  May be NULL.
+ *   flags: TM_FWD_STORE keeps what tm_adjoint needs (every chunk from
+ *      t0 = 0 to nt must pass it); TM_FWD_CHECK returns TM_EUNSTABLE before
+ *      stepping when the Courant number exceeds 1.
+ */
+tm_status tm_forward(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca,
+                     const float* cb, const float* cq, const float* f, float* r,
+                     int64_t t0, int64_t t1, int32_t flags, void* stream);
+
+/*
+ * Exact discrete adjoint (time-reversed transpose of the forward step, CPML
+ * included) over all nt steps, after a storing tm_forward that reached nt on
+ * the same workspace (else TM_ESTATE).  May be called repeatedly.
+ *   ca, cb, cq, f: the same arrays as the forward (f is re-read by the
+ *      segment replay of checkpoint mode).
+ *   grad_r: device float32 [nt][S][n_rec], dJ/dr (required when n_rec > 0).
+ *   grad_f: device float32 [nt][S][n_src], receives dJ/df (adjoint field at
+ *      the sources); may be NULL.
+ *   grad_ca_shot, grad_cb_shot: device float32 [S][ny][nx]; overwritten with
+ *      the per-shot gradients sum_n lambda^{n+1} Ey^n and
+ *      sum_n lambda^{n+1} curlH^n on the interior window, 0 elsewhere.
+ *      Either may be NULL.
+ */
+tm_status tm_adjoint(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca,
+                     const float* cb, const float* cq, const float* f, const float* grad_r,
+                     float* grad_f, float* grad_ca_shot, float* grad_cb_shot, void* stream);
+
+/*
+ * Shot sum of the per-shot gradients (combine_grad): grad[j] = sum_s
+ * grad_shot[s][j], shots summed in ascending order (deterministic).
+ * grad_ca/grad_cb: device float32 [ny][nx], overwritten.  A NULL pair
+ * member is skipped.
+ */
+tm_status tm_grad(const tm_plan* plan, const float* grad_ca_shot, const float* grad_cb_shot,
+                  float* grad_ca, float* grad_cb, void* stream);
+
+/* Static description of a status code. */
+const char* tm_status_string(tm_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TM_FDTD_H */

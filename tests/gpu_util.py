@@ -1,0 +1,80 @@
+"""Helpers shared by the GPU tests: run a workload through the C ABI and
+through the oracle, and compare."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from tm_maxwell_fdtd_amd import inputs
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
+
+
+def observed_records_oracle(orc, wl):
+    """Observed data of a workload with an anomaly model (oracle side)."""
+    obs = inputs.observed_coefficients(wl)
+    if obs is None:
+        return None
+    ca, cb, cq = (np.asarray(x, np.float32).astype(np.float64) for x in obs)
+    r, _, _ = orc.forward(wl, ca=ca, cb=cb, cq=cq)
+    return r
+
+
+def run_oracle(orc, wl, observed=None):
+    return orc.misfit_and_gradient(wl, observed=observed)
+
+
+def run_gpu(wl, observed=None, snap=None, ckpt_every=None, grad_r=None, obs_coefs=None):
+    """Forward (storing), residual, adjoint and shot sum on the GPU.
+
+    ``observed``: records of the observed model, a numpy array, or the
+    string "gpu" to compute them on the GPU from the workload's observed
+    model.  Returns numpy arrays.
+    """
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    prop = native.Propagator(wl, snap=snap, ckpt_every=ckpt_every)
+    try:
+        r = prop.forward(store=True)
+        if grad_r is not None:
+            resid = torch.as_tensor(np.asarray(grad_r, np.float32), device=prop.device)
+        elif observed is None:
+            resid = r
+        else:
+            d = torch.as_tensor(np.asarray(observed, np.float32), device=prop.device)
+            resid = (r - d).contiguous()
+        grad_f, gca, gcb = prop.adjoint(resid)
+        ga, gb = prop.grad(gca, gcb)
+        torch.cuda.synchronize()
+        out = dict(records=r.cpu().numpy(), grad_f=grad_f.cpu().numpy(), gca_shot=gca.cpu().numpy(),
+                   gcb_shot=gcb.cpu().numpy(), gca=ga.cpu().numpy(), gcb=gb.cpu().numpy(),
+                   residual=resid.cpu().numpy())
+    finally:
+        prop.close()
+    return out
+
+
+def gpu_observed(wl):
+    """Records of the workload's observed model computed on the GPU."""
+    import dataclasses
+
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    ca, cb, cq = inputs.observed_coefficients(wl)
+    w2 = dataclasses.replace(wl, ca=ca, cb=cb, cq=cq)
+    prop = native.Propagator(w2)
+    try:
+        r = prop.forward(store=False)
+        torch.cuda.synchronize()
+        return r.cpu().numpy()
+    finally:
+        prop.close()

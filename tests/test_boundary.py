@@ -1,0 +1,164 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+and rejects invalid problems and call sequences on the host, before any HIP
+call (no GPU is touched by these tests)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from tm_maxwell_fdtd_amd import inputs, native
+
+FAKE_WS = 1 << 20          # an aligned address never dereferenced by these calls
+
+
+def make(wl, **over):
+    d = native.make_desc(wl)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def create(wl, cpml=None, src="wl", rec="wl", **over):
+    d = make(wl, **over)
+    st, plan = native.tm_plan_create(d, wl.cpml if cpml is None else cpml,
+                                     wl.src if isinstance(src, str) else src,
+                                     wl.rec if isinstance(rec, str) else rec)
+    if plan:
+        native.tm_plan_destroy(plan)
+    return st
+
+
+@pytest.fixture(scope="module")
+def wl():
+    return inputs.make_config(2, n_int=40, nt=30, n_shots=2, n_rec=5)
+
+
+def test_library_exports_every_declared_function():
+    names = native.declared_functions()
+    assert "tm_forward" in names and "tm_adjoint" in names and "tm_grad" in names
+    lib = native.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_distinct():
+    s = [native.status_string(i) for i in range(7)]
+    assert len(set(s)) == 7 and all(s)
+    assert native.status_string(99) == "unknown status"
+
+
+def test_valid_plan_and_workspace_size(wl):
+    st, plan = native.tm_plan_create(make(wl), wl.cpml, wl.src, wl.rec)
+    assert st == native.TM_OK and plan
+    st, nbytes = native.tm_workspace_bytes(plan)
+    assert st == native.TM_OK
+    S, N = wl.n_shots, wl.ny * wl.nx
+    snaps = 2 * wl.nt * S * (wl.pml_y1 - wl.pml_y0) * (wl.pml_x1 - wl.pml_x0) * 4
+    assert snaps + 6 * S * N * 4 <= nbytes <= snaps + 6 * S * N * 4 + 16 * S * N * 4 + (1 << 20)
+    native.tm_plan_destroy(plan)
+    # checkpoint mode needs less memory than the full store for long runs
+    long = inputs.make_config(2, n_int=40, nt=400, n_shots=2, n_rec=5)
+    st, p_full = native.tm_plan_create(make(long, ckpt_every=0), long.cpml, long.src, long.rec)
+    st2, p_ck = native.tm_plan_create(make(long, ckpt_every=20), long.cpml, long.src, long.rec)
+    assert st == st2 == native.TM_OK
+    assert native.tm_workspace_bytes(p_ck)[1] < native.tm_workspace_bytes(p_full)[1]
+    bf = inputs.make_config(2, n_int=40, nt=400, n_shots=2, n_rec=5, snap="bf16")
+    st3, p_bf = native.tm_plan_create(make(bf), bf.cpml, bf.src, bf.rec)
+    assert native.tm_workspace_bytes(p_bf)[1] < native.tm_workspace_bytes(p_full)[1]
+    for p in (p_full, p_ck, p_bf):
+        native.tm_plan_destroy(p)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("order", 3), ("order", 6), ("order", 0), ("n_shots", 0), ("nt", 0), ("n_src", -1),
+    ("snap", 2), ("ckpt_every", -1), ("ny", 5), ("dx", 0.0), ("dy", float("nan")),
+    ("pml_y0", 1), ("pml_x1", 10 ** 6), ("pml_y1", 20),
+])
+def test_invalid_descriptor(wl, field, value):
+    over = {field: value}
+    if field == "pml_y1":
+        over["pml_y0"] = 20            # empty window
+    assert create(wl, **over) == native.TM_EINVAL
+
+
+def test_window_outside_grid(wl):
+    p = wl.order // 2
+    assert create(wl, pml_y1=wl.ny - p + 2) == native.TM_EINVAL
+    assert create(wl, pml_y1=wl.ny - p + 1) == native.TM_OK      # touches the last E row
+
+
+def test_invalid_indices(wl):
+    p = wl.order // 2
+    src = wl.src.copy()
+    src[0, 0] = 1 * wl.nx + 5                     # in the zero halo (row < P)
+    assert create(wl, src=src) == native.TM_EINVAL
+    src[0, 0] = wl.ny * wl.nx                     # past the slab
+    assert create(wl, src=src) == native.TM_EINVAL
+    src[0, 0] = (wl.ny - p) * wl.nx + (wl.nx - p)  # last E cell: allowed
+    assert create(wl, src=src) == native.TM_OK
+    src[0, 0] = -7                                 # negative: no source
+    assert create(wl, src=src) == native.TM_OK
+    rec = wl.rec.copy()
+    rec[1, 2] = 5 * wl.nx + (wl.nx - 1)            # last column is halo
+    assert create(wl, rec=rec) == native.TM_EINVAL
+    st, plan = native.tm_plan_create(make(wl), wl.cpml, None, wl.rec)
+    assert st == native.TM_EINVAL                  # n_src > 0 needs indices
+
+
+def test_invalid_cpml(wl):
+    bad = wl.cpml.copy()
+    bad[2, 0] = 0.0                                 # kappa_y = 0 on a band row
+    assert create(wl, cpml=bad) == native.TM_EINVAL
+    bad = wl.cpml.copy()
+    bad[7, 3] = np.nan
+    assert create(wl, cpml=bad) == native.TM_EINVAL
+    ok = wl.cpml.copy()
+    ok[2, wl.pml_y0 + 3] = 0.0                      # kappa unused off the band
+    assert create(wl, cpml=ok) == native.TM_OK
+
+
+def test_memory_budget(wl):
+    st, plan = native.tm_plan_create(make(wl), wl.cpml, wl.src, wl.rec)
+    need = native.tm_workspace_bytes(plan)[1]
+    native.tm_plan_destroy(plan)
+    assert create(wl, hbm_budget=need) == native.TM_OK
+    assert create(wl, hbm_budget=need - 1) == native.TM_ENOMEM
+
+
+def test_null_arguments():
+    L = native.lib()
+    out = ctypes.c_void_p()
+    assert L.tm_plan_create(None, None, None, None, ctypes.byref(out)) == native.TM_EINVAL
+    assert L.tm_workspace_bytes(None, None) == native.TM_EINVAL
+    assert L.tm_forward(None, None, 0, None, None, None, None, None, 0, 1, 0, None) == native.TM_EINVAL
+    assert L.tm_adjoint(None, None, 0, None, None, None, None, None, None, None, None, None) == native.TM_EINVAL
+    assert L.tm_grad(None, None, None, None, None, None) == native.TM_EINVAL
+
+
+def test_call_sequence_checked_before_launch(wl):
+    st, plan = native.tm_plan_create(make(wl), wl.cpml, wl.src, wl.rec)
+    nbytes = native.tm_workspace_bytes(plan)[1]
+    dev = FAKE_WS
+    try:
+        # step range
+        for t0, t1 in ((0, 0), (-1, 3), (5, 4), (0, wl.nt + 1)):
+            assert native.tm_forward(plan, dev, nbytes, dev, dev, dev, dev, None, t0, t1, 0, None) == native.TM_EINVAL
+        # unknown flag bits
+        assert native.tm_forward(plan, dev, nbytes, dev, dev, dev, dev, None, 0, 1, 8, None) == native.TM_EINVAL
+        # too-small workspace / misaligned workspace
+        assert native.tm_forward(plan, dev, nbytes - 1, dev, dev, dev, dev, None, 0, 1, 0, None) == native.TM_ENOMEM
+        assert native.tm_forward(plan, dev + 4, nbytes, dev, dev, dev, dev, None, 0, 1, 0, None) == native.TM_EINVAL
+        # missing wavelet with sources
+        assert native.tm_forward(plan, dev, nbytes, dev, dev, dev, None, None, 0, 1, 0, None) == native.TM_EINVAL
+        # continuing a forward that never started
+        assert native.tm_forward(plan, dev, nbytes, dev, dev, dev, dev, None, 3, 5, 0, None) == native.TM_ESTATE
+        # gradients without a storing forward
+        assert native.tm_adjoint(plan, dev, nbytes, dev, dev, dev, dev, dev, None, dev, dev, None) == native.TM_ESTATE
+        # residual required when there are receivers
+        assert native.tm_adjoint(plan, dev, nbytes, dev, dev, dev, dev, None, None, None, None, None) == native.TM_EINVAL
+        # shot sum needs matching pairs
+        assert native.tm_grad(plan, dev, None, None, None, None) == native.TM_EINVAL
+        assert native.tm_grad(plan, None, None, None, dev, None) == native.TM_EINVAL
+    finally:
+        native.tm_plan_destroy(plan)

@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: records relative L2 <= 1e-5; gradients dJ/dCa, dJ/dCb (and the
+source gradient) relative L2 <= 1e-4 with float32 snapshots and <= 2e-2
+with bfloat16 snapshots.  Both sides start from the same float32 inputs
+(``inputs.as_f32``).  Sizes are reduced versions of the five workloads
+(same recipes) that span several 64x4 tiles with ragged tails.
+"""
+
+import numpy as np
+import pytest
+
+from tm_maxwell_fdtd_amd import inputs
+
+from gpu_util import gpu_observed, observed_records_oracle, rel_l2, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+REC_TOL = 1e-5
+GRAD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on the CPU)")
+    from tm_maxwell_fdtd_amd import native
+
+    native.lib()
+
+
+def check(orc, wl, observed_orc=None, snap=None, ckpt_every=None, label=""):
+    """Records, gradients and grad_f of the GPU path against the oracle.
+
+    tm_adjoint takes dJ/dr as an input; both sides get the same residual
+    (the oracle's, rounded to float32 for the GPU), so the comparison
+    measures the propagator and not the conditioning of a misfit.
+    """
+    snap = wl.snap if snap is None else snap
+    ref = run_oracle(orc, wl, observed=observed_orc)
+    got = run_gpu(wl, snap=snap, ckpt_every=ckpt_every, grad_r=ref["residual"])
+    e_r = rel_l2(got["records"], ref["records"])
+    e_a = rel_l2(got["gca"], ref["gca"])
+    e_b = rel_l2(got["gcb"], ref["gcb"])
+    e_f = rel_l2(got["grad_f"], ref["grad_f"])
+    e_as = rel_l2(got["gca_shot"], ref["gca_shot"])
+    print(f"[{label}] records {e_r:.2e}  gCa {e_a:.2e}  gCb {e_b:.2e}  grad_f {e_f:.2e}  gCa/shot {e_as:.2e}",
+          flush=True)
+    tol = GRAD_TOL[snap]
+    assert e_r <= REC_TOL, e_r
+    assert e_a <= tol and e_b <= tol and e_as <= tol, (e_a, e_b, e_as)
+    assert e_f <= max(tol, 1e-4), e_f
+    # masked cells are exactly zero
+    mask = np.zeros((wl.ny, wl.nx), bool)
+    mask[wl.pml_y0:wl.pml_y1, wl.pml_x0:wl.pml_x1] = True
+    assert np.all(got["gca_shot"][:, ~mask] == 0) and np.all(got["gcb_shot"][:, ~mask] == 0)
+    return got, ref
+
+
+def test_config1_full_size(orc):
+    wl = inputs.as_f32(inputs.make_config(1))
+    d_orc = observed_records_oracle(orc, wl)
+    d_gpu = gpu_observed(wl)
+    assert rel_l2(d_gpu, d_orc) <= REC_TOL
+    _, ref = check(orc, wl, observed_orc=d_orc, label="config1")
+    # End to end, with the residual r - d formed from the GPU's own records of
+    # both models.  The subtraction cancels most of the records, so its error
+    # is the records' error times |r| / |r - d|; the gradients (linear in the
+    # residual) may carry that error but no more.
+    e2e = run_gpu(wl, observed=d_gpu, snap="f32")
+    e_res = rel_l2(e2e["residual"], ref["residual"])
+    cond = np.linalg.norm(ref["records"]) / np.linalg.norm(ref["residual"])
+    print(f"[config1 end-to-end] residual {e_res:.2e} (|r|/|r-d| = {cond:.0f})  "
+          f"gCa {rel_l2(e2e['gca'], ref['gca']):.2e}  gCb {rel_l2(e2e['gcb'], ref['gcb']):.2e}  "
+          f"grad_f {rel_l2(e2e['grad_f'], ref['grad_f']):.2e}", flush=True)
+    assert e_res <= 2 * REC_TOL * cond
+    for key in ("gca", "gcb", "grad_f"):
+        assert rel_l2(e2e[key], ref[key]) <= GRAD_TOL["f32"] + 2 * e_res, key
+
+
+@pytest.mark.parametrize("cfg,over", [
+    (2, dict(n_int=100, nt=300, n_shots=4, n_rec=20)),
+    (3, dict(n_int=120, nt=300, n_shots=3, n_rec=24)),
+    (4, dict(n_int=100, nt=200, n_shots=2, n_rec=32, ckpt_every=64)),
+    (5, dict(n_int=96, nt=250, n_shots=8, n_rec=12)),
+])
+def test_reduced_configs(orc, cfg, over):
+    wl = inputs.as_f32(inputs.make_config(cfg, **over))
+    check(orc, wl, label=f"config{cfg}-reduced")
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_random_heterogeneous(orc, order):
+    wl = inputs.as_f32(inputs.random_workload(order, 70, 9, nt=160, n_shots=3, n_src=3, n_rec=7,
+                                              seed=100 + order, src_anywhere=True))
+    # duplicate and negative indices
+    wl.src[1, 1] = wl.src[1, 0]
+    wl.src[2, 2] = -1
+    wl.rec[0, 3] = wl.rec[0, 2]
+    wl.rec[2, 0] = -1
+    wl.rec[1, 4] = wl.src[1, 0]          # receiver on a source cell
+    check(orc, wl, snap="f32", label=f"random-o{order}")
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_bf16_snapshots(orc, order):
+    wl = inputs.as_f32(inputs.random_workload(order, 60, 8, nt=140, n_shots=2, n_src=1, n_rec=9,
+                                              seed=200 + order))
+    check(orc, wl, snap="bf16", label=f"bf16-o{order}")
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_gpu_dot_test(order):
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.random_workload(order, 50, 8, nt=120, n_shots=2, n_src=3, n_rec=6,
+                                              seed=300 + order, src_anywhere=True))
+    prop = native.Propagator(wl)
+    try:
+        r = prop.forward(store=False)
+        d = torch.randn(r.shape, generator=torch.Generator().manual_seed(order)).to(prop.device)
+        grad_f, _, _ = prop.adjoint(d, want_grads=False)
+        lhs = float((r.double() * d.double()).sum())
+        rhs = float((prop.f.double() * grad_f.double()).sum())
+    finally:
+        prop.close()
+    assert abs(lhs - rhs) <= 1e-5 * abs(lhs), (lhs, rhs)
+
+
+def test_deterministic_and_chunked():
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.random_workload(8, 80, 10, nt=90, n_shots=3, n_src=2, n_rec=8, seed=401))
+    prop = native.Propagator(wl)
+    try:
+        r1 = prop.forward(store=True)
+        _, a1, b1 = prop.adjoint(r1)
+        r2 = torch.zeros_like(r1)
+        prop.forward(r=r2, store=True, t0=0, t1=37)
+        prop.forward(r=r2, store=True, t0=37, t1=90)
+        _, a2, b2 = prop.adjoint(r2)
+        torch.cuda.synchronize()
+        assert torch.equal(r1, r2)
+        assert torch.equal(a1, a2) and torch.equal(b1, b2)
+    finally:
+        prop.close()
+
+
+def test_checkpoint_replay_bitwise_equals_full_store():
+    wl = inputs.as_f32(inputs.random_workload(4, 64, 8, nt=150, n_shots=2, n_src=1, n_rec=6, seed=501))
+    full = run_gpu(wl, snap="f32", ckpt_every=0)
+    for k in (16, 64, 149):
+        ck = run_gpu(wl, snap="f32", ckpt_every=k)
+        for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+            np.testing.assert_array_equal(ck[key], full[key], err_msg=f"K={k} {key}")
+
+
+def test_batched_shots_bitwise_equal_single_shots():
+    import dataclasses
+
+    wl = inputs.as_f32(inputs.random_workload(8, 60, 8, nt=80, n_shots=3, n_src=2, n_rec=5, seed=601))
+    allr = run_gpu(wl, snap="f32")
+    for s in range(3):
+        one = dataclasses.replace(wl, n_shots=1, src=wl.src[s:s + 1].copy(), rec=wl.rec[s:s + 1].copy(),
+                                  f=wl.f[:, s:s + 1].copy())
+        o = run_gpu(one, snap="f32")
+        np.testing.assert_array_equal(o["records"][:, 0], allr["records"][:, s])
+        np.testing.assert_array_equal(o["gca_shot"][0], allr["gca_shot"][s])
+        np.testing.assert_array_equal(o["gcb_shot"][0], allr["gcb_shot"][s])
+
+
+def test_error_codes_on_device():
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.make_config(1, nt=20))
+    prop = native.Propagator(wl)
+    try:
+        # adjoint with gradients before any storing forward
+        with pytest.raises(native.TmError) as ei:
+            prop.adjoint(torch.zeros((wl.nt, 1, wl.n_rec), device=prop.device))
+        assert ei.value.status == native.TM_ESTATE
+        prop.forward(store=False)
+        with pytest.raises(native.TmError) as ei:
+            prop.adjoint(torch.zeros((wl.nt, 1, wl.n_rec), device=prop.device))
+        assert ei.value.status == native.TM_ESTATE
+        # continuing a chunk from the wrong step
+        with pytest.raises(native.TmError) as ei:
+            prop.forward(t0=5, t1=10)
+        assert ei.value.status == native.TM_ESTATE
+        # workspace too small
+        st = native.tm_forward(prop.plan, native.ptr(prop.ws), prop.ws_bytes - 256, native.ptr(prop.ca),
+                               native.ptr(prop.cb), native.ptr(prop.cq), native.ptr(prop.f), None, 0, 5, 0,
+                               native.stream_handle())
+        assert st == native.TM_ENOMEM
+        # unstable model: Courant number above 1
+        assert prop.courant() == pytest.approx(0.9, rel=1e-5)
+        prop.cb.mul_(1.5)
+        with pytest.raises(native.TmError) as ei:
+            prop.forward(check=True)
+        assert ei.value.status == native.TM_EUNSTABLE
+    finally:
+        prop.close()

@@ -1,0 +1,87 @@
+// Shared device-side definitions of the TM FDTD kernels (gfx950, wave64).
+//
+// Notation follows tide-GPR 0.0.9 tide/csrc/maxwell.cu: fields Ey, Hx, Hz;
+// update coefficients Ca, Cb (E) and Cq (H); CPML arrays a, b, kappa on the
+// integer grid (E-update derivatives) and on the half grid (H-update
+// derivatives); FD_PAD = P = order / 2 zero halo cells per side.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tmf {
+
+// Geometry handed to every kernel by value.
+struct Geo {
+    int ny, nx, P;
+    int y0, y1, x0, x1;   // interior window [y0, y1) x [x0, x1)
+    int hy1, hx1;         // upper bound of the H-flag interior: y1 - 1, x1 - 1
+    int byl, by;          // band rows: [0, y0) -> [0, byl), [y1-1, ny) -> byl + (y - (y1-1))
+    int bxl, bx;          // band columns, same mapping along x
+    int nyi, nxi;         // interior window size (snapshot slab)
+    int L;                // row length of the packed CPML table
+    float rdy, rdx;       // 1/dy, 1/dx
+    int64_t slab;         // ny * nx
+};
+
+// Rows of the packed CPML table [12][L].
+enum CpmlRow { AY = 0, BY, KY, AYH, BYH, KYH, AX, BX, KX, AXH, BXH, KXH };
+
+// Staggered-grid Taylor coefficients c_1..c_P (the page's stencil header is
+// not on the page; these are the standard staggered coefficients).
+template <int P>
+__device__ __forceinline__ constexpr float coef(int k);
+
+template <>
+__device__ __forceinline__ constexpr float coef<1>(int) { return 1.0f; }
+template <>
+__device__ __forceinline__ constexpr float coef<2>(int k)
+{
+    return k == 1 ? (float)(9.0 / 8.0) : (float)(-1.0 / 24.0);
+}
+template <>
+__device__ __forceinline__ constexpr float coef<4>(int k)
+{
+    return k == 1 ? (float)(1225.0 / 1024.0)
+         : k == 2 ? (float)(-245.0 / 3072.0)
+         : k == 3 ? (float)(49.0 / 5120.0)
+                  : (float)(-5.0 / 7168.0);
+}
+
+__device__ __forceinline__ int band_x(const Geo& g, int x) { return x < g.x0 ? x : g.bxl + (x - g.hx1); }
+__device__ __forceinline__ int band_y(const Geo& g, int y) { return y < g.y0 ? y : g.byl + (y - g.hy1); }
+
+// CPML flags: E derivatives outside [lo, hi), H derivatives outside [lo, hi-1).
+__device__ __forceinline__ bool flag_ex(const Geo& g, int x) { return x < g.x0 || x >= g.x1; }
+__device__ __forceinline__ bool flag_ey(const Geo& g, int y) { return y < g.y0 || y >= g.y1; }
+__device__ __forceinline__ bool flag_hx(const Geo& g, int x) { return x < g.x0 || x >= g.hx1; }
+__device__ __forceinline__ bool flag_hy(const Geo& g, int y) { return y < g.y0 || y >= g.hy1; }
+
+// float -> bfloat16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Snapshot element types.
+enum SnapKind { SNAP_NONE = 0, SNAP_F32 = 1, SNAP_BF16 = 2 };
+
+template <int SNAP>
+__device__ __forceinline__ void snap_store(void* base, int64_t w, float v)
+{
+    if constexpr (SNAP == SNAP_F32) static_cast<float*>(base)[w] = v;
+    else if constexpr (SNAP == SNAP_BF16) static_cast<uint16_t*>(base)[w] = f32_to_bf16(v);
+}
+template <int SNAP>
+__device__ __forceinline__ float snap_load(const void* base, int64_t w)
+{
+    if constexpr (SNAP == SNAP_F32) return static_cast<const float*>(base)[w];
+    else if constexpr (SNAP == SNAP_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[w]);
+    else return 0.0f;
+}
+
+}  // namespace tmf

@@ -1,0 +1,590 @@
+// Host runtime and C ABI of the TM FDTD propagator (see include/tm_fdtd.h).
+//
+// The plan validates a problem on the host, builds conflict-free scatter
+// tables for the sources and receivers, and lays out the caller-allocated
+// workspace.  tm_forward / tm_adjoint / tm_grad enqueue kernels on the
+// caller's stream; there is no global state, so plans are independent.
+//
+// Host loop structure follows the launchers of tide-GPR 0.0.9
+// tide/csrc/maxwell.cu: forward = H pass, E pass (storing variant on stored
+// steps), sources, receivers; backward (reverse time) = residual injection
+// at receivers, adjoint read at sources, lambda_H pass, lambda_E pass with
+// gradient accumulation; then combine_grad.  Checkpoint mode stores the
+// full state (fields and band CPML memories) every K steps and replays each
+// segment into a K-step snapshot buffer inside tm_adjoint.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "tm_fdtd.h"
+#include "tm_kernels.hpp"
+
+using namespace tmf;
+
+#define TM_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr uint64_t ALIGN = 256;
+uint64_t align_up(uint64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+double abs_coef_sum(int order)
+{
+    switch (order) {
+    case 2: return 1.0;
+    case 4: return 9.0 / 8.0 + 1.0 / 24.0;
+    case 8: return 1225.0 / 1024.0 + 245.0 / 3072.0 + 49.0 / 5120.0 + 5.0 / 7168.0;
+    default: return 0.0;
+    }
+}
+
+// Distinct-cell scatter table of one index set ([S][n] cells, negative = none).
+struct Scatter {
+    std::vector<int32_t> cell;   // [S][n] distinct cells, -1 padded
+    std::vector<int32_t> ptr;    // [S][n+1] CSR offsets into list
+    std::vector<int32_t> list;   // [S][n] member indices grouped by cell (ascending)
+    std::vector<int32_t> idx;    // [S][n] raw cell or -1 (for gathers)
+};
+
+Scatter build_scatter(const int64_t* ids, int64_t S, int64_t n)
+{
+    Scatter t;
+    t.cell.assign(S * n, -1);
+    t.ptr.assign(S * (n + 1), 0);
+    t.list.assign(S * n, 0);
+    t.idx.assign(S * n, -1);
+    std::vector<std::pair<int64_t, int32_t>> v;
+    for (int64_t s = 0; s < S; ++s) {
+        v.clear();
+        for (int64_t i = 0; i < n; ++i) {
+            const int64_t c = ids[s * n + i];
+            t.idx[s * n + i] = c >= 0 ? (int32_t)c : -1;
+            if (c >= 0) v.emplace_back(c, (int32_t)i);
+        }
+        std::stable_sort(v.begin(), v.end(),
+                         [](const auto& a, const auto& b) { return a.first < b.first; });
+        int32_t u = -1, q = 0;
+        int32_t* ptr = t.ptr.data() + s * (n + 1);
+        for (size_t k = 0; k < v.size(); ++k) {
+            if (k == 0 || v[k].first != v[k - 1].first) {
+                ++u;
+                t.cell[s * n + u] = (int32_t)v[k].first;
+                ptr[u] = q;
+            }
+            t.list[s * n + q] = v[k].second;
+            ++q;
+        }
+        for (int64_t k = u + 1; k <= n; ++k) ptr[k] = q;
+    }
+    return t;
+}
+
+struct Layout {
+    uint64_t cpml = 0, tables = 0, scratch = 0;
+    uint64_t fwd = 0, fwd_bytes = 0;       // E, Hx, Hz, psi_ez, psi_ex, psi_hxz, psi_hzx
+    uint64_t E = 0, Hx = 0, Hz = 0, psi_ez = 0, psi_ex = 0, psi_hxz = 0, psi_hzx = 0;
+    uint64_t adj = 0, adj_bytes = 0;       // lambdas, adjoint memories, band temporaries
+    uint64_t lE = 0, lHx = 0, lHz = 0, phi_ez = 0, phi_ex = 0, phi_hxz = 0, phi_hzx = 0;
+    uint64_t Ub = 0, Wb = 0, TZb = 0, TXb = 0;
+    uint64_t snapE = 0, snapC = 0, snap_step = 0;   // per-step bytes of one snapshot array
+    uint64_t ckpt = 0, ckpt_slot = 0;
+    uint64_t total = 0;
+};
+
+}  // namespace
+
+struct tm_plan {
+    tm_desc d{};
+    int P = 0;
+    Geo g{};
+    std::vector<float> cpml;       // [12][L]
+    std::vector<int32_t> tables;   // scatter tables, packed
+    uint64_t t_s_cell = 0, t_s_ptr = 0, t_s_list = 0, t_s_idx = 0;
+    uint64_t t_r_cell = 0, t_r_ptr = 0, t_r_list = 0, t_r_idx = 0;
+    Layout lay;
+    int64_t K = 0, n_seg = 0, n_ckpt = 0, seg_steps = 0;
+    // pinned staging copy of cpml + tables (allocated on first device call)
+    void* pinned = nullptr;
+    uint64_t pinned_bytes = 0;
+    // sequence state
+    void* ws_last = nullptr;
+    int64_t fwd_next = -1;
+    bool stored_ok = false;
+    bool fwd_complete = false;
+};
+
+namespace {
+
+tm_status validate_indices(const int64_t* ids, int64_t S, int64_t n, int64_t ny, int64_t nx, int P)
+{
+    if (n > 0 && ids == nullptr) return TM_EINVAL;
+    for (int64_t k = 0; k < S * n; ++k) {
+        const int64_t c = ids[k];
+        if (c < 0) continue;
+        if (c >= ny * nx) return TM_EINVAL;
+        const int64_t y = c / nx, x = c % nx;
+        if (y < P || y > ny - P || x < P || x > nx - P) return TM_EINVAL;
+    }
+    return TM_OK;
+}
+
+bool finite_all(const float* p, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        if (!std::isfinite(p[i])) return false;
+    return true;
+}
+
+void make_layout(tm_plan* p)
+{
+    const tm_desc& d = p->d;
+    const Geo& g = p->g;
+    Layout& L = p->lay;
+    const uint64_t S = (uint64_t)d.n_shots, slab = (uint64_t)g.slab;
+    const uint64_t fld = S * slab * 4;
+    const uint64_t yb = S * (uint64_t)g.by * (uint64_t)g.nx * 4;
+    const uint64_t xb = S * (uint64_t)g.ny * (uint64_t)g.bx * 4;
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) { uint64_t at = o; o = align_up(o + bytes); return at; };
+    L.cpml = take(12 * (uint64_t)g.L * 4);
+    L.tables = take(p->tables.size() * 4);
+    L.scratch = take(4096);
+    L.fwd = o;
+    L.E = take(fld); L.Hx = take(fld); L.Hz = take(fld);
+    L.psi_ez = take(yb); L.psi_ex = take(xb); L.psi_hxz = take(yb); L.psi_hzx = take(xb);
+    L.fwd_bytes = o - L.fwd;
+    L.adj = o;
+    L.lE = take(fld); L.lHx = take(fld); L.lHz = take(fld);
+    L.phi_ez = take(yb); L.phi_ex = take(xb); L.phi_hxz = take(yb); L.phi_hzx = take(xb);
+    L.Ub = take(xb); L.Wb = take(yb); L.TZb = take(xb); L.TXb = take(yb);
+    L.adj_bytes = o - L.adj;
+    const uint64_t esz = d.snap == TM_SNAP_BF16 ? 2 : 4;
+    L.snap_step = S * (uint64_t)g.nyi * (uint64_t)g.nxi * esz;
+    L.snap_step = align_up(L.snap_step);
+    L.snapE = take(L.snap_step * (uint64_t)p->seg_steps);
+    L.snapC = take(L.snap_step * (uint64_t)p->seg_steps);
+    L.ckpt_slot = align_up(L.fwd_bytes);
+    L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
+    L.total = o;
+}
+
+template <typename T>
+T* wsp(void* ws, uint64_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+#define HIPCHK(expr)                                   \
+    do {                                               \
+        if ((expr) != hipSuccess) return TM_EHIP;      \
+    } while (0)
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+tm_status zero(float* ptr, uint64_t bytes, hipStream_t st)
+{
+    const int64_t n = (int64_t)(bytes / 4);
+    if (n == 0) return TM_OK;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    k_zero<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(ptr, n);
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
+
+tm_status upload_tables(tm_plan* p, void* ws, hipStream_t st)
+{
+    const uint64_t cb = p->cpml.size() * 4, tb = p->tables.size() * 4;
+    if (p->pinned == nullptr) {
+        p->pinned_bytes = cb + tb;
+        HIPCHK(hipHostMalloc(&p->pinned, p->pinned_bytes, hipHostMallocDefault));
+        std::memcpy(p->pinned, p->cpml.data(), cb);
+        if (tb) std::memcpy(static_cast<char*>(p->pinned) + cb, p->tables.data(), tb);
+    }
+    HIPCHK(hipMemcpyAsync(wsp<char>(ws, p->lay.cpml), p->pinned, cb, hipMemcpyHostToDevice, st));
+    if (tb)
+        HIPCHK(hipMemcpyAsync(wsp<char>(ws, p->lay.tables), static_cast<char*>(p->pinned) + cb, tb,
+                              hipMemcpyHostToDevice, st));
+    return TM_OK;
+}
+
+struct Ptrs {
+    float *E, *Hx, *Hz, *psi_ez, *psi_ex, *psi_hxz, *psi_hzx;
+    float *lE, *lHx, *lHz, *phi_ez, *phi_ex, *phi_hxz, *phi_hzx, *Ub, *Wb, *TZb, *TXb;
+    const float* cp;
+    const int32_t *s_cell, *s_ptr, *s_list, *s_idx, *r_cell, *r_ptr, *r_list, *r_idx;
+    char *snapE, *snapC, *ckpt;
+    float* scratch;
+};
+
+Ptrs pointers(const tm_plan* p, void* ws)
+{
+    const Layout& L = p->lay;
+    Ptrs q{};
+    q.E = wsp<float>(ws, L.E); q.Hx = wsp<float>(ws, L.Hx); q.Hz = wsp<float>(ws, L.Hz);
+    q.psi_ez = wsp<float>(ws, L.psi_ez); q.psi_ex = wsp<float>(ws, L.psi_ex);
+    q.psi_hxz = wsp<float>(ws, L.psi_hxz); q.psi_hzx = wsp<float>(ws, L.psi_hzx);
+    q.lE = wsp<float>(ws, L.lE); q.lHx = wsp<float>(ws, L.lHx); q.lHz = wsp<float>(ws, L.lHz);
+    q.phi_ez = wsp<float>(ws, L.phi_ez); q.phi_ex = wsp<float>(ws, L.phi_ex);
+    q.phi_hxz = wsp<float>(ws, L.phi_hxz); q.phi_hzx = wsp<float>(ws, L.phi_hzx);
+    q.Ub = wsp<float>(ws, L.Ub); q.Wb = wsp<float>(ws, L.Wb);
+    q.TZb = wsp<float>(ws, L.TZb); q.TXb = wsp<float>(ws, L.TXb);
+    q.cp = wsp<float>(ws, L.cpml);
+    const int32_t* t = wsp<int32_t>(ws, L.tables);
+    q.s_cell = t + p->t_s_cell; q.s_ptr = t + p->t_s_ptr; q.s_list = t + p->t_s_list; q.s_idx = t + p->t_s_idx;
+    q.r_cell = t + p->t_r_cell; q.r_ptr = t + p->t_r_ptr; q.r_list = t + p->t_r_list; q.r_idx = t + p->t_r_idx;
+    q.snapE = wsp<char>(ws, L.snapE); q.snapC = wsp<char>(ws, L.snapC);
+    q.ckpt = wsp<char>(ws, L.ckpt);
+    q.scratch = wsp<float>(ws, L.scratch);
+    return q;
+}
+
+dim3 stencil_grid(const Geo& g, int64_t S)
+{
+    const int ex = g.nx - 2 * g.P + 1, ey = g.ny - 2 * g.P + 1;
+    return dim3((unsigned)((ex + BLK_X - 1) / BLK_X), (unsigned)((ey + BLK_Y - 1) / BLK_Y), (unsigned)S);
+}
+
+// One forward step t.  snap: SNAP_* kind for the E pass, with destinations.
+template <int P>
+void fwd_step(const tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
+              const float* f, float* r, int64_t t, int snap, void* se, void* sc, hipStream_t st)
+{
+    const Geo& g = p->g;
+    const dim3 grid = stencil_grid(g, p->d.n_shots), blk(BLK_X, BLK_Y);
+    k_fwd_h<P><<<grid, blk, 0, st>>>(g, cq, q.E, q.Hx, q.Hz, q.psi_ez, q.psi_ex, q.cp);
+    if (snap == SNAP_F32)
+        k_fwd_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
+    else if (snap == SNAP_BF16)
+        k_fwd_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
+    else
+        k_fwd_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, nullptr, nullptr);
+    const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
+    if (ns > 0 || (r != nullptr && nr > 0)) {
+        const int64_t S = p->d.n_shots;
+        k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
+            g.slab, q.E, ns > 0 ? f + t * S * ns : nullptr, ns, q.s_cell, q.s_ptr, q.s_list,
+            (r != nullptr && nr > 0) ? r + t * S * nr : nullptr, nr, q.r_idx);
+    }
+}
+
+template <int P>
+void adj_step(const tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
+              const float* grad_r, float* grad_f, int64_t t, int snap, const void* se,
+              const void* sc, float* gca, float* gcb, hipStream_t st)
+{
+    const Geo& g = p->g;
+    const int64_t S = p->d.n_shots;
+    const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
+    if (nr > 0 || (grad_f != nullptr && ns > 0)) {
+        k_adj_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
+            g.slab, q.lE, nr > 0 ? grad_r + t * S * nr : nullptr, nr, q.r_cell, q.r_ptr, q.r_list,
+            (grad_f != nullptr && ns > 0) ? grad_f + t * S * ns : nullptr, ns, q.s_idx);
+    }
+    const int64_t band_cells = (int64_t)g.by * g.nx + (int64_t)(g.ny - g.by) * g.bx;
+    if (band_cells > 0)
+        k_adj_band<P><<<dim3((unsigned)((band_cells + 255) / 256), (unsigned)S), dim3(256), 0, st>>>(
+            g, cb, q.lE, q.phi_hzx, q.phi_hxz, q.Ub, q.Wb, q.cp);
+    const dim3 grid = stencil_grid(g, S), blk(BLK_X, BLK_Y);
+    k_adj_h<P><<<grid, blk, 0, st>>>(g, cb, cq, q.lE, q.lHx, q.lHz, q.phi_ez, q.phi_ex, q.Ub, q.Wb,
+                                     q.TZb, q.TXb, q.cp);
+    if (snap == SNAP_F32)
+        k_adj_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
+    else if (snap == SNAP_BF16)
+        k_adj_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
+    else
+        k_adj_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, nullptr, nullptr, nullptr, nullptr);
+}
+
+int snap_kind(const tm_plan* p) { return p->d.snap == TM_SNAP_BF16 ? SNAP_BF16 : SNAP_F32; }
+
+tm_status check_ws(const tm_plan* p, void* ws, uint64_t ws_bytes)
+{
+    if (ws == nullptr) return TM_EINVAL;
+    if (ws_bytes < p->lay.total) return TM_ENOMEM;
+    if ((reinterpret_cast<uintptr_t>(ws) & (ALIGN - 1)) != 0) return TM_EINVAL;
+    return TM_OK;
+}
+
+template <int P>
+tm_status run_forward(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq,
+                      const float* f, float* r, int64_t t0, int64_t t1, bool store, hipStream_t st)
+{
+    const Ptrs q = pointers(p, ws);
+    const bool full = p->K == 0;
+    for (int64_t t = t0; t < t1; ++t) {
+        if (store && !full && t > 0 && t % p->K == 0) {
+            const int64_t slot = t / p->K - 1;
+            HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, wsp<char>(ws, p->lay.fwd),
+                                  p->lay.fwd_bytes, hipMemcpyDeviceToDevice, st));
+        }
+        if (store && full)
+            fwd_step<P>(p, q, ca, cb, cq, f, r, t, snap_kind(p), q.snapE + t * p->lay.snap_step,
+                        q.snapC + t * p->lay.snap_step, st);
+        else
+            fwd_step<P>(p, q, ca, cb, cq, f, r, t, SNAP_NONE, nullptr, nullptr, st);
+    }
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
+
+template <int P>
+tm_status run_adjoint(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq,
+                      const float* f, const float* grad_r, float* grad_f, float* gca, float* gcb,
+                      hipStream_t st)
+{
+    const Ptrs q = pointers(p, ws);
+    const int64_t nt = p->d.nt;
+    const bool want_grad = gca != nullptr || gcb != nullptr;
+    const int snap = want_grad ? snap_kind(p) : SNAP_NONE;
+    if (p->K == 0 || !want_grad) {
+        for (int64_t t = nt - 1; t >= 0; --t)
+            adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, snap, q.snapE + (want_grad ? t : 0) * p->lay.snap_step,
+                        q.snapC + (want_grad ? t : 0) * p->lay.snap_step, gca, gcb, st);
+    } else {
+        for (int64_t seg = p->n_seg - 1; seg >= 0; --seg) {
+            const int64_t ta = seg * p->K, tb = std::min(ta + p->K, nt);
+            if (seg == 0) {
+                tm_status z = zero(wsp<float>(ws, p->lay.fwd), p->lay.fwd_bytes, st);
+                if (z != TM_OK) return z;
+            } else {
+                HIPCHK(hipMemcpyAsync(wsp<char>(ws, p->lay.fwd), q.ckpt + (seg - 1) * p->lay.ckpt_slot,
+                                      p->lay.fwd_bytes, hipMemcpyDeviceToDevice, st));
+            }
+            for (int64_t t = ta; t < tb; ++t)
+                fwd_step<P>(p, q, ca, cb, cq, f, nullptr, t, snap, q.snapE + (t - ta) * p->lay.snap_step,
+                            q.snapC + (t - ta) * p->lay.snap_step, st);
+            for (int64_t t = tb - 1; t >= ta; --t)
+                adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, snap, q.snapE + (t - ta) * p->lay.snap_step,
+                            q.snapC + (t - ta) * p->lay.snap_step, gca, gcb, st);
+        }
+    }
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
+
+tm_status courant_impl(tm_plan* p, void* ws, const float* cb, const float* cq, hipStream_t st, double* out)
+{
+    const Ptrs q = pointers(p, ws);
+    constexpr int NB = 256;
+    k_max_cbcq<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, p->g.slab, q.scratch);
+    HIPCHK(hipGetLastError());
+    float part[NB];
+    HIPCHK(hipMemcpyAsync(part, q.scratch, sizeof(part), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    double m = 0.0;
+    for (int i = 0; i < NB; ++i) {
+        if (part[i] != part[i]) { m = NAN; break; }
+        m = std::max(m, (double)part[i]);
+    }
+    const double rdx = 1.0 / p->d.dx, rdy = 1.0 / p->d.dy;
+    *out = std::sqrt(m) * abs_coef_sum(p->d.order) * std::sqrt(rdx * rdx + rdy * rdy);
+    return TM_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+TM_API const char* tm_status_string(tm_status s)
+{
+    switch (s) {
+    case TM_OK: return "ok";
+    case TM_EINVAL: return "invalid argument";
+    case TM_EUNSTABLE: return "unstable: Courant number above 1";
+    case TM_ENOMEM: return "workspace too small or over the memory budget";
+    case TM_EHIP: return "HIP runtime error";
+    case TM_ESTATE: return "invalid call sequence";
+    case TM_ENONFINITE: return "non-finite value";
+    default: return "unknown status";
+    }
+}
+
+TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const int64_t* src,
+                                const int64_t* rec, tm_plan** out)
+{
+    if (out == nullptr) return TM_EINVAL;
+    *out = nullptr;
+    if (desc == nullptr || cpml == nullptr) return TM_EINVAL;
+    const tm_desc d = *desc;
+    if (d.order != 2 && d.order != 4 && d.order != 8) return TM_EINVAL;
+    const int P = d.order / 2;
+    if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
+    if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16) return TM_EINVAL;
+    if (d.ny < 2 * P + 2 || d.nx < 2 * P + 2) return TM_EINVAL;
+    if (d.ny * d.nx >= (int64_t(1) << 31)) return TM_EINVAL;
+    if (d.n_shots * std::max<int64_t>(d.n_src, d.n_rec) >= (int64_t(1) << 31)) return TM_EINVAL;
+    if (d.n_shots > 65535) return TM_EINVAL;
+    if (!(d.dy > 0.0) || !(d.dx > 0.0) || !std::isfinite(d.dy) || !std::isfinite(d.dx)) return TM_EINVAL;
+    if (d.pml_y0 < P || d.pml_y1 <= d.pml_y0 || d.pml_y1 > d.ny - P + 1) return TM_EINVAL;
+    if (d.pml_x0 < P || d.pml_x1 <= d.pml_x0 || d.pml_x1 > d.nx - P + 1) return TM_EINVAL;
+    tm_status v = validate_indices(src, d.n_shots, d.n_src, d.ny, d.nx, P);
+    if (v != TM_OK) return v;
+    v = validate_indices(rec, d.n_shots, d.n_rec, d.ny, d.nx, P);
+    if (v != TM_OK) return v;
+    const int64_t L = std::max(d.ny, d.nx);
+    if (!finite_all(cpml, 12 * L)) return TM_EINVAL;
+    for (int64_t y = 0; y < d.ny; ++y) {
+        if ((y < d.pml_y0 || y >= d.pml_y1 - 1) && (cpml[KY * L + y] == 0.0f || cpml[KYH * L + y] == 0.0f))
+            return TM_EINVAL;
+    }
+    for (int64_t x = 0; x < d.nx; ++x) {
+        if ((x < d.pml_x0 || x >= d.pml_x1 - 1) && (cpml[KX * L + x] == 0.0f || cpml[KXH * L + x] == 0.0f))
+            return TM_EINVAL;
+    }
+
+    tm_plan* p = new (std::nothrow) tm_plan();
+    if (p == nullptr) return TM_ENOMEM;
+    p->d = d;
+    p->P = P;
+    Geo& g = p->g;
+    g.ny = (int)d.ny; g.nx = (int)d.nx; g.P = P;
+    g.y0 = (int)d.pml_y0; g.y1 = (int)d.pml_y1; g.x0 = (int)d.pml_x0; g.x1 = (int)d.pml_x1;
+    g.hy1 = g.y1 - 1; g.hx1 = g.x1 - 1;
+    g.byl = g.y0; g.by = g.y0 + (g.ny - g.hy1);
+    g.bxl = g.x0; g.bx = g.x0 + (g.nx - g.hx1);
+    g.nyi = g.y1 - g.y0; g.nxi = g.x1 - g.x0;
+    g.L = (int)L;
+    g.rdy = (float)(1.0 / d.dy); g.rdx = (float)(1.0 / d.dx);
+    g.slab = d.ny * d.nx;
+    p->cpml.assign(cpml, cpml + 12 * L);
+
+    const Scatter ss = build_scatter(src, d.n_shots, d.n_src);
+    const Scatter rs = build_scatter(rec, d.n_shots, d.n_rec);
+    auto append = [&](const std::vector<int32_t>& v) {
+        const uint64_t at = p->tables.size();
+        p->tables.insert(p->tables.end(), v.begin(), v.end());
+        return at;
+    };
+    p->t_s_cell = append(ss.cell); p->t_s_ptr = append(ss.ptr); p->t_s_list = append(ss.list); p->t_s_idx = append(ss.idx);
+    p->t_r_cell = append(rs.cell); p->t_r_ptr = append(rs.ptr); p->t_r_list = append(rs.list); p->t_r_idx = append(rs.idx);
+
+    if (d.ckpt_every > 0 && d.ckpt_every < d.nt) {
+        p->K = d.ckpt_every;
+        p->n_seg = (d.nt + p->K - 1) / p->K;
+        p->n_ckpt = p->n_seg - 1;
+        p->seg_steps = p->K;
+    } else {
+        p->K = 0;
+        p->n_seg = 1;
+        p->n_ckpt = 0;
+        p->seg_steps = d.nt;
+    }
+    make_layout(p);
+    if (d.hbm_budget > 0 && p->lay.total > d.hbm_budget) {
+        delete p;
+        return TM_ENOMEM;
+    }
+    *out = p;
+    return TM_OK;
+}
+
+TM_API void tm_plan_destroy(tm_plan* p)
+{
+    if (p == nullptr) return;
+    if (p->pinned != nullptr) (void)hipHostFree(p->pinned);
+    delete p;
+}
+
+TM_API tm_status tm_workspace_bytes(const tm_plan* p, uint64_t* bytes)
+{
+    if (p == nullptr || bytes == nullptr) return TM_EINVAL;
+    *bytes = p->lay.total;
+    return TM_OK;
+}
+
+TM_API tm_status tm_courant(tm_plan* p, void* ws, uint64_t ws_bytes, const float* cb, const float* cq,
+                            void* stream, double* courant)
+{
+    if (p == nullptr || cb == nullptr || cq == nullptr || courant == nullptr) return TM_EINVAL;
+    tm_status v = check_ws(p, ws, ws_bytes);
+    if (v != TM_OK) return v;
+    return courant_impl(p, ws, cb, cq, as_stream(stream), courant);
+}
+
+TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float* ca, const float* cb,
+                            const float* cq, const float* f, float* r, int64_t t0, int64_t t1,
+                            int32_t flags, void* stream)
+{
+    if (p == nullptr || ca == nullptr || cb == nullptr || cq == nullptr) return TM_EINVAL;
+    if (p->d.n_src > 0 && f == nullptr) return TM_EINVAL;
+    if (t0 < 0 || t1 <= t0 || t1 > p->d.nt) return TM_EINVAL;
+    if ((flags & ~(TM_FWD_STORE | TM_FWD_CHECK)) != 0) return TM_EINVAL;
+    tm_status v = check_ws(p, ws, ws_bytes);
+    if (v != TM_OK) return v;
+    if (t0 > 0 && (ws != p->ws_last || p->fwd_next != t0)) return TM_ESTATE;
+    hipStream_t st = as_stream(stream);
+    const bool store = (flags & TM_FWD_STORE) != 0;
+    if (flags & TM_FWD_CHECK) {
+        double c = 0.0;
+        v = courant_impl(p, ws, cb, cq, st, &c);
+        if (v != TM_OK) return v;
+        if (!(c <= 1.0)) return TM_EUNSTABLE;
+    }
+    v = upload_tables(p, ws, st);
+    if (v != TM_OK) return v;
+    if (t0 == 0) {
+        p->fwd_complete = false;
+        v = zero(wsp<float>(ws, p->lay.fwd), p->lay.fwd_bytes, st);
+        if (v != TM_OK) return v;
+        p->stored_ok = store;
+    } else {
+        p->stored_ok = p->stored_ok && store;
+    }
+    p->ws_last = ws;
+    p->fwd_next = -1;
+    switch (p->P) {
+    case 1: v = run_forward<1>(p, ws, ca, cb, cq, f, r, t0, t1, store, st); break;
+    case 2: v = run_forward<2>(p, ws, ca, cb, cq, f, r, t0, t1, store, st); break;
+    default: v = run_forward<4>(p, ws, ca, cb, cq, f, r, t0, t1, store, st); break;
+    }
+    if (v != TM_OK) return v;
+    p->fwd_next = t1;
+    p->fwd_complete = (t1 == p->d.nt) && p->stored_ok;
+    return TM_OK;
+}
+
+TM_API tm_status tm_adjoint(tm_plan* p, void* ws, uint64_t ws_bytes, const float* ca, const float* cb,
+                            const float* cq, const float* f, const float* grad_r, float* grad_f,
+                            float* grad_ca_shot, float* grad_cb_shot, void* stream)
+{
+    if (p == nullptr || ca == nullptr || cb == nullptr || cq == nullptr) return TM_EINVAL;
+    if (p->d.n_rec > 0 && grad_r == nullptr) return TM_EINVAL;
+    tm_status v = check_ws(p, ws, ws_bytes);
+    if (v != TM_OK) return v;
+    const bool want_grad = grad_ca_shot != nullptr || grad_cb_shot != nullptr;
+    if (want_grad) {
+        if (ws != p->ws_last || !p->fwd_complete) return TM_ESTATE;
+        if (p->K > 0 && p->d.n_src > 0 && f == nullptr) return TM_EINVAL;
+    }
+    hipStream_t st = as_stream(stream);
+    v = upload_tables(p, ws, st);
+    if (v != TM_OK) return v;
+    v = zero(wsp<float>(ws, p->lay.adj), p->lay.adj_bytes, st);
+    if (v != TM_OK) return v;
+    const uint64_t gbytes = (uint64_t)p->d.n_shots * (uint64_t)p->g.slab * 4;
+    if (grad_ca_shot && (v = zero(grad_ca_shot, gbytes, st)) != TM_OK) return v;
+    if (grad_cb_shot && (v = zero(grad_cb_shot, gbytes, st)) != TM_OK) return v;
+    switch (p->P) {
+    case 1: v = run_adjoint<1>(p, ws, ca, cb, cq, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
+    case 2: v = run_adjoint<2>(p, ws, ca, cb, cq, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
+    default: v = run_adjoint<4>(p, ws, ca, cb, cq, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
+    }
+    if (v != TM_OK) return v;
+    if (p->K > 0 && want_grad) p->fwd_next = -1;   // the replay overwrote the forward state
+    return TM_OK;
+}
+
+TM_API tm_status tm_grad(const tm_plan* p, const float* grad_ca_shot, const float* grad_cb_shot,
+                         float* grad_ca, float* grad_cb, void* stream)
+{
+    if (p == nullptr) return TM_EINVAL;
+    if ((grad_ca == nullptr) != (grad_ca_shot == nullptr)) return TM_EINVAL;
+    if ((grad_cb == nullptr) != (grad_cb_shot == nullptr)) return TM_EINVAL;
+    hipStream_t st = as_stream(stream);
+    const int64_t slab = p->g.slab;
+    const dim3 grid((unsigned)((slab + 255) / 256)), blk(256);
+    if (grad_ca) k_shot_sum<<<grid, blk, 0, st>>>(slab, (int)p->d.n_shots, grad_ca_shot, grad_ca);
+    if (grad_cb) k_shot_sum<<<grid, blk, 0, st>>>(slab, (int)p->d.n_shots, grad_cb_shot, grad_cb);
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
