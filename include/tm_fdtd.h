@@ -158,6 +158,28 @@ tm_status tm_adjoint(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca
 tm_status tm_grad(const tm_plan* plan, const float* grad_ca_shot, const float* grad_cb_shot,
                   float* grad_ca, float* grad_cb, void* stream);
 
+/*
+ * Kernel timing, a diagnostic for roofline figures.  With sampling on
+ * (every > 0), every ``every``-th time step of tm_forward and tm_adjoint
+ * brackets each of its stencil-kernel launches with a pair of HIP events
+ * recorded on the call's stream; every = 0 turns sampling off.  Nothing else
+ * changes: the same kernels run in the same order.
+ */
+tm_status tm_timing_enable(tm_plan* plan, int32_t every);
+
+/*
+ * Per-kernel sums of the sampled durations (milliseconds) and sample counts
+ * since the previous read, for kernels 0 .. tm_kernel_count()-1, into
+ * caller arrays of tm_kernel_count() entries; then clears them.  Waits for
+ * the recorded events (host-blocking).
+ */
+tm_status tm_timing_read(tm_plan* plan, double* total_ms, int64_t* count);
+
+/* Number of timed kernels, and the name of kernel ``k`` (the prefix of its
+ * symbol name as profilers print it; NULL when k is out of range). */
+int32_t tm_kernel_count(void);
+const char* tm_kernel_name(int32_t k);
+
 /* Static description of a status code. */
 const char* tm_status_string(tm_status status);
 

@@ -66,18 +66,23 @@ def test_config1_full_size(orc):
     assert rel_l2(d_gpu, d_orc) <= REC_TOL
     _, ref = check(orc, wl, observed_orc=d_orc, label="config1")
     # End to end, with the residual r - d formed from the GPU's own records of
-    # both models.  The subtraction cancels most of the records, so its error
-    # is the records' error times |r| / |r - d|; the gradients (linear in the
-    # residual) may carry that error but no more.
+    # both models.  The subtraction cancels most of the records, so the
+    # residual's error is the records' error times |r| / |r - d|.  The adjoint
+    # is then checked against the oracle's adjoint of that same float32
+    # residual (the map from residual to gradients is linear and fixed by the
+    # forward snapshots), so no conditioning enters the gradient comparison.
     e2e = run_gpu(wl, observed=d_gpu, snap="f32")
     e_res = rel_l2(e2e["residual"], ref["residual"])
     cond = np.linalg.norm(ref["records"]) / np.linalg.norm(ref["residual"])
+    _, _, snaps = orc.forward(wl, store=True)
+    gf2, gca2, gcb2 = orc.adjoint(wl, e2e["residual"].astype(np.float64), snaps)
+    errs = dict(gca=rel_l2(e2e["gca"], orc.shot_sum(gca2)), gcb=rel_l2(e2e["gcb"], orc.shot_sum(gcb2)),
+                grad_f=rel_l2(e2e["grad_f"], gf2))
     print(f"[config1 end-to-end] residual {e_res:.2e} (|r|/|r-d| = {cond:.0f})  "
-          f"gCa {rel_l2(e2e['gca'], ref['gca']):.2e}  gCb {rel_l2(e2e['gcb'], ref['gcb']):.2e}  "
-          f"grad_f {rel_l2(e2e['grad_f'], ref['grad_f']):.2e}", flush=True)
+          + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     assert e_res <= 2 * REC_TOL * cond
-    for key in ("gca", "gcb", "grad_f"):
-        assert rel_l2(e2e[key], ref[key]) <= GRAD_TOL["f32"] + 2 * e_res, key
+    for key, v in errs.items():
+        assert v <= GRAD_TOL["f32"], key
 
 
 @pytest.mark.parametrize("cfg,over", [

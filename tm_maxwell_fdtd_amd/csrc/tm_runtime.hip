@@ -98,6 +98,15 @@ struct Layout {
 
 }  // namespace
 
+// Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
+enum KernelId { KID_FWD_H = 0, KID_FWD_E, KID_ADJ_BAND, KID_ADJ_H, KID_ADJ_E, KID_COUNT };
+const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_h", "k_fwd_e", "k_adj_band", "k_adj_h", "k_adj_e"};
+
+struct TimedLaunch {
+    int kid;
+    hipEvent_t a, b;
+};
+
 struct tm_plan {
     tm_desc d{};
     int P = 0;
@@ -116,6 +125,12 @@ struct tm_plan {
     int64_t fwd_next = -1;
     bool stored_ok = false;
     bool fwd_complete = false;
+    // sampled kernel timing
+    int timing_every = 0;
+    std::vector<hipEvent_t> ev_free;
+    std::vector<TimedLaunch> ev_used;
+    double t_ms[KID_COUNT] = {};
+    int64_t t_n[KID_COUNT] = {};
 };
 
 namespace {
@@ -183,6 +198,40 @@ T* wsp(void* ws, uint64_t off) { return reinterpret_cast<T*>(static_cast<char*>(
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+hipEvent_t take_event(tm_plan* p)
+{
+    if (!p->ev_free.empty()) {
+        hipEvent_t e = p->ev_free.back();
+        p->ev_free.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch ``body`` (one kernel launch on ``st``), bracketed by a pair of
+// events when this time step is sampled.
+template <typename F>
+void timed(tm_plan* p, int kid, int64_t t, hipStream_t st, F&& body)
+{
+    if (p->timing_every <= 0 || t % p->timing_every != 0) {
+        body();
+        return;
+    }
+    hipEvent_t a = take_event(p), b = take_event(p);
+    if (a == nullptr || b == nullptr) {
+        if (a) p->ev_free.push_back(a);
+        if (b) p->ev_free.push_back(b);
+        body();
+        return;
+    }
+    (void)hipEventRecord(a, st);
+    body();
+    (void)hipEventRecord(b, st);
+    p->ev_used.push_back(TimedLaunch{kid, a, b});
+}
+
 tm_status zero(float* ptr, uint64_t bytes, hipStream_t st)
 {
     const int64_t n = (int64_t)(bytes / 4);
@@ -247,18 +296,22 @@ dim3 stencil_grid(const Geo& g, int64_t S)
 
 // One forward step t.  snap: SNAP_* kind for the E pass, with destinations.
 template <int P>
-void fwd_step(const tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
+void fwd_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
               const float* f, float* r, int64_t t, int snap, void* se, void* sc, hipStream_t st)
 {
     const Geo& g = p->g;
     const dim3 grid = stencil_grid(g, p->d.n_shots), blk(BLK_X, BLK_Y);
-    k_fwd_h<P><<<grid, blk, 0, st>>>(g, cq, q.E, q.Hx, q.Hz, q.psi_ez, q.psi_ex, q.cp);
-    if (snap == SNAP_F32)
-        k_fwd_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
-    else if (snap == SNAP_BF16)
-        k_fwd_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
-    else
-        k_fwd_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, nullptr, nullptr);
+    timed(p, KID_FWD_H, t, st, [&] {
+        k_fwd_h<P><<<grid, blk, 0, st>>>(g, cq, q.E, q.Hx, q.Hz, q.psi_ez, q.psi_ex, q.cp);
+    });
+    timed(p, KID_FWD_E, t, st, [&] {
+        if (snap == SNAP_F32)
+            k_fwd_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
+        else if (snap == SNAP_BF16)
+            k_fwd_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
+        else
+            k_fwd_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, nullptr, nullptr);
+    });
     const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
     if (ns > 0 || (r != nullptr && nr > 0)) {
         const int64_t S = p->d.n_shots;
@@ -269,7 +322,7 @@ void fwd_step(const tm_plan* p, const Ptrs& q, const float* ca, const float* cb,
 }
 
 template <int P>
-void adj_step(const tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
+void adj_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
               const float* grad_r, float* grad_f, int64_t t, int snap, const void* se,
               const void* sc, float* gca, float* gcb, hipStream_t st)
 {
@@ -283,17 +336,23 @@ void adj_step(const tm_plan* p, const Ptrs& q, const float* ca, const float* cb,
     }
     const int64_t band_cells = (int64_t)g.by * g.nx + (int64_t)(g.ny - g.by) * g.bx;
     if (band_cells > 0)
-        k_adj_band<P><<<dim3((unsigned)((band_cells + 255) / 256), (unsigned)S), dim3(256), 0, st>>>(
-            g, cb, q.lE, q.phi_hzx, q.phi_hxz, q.Ub, q.Wb, q.cp);
+        timed(p, KID_ADJ_BAND, t, st, [&] {
+            k_adj_band<P><<<dim3((unsigned)((band_cells + 255) / 256), (unsigned)S), dim3(256), 0, st>>>(
+                g, cb, q.lE, q.phi_hzx, q.phi_hxz, q.Ub, q.Wb, q.cp);
+        });
     const dim3 grid = stencil_grid(g, S), blk(BLK_X, BLK_Y);
-    k_adj_h<P><<<grid, blk, 0, st>>>(g, cb, cq, q.lE, q.lHx, q.lHz, q.phi_ez, q.phi_ex, q.Ub, q.Wb,
-                                     q.TZb, q.TXb, q.cp);
-    if (snap == SNAP_F32)
-        k_adj_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
-    else if (snap == SNAP_BF16)
-        k_adj_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
-    else
-        k_adj_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, nullptr, nullptr, nullptr, nullptr);
+    timed(p, KID_ADJ_H, t, st, [&] {
+        k_adj_h<P><<<grid, blk, 0, st>>>(g, cb, cq, q.lE, q.lHx, q.lHz, q.phi_ez, q.phi_ex, q.Ub, q.Wb,
+                                         q.TZb, q.TXb, q.cp);
+    });
+    timed(p, KID_ADJ_E, t, st, [&] {
+        if (snap == SNAP_F32)
+            k_adj_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
+        else if (snap == SNAP_BF16)
+            k_adj_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
+        else
+            k_adj_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, nullptr, nullptr, nullptr, nullptr);
+    });
 }
 
 int snap_kind(const tm_plan* p) { return p->d.snap == TM_SNAP_BF16 ? SNAP_BF16 : SNAP_F32; }
@@ -483,7 +542,52 @@ TM_API void tm_plan_destroy(tm_plan* p)
 {
     if (p == nullptr) return;
     if (p->pinned != nullptr) (void)hipHostFree(p->pinned);
+    for (const TimedLaunch& r : p->ev_used) {
+        (void)hipEventSynchronize(r.b);
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (hipEvent_t e : p->ev_free) (void)hipEventDestroy(e);
     delete p;
+}
+
+TM_API tm_status tm_timing_enable(tm_plan* p, int32_t every)
+{
+    if (p == nullptr || every < 0) return TM_EINVAL;
+    p->timing_every = every;
+    return TM_OK;
+}
+
+TM_API tm_status tm_timing_read(tm_plan* p, double* total_ms, int64_t* count)
+{
+    if (p == nullptr || total_ms == nullptr || count == nullptr) return TM_EINVAL;
+    tm_status rc = TM_OK;
+    for (const TimedLaunch& r : p->ev_used) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+            rc = TM_EHIP;
+        } else {
+            p->t_ms[r.kid] += ms;
+            p->t_n[r.kid] += 1;
+        }
+        p->ev_free.push_back(r.a);
+        p->ev_free.push_back(r.b);
+    }
+    p->ev_used.clear();
+    for (int k = 0; k < KID_COUNT; ++k) {
+        total_ms[k] = p->t_ms[k];
+        count[k] = p->t_n[k];
+        p->t_ms[k] = 0.0;
+        p->t_n[k] = 0;
+    }
+    return rc;
+}
+
+TM_API int32_t tm_kernel_count(void) { return KID_COUNT; }
+
+TM_API const char* tm_kernel_name(int32_t k)
+{
+    return (k >= 0 && k < KID_COUNT) ? KERNEL_NAMES[k] : nullptr;
 }
 
 TM_API tm_status tm_workspace_bytes(const tm_plan* p, uint64_t* bytes)

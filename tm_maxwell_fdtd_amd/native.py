@@ -77,6 +77,14 @@ def lib():
         L.tm_adjoint.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.tm_grad.restype = ctypes.c_int
         L.tm_grad.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+        L.tm_timing_enable.restype = ctypes.c_int
+        L.tm_timing_enable.argtypes = [_vp, ctypes.c_int32]
+        L.tm_timing_read.restype = ctypes.c_int
+        L.tm_timing_read.argtypes = [_vp, _vp, _vp]
+        L.tm_kernel_count.restype = ctypes.c_int32
+        L.tm_kernel_count.argtypes = []
+        L.tm_kernel_name.restype = ctypes.c_char_p
+        L.tm_kernel_name.argtypes = [ctypes.c_int32]
         _lib = L
     return _lib
 
@@ -159,6 +167,28 @@ def tm_grad(plan, grad_ca_shot, grad_cb_shot, grad_ca, grad_cb, stream):
 
 def tm_status_string(status: int) -> str:
     return status_string(status)
+
+
+def tm_timing_enable(plan, every: int):
+    return lib().tm_timing_enable(plan, int(every))
+
+
+def tm_kernel_count() -> int:
+    return int(lib().tm_kernel_count())
+
+
+def tm_kernel_name(k: int) -> Optional[str]:
+    n = lib().tm_kernel_name(int(k))
+    return None if n is None else n.decode()
+
+
+def tm_timing_read(plan):
+    """Returns (status, {kernel name: (total ms, samples)})."""
+    n = tm_kernel_count()
+    ms = np.zeros(n, dtype=np.float64)
+    cnt = np.zeros(n, dtype=np.int64)
+    st = lib().tm_timing_read(plan, ms.ctypes.data, cnt.ctypes.data)
+    return st, {tm_kernel_name(k): (float(ms[k]), int(cnt[k])) for k in range(n)}
 
 
 # ---- convenience layer (still marshalling only) -----------------------------
