@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Throughput of the TM FDTD hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of shots: tm_forward
+with storage (stencil steps, source injection, receiver gather, snapshot
+epilogue), tm_adjoint (residual injection, exact adjoint steps, gradient
+accumulation; segment replay in checkpoint mode) and tm_grad (shot sum), on
+the order-8 workload: 1024x1024 interior + 32-cell CPML per side, 16 shots,
+2000 time steps, bfloat16 snapshots.  The misfit is J = 1/2 |r|^2, so the
+adjoint source is the records themselves.
+
+value = cell-updates / time of one step (Gcell-updates/s), where
+cell-updates = shots x (interior + CPML cells) x time steps.  The forward
+pass alone (no storage) is timed as well and reported as ``fwd_value``.
+
+The ``roofline`` object is for the dominant stencil kernel: algorithmic
+bytes per launch over its average launch duration, sampled with HIP events
+inside the library on the stream the kernels run on (tm_timing_*).  HBM
+traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in
+``profiles/`` and is used only while the kernel source is unchanged.
+
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload (one shot, a few dozen time steps) on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Gcell-updates/s fwd and fwd+adjoint (8th order) + % of HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+WORKLOADS = {
+    3: "order-8 TM FDTD, 1024x1024 interior + 32-cell CPML (1096x1096 padded), 16 shots, "
+       "2000 steps, 256 receivers/shot, 600 MHz Ricker, bf16 snapshots, fwd(store)+adjoint+shot-sum",
+    2: "order-4 TM FDTD, 256x256 interior + 20-cell CPML, 4 shots, 1000 steps, fp32 snapshots",
+    5: "order-4 TM FDTD, 384x384 interior + 20-cell CPML, 128 shots, 800 steps, fp32 snapshots",
+    4: "order-8 TM FDTD, 4096x4096 interior + 40-cell CPML, 8 shots, 4000 steps, fp32, "
+       "checkpoint every 64 steps + segment replay",
+    1: "order-2 TM FDTD, 64x64 interior + 10-cell CPML, 1 shot, 300 steps, fp32 snapshots",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes per launch of each stencil kernel.  Per cell of the
+# launch: every field and coefficient the update reads once, every field it
+# writes once, the CPML memory read-modify-write on band cells, the snapshot
+# writes / reads and the gradient read-modify-write on interior cells.
+# ---------------------------------------------------------------------------
+
+def _counts(wl):
+    p = wl.order // 2
+    cells = (wl.ny - 2 * p) * (wl.nx - 2 * p)                  # per shot
+    nyi, nxi = wl.pml_y1 - wl.pml_y0, wl.pml_x1 - wl.pml_x0
+    interior = nyi * nxi
+    ny_e, nx_e = wl.ny - 2 * p, wl.nx - 2 * p
+    yband_rows = ny_e - (nyi - 1)                               # H flag: outside [y0, y1-1)
+    xband_cols = nx_e - (nxi - 1)
+    band_y = yband_rows * nx_e                                  # cells in y bands
+    band_x = xband_cols * ny_e
+    return cells, interior, band_y, band_x
+
+
+def kernel_bytes(name, wl, store, snap_bytes):
+    """Algorithmic HBM bytes of one launch of kernel ``name`` (all shots)."""
+    cells, interior, band_y, band_x = _counts(wl)
+    S = wl.n_shots
+    if name == "k_fwd_h":        # read E, Hx, Hz, Cq; write Hx, Hz; psi RMW on bands
+        per = 4 * 4 + 2 * 4
+        return S * (per * cells + 8 * (band_y + band_x))
+    if name == "k_fwd_e":        # read Hx, Hz, E, Ca, Cb; write E; psi RMW; snapshots
+        per = 5 * 4 + 4
+        snaps = 2 * snap_bytes * interior if store else 0
+        return S * (per * cells + 8 * (band_y + band_x) + snaps)
+    if name == "k_adj_band":     # band E cells: read Cb, lambda; phi RMW; write filtered
+        return S * (band_y + band_x) * (8 + 8 + 4)
+    if name == "k_adj_h":        # read lE, Cb, lHx, lHz, Cq; write lHx, lHz; band terms
+        per = 5 * 4 + 2 * 4
+        return S * (per * cells + 16 * (band_y + band_x))
+    if name == "k_adj_e":        # read lE, Ca, Cq, lHx, lHz; write lE; snapshots; grad RMW
+        per = 5 * 4 + 4
+        return S * (per * cells + 4 * (band_y + band_x) + (2 * snap_bytes + 16) * interior)
+    return None
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tm_maxwell_fdtd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode())
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, cfg):
+    """Measured HBM bytes per launch, if recorded for the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_config{cfg}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_src_sha") != kernel_source_sha():
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, steps, min_seconds=10.0, max_runs=8):
+    """fp64 oracle on one shot of the workload for ``steps`` time steps.
+
+    The sample (forward with storage, then the exact adjoint) is repeated
+    until at least ``min_seconds`` of CPU work has been timed; the rate is
+    total cell-updates over total time.
+    """
+    import dataclasses
+
+    import oracle
+
+    one = dataclasses.replace(wl, n_shots=1, nt=steps, src=wl.src[:1].copy(), rec=wl.rec[:1].copy(),
+                              f=wl.f[:steps, :1].copy())
+    p = wl.order // 2
+    cells = (wl.ny - 2 * p) * (wl.nx - 2 * p) * steps
+    total, runs = 0.0, 0
+    while runs < max_runs and (runs == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        r, _, snaps = oracle.forward(one, store=True)
+        oracle.adjoint(one, r, snaps)
+        total += time.perf_counter() - t0
+        runs += 1
+        del r, snaps
+    return {"value": cells * runs / total / 1e9, "unit": "Gcell-updates/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"1 of {wl.n_shots} shots, {steps} of {wl.nt} time steps, same grid and model; "
+                      f"forward with storage + exact adjoint in fp64, {runs} run(s), {total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
+    ap.add_argument("--timing-every", type=int, default=8,
+                    help="sample every k-th time step's stencil kernels with HIP events")
+    ap.add_argument("--cpu-steps", type=int, default=200, help="time steps of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(shots would be sharded across GPUs with one gradient all-reduce; not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tm_maxwell_fdtd_amd import inputs, native
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    native.lib()                 # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"building workload config{args.config}")
+    wl = inputs.as_f32(inputs.make_config(args.config))
+    prop = native.Propagator(wl, device=dev)
+    log(f"workspace {prop.ws_bytes / 2**30:.1f} GiB, grid {wl.ny}x{wl.nx}, S={wl.n_shots}, nt={wl.nt}")
+    S, ny, nx = wl.n_shots, wl.ny, wl.nx
+    f32 = dict(dtype=torch.float32, device=dev)
+    r = torch.zeros((wl.nt, S, wl.n_rec), **f32)
+    grad_f = torch.empty((wl.nt, S, wl.n_src), **f32)
+    gca_s = torch.empty((S, ny, nx), **f32)
+    gcb_s = torch.empty((S, ny, nx), **f32)
+    gca = torch.empty((ny, nx), **f32)
+    gcb = torch.empty((ny, nx), **f32)
+    P = native.ptr
+    ws, wsb = P(prop.ws), prop.ws_bytes
+    ca, cb, cq, f = P(prop.ca), P(prop.cb), P(prop.cq), P(prop.f)
+    courant = prop.courant()
+    log(f"Courant number {courant:.4f}")
+
+    def stream():
+        return native.stream_handle()
+
+    def step():
+        st = native.tm_forward(prop.plan, ws, wsb, ca, cb, cq, f, P(r), 0, wl.nt, native.TM_FWD_STORE, stream())
+        assert st == 0, native.status_string(st)
+        # J = 1/2 |r|^2: dJ/dr = r
+        st = native.tm_adjoint(prop.plan, ws, wsb, ca, cb, cq, f, P(r), P(grad_f), P(gca_s), P(gcb_s), stream())
+        assert st == 0, native.status_string(st)
+        st = native.tm_grad(prop.plan, P(gca_s), P(gcb_s), P(gca), P(gcb), stream())
+        assert st == 0, native.status_string(st)
+
+    def fwd_only():
+        st = native.tm_forward(prop.plan, ws, wsb, ca, cb, cq, f, P(r), 0, wl.nt, 0, stream())
+        assert st == 0, native.status_string(st)
+
+    cell_updates = wl.cell_updates()
+
+    def timed(fn, k, w, label):
+        for i in range(w):
+            fn()
+            torch.cuda.synchronize()
+            log(f"{label} warmup {i + 1}/{w} done")
+        native.tm_timing_read(prop.plan)                      # discard warmup samples
+        native.tm_timing_enable(prop.plan, args.timing_every)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        native.tm_timing_enable(prop.plan, 0)
+        st, kt = native.tm_timing_read(prop.plan)
+        assert st == 0
+        ev_ms = e0.elapsed_time(e1)
+        log(f"{label}: {k} steps, wall {wall:.3f} s, events {ev_ms / 1e3:.3f} s")
+        return wall, ev_ms / 1e3, kt
+
+    results = {}
+    if not args.no_fwd:
+        wall, ev, kt = timed(fwd_only, args.steps, args.warmup, "forward")
+        results["fwd"] = (max(wall, ev), kt)
+    wall, ev, kt = timed(step, args.steps, args.warmup, "fwd+adj")
+    results["step"] = (max(wall, ev), kt)
+    ok = bool(torch.isfinite(gca).all() and torch.isfinite(gcb).all() and torch.isfinite(r).all())
+    if not ok:
+        log("non-finite values in the outputs")
+
+    t_step = results["step"][0] / args.steps
+    value = cell_updates / t_step / 1e9
+    fwd_value = cell_updates / (results["fwd"][0] / args.steps) / 1e9 if "fwd" in results else None
+
+    # roofline of the dominant kernel of the full step
+    snap_bytes = 2 if wl.snap == "bf16" else 4
+    p = wl.order // 2
+    launches_fwd = wl.nt
+    kernels = {}
+    for name, (ms, n) in results["step"][1].items():
+        if n == 0:
+            continue
+        avg_ms = ms / n
+        launches = 2 * wl.nt if name.startswith("k_fwd") and wl.ckpt_every else wl.nt
+        # the forward kernels run with storage in this step
+        nbytes = kernel_bytes(name, wl, store=name.startswith("k_fwd"), snap_bytes=snap_bytes)
+        kernels[name] = dict(avg_us=avg_ms * 1e3, samples=n, est_total_s=avg_ms * launches / 1e3,
+                             alg_bytes=nbytes, gbs=nbytes / (avg_ms * 1e-3) / 1e9)
+    dom = max(kernels, key=lambda k: kernels[k]["est_total_s"])
+    kd = kernels[dom]
+    traffic = load_traffic(dom, args.config)
+    roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                "avg_launch_us": round(kd["avg_us"], 2), "alg_bytes_per_launch": kd["alg_bytes"]}
+    for name, k in sorted(kernels.items()):
+        log(f"  {name:12s} avg {k['avg_us']:9.2f} us  ({k['samples']} samples)  "
+            f"alg {k['alg_bytes'] / 1e6:8.1f} MB  -> {k['gbs']:7.1f} GB/s  est {k['est_total_s']:.3f} s/step")
+    fwd_kern = {}
+    if "fwd" in results:
+        for name, (ms, n) in results["fwd"][1].items():
+            if n:
+                nb = kernel_bytes(name, wl, store=False, snap_bytes=snap_bytes)
+                fwd_kern[name] = dict(avg_us=round(ms / n * 1e3, 2),
+                                      gbs=round(nb / (ms / n * 1e-3) / 1e9, 1))
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "Gcell-updates/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"config{args.config}: " + WORKLOADS[args.config],
+                   "grid": [wl.ny, wl.nx], "shots": wl.n_shots, "time_steps": wl.nt, "order": wl.order,
+                   "snapshots": wl.snap, "ckpt_every": wl.ckpt_every, "cell_updates": cell_updates},
+        "fwd_value": None if fwd_value is None else round(fwd_value, 3),
+        "fwd_kernels": fwd_kern,
+        "roofline": roofline,
+        "outputs_finite": ok,
+    }
+    prop.close()
+    del prop
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log(f"timing the fp64 oracle on {args.cpu_steps} steps of one shot")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

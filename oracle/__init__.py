@@ -69,6 +69,8 @@ def lib():
                                   _dp, _dp, _dp, _dp, _dp, _dp]
         L.orc_shot_sum.restype = None
         L.orc_shot_sum.argtypes = [_ll, _ll, _dp, _dp]
+        L.orc_num_threads.restype = ctypes.c_int
+        L.orc_num_threads.argtypes = []
         L.orc_coefficients.restype = ctypes.c_int
         L.orc_coefficients.argtypes = [ctypes.c_int, _dp]
         _lib = L
@@ -95,6 +97,11 @@ def geom(wl, periodic: bool = False) -> Geom:
     return Geom(order=wl.order, periodic=int(periodic), n_shots=wl.n_shots, ny=wl.ny, nx=wl.nx,
                 pml_y0=wl.pml_y0, pml_y1=wl.pml_y1, pml_x0=wl.pml_x0, pml_x1=wl.pml_x1,
                 rdy=1.0 / wl.dy, rdx=1.0 / wl.dx, n_src=wl.n_src, n_rec=wl.n_rec)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
 
 
 def coefficients(order: int) -> np.ndarray:

@@ -74,6 +74,14 @@ static int coefs(int order, double *c)
 
 int orc_coefficients(int order, double *c) { return coefs(order, c); }
 
+/* Threads an OpenMP parallel region of the oracle uses (1 without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif
+
 /* ---- geometry helpers ---------------------------------------------------- */
 
 typedef struct {
