@@ -74,24 +74,25 @@ def _counts(wl):
 
 
 def kernel_bytes(name, wl, store, snap_bytes):
-    """Algorithmic HBM bytes of one launch of kernel ``name`` (all shots)."""
+    """Algorithmic HBM bytes of one launch of kernel ``name`` (all shots).
+
+    k_fwd_step: read E, Hx, Hz, Ca, Cb, Cq and write E, Hx, Hz (36 B per
+    cell); read-modify-write of one H-update and one E-update CPML memory
+    per band axis (16 B per band cell and axis); with storage, Ey^n and
+    curl H^n of every interior cell (2 x 4 B, or 2 x 2 B in bf16).
+    k_adj_step: the same 36 B for the adjoint fields and coefficients, the
+    same 16 B per band cell and axis for the four adjoint memories, and on
+    interior cells the two snapshot reads plus the read-modify-write of the
+    two per-shot gradients (16 B).
+    """
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
-    if name == "k_fwd_h":        # read E, Hx, Hz, Cq; write Hx, Hz; psi RMW on bands
-        per = 4 * 4 + 2 * 4
-        return S * (per * cells + 8 * (band_y + band_x))
-    if name == "k_fwd_e":        # read Hx, Hz, E, Ca, Cb; write E; psi RMW; snapshots
-        per = 5 * 4 + 4
+    if name == "k_fwd_step":
         snaps = 2 * snap_bytes * interior if store else 0
-        return S * (per * cells + 8 * (band_y + band_x) + snaps)
-    if name == "k_adj_band":     # band E cells: read Cb, lambda; phi RMW; write filtered
-        return S * (band_y + band_x) * (8 + 8 + 4)
-    if name == "k_adj_h":        # read lE, Cb, lHx, lHz, Cq; write lHx, lHz; band terms
-        per = 5 * 4 + 2 * 4
-        return S * (per * cells + 16 * (band_y + band_x))
-    if name == "k_adj_e":        # read lE, Ca, Cq, lHx, lHz; write lE; snapshots; grad RMW
-        per = 5 * 4 + 4
-        return S * (per * cells + 4 * (band_y + band_x) + (2 * snap_bytes + 16) * interior)
+        return S * (36 * cells + 16 * (band_y + band_x) + snaps)
+    if name == "k_adj_step":
+        grads = (2 * snap_bytes + 16) * interior if store else 0
+        return S * (36 * cells + 16 * (band_y + band_x) + grads)
     return None
 
 
@@ -263,8 +264,8 @@ def main():
             continue
         avg_ms = ms / n
         launches = 2 * wl.nt if name.startswith("k_fwd") and wl.ckpt_every else wl.nt
-        # the forward kernels run with storage in this step
-        nbytes = kernel_bytes(name, wl, store=name.startswith("k_fwd"), snap_bytes=snap_bytes)
+        # in a full step the forward stores snapshots and the adjoint accumulates gradients
+        nbytes = kernel_bytes(name, wl, store=True, snap_bytes=snap_bytes)
         kernels[name] = dict(avg_us=avg_ms * 1e3, samples=n, est_total_s=avg_ms * launches / 1e3,
                              alg_bytes=nbytes, gbs=nbytes / (avg_ms * 1e-3) / 1e9)
     dom = max(kernels, key=lambda k: kernels[k]["est_total_s"])

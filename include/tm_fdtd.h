@@ -68,7 +68,7 @@ typedef struct tm_desc {
     int32_t order;          /* spatial order: 2, 4 or 8                         */
     int32_t snap;           /* tm_snap                                          */
     int64_t n_shots;        /* shots S sharing one model                        */
-    int64_t ny, nx;         /* padded grid; ny * nx < 2^31                      */
+    int64_t ny, nx;         /* padded grid; ny * nx < 2^29                      */
     int64_t pml_y0, pml_y1; /* interior window rows [pml_y0, pml_y1)            */
     int64_t pml_x0, pml_x1; /* interior window columns [pml_x0, pml_x1)         */
     double dy, dx;          /* grid spacing in metres (kernels use 1/dy, 1/dx)  */
@@ -92,7 +92,7 @@ typedef struct tm_plan tm_plan;
  *         "no source/receiver"; any other index must be an Ey cell.  Several
  *         sources (receivers) of one shot may share a cell: they add up.
  * Returns TM_EINVAL on an inconsistent descriptor (order not in {2,4,8},
- * grid too small, window outside [P, n-P], empty window, ny*nx >= 2^31,
+ * grid too small, window outside [P, n-P], empty window, ny*nx >= 2^29,
  * bad indices, ckpt_every < 0), TM_ENOMEM when the workspace would exceed
  * hbm_budget.  The plan copies everything it needs.
  */

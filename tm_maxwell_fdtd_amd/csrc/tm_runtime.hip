@@ -1,21 +1,31 @@
 // Host runtime and C ABI of the TM FDTD propagator (see include/tm_fdtd.h).
 //
 // The plan validates a problem on the host, builds conflict-free scatter
-// tables for the sources and receivers, and lays out the caller-allocated
-// workspace.  tm_forward / tm_adjoint / tm_grad enqueue kernels on the
-// caller's stream; there is no global state, so plans are independent.
+// tables for the sources and receivers, chooses the tiling of the step
+// kernels and lays out the caller-allocated workspace.  tm_forward /
+// tm_adjoint / tm_grad enqueue kernels on the caller's stream; there is no
+// global state, so plans are independent.
 //
-// Host loop structure follows the launchers of tide-GPR 0.0.9
-// tide/csrc/maxwell.cu: forward = H pass, E pass (storing variant on stored
-// steps), sources, receivers; backward (reverse time) = residual injection
-// at receivers, adjoint read at sources, lambda_H pass, lambda_E pass with
-// gradient accumulation; then combine_grad.  Checkpoint mode stores the
-// full state (fields and band CPML memories) every K steps and replays each
-// segment into a K-step snapshot buffer inside tm_adjoint.
+// Host loop structure follows the launchers of tide-GPR 0.0.9,
+// maxwell.cu (forward, forward_with_storage, backward): per forward step
+// the H and E updates (one fused kernel here, with the snapshot epilogue on
+// stored steps), then sources, then receivers; per adjoint step (reverse
+// time) the residual injection at the receivers, the adjoint read at the
+// sources, then the transposed H and E updates with gradient accumulation
+// (one fused kernel); then combine_grad.  Checkpoint mode stores the state
+// (fields and band CPML memories) every K steps and replays each segment
+// into a K-step snapshot buffer inside tm_adjoint.
+//
+// State double buffering: the forward state at time t lives in set t % 2;
+// a step reads one set and writes the other.  The E-update CPML memories,
+// which only their owner thread touches, live between the two sets, so
+// "set 0 + in-place memories" and "in-place memories + set 1" are each one
+// contiguous range (a checkpoint is one copy).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <utility>
@@ -23,6 +33,7 @@
 
 #include "tm_fdtd.h"
 #include "tm_kernels.hpp"
+#include "tm_step.hpp"
 
 using namespace tmf;
 
@@ -86,11 +97,15 @@ Scatter build_scatter(const int64_t* ids, int64_t S, int64_t n)
 
 struct Layout {
     uint64_t cpml = 0, tables = 0, scratch = 0;
-    uint64_t fwd = 0, fwd_bytes = 0;       // E, Hx, Hz, psi_ez, psi_ex, psi_hxz, psi_hzx
-    uint64_t E = 0, Hx = 0, Hz = 0, psi_ez = 0, psi_ex = 0, psi_hxz = 0, psi_hzx = 0;
-    uint64_t adj = 0, adj_bytes = 0;       // lambdas, adjoint memories, band temporaries
-    uint64_t lE = 0, lHx = 0, lHz = 0, phi_ez = 0, phi_ex = 0, phi_hxz = 0, phi_hzx = 0;
-    uint64_t Ub = 0, Wb = 0, TZb = 0, TXb = 0;
+    // forward state: [set 0][in-place memories][set 1]
+    uint64_t fwd = 0, fwd_bytes = 0;
+    uint64_t fset[2] = {0, 0}, set_bytes = 0;
+    uint64_t inplace = 0, inplace_bytes = 0;
+    uint64_t oE = 0, oHx = 0, oHz = 0, opez = 0, opex = 0;   // within a set
+    uint64_t ophxz = 0, ophzx = 0;                           // within the in-place block
+    // adjoint state: [set 0][set 1]
+    uint64_t adj = 0, adj_bytes = 0, aset[2] = {0, 0}, aset_bytes = 0;
+    uint64_t olE = 0, olHx = 0, olHz = 0, ofhzx = 0, ofhxz = 0, ofex = 0, ofez = 0;
     uint64_t snapE = 0, snapC = 0, snap_step = 0;   // per-step bytes of one snapshot array
     uint64_t ckpt = 0, ckpt_slot = 0;
     uint64_t total = 0;
@@ -99,8 +114,8 @@ struct Layout {
 }  // namespace
 
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
-enum KernelId { KID_FWD_H = 0, KID_FWD_E, KID_ADJ_BAND, KID_ADJ_H, KID_ADJ_E, KID_COUNT };
-const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_h", "k_fwd_e", "k_adj_band", "k_adj_h", "k_adj_e"};
+enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_COUNT };
+const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step"};
 
 struct TimedLaunch {
     int kid;
@@ -111,6 +126,8 @@ struct tm_plan {
     tm_desc d{};
     int P = 0;
     Geo g{};
+    Tiling tiling_fwd{}, tiling_adj{};   // per device, made at the first device call
+    int tiling_device = -1;
     std::vector<float> cpml;       // [12][L]
     std::vector<int32_t> tables;   // scatter tables, packed
     uint64_t t_s_cell = 0, t_s_ptr = 0, t_s_list = 0, t_s_idx = 0;
@@ -161,31 +178,73 @@ void make_layout(tm_plan* p)
     const Geo& g = p->g;
     Layout& L = p->lay;
     const uint64_t S = (uint64_t)d.n_shots, slab = (uint64_t)g.slab;
-    const uint64_t fld = S * slab * 4;
-    const uint64_t yb = S * (uint64_t)g.by * (uint64_t)g.nx * 4;
-    const uint64_t xb = S * (uint64_t)g.ny * (uint64_t)g.bx * 4;
+    const uint64_t fld = align_up(S * slab * 4);
+    const uint64_t yb = align_up(S * (uint64_t)g.by * (uint64_t)g.nx * 4);
+    const uint64_t xb = align_up(S * (uint64_t)g.ny * (uint64_t)g.bx * 4);
     uint64_t o = 0;
     auto take = [&](uint64_t bytes) { uint64_t at = o; o = align_up(o + bytes); return at; };
     L.cpml = take(12 * (uint64_t)g.L * 4);
     L.tables = take(p->tables.size() * 4);
     L.scratch = take(4096);
+    // one forward set: E, Hx, Hz, Hx-update y memory, Hz-update x memory
+    L.oE = 0; L.oHx = fld; L.oHz = 2 * fld; L.opez = 3 * fld; L.opex = 3 * fld + yb;
+    L.set_bytes = 3 * fld + yb + xb;
+    L.ophxz = 0; L.ophzx = yb;
+    L.inplace_bytes = yb + xb;
     L.fwd = o;
-    L.E = take(fld); L.Hx = take(fld); L.Hz = take(fld);
-    L.psi_ez = take(yb); L.psi_ex = take(xb); L.psi_hxz = take(yb); L.psi_hzx = take(xb);
+    L.fset[0] = take(L.set_bytes);
+    L.inplace = take(L.inplace_bytes);
+    L.fset[1] = take(L.set_bytes);
     L.fwd_bytes = o - L.fwd;
+    // one adjoint set: lambdas and the four adjoint CPML memories
+    L.olE = 0; L.olHx = fld; L.olHz = 2 * fld;
+    L.ofhzx = 3 * fld; L.ofhxz = 3 * fld + xb; L.ofex = 3 * fld + xb + yb; L.ofez = 3 * fld + 2 * xb + yb;
+    L.aset_bytes = 3 * fld + 2 * xb + 2 * yb;
     L.adj = o;
-    L.lE = take(fld); L.lHx = take(fld); L.lHz = take(fld);
-    L.phi_ez = take(yb); L.phi_ex = take(xb); L.phi_hxz = take(yb); L.phi_hzx = take(xb);
-    L.Ub = take(xb); L.Wb = take(yb); L.TZb = take(xb); L.TXb = take(yb);
+    L.aset[0] = take(L.aset_bytes);
+    L.aset[1] = take(L.aset_bytes);
     L.adj_bytes = o - L.adj;
     const uint64_t esz = d.snap == TM_SNAP_BF16 ? 2 : 4;
-    L.snap_step = S * (uint64_t)g.nyi * (uint64_t)g.nxi * esz;
-    L.snap_step = align_up(L.snap_step);
+    L.snap_step = align_up(S * (uint64_t)g.nyi * (uint64_t)g.nxi * esz);
     L.snapE = take(L.snap_step * (uint64_t)p->seg_steps);
     L.snapC = take(L.snap_step * (uint64_t)p->seg_steps);
-    L.ckpt_slot = align_up(L.fwd_bytes);
+    L.ckpt_slot = L.set_bytes + L.inplace_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
     L.total = o;
+}
+
+// Tiling of the step kernels over one device.  Strips are Strip<P>::W
+// columns wide; every (strip, shot) pair of the R = ny - 2P + 1 computed rows
+// is cut into m chunks so that the grid is just below a whole number of
+// "rounds" of the device's resident workgroups (cap), chunks stay between
+// 16 and CH_MAX rows, and no round runs half empty.  TM_FDTD_CHUNK_ROWS
+// (environment, read when the tiling is made) forces the chunk height, for
+// tuning.
+Tiling make_tiling(const tm_desc& d, int P, int64_t cap)
+{
+    Tiling t{};
+    const int W = NT - 4 * P + 2;
+    const int R = (int)d.ny - 2 * P + 1, nx_e = (int)d.nx - 2 * P + 1;
+    t.W = W;
+    t.nstrip = (nx_e + W - 1) / W;
+    const int64_t U = (int64_t)t.nstrip * d.n_shots;
+    const int64_t m_max = std::max<int64_t>(1, (R + 15) / 16);
+    int ch = R;
+    for (int64_t k = 1; k <= 1 << 20; ++k) {
+        const int64_t m = std::min<int64_t>(k * cap / U, m_max);
+        if (m < 1) continue;
+        ch = (int)((R + m - 1) / m);
+        if (ch <= CH_MAX) break;
+    }
+    ch = std::min(ch, CH_MAX);
+    if (const char* env = std::getenv("TM_FDTD_CHUNK_ROWS")) {
+        const int v = std::atoi(env);
+        if (v >= 1 && v <= CH_MAX) ch = v;
+    }
+    t.CH = ch;
+    t.nchunk = (R + ch - 1) / ch;
+    t.nblk = (int)(U * t.nchunk);
+    return t;
 }
 
 template <typename T>
@@ -257,9 +316,9 @@ tm_status upload_tables(tm_plan* p, void* ws, hipStream_t st)
     return TM_OK;
 }
 
+// Device pointers of one workspace.
 struct Ptrs {
-    float *E, *Hx, *Hz, *psi_ez, *psi_ex, *psi_hxz, *psi_hzx;
-    float *lE, *lHx, *lHz, *phi_ez, *phi_ex, *phi_hxz, *phi_hzx, *Ub, *Wb, *TZb, *TXb;
+    char* base;
     const float* cp;
     const int32_t *s_cell, *s_ptr, *s_list, *s_idx, *r_cell, *r_ptr, *r_list, *r_idx;
     char *snapE, *snapC, *ckpt;
@@ -270,14 +329,7 @@ Ptrs pointers(const tm_plan* p, void* ws)
 {
     const Layout& L = p->lay;
     Ptrs q{};
-    q.E = wsp<float>(ws, L.E); q.Hx = wsp<float>(ws, L.Hx); q.Hz = wsp<float>(ws, L.Hz);
-    q.psi_ez = wsp<float>(ws, L.psi_ez); q.psi_ex = wsp<float>(ws, L.psi_ex);
-    q.psi_hxz = wsp<float>(ws, L.psi_hxz); q.psi_hzx = wsp<float>(ws, L.psi_hzx);
-    q.lE = wsp<float>(ws, L.lE); q.lHx = wsp<float>(ws, L.lHx); q.lHz = wsp<float>(ws, L.lHz);
-    q.phi_ez = wsp<float>(ws, L.phi_ez); q.phi_ex = wsp<float>(ws, L.phi_ex);
-    q.phi_hxz = wsp<float>(ws, L.phi_hxz); q.phi_hzx = wsp<float>(ws, L.phi_hzx);
-    q.Ub = wsp<float>(ws, L.Ub); q.Wb = wsp<float>(ws, L.Wb);
-    q.TZb = wsp<float>(ws, L.TZb); q.TXb = wsp<float>(ws, L.TXb);
+    q.base = static_cast<char*>(ws);
     q.cp = wsp<float>(ws, L.cpml);
     const int32_t* t = wsp<int32_t>(ws, L.tables);
     q.s_cell = t + p->t_s_cell; q.s_ptr = t + p->t_s_ptr; q.s_list = t + p->t_s_list; q.s_idx = t + p->t_s_idx;
@@ -288,70 +340,100 @@ Ptrs pointers(const tm_plan* p, void* ws)
     return q;
 }
 
-dim3 stencil_grid(const Geo& g, int64_t S)
+// First byte and size of the state of time t (its set plus the in-place
+// memories), one contiguous range.
+uint64_t state_offset(const tm_plan* p, int64_t t)
 {
-    const int ex = g.nx - 2 * g.P + 1, ey = g.ny - 2 * g.P + 1;
-    return dim3((unsigned)((ex + BLK_X - 1) / BLK_X), (unsigned)((ey + BLK_Y - 1) / BLK_Y), (unsigned)S);
+    return (t & 1) ? p->lay.inplace : p->lay.fset[0];
 }
 
-// One forward step t.  snap: SNAP_* kind for the E pass, with destinations.
+// One forward step t: the fused H/E kernel (set t%2 -> set (t+1)%2), then
+// the sources and receivers on the new E.
 template <int P>
 void fwd_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
               const float* f, float* r, int64_t t, int snap, void* se, void* sc, hipStream_t st)
 {
-    const Geo& g = p->g;
-    const dim3 grid = stencil_grid(g, p->d.n_shots), blk(BLK_X, BLK_Y);
-    timed(p, KID_FWD_H, t, st, [&] {
-        k_fwd_h<P><<<grid, blk, 0, st>>>(g, cq, q.E, q.Hx, q.Hz, q.psi_ez, q.psi_ex, q.cp);
-    });
-    timed(p, KID_FWD_E, t, st, [&] {
-        if (snap == SNAP_F32)
-            k_fwd_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
-        else if (snap == SNAP_BF16)
-            k_fwd_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, se, sc);
-        else
-            k_fwd_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cb, q.Hx, q.Hz, q.E, q.psi_hxz, q.psi_hzx, q.cp, nullptr, nullptr);
+    const Layout& L = p->lay;
+    char* s0 = q.base + L.fset[t & 1];
+    char* s1 = q.base + L.fset[(t + 1) & 1];
+    char* ip = q.base + L.inplace;
+    FwdArgs a;
+    a.g = p->g;
+    a.t = p->tiling_fwd;
+    a.ca = ca; a.cb = cb; a.cq = cq; a.cp = q.cp;
+    a.E0 = reinterpret_cast<const float*>(s0 + L.oE);
+    a.Hx0 = reinterpret_cast<const float*>(s0 + L.oHx);
+    a.Hz0 = reinterpret_cast<const float*>(s0 + L.oHz);
+    a.pez0 = reinterpret_cast<const float*>(s0 + L.opez);
+    a.pex0 = reinterpret_cast<const float*>(s0 + L.opex);
+    a.E1 = reinterpret_cast<float*>(s1 + L.oE);
+    a.Hx1 = reinterpret_cast<float*>(s1 + L.oHx);
+    a.Hz1 = reinterpret_cast<float*>(s1 + L.oHz);
+    a.pez1 = reinterpret_cast<float*>(s1 + L.opez);
+    a.pex1 = reinterpret_cast<float*>(s1 + L.opex);
+    a.phxz = reinterpret_cast<float*>(ip + L.ophxz);
+    a.phzx = reinterpret_cast<float*>(ip + L.ophzx);
+    a.snap_e = se;
+    a.snap_c = sc;
+    const dim3 grid((unsigned)p->tiling_fwd.nblk), blk(NT);
+    timed(p, KID_FWD_STEP, t, st, [&] {
+        if (snap == SNAP_F32) k_fwd_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_BF16) k_fwd_step<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else k_fwd_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
     const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
     if (ns > 0 || (r != nullptr && nr > 0)) {
         const int64_t S = p->d.n_shots;
         k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            g.slab, q.E, ns > 0 ? f + t * S * ns : nullptr, ns, q.s_cell, q.s_ptr, q.s_list,
+            p->g.slab, a.E1, ns > 0 ? f + t * S * ns : nullptr, ns, q.s_cell, q.s_ptr, q.s_list,
             (r != nullptr && nr > 0) ? r + t * S * nr : nullptr, nr, q.r_idx);
     }
 }
 
+// One adjoint step t; k counts the adjoint steps taken (set k%2 -> (k+1)%2).
 template <int P>
 void adj_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
-              const float* grad_r, float* grad_f, int64_t t, int snap, const void* se,
+              const float* grad_r, float* grad_f, int64_t t, int64_t k, int snap, const void* se,
               const void* sc, float* gca, float* gcb, hipStream_t st)
 {
-    const Geo& g = p->g;
+    const Layout& L = p->lay;
     const int64_t S = p->d.n_shots;
     const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
+    char* s0 = q.base + L.aset[k & 1];
+    char* s1 = q.base + L.aset[(k + 1) & 1];
+    float* lE0 = reinterpret_cast<float*>(s0 + L.olE);
     if (nr > 0 || (grad_f != nullptr && ns > 0)) {
         k_adj_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            g.slab, q.lE, nr > 0 ? grad_r + t * S * nr : nullptr, nr, q.r_cell, q.r_ptr, q.r_list,
+            p->g.slab, lE0, nr > 0 ? grad_r + t * S * nr : nullptr, nr, q.r_cell, q.r_ptr, q.r_list,
             (grad_f != nullptr && ns > 0) ? grad_f + t * S * ns : nullptr, ns, q.s_idx);
     }
-    const int64_t band_cells = (int64_t)g.by * g.nx + (int64_t)(g.ny - g.by) * g.bx;
-    if (band_cells > 0)
-        timed(p, KID_ADJ_BAND, t, st, [&] {
-            k_adj_band<P><<<dim3((unsigned)((band_cells + 255) / 256), (unsigned)S), dim3(256), 0, st>>>(
-                g, cb, q.lE, q.phi_hzx, q.phi_hxz, q.Ub, q.Wb, q.cp);
-        });
-    const dim3 grid = stencil_grid(g, S), blk(BLK_X, BLK_Y);
-    timed(p, KID_ADJ_H, t, st, [&] {
-        k_adj_h<P><<<grid, blk, 0, st>>>(g, cb, cq, q.lE, q.lHx, q.lHz, q.phi_ez, q.phi_ex, q.Ub, q.Wb,
-                                         q.TZb, q.TXb, q.cp);
-    });
-    timed(p, KID_ADJ_E, t, st, [&] {
-        if (snap == SNAP_F32)
-            k_adj_e<P, SNAP_F32><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
-        else if (snap == SNAP_BF16)
-            k_adj_e<P, SNAP_BF16><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, se, sc, gca, gcb);
-        else
-            k_adj_e<P, SNAP_NONE><<<grid, blk, 0, st>>>(g, ca, cq, q.lHx, q.lHz, q.lE, q.TZb, q.TXb, nullptr, nullptr, nullptr, nullptr);
+    AdjArgs a;
+    a.g = p->g;
+    a.t = p->tiling_adj;
+    a.ca = ca; a.cb = cb; a.cq = cq; a.cp = q.cp;
+    a.lE0 = lE0;
+    a.lHx0 = reinterpret_cast<const float*>(s0 + L.olHx);
+    a.lHz0 = reinterpret_cast<const float*>(s0 + L.olHz);
+    a.fhzx0 = reinterpret_cast<const float*>(s0 + L.ofhzx);
+    a.fhxz0 = reinterpret_cast<const float*>(s0 + L.ofhxz);
+    a.fex0 = reinterpret_cast<const float*>(s0 + L.ofex);
+    a.fez0 = reinterpret_cast<const float*>(s0 + L.ofez);
+    a.lE1 = reinterpret_cast<float*>(s1 + L.olE);
+    a.lHx1 = reinterpret_cast<float*>(s1 + L.olHx);
+    a.lHz1 = reinterpret_cast<float*>(s1 + L.olHz);
+    a.fhzx1 = reinterpret_cast<float*>(s1 + L.ofhzx);
+    a.fhxz1 = reinterpret_cast<float*>(s1 + L.ofhxz);
+    a.fex1 = reinterpret_cast<float*>(s1 + L.ofex);
+    a.fez1 = reinterpret_cast<float*>(s1 + L.ofez);
+    a.snap_e = se;
+    a.snap_c = sc;
+    a.gca = gca;
+    a.gcb = gcb;
+    const dim3 grid((unsigned)p->tiling_adj.nblk), blk(NT);
+    timed(p, KID_ADJ_STEP, t, st, [&] {
+        if (snap == SNAP_F32) k_adj_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_BF16) k_adj_step<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else k_adj_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
 }
 
@@ -365,17 +447,51 @@ tm_status check_ws(const tm_plan* p, void* ws, uint64_t ws_bytes)
     return TM_OK;
 }
 
+// Resident workgroups of one step kernel on the current device.
+tm_status resident(const void* fn, int64_t* cap)
+{
+    int dev = 0, ncu = 0, nb = 0;
+    HIPCHK(hipGetDevice(&dev));
+    HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, NT, 0));
+    *cap = (int64_t)std::max(nb, 1) * std::max(ncu, 1);
+    return TM_OK;
+}
+
+// Make the tilings for the current device (once per device).
+template <int P>
+tm_status device_tiling(tm_plan* p)
+{
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev == p->tiling_device) return TM_OK;
+    const bool bf = p->d.snap == TM_SNAP_BF16;
+    int64_t cf = 0, ca = 0;
+    tm_status v = resident(bf ? reinterpret_cast<const void*>(&k_fwd_step<P, SNAP_BF16>)
+                              : reinterpret_cast<const void*>(&k_fwd_step<P, SNAP_F32>), &cf);
+    if (v != TM_OK) return v;
+    v = resident(bf ? reinterpret_cast<const void*>(&k_adj_step<P, SNAP_BF16>)
+                    : reinterpret_cast<const void*>(&k_adj_step<P, SNAP_F32>), &ca);
+    if (v != TM_OK) return v;
+    p->tiling_fwd = make_tiling(p->d, P, cf);
+    p->tiling_adj = make_tiling(p->d, P, ca);
+    p->tiling_device = dev;
+    return TM_OK;
+}
+
 template <int P>
 tm_status run_forward(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq,
                       const float* f, float* r, int64_t t0, int64_t t1, bool store, hipStream_t st)
 {
+    tm_status v = device_tiling<P>(p);
+    if (v != TM_OK) return v;
     const Ptrs q = pointers(p, ws);
     const bool full = p->K == 0;
     for (int64_t t = t0; t < t1; ++t) {
         if (store && !full && t > 0 && t % p->K == 0) {
             const int64_t slot = t / p->K - 1;
-            HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, wsp<char>(ws, p->lay.fwd),
-                                  p->lay.fwd_bytes, hipMemcpyDeviceToDevice, st));
+            HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, q.base + state_offset(p, t),
+                                  p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
         }
         if (store && full)
             fwd_step<P>(p, q, ca, cb, cq, f, r, t, snap_kind(p), q.snapE + t * p->lay.snap_step,
@@ -391,14 +507,19 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* ca, const float* cb, co
                       const float* f, const float* grad_r, float* grad_f, float* gca, float* gcb,
                       hipStream_t st)
 {
+    tm_status v = device_tiling<P>(p);
+    if (v != TM_OK) return v;
     const Ptrs q = pointers(p, ws);
     const int64_t nt = p->d.nt;
     const bool want_grad = gca != nullptr || gcb != nullptr;
     const int snap = want_grad ? snap_kind(p) : SNAP_NONE;
+    int64_t k = 0;
     if (p->K == 0 || !want_grad) {
-        for (int64_t t = nt - 1; t >= 0; --t)
-            adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, snap, q.snapE + (want_grad ? t : 0) * p->lay.snap_step,
-                        q.snapC + (want_grad ? t : 0) * p->lay.snap_step, gca, gcb, st);
+        for (int64_t t = nt - 1; t >= 0; --t, ++k) {
+            const uint64_t so = want_grad ? (uint64_t)t * p->lay.snap_step : 0;
+            adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, k, snap, want_grad ? q.snapE + so : nullptr,
+                        want_grad ? q.snapC + so : nullptr, gca, gcb, st);
+        }
     } else {
         for (int64_t seg = p->n_seg - 1; seg >= 0; --seg) {
             const int64_t ta = seg * p->K, tb = std::min(ta + p->K, nt);
@@ -406,14 +527,14 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* ca, const float* cb, co
                 tm_status z = zero(wsp<float>(ws, p->lay.fwd), p->lay.fwd_bytes, st);
                 if (z != TM_OK) return z;
             } else {
-                HIPCHK(hipMemcpyAsync(wsp<char>(ws, p->lay.fwd), q.ckpt + (seg - 1) * p->lay.ckpt_slot,
-                                      p->lay.fwd_bytes, hipMemcpyDeviceToDevice, st));
+                HIPCHK(hipMemcpyAsync(q.base + state_offset(p, ta), q.ckpt + (seg - 1) * p->lay.ckpt_slot,
+                                      p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
             }
             for (int64_t t = ta; t < tb; ++t)
                 fwd_step<P>(p, q, ca, cb, cq, f, nullptr, t, snap, q.snapE + (t - ta) * p->lay.snap_step,
                             q.snapC + (t - ta) * p->lay.snap_step, st);
-            for (int64_t t = tb - 1; t >= ta; --t)
-                adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, snap, q.snapE + (t - ta) * p->lay.snap_step,
+            for (int64_t t = tb - 1; t >= ta; --t, ++k)
+                adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
                             q.snapC + (t - ta) * p->lay.snap_step, gca, gcb, st);
         }
     }
@@ -471,7 +592,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16) return TM_EINVAL;
     if (d.ny < 2 * P + 2 || d.nx < 2 * P + 2) return TM_EINVAL;
-    if (d.ny * d.nx >= (int64_t(1) << 31)) return TM_EINVAL;
+    if (d.ny * d.nx >= (int64_t(1) << 29)) return TM_EINVAL;   // per-shot slabs < 2 GiB (buffer views)
     if (d.n_shots * std::max<int64_t>(d.n_src, d.n_rec) >= (int64_t(1) << 31)) return TM_EINVAL;
     if (d.n_shots > 65535) return TM_EINVAL;
     if (!(d.dy > 0.0) || !(d.dx > 0.0) || !std::isfinite(d.dy) || !std::isfinite(d.dx)) return TM_EINVAL;
@@ -529,6 +650,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         p->n_ckpt = 0;
         p->seg_steps = d.nt;
     }
+    p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024);
     make_layout(p);
     if (d.hbm_budget > 0 && p->lay.total > d.hbm_budget) {
         delete p;
