@@ -161,6 +161,12 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=200, help="time steps of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only timing")
+    ap.add_argument("--nt", type=int, default=0,
+                    help="override the number of time steps (profiling runs only; "
+                         "the bench line then names the reduced workload)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -181,8 +187,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.copy_mb > 0:
+        n = args.copy_mb * (1 << 20) // 4
+        src_t = torch.ones(n, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_mb} MiB done")
+        del src_t, dst_t
+
     log(f"building workload config{args.config}")
-    wl = inputs.as_f32(inputs.make_config(args.config))
+    over = {"nt": args.nt} if args.nt > 0 else {}
+    wl = inputs.as_f32(inputs.make_config(args.config, **over))
     prop = native.Propagator(wl, device=dev)
     log(f"workspace {prop.ws_bytes / 2**30:.1f} GiB, grid {wl.ny}x{wl.nx}, S={wl.n_shots}, nt={wl.nt}")
     S, ny, nx = wl.n_shots, wl.ny, wl.nx
@@ -290,7 +307,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"config{args.config}: " + WORKLOADS[args.config],
+        "config": {"workload": f"config{args.config}: " + WORKLOADS[args.config]
+                   + (f" (reduced to {wl.nt} time steps)" if args.nt > 0 else ""),
                    "grid": [wl.ny, wl.nx], "shots": wl.n_shots, "time_steps": wl.nt, "order": wl.order,
                    "snapshots": wl.snap, "ckpt_every": wl.ckpt_every, "cell_updates": cell_updates},
         "fwd_value": None if fwd_value is None else round(fwd_value, 3),
