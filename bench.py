@@ -90,6 +90,9 @@ def kernel_bytes(name, wl, store, snap_bytes):
     if name == "k_fwd_step":
         snaps = 2 * snap_bytes * interior if store else 0
         return S * (36 * cells + 16 * (band_y + band_x) + snaps)
+    if name == "k_fwd_step2":    # two steps per launch: the state crosses HBM once
+        snaps = 2 * 2 * snap_bytes * interior if store else 0
+        return S * (36 * cells + 16 * (band_y + band_x) + snaps)
     if name == "k_adj_step":
         grads = (2 * snap_bytes + 16) * interior if store else 0
         return S * (36 * cells + 16 * (band_y + band_x) + grads)
@@ -280,7 +283,9 @@ def main():
         if n == 0:
             continue
         avg_ms = ms / n
-        launches = 2 * wl.nt if name.startswith("k_fwd") and wl.ckpt_every else wl.nt
+        launches = wl.nt // 2 if name == "k_fwd_step2" else wl.nt
+        if name.startswith("k_fwd") and wl.ckpt_every:
+            launches *= 2
         # in a full step the forward stores snapshots and the adjoint accumulates gradients
         nbytes = kernel_bytes(name, wl, store=True, snap_bytes=snap_bytes)
         kernels[name] = dict(avg_us=avg_ms * 1e3, samples=n, est_total_s=avg_ms * launches / 1e3,

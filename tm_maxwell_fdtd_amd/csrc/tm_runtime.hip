@@ -16,11 +16,10 @@
 // (fields and band CPML memories) every K steps and replays each segment
 // into a K-step snapshot buffer inside tm_adjoint.
 //
-// State double buffering: the forward state at time t lives in set t % 2;
-// a step reads one set and writes the other.  The E-update CPML memories,
-// which only their owner thread touches, live between the two sets, so
-// "set 0 + in-place memories" and "in-place memories + set 1" are each one
-// contiguous range (a checkpoint is one copy).
+// State double buffering: each forward launch (one or two time steps) reads
+// one set of fields and CPML memories and writes the other; the plan tracks
+// which set holds the current state.  A checkpoint is a copy of one set and
+// is restored into set 0.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -34,6 +33,7 @@
 #include "tm_fdtd.h"
 #include "tm_kernels.hpp"
 #include "tm_step.hpp"
+#include "tm_step2.hpp"
 
 using namespace tmf;
 
@@ -95,14 +95,65 @@ Scatter build_scatter(const int64_t* ids, int64_t S, int64_t n)
     return t;
 }
 
+// Per-row event tables of the two-step kernel: for shot s and row y,
+// row[s*ny + y] is -1 or an event row k; col[k*nx + x] is -1 or an event e
+// (a cell carrying sources and/or receivers of that shot); the sources of e
+// are src[sp[e] .. sp[e+1]) and its receivers rec[rp[e] .. rp[e+1]), in
+// ascending index order.
+struct EventTables {
+    std::vector<int32_t> row, col, sp, src, rp, rec;
+    bool any = false;
+};
+
+EventTables build_events(const int64_t* src, int64_t n_src, const int64_t* rec, int64_t n_rec, int64_t S,
+                         int64_t ny, int64_t nx)
+{
+    EventTables t;
+    t.row.assign(S * ny, -1);
+    std::vector<std::pair<int64_t, int32_t>> v;   // (cell, index); index >= 0 source, < 0 receiver -1-j
+    int32_t n_rows = 0;
+    for (int64_t s = 0; s < S; ++s) {
+        v.clear();
+        for (int64_t i = 0; i < n_src; ++i)
+            if (src[s * n_src + i] >= 0) v.emplace_back(src[s * n_src + i], (int32_t)i);
+        for (int64_t j = 0; j < n_rec; ++j)
+            if (rec[s * n_rec + j] >= 0) v.emplace_back(rec[s * n_rec + j], (int32_t)(-1 - j));
+        // by cell, then sources (ascending) before receivers (ascending)
+        std::sort(v.begin(), v.end(), [](const auto& a, const auto& b) {
+            if (a.first != b.first) return a.first < b.first;
+            const bool sa = a.second >= 0, sb = b.second >= 0;
+            if (sa != sb) return sa;
+            return sa ? a.second < b.second : a.second > b.second;
+        });
+        for (size_t q = 0; q < v.size();) {
+            const int64_t cell = v[q].first, y = cell / nx, x = cell % nx;
+            int32_t& rk = t.row[s * ny + y];
+            if (rk < 0) {
+                rk = n_rows++;
+                t.col.resize((size_t)n_rows * nx, -1);
+            }
+            const int32_t e = (int32_t)t.sp.size();
+            t.col[(size_t)rk * nx + x] = e;
+            t.sp.push_back((int32_t)t.src.size());
+            t.rp.push_back((int32_t)t.rec.size());
+            for (; q < v.size() && v[q].first == cell; ++q) {
+                if (v[q].second >= 0) t.src.push_back(v[q].second);
+                else t.rec.push_back(-1 - v[q].second);
+            }
+            t.any = true;
+        }
+    }
+    t.sp.push_back((int32_t)t.src.size());
+    t.rp.push_back((int32_t)t.rec.size());
+    return t;
+}
+
 struct Layout {
     uint64_t cpml = 0, tables = 0, scratch = 0;
-    // forward state: [set 0][in-place memories][set 1]
+    // forward state: [set 0][set 1]; a set is E, Hx, Hz and the four CPML memories
     uint64_t fwd = 0, fwd_bytes = 0;
     uint64_t fset[2] = {0, 0}, set_bytes = 0;
-    uint64_t inplace = 0, inplace_bytes = 0;
-    uint64_t oE = 0, oHx = 0, oHz = 0, opez = 0, opex = 0;   // within a set
-    uint64_t ophxz = 0, ophzx = 0;                           // within the in-place block
+    uint64_t oE = 0, oHx = 0, oHz = 0, opez = 0, opex = 0, ophxz = 0, ophzx = 0;   // within a set
     // adjoint state: [set 0][set 1]
     uint64_t adj = 0, adj_bytes = 0, aset[2] = {0, 0}, aset_bytes = 0;
     uint64_t olE = 0, olHx = 0, olHz = 0, ofhzx = 0, ofhxz = 0, ofex = 0, ofez = 0;
@@ -114,8 +165,8 @@ struct Layout {
 }  // namespace
 
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
-enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_COUNT };
-const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step"};
+enum KernelId { KID_FWD_STEP = 0, KID_FWD_STEP2, KID_ADJ_STEP, KID_COUNT };
+const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_fwd_step2", "k_adj_step"};
 
 struct TimedLaunch {
     int kid;
@@ -126,12 +177,14 @@ struct tm_plan {
     tm_desc d{};
     int P = 0;
     Geo g{};
-    Tiling tiling_fwd{}, tiling_adj{};   // per device, made at the first device call
+    Tiling tiling_fwd{}, tiling_fwd2{}, tiling_adj{};   // per device, made at the first device call
     int tiling_device = -1;
     std::vector<float> cpml;       // [12][L]
     std::vector<int32_t> tables;   // scatter tables, packed
     uint64_t t_s_cell = 0, t_s_ptr = 0, t_s_list = 0, t_s_idx = 0;
     uint64_t t_r_cell = 0, t_r_ptr = 0, t_r_list = 0, t_r_idx = 0;
+    uint64_t t_ev_row = 0, t_ev_col = 0, t_ev_sp = 0, t_ev_src = 0, t_ev_rp = 0, t_ev_rec = 0;
+    bool has_events = false;
     Layout lay;
     int64_t K = 0, n_seg = 0, n_ckpt = 0, seg_steps = 0;
     // pinned staging copy of cpml + tables (allocated on first device call)
@@ -140,6 +193,8 @@ struct tm_plan {
     // sequence state
     void* ws_last = nullptr;
     int64_t fwd_next = -1;
+    int fwd_cur = 0;               // forward set holding the state at fwd_next
+    bool single_step = true;       // one time step per forward launch (time_block != 2)
     bool stored_ok = false;
     bool fwd_complete = false;
     // sampled kernel timing
@@ -186,14 +241,13 @@ void make_layout(tm_plan* p)
     L.cpml = take(12 * (uint64_t)g.L * 4);
     L.tables = take(p->tables.size() * 4);
     L.scratch = take(4096);
-    // one forward set: E, Hx, Hz, Hx-update y memory, Hz-update x memory
+    // one forward set: E, Hx, Hz, Hx-update y memory, Hz-update x memory,
+    // E-update y memory, E-update x memory
     L.oE = 0; L.oHx = fld; L.oHz = 2 * fld; L.opez = 3 * fld; L.opex = 3 * fld + yb;
-    L.set_bytes = 3 * fld + yb + xb;
-    L.ophxz = 0; L.ophzx = yb;
-    L.inplace_bytes = yb + xb;
+    L.ophxz = 3 * fld + yb + xb; L.ophzx = 3 * fld + 2 * yb + xb;
+    L.set_bytes = 3 * fld + 2 * yb + 2 * xb;
     L.fwd = o;
     L.fset[0] = take(L.set_bytes);
-    L.inplace = take(L.inplace_bytes);
     L.fset[1] = take(L.set_bytes);
     L.fwd_bytes = o - L.fwd;
     // one adjoint set: lambdas and the four adjoint CPML memories
@@ -208,7 +262,7 @@ void make_layout(tm_plan* p)
     L.snap_step = align_up(S * (uint64_t)g.nyi * (uint64_t)g.nxi * esz);
     L.snapE = take(L.snap_step * (uint64_t)p->seg_steps);
     L.snapC = take(L.snap_step * (uint64_t)p->seg_steps);
-    L.ckpt_slot = L.set_bytes + L.inplace_bytes;
+    L.ckpt_slot = L.set_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
     L.total = o;
 }
@@ -220,10 +274,9 @@ void make_layout(tm_plan* p)
 // 16 and CH_MAX rows, and no round runs half empty.  TM_FDTD_CHUNK_ROWS
 // (environment, read when the tiling is made) forces the chunk height, for
 // tuning.
-Tiling make_tiling(const tm_desc& d, int P, int64_t cap)
+Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W)
 {
     Tiling t{};
-    const int W = NT - 4 * P + 2;
     const int R = (int)d.ny - 2 * P + 1, nx_e = (int)d.nx - 2 * P + 1;
     t.W = W;
     t.nstrip = (nx_e + W - 1) / W;
@@ -340,23 +393,26 @@ Ptrs pointers(const tm_plan* p, void* ws)
     return q;
 }
 
-// First byte and size of the state of time t (its set plus the in-place
-// memories), one contiguous range.
-uint64_t state_offset(const tm_plan* p, int64_t t)
+// Source/receiver pointers of one step (null when there are none).
+struct StepIO {
+    const float* f;   // [S][n_src] of this step
+    float* r;         // [S][n_rec] of this step
+};
+StepIO step_io(const tm_plan* p, const float* f, float* r, int64_t t)
 {
-    return (t & 1) ? p->lay.inplace : p->lay.fset[0];
+    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
+    return StepIO{ns > 0 ? f + t * S * ns : nullptr, (r != nullptr && nr > 0) ? r + t * S * nr : nullptr};
 }
 
-// One forward step t: the fused H/E kernel (set t%2 -> set (t+1)%2), then
-// the sources and receivers on the new E.
+// One forward step t: the fused H/E kernel (set cur -> 1-cur), then the
+// sources and receivers on the new E.
 template <int P>
-void fwd_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
+void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* ca, const float* cb, const float* cq,
               const float* f, float* r, int64_t t, int snap, void* se, void* sc, hipStream_t st)
 {
     const Layout& L = p->lay;
-    char* s0 = q.base + L.fset[t & 1];
-    char* s1 = q.base + L.fset[(t + 1) & 1];
-    char* ip = q.base + L.inplace;
+    char* s0 = q.base + L.fset[cur];
+    char* s1 = q.base + L.fset[1 - cur];
     FwdArgs a;
     a.g = p->g;
     a.t = p->tiling_fwd;
@@ -366,13 +422,15 @@ void fwd_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const
     a.Hz0 = reinterpret_cast<const float*>(s0 + L.oHz);
     a.pez0 = reinterpret_cast<const float*>(s0 + L.opez);
     a.pex0 = reinterpret_cast<const float*>(s0 + L.opex);
+    a.phxz0 = reinterpret_cast<const float*>(s0 + L.ophxz);
+    a.phzx0 = reinterpret_cast<const float*>(s0 + L.ophzx);
     a.E1 = reinterpret_cast<float*>(s1 + L.oE);
     a.Hx1 = reinterpret_cast<float*>(s1 + L.oHx);
     a.Hz1 = reinterpret_cast<float*>(s1 + L.oHz);
     a.pez1 = reinterpret_cast<float*>(s1 + L.opez);
     a.pex1 = reinterpret_cast<float*>(s1 + L.opex);
-    a.phxz = reinterpret_cast<float*>(ip + L.ophxz);
-    a.phzx = reinterpret_cast<float*>(ip + L.ophzx);
+    a.phxz1 = reinterpret_cast<float*>(s1 + L.ophxz);
+    a.phzx1 = reinterpret_cast<float*>(s1 + L.ophzx);
     a.snap_e = se;
     a.snap_c = sc;
     const dim3 grid((unsigned)p->tiling_fwd.nblk), blk(NT);
@@ -382,12 +440,62 @@ void fwd_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const
         else k_fwd_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
     const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
-    if (ns > 0 || (r != nullptr && nr > 0)) {
-        const int64_t S = p->d.n_shots;
-        k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            p->g.slab, a.E1, ns > 0 ? f + t * S * ns : nullptr, ns, q.s_cell, q.s_ptr, q.s_list,
-            (r != nullptr && nr > 0) ? r + t * S * nr : nullptr, nr, q.r_idx);
+    const StepIO io = step_io(p, f, r, t);
+    if (io.f != nullptr || io.r != nullptr) {
+        k_fwd_srcrec<<<dim3((unsigned)p->d.n_shots), dim3(256), 0, st>>>(
+            p->g.slab, a.E1, io.f, ns, q.s_cell, q.s_ptr, q.s_list, io.r, nr, q.r_idx);
     }
+}
+
+// Steps t and t+1 in one launch (set cur -> 1-cur), sources and receivers
+// included.  se/sc: snapshot destinations of step t (those of step t+1
+// follow at snap_step bytes), or null.
+template <int P>
+void fwd_step2(tm_plan* p, const Ptrs& q, int cur, const float* ca, const float* cb, const float* cq,
+               const float* f, float* r, int64_t t, int snap, char* se, char* sc, hipStream_t st)
+{
+    const Layout& L = p->lay;
+    char* s0 = q.base + L.fset[cur];
+    char* s1 = q.base + L.fset[1 - cur];
+    Fwd2Args a;
+    a.g = p->g;
+    a.t = p->tiling_fwd2;
+    a.ca = ca; a.cb = cb; a.cq = cq; a.cp = q.cp;
+    a.E0 = reinterpret_cast<const float*>(s0 + L.oE);
+    a.Hx0 = reinterpret_cast<const float*>(s0 + L.oHx);
+    a.Hz0 = reinterpret_cast<const float*>(s0 + L.oHz);
+    a.pez0 = reinterpret_cast<const float*>(s0 + L.opez);
+    a.pex0 = reinterpret_cast<const float*>(s0 + L.opex);
+    a.phxz0 = reinterpret_cast<const float*>(s0 + L.ophxz);
+    a.phzx0 = reinterpret_cast<const float*>(s0 + L.ophzx);
+    a.E1 = reinterpret_cast<float*>(s1 + L.oE);
+    a.Hx1 = reinterpret_cast<float*>(s1 + L.oHx);
+    a.Hz1 = reinterpret_cast<float*>(s1 + L.oHz);
+    a.pez1 = reinterpret_cast<float*>(s1 + L.opez);
+    a.pex1 = reinterpret_cast<float*>(s1 + L.opex);
+    a.phxz1 = reinterpret_cast<float*>(s1 + L.ophxz);
+    a.phzx1 = reinterpret_cast<float*>(s1 + L.ophzx);
+    a.snapA_e = se;
+    a.snapA_c = sc;
+    a.snapB_e = se ? se + L.snap_step : nullptr;
+    a.snapB_c = sc ? sc + L.snap_step : nullptr;
+    const StepIO io0 = step_io(p, f, r, t), io1 = step_io(p, f, r, t + 1);
+    a.fA = io0.f; a.fB = io1.f; a.rA = io0.r; a.rB = io1.r;
+    const int32_t* tb = reinterpret_cast<const int32_t*>(q.base + L.tables);
+    a.ev.row = p->has_events ? tb + p->t_ev_row : nullptr;
+    a.ev.col = tb + p->t_ev_col;
+    a.ev.sp = tb + p->t_ev_sp;
+    a.ev.src = tb + p->t_ev_src;
+    a.ev.rp = tb + p->t_ev_rp;
+    a.ev.rec = tb + p->t_ev_rec;
+    a.ev.n_src = (int)p->d.n_src;
+    a.ev.n_rec = (int)p->d.n_rec;
+    const dim3 grid((unsigned)p->tiling_fwd2.nblk), blk(NT);
+    timed(p, KID_FWD_STEP2, t, st, [&] {
+        if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else k_fwd_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
+    });
 }
 
 // One adjoint step t; k counts the adjoint steps taken (set k%2 -> (k+1)%2).
@@ -473,10 +581,50 @@ tm_status device_tiling(tm_plan* p)
     v = resident(bf ? reinterpret_cast<const void*>(&k_adj_step<P, SNAP_BF16>)
                     : reinterpret_cast<const void*>(&k_adj_step<P, SNAP_F32>), &ca);
     if (v != TM_OK) return v;
-    p->tiling_fwd = make_tiling(p->d, P, cf);
-    p->tiling_adj = make_tiling(p->d, P, ca);
+    int64_t c2 = 0;
+    v = resident(bf ? reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_BF16>)
+                    : reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_F32>), &c2);
+    if (v != TM_OK) return v;
+    p->tiling_fwd = make_tiling(p->d, P, cf, NT - 4 * P + 2);
+    p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W);
+    p->tiling_adj = make_tiling(p->d, P, ca, NT - 4 * P + 2);
     p->tiling_device = dev;
     return TM_OK;
+}
+
+// Forward steps [t0, t1) from set *cur (updated).  snap: SNAP_* kind of the
+// stored steps; snap_base(t) gives the destinations of step t (null: none).
+// ckpt: save the state every K steps into the checkpoint slots.  Steps are
+// taken two per launch, except a last odd step and the step before a
+// checkpoint time.
+template <int P, typename SnapAt>
+tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* ca, const float* cb,
+                        const float* cq, const float* f, float* r, int64_t t0, int64_t t1, int snap,
+                        SnapAt snap_at, bool ckpt, hipStream_t st)
+{
+    const int64_t K = p->K;
+    const bool two = !p->single_step;
+    int64_t t = t0;
+    while (t < t1) {
+        if (ckpt && t > 0 && t % K == 0) {
+            const int64_t slot = t / K - 1;
+            HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, q.base + p->lay.fset[*cur],
+                                  p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
+        }
+        const bool pair = two && t + 1 < t1 && !(ckpt && (t + 1) % K == 0);
+        char* se = nullptr;
+        char* sc = nullptr;
+        if (snap != SNAP_NONE) snap_at(t, se, sc);
+        if (pair) {
+            fwd_step2<P>(p, q, *cur, ca, cb, cq, f, r, t, snap, se, sc, st);
+            t += 2;
+        } else {
+            fwd_step<P>(p, q, *cur, ca, cb, cq, f, r, t, snap, se, sc, st);
+            t += 1;
+        }
+        *cur = 1 - *cur;
+    }
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
 
 template <int P>
@@ -487,19 +635,12 @@ tm_status run_forward(tm_plan* p, void* ws, const float* ca, const float* cb, co
     if (v != TM_OK) return v;
     const Ptrs q = pointers(p, ws);
     const bool full = p->K == 0;
-    for (int64_t t = t0; t < t1; ++t) {
-        if (store && !full && t > 0 && t % p->K == 0) {
-            const int64_t slot = t / p->K - 1;
-            HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, q.base + state_offset(p, t),
-                                  p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
-        }
-        if (store && full)
-            fwd_step<P>(p, q, ca, cb, cq, f, r, t, snap_kind(p), q.snapE + t * p->lay.snap_step,
-                        q.snapC + t * p->lay.snap_step, st);
-        else
-            fwd_step<P>(p, q, ca, cb, cq, f, r, t, SNAP_NONE, nullptr, nullptr, st);
-    }
-    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+    const int snap = (store && full) ? snap_kind(p) : SNAP_NONE;
+    auto at = [&](int64_t t, char*& se, char*& sc) {
+        se = q.snapE + t * p->lay.snap_step;
+        sc = q.snapC + t * p->lay.snap_step;
+    };
+    return forward_range<P>(p, q, &p->fwd_cur, ca, cb, cq, f, r, t0, t1, snap, at, store && !full, st);
 }
 
 template <int P>
@@ -523,16 +664,21 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* ca, const float* cb, co
     } else {
         for (int64_t seg = p->n_seg - 1; seg >= 0; --seg) {
             const int64_t ta = seg * p->K, tb = std::min(ta + p->K, nt);
+            // the segment's initial state into set 0
             if (seg == 0) {
                 tm_status z = zero(wsp<float>(ws, p->lay.fwd), p->lay.fwd_bytes, st);
                 if (z != TM_OK) return z;
             } else {
-                HIPCHK(hipMemcpyAsync(q.base + state_offset(p, ta), q.ckpt + (seg - 1) * p->lay.ckpt_slot,
+                HIPCHK(hipMemcpyAsync(q.base + p->lay.fset[0], q.ckpt + (seg - 1) * p->lay.ckpt_slot,
                                       p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
             }
-            for (int64_t t = ta; t < tb; ++t)
-                fwd_step<P>(p, q, ca, cb, cq, f, nullptr, t, snap, q.snapE + (t - ta) * p->lay.snap_step,
-                            q.snapC + (t - ta) * p->lay.snap_step, st);
+            int cur = 0;
+            auto at = [&](int64_t t, char*& se, char*& sc) {
+                se = q.snapE + (t - ta) * p->lay.snap_step;
+                sc = q.snapC + (t - ta) * p->lay.snap_step;
+            };
+            v = forward_range<P>(p, q, &cur, ca, cb, cq, f, nullptr, ta, tb, snap, at, false, st);
+            if (v != TM_OK) return v;
             for (int64_t t = tb - 1; t >= ta; --t, ++k)
                 adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
                             q.snapC + (t - ta) * p->lay.snap_step, gca, gcb, st);
@@ -591,6 +737,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16) return TM_EINVAL;
+    if (d.time_block < 0 || d.time_block > 2 || d.reserved != 0) return TM_EINVAL;
     if (d.ny < 2 * P + 2 || d.nx < 2 * P + 2) return TM_EINVAL;
     if (d.ny * d.nx >= (int64_t(1) << 29)) return TM_EINVAL;   // per-shot slabs < 2 GiB (buffer views)
     if (d.n_shots * std::max<int64_t>(d.n_src, d.n_rec) >= (int64_t(1) << 31)) return TM_EINVAL;
@@ -638,6 +785,12 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     };
     p->t_s_cell = append(ss.cell); p->t_s_ptr = append(ss.ptr); p->t_s_list = append(ss.list); p->t_s_idx = append(ss.idx);
     p->t_r_cell = append(rs.cell); p->t_r_ptr = append(rs.ptr); p->t_r_list = append(rs.list); p->t_r_idx = append(rs.idx);
+    const EventTables ev = build_events(src, d.n_src, rec, d.n_rec, d.n_shots, d.ny, d.nx);
+    p->has_events = ev.any;
+    p->t_ev_row = append(ev.row); p->t_ev_col = append(ev.col);
+    p->t_ev_sp = append(ev.sp); p->t_ev_src = append(ev.src);
+    p->t_ev_rp = append(ev.rp); p->t_ev_rec = append(ev.rec);
+    p->single_step = d.time_block != 2;
 
     if (d.ckpt_every > 0 && d.ckpt_every < d.nt) {
         p->K = d.ckpt_every;
@@ -650,7 +803,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         p->n_ckpt = 0;
         p->seg_steps = d.nt;
     }
-    p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024);
+    p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024, NT - 4 * P + 2);
     make_layout(p);
     if (d.hbm_budget > 0 && p->lay.total > d.hbm_budget) {
         delete p;
@@ -753,6 +906,7 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
         p->fwd_complete = false;
         v = zero(wsp<float>(ws, p->lay.fwd), p->lay.fwd_bytes, st);
         if (v != TM_OK) return v;
+        p->fwd_cur = 0;
         p->stored_ok = store;
     } else {
         p->stored_ok = p->stored_ok && store;

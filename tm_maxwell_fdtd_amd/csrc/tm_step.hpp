@@ -13,8 +13,7 @@
 // Columns within 2P-1 of the strip edges and rows within 2P-1 of the chunk
 // edges are read (and their H values recomputed) but written by the
 // neighbouring workgroup only.  The state is therefore double-buffered: a
-// step reads set "0" and writes set "1" (fields and the CPML memories that
-// halo cells recompute); memories only the owner ever touches stay in place.
+// step reads set "0" and writes set "1" (fields and CPML memories).
 //
 // Forward step (tide-GPR 0.0.9, maxwell.cu, forward_kernel_h then
 // forward_kernel_e):
@@ -185,8 +184,10 @@ struct FwdArgs {
     float* __restrict__ Hz1;
     float* __restrict__ pez1;
     float* __restrict__ pex1;
-    float* __restrict__ phxz;          // E-update y memory [S][by][nx], in place
-    float* __restrict__ phzx;          // E-update x memory [S][ny][bx], in place
+    const float* __restrict__ phxz0;   // E-update y memory [S][by][nx]
+    const float* __restrict__ phzx0;   // E-update x memory [S][ny][bx]
+    float* __restrict__ phxz1;
+    float* __restrict__ phzx1;
     void* __restrict__ snap_e;         // Ey^n on the interior window, or null
     void* __restrict__ snap_c;         // curl H^n on the interior window
 };
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
     // Buffers of this shot's slabs.
     const uint32_t yb_b = (uint32_t)((int64_t)g.by * nx * 4), xb_b = (uint32_t)((int64_t)ny * g.bx * 4);
     const RBuf bMez(a.pez0 + ysh, yb_b), bMex(a.pex0 + xsh, xb_b);
-    const RBuf bMhxz(a.phxz + ysh, yb_b), bMhzx(a.phzx + xsh, xb_b);
+    const RBuf bMhxz(a.phxz0 + ysh, yb_b), bMhzx(a.phzx0 + xsh, xb_b);
 
     // Prefetch ring: every global load of iteration r (fields, coefficients
     // and CPML memories) is issued at iteration r - D into slot
@@ -355,14 +356,14 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
                 if (fx_e) {
                     float m = fMhzx[u];
                     uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
-                    a.phzx[xbase + (int64_t)y * g.bx] = m;
+                    a.phzx1[xbase + (int64_t)y * g.bx] = m;
                 }
                 float v = g.rdy * stencil<P>([&](int k) { return hw[P - 1 + k]; },
                                              [&](int k) { return hw[P - k]; });
                 if (ey_band) {
                     float m = fMhxz[u];
                     v = cpml_step(m, cte[3], cte[4], cte[5], v);
-                    a.phxz[ybase + (int64_t)band_y(g, y) * nx] = m;
+                    a.phxz1[ybase + (int64_t)band_y(g, y) * nx] = m;
                 }
                 const float curl = uu_ - v;
                 const float ev = ew[0];
