@@ -17,7 +17,9 @@ The ``roofline`` object is for the dominant stencil kernel: algorithmic
 bytes per launch over its average launch duration, sampled with HIP events
 inside the library on the stream the kernels run on (tm_timing_*).  HBM
 traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in
-``profiles/`` and is used only while the kernel source is unchanged.
+``profiles/`` (bytes per launch, scaled by what the counters read for a
+plain 1 GiB copy), is reported as a rate over the same launch time as
+``achieved`` and is used only while the kernel source is unchanged.
 
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload (one shot, a few dozen time steps) on the host cores.
@@ -89,9 +91,6 @@ def kernel_bytes(name, wl, store, snap_bytes):
     S = wl.n_shots
     if name == "k_fwd_step":
         snaps = 2 * snap_bytes * interior if store else 0
-        return S * (36 * cells + 16 * (band_y + band_x) + snaps)
-    if name == "k_fwd_step2":    # two steps per launch: the state crosses HBM once
-        snaps = 2 * 2 * snap_bytes * interior if store else 0
         return S * (36 * cells + 16 * (band_y + band_x) + snaps)
     if name == "k_adj_step":
         grads = (2 * snap_bytes + 16) * interior if store else 0
@@ -283,7 +282,7 @@ def main():
         if n == 0:
             continue
         avg_ms = ms / n
-        launches = wl.nt // 2 if name == "k_fwd_step2" else wl.nt
+        launches = wl.nt
         if name.startswith("k_fwd") and wl.ckpt_every:
             launches *= 2
         # in a full step the forward stores snapshots and the adjoint accumulates gradients
@@ -292,10 +291,14 @@ def main():
                              alg_bytes=nbytes, gbs=nbytes / (avg_ms * 1e-3) / 1e9)
     dom = max(kernels, key=lambda k: kernels[k]["est_total_s"])
     kd = kernels[dom]
-    traffic = load_traffic(dom, args.config)
+    # measured HBM bytes per launch (counter run of the same kernel source), as
+    # a rate over the same average launch time as ``achieved``
+    traffic_b = load_traffic(dom, args.config)
+    traffic = None if traffic_b is None else round(traffic_b / (kd["avg_us"] * 1e-6) / 1e9, 1)
     roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-                "avg_launch_us": round(kd["avg_us"], 2), "alg_bytes_per_launch": kd["alg_bytes"]}
+                "avg_launch_us": round(kd["avg_us"], 2), "alg_bytes_per_launch": kd["alg_bytes"],
+                "traffic_bytes_per_launch": None if traffic_b is None else int(traffic_b)}
     for name, k in sorted(kernels.items()):
         log(f"  {name:12s} avg {k['avg_us']:9.2f} us  ({k['samples']} samples)  "
             f"alg {k['alg_bytes'] / 1e6:8.1f} MB  -> {k['gbs']:7.1f} GB/s  est {k['est_total_s']:.3f} s/step")

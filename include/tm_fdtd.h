@@ -67,9 +67,6 @@ typedef enum tm_snap {
 typedef struct tm_desc {
     int32_t order;          /* spatial order: 2, 4 or 8                         */
     int32_t snap;           /* tm_snap                                          */
-    int32_t time_block;     /* time steps per forward launch: 0 or 1 = one,
-                               2 = two (temporally blocked; same results)       */
-    int32_t reserved;       /* must be 0                                        */
     int64_t n_shots;        /* shots S sharing one model                        */
     int64_t ny, nx;         /* padded grid; ny * nx < 2^29                      */
     int64_t pml_y0, pml_y1; /* interior window rows [pml_y0, pml_y1)            */

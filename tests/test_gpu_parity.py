@@ -214,41 +214,3 @@ def test_error_codes_on_device():
     finally:
         prop.close()
 
-
-@pytest.mark.parametrize("order", inputs.ORDERS)
-@pytest.mark.parametrize("ckpt", [0, 7])
-def test_two_steps_per_launch_bitwise_equal_single_steps(order, ckpt):
-    """The temporally blocked forward (two steps per launch, sources and
-    receivers in the kernel) computes exactly the single-step arithmetic."""
-    wl = inputs.as_f32(inputs.random_workload(order, 70, 9, nt=41, n_shots=3, n_src=3, n_rec=7,
-                                              seed=700 + order, src_anywhere=True))
-    wl.src[1, 1] = wl.src[1, 0]          # duplicate source cell
-    wl.src[2, 2] = -1                     # no source
-    wl.rec[0, 3] = wl.rec[0, 2]          # duplicate receiver cell
-    wl.rec[1, 4] = wl.src[1, 0]          # receiver on a source cell
-    one = run_gpu(wl, snap="f32", ckpt_every=ckpt, time_block=1)
-    two = run_gpu(wl, snap="f32", ckpt_every=ckpt, time_block=2)
-    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
-        np.testing.assert_array_equal(two[key], one[key], err_msg=key)
-
-
-def test_two_steps_per_launch_chunked_odd():
-    """Chunks of odd length pair steps differently; results stay bitwise equal."""
-    import torch
-
-    from tm_maxwell_fdtd_amd import native
-
-    wl = inputs.as_f32(inputs.random_workload(4, 60, 8, nt=30, n_shots=2, n_src=2, n_rec=5, seed=801))
-    prop = native.Propagator(wl, time_block=2)
-    try:
-        r1 = prop.forward(store=True)
-        _, a1, b1 = prop.adjoint(r1)
-        r2 = torch.zeros_like(r1)
-        for t0, t1 in ((0, 7), (7, 8), (8, 19), (19, 30)):
-            prop.forward(r=r2, store=True, t0=t0, t1=t1)
-        _, a2, b2 = prop.adjoint(r2)
-        torch.cuda.synchronize()
-        assert torch.equal(r1, r2)
-        assert torch.equal(a1, a2) and torch.equal(b1, b2)
-    finally:
-        prop.close()

@@ -1,8 +1,7 @@
 // Small kernels around the time-step kernels: source injection and
-// receiver gather (tide-GPR 0.0.9, maxwell.cu: add_sources_ey,
-// record_receivers_ey), their adjoints (add_adjoint_sources_ey,
-// record_adjoint_at_sources), the gradient shot sum (combine_grad), a fill
-// kernel and the Courant-number reduction (gfx950, wave64).
+// receiver gather and their adjoints, the gradient shot sum (tide-GPR
+// 0.0.9, maxwell.cu: combine_grad), a fill kernel and the Courant-number
+// reduction (gfx950, wave64).
 #pragma once
 
 #include "tm_common.hpp"
@@ -10,14 +9,17 @@
 namespace tmf {
 
 // ---------------------------------------------------------------------------
-// Sources and receivers of one step.  One workgroup per shot: first every
+// Sources and receivers of one step (tide-GPR 0.0.9, maxwell.cu:
+// add_sources_ey, record_receivers_ey), on the Ey of a state set whose
+// shots are blocks of shot_bytes with Ey at byte oE.  One workgroup per
+// shot: first every
 // distinct source cell adds the sum of its sources (ascending source order),
 // then, after the barrier, every receiver reads Ey.  Duplicate cells
 // therefore never race.
 //   cell/ptr/list: per shot, the distinct cells (padded with -1), CSR offsets
 //   into list, and list = source indices grouped by cell.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_fwd_srcrec(int64_t slab, float* __restrict__ E,
+__global__ __launch_bounds__(256) void k_fwd_srcrec(char* __restrict__ set, uint64_t shot_bytes, uint32_t oE,
                                                     const float* __restrict__ f_t, int n_src,
                                                     const int* __restrict__ s_cell,
                                                     const int* __restrict__ s_ptr,
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(256) void k_fwd_srcrec(int64_t slab, float* __restr
                                                     const int* __restrict__ r_idx)
 {
     const int s = blockIdx.x;
-    float* e = E + (int64_t)s * slab;
+    float* e = reinterpret_cast<float*>(set + (uint64_t)s * shot_bytes + oE);
     for (int u = threadIdx.x; u < n_src; u += blockDim.x) {
         const int c = s_cell[s * n_src + u];
         if (c < 0) continue;
@@ -43,10 +45,11 @@ __global__ __launch_bounds__(256) void k_fwd_srcrec(int64_t slab, float* __restr
     }
 }
 
-// Adjoint of the above: residuals injected at the receivers (distinct
+// Adjoint of the above (add_adjoint_sources_ey, record_adjoint_at_sources):
+// residuals injected at the receivers (distinct
 // receiver cells, ascending receiver order), then the adjoint field read at
 // the sources (source-wavelet gradient).
-__global__ __launch_bounds__(256) void k_adj_srcrec(int64_t slab, float* __restrict__ lE,
+__global__ __launch_bounds__(256) void k_adj_srcrec(char* __restrict__ set, uint64_t shot_bytes, uint32_t oE,
                                                     const float* __restrict__ gr_t, int n_rec,
                                                     const int* __restrict__ r_cell,
                                                     const int* __restrict__ r_ptr,
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(256) void k_adj_srcrec(int64_t slab, float* __restr
                                                     const int* __restrict__ s_idx)
 {
     const int s = blockIdx.x;
-    float* e = lE + (int64_t)s * slab;
+    float* e = reinterpret_cast<float*>(set + (uint64_t)s * shot_bytes + oE);
     for (int u = threadIdx.x; u < n_rec; u += blockDim.x) {
         const int c = r_cell[s * n_rec + u];
         if (c < 0) continue;

@@ -1,25 +1,27 @@
 // Host runtime and C ABI of the TM FDTD propagator (see include/tm_fdtd.h).
 //
 // The plan validates a problem on the host, builds conflict-free scatter
-// tables for the sources and receivers, chooses the tiling of the step
-// kernels and lays out the caller-allocated workspace.  tm_forward /
-// tm_adjoint / tm_grad enqueue kernels on the caller's stream; there is no
-// global state, so plans are independent.
+// tables for the sources and receivers, chooses the tiling of the step kernels and lays
+// out the caller-allocated workspace.  tm_forward / tm_adjoint / tm_grad
+// enqueue kernels on the caller's stream; there is no global state, so plans
+// are independent.
 //
-// Host loop structure follows the launchers of tide-GPR 0.0.9,
-// maxwell.cu (forward, forward_with_storage, backward): per forward step
-// the H and E updates (one fused kernel here, with the snapshot epilogue on
-// stored steps), then sources, then receivers; per adjoint step (reverse
-// time) the residual injection at the receivers, the adjoint read at the
-// sources, then the transposed H and E updates with gradient accumulation
-// (one fused kernel); then combine_grad.  Checkpoint mode stores the state
-// (fields and band CPML memories) every K steps and replays each segment
-// into a K-step snapshot buffer inside tm_adjoint.
+// Host loop structure follows the launchers of tide-GPR 0.0.9, maxwell.cu
+// (forward, forward_with_storage, backward): per forward step one fused
+// kernel (H and E updates, snapshot epilogue on stored steps) and one small
+// kernel for the sources and then the receivers; per adjoint step, in
+// reverse time, one small kernel (residual injection at the receivers,
+// adjoint read at the sources) and one fused kernel (transposed H and E
+// updates, gradient accumulation); then combine_grad.  Checkpoint mode
+// stores the state (fields and band CPML memories) every K steps and replays
+// each segment into a K-step snapshot buffer inside tm_adjoint.
 //
-// State double buffering: each forward launch (one or two time steps) reads
-// one set of fields and CPML memories and writes the other; the plan tracks
-// which set holds the current state.  A checkpoint is a copy of one set and
-// is restored into set 0.
+// Workspace: each step reads one state set and writes the other (double
+// buffering); a set holds, shot after shot, one contiguous block of fields
+// and CPML memories per shot, so a kernel addresses a shot's whole state
+// through one buffer descriptor.  The model arrays are copied into one
+// block [Ca | Cb | Cq] at the start of each call.  A checkpoint is a copy
+// of one set and is restored into set 0.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -33,7 +35,6 @@
 #include "tm_fdtd.h"
 #include "tm_kernels.hpp"
 #include "tm_step.hpp"
-#include "tm_step2.hpp"
 
 using namespace tmf;
 
@@ -43,6 +44,7 @@ namespace {
 
 constexpr uint64_t ALIGN = 256;
 uint64_t align_up(uint64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+constexpr uint64_t BLOCK_MAX = (uint64_t(1) << 31) - ALIGN;   // one buffer view
 
 double abs_coef_sum(int order)
 {
@@ -95,69 +97,16 @@ Scatter build_scatter(const int64_t* ids, int64_t S, int64_t n)
     return t;
 }
 
-// Per-row event tables of the two-step kernel: for shot s and row y,
-// row[s*ny + y] is -1 or an event row k; col[k*nx + x] is -1 or an event e
-// (a cell carrying sources and/or receivers of that shot); the sources of e
-// are src[sp[e] .. sp[e+1]) and its receivers rec[rp[e] .. rp[e+1]), in
-// ascending index order.
-struct EventTables {
-    std::vector<int32_t> row, col, sp, src, rp, rec;
-    bool any = false;
-};
-
-EventTables build_events(const int64_t* src, int64_t n_src, const int64_t* rec, int64_t n_rec, int64_t S,
-                         int64_t ny, int64_t nx)
-{
-    EventTables t;
-    t.row.assign(S * ny, -1);
-    std::vector<std::pair<int64_t, int32_t>> v;   // (cell, index); index >= 0 source, < 0 receiver -1-j
-    int32_t n_rows = 0;
-    for (int64_t s = 0; s < S; ++s) {
-        v.clear();
-        for (int64_t i = 0; i < n_src; ++i)
-            if (src[s * n_src + i] >= 0) v.emplace_back(src[s * n_src + i], (int32_t)i);
-        for (int64_t j = 0; j < n_rec; ++j)
-            if (rec[s * n_rec + j] >= 0) v.emplace_back(rec[s * n_rec + j], (int32_t)(-1 - j));
-        // by cell, then sources (ascending) before receivers (ascending)
-        std::sort(v.begin(), v.end(), [](const auto& a, const auto& b) {
-            if (a.first != b.first) return a.first < b.first;
-            const bool sa = a.second >= 0, sb = b.second >= 0;
-            if (sa != sb) return sa;
-            return sa ? a.second < b.second : a.second > b.second;
-        });
-        for (size_t q = 0; q < v.size();) {
-            const int64_t cell = v[q].first, y = cell / nx, x = cell % nx;
-            int32_t& rk = t.row[s * ny + y];
-            if (rk < 0) {
-                rk = n_rows++;
-                t.col.resize((size_t)n_rows * nx, -1);
-            }
-            const int32_t e = (int32_t)t.sp.size();
-            t.col[(size_t)rk * nx + x] = e;
-            t.sp.push_back((int32_t)t.src.size());
-            t.rp.push_back((int32_t)t.rec.size());
-            for (; q < v.size() && v[q].first == cell; ++q) {
-                if (v[q].second >= 0) t.src.push_back(v[q].second);
-                else t.rec.push_back(-1 - v[q].second);
-            }
-            t.any = true;
-        }
-    }
-    t.sp.push_back((int32_t)t.src.size());
-    t.rp.push_back((int32_t)t.rec.size());
-    return t;
-}
-
 struct Layout {
     uint64_t cpml = 0, tables = 0, scratch = 0;
-    // forward state: [set 0][set 1]; a set is E, Hx, Hz and the four CPML memories
-    uint64_t fwd = 0, fwd_bytes = 0;
-    uint64_t fset[2] = {0, 0}, set_bytes = 0;
-    uint64_t oE = 0, oHx = 0, oHz = 0, opez = 0, opex = 0, ophxz = 0, ophzx = 0;   // within a set
-    // adjoint state: [set 0][set 1]
-    uint64_t adj = 0, adj_bytes = 0, aset[2] = {0, 0}, aset_bytes = 0;
-    uint64_t olE = 0, olHx = 0, olHz = 0, ofhzx = 0, ofhxz = 0, ofex = 0, ofez = 0;
-    uint64_t snapE = 0, snapC = 0, snap_step = 0;   // per-step bytes of one snapshot array
+    uint64_t model = 0, model_bytes = 0;          // [Ca | Cb | Cq]
+    uint64_t slab_b = 0;                          // bytes of one [ny][nx] array, aligned
+    StateLayout st{};                             // one shot's block (forward and adjoint alike)
+    uint64_t set_bytes = 0;                       // S blocks
+    uint64_t fwd = 0, fwd_bytes = 0, fset[2] = {0, 0};
+    uint64_t adj = 0, adj_bytes = 0, aset[2] = {0, 0};
+    uint64_t snapE = 0, snapC = 0, snap_step = 0; // per-step bytes of one snapshot array (all shots)
+    uint64_t snap_shot = 0;                       // ... of one shot
     uint64_t ckpt = 0, ckpt_slot = 0;
     uint64_t total = 0;
 };
@@ -165,8 +114,8 @@ struct Layout {
 }  // namespace
 
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
-enum KernelId { KID_FWD_STEP = 0, KID_FWD_STEP2, KID_ADJ_STEP, KID_COUNT };
-const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_fwd_step2", "k_adj_step"};
+enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_COUNT };
+const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step"};
 
 struct TimedLaunch {
     int kid;
@@ -177,14 +126,12 @@ struct tm_plan {
     tm_desc d{};
     int P = 0;
     Geo g{};
-    Tiling tiling_fwd{}, tiling_fwd2{}, tiling_adj{};   // per device, made at the first device call
+    Tiling tiling_fwd{}, tiling_adj{};   // per device, made at the first device call
     int tiling_device = -1;
-    std::vector<float> cpml;       // [12][L]
-    std::vector<int32_t> tables;   // scatter tables, packed
+    std::vector<float> cpml;             // [12][L]
+    std::vector<int32_t> tables;         // scatter tables, packed
     uint64_t t_s_cell = 0, t_s_ptr = 0, t_s_list = 0, t_s_idx = 0;
     uint64_t t_r_cell = 0, t_r_ptr = 0, t_r_list = 0, t_r_idx = 0;
-    uint64_t t_ev_row = 0, t_ev_col = 0, t_ev_sp = 0, t_ev_src = 0, t_ev_rp = 0, t_ev_rec = 0;
-    bool has_events = false;
     Layout lay;
     int64_t K = 0, n_seg = 0, n_ckpt = 0, seg_steps = 0;
     // pinned staging copy of cpml + tables (allocated on first device call)
@@ -193,8 +140,7 @@ struct tm_plan {
     // sequence state
     void* ws_last = nullptr;
     int64_t fwd_next = -1;
-    int fwd_cur = 0;               // forward set holding the state at fwd_next
-    bool single_step = true;       // one time step per forward launch (time_block != 2)
+    int fwd_cur = 0;                     // forward set holding the state at fwd_next
     bool stored_ok = false;
     bool fwd_complete = false;
     // sampled kernel timing
@@ -227,44 +173,53 @@ bool finite_all(const float* p, int64_t n)
     return true;
 }
 
-void make_layout(tm_plan* p)
+// Returns false when a per-shot block or the model block exceeds one
+// buffer view.
+bool make_layout(tm_plan* p)
 {
     const tm_desc& d = p->d;
     const Geo& g = p->g;
     Layout& L = p->lay;
-    const uint64_t S = (uint64_t)d.n_shots, slab = (uint64_t)g.slab;
-    const uint64_t fld = align_up(S * slab * 4);
-    const uint64_t yb = align_up(S * (uint64_t)g.by * (uint64_t)g.nx * 4);
-    const uint64_t xb = align_up(S * (uint64_t)g.ny * (uint64_t)g.bx * 4);
+    const uint64_t S = (uint64_t)d.n_shots;
+    L.slab_b = align_up((uint64_t)g.slab * 4);
+    const uint64_t yb = align_up((uint64_t)g.by * (uint64_t)g.nx * 4);
+    const uint64_t xb = align_up((uint64_t)g.ny * (uint64_t)g.bx * 4);
+    const uint64_t shot = 3 * L.slab_b + 2 * yb + 2 * xb;
+    if (shot > BLOCK_MAX || 3 * L.slab_b > BLOCK_MAX) return false;
+    L.st.shot_bytes = (uint32_t)shot;
+    L.st.oE = 0;
+    L.st.oHx = (uint32_t)L.slab_b;
+    L.st.oHz = (uint32_t)(2 * L.slab_b);
+    L.st.oMyh = (uint32_t)(3 * L.slab_b);
+    L.st.oMxh = (uint32_t)(3 * L.slab_b + yb);
+    L.st.oMye = (uint32_t)(3 * L.slab_b + yb + xb);
+    L.st.oMxe = (uint32_t)(3 * L.slab_b + 2 * yb + xb);
+    L.set_bytes = S * shot;
+
     uint64_t o = 0;
     auto take = [&](uint64_t bytes) { uint64_t at = o; o = align_up(o + bytes); return at; };
     L.cpml = take(12 * (uint64_t)g.L * 4);
     L.tables = take(p->tables.size() * 4);
     L.scratch = take(4096);
-    // one forward set: E, Hx, Hz, Hx-update y memory, Hz-update x memory,
-    // E-update y memory, E-update x memory
-    L.oE = 0; L.oHx = fld; L.oHz = 2 * fld; L.opez = 3 * fld; L.opex = 3 * fld + yb;
-    L.ophxz = 3 * fld + yb + xb; L.ophzx = 3 * fld + 2 * yb + xb;
-    L.set_bytes = 3 * fld + 2 * yb + 2 * xb;
+    L.model_bytes = 3 * L.slab_b;
+    L.model = take(L.model_bytes);
     L.fwd = o;
     L.fset[0] = take(L.set_bytes);
     L.fset[1] = take(L.set_bytes);
     L.fwd_bytes = o - L.fwd;
-    // one adjoint set: lambdas and the four adjoint CPML memories
-    L.olE = 0; L.olHx = fld; L.olHz = 2 * fld;
-    L.ofhzx = 3 * fld; L.ofhxz = 3 * fld + xb; L.ofex = 3 * fld + xb + yb; L.ofez = 3 * fld + 2 * xb + yb;
-    L.aset_bytes = 3 * fld + 2 * xb + 2 * yb;
     L.adj = o;
-    L.aset[0] = take(L.aset_bytes);
-    L.aset[1] = take(L.aset_bytes);
+    L.aset[0] = take(L.set_bytes);
+    L.aset[1] = take(L.set_bytes);
     L.adj_bytes = o - L.adj;
     const uint64_t esz = d.snap == TM_SNAP_BF16 ? 2 : 4;
-    L.snap_step = align_up(S * (uint64_t)g.nyi * (uint64_t)g.nxi * esz);
+    L.snap_shot = (uint64_t)g.nyi * (uint64_t)g.nxi * esz;
+    L.snap_step = align_up(S * L.snap_shot);
     L.snapE = take(L.snap_step * (uint64_t)p->seg_steps);
     L.snapC = take(L.snap_step * (uint64_t)p->seg_steps);
     L.ckpt_slot = L.set_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
     L.total = o;
+    return true;
 }
 
 // Tiling of the step kernels over one device.  Strips are Strip<P>::W
@@ -369,11 +324,24 @@ tm_status upload_tables(tm_plan* p, void* ws, hipStream_t st)
     return TM_OK;
 }
 
+// Copy the caller's model arrays into the workspace's model block.
+tm_status stage_model(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq, hipStream_t st)
+{
+    const uint64_t n = (uint64_t)p->g.slab * 4;
+    char* m = wsp<char>(ws, p->lay.model);
+    HIPCHK(hipMemcpyAsync(m, ca, n, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(m + p->lay.slab_b, cb, n, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(m + 2 * p->lay.slab_b, cq, n, hipMemcpyDeviceToDevice, st));
+    return TM_OK;
+}
+
 // Device pointers of one workspace.
 struct Ptrs {
     char* base;
     const float* cp;
-    const int32_t *s_cell, *s_ptr, *s_list, *s_idx, *r_cell, *r_ptr, *r_list, *r_idx;
+    Model model;
+    const int32_t *s_cell, *s_ptr, *s_list, *s_idx;
+    const int32_t *r_cell, *r_ptr, *r_list, *r_idx;
     char *snapE, *snapC, *ckpt;
     float* scratch;
 };
@@ -384,157 +352,75 @@ Ptrs pointers(const tm_plan* p, void* ws)
     Ptrs q{};
     q.base = static_cast<char*>(ws);
     q.cp = wsp<float>(ws, L.cpml);
+    q.model = Model{wsp<char>(ws, L.model), (uint32_t)L.model_bytes, 0u, (uint32_t)L.slab_b,
+                    (uint32_t)(2 * L.slab_b)};
     const int32_t* t = wsp<int32_t>(ws, L.tables);
     q.s_cell = t + p->t_s_cell; q.s_ptr = t + p->t_s_ptr; q.s_list = t + p->t_s_list; q.s_idx = t + p->t_s_idx;
     q.r_cell = t + p->t_r_cell; q.r_ptr = t + p->t_r_ptr; q.r_list = t + p->t_r_list; q.r_idx = t + p->t_r_idx;
-    q.snapE = wsp<char>(ws, L.snapE); q.snapC = wsp<char>(ws, L.snapC);
+    q.snapE = wsp<char>(ws, L.snapE);
+    q.snapC = wsp<char>(ws, L.snapC);
     q.ckpt = wsp<char>(ws, L.ckpt);
     q.scratch = wsp<float>(ws, L.scratch);
     return q;
 }
 
-// Source/receiver pointers of one step (null when there are none).
-struct StepIO {
-    const float* f;   // [S][n_src] of this step
-    float* r;         // [S][n_rec] of this step
-};
-StepIO step_io(const tm_plan* p, const float* f, float* r, int64_t t)
-{
-    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
-    return StepIO{ns > 0 ? f + t * S * ns : nullptr, (r != nullptr && nr > 0) ? r + t * S * nr : nullptr};
-}
-
-// One forward step t: the fused H/E kernel (set cur -> 1-cur), then the
-// sources and receivers on the new E.
+// One forward step t (set cur -> 1-cur): H and E updates with the snapshot
+// epilogue (se/sc non-null) in one kernel, then sources and receivers.
 template <int P>
-void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* ca, const float* cb, const float* cq,
-              const float* f, float* r, int64_t t, int snap, void* se, void* sc, hipStream_t st)
+void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int64_t t, int snap, char* se,
+              char* sc, hipStream_t st)
 {
     const Layout& L = p->lay;
-    char* s0 = q.base + L.fset[cur];
-    char* s1 = q.base + L.fset[1 - cur];
+    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
     FwdArgs a;
     a.g = p->g;
     a.t = p->tiling_fwd;
-    a.ca = ca; a.cb = cb; a.cq = cq; a.cp = q.cp;
-    a.E0 = reinterpret_cast<const float*>(s0 + L.oE);
-    a.Hx0 = reinterpret_cast<const float*>(s0 + L.oHx);
-    a.Hz0 = reinterpret_cast<const float*>(s0 + L.oHz);
-    a.pez0 = reinterpret_cast<const float*>(s0 + L.opez);
-    a.pex0 = reinterpret_cast<const float*>(s0 + L.opex);
-    a.phxz0 = reinterpret_cast<const float*>(s0 + L.ophxz);
-    a.phzx0 = reinterpret_cast<const float*>(s0 + L.ophzx);
-    a.E1 = reinterpret_cast<float*>(s1 + L.oE);
-    a.Hx1 = reinterpret_cast<float*>(s1 + L.oHx);
-    a.Hz1 = reinterpret_cast<float*>(s1 + L.oHz);
-    a.pez1 = reinterpret_cast<float*>(s1 + L.opez);
-    a.pex1 = reinterpret_cast<float*>(s1 + L.opex);
-    a.phxz1 = reinterpret_cast<float*>(s1 + L.ophxz);
-    a.phzx1 = reinterpret_cast<float*>(s1 + L.ophzx);
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.fset[cur];
+    a.set1 = q.base + L.fset[1 - cur];
     a.snap_e = se;
     a.snap_c = sc;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
     const dim3 grid((unsigned)p->tiling_fwd.nblk), blk(NT);
     timed(p, KID_FWD_STEP, t, st, [&] {
         if (snap == SNAP_F32) k_fwd_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
         else if (snap == SNAP_BF16) k_fwd_step<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
         else k_fwd_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
-    const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
-    const StepIO io = step_io(p, f, r, t);
-    if (io.f != nullptr || io.r != nullptr) {
-        k_fwd_srcrec<<<dim3((unsigned)p->d.n_shots), dim3(256), 0, st>>>(
-            p->g.slab, a.E1, io.f, ns, q.s_cell, q.s_ptr, q.s_list, io.r, nr, q.r_idx);
+    const float* ft = ns > 0 ? f + t * S * ns : nullptr;
+    float* rt = (r != nullptr && nr > 0) ? r + t * S * nr : nullptr;
+    if (ft != nullptr || rt != nullptr) {
+        k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
+            a.set1, L.st.shot_bytes, L.st.oE, ft, (int)ns, q.s_cell, q.s_ptr, q.s_list, rt, (int)nr, q.r_idx);
     }
-}
-
-// Steps t and t+1 in one launch (set cur -> 1-cur), sources and receivers
-// included.  se/sc: snapshot destinations of step t (those of step t+1
-// follow at snap_step bytes), or null.
-template <int P>
-void fwd_step2(tm_plan* p, const Ptrs& q, int cur, const float* ca, const float* cb, const float* cq,
-               const float* f, float* r, int64_t t, int snap, char* se, char* sc, hipStream_t st)
-{
-    const Layout& L = p->lay;
-    char* s0 = q.base + L.fset[cur];
-    char* s1 = q.base + L.fset[1 - cur];
-    Fwd2Args a;
-    a.g = p->g;
-    a.t = p->tiling_fwd2;
-    a.ca = ca; a.cb = cb; a.cq = cq; a.cp = q.cp;
-    a.E0 = reinterpret_cast<const float*>(s0 + L.oE);
-    a.Hx0 = reinterpret_cast<const float*>(s0 + L.oHx);
-    a.Hz0 = reinterpret_cast<const float*>(s0 + L.oHz);
-    a.pez0 = reinterpret_cast<const float*>(s0 + L.opez);
-    a.pex0 = reinterpret_cast<const float*>(s0 + L.opex);
-    a.phxz0 = reinterpret_cast<const float*>(s0 + L.ophxz);
-    a.phzx0 = reinterpret_cast<const float*>(s0 + L.ophzx);
-    a.E1 = reinterpret_cast<float*>(s1 + L.oE);
-    a.Hx1 = reinterpret_cast<float*>(s1 + L.oHx);
-    a.Hz1 = reinterpret_cast<float*>(s1 + L.oHz);
-    a.pez1 = reinterpret_cast<float*>(s1 + L.opez);
-    a.pex1 = reinterpret_cast<float*>(s1 + L.opex);
-    a.phxz1 = reinterpret_cast<float*>(s1 + L.ophxz);
-    a.phzx1 = reinterpret_cast<float*>(s1 + L.ophzx);
-    a.snapA_e = se;
-    a.snapA_c = sc;
-    a.snapB_e = se ? se + L.snap_step : nullptr;
-    a.snapB_c = sc ? sc + L.snap_step : nullptr;
-    const StepIO io0 = step_io(p, f, r, t), io1 = step_io(p, f, r, t + 1);
-    a.fA = io0.f; a.fB = io1.f; a.rA = io0.r; a.rB = io1.r;
-    const int32_t* tb = reinterpret_cast<const int32_t*>(q.base + L.tables);
-    a.ev.row = p->has_events ? tb + p->t_ev_row : nullptr;
-    a.ev.col = tb + p->t_ev_col;
-    a.ev.sp = tb + p->t_ev_sp;
-    a.ev.src = tb + p->t_ev_src;
-    a.ev.rp = tb + p->t_ev_rp;
-    a.ev.rec = tb + p->t_ev_rec;
-    a.ev.n_src = (int)p->d.n_src;
-    a.ev.n_rec = (int)p->d.n_rec;
-    const dim3 grid((unsigned)p->tiling_fwd2.nblk), blk(NT);
-    timed(p, KID_FWD_STEP2, t, st, [&] {
-        if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
-        else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
-        else k_fwd_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
-    });
 }
 
 // One adjoint step t; k counts the adjoint steps taken (set k%2 -> (k+1)%2).
 template <int P>
-void adj_step(tm_plan* p, const Ptrs& q, const float* ca, const float* cb, const float* cq,
-              const float* grad_r, float* grad_f, int64_t t, int64_t k, int snap, const void* se,
-              const void* sc, float* gca, float* gcb, hipStream_t st)
+void adj_step(tm_plan* p, const Ptrs& q, const float* grad_r, float* grad_f, int64_t t, int64_t k, int snap,
+              const char* se, const char* sc, float* gca, float* gcb, hipStream_t st)
 {
     const Layout& L = p->lay;
-    const int64_t S = p->d.n_shots;
-    const int ns = (int)p->d.n_src, nr = (int)p->d.n_rec;
-    char* s0 = q.base + L.aset[k & 1];
-    char* s1 = q.base + L.aset[(k + 1) & 1];
-    float* lE0 = reinterpret_cast<float*>(s0 + L.olE);
-    if (nr > 0 || (grad_f != nullptr && ns > 0)) {
-        k_adj_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            p->g.slab, lE0, nr > 0 ? grad_r + t * S * nr : nullptr, nr, q.r_cell, q.r_ptr, q.r_list,
-            (grad_f != nullptr && ns > 0) ? grad_f + t * S * ns : nullptr, ns, q.s_idx);
-    }
+    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
     AdjArgs a;
     a.g = p->g;
     a.t = p->tiling_adj;
-    a.ca = ca; a.cb = cb; a.cq = cq; a.cp = q.cp;
-    a.lE0 = lE0;
-    a.lHx0 = reinterpret_cast<const float*>(s0 + L.olHx);
-    a.lHz0 = reinterpret_cast<const float*>(s0 + L.olHz);
-    a.fhzx0 = reinterpret_cast<const float*>(s0 + L.ofhzx);
-    a.fhxz0 = reinterpret_cast<const float*>(s0 + L.ofhxz);
-    a.fex0 = reinterpret_cast<const float*>(s0 + L.ofex);
-    a.fez0 = reinterpret_cast<const float*>(s0 + L.ofez);
-    a.lE1 = reinterpret_cast<float*>(s1 + L.olE);
-    a.lHx1 = reinterpret_cast<float*>(s1 + L.olHx);
-    a.lHz1 = reinterpret_cast<float*>(s1 + L.olHz);
-    a.fhzx1 = reinterpret_cast<float*>(s1 + L.ofhzx);
-    a.fhxz1 = reinterpret_cast<float*>(s1 + L.ofhxz);
-    a.fex1 = reinterpret_cast<float*>(s1 + L.ofex);
-    a.fez1 = reinterpret_cast<float*>(s1 + L.ofez);
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.aset[k & 1];
+    a.set1 = q.base + L.aset[(k + 1) & 1];
+    const float* grt = nr > 0 ? grad_r + t * S * nr : nullptr;
+    float* gft = (grad_f != nullptr && ns > 0) ? grad_f + t * S * ns : nullptr;
+    if (grt != nullptr || gft != nullptr) {
+        k_adj_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
+            q.base + L.aset[k & 1], L.st.shot_bytes, L.st.oE, grt, (int)nr, q.r_cell, q.r_ptr, q.r_list, gft, (int)ns, q.s_idx);
+    }
     a.snap_e = se;
     a.snap_c = sc;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
     a.gca = gca;
     a.gcb = gcb;
     const dim3 grid((unsigned)p->tiling_adj.nblk), blk(NT);
@@ -556,13 +442,19 @@ tm_status check_ws(const tm_plan* p, void* ws, uint64_t ws_bytes)
 }
 
 // Resident workgroups of one step kernel on the current device.
+// Target workgroups per CU for the step kernels: more resident workgroups
+// than this only shorten the chunks (more halo rows re-read) without
+// raising the bandwidth of this access pattern (measured on MI355X at the
+// order-8, 1096^2 x 16-shot size: 5 per CU beat 4 and 7).
+constexpr int WG_PER_CU = 5;
+
 tm_status resident(const void* fn, int64_t* cap)
 {
     int dev = 0, ncu = 0, nb = 0;
     HIPCHK(hipGetDevice(&dev));
     HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
     HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, NT, 0));
-    *cap = (int64_t)std::max(nb, 1) * std::max(ncu, 1);
+    *cap = (int64_t)std::min(std::max(nb, 1), WG_PER_CU) * std::max(ncu, 1);
     return TM_OK;
 }
 
@@ -581,55 +473,37 @@ tm_status device_tiling(tm_plan* p)
     v = resident(bf ? reinterpret_cast<const void*>(&k_adj_step<P, SNAP_BF16>)
                     : reinterpret_cast<const void*>(&k_adj_step<P, SNAP_F32>), &ca);
     if (v != TM_OK) return v;
-    int64_t c2 = 0;
-    v = resident(bf ? reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_BF16>)
-                    : reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_F32>), &c2);
-    if (v != TM_OK) return v;
-    p->tiling_fwd = make_tiling(p->d, P, cf, NT - 4 * P + 2);
-    p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W);
-    p->tiling_adj = make_tiling(p->d, P, ca, NT - 4 * P + 2);
+    p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W);
+    p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W);
     p->tiling_device = dev;
     return TM_OK;
 }
 
 // Forward steps [t0, t1) from set *cur (updated).  snap: SNAP_* kind of the
-// stored steps; snap_base(t) gives the destinations of step t (null: none).
-// ckpt: save the state every K steps into the checkpoint slots.  Steps are
-// taken two per launch, except a last odd step and the step before a
-// checkpoint time.
+// stored steps, whose destinations snap_at(t, se, sc) gives; ckpt: save the
+// state at every multiple of K into the checkpoint slots.
 template <int P, typename SnapAt>
-tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* ca, const float* cb,
-                        const float* cq, const float* f, float* r, int64_t t0, int64_t t1, int snap,
-                        SnapAt snap_at, bool ckpt, hipStream_t st)
+tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, float* r, int64_t t0, int64_t t1,
+                        int snap, SnapAt snap_at, bool ckpt, hipStream_t st)
 {
-    const int64_t K = p->K;
-    const bool two = !p->single_step;
-    int64_t t = t0;
-    while (t < t1) {
-        if (ckpt && t > 0 && t % K == 0) {
-            const int64_t slot = t / K - 1;
+    for (int64_t t = t0; t < t1; ++t) {
+        if (ckpt && t > 0 && t % p->K == 0) {
+            const int64_t slot = t / p->K - 1;
             HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, q.base + p->lay.fset[*cur],
                                   p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
         }
-        const bool pair = two && t + 1 < t1 && !(ckpt && (t + 1) % K == 0);
         char* se = nullptr;
         char* sc = nullptr;
         if (snap != SNAP_NONE) snap_at(t, se, sc);
-        if (pair) {
-            fwd_step2<P>(p, q, *cur, ca, cb, cq, f, r, t, snap, se, sc, st);
-            t += 2;
-        } else {
-            fwd_step<P>(p, q, *cur, ca, cb, cq, f, r, t, snap, se, sc, st);
-            t += 1;
-        }
+        fwd_step<P>(p, q, *cur, f, r, t, snap, se, sc, st);
         *cur = 1 - *cur;
     }
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
 
 template <int P>
-tm_status run_forward(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq,
-                      const float* f, float* r, int64_t t0, int64_t t1, bool store, hipStream_t st)
+tm_status run_forward(tm_plan* p, void* ws, const float* f, float* r, int64_t t0, int64_t t1, bool store,
+                      hipStream_t st)
 {
     tm_status v = device_tiling<P>(p);
     if (v != TM_OK) return v;
@@ -640,13 +514,12 @@ tm_status run_forward(tm_plan* p, void* ws, const float* ca, const float* cb, co
         se = q.snapE + t * p->lay.snap_step;
         sc = q.snapC + t * p->lay.snap_step;
     };
-    return forward_range<P>(p, q, &p->fwd_cur, ca, cb, cq, f, r, t0, t1, snap, at, store && !full, st);
+    return forward_range<P>(p, q, &p->fwd_cur, f, r, t0, t1, snap, at, store && !full, st);
 }
 
 template <int P>
-tm_status run_adjoint(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq,
-                      const float* f, const float* grad_r, float* grad_f, float* gca, float* gcb,
-                      hipStream_t st)
+tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r, float* grad_f, float* gca,
+                      float* gcb, hipStream_t st)
 {
     tm_status v = device_tiling<P>(p);
     if (v != TM_OK) return v;
@@ -657,8 +530,8 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* ca, const float* cb, co
     int64_t k = 0;
     if (p->K == 0 || !want_grad) {
         for (int64_t t = nt - 1; t >= 0; --t, ++k) {
-            const uint64_t so = want_grad ? (uint64_t)t * p->lay.snap_step : 0;
-            adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, k, snap, want_grad ? q.snapE + so : nullptr,
+            const uint64_t so = (uint64_t)t * p->lay.snap_step;
+            adj_step<P>(p, q, grad_r, grad_f, t, k, snap, want_grad ? q.snapE + so : nullptr,
                         want_grad ? q.snapC + so : nullptr, gca, gcb, st);
         }
     } else {
@@ -677,10 +550,10 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* ca, const float* cb, co
                 se = q.snapE + (t - ta) * p->lay.snap_step;
                 sc = q.snapC + (t - ta) * p->lay.snap_step;
             };
-            v = forward_range<P>(p, q, &cur, ca, cb, cq, f, nullptr, ta, tb, snap, at, false, st);
+            v = forward_range<P>(p, q, &cur, f, nullptr, ta, tb, snap, at, false, st);
             if (v != TM_OK) return v;
             for (int64_t t = tb - 1; t >= ta; --t, ++k)
-                adj_step<P>(p, q, ca, cb, cq, grad_r, grad_f, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
+                adj_step<P>(p, q, grad_r, grad_f, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
                             q.snapC + (t - ta) * p->lay.snap_step, gca, gcb, st);
         }
     }
@@ -737,9 +610,8 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16) return TM_EINVAL;
-    if (d.time_block < 0 || d.time_block > 2 || d.reserved != 0) return TM_EINVAL;
     if (d.ny < 2 * P + 2 || d.nx < 2 * P + 2) return TM_EINVAL;
-    if (d.ny * d.nx >= (int64_t(1) << 29)) return TM_EINVAL;   // per-shot slabs < 2 GiB (buffer views)
+    if (d.ny * d.nx >= (int64_t(1) << 29)) return TM_EINVAL;
     if (d.n_shots * std::max<int64_t>(d.n_src, d.n_rec) >= (int64_t(1) << 31)) return TM_EINVAL;
     if (d.n_shots > 65535) return TM_EINVAL;
     if (!(d.dy > 0.0) || !(d.dx > 0.0) || !std::isfinite(d.dy) || !std::isfinite(d.dx)) return TM_EINVAL;
@@ -776,21 +648,15 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     g.slab = d.ny * d.nx;
     p->cpml.assign(cpml, cpml + 12 * L);
 
-    const Scatter ss = build_scatter(src, d.n_shots, d.n_src);
-    const Scatter rs = build_scatter(rec, d.n_shots, d.n_rec);
     auto append = [&](const std::vector<int32_t>& v) {
         const uint64_t at = p->tables.size();
         p->tables.insert(p->tables.end(), v.begin(), v.end());
         return at;
     };
+    const Scatter ss = build_scatter(src, d.n_shots, d.n_src);
+    const Scatter rs = build_scatter(rec, d.n_shots, d.n_rec);
     p->t_s_cell = append(ss.cell); p->t_s_ptr = append(ss.ptr); p->t_s_list = append(ss.list); p->t_s_idx = append(ss.idx);
     p->t_r_cell = append(rs.cell); p->t_r_ptr = append(rs.ptr); p->t_r_list = append(rs.list); p->t_r_idx = append(rs.idx);
-    const EventTables ev = build_events(src, d.n_src, rec, d.n_rec, d.n_shots, d.ny, d.nx);
-    p->has_events = ev.any;
-    p->t_ev_row = append(ev.row); p->t_ev_col = append(ev.col);
-    p->t_ev_sp = append(ev.sp); p->t_ev_src = append(ev.src);
-    p->t_ev_rp = append(ev.rp); p->t_ev_rec = append(ev.rec);
-    p->single_step = d.time_block != 2;
 
     if (d.ckpt_every > 0 && d.ckpt_every < d.nt) {
         p->K = d.ckpt_every;
@@ -804,7 +670,10 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         p->seg_steps = d.nt;
     }
     p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024, NT - 4 * P + 2);
-    make_layout(p);
+    if (!make_layout(p)) {
+        delete p;
+        return TM_EINVAL;
+    }
     if (d.hbm_budget > 0 && p->lay.total > d.hbm_budget) {
         delete p;
         return TM_ENOMEM;
@@ -900,8 +769,8 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
         if (v != TM_OK) return v;
         if (!(c <= 1.0)) return TM_EUNSTABLE;
     }
-    v = upload_tables(p, ws, st);
-    if (v != TM_OK) return v;
+    if ((v = upload_tables(p, ws, st)) != TM_OK) return v;
+    if ((v = stage_model(p, ws, ca, cb, cq, st)) != TM_OK) return v;
     if (t0 == 0) {
         p->fwd_complete = false;
         v = zero(wsp<float>(ws, p->lay.fwd), p->lay.fwd_bytes, st);
@@ -914,9 +783,9 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     p->ws_last = ws;
     p->fwd_next = -1;
     switch (p->P) {
-    case 1: v = run_forward<1>(p, ws, ca, cb, cq, f, r, t0, t1, store, st); break;
-    case 2: v = run_forward<2>(p, ws, ca, cb, cq, f, r, t0, t1, store, st); break;
-    default: v = run_forward<4>(p, ws, ca, cb, cq, f, r, t0, t1, store, st); break;
+    case 1: v = run_forward<1>(p, ws, f, r, t0, t1, store, st); break;
+    case 2: v = run_forward<2>(p, ws, f, r, t0, t1, store, st); break;
+    default: v = run_forward<4>(p, ws, f, r, t0, t1, store, st); break;
     }
     if (v != TM_OK) return v;
     p->fwd_next = t1;
@@ -938,17 +807,17 @@ TM_API tm_status tm_adjoint(tm_plan* p, void* ws, uint64_t ws_bytes, const float
         if (p->K > 0 && p->d.n_src > 0 && f == nullptr) return TM_EINVAL;
     }
     hipStream_t st = as_stream(stream);
-    v = upload_tables(p, ws, st);
-    if (v != TM_OK) return v;
+    if ((v = upload_tables(p, ws, st)) != TM_OK) return v;
+    if ((v = stage_model(p, ws, ca, cb, cq, st)) != TM_OK) return v;
     v = zero(wsp<float>(ws, p->lay.adj), p->lay.adj_bytes, st);
     if (v != TM_OK) return v;
     const uint64_t gbytes = (uint64_t)p->d.n_shots * (uint64_t)p->g.slab * 4;
     if (grad_ca_shot && (v = zero(grad_ca_shot, gbytes, st)) != TM_OK) return v;
     if (grad_cb_shot && (v = zero(grad_cb_shot, gbytes, st)) != TM_OK) return v;
     switch (p->P) {
-    case 1: v = run_adjoint<1>(p, ws, ca, cb, cq, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
-    case 2: v = run_adjoint<2>(p, ws, ca, cb, cq, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
-    default: v = run_adjoint<4>(p, ws, ca, cb, cq, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
+    case 1: v = run_adjoint<1>(p, ws, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
+    case 2: v = run_adjoint<2>(p, ws, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
+    default: v = run_adjoint<4>(p, ws, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
     }
     if (v != TM_OK) return v;
     if (p->K > 0 && want_grad) p->fwd_next = -1;   // the replay overwrote the forward state

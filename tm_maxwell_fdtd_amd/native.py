@@ -37,8 +37,6 @@ class tm_desc(ctypes.Structure):
     _fields_ = [
         ("order", ctypes.c_int32),
         ("snap", ctypes.c_int32),
-        ("time_block", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
         ("n_shots", ctypes.c_int64),
         ("ny", ctypes.c_int64), ("nx", ctypes.c_int64),
         ("pml_y0", ctypes.c_int64), ("pml_y1", ctypes.c_int64),
@@ -195,11 +193,9 @@ def tm_timing_read(plan):
 
 # ---- convenience layer (still marshalling only) -----------------------------
 
-def make_desc(wl, snap: Optional[str] = None, ckpt_every: Optional[int] = None, hbm_budget: int = 0,
-              time_block: int = 0) -> tm_desc:
+def make_desc(wl, snap: Optional[str] = None, ckpt_every: Optional[int] = None, hbm_budget: int = 0) -> tm_desc:
     snap = wl.snap if snap is None else snap
     return tm_desc(order=wl.order, snap=TM_SNAP_BF16 if snap == "bf16" else TM_SNAP_F32,
-                   time_block=time_block, reserved=0,
                    n_shots=wl.n_shots, ny=wl.ny, nx=wl.nx,
                    pml_y0=wl.pml_y0, pml_y1=wl.pml_y1, pml_x0=wl.pml_x0, pml_x1=wl.pml_x1,
                    dy=wl.dy, dx=wl.dx, nt=wl.nt, n_src=wl.n_src, n_rec=wl.n_rec,
@@ -215,12 +211,12 @@ class Propagator:
     tensors; the model arrays are passed at construction.
     """
 
-    def __init__(self, wl, device="cuda", snap=None, ckpt_every=None, hbm_budget=0, time_block=0):
+    def __init__(self, wl, device="cuda", snap=None, ckpt_every=None, hbm_budget=0):
         import torch
 
         self.wl = wl
         self.device = torch.device(device)
-        self.desc = make_desc(wl, snap, ckpt_every, hbm_budget, time_block)
+        self.desc = make_desc(wl, snap, ckpt_every, hbm_budget)
         st, plan = tm_plan_create(self.desc, wl.cpml, wl.src, wl.rec)
         _check(st, "tm_plan_create")
         self.plan = plan
