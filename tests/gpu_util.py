@@ -78,3 +78,45 @@ def gpu_observed(wl):
         return r.cpu().numpy()
     finally:
         prop.close()
+
+
+def sub_workload(wl, shots, nt=None):
+    """The same problem restricted to some shots and the first ``nt`` steps.
+
+    Shots are independent and the first nt records of a run do not depend on
+    later steps, so the oracle can check sampled outputs of a full-size run.
+    """
+    import dataclasses
+
+    shots = list(shots)
+    nt = wl.nt if nt is None else nt
+    return dataclasses.replace(wl, n_shots=len(shots), nt=nt, f=wl.f[:nt, shots].copy(),
+                               src=wl.src[shots].copy(), rec=wl.rec[shots].copy())
+
+
+def run_gpu_window(wl, t_window=None):
+    """Full-size GPU run: forward with storage, then the adjoint of
+    J = 1/2 |r|^2 restricted to time steps t < t_window (grad_r = r there,
+    0 later; None = all steps), the shot sum, and the residual used."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    prop = native.Propagator(wl)
+    try:
+        r = prop.forward(store=True)
+        resid = r.clone()
+        if t_window is not None:
+            resid[t_window:] = 0
+        grad_f, gca, gcb = prop.adjoint(resid)
+        ga, gb = prop.grad(gca, gcb)
+        torch.cuda.synchronize()
+        out = dict(records=r.cpu().numpy(), grad_f=grad_f.cpu().numpy(), gca_shot=gca.cpu().numpy(),
+                   gcb_shot=gcb.cpu().numpy(), gca=ga.cpu().numpy(), gcb=gb.cpu().numpy(),
+                   residual=resid.cpu().numpy())
+        del r, resid, grad_f, gca, gcb, ga, gb
+    finally:
+        prop.close()
+        del prop
+        torch.cuda.empty_cache()
+    return out

@@ -243,7 +243,6 @@ def smooth_random(rng, n_int, smooth, lo, hi):
 def paint_ellipses(rng, eps, sig, count, ax_lo, ax_hi, eps_lo, eps_hi, sig_lo, sig_hi):
     """Paint ``count`` rotated ellipses, in order, onto the interior models."""
     n = eps.shape[0]
-    yy, xx = np.mgrid[0:n, 0:n].astype(np.float64)
     for _ in range(count):
         cy, cx = rng.uniform(0, n, size=2)
         a_ax, b_ax = rng.uniform(ax_lo, ax_hi, size=2)
@@ -251,11 +250,18 @@ def paint_ellipses(rng, eps, sig, count, ax_lo, ax_hi, eps_lo, eps_hi, sig_lo, s
         e_val = rng.uniform(eps_lo, eps_hi)
         s_val = rng.uniform(sig_lo, sig_hi)
         c, s = math.cos(th), math.sin(th)
+        # only the bounding box of the ellipse can hold inside points
+        rad = max(a_ax, b_ax) + 1.0
+        ylo, yhi = max(0, int(cy - rad)), min(n, int(cy + rad) + 1)
+        xlo, xhi = max(0, int(cx - rad)), min(n, int(cx + rad) + 1)
+        if ylo >= yhi or xlo >= xhi:
+            continue
+        yy, xx = np.mgrid[ylo:yhi, xlo:xhi].astype(np.float64)
         u = (xx - cx) * c + (yy - cy) * s
         v = -(xx - cx) * s + (yy - cy) * c
         inside = (u / a_ax) ** 2 + (v / b_ax) ** 2 <= 1.0
-        eps[inside] = e_val
-        sig[inside] = s_val
+        eps[ylo:yhi, xlo:xhi][inside] = e_val
+        sig[ylo:yhi, xlo:xhi][inside] = s_val
     return eps, sig
 
 

@@ -237,6 +237,7 @@ class Propagator:
             torch.cuda.synchronize(self.device)
             tm_plan_destroy(self.plan)
             self.plan = None
+        self.ws = None            # the workspace goes back to torch's allocator
 
     def __del__(self):
         try:
