@@ -159,6 +159,29 @@ tm_status tm_grad(const tm_plan* plan, const float* grad_ca_shot, const float* g
                   float* grad_ca, float* grad_cb, void* stream);
 
 /*
+ * Gradients in the physical parameters by the chain rule
+ * (convert_grad_ca_cb_to_eps_sigma): with eps = EP0 eps_r (EP0 =
+ * 8.8541878128e-12 F/m) and s = sigma dt / (2 eps), the update
+ * coefficients are Ca = (1 - s) / (1 + s) and Cb = (dt / eps) / (1 + s), so
+ *   dJ/deps_r  = EP0 (dJ/dCa (1 - Ca) Cb / dt - dJ/dCb Cb^2 / dt),
+ *   dJ/dsigma  = -dJ/dCa (1 + Ca) Cb / 2 - dJ/dCb Cb^2 / 2,
+ * per cell, in float32.  Cq (the magnetic coefficient) is not involved.
+ *   ca, cb: device float32 [ny][nx], the coefficients the gradients were
+ *      taken at (required).
+ *   grad_ca, grad_cb: device float32 [ny][nx] (e.g. tm_grad's outputs); a
+ *      NULL input counts as zero.
+ *   dt: the time step (seconds) the coefficients were built with; must be
+ *      finite and > 0 (TM_EINVAL otherwise).
+ *   grad_eps_r, grad_sigma: device float32 [ny][nx], overwritten; a NULL
+ *      output is skipped (both NULL: nothing is launched).
+ * The result is exact for coefficients of the form above; for other Ca/Cb
+ * it is the chain rule of that form evaluated at the given values.
+ */
+tm_status tm_grad_eps_sigma(const tm_plan* plan, const float* ca, const float* cb,
+                            const float* grad_ca, const float* grad_cb, double dt,
+                            float* grad_eps_r, float* grad_sigma, void* stream);
+
+/*
  * Kernel timing, a diagnostic for roofline figures.  With sampling on
  * (every > 0), every ``every``-th time step of tm_forward and tm_adjoint
  * brackets each of its stencil-kernel launches with a pair of HIP events

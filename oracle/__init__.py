@@ -69,6 +69,8 @@ def lib():
                                   _dp, _dp, _dp, _dp, _dp, _dp]
         L.orc_shot_sum.restype = None
         L.orc_shot_sum.argtypes = [_ll, _ll, _dp, _dp]
+        L.orc_eps_sigma_grad.restype = None
+        L.orc_eps_sigma_grad.argtypes = [_ll, _dp, _dp, ctypes.c_double, _dp, _dp, _dp, _dp]
         L.orc_num_threads.restype = ctypes.c_int
         L.orc_num_threads.argtypes = []
         L.orc_coefficients.restype = ctypes.c_int
@@ -194,6 +196,20 @@ def shot_sum(grad_shot: np.ndarray) -> np.ndarray:
     out = np.zeros(gs.shape[1:])
     lib().orc_shot_sum(gs.shape[0], int(np.prod(gs.shape[1:])), _d(gs), _d(out))
     return out
+
+
+def eps_sigma_grad(eps_r, sigma, dt, grad_ca, grad_cb):
+    """dJ/deps_r and dJ/dsigma from dJ/dCa and dJ/dCb (chain rule through the
+    coefficient definitions, see ``orc_eps_sigma_grad``).  Shapes are kept."""
+    eps_r = _c64(eps_r)
+    sigma = _c64(sigma)
+    gca = _c64(grad_ca)
+    gcb = _c64(grad_cb)
+    assert eps_r.shape == sigma.shape == gca.shape == gcb.shape
+    ge = np.zeros(eps_r.shape)
+    gs = np.zeros(eps_r.shape)
+    lib().orc_eps_sigma_grad(eps_r.size, _d(eps_r), _d(sigma), float(dt), _d(gca), _d(gcb), _d(ge), _d(gs))
+    return ge, gs
 
 
 def misfit_and_gradient(wl, observed=None):

@@ -420,3 +420,30 @@ void orc_shot_sum(ll n_shots, ll numel, const double *grad_shot, double *grad)
         grad[j] = acc;
     }
 }
+
+/* ---- gradients in the physical parameters ------------------------------- */
+/*
+ * dJ/deps_r and dJ/dsigma from dJ/dCa and dJ/dCb by the chain rule (the
+ * page's convert_grad_ca_cb_to_eps_sigma computes the same quantities from
+ * Ca, Cb and dt).  Written here directly from the coefficient definitions
+ * with eps = EP0 eps_r and D = eps + sigma dt / 2:
+ *     Ca = (eps - sigma dt / 2) / D,      Cb = dt / D,
+ *     dCa/deps   =  sigma dt / D^2,       dCb/deps   = -dt / D^2,
+ *     dCa/dsigma = -eps dt / D^2,         dCb/dsigma = -dt^2 / (2 D^2),
+ * and d/deps_r = EP0 d/deps.  Either output may be NULL.
+ */
+void orc_eps_sigma_grad(ll n, const double *eps_r, const double *sigma, double dt,
+                        const double *grad_ca, const double *grad_cb,
+                        double *grad_eps_r, double *grad_sigma)
+{
+    const double ep0 = 8.8541878128e-12;
+    for (ll j = 0; j < n; ++j) {
+        const double eps = ep0 * eps_r[j];
+        const double D = eps + 0.5 * sigma[j] * dt;
+        const double D2 = D * D;
+        const double dca_de = sigma[j] * dt / D2, dcb_de = -dt / D2;
+        const double dca_ds = -eps * dt / D2, dcb_ds = -0.5 * dt * dt / D2;
+        if (grad_eps_r) grad_eps_r[j] = ep0 * (grad_ca[j] * dca_de + grad_cb[j] * dcb_de);
+        if (grad_sigma) grad_sigma[j] = grad_ca[j] * dca_ds + grad_cb[j] * dcb_ds;
+    }
+}

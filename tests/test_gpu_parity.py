@@ -214,3 +214,51 @@ def test_error_codes_on_device():
     finally:
         prop.close()
 
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_grad_eps_sigma(orc, order):
+    """tm_grad_eps_sigma against the oracle's chain rule, on the GPU's own
+    dJ/dCa, dJ/dCb (isolates the chain rule) and end to end (the oracle's
+    fp64 gradients through the oracle's chain rule)."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.random_workload(order, 40, 8, nt=120, n_shots=2, n_src=1, n_rec=7,
+                                              seed=500 + order, sig_range=(0.0, 0.04)))
+    ref = run_oracle(orc, wl)
+    prop = native.Propagator(wl)
+    try:
+        r = prop.forward(store=True)
+        resid = torch.as_tensor(np.asarray(ref["residual"], np.float32), device=prop.device)
+        _, gca_s, gcb_s = prop.adjoint(resid)
+        gca, gcb = prop.grad(gca_s, gcb_s)
+        geps, gsig = prop.grad_eps_sigma(gca, gcb)
+        # a null output is skipped, a null input counts as zero
+        geps_a, gsig_a = prop.grad_eps_sigma(gca, None)
+        st = native.tm_grad_eps_sigma(prop.plan, native.ptr(prop.ca), native.ptr(prop.cb), native.ptr(gca),
+                                      native.ptr(gcb), 0.0, native.ptr(geps_a), None, native.stream_handle())
+        assert st == native.TM_EINVAL
+        torch.cuda.synchronize()
+        g_ca, g_cb = gca.cpu().numpy().astype(np.float64), gcb.cpu().numpy().astype(np.float64)
+        got_e, got_s = geps.cpu().numpy(), gsig.cpu().numpy()
+        got_ea, got_sa = geps_a.cpu().numpy(), gsig_a.cpu().numpy()
+        del r
+    finally:
+        prop.close()
+    # the chain rule alone, on identical float32 inputs
+    ce, cs = orc.eps_sigma_grad(wl.eps_r, wl.sigma, wl.dt, g_ca, g_cb)
+    e1, s1 = rel_l2(got_e, ce), rel_l2(got_s, cs)
+    ce_a, cs_a = orc.eps_sigma_grad(wl.eps_r, wl.sigma, wl.dt, g_ca, np.zeros_like(g_cb))
+    e2, s2 = rel_l2(got_ea, ce_a), rel_l2(got_sa, cs_a)
+    # end to end against the oracle's gradients
+    oe, os_ = orc.eps_sigma_grad(wl.eps_r, wl.sigma, wl.dt, ref["gca"], ref["gcb"])
+    e3, s3 = rel_l2(got_e, oe), rel_l2(got_s, os_)
+    print(f"[eps/sigma o{order}] chain rule {e1:.2e} {s1:.2e}  (Cb input null) {e2:.2e} {s2:.2e}  "
+          f"end to end {e3:.2e} {s3:.2e}", flush=True)
+    assert max(e1, s1, e2, s2) <= 1e-5
+    assert max(e3, s3) <= GRAD_TOL["f32"]
+    mask = np.zeros((wl.ny, wl.nx), bool)
+    mask[wl.pml_y0:wl.pml_y1, wl.pml_x0:wl.pml_x1] = True
+    assert not np.any(got_e[~mask]) and not np.any(got_s[~mask])

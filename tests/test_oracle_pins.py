@@ -12,7 +12,9 @@ Each test fixes one part of the oracle by something independent of it:
     E-update difference operator is minus the transpose of the H-update one,
     and that Cb and Cq enter as per-cell weights at their own cells);
   * the adjoint dot test <F f, d> = <f, F^T d> with the CPML on;
-  * central finite differences of the misfit for the Ca and Cb gradients;
+  * central finite differences of the misfit for the Ca and Cb gradients,
+    and for the eps_r / sigma gradients of the chain rule (whose partials
+    are also checked against differences of the coefficient definitions);
   * CPML absorption against a reflection-free larger domain;
   * brute-force properties (chunking, shot batching, duplicate sources,
     negative indices, record timing).
@@ -332,3 +334,66 @@ def test_duplicate_sources_add_and_negative_indices_skip(orc):
     d2[:, 0, 1:] = 0.0
     gf2, _, _ = orc.adjoint(wl, d2)
     np.testing.assert_allclose(gf1, gf2, rtol=1e-13, atol=1e-300)
+
+
+def test_eps_sigma_partials_match_coefficient_differences(orc):
+    """Each partial derivative of the chain rule against central differences
+    of the coefficient definitions (``inputs.update_coefficients``)."""
+    rng = np.random.default_rng(5)
+    n = 64
+    eps_r = rng.uniform(1.0, 30.0, n)
+    sigma = rng.uniform(0.0, 0.05, n)
+    sigma[:4] = 0.0
+    mu_r = np.ones(n)
+    dt = 7.3e-12
+    one, zero = np.ones(n), np.zeros(n)
+    # unit upstream gradients pick out single partials
+    dca_de, dca_ds = orc.eps_sigma_grad(eps_r, sigma, dt, one, zero)
+    dcb_de, dcb_ds = orc.eps_sigma_grad(eps_r, sigma, dt, zero, one)
+    he = 1e-4 * eps_r
+    hs = 1e-4 * np.maximum(sigma, 1e-3)
+    cap, cbp, _ = inputs.update_coefficients(eps_r + he, sigma, mu_r, dt)
+    cam, cbm, _ = inputs.update_coefficients(eps_r - he, sigma, mu_r, dt)
+    np.testing.assert_allclose(dca_de, (cap - cam) / (2 * he), rtol=1e-7, atol=1e-12 * np.abs(dcb_de).max())
+    np.testing.assert_allclose(dcb_de, (cbp - cbm) / (2 * he), rtol=1e-7)
+    cap, cbp, _ = inputs.update_coefficients(eps_r, sigma + hs, mu_r, dt)
+    cam, cbm, _ = inputs.update_coefficients(eps_r, sigma - hs, mu_r, dt)
+    np.testing.assert_allclose(dca_ds, (cap - cam) / (2 * hs), rtol=1e-7)
+    np.testing.assert_allclose(dcb_ds, (cbp - cbm) / (2 * hs), rtol=1e-7)
+    # lossless cells: Ca does not depend on eps_r
+    assert np.all(dca_de[:4] == 0.0)
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_eps_sigma_gradient_matches_central_differences(orc, order):
+    """dJ/deps_r and dJ/dsigma of the full misfit against central differences
+    of J with the coefficients rebuilt from the perturbed eps_r / sigma."""
+    wl = inputs.random_workload(order, 16, 8, nt=180, n_shots=2, n_src=1, n_rec=6, seed=47)
+    d = np.random.default_rng(11).standard_normal((wl.nt, wl.n_shots, wl.n_rec)) * 1e-3
+    res = orc.misfit_and_gradient(wl, observed=d)
+    ge, gs = orc.eps_sigma_grad(wl.eps_r, wl.sigma, wl.dt, res["gca"], res["gcb"])
+
+    def J(eps_r, sigma):
+        ca, cb, _ = inputs.update_coefficients(eps_r, sigma, wl.mu_r, wl.dt)
+        r, _, _ = orc.forward(wl, ca=ca, cb=cb)
+        return 0.5 * float(np.sum((r - d) ** 2))
+
+    rng = np.random.default_rng(100 + order)
+    ys = rng.integers(wl.pml_y0, wl.pml_y1, size=6)
+    xs = rng.integers(wl.pml_x0, wl.pml_x1, size=6)
+    for name, g, base in (("eps_r", ge, wl.eps_r), ("sigma", gs, wl.sigma)):
+        gmax = np.abs(g).max()
+        for y, x in zip(ys, xs):
+            h = 1e-5 * max(abs(base[y, x]), 1e-2)
+            plus, minus = base.copy(), base.copy()
+            plus[y, x] += h
+            minus[y, x] -= h
+            if name == "eps_r":
+                fd = (J(plus, wl.sigma) - J(minus, wl.sigma)) / (2 * h)
+            else:
+                fd = (J(wl.eps_r, plus) - J(wl.eps_r, minus)) / (2 * h)
+            assert abs(fd - g[y, x]) <= 1e-6 * gmax + 1e-6 * abs(fd), (name, y, x, fd, g[y, x])
+    # outside the interior window the model gradients, hence these, vanish
+    mask = np.zeros((wl.ny, wl.nx), bool)
+    mask[wl.pml_y0:wl.pml_y1, wl.pml_x0:wl.pml_x1] = True
+    assert np.all(ge[~mask] == 0.0) and np.all(gs[~mask] == 0.0)

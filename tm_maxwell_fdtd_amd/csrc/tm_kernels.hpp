@@ -1,7 +1,8 @@
 // Small kernels around the time-step kernels: source injection and
 // receiver gather and their adjoints, the gradient shot sum (tide-GPR
-// 0.0.9, maxwell.cu: combine_grad), a fill kernel and the Courant-number
-// reduction (gfx950, wave64).
+// 0.0.9, maxwell.cu: combine_grad), the chain rule to eps_r / sigma
+// gradients, a fill kernel and the Courant-number reduction (gfx950,
+// wave64).
 #pragma once
 
 #include "tm_common.hpp"
@@ -89,6 +90,38 @@ __global__ __launch_bounds__(256) void k_shot_sum(int64_t slab, int n_shots,
     out[j] = acc;
 }
 
+// Gradients in the physical parameters (tide-GPR 0.0.9, maxwell.cu:
+// convert_grad_ca_cb_to_eps_sigma).  With s = sigma dt / (2 eps) and
+// eps = EP0 eps_r, Ca = (1 - s) / (1 + s) and Cb = (dt / eps) / (1 + s), so
+//   dCa/deps = (1 - Ca) Cb / dt,  dCb/deps = -Cb^2 / dt,
+//   dCa/dsigma = -(1 + Ca) Cb / 2,  dCb/dsigma = -Cb^2 / 2,
+// and dJ/deps_r = EP0 (gCa dCa/deps + gCb dCb/deps).  A null gradient input
+// counts as zero; a null output is skipped.
+// ---------------------------------------------------------------------------
+constexpr float EP0 = 8.8541878128e-12f;
+
+__global__ __launch_bounds__(256) void k_eps_sigma(int64_t n, const float* __restrict__ ca,
+                                                   const float* __restrict__ cb,
+                                                   const float* __restrict__ gca,
+                                                   const float* __restrict__ gcb, float inv_dt,
+                                                   float* __restrict__ geps, float* __restrict__ gsig)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride) {
+        const float a = ca[j], b = cb[j];
+        const float ga = gca != nullptr ? gca[j] : 0.0f;
+        const float gb = gcb != nullptr ? gcb[j] : 0.0f;
+        const float b2 = b * b;
+        const float dca_de = (1.0f - a) * b * inv_dt;
+        const float dcb_de = -b2 * inv_dt;
+        const float dca_ds = -0.5f * (1.0f + a) * b;
+        const float dcb_ds = -0.5f * b2;
+        if (geps != nullptr) geps[j] = (ga * dca_de + gb * dcb_de) * EP0;
+        if (gsig != nullptr) gsig[j] = ga * dca_ds + gb * dcb_ds;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fill with zeros (used instead of memset so callers may capture the calls).
 __global__ __launch_bounds__(256) void k_zero(float* __restrict__ p, int64_t n)
 {

@@ -837,3 +837,18 @@ TM_API tm_status tm_grad(const tm_plan* p, const float* grad_ca_shot, const floa
     if (grad_cb) k_shot_sum<<<grid, blk, 0, st>>>(slab, (int)p->d.n_shots, grad_cb_shot, grad_cb);
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
+
+TM_API tm_status tm_grad_eps_sigma(const tm_plan* p, const float* ca, const float* cb, const float* grad_ca,
+                                   const float* grad_cb, double dt, float* grad_eps_r, float* grad_sigma,
+                                   void* stream)
+{
+    if (p == nullptr || ca == nullptr || cb == nullptr) return TM_EINVAL;
+    if (!(dt > 0.0) || !std::isfinite(dt) || !std::isfinite(1.0 / dt)) return TM_EINVAL;
+    if (grad_eps_r == nullptr && grad_sigma == nullptr) return TM_OK;
+    hipStream_t st = as_stream(stream);
+    const int64_t n = p->g.slab;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    k_eps_sigma<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(n, ca, cb, grad_ca, grad_cb, (float)(1.0 / dt),
+                                                             grad_eps_r, grad_sigma);
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}

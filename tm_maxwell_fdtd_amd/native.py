@@ -77,6 +77,8 @@ def lib():
         L.tm_adjoint.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.tm_grad.restype = ctypes.c_int
         L.tm_grad.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+        L.tm_grad_eps_sigma.restype = ctypes.c_int
+        L.tm_grad_eps_sigma.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp, _vp]
         L.tm_timing_enable.restype = ctypes.c_int
         L.tm_timing_enable.argtypes = [_vp, ctypes.c_int32]
         L.tm_timing_read.restype = ctypes.c_int
@@ -163,6 +165,10 @@ def tm_adjoint(plan, ws, ws_bytes, ca, cb, cq, f, grad_r, grad_f, grad_ca_shot, 
 
 def tm_grad(plan, grad_ca_shot, grad_cb_shot, grad_ca, grad_cb, stream):
     return lib().tm_grad(plan, grad_ca_shot, grad_cb_shot, grad_ca, grad_cb, stream)
+
+
+def tm_grad_eps_sigma(plan, ca, cb, grad_ca, grad_cb, dt, grad_eps_r, grad_sigma, stream):
+    return lib().tm_grad_eps_sigma(plan, ca, cb, grad_ca, grad_cb, dt, grad_eps_r, grad_sigma, stream)
 
 
 def tm_status_string(status: int) -> str:
@@ -288,3 +294,19 @@ class Propagator:
         st = tm_grad(self.plan, ptr(gca_shot), ptr(gcb_shot), ptr(gca), ptr(gcb), stream_handle())
         _check(st, "tm_grad")
         return gca, gcb
+
+    def grad_eps_sigma(self, gca, gcb, dt=None):
+        """dJ/deps_r, dJ/dsigma [ny][nx] from dJ/dCa, dJ/dCb [ny][nx] (either
+        may be None) at this propagator's coefficients; ``dt`` defaults to the
+        workload's time step."""
+        import torch
+
+        wl = self.wl
+        dt = wl.dt if dt is None else dt
+        f32 = dict(dtype=torch.float32, device=self.device)
+        geps = torch.empty((wl.ny, wl.nx), **f32)
+        gsig = torch.empty((wl.ny, wl.nx), **f32)
+        st = tm_grad_eps_sigma(self.plan, ptr(self.ca), ptr(self.cb), ptr(gca), ptr(gcb), float(dt),
+                               ptr(geps), ptr(gsig), stream_handle())
+        _check(st, "tm_grad_eps_sigma")
+        return geps, gsig
