@@ -86,12 +86,17 @@ def kernel_bytes(name, wl, store, snap_bytes):
     same 16 B per band cell and axis for the four adjoint memories, and on
     interior cells the two snapshot reads plus the read-modify-write of the
     two per-shot gradients (16 B).
+    k_fwd_step2 advances two time steps per launch: twice the bytes of
+    k_fwd_step (the per-cell-update figure times the cell-updates of the
+    launch), although the state crosses HBM only once.
     """
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
     if name == "k_fwd_step":
         snaps = 2 * snap_bytes * interior if store else 0
         return S * (36 * cells + 16 * (band_y + band_x) + snaps)
+    if name == "k_fwd_step2":
+        return 2 * kernel_bytes("k_fwd_step", wl, store, snap_bytes)
     if name == "k_adj_step":
         grads = (2 * snap_bytes + 16) * interior if store else 0
         return S * (36 * cells + 16 * (band_y + band_x) + grads)
@@ -282,7 +287,7 @@ def main():
         if n == 0:
             continue
         avg_ms = ms / n
-        launches = wl.nt
+        launches = wl.nt // 2 if name == "k_fwd_step2" else wl.nt
         if name.startswith("k_fwd") and wl.ckpt_every:
             launches *= 2
         # in a full step the forward stores snapshots and the adjoint accumulates gradients

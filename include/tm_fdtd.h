@@ -77,6 +77,10 @@ typedef struct tm_desc {
     int64_t ckpt_every;     /* 0: store every step; K > 0: checkpoint the state
                                every K steps and replay segments in tm_adjoint  */
     uint64_t hbm_budget;    /* bytes the workspace may use; 0 = unlimited       */
+    int32_t time_block;     /* forward time steps per launch: 1, or 2 (two steps
+                               in one pass over the state); 0 = default (2).
+                               Both give bitwise the same results.             */
+    int32_t reserved;       /* must be 0                                        */
 } tm_desc;
 
 typedef struct tm_plan tm_plan;

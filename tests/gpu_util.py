@@ -29,7 +29,7 @@ def run_oracle(orc, wl, observed=None):
     return orc.misfit_and_gradient(wl, observed=observed)
 
 
-def run_gpu(wl, observed=None, snap=None, ckpt_every=None, grad_r=None, obs_coefs=None):
+def run_gpu(wl, observed=None, snap=None, ckpt_every=None, grad_r=None, obs_coefs=None, time_block=0):
     """Forward (storing), residual, adjoint and shot sum on the GPU.
 
     ``observed``: records of the observed model, a numpy array, or the
@@ -40,7 +40,7 @@ def run_gpu(wl, observed=None, snap=None, ckpt_every=None, grad_r=None, obs_coef
 
     from tm_maxwell_fdtd_amd import native
 
-    prop = native.Propagator(wl, snap=snap, ckpt_every=ckpt_every)
+    prop = native.Propagator(wl, snap=snap, ckpt_every=ckpt_every, time_block=time_block)
     try:
         r = prop.forward(store=True)
         if grad_r is not None:

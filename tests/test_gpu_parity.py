@@ -180,6 +180,25 @@ def test_batched_shots_bitwise_equal_single_shots():
         np.testing.assert_array_equal(o["gcb_shot"][0], allr["gcb_shot"][s])
 
 
+@pytest.mark.parametrize("order", inputs.ORDERS)
+@pytest.mark.parametrize("snap,ckpt", [("f32", 0), ("bf16", 0), ("f32", 7)])
+def test_two_step_launch_bitwise_equals_single_steps(order, snap, ckpt):
+    """Two time steps per launch (with the first step's sources and receivers
+    inside the kernel) give bitwise the state, records and gradients of one
+    step per launch; odd nt and an odd checkpoint interval split pairs."""
+    wl = inputs.as_f32(inputs.random_workload(order, 70, 9, nt=101, n_shots=3, n_src=3, n_rec=7,
+                                              seed=700 + order, src_anywhere=True))
+    wl.src[1, 1] = wl.src[1, 0]          # duplicate source cell
+    wl.src[2, 2] = -1
+    wl.rec[0, 3] = wl.rec[0, 2]          # duplicate receiver cell
+    wl.rec[1, 4] = wl.src[1, 0]          # receiver on a source cell
+    wl.rec[2, 0] = -1
+    one = run_gpu(wl, snap=snap, ckpt_every=ckpt, time_block=1)
+    two = run_gpu(wl, snap=snap, ckpt_every=ckpt, time_block=2)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} order {order} {snap} K={ckpt}")
+
+
 def test_error_codes_on_device():
     import torch
 

@@ -58,30 +58,18 @@ __device__ __forceinline__ bool flag_hx(const Geo& g, int x) { return x < g.x0 |
 __device__ __forceinline__ bool flag_hy(const Geo& g, int y) { return y < g.y0 || y >= g.hy1; }
 
 // float -> bfloat16 bits, round to nearest even (NaN kept quiet).
+// Written as a select, not a branch, so it adds no exec-mask changes to the
+// step kernels' row loops.
 __device__ __forceinline__ uint16_t f32_to_bf16(float v)
 {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // Snapshot element types.
 enum SnapKind { SNAP_NONE = 0, SNAP_F32 = 1, SNAP_BF16 = 2 };
-
-template <int SNAP>
-__device__ __forceinline__ void snap_store(void* base, int64_t w, float v)
-{
-    if constexpr (SNAP == SNAP_F32) static_cast<float*>(base)[w] = v;
-    else if constexpr (SNAP == SNAP_BF16) static_cast<uint16_t*>(base)[w] = f32_to_bf16(v);
-}
-template <int SNAP>
-__device__ __forceinline__ float snap_load(const void* base, int64_t w)
-{
-    if constexpr (SNAP == SNAP_F32) return static_cast<const float*>(base)[w];
-    else if constexpr (SNAP == SNAP_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[w]);
-    else return 0.0f;
-}
 
 }  // namespace tmf

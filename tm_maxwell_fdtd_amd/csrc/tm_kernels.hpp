@@ -20,15 +20,27 @@ namespace tmf {
 //   cell/ptr/list: per shot, the distinct cells (padded with -1), CSR offsets
 //   into list, and list = source indices grouped by cell.
 // ---------------------------------------------------------------------------
+//   rec_rows/r_gather/r_prev (optional): after a two-step launch, the
+//   receivers of the launch's first step are gathered from the receiver-row
+//   buffer the step kernel wrote (r_gather = slot * nx + x, or -1).
 __global__ __launch_bounds__(256) void k_fwd_srcrec(char* __restrict__ set, uint64_t shot_bytes, uint32_t oE,
                                                     const float* __restrict__ f_t, int n_src,
                                                     const int* __restrict__ s_cell,
                                                     const int* __restrict__ s_ptr,
                                                     const int* __restrict__ s_list,
                                                     float* __restrict__ r_t, int n_rec,
-                                                    const int* __restrict__ r_idx)
+                                                    const int* __restrict__ r_idx,
+                                                    const float* __restrict__ rec_rows,
+                                                    const int* __restrict__ r_gather,
+                                                    float* __restrict__ r_prev, int n_slots, int nx)
 {
     const int s = blockIdx.x;
+    if (r_prev != nullptr) {
+        for (int i = threadIdx.x; i < n_rec; i += blockDim.x) {
+            const int gidx = r_gather[s * n_rec + i];
+            r_prev[s * n_rec + i] = gidx >= 0 ? rec_rows[(int64_t)s * n_slots * nx + gidx] : 0.0f;
+        }
+    }
     float* e = reinterpret_cast<float*>(set + (uint64_t)s * shot_bytes + oE);
     for (int u = threadIdx.x; u < n_src; u += blockDim.x) {
         const int c = s_cell[s * n_src + u];

@@ -35,6 +35,7 @@
 #include "tm_fdtd.h"
 #include "tm_kernels.hpp"
 #include "tm_step.hpp"
+#include "tm_step2.hpp"
 
 using namespace tmf;
 
@@ -97,6 +98,58 @@ Scatter build_scatter(const int64_t* ids, int64_t S, int64_t n)
     return t;
 }
 
+// Tables of the intermediate step of a two-step launch.
+//   row_cells [S*ny + 1]: CSR over (shot, row) of the distinct source cells
+//     (ascending cell), each with its column and its source indices
+//     (ascending);
+//   rec_slot [S*ny]: slot of each row holding receivers of that shot, or -1;
+//   rec_gather [S][n_rec]: slot * nx + x of each receiver, or -1.
+struct MidTables {
+    std::vector<int32_t> row_cells, cell_x, cell_src, src_list, rec_slot, rec_gather;
+    int n_slots = 0;
+};
+
+MidTables build_mid(const int64_t* src, int64_t n_src, const int64_t* rec, int64_t n_rec, int64_t S, int64_t ny,
+                    int64_t nx)
+{
+    MidTables t;
+    std::vector<int32_t> count(S * ny, 0);
+    std::vector<std::pair<int64_t, int32_t>> v;
+    for (int64_t s = 0; s < S; ++s) {
+        v.clear();
+        for (int64_t i = 0; i < n_src; ++i)
+            if (src[s * n_src + i] >= 0) v.emplace_back(src[s * n_src + i], (int32_t)i);
+        std::stable_sort(v.begin(), v.end(), [](const auto& a, const auto& b) { return a.first < b.first; });
+        for (size_t k = 0; k < v.size(); ++k) {
+            if (k == 0 || v[k].first != v[k - 1].first) {
+                ++count[s * ny + v[k].first / nx];
+                t.cell_x.push_back((int32_t)(v[k].first % nx));
+                t.cell_src.push_back((int32_t)t.src_list.size());
+            }
+            t.src_list.push_back(v[k].second);
+        }
+    }
+    t.cell_src.push_back((int32_t)t.src_list.size());
+    t.row_cells.assign(S * ny + 1, 0);
+    for (int64_t j = 0; j < S * ny; ++j) t.row_cells[j + 1] = t.row_cells[j] + count[j];
+    t.rec_slot.assign(S * ny, -1);
+    t.rec_gather.assign(S * n_rec, -1);
+    for (int64_t s = 0; s < S; ++s) {
+        std::vector<int64_t> rows;
+        for (int64_t j = 0; j < n_rec; ++j)
+            if (rec[s * n_rec + j] >= 0) rows.push_back(rec[s * n_rec + j] / nx);
+        std::sort(rows.begin(), rows.end());
+        rows.erase(std::unique(rows.begin(), rows.end()), rows.end());
+        for (size_t k = 0; k < rows.size(); ++k) t.rec_slot[s * ny + rows[k]] = (int32_t)k;
+        t.n_slots = std::max(t.n_slots, (int)rows.size());
+        for (int64_t j = 0; j < n_rec; ++j) {
+            const int64_t c = rec[s * n_rec + j];
+            if (c >= 0) t.rec_gather[s * n_rec + j] = t.rec_slot[s * ny + c / nx] * (int32_t)nx + (int32_t)(c % nx);
+        }
+    }
+    return t;
+}
+
 struct Layout {
     uint64_t cpml = 0, tables = 0, scratch = 0;
     uint64_t model = 0, model_bytes = 0;          // [Ca | Cb | Cq]
@@ -108,14 +161,15 @@ struct Layout {
     uint64_t snapE = 0, snapC = 0, snap_step = 0; // per-step bytes of one snapshot array (all shots)
     uint64_t snap_shot = 0;                       // ... of one shot
     uint64_t ckpt = 0, ckpt_slot = 0;
+    uint64_t recrows = 0;                         // receiver-row buffer of two-step launches
     uint64_t total = 0;
 };
 
 }  // namespace
 
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
-enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_COUNT };
-const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step"};
+enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_COUNT };
+const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2"};
 
 struct TimedLaunch {
     int kid;
@@ -127,11 +181,15 @@ struct tm_plan {
     int P = 0;
     Geo g{};
     Tiling tiling_fwd{}, tiling_adj{};   // per device, made at the first device call
+    Tiling tiling_fwd2{};
+    int time_block = 2;                  // forward time steps per launch (1 or 2)
     int tiling_device = -1;
     std::vector<float> cpml;             // [12][L]
     std::vector<int32_t> tables;         // scatter tables, packed
     uint64_t t_s_cell = 0, t_s_ptr = 0, t_s_list = 0, t_s_idx = 0;
     uint64_t t_r_cell = 0, t_r_ptr = 0, t_r_list = 0, t_r_idx = 0;
+    uint64_t t_m_row = 0, t_m_cx = 0, t_m_cs = 0, t_m_sl = 0, t_m_rslot = 0, t_m_rg = 0;
+    int n_slots = 0;
     Layout lay;
     int64_t K = 0, n_seg = 0, n_ckpt = 0, seg_steps = 0;
     // pinned staging copy of cpml + tables (allocated on first device call)
@@ -218,6 +276,7 @@ bool make_layout(tm_plan* p)
     L.snapC = take(L.snap_step * (uint64_t)p->seg_steps);
     L.ckpt_slot = L.set_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
+    L.recrows = take(S * (uint64_t)p->n_slots * (uint64_t)g.nx * 4);
     L.total = o;
     return true;
 }
@@ -229,7 +288,7 @@ bool make_layout(tm_plan* p)
 // 16 and CH_MAX rows, and no round runs half empty.  TM_FDTD_CHUNK_ROWS
 // (environment, read when the tiling is made) forces the chunk height, for
 // tuning.
-Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W)
+Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_MAX)
 {
     Tiling t{};
     const int R = (int)d.ny - 2 * P + 1, nx_e = (int)d.nx - 2 * P + 1;
@@ -242,12 +301,12 @@ Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W)
         const int64_t m = std::min<int64_t>(k * cap / U, m_max);
         if (m < 1) continue;
         ch = (int)((R + m - 1) / m);
-        if (ch <= CH_MAX) break;
+        if (ch <= chmax) break;
     }
-    ch = std::min(ch, CH_MAX);
+    ch = std::min(ch, chmax);
     if (const char* env = std::getenv("TM_FDTD_CHUNK_ROWS")) {
         const int v = std::atoi(env);
-        if (v >= 1 && v <= CH_MAX) ch = v;
+        if (v >= 1) ch = std::min(v, chmax);
     }
     t.CH = ch;
     t.nchunk = (R + ch - 1) / ch;
@@ -342,6 +401,8 @@ struct Ptrs {
     Model model;
     const int32_t *s_cell, *s_ptr, *s_list, *s_idx;
     const int32_t *r_cell, *r_ptr, *r_list, *r_idx;
+    const int32_t *m_row, *m_cx, *m_cs, *m_sl, *m_rslot, *m_rg;
+    float* recrows;
     char *snapE, *snapC, *ckpt;
     float* scratch;
 };
@@ -357,6 +418,9 @@ Ptrs pointers(const tm_plan* p, void* ws)
     const int32_t* t = wsp<int32_t>(ws, L.tables);
     q.s_cell = t + p->t_s_cell; q.s_ptr = t + p->t_s_ptr; q.s_list = t + p->t_s_list; q.s_idx = t + p->t_s_idx;
     q.r_cell = t + p->t_r_cell; q.r_ptr = t + p->t_r_ptr; q.r_list = t + p->t_r_list; q.r_idx = t + p->t_r_idx;
+    q.m_row = t + p->t_m_row; q.m_cx = t + p->t_m_cx; q.m_cs = t + p->t_m_cs; q.m_sl = t + p->t_m_sl;
+    q.m_rslot = t + p->t_m_rslot; q.m_rg = t + p->t_m_rg;
+    q.recrows = wsp<float>(ws, L.recrows);
     q.snapE = wsp<char>(ws, L.snapE);
     q.snapC = wsp<char>(ws, L.snapC);
     q.ckpt = wsp<char>(ws, L.ckpt);
@@ -393,7 +457,57 @@ void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int6
     float* rt = (r != nullptr && nr > 0) ? r + t * S * nr : nullptr;
     if (ft != nullptr || rt != nullptr) {
         k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            a.set1, L.st.shot_bytes, L.st.oE, ft, (int)ns, q.s_cell, q.s_ptr, q.s_list, rt, (int)nr, q.r_idx);
+            a.set1, L.st.shot_bytes, L.st.oE, ft, (int)ns, q.s_cell, q.s_ptr, q.s_list, rt, (int)nr, q.r_idx,
+            nullptr, nullptr, nullptr, 0, 0);
+    }
+}
+
+// Forward steps t and t+1 in one launch (set cur -> 1-cur), the step-t
+// sources and receivers inside it; then step t+1's sources and receivers
+// and the gather of step t's receivers.  se0/sc0, se1/sc1: snapshot
+// destinations of steps t and t+1, or null.
+template <int P>
+void fwd_step2(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int64_t t, int snap, char* se0,
+               char* sc0, char* se1, char* sc1, hipStream_t st)
+{
+    const Layout& L = p->lay;
+    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
+    Fwd2Args a;
+    a.g = p->g;
+    a.t = p->tiling_fwd2;
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.fset[cur];
+    a.set1 = q.base + L.fset[1 - cur];
+    a.snap_e0 = se0;
+    a.snap_c0 = sc0;
+    a.snap_e1 = se1;
+    a.snap_c1 = sc1;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
+    const bool recs = r != nullptr && nr > 0;
+    a.ev.row_cells = ns > 0 ? q.m_row : nullptr;
+    a.ev.cell_x = q.m_cx;
+    a.ev.cell_src = q.m_cs;
+    a.ev.src_list = q.m_sl;
+    a.ev.f = ns > 0 ? f + t * S * ns : nullptr;
+    a.ev.n_src = (int)ns;
+    a.ev.rec_slot = recs ? q.m_rslot : nullptr;
+    a.ev.rec_rows = q.recrows;
+    a.ev.n_slots = p->n_slots;
+    const dim3 grid((unsigned)p->tiling_fwd2.nblk), blk(NT);
+    timed(p, KID_FWD_STEP2, t, st, [&] {
+        if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else k_fwd_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
+    });
+    const float* ft = ns > 0 ? f + (t + 1) * S * ns : nullptr;
+    float* rt = recs ? r + (t + 1) * S * nr : nullptr;
+    float* rp = recs ? r + t * S * nr : nullptr;
+    if (ft != nullptr || rt != nullptr) {
+        k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
+            a.set1, L.st.shot_bytes, L.st.oE, ft, (int)ns, q.s_cell, q.s_ptr, q.s_list, rt, (int)nr, q.r_idx,
+            q.recrows, q.m_rg, rp, p->n_slots, p->g.nx);
     }
 }
 
@@ -473,8 +587,13 @@ tm_status device_tiling(tm_plan* p)
     v = resident(bf ? reinterpret_cast<const void*>(&k_adj_step<P, SNAP_BF16>)
                     : reinterpret_cast<const void*>(&k_adj_step<P, SNAP_F32>), &ca);
     if (v != TM_OK) return v;
+    int64_t c2 = 0;
+    v = resident(bf ? reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_BF16>)
+                    : reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_F32>), &c2);
+    if (v != TM_OK) return v;
     p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W);
     p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W);
+    p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W, CH2_MAX);
     p->tiling_device = dev;
     return TM_OK;
 }
@@ -486,16 +605,24 @@ template <int P, typename SnapAt>
 tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, float* r, int64_t t0, int64_t t1,
                         int snap, SnapAt snap_at, bool ckpt, hipStream_t st)
 {
-    for (int64_t t = t0; t < t1; ++t) {
+    for (int64_t t = t0; t < t1;) {
         if (ckpt && t > 0 && t % p->K == 0) {
             const int64_t slot = t / p->K - 1;
             HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, q.base + p->lay.fset[*cur],
                                   p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
         }
-        char* se = nullptr;
-        char* sc = nullptr;
+        // two steps per launch unless step t+1 starts a checkpoint interval
+        const bool pair = p->time_block == 2 && t + 1 < t1 && !(ckpt && (t + 1) % p->K == 0);
+        char *se = nullptr, *sc = nullptr, *se1 = nullptr, *sc1 = nullptr;
         if (snap != SNAP_NONE) snap_at(t, se, sc);
-        fwd_step<P>(p, q, *cur, f, r, t, snap, se, sc, st);
+        if (pair) {
+            if (snap != SNAP_NONE) snap_at(t + 1, se1, sc1);
+            fwd_step2<P>(p, q, *cur, f, r, t, snap, se, sc, se1, sc1, st);
+            t += 2;
+        } else {
+            fwd_step<P>(p, q, *cur, f, r, t, snap, se, sc, st);
+            t += 1;
+        }
         *cur = 1 - *cur;
     }
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
@@ -610,6 +737,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16) return TM_EINVAL;
+    if (d.time_block < 0 || d.time_block > 2 || d.reserved != 0) return TM_EINVAL;
     if (d.ny < 2 * P + 2 || d.nx < 2 * P + 2) return TM_EINVAL;
     if (d.ny * d.nx >= (int64_t(1) << 29)) return TM_EINVAL;
     if (d.n_shots * std::max<int64_t>(d.n_src, d.n_rec) >= (int64_t(1) << 31)) return TM_EINVAL;
@@ -657,6 +785,11 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const Scatter rs = build_scatter(rec, d.n_shots, d.n_rec);
     p->t_s_cell = append(ss.cell); p->t_s_ptr = append(ss.ptr); p->t_s_list = append(ss.list); p->t_s_idx = append(ss.idx);
     p->t_r_cell = append(rs.cell); p->t_r_ptr = append(rs.ptr); p->t_r_list = append(rs.list); p->t_r_idx = append(rs.idx);
+    const MidTables mt = build_mid(src, d.n_src, rec, d.n_rec, d.n_shots, d.ny, d.nx);
+    p->t_m_row = append(mt.row_cells); p->t_m_cx = append(mt.cell_x); p->t_m_cs = append(mt.cell_src);
+    p->t_m_sl = append(mt.src_list); p->t_m_rslot = append(mt.rec_slot); p->t_m_rg = append(mt.rec_gather);
+    p->n_slots = mt.n_slots;
+    p->time_block = d.time_block == 0 ? 2 : (int)d.time_block;
 
     if (d.ckpt_every > 0 && d.ckpt_every < d.nt) {
         p->K = d.ckpt_every;
@@ -670,6 +803,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         p->seg_steps = d.nt;
     }
     p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024, NT - 4 * P + 2);
+    p->tiling_fwd2 = make_tiling(d, P, 1024, NT - 8 * P + 4, CH2_MAX);
     if (!make_layout(p)) {
         delete p;
         return TM_EINVAL;

@@ -1,0 +1,363 @@
+// Two forward time steps per launch (temporal blocking), gfx950 / wave64.
+//
+// k_fwd_step2 advances every shot from step n to step n+2 in one pass over
+// the state: stage A computes the step n -> n+1 exactly as k_fwd_step does,
+// and stage B consumes stage A's rows while they are still in registers and
+// LDS and computes the step n+1 -> n+2.  The state crosses HBM once per two
+// steps; the intermediate state never leaves the chip.
+//
+// Streaming (iteration r, one row per stage):
+//   stage A: H row hA = r - P,    E row yA = r - 2P + 1   (as k_fwd_step)
+//   stage B: H row hB = r - 3P+1, E row yB = r - 4P + 2
+// Stage B needs the E^{n+1} rows up to yA (register window ewB), the old
+// H^{n+1/2} of row hB (the oldest Hx row of stage A's window; Hz from a ring
+// of 2P rows in LDS) and the CPML memories stage A produced for its rows,
+// which wait 2P-1 iterations in a lane-private LDS FIFO (each lane reads
+// back only what it wrote, so the FIFO needs no barrier).  The model
+// coefficients of stage B's rows are loaded again (they were read 2P-1 rows
+// earlier by the same workgroup and are served by the caches).
+//
+// A strip of 256 lanes owns W = 256 - 8P + 4 columns: stage A's values are
+// valid 2P-1 lanes further in from the edges than the loaded E^n, stage B's
+// another 2P-1.  A chunk of CH owned rows reads 4P-2 rows above and below.
+// Values of stage A outside the field's index set are forced to 0 exactly
+// as the untouched cells of the single-step path stay 0, and every
+// operation is written as in k_fwd_step, so both kernels give bitwise the
+// same state.
+//
+// Sources of step n are added to E^{n+1} inside the kernel (per-row
+// distinct-cell lists staged in LDS; several sources on one cell are summed
+// first, in index order, then added, as in k_fwd_srcrec), at every lane
+// that computes that cell, halo lanes included.  Receivers of step n read
+// E^{n+1} after the injection: the owned part of each receiver row is
+// written to a small row buffer that the step's small follow-up kernel
+// gathers from.  Sources and receivers of step n+1 are handled by that
+// kernel on the written state, as after a single step.
+#pragma once
+
+#include "tm_step.hpp"
+
+namespace tmf {
+
+constexpr int CH2_MAX = 128;   // largest chunk height of the two-step kernel (LDS tables)
+
+template <int P>
+struct Strip2 {
+    static constexpr int W = NT - 8 * P + 4;   // owned columns per strip
+    static constexpr int OFF = 4 * P - 2;      // lane of the first owned column
+};
+
+// Sources and receivers of the intermediate step (step n of the pair).
+struct MidEvents {
+    const int* __restrict__ row_cells;   // [S*ny + 1]: distinct source cells of (shot, row) are
+                                         //   [row_cells[s*ny+y], row_cells[s*ny+y+1]); null = none
+    const int* __restrict__ cell_x;      // column of each distinct cell
+    const int* __restrict__ cell_src;    // [n_cells + 1]: its sources are src_list[cell_src[k] ..)
+    const int* __restrict__ src_list;    // source indices, ascending per cell
+    const float* __restrict__ f;         // f[n]: [S][n_src]
+    int n_src;
+    const int* __restrict__ rec_slot;    // [S*ny]: row-buffer slot of a receiver row, or -1; null = none
+    float* __restrict__ rec_rows;        // [S][n_slots][nx]
+    int n_slots;
+};
+
+struct Fwd2Args {
+    Geo g;
+    Tiling t;
+    StateLayout L;
+    Model m;
+    const float* __restrict__ cp;      // CPML table [12][L]
+    const char* __restrict__ set0;     // state at step n
+    char* __restrict__ set1;           // state at step n+2
+    char* __restrict__ snap_e0;        // Ey^n, curl H^n [S][nyi][nxi], or null
+    char* __restrict__ snap_c0;
+    char* __restrict__ snap_e1;        // Ey^{n+1}, curl H^{n+1}
+    char* __restrict__ snap_c1;
+    uint32_t snap_shot_bytes;
+    MidEvents ev;
+};
+
+template <int P, int SNAP>
+__global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
+{
+    constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
+    constexpr int D = PREFETCH;
+    constexpr int R2 = 2 * P;                       // ring / FIFO depth (a power of two)
+    __shared__ float rowA[NT];                      // E^n row hA
+    __shared__ float rowB[NT];                      // E^{n+1} row hB
+    __shared__ float ringA[R2][NT];                 // Hz^{n+1/2} rows
+    __shared__ float ringB[P][NT];                  // Hz^{n+3/2} rows
+    __shared__ float mfifo[4][R2][NT];              // stage A's CPML memories, lane-private
+    __shared__ float cyt[CH2_MAX + 6 * P - 3][6];   // per-row CPML coefficients
+    __shared__ int evs[CH2_MAX + 4 * P - 2][2];     // source-cell range per stage-A E row
+    __shared__ int evr[CH2_MAX];                    // receiver slot per owned row
+
+    const Geo& g = a.g;
+    const StateLayout& L = a.L;
+    int s, strip, chunk;
+    tile_of(a.t, s, strip, chunk);
+    const int tid = threadIdx.x;
+    const int nx = g.nx, ny = g.ny;
+    const int xs = P + strip * W;
+    const int xe = min(xs + W, nx - P + 1);
+    const int ya = P + chunk * a.t.CH;
+    const int yb = min(ya + a.t.CH, ny - P + 1);
+    const int yc0 = ya - 3 * P + 1;                 // first row of the CPML table
+    const int ye0 = ya - 2 * P + 1;                 // first stage-A E row
+    load_row_cpml(cyt, a.cp, g, yc0, yb - ya + 6 * P - 3);
+    for (int i = tid; i < yb - ya + 4 * P - 2; i += NT) {
+        const int y = ye0 + i;
+        int b = 0, e = 0;
+        if (a.ev.row_cells != nullptr && y >= 0 && y < ny) {
+            b = a.ev.row_cells[s * ny + y];
+            e = a.ev.row_cells[s * ny + y + 1];
+        }
+        evs[i][0] = b;
+        evs[i][1] = e;
+    }
+    for (int i = tid; i < yb - ya; i += NT) evr[i] = a.ev.rec_slot != nullptr ? a.ev.rec_slot[s * ny + ya + i] : -1;
+    __syncthreads();
+
+    const int c = xs - OFF + tid;                   // this lane's column
+    const bool own = (c >= xs) & (c < xe);
+    const bool incol = (c >= 0) & (c < nx);
+    const bool colE = (c >= P) & (c <= nx - P);     // Ey and Hx columns
+    const bool colHz = (c >= P) & (c <= nx - P - 1);
+    // lanes whose stencil inputs are all valid, per stage
+    const bool hzA_ok = colHz & (tid >= P - 1) & (tid <= NT - P - 1);
+    const bool eA_ok = colE & (tid >= 2 * P - 1) & (tid <= NT - 2 * P);
+    const bool hzB_ok = colHz & (tid >= 3 * P - 2) & (tid <= NT - 3 * P);
+    const bool fx_h = incol & ((c < g.x0) | (c >= g.hx1));
+    const bool fx_e = incol & ((c < g.x0) | (c >= g.x1));
+    const bool in_x = (c >= g.x0) & (c < g.x1);
+    const int c0 = xs - OFF;
+    const bool xband = c0 < g.x0 || c0 + NT - 1 >= g.hx1;   // uniform
+    const int bxc = band_x(g, incol ? c : 0);
+    const int th = min(max(tid, P - 1), NT - P - 1);
+    const int te = min(max(tid, P), NT - P);
+
+    Cpml1 cx_h{0.f, 0.f, 1.f}, cx_e{0.f, 0.f, 1.f};
+    if (fx_h) cx_h = cpml_at(a.cp, g.L, AXH, c);
+    if (fx_e) cx_e = cpml_at(a.cp, g.L, AX, c);
+
+    auto in_rows = [&](int y) { return (y >= 0) & (y < ny); };
+    auto rowE = [&](int y) { return (y >= P) & (y <= ny - P); };
+    auto hx_row = [&](int h) { return (h >= P) & (h <= ny - P - 1); };
+    auto hz_row = [&](int h) { return (h >= P) & (h <= ny - P); };
+    auto own_row = [&](int y) { return (y >= ya) & (y < yb); };
+    auto fy_h = [&](int h) { return (h < g.y0) | (h >= g.hy1); };
+    auto fy_e = [&](int y) { return (y < g.y0) | (y >= g.y1); };
+    auto slot2 = [&](int y) { return (y + 4 * P) & (R2 - 1); };   // y >= -4P
+    auto slot1 = [&](int y) { return (y + 4 * P) & (P - 1); };
+
+    const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf bm(a.m.base, a.m.bytes);
+    const uint32_t sb = SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u;
+    const RBuf bse0(a.snap_e0 + (int64_t)s * a.snap_shot_bytes, sb);
+    const RBuf bsc0(a.snap_c0 + (int64_t)s * a.snap_shot_bytes, sb);
+    const RBuf bse1(a.snap_e1 + (int64_t)s * a.snap_shot_bytes, sb);
+    const RBuf bsc1(a.snap_c1 + (int64_t)s * a.snap_shot_bytes, sb);
+    const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
+
+    const int r_first = ya - 2 * P + 1;
+    const int r_end = yb + 4 * P - 3;
+
+    // Prefetch ring: the loads of iteration r are issued at iteration r - D
+    // into slot (r - r_first) % D.
+    float fE[D], fQa[D], fHx[D], fHz[D], fMyh[D], fMxh[D], fCa[D], fCb[D], fMxe[D], fMye[D];
+    float fQb[D], fCaB[D], fCbB[D];
+    auto issue = [&](int u, int r, bool live) {
+        const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
+        const uint32_t ohA = (uint32_t)(hA * nx) * 4u + c4, oyA = (uint32_t)(yA * nx) * 4u + c4;
+        const uint32_t ohB = (uint32_t)(hB * nx) * 4u + c4, oyB = (uint32_t)(yB * nx) * 4u + c4;
+        fE[u] = b0.ld(live & in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
+        fQa[u] = bm.ld(live & in_rows(hA) & incol, ohA, a.m.oCq);
+        const bool hx_do = live & colE & hx_row(hA);
+        fHx[u] = b0.ld(hx_do, ohA, L.oHx);
+        fMyh[u] = b0.ld(hx_do & fy_h(hA), (uint32_t)(band_y(g, hA) * nx) * 4u + c4, L.oMyh);
+        const bool hz_do = live & colHz & hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2);
+        fHz[u] = b0.ld(hz_do, ohA, L.oHz);
+        fMxh[u] = b0.ld(hz_do & fx_h, (uint32_t)(hA * g.bx) * 4u + bx4, L.oMxh);
+        const bool e_do = live & colE & rowE(yA) & (yA >= ye0);
+        fCa[u] = bm.ld(e_do, oyA, a.m.oCa);
+        fCb[u] = bm.ld(e_do, oyA, a.m.oCb);
+        fMxe[u] = b0.ld(e_do & fx_e, (uint32_t)(yA * g.bx) * 4u + bx4, L.oMxe);
+        fMye[u] = b0.ld(e_do & fy_e(yA), (uint32_t)(band_y(g, yA) * nx) * 4u + c4, L.oMye);
+        fQb[u] = bm.ld(live & in_rows(hB) & incol & (hB >= ya - P), ohB, a.m.oCq);
+        const bool eb_do = live & own & own_row(yB);
+        fCaB[u] = bm.ld(eb_do, oyB, a.m.oCa);
+        fCbB[u] = bm.ld(eb_do, oyB, a.m.oCb);
+    };
+
+    float ewA[2 * P];    // E^n rows r-2P+1 .. r
+    float hwA[2 * P];    // Hx^{n+1/2} rows hA-2P+1 .. hA
+    float ewB[2 * P];    // E^{n+1} rows yA-2P+1 .. yA
+    float hwB[2 * P];    // Hx^{n+3/2} rows hB-2P+1 .. hB
+#pragma unroll
+    for (int i = 0; i < 2 * P; ++i) { ewA[i] = 0.0f; hwA[i] = 0.0f; ewB[i] = 0.0f; hwB[i] = 0.0f; }
+#pragma unroll
+    for (int i = 1; i < 2 * P; ++i) {
+        const int r = r_first - 2 * P + i;
+        ewA[i] = b0.ld(in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u) issue(u, r_first + u, r_first + u <= r_end);
+
+    for (int r0 = r_first;; r0 += UNROLL) {
+#pragma unroll
+        for (int uu = 0; uu < UNROLL; ++uu) {
+            const int r = r0 + uu;
+            if (r > r_end) return;
+            const int u = uu % D;
+            const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
+
+            // ---- (a) new E^n row; LDS rows for the two Hz stencils; Hx of stage A
+#pragma unroll
+            for (int i = 0; i < 2 * P - 1; ++i) ewA[i] = ewA[i + 1];
+            ewA[2 * P - 1] = fE[u];
+            rowA[tid] = ewA[P - 1];
+            rowB[tid] = ewB[P];
+            {
+                float d = g.rdy * stencil<P>([&](int k) { return ewA[P - 1 + k]; },
+                                             [&](int k) { return ewA[P - k]; });
+                if (fy_h(hA)) {                                     // uniform
+                    const float* ct = cyt[hA - yc0];
+                    float m = fMyh[u];
+                    d = cpml_step(m, ct[0], ct[1], ct[2], d);
+                    mfifo[0][slot2(hA)][tid] = m;
+                }
+                const float hxn = (colE & hx_row(hA)) ? fmaf(-fQa[u], d, fHx[u]) : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 2 * P - 1; ++i) hwA[i] = hwA[i + 1];
+                hwA[2 * P - 1] = hxn;
+            }
+            __syncthreads();
+
+            // ---- (b) Hz of stage A (row hA) and of stage B (row hB)
+            if (hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2)) {   // uniform
+                float d = g.rdx * stencil<P>([&](int k) { return rowA[th + k]; },
+                                             [&](int k) { return rowA[th - k + 1]; });
+                if (xband) {
+                    float m = fMxh[u];
+                    d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
+                    mfifo[1][slot2(hA)][tid] = m;
+                }
+                ringA[slot2(hA)][tid] = hzA_ok ? fmaf(fQa[u], d, fHz[u]) : 0.0f;
+            }
+            if (hz_row(hB) & own_row(hB)) {                             // uniform
+                float d = g.rdx * stencil<P>([&](int k) { return rowB[th + k]; },
+                                             [&](int k) { return rowB[th - k + 1]; });
+                if (xband) {
+                    float m = mfifo[1][slot2(hB)][tid];
+                    d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
+                    b1.st(own & colHz & fx_h, m, (uint32_t)(hB * g.bx) * 4u + bx4, L.oMxh);
+                }
+                const float hzn = hzB_ok ? fmaf(fQb[u], d, ringA[slot2(hB)][tid]) : 0.0f;
+                b1.st(own & colHz, hzn, (uint32_t)(hB * nx) * 4u + c4, L.oHz);
+                ringB[slot1(hB)][tid] = hzn;
+            }
+            __syncthreads();
+
+            // ---- (c) E of stage A (row yA), with the step-n sources and receivers
+            if (r >= ya) {                                              // uniform
+                const float* hzr = ringA[slot2(yA)];
+                float uu_ = g.rdx * stencil<P>([&](int k) { return hzr[te + k - 1]; },
+                                               [&](int k) { return hzr[te - k]; });
+                if (xband) {
+                    float m = fMxe[u];
+                    uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
+                    mfifo[2][slot2(yA)][tid] = m;
+                }
+                float v = g.rdy * stencil<P>([&](int k) { return hwA[P - 1 + k]; },
+                                             [&](int k) { return hwA[P - k]; });
+                if (fy_e(yA)) {
+                    const float* ct = cyt[yA - yc0];
+                    float m = fMye[u];
+                    v = cpml_step(m, ct[3], ct[4], ct[5], v);
+                    mfifo[3][slot2(yA)][tid] = m;
+                }
+                const float curl = uu_ - v;
+                const float ev = ewA[0];
+                if constexpr (SNAP != SNAP_NONE) {
+                    if ((yA >= g.y0) & (yA < g.y1) & own_row(yA)) {
+                        const uint32_t w = (uint32_t)((yA - g.y0) * g.nxi + (c - g.x0));
+                        snap_put<SNAP>(bse0, own & in_x, w, ev);
+                        snap_put<SNAP>(bsc0, own & in_x, w, curl);
+                    }
+                }
+                float en = fmaf(fCa[u], ev, fCb[u] * curl);
+                en = (eA_ok & rowE(yA)) ? en : 0.0f;
+                const int kb = __builtin_amdgcn_readfirstlane(evs[yA - ye0][0]);
+                const int ke = __builtin_amdgcn_readfirstlane(evs[yA - ye0][1]);
+                for (int k = kb; k < ke; ++k) {                         // distinct source cells of the row
+                    const int col = a.ev.cell_x[k];
+                    float acc = 0.0f;
+                    for (int q = a.ev.cell_src[k]; q < a.ev.cell_src[k + 1]; ++q)
+                        acc += a.ev.f[s * a.ev.n_src + a.ev.src_list[q]];
+                    if (c == col) en = en + acc;
+                }
+                if (own_row(yA)) {
+                    const int slot = __builtin_amdgcn_readfirstlane(evr[yA - ya]);
+                    if (slot >= 0 && own)
+                        a.ev.rec_rows[((int64_t)s * a.ev.n_slots + slot) * nx + c] = en;
+                }
+#pragma unroll
+                for (int i = 0; i < 2 * P - 1; ++i) ewB[i] = ewB[i + 1];
+                ewB[2 * P - 1] = en;
+            }
+
+            // ---- Hx of stage B (row hB)
+            if (r >= ya + 2 * P - 1) {                                  // uniform
+                float d = g.rdy * stencil<P>([&](int k) { return ewB[P - 1 + k]; },
+                                             [&](int k) { return ewB[P - k]; });
+                const bool st_h = own & hx_row(hB) & own_row(hB);
+                if (fy_h(hB)) {
+                    const float* ct = cyt[hB - yc0];
+                    float m = mfifo[0][slot2(hB)][tid];
+                    d = cpml_step(m, ct[0], ct[1], ct[2], d);
+                    b1.st(st_h, m, (uint32_t)(band_y(g, hB) * nx) * 4u + c4, L.oMyh);
+                }
+                const float hxn = (colE & hx_row(hB)) ? fmaf(-fQb[u], d, hwA[0]) : 0.0f;
+                b1.st(st_h, hxn, (uint32_t)(hB * nx) * 4u + c4, L.oHx);
+#pragma unroll
+                for (int i = 0; i < 2 * P - 1; ++i) hwB[i] = hwB[i + 1];
+                hwB[2 * P - 1] = hxn;
+            }
+
+            // ---- E of stage B (row yB): the owned output row
+            if (r >= ya + 4 * P - 2) {                                  // uniform
+                const float* hzr = ringB[slot1(yB)];
+                float uu_ = g.rdx * stencil<P>([&](int k) { return hzr[te + k - 1]; },
+                                               [&](int k) { return hzr[te - k]; });
+                if (xband) {
+                    float m = mfifo[2][slot2(yB)][tid];
+                    uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
+                    b1.st(own & fx_e, m, (uint32_t)(yB * g.bx) * 4u + bx4, L.oMxe);
+                }
+                float v = g.rdy * stencil<P>([&](int k) { return hwB[P - 1 + k]; },
+                                             [&](int k) { return hwB[P - k]; });
+                if (fy_e(yB)) {
+                    const float* ct = cyt[yB - yc0];
+                    float m = mfifo[3][slot2(yB)][tid];
+                    v = cpml_step(m, ct[3], ct[4], ct[5], v);
+                    b1.st(own, m, (uint32_t)(band_y(g, yB) * nx) * 4u + c4, L.oMye);
+                }
+                const float curl = uu_ - v;
+                const float ev = ewB[0];
+                if constexpr (SNAP != SNAP_NONE) {
+                    if ((yB >= g.y0) & (yB < g.y1)) {
+                        const uint32_t w = (uint32_t)((yB - g.y0) * g.nxi + (c - g.x0));
+                        snap_put<SNAP>(bse1, own & in_x, w, ev);
+                        snap_put<SNAP>(bsc1, own & in_x, w, curl);
+                    }
+                }
+                const float en = fmaf(fCaB[u], ev, fCbB[u] * curl);
+                b1.st(own, en, (uint32_t)(yB * nx) * 4u + c4, L.oE);
+            }
+            issue(u, r + D, r + D <= r_end);
+        }
+    }
+}
+
+}  // namespace tmf

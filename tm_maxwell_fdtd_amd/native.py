@@ -46,6 +46,8 @@ class tm_desc(ctypes.Structure):
         ("n_src", ctypes.c_int64), ("n_rec", ctypes.c_int64),
         ("ckpt_every", ctypes.c_int64),
         ("hbm_budget", ctypes.c_uint64),
+        ("time_block", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -199,14 +201,15 @@ def tm_timing_read(plan):
 
 # ---- convenience layer (still marshalling only) -----------------------------
 
-def make_desc(wl, snap: Optional[str] = None, ckpt_every: Optional[int] = None, hbm_budget: int = 0) -> tm_desc:
+def make_desc(wl, snap: Optional[str] = None, ckpt_every: Optional[int] = None, hbm_budget: int = 0,
+              time_block: int = 0) -> tm_desc:
     snap = wl.snap if snap is None else snap
     return tm_desc(order=wl.order, snap=TM_SNAP_BF16 if snap == "bf16" else TM_SNAP_F32,
                    n_shots=wl.n_shots, ny=wl.ny, nx=wl.nx,
                    pml_y0=wl.pml_y0, pml_y1=wl.pml_y1, pml_x0=wl.pml_x0, pml_x1=wl.pml_x1,
                    dy=wl.dy, dx=wl.dx, nt=wl.nt, n_src=wl.n_src, n_rec=wl.n_rec,
                    ckpt_every=wl.ckpt_every if ckpt_every is None else ckpt_every,
-                   hbm_budget=hbm_budget)
+                   hbm_budget=hbm_budget, time_block=time_block)
 
 
 class Propagator:
@@ -217,12 +220,12 @@ class Propagator:
     tensors; the model arrays are passed at construction.
     """
 
-    def __init__(self, wl, device="cuda", snap=None, ckpt_every=None, hbm_budget=0):
+    def __init__(self, wl, device="cuda", snap=None, ckpt_every=None, hbm_budget=0, time_block=0):
         import torch
 
         self.wl = wl
         self.device = torch.device(device)
-        self.desc = make_desc(wl, snap, ckpt_every, hbm_budget)
+        self.desc = make_desc(wl, snap, ckpt_every, hbm_budget, time_block)
         st, plan = tm_plan_create(self.desc, wl.cpml, wl.src, wl.rec)
         _check(st, "tm_plan_create")
         self.plan = plan
