@@ -162,7 +162,23 @@ struct RBuf {
     {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, ok ? (int)off : OOB, 0, 0);
     }
+    // per-lane offset `voff` (already OOB where masked), uniform offset `soff`
+    __device__ __forceinline__ float ldv(int voff, uint32_t soff) const
+    {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, (int)soff, 0));
+    }
+    __device__ __forceinline__ void stv(float v, int voff, uint32_t soff) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, (int)soff, 0);
+    }
+    __device__ __forceinline__ void stv_bf16(float v, int voff, uint32_t soff) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, (int)soff, 0);
+    }
 };
+
+// Lane offset, or the out-of-range offset where the lane is masked.
+__device__ __forceinline__ int lane_off(bool ok, uint32_t off) { return ok ? (int)off : RBuf::OOB; }
 
 // Snapshot element access (f32 or bf16), element index w.
 template <int SNAP>

@@ -33,7 +33,18 @@
 // written to a small row buffer that the step's small follow-up kernel
 // gathers from.  Sources and receivers of step n+1 are handled by that
 // kernel on the written state, as after a single step.
+//
+// Fast blocks: most unrolled blocks of a chunk lie where every stage is
+// active, no row is a CPML band row or carries sources or receivers, and
+// every row is owned or inside the index sets.  Those blocks run an
+// instance of the iteration with all row predicates folded away: loads and
+// stores use a loop-invariant lane offset (out of range where the lane is
+// masked) plus a uniform row offset, so they cost no vector instructions
+// for addressing.  The other blocks run the general iteration.  Both compute
+// the same values.
 #pragma once
+
+#include <type_traits>
 
 #include "tm_step.hpp"
 
@@ -83,6 +94,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH;
     constexpr int R2 = 2 * P;                       // ring / FIFO depth (a power of two)
+    constexpr uint32_t ESZ = SNAP == SNAP_BF16 ? 2u : 4u;
     __shared__ float rowA[NT];                      // E^n row hA
     __shared__ float rowB[NT];                      // E^{n+1} row hB
     __shared__ float ringA[R2][NT];                 // Hz^{n+1/2} rows
@@ -91,6 +103,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     __shared__ float cyt[CH2_MAX + 6 * P - 3][6];   // per-row CPML coefficients
     __shared__ int evs[CH2_MAX + 4 * P - 2][2];     // source-cell range per stage-A E row
     __shared__ int evr[CH2_MAX];                    // receiver slot per owned row
+    __shared__ int ev_lo, ev_hi;                    // first / last stage-A E row with events
 
     const Geo& g = a.g;
     const StateLayout& L = a.L;
@@ -104,18 +117,28 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     const int yb = min(ya + a.t.CH, ny - P + 1);
     const int yc0 = ya - 3 * P + 1;                 // first row of the CPML table
     const int ye0 = ya - 2 * P + 1;                 // first stage-A E row
+    if (tid == 0) {
+        ev_lo = INT32_MAX;
+        ev_hi = INT32_MIN;
+    }
     load_row_cpml(cyt, a.cp, g, yc0, yb - ya + 6 * P - 3);
+    __syncthreads();
     for (int i = tid; i < yb - ya + 4 * P - 2; i += NT) {
         const int y = ye0 + i;
-        int b = 0, e = 0;
+        int b = 0, e = 0, slot = -1;
         if (a.ev.row_cells != nullptr && y >= 0 && y < ny) {
             b = a.ev.row_cells[s * ny + y];
             e = a.ev.row_cells[s * ny + y + 1];
         }
+        if (a.ev.rec_slot != nullptr && y >= ya && y < yb) slot = a.ev.rec_slot[s * ny + y];
         evs[i][0] = b;
         evs[i][1] = e;
+        if (y >= ya && y < yb) evr[y - ya] = slot;
+        if (b < e || slot >= 0) {
+            atomicMin(&ev_lo, y);
+            atomicMax(&ev_hi, y);
+        }
     }
-    for (int i = tid; i < yb - ya; i += NT) evr[i] = a.ev.rec_slot != nullptr ? a.ev.rec_slot[s * ny + ya + i] : -1;
     __syncthreads();
 
     const int c = xs - OFF + tid;                   // this lane's column
@@ -159,35 +182,64 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     const RBuf bse1(a.snap_e1 + (int64_t)s * a.snap_shot_bytes, sb);
     const RBuf bsc1(a.snap_c1 + (int64_t)s * a.snap_shot_bytes, sb);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
+    const uint32_t rowb = (uint32_t)nx * 4u, brow = (uint32_t)g.bx * 4u;
+
+    // loop-invariant lane offsets of the fast blocks
+    const int v_in = lane_off(incol, c4), v_e = lane_off(colE, c4), v_hz = lane_off(colHz, c4);
+    const int v_own = lane_off(own, c4), v_ownhz = lane_off(own & colHz, c4);
+    const int v_mxh = lane_off(colHz & fx_h, bx4), v_mxe = lane_off(colE & fx_e, bx4);
+    const int v_snap = lane_off(own & in_x, (uint32_t)(c - g.x0) * ESZ);
 
     const int r_first = ya - 2 * P + 1;
     const int r_end = yb + 4 * P - 3;
+    // Unrolled blocks starting at r0 in [f_lo, f_hi] are fast: every stage
+    // active, no band row, rows owned / inside the sets, no event row, for
+    // all rows the block computes and prefetches (r0 .. r0+UNROLL-1+D).
+    const int f_lo = max(ya, g.y0) + 4 * P - 2;
+    const int f_hi = min(yb + 2 * P - 2, g.hy1 + P - 1) - (UNROLL - 1 + D);
+    const int e_lo = ev_lo, e_hi = ev_hi;
 
     // Prefetch ring: the loads of iteration r are issued at iteration r - D
     // into slot (r - r_first) % D.
     float fE[D], fQa[D], fHx[D], fHz[D], fMyh[D], fMxh[D], fCa[D], fCb[D], fMxe[D], fMye[D];
     float fQb[D], fCaB[D], fCbB[D];
-    auto issue = [&](int u, int r, bool live) {
+    auto issue = [&](auto fast_t, int u, int r, bool live) {
+        constexpr bool FAST = decltype(fast_t)::value;
         const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
-        const uint32_t ohA = (uint32_t)(hA * nx) * 4u + c4, oyA = (uint32_t)(yA * nx) * 4u + c4;
-        const uint32_t ohB = (uint32_t)(hB * nx) * 4u + c4, oyB = (uint32_t)(yB * nx) * 4u + c4;
-        fE[u] = b0.ld(live & in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
-        fQa[u] = bm.ld(live & in_rows(hA) & incol, ohA, a.m.oCq);
-        const bool hx_do = live & colE & hx_row(hA);
-        fHx[u] = b0.ld(hx_do, ohA, L.oHx);
-        fMyh[u] = b0.ld(hx_do & fy_h(hA), (uint32_t)(band_y(g, hA) * nx) * 4u + c4, L.oMyh);
-        const bool hz_do = live & colHz & hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2);
-        fHz[u] = b0.ld(hz_do, ohA, L.oHz);
-        fMxh[u] = b0.ld(hz_do & fx_h, (uint32_t)(hA * g.bx) * 4u + bx4, L.oMxh);
-        const bool e_do = live & colE & rowE(yA) & (yA >= ye0);
-        fCa[u] = bm.ld(e_do, oyA, a.m.oCa);
-        fCb[u] = bm.ld(e_do, oyA, a.m.oCb);
-        fMxe[u] = b0.ld(e_do & fx_e, (uint32_t)(yA * g.bx) * 4u + bx4, L.oMxe);
-        fMye[u] = b0.ld(e_do & fy_e(yA), (uint32_t)(band_y(g, yA) * nx) * 4u + c4, L.oMye);
-        fQb[u] = bm.ld(live & in_rows(hB) & incol & (hB >= ya - P), ohB, a.m.oCq);
-        const bool eb_do = live & own & own_row(yB);
-        fCaB[u] = bm.ld(eb_do, oyB, a.m.oCa);
-        fCbB[u] = bm.ld(eb_do, oyB, a.m.oCb);
+        if constexpr (FAST) {
+            const uint32_t rA = (uint32_t)hA * rowb, eA = (uint32_t)yA * rowb;
+            fE[u] = b0.ldv(v_in, L.oE + (uint32_t)r * rowb);
+            fQa[u] = bm.ldv(v_in, a.m.oCq + rA);
+            fHx[u] = b0.ldv(v_e, L.oHx + rA);
+            fHz[u] = b0.ldv(v_hz, L.oHz + rA);
+            fMxh[u] = b0.ldv(xband ? v_mxh : RBuf::OOB, L.oMxh + (uint32_t)hA * brow);
+            fCa[u] = bm.ldv(v_e, a.m.oCa + eA);
+            fCb[u] = bm.ldv(v_e, a.m.oCb + eA);
+            fMxe[u] = b0.ldv(xband ? v_mxe : RBuf::OOB, L.oMxe + (uint32_t)yA * brow);
+            fQb[u] = bm.ldv(v_in, a.m.oCq + (uint32_t)hB * rowb);
+            fCaB[u] = bm.ldv(v_own, a.m.oCa + (uint32_t)yB * rowb);
+            fCbB[u] = bm.ldv(v_own, a.m.oCb + (uint32_t)yB * rowb);
+        } else {
+            const uint32_t ohA = (uint32_t)(hA * nx) * 4u + c4, oyA = (uint32_t)(yA * nx) * 4u + c4;
+            const uint32_t ohB = (uint32_t)(hB * nx) * 4u + c4, oyB = (uint32_t)(yB * nx) * 4u + c4;
+            fE[u] = b0.ld(live & in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
+            fQa[u] = bm.ld(live & in_rows(hA) & incol, ohA, a.m.oCq);
+            const bool hx_do = live & colE & hx_row(hA);
+            fHx[u] = b0.ld(hx_do, ohA, L.oHx);
+            fMyh[u] = b0.ld(hx_do & fy_h(hA), (uint32_t)(band_y(g, hA) * nx) * 4u + c4, L.oMyh);
+            const bool hz_do = live & colHz & hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2);
+            fHz[u] = b0.ld(hz_do, ohA, L.oHz);
+            fMxh[u] = b0.ld(hz_do & fx_h, (uint32_t)(hA * g.bx) * 4u + bx4, L.oMxh);
+            const bool e_do = live & colE & rowE(yA) & (yA >= ye0);
+            fCa[u] = bm.ld(e_do, oyA, a.m.oCa);
+            fCb[u] = bm.ld(e_do, oyA, a.m.oCb);
+            fMxe[u] = b0.ld(e_do & fx_e, (uint32_t)(yA * g.bx) * 4u + bx4, L.oMxe);
+            fMye[u] = b0.ld(e_do & fy_e(yA), (uint32_t)(band_y(g, yA) * nx) * 4u + c4, L.oMye);
+            fQb[u] = bm.ld(live & in_rows(hB) & incol & (hB >= ya - P), ohB, a.m.oCq);
+            const bool eb_do = live & own & own_row(yB);
+            fCaB[u] = bm.ld(eb_do, oyB, a.m.oCa);
+            fCbB[u] = bm.ld(eb_do, oyB, a.m.oCb);
+        }
     };
 
     float ewA[2 * P];    // E^n rows r-2P+1 .. r
@@ -202,92 +254,103 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
         ewA[i] = b0.ld(in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
     }
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue(u, r_first + u, r_first + u <= r_end);
+    for (int u = 0; u < D; ++u) issue(std::false_type{}, u, r_first + u, r_first + u <= r_end);
 
-    for (int r0 = r_first;; r0 += UNROLL) {
+    // One iteration (row r, prefetch slot u).  FAST: the block is fast (all
+    // row predicates true / false as described above).
+    auto iter = [&](auto fast_t, int r, int u) {
+        constexpr bool FAST = decltype(fast_t)::value;
+        const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
+
+        // ---- (a) new E^n row; LDS rows for the two Hz stencils; Hx of stage A
 #pragma unroll
-        for (int uu = 0; uu < UNROLL; ++uu) {
-            const int r = r0 + uu;
-            if (r > r_end) return;
-            const int u = uu % D;
-            const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
-
-            // ---- (a) new E^n row; LDS rows for the two Hz stencils; Hx of stage A
+        for (int i = 0; i < 2 * P - 1; ++i) ewA[i] = ewA[i + 1];
+        ewA[2 * P - 1] = fE[u];
+        rowA[tid] = ewA[P - 1];
+        rowB[tid] = ewB[P];
+        {
+            float d = g.rdy * stencil<P>([&](int k) { return ewA[P - 1 + k]; },
+                                         [&](int k) { return ewA[P - k]; });
+            if (!FAST && fy_h(hA)) {                                    // uniform
+                const float* ct = cyt[hA - yc0];
+                float m = fMyh[u];
+                d = cpml_step(m, ct[0], ct[1], ct[2], d);
+                mfifo[0][slot2(hA)][tid] = m;
+            }
+            const bool hx_ok = FAST ? colE : (colE & hx_row(hA));
+            const float hxn = hx_ok ? fmaf(-fQa[u], d, fHx[u]) : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 2 * P - 1; ++i) ewA[i] = ewA[i + 1];
-            ewA[2 * P - 1] = fE[u];
-            rowA[tid] = ewA[P - 1];
-            rowB[tid] = ewB[P];
-            {
-                float d = g.rdy * stencil<P>([&](int k) { return ewA[P - 1 + k]; },
-                                             [&](int k) { return ewA[P - k]; });
-                if (fy_h(hA)) {                                     // uniform
-                    const float* ct = cyt[hA - yc0];
-                    float m = fMyh[u];
-                    d = cpml_step(m, ct[0], ct[1], ct[2], d);
-                    mfifo[0][slot2(hA)][tid] = m;
-                }
-                const float hxn = (colE & hx_row(hA)) ? fmaf(-fQa[u], d, fHx[u]) : 0.0f;
-#pragma unroll
-                for (int i = 0; i < 2 * P - 1; ++i) hwA[i] = hwA[i + 1];
-                hwA[2 * P - 1] = hxn;
-            }
-            __syncthreads();
+            for (int i = 0; i < 2 * P - 1; ++i) hwA[i] = hwA[i + 1];
+            hwA[2 * P - 1] = hxn;
+        }
+        __syncthreads();
 
-            // ---- (b) Hz of stage A (row hA) and of stage B (row hB)
-            if (hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2)) {   // uniform
-                float d = g.rdx * stencil<P>([&](int k) { return rowA[th + k]; },
-                                             [&](int k) { return rowA[th - k + 1]; });
-                if (xband) {
-                    float m = fMxh[u];
-                    d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
-                    mfifo[1][slot2(hA)][tid] = m;
-                }
-                ringA[slot2(hA)][tid] = hzA_ok ? fmaf(fQa[u], d, fHz[u]) : 0.0f;
+        // ---- (b) Hz of stage A (row hA) and of stage B (row hB)
+        if (FAST || (hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2))) {   // uniform
+            float d = g.rdx * stencil<P>([&](int k) { return rowA[th + k]; },
+                                         [&](int k) { return rowA[th - k + 1]; });
+            if (xband) {
+                float m = fMxh[u];
+                d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
+                mfifo[1][slot2(hA)][tid] = m;
             }
-            if (hz_row(hB) & own_row(hB)) {                             // uniform
-                float d = g.rdx * stencil<P>([&](int k) { return rowB[th + k]; },
-                                             [&](int k) { return rowB[th - k + 1]; });
-                if (xband) {
-                    float m = mfifo[1][slot2(hB)][tid];
-                    d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
-                    b1.st(own & colHz & fx_h, m, (uint32_t)(hB * g.bx) * 4u + bx4, L.oMxh);
-                }
-                const float hzn = hzB_ok ? fmaf(fQb[u], d, ringA[slot2(hB)][tid]) : 0.0f;
-                b1.st(own & colHz, hzn, (uint32_t)(hB * nx) * 4u + c4, L.oHz);
-                ringB[slot1(hB)][tid] = hzn;
+            ringA[slot2(hA)][tid] = hzA_ok ? fmaf(fQa[u], d, fHz[u]) : 0.0f;
+        }
+        if (FAST || (hz_row(hB) & own_row(hB))) {                             // uniform
+            float d = g.rdx * stencil<P>([&](int k) { return rowB[th + k]; },
+                                         [&](int k) { return rowB[th - k + 1]; });
+            if (xband) {
+                float m = mfifo[1][slot2(hB)][tid];
+                d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
+                if constexpr (FAST) b1.stv(m, lane_off(own & colHz & fx_h, bx4), L.oMxh + (uint32_t)hB * brow);
+                else b1.st(own & colHz & fx_h, m, (uint32_t)(hB * g.bx) * 4u + bx4, L.oMxh);
             }
-            __syncthreads();
+            const float hzn = hzB_ok ? fmaf(fQb[u], d, ringA[slot2(hB)][tid]) : 0.0f;
+            if constexpr (FAST) b1.stv(hzn, v_ownhz, L.oHz + (uint32_t)hB * rowb);
+            else b1.st(own & colHz, hzn, (uint32_t)(hB * nx) * 4u + c4, L.oHz);
+            ringB[slot1(hB)][tid] = hzn;
+        }
+        __syncthreads();
 
-            // ---- (c) E of stage A (row yA), with the step-n sources and receivers
-            if (r >= ya) {                                              // uniform
-                const float* hzr = ringA[slot2(yA)];
-                float uu_ = g.rdx * stencil<P>([&](int k) { return hzr[te + k - 1]; },
-                                               [&](int k) { return hzr[te - k]; });
-                if (xband) {
-                    float m = fMxe[u];
-                    uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
-                    mfifo[2][slot2(yA)][tid] = m;
-                }
-                float v = g.rdy * stencil<P>([&](int k) { return hwA[P - 1 + k]; },
-                                             [&](int k) { return hwA[P - k]; });
-                if (fy_e(yA)) {
-                    const float* ct = cyt[yA - yc0];
-                    float m = fMye[u];
-                    v = cpml_step(m, ct[3], ct[4], ct[5], v);
-                    mfifo[3][slot2(yA)][tid] = m;
-                }
-                const float curl = uu_ - v;
-                const float ev = ewA[0];
-                if constexpr (SNAP != SNAP_NONE) {
-                    if ((yA >= g.y0) & (yA < g.y1) & own_row(yA)) {
-                        const uint32_t w = (uint32_t)((yA - g.y0) * g.nxi + (c - g.x0));
-                        snap_put<SNAP>(bse0, own & in_x, w, ev);
-                        snap_put<SNAP>(bsc0, own & in_x, w, curl);
+        // ---- (c) E of stage A (row yA), with the step-n sources and receivers
+        if (FAST || r >= ya) {                                                // uniform
+            const float* hzr = ringA[slot2(yA)];
+            float uu_ = g.rdx * stencil<P>([&](int k) { return hzr[te + k - 1]; },
+                                           [&](int k) { return hzr[te - k]; });
+            if (xband) {
+                float m = fMxe[u];
+                uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
+                mfifo[2][slot2(yA)][tid] = m;
+            }
+            float v = g.rdy * stencil<P>([&](int k) { return hwA[P - 1 + k]; },
+                                         [&](int k) { return hwA[P - k]; });
+            if (!FAST && fy_e(yA)) {
+                const float* ct = cyt[yA - yc0];
+                float m = fMye[u];
+                v = cpml_step(m, ct[3], ct[4], ct[5], v);
+                mfifo[3][slot2(yA)][tid] = m;
+            }
+            const float curl = uu_ - v;
+            const float ev = ewA[0];
+            if constexpr (SNAP != SNAP_NONE) {
+                if constexpr (FAST) {
+                    const uint32_t so = (uint32_t)((yA - g.y0) * g.nxi) * ESZ;
+                    if constexpr (SNAP == SNAP_BF16) {
+                        bse0.stv_bf16(ev, v_snap, so);
+                        bsc0.stv_bf16(curl, v_snap, so);
+                    } else {
+                        bse0.stv(ev, v_snap, so);
+                        bsc0.stv(curl, v_snap, so);
                     }
+                } else if ((yA >= g.y0) & (yA < g.y1) & own_row(yA)) {
+                    const uint32_t w = (uint32_t)((yA - g.y0) * g.nxi + (c - g.x0));
+                    snap_put<SNAP>(bse0, own & in_x, w, ev);
+                    snap_put<SNAP>(bsc0, own & in_x, w, curl);
                 }
-                float en = fmaf(fCa[u], ev, fCb[u] * curl);
-                en = (eA_ok & rowE(yA)) ? en : 0.0f;
+            }
+            float en = fmaf(fCa[u], ev, fCb[u] * curl);
+            en = (FAST ? eA_ok : (eA_ok & rowE(yA))) ? en : 0.0f;
+            if constexpr (!FAST) {
                 const int kb = __builtin_amdgcn_readfirstlane(evs[yA - ye0][0]);
                 const int ke = __builtin_amdgcn_readfirstlane(evs[yA - ye0][1]);
                 for (int k = kb; k < ke; ++k) {                         // distinct source cells of the row
@@ -302,60 +365,93 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
                     if (slot >= 0 && own)
                         a.ev.rec_rows[((int64_t)s * a.ev.n_slots + slot) * nx + c] = en;
                 }
-#pragma unroll
-                for (int i = 0; i < 2 * P - 1; ++i) ewB[i] = ewB[i + 1];
-                ewB[2 * P - 1] = en;
             }
-
-            // ---- Hx of stage B (row hB)
-            if (r >= ya + 2 * P - 1) {                                  // uniform
-                float d = g.rdy * stencil<P>([&](int k) { return ewB[P - 1 + k]; },
-                                             [&](int k) { return ewB[P - k]; });
-                const bool st_h = own & hx_row(hB) & own_row(hB);
-                if (fy_h(hB)) {
-                    const float* ct = cyt[hB - yc0];
-                    float m = mfifo[0][slot2(hB)][tid];
-                    d = cpml_step(m, ct[0], ct[1], ct[2], d);
-                    b1.st(st_h, m, (uint32_t)(band_y(g, hB) * nx) * 4u + c4, L.oMyh);
-                }
-                const float hxn = (colE & hx_row(hB)) ? fmaf(-fQb[u], d, hwA[0]) : 0.0f;
-                b1.st(st_h, hxn, (uint32_t)(hB * nx) * 4u + c4, L.oHx);
 #pragma unroll
-                for (int i = 0; i < 2 * P - 1; ++i) hwB[i] = hwB[i + 1];
-                hwB[2 * P - 1] = hxn;
-            }
+            for (int i = 0; i < 2 * P - 1; ++i) ewB[i] = ewB[i + 1];
+            ewB[2 * P - 1] = en;
+        }
 
-            // ---- E of stage B (row yB): the owned output row
-            if (r >= ya + 4 * P - 2) {                                  // uniform
-                const float* hzr = ringB[slot1(yB)];
-                float uu_ = g.rdx * stencil<P>([&](int k) { return hzr[te + k - 1]; },
-                                               [&](int k) { return hzr[te - k]; });
-                if (xband) {
-                    float m = mfifo[2][slot2(yB)][tid];
-                    uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
-                    b1.st(own & fx_e, m, (uint32_t)(yB * g.bx) * 4u + bx4, L.oMxe);
-                }
-                float v = g.rdy * stencil<P>([&](int k) { return hwB[P - 1 + k]; },
-                                             [&](int k) { return hwB[P - k]; });
-                if (fy_e(yB)) {
-                    const float* ct = cyt[yB - yc0];
-                    float m = mfifo[3][slot2(yB)][tid];
-                    v = cpml_step(m, ct[3], ct[4], ct[5], v);
-                    b1.st(own, m, (uint32_t)(band_y(g, yB) * nx) * 4u + c4, L.oMye);
-                }
-                const float curl = uu_ - v;
-                const float ev = ewB[0];
-                if constexpr (SNAP != SNAP_NONE) {
-                    if ((yB >= g.y0) & (yB < g.y1)) {
-                        const uint32_t w = (uint32_t)((yB - g.y0) * g.nxi + (c - g.x0));
-                        snap_put<SNAP>(bse1, own & in_x, w, ev);
-                        snap_put<SNAP>(bsc1, own & in_x, w, curl);
+        // ---- Hx of stage B (row hB)
+        if (FAST || r >= ya + 2 * P - 1) {                                    // uniform
+            float d = g.rdy * stencil<P>([&](int k) { return ewB[P - 1 + k]; },
+                                         [&](int k) { return ewB[P - k]; });
+            const bool st_h = FAST ? own : (own & hx_row(hB) & own_row(hB));
+            if (!FAST && fy_h(hB)) {
+                const float* ct = cyt[hB - yc0];
+                float m = mfifo[0][slot2(hB)][tid];
+                d = cpml_step(m, ct[0], ct[1], ct[2], d);
+                b1.st(st_h, m, (uint32_t)(band_y(g, hB) * nx) * 4u + c4, L.oMyh);
+            }
+            const bool hx_ok = FAST ? colE : (colE & hx_row(hB));
+            const float hxn = hx_ok ? fmaf(-fQb[u], d, hwA[0]) : 0.0f;
+            if constexpr (FAST) b1.stv(hxn, v_own, L.oHx + (uint32_t)hB * rowb);
+            else b1.st(st_h, hxn, (uint32_t)(hB * nx) * 4u + c4, L.oHx);
+#pragma unroll
+            for (int i = 0; i < 2 * P - 1; ++i) hwB[i] = hwB[i + 1];
+            hwB[2 * P - 1] = hxn;
+        }
+
+        // ---- E of stage B (row yB): the owned output row
+        if (FAST || r >= ya + 4 * P - 2) {                                    // uniform
+            const float* hzr = ringB[slot1(yB)];
+            float uu_ = g.rdx * stencil<P>([&](int k) { return hzr[te + k - 1]; },
+                                           [&](int k) { return hzr[te - k]; });
+            if (xband) {
+                float m = mfifo[2][slot2(yB)][tid];
+                uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
+                if constexpr (FAST) b1.stv(m, lane_off(own & fx_e, bx4), L.oMxe + (uint32_t)yB * brow);
+                else b1.st(own & fx_e, m, (uint32_t)(yB * g.bx) * 4u + bx4, L.oMxe);
+            }
+            float v = g.rdy * stencil<P>([&](int k) { return hwB[P - 1 + k]; },
+                                         [&](int k) { return hwB[P - k]; });
+            if (!FAST && fy_e(yB)) {
+                const float* ct = cyt[yB - yc0];
+                float m = mfifo[3][slot2(yB)][tid];
+                v = cpml_step(m, ct[3], ct[4], ct[5], v);
+                b1.st(own, m, (uint32_t)(band_y(g, yB) * nx) * 4u + c4, L.oMye);
+            }
+            const float curl = uu_ - v;
+            const float ev = ewB[0];
+            if constexpr (SNAP != SNAP_NONE) {
+                if constexpr (FAST) {
+                    const uint32_t so = (uint32_t)((yB - g.y0) * g.nxi) * ESZ;
+                    if constexpr (SNAP == SNAP_BF16) {
+                        bse1.stv_bf16(ev, v_snap, so);
+                        bsc1.stv_bf16(curl, v_snap, so);
+                    } else {
+                        bse1.stv(ev, v_snap, so);
+                        bsc1.stv(curl, v_snap, so);
                     }
+                } else if ((yB >= g.y0) & (yB < g.y1)) {
+                    const uint32_t w = (uint32_t)((yB - g.y0) * g.nxi + (c - g.x0));
+                    snap_put<SNAP>(bse1, own & in_x, w, ev);
+                    snap_put<SNAP>(bsc1, own & in_x, w, curl);
                 }
-                const float en = fmaf(fCaB[u], ev, fCbB[u] * curl);
-                b1.st(own, en, (uint32_t)(yB * nx) * 4u + c4, L.oE);
             }
-            issue(u, r + D, r + D <= r_end);
+            const float en = fmaf(fCaB[u], ev, fCbB[u] * curl);
+            if constexpr (FAST) b1.stv(en, v_own, L.oE + (uint32_t)yB * rowb);
+            else b1.st(own, en, (uint32_t)(yB * nx) * 4u + c4, L.oE);
+        }
+    };
+
+    for (int r0 = r_first;; r0 += UNROLL) {
+        // uniform: all rows this block computes and prefetches are steady
+        const bool fast = r0 >= f_lo && r0 <= f_hi &&
+                          (r0 + UNROLL - 2 * P < e_lo || r0 - 2 * P + 1 > e_hi);
+        if (fast) {
+#pragma unroll
+            for (int uu = 0; uu < UNROLL; ++uu) {
+                iter(std::true_type{}, r0 + uu, uu % D);
+                issue(std::true_type{}, uu % D, r0 + uu + D, true);
+            }
+        } else {
+#pragma unroll
+            for (int uu = 0; uu < UNROLL; ++uu) {
+                const int r = r0 + uu;
+                if (r > r_end) return;
+                iter(std::false_type{}, r, uu % D);
+                issue(std::false_type{}, uu % D, r + D, r + D <= r_end);
+            }
         }
     }
 }
