@@ -274,14 +274,15 @@ def assemble(name, order, eps_int, sig_int, npml, h, nt, n_shots, n_rec, freq,
              obs_eps_int=None, src_cols=None, mu_int=None, cfl_fraction=0.9):
     """Build a Workload from an interior model and acquisition parameters."""
     p = order // 2
-    n_int = eps_int.shape[0]
-    assert eps_int.shape == (n_int, n_int)
+    ny_int, nx_int = eps_int.shape                  # the interior may be rectangular
     eps_r = pad_model(eps_int, npml, p)
     sigma = pad_model(sig_int, npml, p)
     mu_r = pad_model(np.ones_like(eps_int) if mu_int is None else mu_int, npml, p)
-    ny = nx = n_int + 2 * npml + 2 * p
+    ny = ny_int + 2 * npml + 2 * p
+    nx = nx_int + 2 * npml + 2 * p
     y0 = x0 = p + npml
-    y1 = x1 = y0 + n_int
+    y1 = y0 + ny_int
+    x1 = x0 + nx_int
     eps_min = float(eps_r.min()) if obs_eps_int is None else float(min(eps_r.min(), obs_eps_int.min()))
     if dt is None:
         dt = stable_dt(eps_min, float(mu_r.min()), h, h, order, cfl_fraction)
@@ -293,9 +294,9 @@ def assemble(name, order, eps_int, sig_int, npml, h, nt, n_shots, n_rec, freq,
     wav = ricker(freq, nt, dt)
     f = np.repeat(wav[:, None, None], n_shots, axis=1)          # [nt][S][1]
     if src_cols is None:
-        src_cols = spread(n_int, n_shots)
+        src_cols = spread(nx_int, n_shots)
     src = ((y0 + src_row) * nx + x0 + np.asarray(src_cols, dtype=np.int64))[:, None]
-    rec_cols = spread(n_int, n_rec)
+    rec_cols = spread(nx_int, n_rec)
     rec_row_idx = (y0 + rec_row) * nx + x0 + rec_cols
     rec = np.repeat(rec_row_idx[None, :], n_shots, axis=0)
     wl = Workload(
@@ -382,7 +383,7 @@ def make_config(cfg: int, **over) -> Workload:
 
 def random_workload(order, n_int, npml, nt, n_shots, n_src, n_rec, seed, h=0.01,
                     freq=700e6, eps_range=(1.5, 9.0), sig_range=(0.0, 0.02),
-                    identity_pml=False, src_anywhere=False):
+                    identity_pml=False, src_anywhere=False, nx_int=None):
     """A small heterogeneous workload for property tests.
 
     Models are random per cell (not smooth), several sources per shot at
@@ -391,9 +392,10 @@ def random_workload(order, n_int, npml, nt, n_shots, n_src, n_rec, seed, h=0.01,
     through the kernels is exercised.
     """
     rng = np.random.default_rng(seed)
-    eps = rng.uniform(*eps_range, size=(n_int, n_int))
-    sig = rng.uniform(*sig_range, size=(n_int, n_int))
-    mu = rng.uniform(1.0, 2.0, size=(n_int, n_int))
+    shape = (n_int, n_int if nx_int is None else nx_int)   # rows x columns of the interior
+    eps = rng.uniform(*eps_range, size=shape)
+    sig = rng.uniform(*sig_range, size=shape)
+    mu = rng.uniform(1.0, 2.0, size=shape)
     wl = assemble(f"random{seed}", order, eps, sig, npml, h, nt, n_shots, n_rec, freq,
                   mu_int=mu)
     p = order // 2
