@@ -57,7 +57,10 @@ typedef enum tm_status {
 
 typedef enum tm_snap {
     TM_SNAP_F32 = 0,    /* snapshots stored as float32                          */
-    TM_SNAP_BF16 = 1    /* snapshots stored as bfloat16, round-to-nearest-even  */
+    TM_SNAP_BF16 = 1,   /* snapshots stored as bfloat16, round-to-nearest-even  */
+    TM_SNAP_FP8 = 2     /* snapshots stored as OCP FP8 E4M3 (E4M3FN: bias 7, no
+                           infinities, max 448), round-to-nearest-even, finite
+                           values saturated at +-448 (tm_fp8_encode)          */
 } tm_snap;
 
 /* tm_forward flags */
@@ -184,6 +187,18 @@ tm_status tm_grad(const tm_plan* plan, const float* grad_ca_shot, const float* g
 tm_status tm_grad_eps_sigma(const tm_plan* plan, const float* ca, const float* cb,
                             const float* grad_ca, const float* grad_cb, double dt,
                             float* grad_eps_r, float* grad_sigma, void* stream);
+
+/*
+ * The FP8 snapshot encoding (TM_SNAP_FP8; FP8 E4M3 storage of the page's
+ * fp8_e4m3_from_float / fp8_e4m3_to_float, its intrinsic path: OCP E4M3
+ * with saturation to the largest finite value).  encode: float32 -> one
+ * byte per element, round to nearest even, |x| > 448 -> +-448, NaN -> NaN;
+ * decode: byte -> float32 (exact).  in/out: device arrays of n elements
+ * (n >= 0; NULL allowed only for n == 0).  The same conversions are used
+ * by the step kernels.
+ */
+tm_status tm_fp8_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+tm_status tm_fp8_decode(const uint8_t* in, float* out, int64_t n, void* stream);
 
 /*
  * Kernel timing, a diagnostic for roofline figures.  With sampling on

@@ -71,6 +71,12 @@ def lib():
         L.orc_shot_sum.argtypes = [_ll, _ll, _dp, _dp]
         L.orc_eps_sigma_grad.restype = None
         L.orc_eps_sigma_grad.argtypes = [_ll, _dp, _dp, ctypes.c_double, _dp, _dp, _dp, _dp]
+        L.orc_e4m3_encode.restype = ctypes.c_int
+        L.orc_e4m3_encode.argtypes = [ctypes.c_double]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_e4m3_decode.argtypes = [ctypes.c_int]
+        L.orc_quantize_e4m3.restype = None
+        L.orc_quantize_e4m3.argtypes = [_ll, _dp]
         L.orc_num_threads.restype = ctypes.c_int
         L.orc_num_threads.argtypes = []
         L.orc_coefficients.restype = ctypes.c_int
@@ -212,12 +218,34 @@ def eps_sigma_grad(eps_r, sigma, dt, grad_ca, grad_cb):
     return ge, gs
 
 
-def misfit_and_gradient(wl, observed=None):
+def e4m3_encode(x: float) -> int:
+    """FP8 E4M3 code of x (round to nearest even, saturating at +-448)."""
+    return int(lib().orc_e4m3_encode(float(x)))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().orc_e4m3_decode(int(code)))
+
+
+def quantize_e4m3(a: np.ndarray) -> np.ndarray:
+    """Values an FP8 E4M3 snapshot store keeps for ``a`` (a new fp64 array)."""
+    out = np.array(a, dtype=np.float64, order="C", copy=True)
+    lib().orc_quantize_e4m3(out.size, _d(out))
+    return out
+
+
+def misfit_and_gradient(wl, observed=None, snap_quant=None):
     """J = 1/2 ||r - d||^2 (d = 0 when ``observed`` is None) and its gradients.
 
-    Returns dict with records, J, grad_f, per-shot gca/gcb and the shot sums.
+    ``snap_quant="fp8"`` quantizes the stored snapshots to FP8 E4M3 before the
+    adjoint uses them (what an FP8 snapshot store keeps).  Returns dict with
+    records, J, grad_f, per-shot gca/gcb and the shot sums.
     """
     r, _, snaps = forward(wl, store=True)
+    if snap_quant == "fp8":
+        snaps = (quantize_e4m3(snaps[0]), quantize_e4m3(snaps[1]))
+    elif snap_quant is not None:
+        raise ValueError(f"unknown snapshot quantization {snap_quant!r}")
     resid = r if observed is None else r - observed
     J = 0.5 * float(np.sum(resid * resid))
     grad_f, gca, gcb = adjoint(wl, resid, snaps)

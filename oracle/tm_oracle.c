@@ -447,3 +447,49 @@ void orc_eps_sigma_grad(ll n, const double *eps_r, const double *sigma, double d
         if (grad_sigma) grad_sigma[j] = grad_ca[j] * dca_ds + grad_cb[j] * dcb_ds;
     }
 }
+
+/* ---- FP8 E4M3 snapshot quantization ------------------------------------- */
+/*
+ * OCP FP8 E4M3 (the E4M3FN encoding): sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the
+ * exponent field 15 with mantissa 7 is NaN (no infinities), so the largest
+ * finite value is 1.75 * 2^8 = 448.  Encoding rounds to the nearest value,
+ * ties to an even mantissa, and saturates finite values beyond 448 (the
+ * page's intrinsic path converts with saturation to the finite range).
+ */
+double orc_e4m3_decode(int code)
+{
+    const int sign = code & 0x80, e = (code >> 3) & 0xF, m = code & 7;
+    double v;
+    if (e == 0xF && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+int orc_e4m3_encode(double x)
+{
+    if (isnan(x)) return 0x7F;
+    const int sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 448.0) return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {                       /* subnormal range: steps of 2^-9 */
+        const double q = nearbyint(a * 512.0);      /* ties to even (default rounding) */
+        return sign | (int)q;                       /* q == 8 is the smallest normal, code 0x08 */
+    }
+    int k;
+    (void)frexp(a, &k);                             /* a = f 2^k, f in [0.5, 1) */
+    int e = k - 1;                                  /* a in [2^e, 2^(e+1)) */
+    int m = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8) { m = 0; e += 1; }
+    int code = ((e + 7) << 3) | m;
+    if (code > 0x7E) code = 0x7E;
+    return sign | code;
+}
+
+/* x[i] <- decode(encode(float(x[i]))): the value a snapshot store keeps,
+ * with the encoding decision taken on the float32 value as the kernels do. */
+void orc_quantize_e4m3(ll n, double *x)
+{
+    for (ll i = 0; i < n; ++i) x[i] = orc_e4m3_decode(orc_e4m3_encode((double)(float)x[i]));
+}

@@ -65,14 +65,21 @@ def test_valid_plan_and_workspace_size(wl):
     assert native.tm_workspace_bytes(p_ck)[1] < native.tm_workspace_bytes(p_full)[1]
     bf = inputs.make_config(2, n_int=40, nt=400, n_shots=2, n_rec=5, snap="bf16")
     st3, p_bf = native.tm_plan_create(make(bf), bf.cpml, bf.src, bf.rec)
-    assert native.tm_workspace_bytes(p_bf)[1] < native.tm_workspace_bytes(p_full)[1]
-    for p in (p_full, p_ck, p_bf):
+    f8 = inputs.make_config(2, n_int=40, nt=400, n_shots=2, n_rec=5, snap="fp8")
+    st4, p_f8 = native.tm_plan_create(make(f8), f8.cpml, f8.src, f8.rec)
+    assert st3 == st4 == native.TM_OK
+    b_full, b_bf, b_f8 = (native.tm_workspace_bytes(p)[1] for p in (p_full, p_bf, p_f8))
+    # snapshot store: 4, 2 and 1 byte(s) per element
+    elems = 2 * 400 * 2 * 40 * 40
+    assert abs((b_full - b_bf) - 2 * elems) < (1 << 20) and abs((b_bf - b_f8) - elems) < (1 << 20)
+    for p in (p_full, p_ck, p_bf, p_f8):
         native.tm_plan_destroy(p)
 
 
 @pytest.mark.parametrize("field,value", [
     ("order", 3), ("order", 6), ("order", 0), ("n_shots", 0), ("nt", 0), ("n_src", -1),
-    ("snap", 2), ("ckpt_every", -1), ("ny", 5), ("dx", 0.0), ("dy", float("nan")),
+    ("snap", 3), ("snap", -1), ("ckpt_every", -1), ("ny", 5), ("dx", 0.0), ("dy", float("nan")),
+    ("time_block", 3), ("time_block", -1), ("reserved", 1),
     ("pml_y0", 1), ("pml_x1", 10 ** 6), ("pml_y1", 20),
 ])
 def test_invalid_descriptor(wl, field, value):

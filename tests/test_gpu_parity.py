@@ -18,6 +18,10 @@ pytestmark = pytest.mark.gpu
 
 REC_TOL = 1e-5
 GRAD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+# FP8 snapshots against the oracle's FP8-quantized snapshots: both sides
+# quantize float32 values, whose fp32/fp64 differences (~1e-7) flip a code
+# only for values within that distance of a rounding midpoint.
+FP8_TOL = 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -181,7 +185,7 @@ def test_batched_shots_bitwise_equal_single_shots():
 
 
 @pytest.mark.parametrize("order", inputs.ORDERS)
-@pytest.mark.parametrize("snap,ckpt", [("f32", 0), ("bf16", 0), ("f32", 7)])
+@pytest.mark.parametrize("snap,ckpt", [("f32", 0), ("bf16", 0), ("fp8", 0), ("f32", 7)])
 def test_two_step_launch_bitwise_equals_single_steps(order, snap, ckpt):
     """Two time steps per launch (with the first step's sources and receivers
     inside the kernel) give bitwise the state, records and gradients of one
@@ -281,3 +285,63 @@ def test_grad_eps_sigma(orc, order):
     mask = np.zeros((wl.ny, wl.nx), bool)
     mask[wl.pml_y0:wl.pml_y1, wl.pml_x0:wl.pml_x1] = True
     assert not np.any(got_e[~mask]) and not np.any(got_s[~mask])
+
+
+def test_fp8_conversion_matches_oracle(orc):
+    """tm_fp8_encode / tm_fp8_decode (the conversions of the FP8 snapshot
+    store) against the oracle's encoder written from the E4M3 format."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    vals = [orc.e4m3_decode(c) for c in range(0x7F)]
+    mids = [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+    rng = np.random.default_rng(9)
+    x = np.concatenate([
+        np.float32(vals), -np.float32(vals), np.float32(mids), -np.float32(mids),
+        np.nextafter(np.float32(mids), np.float32(0)), np.nextafter(np.float32(mids), np.float32(1e9)),
+        np.float32([448.0, 449.0, 464.0, 1e5, -1e30, np.inf, -np.inf, 2.0 ** -10, 2.0 ** -11, -0.0]),
+        (2.0 ** rng.uniform(-14, 10, 20000) * rng.choice([-1, 1], 20000)).astype(np.float32),
+    ]).astype(np.float32)
+    dev = torch.device("cuda")
+    xin = torch.from_numpy(x).to(dev)
+    codes = torch.empty(x.size, dtype=torch.uint8, device=dev)
+    assert native.tm_fp8_encode(native.ptr(xin), native.ptr(codes), x.size, native.stream_handle()) == 0
+    allc = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(dev)
+    dec = torch.empty(256, dtype=torch.float32, device=dev)
+    assert native.tm_fp8_decode(native.ptr(allc), native.ptr(dec), 256, native.stream_handle()) == 0
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    ref = np.array([orc.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:10]]
+    d = dec.cpu().numpy().astype(np.float64)
+    r = np.array([orc.e4m3_decode(c) for c in range(256)])
+    np.testing.assert_array_equal(np.isnan(d), np.isnan(r))
+    np.testing.assert_array_equal(d[~np.isnan(d)], r[~np.isnan(r)])
+    # a NaN input stays NaN
+    nan = torch.full((4,), float("nan"), device=dev)
+    c4 = torch.empty(4, dtype=torch.uint8, device=dev)
+    assert native.tm_fp8_encode(native.ptr(nan), native.ptr(c4), 4, native.stream_handle()) == 0
+    assert all((int(v) & 0x7F) == 0x7F for v in c4.cpu().numpy())
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_fp8_snapshots(orc, order):
+    """FP8 E4M3 snapshots against the oracle's adjoint of the same quantized
+    snapshots (the oracle quantizes its float32-rounded values, as the kernels
+    do)."""
+    wl = inputs.as_f32(inputs.random_workload(order, 60, 8, nt=140, n_shots=2, n_src=1, n_rec=9,
+                                              seed=220 + order))
+    ref = orc.misfit_and_gradient(wl, snap_quant="fp8")
+    got = run_gpu(wl, snap="fp8", grad_r=ref["residual"])
+    e_r = rel_l2(got["records"], ref["records"])
+    e_a = rel_l2(got["gca_shot"], ref["gca_shot"])
+    e_b = rel_l2(got["gcb_shot"], ref["gcb_shot"])
+    e_f = rel_l2(got["grad_f"], ref["grad_f"])
+    exact = orc.misfit_and_gradient(wl)
+    q_a = rel_l2(ref["gca_shot"], exact["gca_shot"])
+    print(f"[fp8-o{order}] records {e_r:.2e}  gCa {e_a:.2e}  gCb {e_b:.2e}  grad_f {e_f:.2e}  "
+          f"(fp8 vs exact snapshots in the oracle: gCa {q_a:.2e})", flush=True)
+    assert e_r <= REC_TOL and e_f <= GRAD_TOL["f32"]
+    assert e_a <= FP8_TOL and e_b <= FP8_TOL

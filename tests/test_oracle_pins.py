@@ -397,3 +397,39 @@ def test_eps_sigma_gradient_matches_central_differences(orc, order):
     mask = np.zeros((wl.ny, wl.nx), bool)
     mask[wl.pml_y0:wl.pml_y1, wl.pml_x0:wl.pml_x1] = True
     assert np.all(ge[~mask] == 0.0) and np.all(gs[~mask] == 0.0)
+
+
+def test_e4m3_encoding_pinned_to_format_and_library(orc):
+    """The oracle's FP8 E4M3 encoder against the format's published values,
+    its code ordering, and torch's float8_e4m3fn conversion (an independent
+    round-to-nearest-even implementation) on in-range values; saturation
+    beyond the largest finite value as the page's intrinsic path does."""
+    import torch
+
+    # published values of the E4M3FN encoding
+    for value, code in ((1.0, 0x38), (448.0, 0x7E), (2.0 ** -6, 0x08), (2.0 ** -9, 0x01), (-2.0, 0xC0),
+                        (0.0, 0x00), (1.75, 0x3E), (240.0, 0x77)):
+        assert orc.e4m3_encode(value) == code, (value, code)
+        assert orc.e4m3_decode(code) == value
+    assert np.isnan(orc.e4m3_decode(0x7F)) and orc.e4m3_encode(float("nan")) == 0x7F
+    # every finite code: strictly increasing values, exact round trip, sign symmetry
+    vals = [orc.e4m3_decode(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))
+    for c in range(0x7F):
+        assert orc.e4m3_encode(vals[c]) == c
+        assert orc.e4m3_encode(-vals[c]) == (c | 0x80 if c else 0x80 if np.signbit(-vals[c]) else 0)
+    # saturation (finite and infinite) beyond 448
+    for x in (448.0001, 464.0, 1e6, float("inf")):
+        assert orc.e4m3_encode(x) == 0x7E and orc.e4m3_encode(-x) == 0xFE
+    # in-range values, including every midpoint between adjacent codes and
+    # its float32 neighbours, against torch's conversion
+    rng = np.random.default_rng(8)
+    mids = [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+    x = np.concatenate([
+        np.float32(mids), np.nextafter(np.float32(mids), np.float32(0)), np.nextafter(np.float32(mids), np.float32(1e9)),
+        np.float32(vals), (2.0 ** rng.uniform(-12, 8.8, 200000) * rng.choice([-1, 1], 200000)).astype(np.float32),
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    ours = orc.quantize_e4m3(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)

@@ -69,7 +69,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v)
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// float -> OCP FP8 E4M3 bits (the E4M3FN encoding: exponent bias 7, no
+// infinities, largest finite 448), round to nearest even; finite values
+// beyond +-448 saturate to +-448 and NaN stays NaN.  The conversion
+// instruction rounds; the input is clamped first so that no finite value
+// becomes NaN.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+{
+    const float c = __builtin_isnan(v) ? v : fminf(fmaxf(v, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false) & 0xffu;
+}
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
 // Snapshot element types.
-enum SnapKind { SNAP_NONE = 0, SNAP_F32 = 1, SNAP_BF16 = 2 };
+enum SnapKind { SNAP_NONE = 0, SNAP_F32 = 1, SNAP_BF16 = 2, SNAP_FP8 = 3 };
+
+// Bytes of one snapshot element.
+template <int SNAP>
+constexpr uint32_t snap_bytes() { return SNAP == SNAP_BF16 ? 2u : SNAP == SNAP_FP8 ? 1u : 4u; }
 
 }  // namespace tmf

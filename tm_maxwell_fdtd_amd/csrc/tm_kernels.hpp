@@ -134,6 +134,24 @@ __global__ __launch_bounds__(256) void k_eps_sigma(int64_t n, const float* __res
 }
 
 // ---------------------------------------------------------------------------
+// Element-wise conversion to and from the FP8 E4M3 snapshot encoding
+// (f32_to_e4m3 / e4m3_to_f32).
+__global__ __launch_bounds__(256) void k_fp8_encode(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                                    int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride)
+        out[j] = (uint8_t)f32_to_e4m3(in[j]);
+}
+__global__ __launch_bounds__(256) void k_fp8_decode(const uint8_t* __restrict__ in, float* __restrict__ out,
+                                                    int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride)
+        out[j] = e4m3_to_f32(in[j]);
+}
+
+// ---------------------------------------------------------------------------
 // Fill with zeros (used instead of memset so callers may capture the calls).
 __global__ __launch_bounds__(256) void k_zero(float* __restrict__ p, int64_t n)
 {

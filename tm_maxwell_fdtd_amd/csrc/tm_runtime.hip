@@ -269,7 +269,7 @@ bool make_layout(tm_plan* p)
     L.aset[0] = take(L.set_bytes);
     L.aset[1] = take(L.set_bytes);
     L.adj_bytes = o - L.adj;
-    const uint64_t esz = d.snap == TM_SNAP_BF16 ? 2 : 4;
+    const uint64_t esz = d.snap == TM_SNAP_BF16 ? 2 : d.snap == TM_SNAP_FP8 ? 1 : 4;
     L.snap_shot = (uint64_t)g.nyi * (uint64_t)g.nxi * esz;
     L.snap_step = align_up(S * L.snap_shot);
     L.snapE = take(L.snap_step * (uint64_t)p->seg_steps);
@@ -451,6 +451,7 @@ void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int6
     timed(p, KID_FWD_STEP, t, st, [&] {
         if (snap == SNAP_F32) k_fwd_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
         else if (snap == SNAP_BF16) k_fwd_step<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_FP8) k_fwd_step<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
         else k_fwd_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
     const float* ft = ns > 0 ? f + t * S * ns : nullptr;
@@ -499,6 +500,7 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int
     timed(p, KID_FWD_STEP2, t, st, [&] {
         if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
         else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
         else k_fwd_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
     const float* ft = ns > 0 ? f + (t + 1) * S * ns : nullptr;
@@ -541,11 +543,15 @@ void adj_step(tm_plan* p, const Ptrs& q, const float* grad_r, float* grad_f, int
     timed(p, KID_ADJ_STEP, t, st, [&] {
         if (snap == SNAP_F32) k_adj_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
         else if (snap == SNAP_BF16) k_adj_step<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_FP8) k_adj_step<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
         else k_adj_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
 }
 
-int snap_kind(const tm_plan* p) { return p->d.snap == TM_SNAP_BF16 ? SNAP_BF16 : SNAP_F32; }
+int snap_kind(const tm_plan* p)
+{
+    return p->d.snap == TM_SNAP_BF16 ? SNAP_BF16 : p->d.snap == TM_SNAP_FP8 ? SNAP_FP8 : SNAP_F32;
+}
 
 tm_status check_ws(const tm_plan* p, void* ws, uint64_t ws_bytes)
 {
@@ -579,17 +585,18 @@ tm_status device_tiling(tm_plan* p)
     int dev = 0;
     HIPCHK(hipGetDevice(&dev));
     if (dev == p->tiling_device) return TM_OK;
-    const bool bf = p->d.snap == TM_SNAP_BF16;
-    int64_t cf = 0, ca = 0;
-    tm_status v = resident(bf ? reinterpret_cast<const void*>(&k_fwd_step<P, SNAP_BF16>)
-                              : reinterpret_cast<const void*>(&k_fwd_step<P, SNAP_F32>), &cf);
+    // occupancy of the storing instances (the ones the full step launches)
+    auto pick = [&](auto f32, auto b16, auto f8) -> const void* {
+        return p->d.snap == TM_SNAP_BF16 ? reinterpret_cast<const void*>(b16)
+             : p->d.snap == TM_SNAP_FP8  ? reinterpret_cast<const void*>(f8)
+                                         : reinterpret_cast<const void*>(f32);
+    };
+    int64_t cf = 0, ca = 0, c2 = 0;
+    tm_status v = resident(pick(&k_fwd_step<P, SNAP_F32>, &k_fwd_step<P, SNAP_BF16>, &k_fwd_step<P, SNAP_FP8>), &cf);
     if (v != TM_OK) return v;
-    v = resident(bf ? reinterpret_cast<const void*>(&k_adj_step<P, SNAP_BF16>)
-                    : reinterpret_cast<const void*>(&k_adj_step<P, SNAP_F32>), &ca);
+    v = resident(pick(&k_adj_step<P, SNAP_F32>, &k_adj_step<P, SNAP_BF16>, &k_adj_step<P, SNAP_FP8>), &ca);
     if (v != TM_OK) return v;
-    int64_t c2 = 0;
-    v = resident(bf ? reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_BF16>)
-                    : reinterpret_cast<const void*>(&k_fwd_step2<P, SNAP_F32>), &c2);
+    v = resident(pick(&k_fwd_step2<P, SNAP_F32>, &k_fwd_step2<P, SNAP_BF16>, &k_fwd_step2<P, SNAP_FP8>), &c2);
     if (v != TM_OK) return v;
     p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W);
     p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W);
@@ -736,7 +743,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     if (d.order != 2 && d.order != 4 && d.order != 8) return TM_EINVAL;
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
-    if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16) return TM_EINVAL;
+    if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16 && d.snap != TM_SNAP_FP8) return TM_EINVAL;
     if (d.time_block < 0 || d.time_block > 2 || d.reserved != 0) return TM_EINVAL;
     if (d.ny < 2 * P + 2 || d.nx < 2 * P + 2) return TM_EINVAL;
     if (d.ny * d.nx >= (int64_t(1) << 29)) return TM_EINVAL;
@@ -984,5 +991,23 @@ TM_API tm_status tm_grad_eps_sigma(const tm_plan* p, const float* ca, const floa
     const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
     k_eps_sigma<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(n, ca, cb, grad_ca, grad_cb, (float)(1.0 / dt),
                                                              grad_eps_r, grad_sigma);
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
+
+TM_API tm_status tm_fp8_encode(const float* in, uint8_t* out, int64_t n, void* stream)
+{
+    if (n < 0 || (n > 0 && (in == nullptr || out == nullptr))) return TM_EINVAL;
+    if (n == 0) return TM_OK;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    k_fp8_encode<<<dim3((unsigned)blocks), dim3(256), 0, as_stream(stream)>>>(in, out, n);
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
+
+TM_API tm_status tm_fp8_decode(const uint8_t* in, float* out, int64_t n, void* stream)
+{
+    if (n < 0 || (n > 0 && (in == nullptr || out == nullptr))) return TM_EINVAL;
+    if (n == 0) return TM_OK;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    k_fp8_decode<<<dim3((unsigned)blocks), dim3(256), 0, as_stream(stream)>>>(in, out, n);
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }

@@ -175,6 +175,14 @@ struct RBuf {
     {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, (int)soff, 0);
     }
+    __device__ __forceinline__ float ld_fp8(bool ok, uint32_t off) const
+    {
+        return e4m3_to_f32(__builtin_amdgcn_raw_buffer_load_b8(r, ok ? (int)off : OOB, 0, 0));
+    }
+    __device__ __forceinline__ void stv_fp8(float v, int voff, uint32_t soff) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f32_to_e4m3(v), r, voff, (int)soff, 0);
+    }
 };
 
 // Lane offset, or the out-of-range offset where the lane is masked.
@@ -186,13 +194,24 @@ __device__ __forceinline__ void snap_put(const RBuf& b, bool ok, uint32_t w, flo
 {
     if constexpr (SNAP == SNAP_F32) b.st(ok, v, w * 4u, 0u);
     else if constexpr (SNAP == SNAP_BF16) b.st_bf16(ok, v, w * 2u);
+    else if constexpr (SNAP == SNAP_FP8) b.stv_fp8(v, lane_off(ok, w), 0u);
 }
 template <int SNAP>
 __device__ __forceinline__ float snap_get(const RBuf& b, bool ok, uint32_t w)
 {
     if constexpr (SNAP == SNAP_F32) return b.ld(ok, w * 4u, 0u);
     else if constexpr (SNAP == SNAP_BF16) return b.ld_bf16(ok, w * 2u);
+    else if constexpr (SNAP == SNAP_FP8) return b.ld_fp8(ok, w);
     else return 0.0f;
+}
+// Store with a precomputed lane offset (bytes, out of range where masked)
+// and a uniform row offset.
+template <int SNAP>
+__device__ __forceinline__ void snap_putv(const RBuf& b, float v, int voff, uint32_t soff)
+{
+    if constexpr (SNAP == SNAP_F32) b.stv(v, voff, soff);
+    else if constexpr (SNAP == SNAP_BF16) b.stv_bf16(v, voff, soff);
+    else if constexpr (SNAP == SNAP_FP8) b.stv_fp8(v, voff, soff);
 }
 
 // Layout of one shot's state block (byte offsets of the sub-arrays).

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH;
     constexpr int R2 = 2 * P;                       // ring / FIFO depth (a power of two)
-    constexpr uint32_t ESZ = SNAP == SNAP_BF16 ? 2u : 4u;
+    constexpr uint32_t ESZ = snap_bytes<SNAP>();
     __shared__ float rowA[NT];                      // E^n row hA
     __shared__ float rowB[NT];                      // E^{n+1} row hB
     __shared__ float ringA[R2][NT];                 // Hz^{n+1/2} rows
@@ -335,13 +335,8 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
             if constexpr (SNAP != SNAP_NONE) {
                 if constexpr (FAST) {
                     const uint32_t so = (uint32_t)((yA - g.y0) * g.nxi) * ESZ;
-                    if constexpr (SNAP == SNAP_BF16) {
-                        bse0.stv_bf16(ev, v_snap, so);
-                        bsc0.stv_bf16(curl, v_snap, so);
-                    } else {
-                        bse0.stv(ev, v_snap, so);
-                        bsc0.stv(curl, v_snap, so);
-                    }
+                    snap_putv<SNAP>(bse0, ev, v_snap, so);
+                    snap_putv<SNAP>(bsc0, curl, v_snap, so);
                 } else if ((yA >= g.y0) & (yA < g.y1) & own_row(yA)) {
                     const uint32_t w = (uint32_t)((yA - g.y0) * g.nxi + (c - g.x0));
                     snap_put<SNAP>(bse0, own & in_x, w, ev);
@@ -415,13 +410,8 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
             if constexpr (SNAP != SNAP_NONE) {
                 if constexpr (FAST) {
                     const uint32_t so = (uint32_t)((yB - g.y0) * g.nxi) * ESZ;
-                    if constexpr (SNAP == SNAP_BF16) {
-                        bse1.stv_bf16(ev, v_snap, so);
-                        bsc1.stv_bf16(curl, v_snap, so);
-                    } else {
-                        bse1.stv(ev, v_snap, so);
-                        bsc1.stv(curl, v_snap, so);
-                    }
+                    snap_putv<SNAP>(bse1, ev, v_snap, so);
+                    snap_putv<SNAP>(bsc1, curl, v_snap, so);
                 } else if ((yB >= g.y0) & (yB < g.y1)) {
                     const uint32_t w = (uint32_t)((yB - g.y0) * g.nxi + (c - g.x0));
                     snap_put<SNAP>(bse1, own & in_x, w, ev);

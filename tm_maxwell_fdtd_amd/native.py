@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libtm_fdtd.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "tm_fdtd.h")
 
 TM_OK, TM_EINVAL, TM_EUNSTABLE, TM_ENOMEM, TM_EHIP, TM_ESTATE, TM_ENONFINITE = range(7)
-TM_SNAP_F32, TM_SNAP_BF16 = 0, 1
+TM_SNAP_F32, TM_SNAP_BF16, TM_SNAP_FP8 = 0, 1, 2
+SNAP_KINDS = {"f32": TM_SNAP_F32, "bf16": TM_SNAP_BF16, "fp8": TM_SNAP_FP8}
 TM_FWD_STORE, TM_FWD_CHECK = 1, 2
 
 _STATUS_NAMES = {0: "TM_OK", 1: "TM_EINVAL", 2: "TM_EUNSTABLE", 3: "TM_ENOMEM", 4: "TM_EHIP",
@@ -79,6 +80,10 @@ def lib():
         L.tm_adjoint.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.tm_grad.restype = ctypes.c_int
         L.tm_grad.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+        L.tm_fp8_encode.restype = ctypes.c_int
+        L.tm_fp8_encode.argtypes = [_vp, _vp, ctypes.c_int64, _vp]
+        L.tm_fp8_decode.restype = ctypes.c_int
+        L.tm_fp8_decode.argtypes = [_vp, _vp, ctypes.c_int64, _vp]
         L.tm_grad_eps_sigma.restype = ctypes.c_int
         L.tm_grad_eps_sigma.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp, _vp]
         L.tm_timing_enable.restype = ctypes.c_int
@@ -169,6 +174,14 @@ def tm_grad(plan, grad_ca_shot, grad_cb_shot, grad_ca, grad_cb, stream):
     return lib().tm_grad(plan, grad_ca_shot, grad_cb_shot, grad_ca, grad_cb, stream)
 
 
+def tm_fp8_encode(inp, out, n, stream):
+    return lib().tm_fp8_encode(inp, out, n, stream)
+
+
+def tm_fp8_decode(inp, out, n, stream):
+    return lib().tm_fp8_decode(inp, out, n, stream)
+
+
 def tm_grad_eps_sigma(plan, ca, cb, grad_ca, grad_cb, dt, grad_eps_r, grad_sigma, stream):
     return lib().tm_grad_eps_sigma(plan, ca, cb, grad_ca, grad_cb, dt, grad_eps_r, grad_sigma, stream)
 
@@ -204,7 +217,7 @@ def tm_timing_read(plan):
 def make_desc(wl, snap: Optional[str] = None, ckpt_every: Optional[int] = None, hbm_budget: int = 0,
               time_block: int = 0) -> tm_desc:
     snap = wl.snap if snap is None else snap
-    return tm_desc(order=wl.order, snap=TM_SNAP_BF16 if snap == "bf16" else TM_SNAP_F32,
+    return tm_desc(order=wl.order, snap=SNAP_KINDS[snap],
                    n_shots=wl.n_shots, ny=wl.ny, nx=wl.nx,
                    pml_y0=wl.pml_y0, pml_y1=wl.pml_y1, pml_x0=wl.pml_x0, pml_x1=wl.pml_x1,
                    dy=wl.dy, dx=wl.dx, nt=wl.nt, n_src=wl.n_src, n_rec=wl.n_rec,
