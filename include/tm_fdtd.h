@@ -67,6 +67,17 @@ typedef enum tm_snap {
 #define TM_FWD_STORE 1  /* keep what tm_adjoint needs: snapshots, or checkpoints */
 #define TM_FWD_CHECK 2  /* check the Courant number before stepping (synchronises) */
 
+typedef enum tm_storage {
+    TM_STORE_DEVICE = 0,    /* snapshots in the device workspace                */
+    TM_STORE_HOST = 1       /* snapshots in a pinned host store that the plan
+                               allocates at the first storing forward (size
+                               ceil(nt / step_ratio) * 2 * S * ny_i * nx_i *
+                               element bytes); the workspace holds a ring of 3
+                               device slots, copied out after each stored step
+                               on a copy stream of the plan and prefetched back
+                               in the adjoint.  Not with checkpoints.          */
+} tm_storage;
+
 typedef struct tm_desc {
     int32_t order;          /* spatial order: 2, 4 or 8                         */
     int32_t snap;           /* tm_snap                                          */
@@ -83,7 +94,12 @@ typedef struct tm_desc {
     int32_t time_block;     /* forward time steps per launch: 1, or 2 (two steps
                                in one pass over the state); 0 = default (2).
                                Both give bitwise the same results.             */
-    int32_t reserved;       /* must be 0                                        */
+    int32_t storage;        /* tm_storage: where a storing forward keeps the
+                               snapshots (full-store mode only)                */
+    int64_t step_ratio;     /* store snapshots (and accumulate gradients) every
+                               step_ratio-th step only, weighting each term by
+                               step_ratio (an approximation); 0 or 1 = every
+                               step.  Full-store mode only.                     */
 } tm_desc;
 
 typedef struct tm_plan tm_plan;

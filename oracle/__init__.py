@@ -234,18 +234,34 @@ def quantize_e4m3(a: np.ndarray) -> np.ndarray:
     return out
 
 
-def misfit_and_gradient(wl, observed=None, snap_quant=None):
+def subsample_snapshots(snaps, step_ratio: int):
+    """Snapshots as a store that keeps every ``step_ratio``-th step sees them:
+    the kept steps (t % step_ratio == 0) weighted by step_ratio, the others
+    zero, so the adjoint's gradient becomes
+    sum over kept t of step_ratio * lambda^{t+1} * snapshot^t."""
+    out = []
+    for a in snaps:
+        b = np.zeros_like(a)
+        b[::step_ratio] = a[::step_ratio] * float(step_ratio)
+        out.append(b)
+    return tuple(out)
+
+
+def misfit_and_gradient(wl, observed=None, snap_quant=None, step_ratio=1):
     """J = 1/2 ||r - d||^2 (d = 0 when ``observed`` is None) and its gradients.
 
     ``snap_quant="fp8"`` quantizes the stored snapshots to FP8 E4M3 before the
-    adjoint uses them (what an FP8 snapshot store keeps).  Returns dict with
-    records, J, grad_f, per-shot gca/gcb and the shot sums.
+    adjoint uses them (what an FP8 snapshot store keeps); ``step_ratio`` > 1
+    keeps every step_ratio-th snapshot only (``subsample_snapshots``).
+    Returns dict with records, J, grad_f, per-shot gca/gcb and the shot sums.
     """
     r, _, snaps = forward(wl, store=True)
     if snap_quant == "fp8":
         snaps = (quantize_e4m3(snaps[0]), quantize_e4m3(snaps[1]))
     elif snap_quant is not None:
         raise ValueError(f"unknown snapshot quantization {snap_quant!r}")
+    if step_ratio > 1:
+        snaps = subsample_snapshots(snaps, step_ratio)
     resid = r if observed is None else r - observed
     J = 0.5 * float(np.sum(resid * resid))
     grad_f, gca, gcb = adjoint(wl, resid, snaps)

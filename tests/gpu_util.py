@@ -29,8 +29,12 @@ def run_oracle(orc, wl, observed=None):
     return orc.misfit_and_gradient(wl, observed=observed)
 
 
-def run_gpu(wl, observed=None, snap=None, ckpt_every=None, grad_r=None, obs_coefs=None, time_block=0):
+def run_gpu(wl, observed=None, snap=None, ckpt_every=None, grad_r=None, obs_coefs=None, time_block=0,
+            storage=0, step_ratio=0, chunks=None):
     """Forward (storing), residual, adjoint and shot sum on the GPU.
+
+    ``storage`` / ``step_ratio`` / ``time_block`` are the plan options of the
+    same names; ``chunks`` runs the forward in time chunks split at those steps.
 
     ``observed``: records of the observed model, a numpy array, or the
     string "gpu" to compute them on the GPU from the workload's observed
@@ -40,9 +44,16 @@ def run_gpu(wl, observed=None, snap=None, ckpt_every=None, grad_r=None, obs_coef
 
     from tm_maxwell_fdtd_amd import native
 
-    prop = native.Propagator(wl, snap=snap, ckpt_every=ckpt_every, time_block=time_block)
+    prop = native.Propagator(wl, snap=snap, ckpt_every=ckpt_every, time_block=time_block, storage=storage,
+                             step_ratio=step_ratio)
     try:
-        r = prop.forward(store=True)
+        if chunks is None:
+            r = prop.forward(store=True)
+        else:                                   # the forward in time chunks [0, c1), [c1, c2), ...
+            r = None
+            bounds = [0, *chunks, wl.nt]
+            for t0, t1 in zip(bounds, bounds[1:]):
+                r = prop.forward(r=r, store=True, t0=t0, t1=t1)
         if grad_r is not None:
             resid = torch.as_tensor(np.asarray(grad_r, np.float32), device=prop.device)
         elif observed is None:

@@ -79,7 +79,7 @@ def test_valid_plan_and_workspace_size(wl):
 @pytest.mark.parametrize("field,value", [
     ("order", 3), ("order", 6), ("order", 0), ("n_shots", 0), ("nt", 0), ("n_src", -1),
     ("snap", 3), ("snap", -1), ("ckpt_every", -1), ("ny", 5), ("dx", 0.0), ("dy", float("nan")),
-    ("time_block", 3), ("time_block", -1), ("reserved", 1),
+    ("time_block", 3), ("time_block", -1), ("storage", 2), ("step_ratio", -1),
     ("pml_y0", 1), ("pml_x1", 10 ** 6), ("pml_y1", 20),
 ])
 def test_invalid_descriptor(wl, field, value):
@@ -169,3 +169,21 @@ def test_call_sequence_checked_before_launch(wl):
         assert native.tm_grad(plan, None, None, None, dev, None) == native.TM_EINVAL
     finally:
         native.tm_plan_destroy(plan)
+
+
+def test_storage_options_exclude_checkpoints(wl):
+    """Host storage and step ratios apply to the full store only."""
+    assert create(wl, storage=native.TM_STORE_HOST) == native.TM_OK
+    assert create(wl, step_ratio=3) == native.TM_OK
+    assert create(wl, storage=native.TM_STORE_HOST, step_ratio=4) == native.TM_OK
+    assert create(wl, storage=native.TM_STORE_HOST, ckpt_every=5) == native.TM_EINVAL
+    assert create(wl, step_ratio=2, ckpt_every=5) == native.TM_EINVAL
+    # host storage keeps only a ring of device slots in the workspace
+    st, p_dev = native.tm_plan_create(make(wl), wl.cpml, wl.src, wl.rec)
+    st2, p_host = native.tm_plan_create(make(wl, storage=native.TM_STORE_HOST), wl.cpml, wl.src, wl.rec)
+    st3, p_r = native.tm_plan_create(make(wl, step_ratio=4), wl.cpml, wl.src, wl.rec)
+    assert st == st2 == st3 == native.TM_OK
+    b_dev, b_host, b_r = (native.tm_workspace_bytes(p)[1] for p in (p_dev, p_host, p_r))
+    assert b_host < b_r < b_dev
+    for p in (p_dev, p_host, p_r):
+        native.tm_plan_destroy(p)

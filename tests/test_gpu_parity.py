@@ -345,3 +345,34 @@ def test_fp8_snapshots(orc, order):
           f"(fp8 vs exact snapshots in the oracle: gCa {q_a:.2e})", flush=True)
     assert e_r <= REC_TOL and e_f <= GRAD_TOL["f32"]
     assert e_a <= FP8_TOL and e_b <= FP8_TOL
+
+
+@pytest.mark.parametrize("snap", ["f32", "bf16", "fp8"])
+def test_host_storage_bitwise_equals_device_storage(snap):
+    """Snapshots kept in pinned host memory through a ring of device slots
+    give bitwise the results of the device store (one and two steps per
+    launch, whole and chunked forward)."""
+    wl = inputs.as_f32(inputs.random_workload(8, 60, 8, nt=47, n_shots=2, n_src=2, n_rec=6, seed=730,
+                                              src_anywhere=True))
+    dev = run_gpu(wl, snap=snap)
+    for tb, chunks in ((2, None), (1, None), (2, [13, 30])):
+        host = run_gpu(wl, snap=snap, storage=1, time_block=tb, chunks=chunks)
+        for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+            np.testing.assert_array_equal(host[key], dev[key], err_msg=f"{snap} time_block {tb} {chunks} {key}")
+
+
+@pytest.mark.parametrize("ratio,storage", [(2, 0), (3, 0), (3, 1), (5, 1)])
+def test_step_ratio(orc, ratio, storage):
+    """Snapshots every R-th step, gradient terms weighted by R, against the
+    oracle's gradient of the same subsampled store; R = 1 is checked by every
+    other test."""
+    wl = inputs.as_f32(inputs.random_workload(4, 50, 8, nt=61, n_shots=2, n_src=1, n_rec=7, seed=740 + ratio))
+    ref = orc.misfit_and_gradient(wl, step_ratio=ratio)
+    got = run_gpu(wl, snap="f32", grad_r=ref["residual"], storage=storage, step_ratio=ratio)
+    full = orc.misfit_and_gradient(wl)
+    e_a, e_b = rel_l2(got["gca_shot"], ref["gca_shot"]), rel_l2(got["gcb_shot"], ref["gcb_shot"])
+    e_r = rel_l2(got["records"], ref["records"])
+    print(f"[step ratio {ratio}, storage {storage}] records {e_r:.2e}  gCa {e_a:.2e}  gCb {e_b:.2e}  "
+          f"(subsampled vs full gradient in the oracle: {rel_l2(ref['gca'], full['gca']):.2e})", flush=True)
+    assert e_r <= REC_TOL
+    assert e_a <= GRAD_TOL["f32"] and e_b <= GRAD_TOL["f32"]

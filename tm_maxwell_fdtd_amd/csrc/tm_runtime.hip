@@ -167,6 +167,10 @@ struct Layout {
 
 }  // namespace
 
+// Device slots of the host snapshot store (copies of one slot overlap the
+// kernels writing or reading the others).
+constexpr int HOST_RING = 3;
+
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
 enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_COUNT };
 const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2"};
@@ -192,6 +196,17 @@ struct tm_plan {
     int n_slots = 0;
     Layout lay;
     int64_t K = 0, n_seg = 0, n_ckpt = 0, seg_steps = 0;
+    // snapshot storage: every R-th step (R = step ratio), on the device or in
+    // a pinned host store reached through a ring of device slots
+    int64_t R = 1, n_store = 0;
+    int storage = TM_STORE_DEVICE;
+    char* host_store = nullptr;          // pinned [n_store][E | C][S][nyi][nxi]
+    uint64_t host_bytes = 0;
+    hipStream_t copy_stream = nullptr;
+    hipEvent_t slot_copied[HOST_RING] = {};   // last copy into / out of the slot finished
+    hipEvent_t slot_done[HOST_RING] = {};     // last kernel reading / writing the slot finished
+    bool slot_copy_pending[HOST_RING] = {};
+    bool slot_kernel_pending[HOST_RING] = {};
     // pinned staging copy of cpml + tables (allocated on first device call)
     void* pinned = nullptr;
     uint64_t pinned_bytes = 0;
@@ -272,8 +287,10 @@ bool make_layout(tm_plan* p)
     const uint64_t esz = d.snap == TM_SNAP_BF16 ? 2 : d.snap == TM_SNAP_FP8 ? 1 : 4;
     L.snap_shot = (uint64_t)g.nyi * (uint64_t)g.nxi * esz;
     L.snap_step = align_up(S * L.snap_shot);
-    L.snapE = take(L.snap_step * (uint64_t)p->seg_steps);
-    L.snapC = take(L.snap_step * (uint64_t)p->seg_steps);
+    const uint64_t dev_steps = p->storage == TM_STORE_HOST ? (uint64_t)HOST_RING
+                             : p->K > 0 ? (uint64_t)p->seg_steps : (uint64_t)p->n_store;
+    L.snapE = take(L.snap_step * dev_steps);
+    L.snapC = take(L.snap_step * dev_steps);
     L.ckpt_slot = L.set_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
     L.recrows = take(S * (uint64_t)p->n_slots * (uint64_t)g.nx * 4);
@@ -428,6 +445,70 @@ Ptrs pointers(const tm_plan* p, void* ws)
     return q;
 }
 
+// Device destination of stored step t (t a multiple of R) in full-store
+// mode: its own slot in the device store, or its ring slot in host mode.
+int64_t dev_slot(const tm_plan* p, int64_t t)
+{
+    const int64_t j = t / p->R;
+    return p->storage == TM_STORE_HOST ? j % HOST_RING : j;
+}
+
+tm_status host_setup(tm_plan* p)
+{
+    if (p->copy_stream == nullptr) HIPCHK(hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking));
+    for (int i = 0; i < HOST_RING; ++i) {
+        if (p->slot_copied[i] == nullptr) HIPCHK(hipEventCreateWithFlags(&p->slot_copied[i], hipEventDisableTiming));
+        if (p->slot_done[i] == nullptr) HIPCHK(hipEventCreateWithFlags(&p->slot_done[i], hipEventDisableTiming));
+    }
+    if (p->host_store == nullptr) {
+        if (hipHostMalloc(reinterpret_cast<void**>(&p->host_store), p->host_bytes, hipHostMallocDefault) != hipSuccess) {
+            p->host_store = nullptr;
+            return TM_ENOMEM;
+        }
+    }
+    return TM_OK;
+}
+
+// Before a kernel on `st` writes or reads ring slot i: wait for the slot's
+// last copy.
+tm_status slot_acquire(tm_plan* p, int i, hipStream_t st)
+{
+    if (p->slot_copy_pending[i]) HIPCHK(hipStreamWaitEvent(st, p->slot_copied[i], 0));
+    p->slot_copy_pending[i] = false;
+    return TM_OK;
+}
+
+// After the kernel that wrote / read ring slot i was enqueued on `st`.
+tm_status slot_release(tm_plan* p, int i, hipStream_t st)
+{
+    HIPCHK(hipEventRecord(p->slot_done[i], st));
+    p->slot_kernel_pending[i] = true;
+    return TM_OK;
+}
+
+// Copy ring slot i to / from stored step j of the host store, after the
+// slot's last kernel; the next kernel using the slot waits for it.
+tm_status slot_copy(tm_plan* p, const Ptrs& q, int i, int64_t j, bool to_host)
+{
+    const uint64_t n = p->lay.snap_step;
+    hipStream_t cs = p->copy_stream;
+    if (p->slot_kernel_pending[i]) HIPCHK(hipStreamWaitEvent(cs, p->slot_done[i], 0));
+    p->slot_kernel_pending[i] = false;
+    char* he = p->host_store + (uint64_t)j * 2 * n;
+    char* de = q.snapE + (uint64_t)i * n;
+    char* dc = q.snapC + (uint64_t)i * n;
+    if (to_host) {
+        HIPCHK(hipMemcpyAsync(he, de, n, hipMemcpyDeviceToHost, cs));
+        HIPCHK(hipMemcpyAsync(he + n, dc, n, hipMemcpyDeviceToHost, cs));
+    } else {
+        HIPCHK(hipMemcpyAsync(de, he, n, hipMemcpyHostToDevice, cs));
+        HIPCHK(hipMemcpyAsync(dc, he + n, n, hipMemcpyHostToDevice, cs));
+    }
+    HIPCHK(hipEventRecord(p->slot_copied[i], cs));
+    p->slot_copy_pending[i] = true;
+    return TM_OK;
+}
+
 // One forward step t (set cur -> 1-cur): H and E updates with the snapshot
 // epilogue (se/sc non-null) in one kernel, then sources and receivers.
 template <int P>
@@ -539,6 +620,7 @@ void adj_step(tm_plan* p, const Ptrs& q, const float* grad_r, float* grad_f, int
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
     a.gca = gca;
     a.gcb = gcb;
+    a.ratio = (float)p->R;
     const dim3 grid((unsigned)p->tiling_adj.nblk), blk(NT);
     timed(p, KID_ADJ_STEP, t, st, [&] {
         if (snap == SNAP_F32) k_adj_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
@@ -606,12 +688,15 @@ tm_status device_tiling(tm_plan* p)
 }
 
 // Forward steps [t0, t1) from set *cur (updated).  snap: SNAP_* kind of the
-// stored steps, whose destinations snap_at(t, se, sc) gives; ckpt: save the
-// state at every multiple of K into the checkpoint slots.
+// stored steps (the multiples of R), whose device destinations
+// snap_at(t, se, sc) gives; host: copy every stored step to the host store
+// through its ring slot; ckpt: save the state at every multiple of K into
+// the checkpoint slots.
 template <int P, typename SnapAt>
 tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, float* r, int64_t t0, int64_t t1,
-                        int snap, SnapAt snap_at, bool ckpt, hipStream_t st)
+                        int snap, SnapAt snap_at, bool ckpt, bool host, hipStream_t st)
 {
+    auto stored = [&](int64_t t) { return snap != SNAP_NONE && t % p->R == 0; };
     for (int64_t t = t0; t < t1;) {
         if (ckpt && t > 0 && t % p->K == 0) {
             const int64_t slot = t / p->K - 1;
@@ -620,17 +705,36 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
         }
         // two steps per launch unless step t+1 starts a checkpoint interval
         const bool pair = p->time_block == 2 && t + 1 < t1 && !(ckpt && (t + 1) % p->K == 0);
-        char *se = nullptr, *sc = nullptr, *se1 = nullptr, *sc1 = nullptr;
-        if (snap != SNAP_NONE) snap_at(t, se, sc);
-        if (pair) {
-            if (snap != SNAP_NONE) snap_at(t + 1, se1, sc1);
-            fwd_step2<P>(p, q, *cur, f, r, t, snap, se, sc, se1, sc1, st);
-            t += 2;
-        } else {
-            fwd_step<P>(p, q, *cur, f, r, t, snap, se, sc, st);
-            t += 1;
+        const int nstep = pair ? 2 : 1;
+        char *se[2] = {nullptr, nullptr}, *sc[2] = {nullptr, nullptr};
+        bool any = false;
+        for (int i = 0; i < nstep; ++i) {
+            if (!stored(t + i)) continue;
+            snap_at(t + i, se[i], sc[i]);
+            if (host) {
+                tm_status v = slot_acquire(p, (int)dev_slot(p, t + i), st);
+                if (v != TM_OK) return v;
+            }
+            any = true;
         }
+        const int kind = any ? snap : SNAP_NONE;
+        if (pair) fwd_step2<P>(p, q, *cur, f, r, t, kind, se[0], sc[0], se[1], sc[1], st);
+        else fwd_step<P>(p, q, *cur, f, r, t, kind, se[0], sc[0], st);
+        for (int i = 0; host && i < nstep; ++i) {
+            if (!stored(t + i)) continue;
+            const int slot = (int)dev_slot(p, t + i);
+            tm_status v = slot_release(p, slot, st);
+            if (v == TM_OK) v = slot_copy(p, q, slot, (t + i) / p->R, true);
+            if (v != TM_OK) return v;
+        }
+        t += nstep;
         *cur = 1 - *cur;
+    }
+    if (host) {                     // the caller's stream sees the host store complete
+        for (int i = 0; i < HOST_RING; ++i) {
+            tm_status v = slot_acquire(p, i, st);
+            if (v != TM_OK) return v;
+        }
     }
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
@@ -644,11 +748,13 @@ tm_status run_forward(tm_plan* p, void* ws, const float* f, float* r, int64_t t0
     const Ptrs q = pointers(p, ws);
     const bool full = p->K == 0;
     const int snap = (store && full) ? snap_kind(p) : SNAP_NONE;
+    const bool host = snap != SNAP_NONE && p->storage == TM_STORE_HOST;
+    if (host && (v = host_setup(p)) != TM_OK) return v;
     auto at = [&](int64_t t, char*& se, char*& sc) {
-        se = q.snapE + t * p->lay.snap_step;
-        sc = q.snapC + t * p->lay.snap_step;
+        se = q.snapE + dev_slot(p, t) * p->lay.snap_step;
+        sc = q.snapC + dev_slot(p, t) * p->lay.snap_step;
     };
-    return forward_range<P>(p, q, &p->fwd_cur, f, r, t0, t1, snap, at, store && !full, st);
+    return forward_range<P>(p, q, &p->fwd_cur, f, r, t0, t1, snap, at, store && !full, host, st);
 }
 
 template <int P>
@@ -663,10 +769,25 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
     const int snap = want_grad ? snap_kind(p) : SNAP_NONE;
     int64_t k = 0;
     if (p->K == 0 || !want_grad) {
+        const bool host = want_grad && p->storage == TM_STORE_HOST;
+        const int64_t j_last = (nt - 1) / p->R;           // last stored step index
+        if (host) {
+            if ((v = host_setup(p)) != TM_OK) return v;
+            for (int64_t j = j_last; j >= 0 && j > j_last - HOST_RING; --j)
+                if ((v = slot_copy(p, q, (int)(j % HOST_RING), j, false)) != TM_OK) return v;
+        }
         for (int64_t t = nt - 1; t >= 0; --t, ++k) {
-            const uint64_t so = (uint64_t)t * p->lay.snap_step;
-            adj_step<P>(p, q, grad_r, grad_f, t, k, snap, want_grad ? q.snapE + so : nullptr,
-                        want_grad ? q.snapC + so : nullptr, gca, gcb, st);
+            const bool use = want_grad && t % p->R == 0;
+            const int64_t slot = use ? dev_slot(p, t) : 0;
+            if (use && host && (v = slot_acquire(p, (int)slot, st)) != TM_OK) return v;
+            const uint64_t so = (uint64_t)slot * p->lay.snap_step;
+            adj_step<P>(p, q, grad_r, grad_f, t, k, use ? snap : SNAP_NONE, use ? q.snapE + so : nullptr,
+                        use ? q.snapC + so : nullptr, gca, gcb, st);
+            if (use && host) {
+                if ((v = slot_release(p, (int)slot, st)) != TM_OK) return v;
+                const int64_t jn = t / p->R - HOST_RING;   // the stored step that reuses this slot
+                if (jn >= 0 && (v = slot_copy(p, q, (int)slot, jn, false)) != TM_OK) return v;
+            }
         }
     } else {
         for (int64_t seg = p->n_seg - 1; seg >= 0; --seg) {
@@ -684,7 +805,7 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
                 se = q.snapE + (t - ta) * p->lay.snap_step;
                 sc = q.snapC + (t - ta) * p->lay.snap_step;
             };
-            v = forward_range<P>(p, q, &cur, f, nullptr, ta, tb, snap, at, false, st);
+            v = forward_range<P>(p, q, &cur, f, nullptr, ta, tb, snap, at, false, false, st);
             if (v != TM_OK) return v;
             for (int64_t t = tb - 1; t >= ta; --t, ++k)
                 adj_step<P>(p, q, grad_r, grad_f, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
@@ -744,7 +865,13 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16 && d.snap != TM_SNAP_FP8) return TM_EINVAL;
-    if (d.time_block < 0 || d.time_block > 2 || d.reserved != 0) return TM_EINVAL;
+    if (d.time_block < 0 || d.time_block > 2) return TM_EINVAL;
+    if (d.storage != TM_STORE_DEVICE && d.storage != TM_STORE_HOST) return TM_EINVAL;
+    if (d.step_ratio < 0) return TM_EINVAL;
+    {
+        const bool ckpt = d.ckpt_every > 0 && d.ckpt_every < d.nt;
+        if (ckpt && (d.storage == TM_STORE_HOST || d.step_ratio > 1)) return TM_EINVAL;
+    }
     if (d.ny < 2 * P + 2 || d.nx < 2 * P + 2) return TM_EINVAL;
     if (d.ny * d.nx >= (int64_t(1) << 29)) return TM_EINVAL;
     if (d.n_shots * std::max<int64_t>(d.n_src, d.n_rec) >= (int64_t(1) << 31)) return TM_EINVAL;
@@ -797,6 +924,9 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     p->t_m_sl = append(mt.src_list); p->t_m_rslot = append(mt.rec_slot); p->t_m_rg = append(mt.rec_gather);
     p->n_slots = mt.n_slots;
     p->time_block = d.time_block == 0 ? 2 : (int)d.time_block;
+    p->R = d.step_ratio > 1 ? d.step_ratio : 1;
+    p->n_store = (d.nt + p->R - 1) / p->R;
+    p->storage = (int)d.storage;
 
     if (d.ckpt_every > 0 && d.ckpt_every < d.nt) {
         p->K = d.ckpt_every;
@@ -815,6 +945,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         delete p;
         return TM_EINVAL;
     }
+    if (p->storage == TM_STORE_HOST) p->host_bytes = (uint64_t)p->n_store * 2 * p->lay.snap_step;
     if (d.hbm_budget > 0 && p->lay.total > d.hbm_budget) {
         delete p;
         return TM_ENOMEM;
@@ -827,6 +958,13 @@ TM_API void tm_plan_destroy(tm_plan* p)
 {
     if (p == nullptr) return;
     if (p->pinned != nullptr) (void)hipHostFree(p->pinned);
+    if (p->copy_stream != nullptr) (void)hipStreamSynchronize(p->copy_stream);
+    if (p->host_store != nullptr) (void)hipHostFree(p->host_store);
+    if (p->copy_stream != nullptr) (void)hipStreamDestroy(p->copy_stream);
+    for (int i = 0; i < HOST_RING; ++i) {
+        if (p->slot_copied[i] != nullptr) (void)hipEventDestroy(p->slot_copied[i]);
+        if (p->slot_done[i] != nullptr) (void)hipEventDestroy(p->slot_done[i]);
+    }
     for (const TimedLaunch& r : p->ev_used) {
         (void)hipEventSynchronize(r.b);
         (void)hipEventDestroy(r.a);

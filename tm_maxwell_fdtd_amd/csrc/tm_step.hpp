@@ -436,6 +436,7 @@ struct AdjArgs {
     uint32_t snap_shot_bytes;
     float* __restrict__ gca;           // per-shot gradients [S][ny][nx], or null
     float* __restrict__ gcb;
+    float ratio;                       // weight of this step's gradient term (the snapshot step ratio)
 };
 
 template <int P, int SNAP>
@@ -592,8 +593,8 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
                 if constexpr (SNAP != SNAP_NONE) {
                     if (r < yb && r >= g.y0 && r < g.y1) {  // uniform
                         const uint32_t orr = (uint32_t)(r * nx) * 4u + c4;
-                        bga.st(grad, fmaf(e, fSe[u], fGa[u]), orr, 0u);
-                        bgb.st(grad, fmaf(e, fSc[u], fGb[u]), orr, 0u);
+                        bga.st(grad, fmaf(e, fSe[u] * a.ratio, fGa[u]), orr, 0u);
+                        bgb.st(grad, fmaf(e, fSc[u] * a.ratio, fGb[u]), orr, 0u);
                     }
                 }
                 push(e, uv, wv);

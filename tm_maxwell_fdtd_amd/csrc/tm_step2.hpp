@@ -80,9 +80,9 @@ struct Fwd2Args {
     const float* __restrict__ cp;      // CPML table [12][L]
     const char* __restrict__ set0;     // state at step n
     char* __restrict__ set1;           // state at step n+2
-    char* __restrict__ snap_e0;        // Ey^n, curl H^n [S][nyi][nxi], or null
+    char* __restrict__ snap_e0;        // Ey^n, curl H^n [S][nyi][nxi], or null (step n not stored)
     char* __restrict__ snap_c0;
-    char* __restrict__ snap_e1;        // Ey^{n+1}, curl H^{n+1}
+    char* __restrict__ snap_e1;        // Ey^{n+1}, curl H^{n+1}, or null
     char* __restrict__ snap_c1;
     uint32_t snap_shot_bytes;
     MidEvents ev;
@@ -176,11 +176,14 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf bm(a.m.base, a.m.bytes);
-    const uint32_t sb = SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u;
-    const RBuf bse0(a.snap_e0 + (int64_t)s * a.snap_shot_bytes, sb);
-    const RBuf bsc0(a.snap_c0 + (int64_t)s * a.snap_shot_bytes, sb);
-    const RBuf bse1(a.snap_e1 + (int64_t)s * a.snap_shot_bytes, sb);
-    const RBuf bsc1(a.snap_c1 + (int64_t)s * a.snap_shot_bytes, sb);
+    // a stage whose step is not stored gets null destinations: empty views
+    const uint32_t sb0 = (SNAP != SNAP_NONE && a.snap_e0 != nullptr) ? a.snap_shot_bytes : 0u;
+    const uint32_t sb1 = (SNAP != SNAP_NONE && a.snap_e1 != nullptr) ? a.snap_shot_bytes : 0u;
+    const int64_t so_s = (int64_t)s * a.snap_shot_bytes;
+    const RBuf bse0(sb0 ? a.snap_e0 + so_s : nullptr, sb0);
+    const RBuf bsc0(sb0 ? a.snap_c0 + so_s : nullptr, sb0);
+    const RBuf bse1(sb1 ? a.snap_e1 + so_s : nullptr, sb1);
+    const RBuf bsc1(sb1 ? a.snap_c1 + so_s : nullptr, sb1);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
     const uint32_t rowb = (uint32_t)nx * 4u, brow = (uint32_t)g.bx * 4u;
 

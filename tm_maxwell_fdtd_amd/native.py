@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "tm_fdtd.h")
 TM_OK, TM_EINVAL, TM_EUNSTABLE, TM_ENOMEM, TM_EHIP, TM_ESTATE, TM_ENONFINITE = range(7)
 TM_SNAP_F32, TM_SNAP_BF16, TM_SNAP_FP8 = 0, 1, 2
 SNAP_KINDS = {"f32": TM_SNAP_F32, "bf16": TM_SNAP_BF16, "fp8": TM_SNAP_FP8}
+TM_STORE_DEVICE, TM_STORE_HOST = 0, 1
 TM_FWD_STORE, TM_FWD_CHECK = 1, 2
 
 _STATUS_NAMES = {0: "TM_OK", 1: "TM_EINVAL", 2: "TM_EUNSTABLE", 3: "TM_ENOMEM", 4: "TM_EHIP",
@@ -48,7 +49,8 @@ class tm_desc(ctypes.Structure):
         ("ckpt_every", ctypes.c_int64),
         ("hbm_budget", ctypes.c_uint64),
         ("time_block", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("storage", ctypes.c_int32),
+        ("step_ratio", ctypes.c_int64),
     ]
 
 
@@ -215,14 +217,14 @@ def tm_timing_read(plan):
 # ---- convenience layer (still marshalling only) -----------------------------
 
 def make_desc(wl, snap: Optional[str] = None, ckpt_every: Optional[int] = None, hbm_budget: int = 0,
-              time_block: int = 0) -> tm_desc:
+              time_block: int = 0, storage: int = 0, step_ratio: int = 0) -> tm_desc:
     snap = wl.snap if snap is None else snap
     return tm_desc(order=wl.order, snap=SNAP_KINDS[snap],
                    n_shots=wl.n_shots, ny=wl.ny, nx=wl.nx,
                    pml_y0=wl.pml_y0, pml_y1=wl.pml_y1, pml_x0=wl.pml_x0, pml_x1=wl.pml_x1,
                    dy=wl.dy, dx=wl.dx, nt=wl.nt, n_src=wl.n_src, n_rec=wl.n_rec,
                    ckpt_every=wl.ckpt_every if ckpt_every is None else ckpt_every,
-                   hbm_budget=hbm_budget, time_block=time_block)
+                   hbm_budget=hbm_budget, time_block=time_block, storage=storage, step_ratio=step_ratio)
 
 
 class Propagator:
@@ -233,12 +235,13 @@ class Propagator:
     tensors; the model arrays are passed at construction.
     """
 
-    def __init__(self, wl, device="cuda", snap=None, ckpt_every=None, hbm_budget=0, time_block=0):
+    def __init__(self, wl, device="cuda", snap=None, ckpt_every=None, hbm_budget=0, time_block=0, storage=0,
+                 step_ratio=0):
         import torch
 
         self.wl = wl
         self.device = torch.device(device)
-        self.desc = make_desc(wl, snap, ckpt_every, hbm_budget, time_block)
+        self.desc = make_desc(wl, snap, ckpt_every, hbm_budget, time_block, storage, step_ratio)
         st, plan = tm_plan_create(self.desc, wl.cpml, wl.src, wl.rec)
         _check(st, "tm_plan_create")
         self.plan = plan
