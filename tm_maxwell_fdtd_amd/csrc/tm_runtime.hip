@@ -305,7 +305,8 @@ bool make_layout(tm_plan* p)
 // 16 and CH_MAX rows, and no round runs half empty.  TM_FDTD_CHUNK_ROWS
 // (environment, read when the tiling is made) forces the chunk height, for
 // tuning.
-Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_MAX)
+Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_MAX, int64_t ncu = 256,
+                   int halo_iters = 0)
 {
     Tiling t{};
     const int R = (int)d.ny - 2 * P + 1, nx_e = (int)d.nx - 2 * P + 1;
@@ -321,6 +322,18 @@ Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_M
         if (ch <= chmax) break;
     }
     ch = std::min(ch, chmax);
+    // Small problems leave most CUs idle with chunks of 16 rows or more:
+    // then each workgroup's time is its row count (owned rows plus the
+    // halo_iters rows of its halo), so take the chunk height that minimises
+    // (rows per workgroup) x (workgroups per pair of CUs, at least 1).
+    if (U * ((R + ch - 1) / ch) < 2 * ncu) {
+        double best = 1e300;
+        for (int c = std::min(ch, chmax); c >= 1; --c) {
+            const int64_t nblk = U * ((R + c - 1) / c);
+            const double score = (double)(c + halo_iters) * std::max(1.0, (double)nblk / (2.0 * (double)ncu));
+            if (score < best) { best = score; ch = c; }
+        }
+    }
     if (const char* env = std::getenv("TM_FDTD_CHUNK_ROWS")) {
         const int v = std::atoi(env);
         if (v >= 1) ch = std::min(v, chmax);
@@ -650,13 +663,14 @@ tm_status check_ws(const tm_plan* p, void* ws, uint64_t ws_bytes)
 // order-8, 1096^2 x 16-shot size: 5 per CU beat 4 and 7).
 constexpr int WG_PER_CU = 5;
 
-tm_status resident(const void* fn, int64_t* cap)
+tm_status resident(const void* fn, int64_t* cap, int64_t* ncu_out = nullptr)
 {
     int dev = 0, ncu = 0, nb = 0;
     HIPCHK(hipGetDevice(&dev));
     HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
     HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, NT, 0));
     *cap = (int64_t)std::min(std::max(nb, 1), WG_PER_CU) * std::max(ncu, 1);
+    if (ncu_out != nullptr) *ncu_out = std::max(ncu, 1);
     return TM_OK;
 }
 
@@ -673,16 +687,18 @@ tm_status device_tiling(tm_plan* p)
              : p->d.snap == TM_SNAP_FP8  ? reinterpret_cast<const void*>(f8)
                                          : reinterpret_cast<const void*>(f32);
     };
-    int64_t cf = 0, ca = 0, c2 = 0;
-    tm_status v = resident(pick(&k_fwd_step<P, SNAP_F32>, &k_fwd_step<P, SNAP_BF16>, &k_fwd_step<P, SNAP_FP8>), &cf);
+    int64_t cf = 0, ca = 0, c2 = 0, ncu = 0;
+    tm_status v = resident(pick(&k_fwd_step<P, SNAP_F32>, &k_fwd_step<P, SNAP_BF16>, &k_fwd_step<P, SNAP_FP8>), &cf,
+                           &ncu);
     if (v != TM_OK) return v;
     v = resident(pick(&k_adj_step<P, SNAP_F32>, &k_adj_step<P, SNAP_BF16>, &k_adj_step<P, SNAP_FP8>), &ca);
     if (v != TM_OK) return v;
     v = resident(pick(&k_fwd_step2<P, SNAP_F32>, &k_fwd_step2<P, SNAP_BF16>, &k_fwd_step2<P, SNAP_FP8>), &c2);
     if (v != TM_OK) return v;
-    p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W);
-    p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W);
-    p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W, CH2_MAX);
+    // halo_iters: row iterations of a chunk beyond its owned rows
+    p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W, CH_MAX, ncu, 2 * P - 1);
+    p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W, CH_MAX, ncu, 4 * P - 3);
+    p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W, CH2_MAX, ncu, 6 * P - 3);
     p->tiling_device = dev;
     return TM_OK;
 }
