@@ -203,6 +203,28 @@ def test_two_step_launch_bitwise_equals_single_steps(order, snap, ckpt):
         np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} order {order} {snap} K={ckpt}")
 
 
+@pytest.mark.parametrize("steps,ckpt,chunks", [(1, 0, None), (3, 0, None), (8, 0, [5, 50]), (3, 7, None),
+                                               (5, 0, [33])])
+def test_event_blocks_bitwise(monkeypatch, steps, ckpt, chunks):
+    """Sources and receivers go through event rows prepared for runs of
+    steps; short runs (one step, odd lengths that split pairs, a run
+    boundary inside a forward chunk or a checkpoint segment) give bitwise the
+    records and gradients of one run for the whole problem."""
+    wl = inputs.as_f32(inputs.random_workload(8, 40, 8, nt=61, n_shots=3, n_src=3, n_rec=7, seed=740,
+                                              src_anywhere=True))
+    wl.src[1, 1] = wl.src[1, 0]
+    wl.src[2, 2] = -1
+    wl.rec[0, 3] = wl.rec[0, 2]
+    wl.rec[1, 4] = wl.src[1, 0]
+    wl.rec[2, 0] = -1
+    ref = run_gpu(wl, snap="f32", ckpt_every=ckpt)
+    monkeypatch.setenv("TM_FDTD_EVENT_STEPS", str(steps))
+    got = run_gpu(wl, snap="f32", ckpt_every=ckpt, chunks=chunks)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{key} steps {steps} K={ckpt} {chunks}")
+    assert np.all(got["records"][:, 2, 0] == 0) and np.all(got["grad_f"][:, 2, 2] == 0)   # absent entries
+
+
 def test_error_codes_on_device():
     import torch
 

@@ -1,5 +1,5 @@
-// Small kernels around the time-step kernels: source injection and
-// receiver gather and their adjoints, the gradient shot sum (tide-GPR
+// Small kernels around the time-step kernels: the event rows of the
+// sources and receivers, the gradient shot sum (tide-GPR
 // 0.0.9, maxwell.cu: combine_grad), the chain rule to eps_r / sigma
 // gradients, a fill kernel and the Courant-number reduction (gfx950,
 // wave64).
@@ -10,81 +10,46 @@
 namespace tmf {
 
 // ---------------------------------------------------------------------------
-// Sources and receivers of one step (tide-GPR 0.0.9, maxwell.cu:
-// add_sources_ey, record_receivers_ey), on the Ey of a state set whose
-// shots are blocks of shot_bytes with Ey at byte oE.  One workgroup per
-// shot: first every
-// distinct source cell adds the sum of its sources (ascending source order),
-// then, after the barrier, every receiver reads Ey.  Duplicate cells
-// therefore never race.
-//   cell/ptr/list: per shot, the distinct cells (padded with -1), CSR offsets
-//   into list, and list = source indices grouped by cell.
+// Event rows of a run of steps (tide-GPR 0.0.9, maxwell.cu: add_sources_ey
+// and record_receivers_ey, and their adjoints).  Slot g is one grid row of
+// shot slot_shot[g] that holds sources or receivers; colcell[g][x] is the
+// cell number of (that row, x), or -1.
+//
+// k_event_add: rows[j][g][x] = the sum of in[j][s][list[q]] over the cell's
+// entries q = ptr[k] .. ptr[k+1]-1 (in list order, ascending index), 0 at
+// cells without entries; j = 0 .. n_steps-1, in = the first step's values
+// [n_steps][S][n_in] (null when n_in = 0: rows of zeros).
 // ---------------------------------------------------------------------------
-//   rec_rows/r_gather/r_prev (optional): after a two-step launch, the
-//   receivers of the launch's first step are gathered from the receiver-row
-//   buffer the step kernel wrote (r_gather = slot * nx + x, or -1).
-__global__ __launch_bounds__(256) void k_fwd_srcrec(char* __restrict__ set, uint64_t shot_bytes, uint32_t oE,
-                                                    const float* __restrict__ f_t, int n_src,
-                                                    const int* __restrict__ s_cell,
-                                                    const int* __restrict__ s_ptr,
-                                                    const int* __restrict__ s_list,
-                                                    float* __restrict__ r_t, int n_rec,
-                                                    const int* __restrict__ r_idx,
-                                                    const float* __restrict__ rec_rows,
-                                                    const int* __restrict__ r_gather,
-                                                    float* __restrict__ r_prev, int n_slots, int nx)
+__global__ __launch_bounds__(256) void k_event_add(float* __restrict__ rows, int64_t n, int n_slots, int nx,
+                                                   const int* __restrict__ colcell,
+                                                   const int* __restrict__ slot_shot,
+                                                   const int* __restrict__ ptr, const int* __restrict__ list,
+                                                   const float* __restrict__ in, int S, int n_in)
 {
-    const int s = blockIdx.x;
-    if (r_prev != nullptr) {
-        for (int i = threadIdx.x; i < n_rec; i += blockDim.x) {
-            const int gidx = r_gather[s * n_rec + i];
-            r_prev[s * n_rec + i] = gidx >= 0 ? rec_rows[(int64_t)s * n_slots * nx + gidx] : 0.0f;
-        }
-    }
-    float* e = reinterpret_cast<float*>(set + (uint64_t)s * shot_bytes + oE);
-    for (int u = threadIdx.x; u < n_src; u += blockDim.x) {
-        const int c = s_cell[s * n_src + u];
-        if (c < 0) continue;
-        const int* ptr = s_ptr + s * (n_src + 1);
+    const int64_t row = (int64_t)n_slots * nx;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = i / row;
+        const int gx = (int)(i - j * row);
+        const int k = colcell[gx];
         float acc = 0.0f;
-        for (int q = ptr[u]; q < ptr[u + 1]; ++q) acc += f_t[s * n_src + s_list[s * n_src + q]];
-        e[c] = e[c] + acc;
-    }
-    __syncthreads();
-    if (r_t == nullptr) return;
-    for (int i = threadIdx.x; i < n_rec; i += blockDim.x) {
-        const int c = r_idx[s * n_rec + i];
-        r_t[s * n_rec + i] = c >= 0 ? e[c] : 0.0f;
+        if (k >= 0 && in != nullptr) {
+            const float* v = in + (j * S + slot_shot[gx / nx]) * n_in;
+            for (int q = ptr[k]; q < ptr[k + 1]; ++q) acc += v[list[q]];
+        }
+        rows[i] = acc;
     }
 }
 
-// Adjoint of the above (add_adjoint_sources_ey, record_adjoint_at_sources):
-// residuals injected at the receivers (distinct
-// receiver cells, ascending receiver order), then the adjoint field read at
-// the sources (source-wavelet gradient).
-__global__ __launch_bounds__(256) void k_adj_srcrec(char* __restrict__ set, uint64_t shot_bytes, uint32_t oE,
-                                                    const float* __restrict__ gr_t, int n_rec,
-                                                    const int* __restrict__ r_cell,
-                                                    const int* __restrict__ r_ptr,
-                                                    const int* __restrict__ r_list,
-                                                    float* __restrict__ gf_t, int n_src,
-                                                    const int* __restrict__ s_idx)
+// k_event_gather: out[j][i] = rows[j][pos[i]] for the S*n_out entries i of
+// each step (pos = g*nx + x of the entry's cell, or -1: absent, 0).
+__global__ __launch_bounds__(256) void k_event_gather(float* __restrict__ out, int64_t n, int per_step,
+                                                      const int* __restrict__ pos,
+                                                      const float* __restrict__ rows, int64_t row_step)
 {
-    const int s = blockIdx.x;
-    float* e = reinterpret_cast<float*>(set + (uint64_t)s * shot_bytes + oE);
-    for (int u = threadIdx.x; u < n_rec; u += blockDim.x) {
-        const int c = r_cell[s * n_rec + u];
-        if (c < 0) continue;
-        const int* ptr = r_ptr + s * (n_rec + 1);
-        float acc = 0.0f;
-        for (int q = ptr[u]; q < ptr[u + 1]; ++q) acc += gr_t[s * n_rec + r_list[s * n_rec + q]];
-        e[c] = e[c] + acc;
-    }
-    __syncthreads();
-    if (gf_t == nullptr) return;
-    for (int i = threadIdx.x; i < n_src; i += blockDim.x) {
-        const int c = s_idx[s * n_src + i];
-        gf_t[s * n_src + i] = c >= 0 ? e[c] : 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = i / per_step;
+        const int p = pos[i - j * per_step];
+        out[i] = p >= 0 ? rows[j * row_step + p] : 0.0f;
     }
 }
 

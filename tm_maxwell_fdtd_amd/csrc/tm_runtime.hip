@@ -1,18 +1,18 @@
 // Host runtime and C ABI of the TM FDTD propagator (see include/tm_fdtd.h).
 //
-// The plan validates a problem on the host, builds conflict-free scatter
-// tables for the sources and receivers, chooses the tiling of the step kernels and lays
+// The plan validates a problem on the host, builds the per-row event-cell
+// tables of the sources and receivers, chooses the tiling of the step kernels and lays
 // out the caller-allocated workspace.  tm_forward / tm_adjoint / tm_grad
 // enqueue kernels on the caller's stream; there is no global state, so plans
 // are independent.
 //
 // Host loop structure follows the launchers of tide-GPR 0.0.9, maxwell.cu
-// (forward, forward_with_storage, backward): per forward step one fused
-// kernel (H and E updates, snapshot epilogue on stored steps) and one small
-// kernel for the sources and then the receivers; per adjoint step, in
-// reverse time, one small kernel (residual injection at the receivers,
-// adjoint read at the sources) and one fused kernel (transposed H and E
-// updates, gradient accumulation); then combine_grad.  Checkpoint mode
+// (forward, forward_with_storage, backward), with each step's small kernels
+// fused into its stencil kernel: per forward step (or pair of steps) one
+// kernel (H and E updates, sources, then receivers, snapshot epilogue on
+// stored steps); per adjoint step, in reverse time, one kernel (residual
+// injection at the receivers, adjoint read at the sources, transposed H and
+// E updates, gradient accumulation); then combine_grad.  Checkpoint mode
 // stores the state (fields and band CPML memories) every K steps and replays
 // each segment into a K-step snapshot buffer inside tm_adjoint.
 //
@@ -46,6 +46,8 @@ namespace {
 constexpr uint64_t ALIGN = 256;
 uint64_t align_up(uint64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 constexpr uint64_t BLOCK_MAX = (uint64_t(1) << 31) - ALIGN;   // one buffer view
+constexpr uint64_t EV_BLOCK_BYTES = uint64_t(16) << 20;        // one event-row buffer (a run of steps)
+constexpr uint64_t EV_ROW_MAX = uint64_t(1) << 29;              // one step's event rows (add + out in one view)
 
 double abs_coef_sum(int order)
 {
@@ -57,96 +59,57 @@ double abs_coef_sum(int order)
     }
 }
 
-// Distinct-cell scatter table of one index set ([S][n] cells, negative = none).
-struct Scatter {
-    std::vector<int32_t> cell;   // [S][n] distinct cells, -1 padded
-    std::vector<int32_t> ptr;    // [S][n+1] CSR offsets into list
-    std::vector<int32_t> list;   // [S][n] member indices grouped by cell (ascending)
-    std::vector<int32_t> idx;    // [S][n] raw cell or -1 (for gathers)
+// Event-row tables of the sources and receivers (EventRows): per shot the
+// grid rows holding sources or receivers (negative indices = absent) get
+// slots g, ascending by shot then row; the distinct cells of those rows are
+// numbered k, each with its source indices and its receiver indices
+// (ascending, CSR); colcell[g][x] = k or -1; src_pos / rec_pos [S][n] =
+// g*nx + x of each entry's cell, or -1.
+struct EventTables {
+    std::vector<int32_t> row_slot, colcell, slot_shot, cell_src, src_list, cell_rec, rec_list, src_pos, rec_pos;
+    int64_t n_slots = 0;
 };
 
-Scatter build_scatter(const int64_t* ids, int64_t S, int64_t n)
+EventTables build_events(const int64_t* src, int64_t n_src, const int64_t* rec, int64_t n_rec, int64_t S,
+                         int64_t ny, int64_t nx)
 {
-    Scatter t;
-    t.cell.assign(S * n, -1);
-    t.ptr.assign(S * (n + 1), 0);
-    t.list.assign(S * n, 0);
-    t.idx.assign(S * n, -1);
-    std::vector<std::pair<int64_t, int32_t>> v;
-    for (int64_t s = 0; s < S; ++s) {
-        v.clear();
-        for (int64_t i = 0; i < n; ++i) {
-            const int64_t c = ids[s * n + i];
-            t.idx[s * n + i] = c >= 0 ? (int32_t)c : -1;
-            if (c >= 0) v.emplace_back(c, (int32_t)i);
-        }
-        std::stable_sort(v.begin(), v.end(),
-                         [](const auto& a, const auto& b) { return a.first < b.first; });
-        int32_t u = -1, q = 0;
-        int32_t* ptr = t.ptr.data() + s * (n + 1);
-        for (size_t k = 0; k < v.size(); ++k) {
-            if (k == 0 || v[k].first != v[k - 1].first) {
-                ++u;
-                t.cell[s * n + u] = (int32_t)v[k].first;
-                ptr[u] = q;
-            }
-            t.list[s * n + q] = v[k].second;
-            ++q;
-        }
-        for (int64_t k = u + 1; k <= n; ++k) ptr[k] = q;
-    }
-    return t;
-}
-
-// Tables of the intermediate step of a two-step launch.
-//   row_cells [S*ny + 1]: CSR over (shot, row) of the distinct source cells
-//     (ascending cell), each with its column and its source indices
-//     (ascending);
-//   rec_slot [S*ny]: slot of each row holding receivers of that shot, or -1;
-//   rec_gather [S][n_rec]: slot * nx + x of each receiver, or -1.
-struct MidTables {
-    std::vector<int32_t> row_cells, cell_x, cell_src, src_list, rec_slot, rec_gather;
-    int n_slots = 0;
-};
-
-MidTables build_mid(const int64_t* src, int64_t n_src, const int64_t* rec, int64_t n_rec, int64_t S, int64_t ny,
-                    int64_t nx)
-{
-    MidTables t;
-    std::vector<int32_t> count(S * ny, 0);
-    std::vector<std::pair<int64_t, int32_t>> v;
+    EventTables t;
+    t.row_slot.assign(S * ny, -1);
+    t.src_pos.assign(S * n_src, -1);
+    t.rec_pos.assign(S * n_rec, -1);
+    std::vector<std::pair<int64_t, int32_t>> v;       // (cell, entry), receivers as entry >= n_src
     for (int64_t s = 0; s < S; ++s) {
         v.clear();
         for (int64_t i = 0; i < n_src; ++i)
             if (src[s * n_src + i] >= 0) v.emplace_back(src[s * n_src + i], (int32_t)i);
-        std::stable_sort(v.begin(), v.end(), [](const auto& a, const auto& b) { return a.first < b.first; });
+        for (int64_t j = 0; j < n_rec; ++j)
+            if (rec[s * n_rec + j] >= 0) v.emplace_back(rec[s * n_rec + j], (int32_t)(n_src + j));
+        std::sort(v.begin(), v.end());
         for (size_t k = 0; k < v.size(); ++k) {
-            if (k == 0 || v[k].first != v[k - 1].first) {
-                ++count[s * ny + v[k].first / nx];
-                t.cell_x.push_back((int32_t)(v[k].first % nx));
-                t.cell_src.push_back((int32_t)t.src_list.size());
+            const int64_t y = v[k].first / nx, x = v[k].first % nx;
+            int32_t& g = t.row_slot[s * ny + y];
+            if (g < 0) {                                  // a new event row of this shot
+                g = (int32_t)t.n_slots++;
+                t.slot_shot.push_back((int32_t)s);
+                t.colcell.resize(t.n_slots * nx, -1);
             }
-            t.src_list.push_back(v[k].second);
+            if (k == 0 || v[k].first != v[k - 1].first) {
+                t.colcell[g * nx + x] = (int32_t)t.cell_src.size();
+                t.cell_src.push_back((int32_t)t.src_list.size());
+                t.cell_rec.push_back((int32_t)t.rec_list.size());
+            }
+            const int32_t pos = (int32_t)(g * nx + x);
+            if (v[k].second < n_src) {
+                t.src_list.push_back(v[k].second);
+                t.src_pos[s * n_src + v[k].second] = pos;
+            } else {
+                t.rec_list.push_back((int32_t)(v[k].second - n_src));
+                t.rec_pos[s * n_rec + (v[k].second - n_src)] = pos;
+            }
         }
     }
     t.cell_src.push_back((int32_t)t.src_list.size());
-    t.row_cells.assign(S * ny + 1, 0);
-    for (int64_t j = 0; j < S * ny; ++j) t.row_cells[j + 1] = t.row_cells[j] + count[j];
-    t.rec_slot.assign(S * ny, -1);
-    t.rec_gather.assign(S * n_rec, -1);
-    for (int64_t s = 0; s < S; ++s) {
-        std::vector<int64_t> rows;
-        for (int64_t j = 0; j < n_rec; ++j)
-            if (rec[s * n_rec + j] >= 0) rows.push_back(rec[s * n_rec + j] / nx);
-        std::sort(rows.begin(), rows.end());
-        rows.erase(std::unique(rows.begin(), rows.end()), rows.end());
-        for (size_t k = 0; k < rows.size(); ++k) t.rec_slot[s * ny + rows[k]] = (int32_t)k;
-        t.n_slots = std::max(t.n_slots, (int)rows.size());
-        for (int64_t j = 0; j < n_rec; ++j) {
-            const int64_t c = rec[s * n_rec + j];
-            if (c >= 0) t.rec_gather[s * n_rec + j] = t.rec_slot[s * ny + c / nx] * (int32_t)nx + (int32_t)(c % nx);
-        }
-    }
+    t.cell_rec.push_back((int32_t)t.rec_list.size());
     return t;
 }
 
@@ -161,7 +124,8 @@ struct Layout {
     uint64_t snapE = 0, snapC = 0, snap_step = 0; // per-step bytes of one snapshot array (all shots)
     uint64_t snap_shot = 0;                       // ... of one shot
     uint64_t ckpt = 0, ckpt_slot = 0;
-    uint64_t recrows = 0;                         // receiver-row buffer of two-step launches
+    uint64_t ev_row = 0;                          // bytes of one step's event rows [NS][nx]
+    uint64_t ev_fadd = 0, ev_fout = 0, ev_aadd = 0, ev_aout = 0;   // [EB][NS][nx] each
     uint64_t total = 0;
 };
 
@@ -189,11 +153,11 @@ struct tm_plan {
     int time_block = 2;                  // forward time steps per launch (1 or 2)
     int tiling_device = -1;
     std::vector<float> cpml;             // [12][L]
-    std::vector<int32_t> tables;         // scatter tables, packed
-    uint64_t t_s_cell = 0, t_s_ptr = 0, t_s_list = 0, t_s_idx = 0;
-    uint64_t t_r_cell = 0, t_r_ptr = 0, t_r_list = 0, t_r_idx = 0;
-    uint64_t t_m_row = 0, t_m_cx = 0, t_m_cs = 0, t_m_sl = 0, t_m_rslot = 0, t_m_rg = 0;
-    int n_slots = 0;
+    std::vector<int32_t> tables;         // event-row tables, packed
+    uint64_t t_slot = 0, t_colcell = 0, t_sshot = 0, t_cs = 0, t_sl = 0, t_cr = 0, t_rl = 0;
+    uint64_t t_spos = 0, t_rpos = 0;
+    int64_t NS = 0;                      // event rows (all shots)
+    int64_t EB = 1;                      // steps per event block
     Layout lay;
     int64_t K = 0, n_seg = 0, n_ckpt = 0, seg_steps = 0;
     // snapshot storage: every R-th step (R = step ratio), on the device or in
@@ -293,7 +257,12 @@ bool make_layout(tm_plan* p)
     L.snapC = take(L.snap_step * dev_steps);
     L.ckpt_slot = L.set_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
-    L.recrows = take(S * (uint64_t)p->n_slots * (uint64_t)g.nx * 4);
+    L.ev_row = (uint64_t)p->NS * (uint64_t)g.nx * 4;
+    const uint64_t evb = L.ev_row * (uint64_t)p->EB;
+    L.ev_fadd = take(evb);
+    L.ev_fout = take(evb);
+    L.ev_aadd = take(evb);
+    L.ev_aout = take(evb);
     L.total = o;
     return true;
 }
@@ -429,10 +398,8 @@ struct Ptrs {
     char* base;
     const float* cp;
     Model model;
-    const int32_t *s_cell, *s_ptr, *s_list, *s_idx;
-    const int32_t *r_cell, *r_ptr, *r_list, *r_idx;
-    const int32_t *m_row, *m_cx, *m_cs, *m_sl, *m_rslot, *m_rg;
-    float* recrows;
+    const int32_t *row_slot, *colcell, *slot_shot, *cell_src, *src_list, *cell_rec, *rec_list, *src_pos, *rec_pos;
+    float *ev_fadd, *ev_fout, *ev_aadd, *ev_aout;
     char *snapE, *snapC, *ckpt;
     float* scratch;
 };
@@ -446,11 +413,11 @@ Ptrs pointers(const tm_plan* p, void* ws)
     q.model = Model{wsp<char>(ws, L.model), (uint32_t)L.model_bytes, 0u, (uint32_t)L.slab_b,
                     (uint32_t)(2 * L.slab_b)};
     const int32_t* t = wsp<int32_t>(ws, L.tables);
-    q.s_cell = t + p->t_s_cell; q.s_ptr = t + p->t_s_ptr; q.s_list = t + p->t_s_list; q.s_idx = t + p->t_s_idx;
-    q.r_cell = t + p->t_r_cell; q.r_ptr = t + p->t_r_ptr; q.r_list = t + p->t_r_list; q.r_idx = t + p->t_r_idx;
-    q.m_row = t + p->t_m_row; q.m_cx = t + p->t_m_cx; q.m_cs = t + p->t_m_cs; q.m_sl = t + p->t_m_sl;
-    q.m_rslot = t + p->t_m_rslot; q.m_rg = t + p->t_m_rg;
-    q.recrows = wsp<float>(ws, L.recrows);
+    q.row_slot = t + p->t_slot; q.colcell = t + p->t_colcell; q.slot_shot = t + p->t_sshot;
+    q.cell_src = t + p->t_cs; q.src_list = t + p->t_sl; q.cell_rec = t + p->t_cr; q.rec_list = t + p->t_rl;
+    q.src_pos = t + p->t_spos; q.rec_pos = t + p->t_rpos;
+    q.ev_fadd = wsp<float>(ws, L.ev_fadd); q.ev_fout = wsp<float>(ws, L.ev_fout);
+    q.ev_aadd = wsp<float>(ws, L.ev_aadd); q.ev_aout = wsp<float>(ws, L.ev_aout);
     q.snapE = wsp<char>(ws, L.snapE);
     q.snapC = wsp<char>(ws, L.snapC);
     q.ckpt = wsp<char>(ws, L.ckpt);
@@ -522,14 +489,35 @@ tm_status slot_copy(tm_plan* p, const Ptrs& q, int i, int64_t j, bool to_host)
     return TM_OK;
 }
 
-// One forward step t (set cur -> 1-cur): H and E updates with the snapshot
-// epilogue (se/sc non-null) in one kernel, then sources and receivers.
-template <int P>
-void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int64_t t, int snap, char* se,
-              char* sc, hipStream_t st)
+// One forward step t (set cur -> 1-cur): H and E updates, the step's
+// sources and receivers and the snapshot epilogue (se/sc non-null) in one
+// kernel.
+// Event-row view of the forward (adjoint = false) or adjoint buffers: the
+// add rows [EB][NS][nx] followed by the out rows.
+EventRows event_rows(const tm_plan* p, const Ptrs& q, bool adjoint)
 {
     const Layout& L = p->lay;
-    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
+    const uint64_t a = adjoint ? L.ev_aadd : L.ev_fadd, o = adjoint ? L.ev_aout : L.ev_fout;
+    return EventRows{q.row_slot, q.base + a, (uint32_t)(o + L.ev_row * (uint64_t)p->EB - a)};
+}
+
+// Offsets of step t's add and out rows in that view.  Forward: add = the
+// sources, out = the rows the receivers are gathered from; adjoint: add =
+// the residual at the receivers, out = the rows of the source-wavelet
+// gradient.
+EventStep event_step(const tm_plan* p, bool adjoint, int64_t t)
+{
+    const Layout& L = p->lay;
+    const uint64_t a = adjoint ? L.ev_aadd : L.ev_fadd, o = adjoint ? L.ev_aout : L.ev_fout;
+    const uint64_t row = (uint64_t)(t % p->EB) * L.ev_row;
+    return EventStep{(uint32_t)row, (uint32_t)(o - a + row)};
+}
+
+template <int P>
+void fwd_step(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap, char* se, char* sc,
+              hipStream_t st)
+{
+    const Layout& L = p->lay;
     FwdArgs a;
     a.g = p->g;
     a.t = p->tiling_fwd;
@@ -541,6 +529,8 @@ void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int6
     a.snap_e = se;
     a.snap_c = sc;
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
+    a.ev = event_rows(p, q, false);
+    a.es = event_step(p, false, t);
     const dim3 grid((unsigned)p->tiling_fwd.nblk), blk(NT);
     timed(p, KID_FWD_STEP, t, st, [&] {
         if (snap == SNAP_F32) k_fwd_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
@@ -548,25 +538,16 @@ void fwd_step(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int6
         else if (snap == SNAP_FP8) k_fwd_step<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
         else k_fwd_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
-    const float* ft = ns > 0 ? f + t * S * ns : nullptr;
-    float* rt = (r != nullptr && nr > 0) ? r + t * S * nr : nullptr;
-    if (ft != nullptr || rt != nullptr) {
-        k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            a.set1, L.st.shot_bytes, L.st.oE, ft, (int)ns, q.s_cell, q.s_ptr, q.s_list, rt, (int)nr, q.r_idx,
-            nullptr, nullptr, nullptr, 0, 0);
-    }
 }
 
-// Forward steps t and t+1 in one launch (set cur -> 1-cur), the step-t
-// sources and receivers inside it; then step t+1's sources and receivers
-// and the gather of step t's receivers.  se0/sc0, se1/sc1: snapshot
-// destinations of steps t and t+1, or null.
+// Forward steps t and t+1 in one launch (set cur -> 1-cur), with the
+// sources and receivers of both.  se0/sc0, se1/sc1: snapshot destinations
+// of steps t and t+1, or null.
 template <int P>
-void fwd_step2(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int64_t t, int snap, char* se0,
-               char* sc0, char* se1, char* sc1, hipStream_t st)
+void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap, char* se0, char* sc0,
+               char* se1, char* sc1, hipStream_t st)
 {
     const Layout& L = p->lay;
-    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
     Fwd2Args a;
     a.g = p->g;
     a.t = p->tiling_fwd2;
@@ -580,16 +561,9 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int
     a.snap_e1 = se1;
     a.snap_c1 = sc1;
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
-    const bool recs = r != nullptr && nr > 0;
-    a.ev.row_cells = ns > 0 ? q.m_row : nullptr;
-    a.ev.cell_x = q.m_cx;
-    a.ev.cell_src = q.m_cs;
-    a.ev.src_list = q.m_sl;
-    a.ev.f = ns > 0 ? f + t * S * ns : nullptr;
-    a.ev.n_src = (int)ns;
-    a.ev.rec_slot = recs ? q.m_rslot : nullptr;
-    a.ev.rec_rows = q.recrows;
-    a.ev.n_slots = p->n_slots;
+    a.ev = event_rows(p, q, false);
+    a.es0 = event_step(p, false, t);
+    a.es1 = event_step(p, false, t + 1);
     const dim3 grid((unsigned)p->tiling_fwd2.nblk), blk(NT);
     timed(p, KID_FWD_STEP2, t, st, [&] {
         if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
@@ -597,23 +571,16 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, const float* f, float* r, int
         else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
         else k_fwd_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
-    const float* ft = ns > 0 ? f + (t + 1) * S * ns : nullptr;
-    float* rt = recs ? r + (t + 1) * S * nr : nullptr;
-    float* rp = recs ? r + t * S * nr : nullptr;
-    if (ft != nullptr || rt != nullptr) {
-        k_fwd_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            a.set1, L.st.shot_bytes, L.st.oE, ft, (int)ns, q.s_cell, q.s_ptr, q.s_list, rt, (int)nr, q.r_idx,
-            q.recrows, q.m_rg, rp, p->n_slots, p->g.nx);
-    }
 }
 
-// One adjoint step t; k counts the adjoint steps taken (set k%2 -> (k+1)%2).
+// One adjoint step t (residual injection at the receivers, transposed H and
+// E updates, source-wavelet gradient and parameter-gradient accumulation in
+// one kernel); k counts the adjoint steps taken (set k%2 -> (k+1)%2).
 template <int P>
-void adj_step(tm_plan* p, const Ptrs& q, const float* grad_r, float* grad_f, int64_t t, int64_t k, int snap,
-              const char* se, const char* sc, float* gca, float* gcb, hipStream_t st)
+void adj_step(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const char* se,
+              const char* sc, float* gca, float* gcb, hipStream_t st)
 {
     const Layout& L = p->lay;
-    const int64_t S = p->d.n_shots, ns = p->d.n_src, nr = p->d.n_rec;
     AdjArgs a;
     a.g = p->g;
     a.t = p->tiling_adj;
@@ -622,18 +589,14 @@ void adj_step(tm_plan* p, const Ptrs& q, const float* grad_r, float* grad_f, int
     a.cp = q.cp;
     a.set0 = q.base + L.aset[k & 1];
     a.set1 = q.base + L.aset[(k + 1) & 1];
-    const float* grt = nr > 0 ? grad_r + t * S * nr : nullptr;
-    float* gft = (grad_f != nullptr && ns > 0) ? grad_f + t * S * ns : nullptr;
-    if (grt != nullptr || gft != nullptr) {
-        k_adj_srcrec<<<dim3((unsigned)S), dim3(256), 0, st>>>(
-            q.base + L.aset[k & 1], L.st.shot_bytes, L.st.oE, grt, (int)nr, q.r_cell, q.r_ptr, q.r_list, gft, (int)ns, q.s_idx);
-    }
     a.snap_e = se;
     a.snap_c = sc;
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
     a.gca = gca;
     a.gcb = gcb;
     a.ratio = (float)p->R;
+    a.ev = event_rows(p, q, true);
+    a.es = event_step(p, true, t);
     const dim3 grid((unsigned)p->tiling_adj.nblk), blk(NT);
     timed(p, KID_ADJ_STEP, t, st, [&] {
         if (snap == SNAP_F32) k_adj_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
@@ -703,6 +666,39 @@ tm_status device_tiling(tm_plan* p)
     return TM_OK;
 }
 
+// Event rows of the steps [ta, tb) (one event block): the sums of the
+// step's inputs (f: sources, grad_r: receivers) into the add rows.
+tm_status events_add(const tm_plan* p, const Ptrs& q, bool adjoint, const float* in, int64_t ta, int64_t tb,
+                     hipStream_t st)
+{
+    const int64_t S = p->d.n_shots, n_in = adjoint ? p->d.n_rec : p->d.n_src;
+    if (p->NS == 0 || tb <= ta) return TM_OK;           // (no inputs: rows of zeros)
+    const int64_t n = (tb - ta) * p->NS * p->g.nx;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    float* rows = (adjoint ? q.ev_aadd : q.ev_fadd) + (uint64_t)(ta % p->EB) * (p->lay.ev_row / 4);
+    k_event_add<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+        rows, n, (int)p->NS, p->g.nx, q.colcell, q.slot_shot, adjoint ? q.cell_rec : q.cell_src,
+        adjoint ? q.rec_list : q.src_list, n_in > 0 ? in + ta * S * n_in : nullptr, (int)S, (int)n_in);
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
+
+// Outputs of the steps [ta, tb) (one event block) from the out rows:
+// receiver records (forward, into r) or the source-wavelet gradient
+// (adjoint, into grad_f); absent entries get 0.
+tm_status events_gather(const tm_plan* p, const Ptrs& q, bool adjoint, float* out, int64_t ta, int64_t tb,
+                        hipStream_t st)
+{
+    const int64_t S = p->d.n_shots, n_out = adjoint ? p->d.n_src : p->d.n_rec;
+    if (out == nullptr || n_out == 0 || tb <= ta) return TM_OK;
+    const int64_t n = (tb - ta) * S * n_out;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    const float* rows = (adjoint ? q.ev_aout : q.ev_fout) + (uint64_t)(ta % p->EB) * (p->lay.ev_row / 4);
+    k_event_gather<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+        out + ta * S * n_out, n, (int)(S * n_out), adjoint ? q.src_pos : q.rec_pos, rows,
+        (int64_t)(p->lay.ev_row / 4));
+    return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+}
+
 // Forward steps [t0, t1) from set *cur (updated).  snap: SNAP_* kind of the
 // stored steps (the multiples of R), whose device destinations
 // snap_at(t, se, sc) gives; host: copy every stored step to the host store
@@ -713,14 +709,22 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
                         int snap, SnapAt snap_at, bool ckpt, bool host, hipStream_t st)
 {
     auto stored = [&](int64_t t) { return snap != SNAP_NONE && t % p->R == 0; };
+    int64_t ev_a = t0, ev_b = t0;        // event block of the current steps: [ev_a, ev_b)
+    tm_status v = TM_OK;
     for (int64_t t = t0; t < t1;) {
+        if (t == ev_b) {                 // records of the finished block, add rows of the next
+            if ((v = events_gather(p, q, false, r, ev_a, ev_b, st)) != TM_OK) return v;
+            ev_a = t;
+            ev_b = std::min(t1, (t / p->EB + 1) * p->EB);
+            if ((v = events_add(p, q, false, f, ev_a, ev_b, st)) != TM_OK) return v;
+        }
         if (ckpt && t > 0 && t % p->K == 0) {
             const int64_t slot = t / p->K - 1;
             HIPCHK(hipMemcpyAsync(q.ckpt + slot * p->lay.ckpt_slot, q.base + p->lay.fset[*cur],
                                   p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
         }
         // two steps per launch unless step t+1 starts a checkpoint interval
-        const bool pair = p->time_block == 2 && t + 1 < t1 && !(ckpt && (t + 1) % p->K == 0);
+        const bool pair = p->time_block == 2 && t + 1 < ev_b && !(ckpt && (t + 1) % p->K == 0);
         const int nstep = pair ? 2 : 1;
         char *se[2] = {nullptr, nullptr}, *sc[2] = {nullptr, nullptr};
         bool any = false;
@@ -734,8 +738,8 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
             any = true;
         }
         const int kind = any ? snap : SNAP_NONE;
-        if (pair) fwd_step2<P>(p, q, *cur, f, r, t, kind, se[0], sc[0], se[1], sc[1], st);
-        else fwd_step<P>(p, q, *cur, f, r, t, kind, se[0], sc[0], st);
+        if (pair) fwd_step2<P>(p, q, *cur, r, t, kind, se[0], sc[0], se[1], sc[1], st);
+        else fwd_step<P>(p, q, *cur, r, t, kind, se[0], sc[0], st);
         for (int i = 0; host && i < nstep; ++i) {
             if (!stored(t + i)) continue;
             const int slot = (int)dev_slot(p, t + i);
@@ -746,10 +750,10 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
         t += nstep;
         *cur = 1 - *cur;
     }
+    if ((v = events_gather(p, q, false, r, ev_a, ev_b, st)) != TM_OK) return v;
     if (host) {                     // the caller's stream sees the host store complete
         for (int i = 0; i < HOST_RING; ++i) {
-            tm_status v = slot_acquire(p, i, st);
-            if (v != TM_OK) return v;
+            if ((v = slot_acquire(p, i, st)) != TM_OK) return v;
         }
     }
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
@@ -784,6 +788,18 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
     const bool want_grad = gca != nullptr || gcb != nullptr;
     const int snap = want_grad ? snap_kind(p) : SNAP_NONE;
     int64_t k = 0;
+    // Event blocks in reverse time: before the adjoint step t of a new
+    // block [ev_a, ev_b), the source gradient of the finished block and the
+    // residual rows of the new one.
+    int64_t ev_a = nt, ev_b = nt;
+    auto events = [&](int64_t t) {
+        if (t >= ev_a) return TM_OK;
+        tm_status e = events_gather(p, q, true, grad_f, ev_a, ev_b, st);
+        if (e != TM_OK) return e;
+        ev_b = t + 1;
+        ev_a = (t / p->EB) * p->EB;
+        return events_add(p, q, true, grad_r, ev_a, ev_b, st);
+    };
     if (p->K == 0 || !want_grad) {
         const bool host = want_grad && p->storage == TM_STORE_HOST;
         const int64_t j_last = (nt - 1) / p->R;           // last stored step index
@@ -797,7 +813,8 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             const int64_t slot = use ? dev_slot(p, t) : 0;
             if (use && host && (v = slot_acquire(p, (int)slot, st)) != TM_OK) return v;
             const uint64_t so = (uint64_t)slot * p->lay.snap_step;
-            adj_step<P>(p, q, grad_r, grad_f, t, k, use ? snap : SNAP_NONE, use ? q.snapE + so : nullptr,
+            if ((v = events(t)) != TM_OK) return v;
+            adj_step<P>(p, q, t, k, use ? snap : SNAP_NONE, use ? q.snapE + so : nullptr,
                         use ? q.snapC + so : nullptr, gca, gcb, st);
             if (use && host) {
                 if ((v = slot_release(p, (int)slot, st)) != TM_OK) return v;
@@ -823,11 +840,14 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             };
             v = forward_range<P>(p, q, &cur, f, nullptr, ta, tb, snap, at, false, false, st);
             if (v != TM_OK) return v;
-            for (int64_t t = tb - 1; t >= ta; --t, ++k)
-                adj_step<P>(p, q, grad_r, grad_f, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
+            for (int64_t t = tb - 1; t >= ta; --t, ++k) {
+                if ((v = events(t)) != TM_OK) return v;
+                adj_step<P>(p, q, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
                             q.snapC + (t - ta) * p->lay.snap_step, gca, gcb, st);
+            }
         }
     }
+    if ((v = events_gather(p, q, true, grad_f, ev_a, ev_b, st)) != TM_OK) return v;
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
 
@@ -931,14 +951,22 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         p->tables.insert(p->tables.end(), v.begin(), v.end());
         return at;
     };
-    const Scatter ss = build_scatter(src, d.n_shots, d.n_src);
-    const Scatter rs = build_scatter(rec, d.n_shots, d.n_rec);
-    p->t_s_cell = append(ss.cell); p->t_s_ptr = append(ss.ptr); p->t_s_list = append(ss.list); p->t_s_idx = append(ss.idx);
-    p->t_r_cell = append(rs.cell); p->t_r_ptr = append(rs.ptr); p->t_r_list = append(rs.list); p->t_r_idx = append(rs.idx);
-    const MidTables mt = build_mid(src, d.n_src, rec, d.n_rec, d.n_shots, d.ny, d.nx);
-    p->t_m_row = append(mt.row_cells); p->t_m_cx = append(mt.cell_x); p->t_m_cs = append(mt.cell_src);
-    p->t_m_sl = append(mt.src_list); p->t_m_rslot = append(mt.rec_slot); p->t_m_rg = append(mt.rec_gather);
-    p->n_slots = mt.n_slots;
+    const EventTables et = build_events(src, d.n_src, rec, d.n_rec, d.n_shots, d.ny, d.nx);
+    p->t_slot = append(et.row_slot); p->t_colcell = append(et.colcell); p->t_sshot = append(et.slot_shot);
+    p->t_cs = append(et.cell_src); p->t_sl = append(et.src_list);
+    p->t_cr = append(et.cell_rec); p->t_rl = append(et.rec_list);
+    p->t_spos = append(et.src_pos); p->t_rpos = append(et.rec_pos);
+    p->NS = et.n_slots;
+    if ((uint64_t)p->NS * (uint64_t)d.nx * 4 > EV_ROW_MAX) { delete p; return TM_ENOMEM; }
+    // steps per event block: each of the four event buffers stays within
+    // EV_BLOCK_BYTES; even, so that blocks do not split pairs of steps
+    p->EB = p->NS > 0 ? std::max<int64_t>(1, std::min<int64_t>(d.nt, (int64_t)(EV_BLOCK_BYTES / (p->NS * d.nx * 4))))
+                      : d.nt;
+    if (p->EB > 1 && p->EB < d.nt) p->EB &= ~int64_t(1);
+    if (const char* env = std::getenv("TM_FDTD_EVENT_STEPS")) {   // forced block length (tests, tuning)
+        const long long v = std::atoll(env);
+        if (v >= 1) p->EB = std::min<int64_t>(v, d.nt);
+    }
     p->time_block = d.time_block == 0 ? 2 : (int)d.time_block;
     p->R = d.step_ratio > 1 ? d.step_ratio : 1;
     p->n_store = (d.nt + p->R - 1) / p->R;

@@ -23,7 +23,7 @@
 //
 // Adjoint step, the exact transpose of the forward step (the same page's
 // header comment: time-reversed, transposed operators), per cell:
-//   e = lambda_E (the residual already injected at the receivers);
+//   e = lambda_E with the step's residual added at the receivers;
 //   gradients (interior); h = Cb e; u, w = band filters of h (own
 //   memories, run backwards in time); lambda_Hz -= Dx^h[u];
 //   lambda_Hx += Dz^h[w]; t = band filters of Cq lambda_H;
@@ -229,6 +229,49 @@ struct Model {
     uint32_t oCa, oCb, oCq;
 };
 
+// Sources and receivers (tide-GPR 0.0.9, maxwell.cu: add_sources_ey and
+// record_receivers_ey, and their adjoints add_adjoint_sources_ey and
+// record_adjoint_at_sources).  The grid rows of a shot that hold sources or
+// receivers are "event rows", numbered by a slot g (row_slot, -1 for the
+// others).  Before a run of steps a small kernel sums each step's inputs
+// per cell into dense rows add[g][x] (0 at cells without inputs); a step
+// kernel loads the add row of an event row with the field row, adds it to
+// the field wherever it computes the row (halo lanes included, so every
+// workgroup sees the same values), and the owner of each cell writes the
+// field after the addition to out[g][x].  A gather kernel then picks the
+// receivers (forward) or the sources (adjoint) out of the out rows.  The
+// forward adds sources and reads receivers; the adjoint adds the residual
+// at the receivers and reads the sources.
+struct EventRows {
+    const int* __restrict__ row_slot;   // [S*ny]: slot of (shot, row), or -1
+    char* __restrict__ base;            // the event-row buffers of the run (one view)
+    uint32_t bytes;                     // of the view
+};
+// Byte offsets within EventRows::base of one step's add rows and out rows
+// [NS][nx] (both always inside the view: a step without inputs adds rows of
+// zeros, and out rows nobody gathers are simply not read).
+struct EventStep {
+    uint32_t add, out;
+};
+
+// Slots of rows y_first .. y_first+n-1 of shot s into LDS (-1 outside the
+// grid) and the first / last of those rows that are event rows into
+// *lo / *hi, which the caller set to INT32_MAX / INT32_MIN before a barrier;
+// the caller synchronises afterwards.
+__device__ __forceinline__ void load_row_slots(int* t, int* lo, int* hi, const int* __restrict__ row_slot, int s,
+                                               int ny, int y_first, int n)
+{
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int y = y_first + i;
+        const int g = (y >= 0 && y < ny) ? row_slot[s * ny + y] : -1;
+        t[i] = g;
+        if (g >= 0) {
+            atomicMin(lo, y);
+            atomicMax(hi, y);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Forward step
 // ---------------------------------------------------------------------------
@@ -243,6 +286,8 @@ struct FwdArgs {
     char* __restrict__ snap_e;         // Ey^n on the interior window [S][nyi][nxi], or null
     char* __restrict__ snap_c;         // curl H^n
     uint32_t snap_shot_bytes;
+    EventRows ev;                      // sources (add) and receivers (out)
+    EventStep es;                      // ... of this step
 };
 
 template <int P, int SNAP>
@@ -253,6 +298,8 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
     __shared__ float rowE[NT];
     __shared__ float ring[P][NT];
     __shared__ float cyt[CH_MAX + 2 * P][6];
+    __shared__ int evs[CH_MAX];         // slots of the owned rows
+    __shared__ int ev_lo, ev_hi;        // first / last owned event row
 
     const Geo& g = a.g;
     const StateLayout& L = a.L;
@@ -264,8 +311,15 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
     const int xe = min(xs + W, nx - P + 1);
     const int ya = P + chunk * a.t.CH;
     const int yb = min(ya + a.t.CH, ny - P + 1);
-    load_row_cpml(cyt, a.cp, g, ya - P, yb - ya + 2 * P - 1);   // rows ya-P .. yb+P-2
+    if (tid == 0) {
+        ev_lo = INT32_MAX;
+        ev_hi = INT32_MIN;
+    }
     __syncthreads();
+    load_row_cpml(cyt, a.cp, g, ya - P, yb - ya + 2 * P - 1);   // rows ya-P .. yb+P-2
+    load_row_slots(evs, &ev_lo, &ev_hi, a.ev.row_slot, s, ny, ya, yb - ya);
+    __syncthreads();
+    const int e_lo = ev_lo, e_hi = ev_hi;
 
     const int c = xs - OFF + tid;                       // this thread's column
     const bool own = c >= xs && c < xe;
@@ -295,14 +349,20 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
     const RBuf bm(a.m.base, a.m.bytes);
     const RBuf bse(a.snap_e + (int64_t)s * a.snap_shot_bytes, SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u);
     const RBuf bsc(a.snap_c + (int64_t)s * a.snap_shot_bytes, SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u);
+    const RBuf bev(a.ev.base, a.ev.bytes);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
 
     // Prefetch ring: every global load of iteration r is issued at
     // iteration r - D into slot (r - ya) % D; `live` is false past the end
     // of the chunk (those loads are still issued, out of range).
-    float fE[D], fQ[D], fHx[D], fHz[D], fCa[D], fCb[D], fMyh[D], fMxh[D], fMxe[D], fMye[D];
+    float fE[D], fQ[D], fHx[D], fHz[D], fCa[D], fCb[D], fMyh[D], fMxh[D], fMxe[D], fMye[D], fEv[D];
+    int fG[D];                                          // slot of the E row, or -1 (uniform)
     auto issue = [&](int u, int r, bool live) {
         const int h = r - P, y = r - 2 * P + 1;
+        const int gs = (y >= e_lo && y <= e_hi) ? __builtin_amdgcn_readfirstlane(evs[y - ya]) : -1;
+        fG[u] = gs;
+        fEv[u] = 0.0f;
+        if (gs >= 0) fEv[u] = bev.ld(live && own, (uint32_t)(gs * nx) * 4u + c4, a.es.add);   // uniform
         const uint32_t oh = (uint32_t)(h * nx) * 4u + c4, oy = (uint32_t)(y * nx) * 4u + c4;
         fE[u] = b0.ld(live && r >= 0 && r < ny && incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
         fQ[u] = bm.ld(live && incol && (hx_row(h) || h_own(h)), oh, a.m.oCq);
@@ -411,7 +471,11 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
                         snap_put<SNAP>(bsc, own && in_x, w, curl);
                     }
                 }
-                const float en = fmaf(fCa[u], ev, fCb[u] * curl);
+                float en = fmaf(fCa[u], ev, fCb[u] * curl);
+                if (fG[u] >= 0) {                       // uniform: sources, then receivers
+                    en = en + fEv[u];
+                    bev.st(own, en, (uint32_t)(fG[u] * nx) * 4u + c4, a.es.out);
+                }
                 b1.st(own, en, (uint32_t)(y * nx) * 4u + c4, L.oE);
             }
             issue(u, r + D, r + D <= r_end);
@@ -437,6 +501,8 @@ struct AdjArgs {
     float* __restrict__ gca;           // per-shot gradients [S][ny][nx], or null
     float* __restrict__ gcb;
     float ratio;                       // weight of this step's gradient term (the snapshot step ratio)
+    EventRows ev;                      // residual at the receivers (add), sources (out)
+    EventStep es;                      // ... of this step
 };
 
 template <int P, int SNAP>
@@ -448,6 +514,8 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     __shared__ float rowU[NT];
     __shared__ float ring[P][NT];
     __shared__ float cyt[CH_MAX + 4 * P][6];
+    __shared__ int evs[CH_MAX + 4 * P];         // row slots, indexed like cyt
+    __shared__ int ev_lo, ev_hi;                // first / last event row of the window
 
     const Geo& g = a.g;
     const StateLayout& L = a.L;
@@ -459,8 +527,15 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     const int xe = min(xs + W, nx - P + 1);
     const int ya = P + chunk * a.t.CH;
     const int yb = min(ya + a.t.CH, ny - P + 1);
-    load_row_cpml(cyt, a.cp, g, ya - T0, yb - ya + 4 * P - 2);   // rows ya-2P+1 .. yb+2P-2
+    if (tid == 0) {
+        ev_lo = INT32_MAX;
+        ev_hi = INT32_MIN;
+    }
     __syncthreads();
+    load_row_cpml(cyt, a.cp, g, ya - T0, yb - ya + 4 * P - 2);   // rows ya-2P+1 .. yb+2P-2
+    load_row_slots(evs, &ev_lo, &ev_hi, a.ev.row_slot, s, ny, ya - T0, yb - ya + 4 * P - 2);
+    __syncthreads();
+    const int e_lo = ev_lo, e_hi = ev_hi;
 
     const int c = xs - OFF + tid;
     const bool own = c >= xs && c < xe;
@@ -496,15 +571,25 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     const uint32_t slab_b = (uint32_t)(g.slab * 4);
     const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
     const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
+    const RBuf bev(a.ev.base, a.ev.bytes);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
+    // slot of window row r, or -1 (uniform)
+    auto slot_of = [&](int r) {
+        return (r >= e_lo && r <= e_hi) ? __builtin_amdgcn_readfirstlane(evs[r - ya + T0]) : -1;
+    };
 
     // Prefetch ring (see k_fwd_step).
     float fE[D], fCb[D], fMxe[D], fMye[D], fSe[D], fSc[D], fGa[D], fGb[D];
-    float fHx[D], fMyh[D], fQ[D], fHz[D], fMxh[D], fCa[D];
+    float fHx[D], fMyh[D], fQ[D], fHz[D], fMxh[D], fCa[D], fEv[D];
+    int fG[D];
     auto issue = [&](int u, int r, bool live) {
         const int h = r - P, y = r - 2 * P + 1;
         const uint32_t orr = (uint32_t)(r * nx) * 4u + c4, oh = (uint32_t)(h * nx) * 4u + c4;
         const bool e_do = live && e_col && e_row(r);
+        const int gs = slot_of(r);
+        fG[u] = gs;
+        fEv[u] = 0.0f;
+        if (gs >= 0) fEv[u] = bev.ld(e_do, (uint32_t)(gs * nx) * 4u + c4, a.es.add);   // uniform
         fE[u] = b0.ld(e_do, orr, L.oE);
         fCb[u] = bm.ld(e_do, orr, a.m.oCb);
         fMxe[u] = b0.ld(e_do && fx_e, (uint32_t)(r * g.bx) * 4u + bx4, L.oMxe);
@@ -534,6 +619,16 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
 #pragma unroll
     for (int i = 0; i <= P; ++i) ud[i] = 0.0f;
 
+    // lambda_E^{n+1} of row r (slot gs, add-row value ev) with the step's
+    // residual added at the receivers: every workgroup reading the row adds
+    // it; the owner of the cell keeps the result (source-wavelet gradient).
+    auto inject = [&](int r, int gs, float ev, float e) {
+        if (gs >= 0) {                                  // uniform
+            e = e + ev;
+            bev.st(own && r >= ya && r < yb, e, (uint32_t)(gs * nx) * 4u + c4, a.es.out);
+        }
+        return e;
+    };
     // u, w of the E-set cell (r, c) for input row r (0 off the E-set); the
     // filter memories are written back on owned cells.
     auto front = [&](int r, float e, float cbv, float mx, float my, float& u, float& w) {
@@ -569,7 +664,9 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
         const int r = ya - 2 * P + i;
         const bool e_do = e_col && e_row(r);
         const uint32_t orr = (uint32_t)(r * nx) * 4u + c4;
-        const float e0 = b0.ld(e_do, orr, L.oE), cbv = bm.ld(e_do, orr, a.m.oCb);
+        const int gs = slot_of(r);
+        const float ev = bev.ld(e_do && gs >= 0, (uint32_t)(gs * nx) * 4u + c4, a.es.add);
+        const float e0 = inject(r, gs, ev, b0.ld(e_do, orr, L.oE)), cbv = bm.ld(e_do, orr, a.m.oCb);
         const float mx = b0.ld(e_do && fx_e, (uint32_t)(r * g.bx) * 4u + bx4, L.oMxe);
         const float my = b0.ld(e_do && fy_e(r), (uint32_t)(band_y(g, r) * nx) * 4u + c4, L.oMye);
         float u, w;
@@ -587,7 +684,7 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
             if (r > r_end) return;
             const int u = uu % D;
             {
-                const float e = fE[u];
+                const float e = inject(r, fG[u], fEv[u], fE[u]);
                 float uv, wv;
                 front(r, e, fCb[u], fMxe[u], fMye[u], uv, wv);
                 if constexpr (SNAP != SNAP_NONE) {

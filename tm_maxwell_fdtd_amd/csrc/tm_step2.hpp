@@ -25,14 +25,11 @@
 // operation is written as in k_fwd_step, so both kernels give bitwise the
 // same state.
 //
-// Sources of step n are added to E^{n+1} inside the kernel (per-row
-// distinct-cell lists staged in LDS; several sources on one cell are summed
-// first, in index order, then added, as in k_fwd_srcrec), at every lane
-// that computes that cell, halo lanes included.  Receivers of step n read
-// E^{n+1} after the injection: the owned part of each receiver row is
-// written to a small row buffer that the step's small follow-up kernel
-// gathers from.  Sources and receivers of step n+1 are handled by that
-// kernel on the written state, as after a single step.
+// Sources and receivers of both steps are handled inside the kernel through
+// the event rows (EventRows): the add row of step n is added to E^{n+1} at
+// every lane that computes the row, halo lanes included, and the owner
+// keeps the result; stage B does the same for step n+1 on its owned output
+// rows.
 //
 // Fast blocks: most unrolled blocks of a chunk lie where every stage is
 // active, no row is a CPML band row or carries sources or receivers, and
@@ -58,20 +55,6 @@ struct Strip2 {
     static constexpr int OFF = 4 * P - 2;      // lane of the first owned column
 };
 
-// Sources and receivers of the intermediate step (step n of the pair).
-struct MidEvents {
-    const int* __restrict__ row_cells;   // [S*ny + 1]: distinct source cells of (shot, row) are
-                                         //   [row_cells[s*ny+y], row_cells[s*ny+y+1]); null = none
-    const int* __restrict__ cell_x;      // column of each distinct cell
-    const int* __restrict__ cell_src;    // [n_cells + 1]: its sources are src_list[cell_src[k] ..)
-    const int* __restrict__ src_list;    // source indices, ascending per cell
-    const float* __restrict__ f;         // f[n]: [S][n_src]
-    int n_src;
-    const int* __restrict__ rec_slot;    // [S*ny]: row-buffer slot of a receiver row, or -1; null = none
-    float* __restrict__ rec_rows;        // [S][n_slots][nx]
-    int n_slots;
-};
-
 struct Fwd2Args {
     Geo g;
     Tiling t;
@@ -85,7 +68,8 @@ struct Fwd2Args {
     char* __restrict__ snap_e1;        // Ey^{n+1}, curl H^{n+1}, or null
     char* __restrict__ snap_c1;
     uint32_t snap_shot_bytes;
-    MidEvents ev;
+    EventRows ev;                      // sources (add) and receivers (out)
+    EventStep es0, es1;                // ... of steps n and n+1
 };
 
 template <int P, int SNAP>
@@ -101,8 +85,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     __shared__ float ringB[P][NT];                  // Hz^{n+3/2} rows
     __shared__ float mfifo[4][R2][NT];              // stage A's CPML memories, lane-private
     __shared__ float cyt[CH2_MAX + 6 * P - 3][6];   // per-row CPML coefficients
-    __shared__ int evs[CH2_MAX + 4 * P - 2][2];     // source-cell range per stage-A E row
-    __shared__ int evr[CH2_MAX];                    // receiver slot per owned row
+    __shared__ int evs[CH2_MAX + 4 * P - 2];        // slot of each stage-A E row
     __shared__ int ev_lo, ev_hi;                    // first / last stage-A E row with events
 
     const Geo& g = a.g;
@@ -121,24 +104,9 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
         ev_lo = INT32_MAX;
         ev_hi = INT32_MIN;
     }
-    load_row_cpml(cyt, a.cp, g, yc0, yb - ya + 6 * P - 3);
     __syncthreads();
-    for (int i = tid; i < yb - ya + 4 * P - 2; i += NT) {
-        const int y = ye0 + i;
-        int b = 0, e = 0, slot = -1;
-        if (a.ev.row_cells != nullptr && y >= 0 && y < ny) {
-            b = a.ev.row_cells[s * ny + y];
-            e = a.ev.row_cells[s * ny + y + 1];
-        }
-        if (a.ev.rec_slot != nullptr && y >= ya && y < yb) slot = a.ev.rec_slot[s * ny + y];
-        evs[i][0] = b;
-        evs[i][1] = e;
-        if (y >= ya && y < yb) evr[y - ya] = slot;
-        if (b < e || slot >= 0) {
-            atomicMin(&ev_lo, y);
-            atomicMax(&ev_hi, y);
-        }
-    }
+    load_row_cpml(cyt, a.cp, g, yc0, yb - ya + 6 * P - 3);
+    load_row_slots(evs, &ev_lo, &ev_hi, a.ev.row_slot, s, ny, ye0, yb - ya + 4 * P - 2);
     __syncthreads();
 
     const int c = xs - OFF + tid;                   // this lane's column
@@ -184,6 +152,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     const RBuf bsc0(sb0 ? a.snap_c0 + so_s : nullptr, sb0);
     const RBuf bse1(sb1 ? a.snap_e1 + so_s : nullptr, sb1);
     const RBuf bsc1(sb1 ? a.snap_c1 + so_s : nullptr, sb1);
+    const RBuf bev(a.ev.base, a.ev.bytes);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
     const uint32_t rowb = (uint32_t)nx * 4u, brow = (uint32_t)g.bx * 4u;
 
@@ -201,15 +170,22 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     const int f_lo = max(ya, g.y0) + 4 * P - 2;
     const int f_hi = min(yb + 2 * P - 2, g.hy1 + P - 1) - (UNROLL - 1 + D);
     const int e_lo = ev_lo, e_hi = ev_hi;
+    // slot of stage-A E row y (ye0 <= y), or -1 (uniform)
+    auto slot_of = [&](int y) {
+        return (y >= e_lo && y <= e_hi) ? __builtin_amdgcn_readfirstlane(evs[y - ye0]) : -1;
+    };
 
     // Prefetch ring: the loads of iteration r are issued at iteration r - D
     // into slot (r - r_first) % D.
     float fE[D], fQa[D], fHx[D], fHz[D], fMyh[D], fMxh[D], fCa[D], fCb[D], fMxe[D], fMye[D];
-    float fQb[D], fCaB[D], fCbB[D];
+    float fQb[D], fCaB[D], fCbB[D], fEvA[D], fEvB[D];
+    int fGA[D], fGB[D];                             // slots of rows yA / yB, or -1
     auto issue = [&](auto fast_t, int u, int r, bool live) {
         constexpr bool FAST = decltype(fast_t)::value;
         const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
         if constexpr (FAST) {
+            fGA[u] = -1;
+            fGB[u] = -1;
             const uint32_t rA = (uint32_t)hA * rowb, eA = (uint32_t)yA * rowb;
             fE[u] = b0.ldv(v_in, L.oE + (uint32_t)r * rowb);
             fQa[u] = bm.ldv(v_in, a.m.oCq + rA);
@@ -225,6 +201,15 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
         } else {
             const uint32_t ohA = (uint32_t)(hA * nx) * 4u + c4, oyA = (uint32_t)(yA * nx) * 4u + c4;
             const uint32_t ohB = (uint32_t)(hB * nx) * 4u + c4, oyB = (uint32_t)(yB * nx) * 4u + c4;
+            // event rows first (uniform branches), then the loads every row has
+            const bool eb_do = live & own & own_row(yB);
+            const int gA = slot_of(yA), gB = slot_of(yB);
+            fGA[u] = gA;
+            fGB[u] = gB;
+            fEvA[u] = 0.0f;
+            fEvB[u] = 0.0f;
+            if (gA >= 0) fEvA[u] = bev.ld(live & incol, (uint32_t)(gA * nx) * 4u + c4, a.es0.add);
+            if (gB >= 0) fEvB[u] = bev.ld(eb_do, (uint32_t)(gB * nx) * 4u + c4, a.es1.add);
             fE[u] = b0.ld(live & in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
             fQa[u] = bm.ld(live & in_rows(hA) & incol, ohA, a.m.oCq);
             const bool hx_do = live & colE & hx_row(hA);
@@ -239,7 +224,6 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
             fMxe[u] = b0.ld(e_do & fx_e, (uint32_t)(yA * g.bx) * 4u + bx4, L.oMxe);
             fMye[u] = b0.ld(e_do & fy_e(yA), (uint32_t)(band_y(g, yA) * nx) * 4u + c4, L.oMye);
             fQb[u] = bm.ld(live & in_rows(hB) & incol & (hB >= ya - P), ohB, a.m.oCq);
-            const bool eb_do = live & own & own_row(yB);
             fCaB[u] = bm.ld(eb_do, oyB, a.m.oCa);
             fCbB[u] = bm.ld(eb_do, oyB, a.m.oCb);
         }
@@ -348,21 +332,9 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
             }
             float en = fmaf(fCa[u], ev, fCb[u] * curl);
             en = (FAST ? eA_ok : (eA_ok & rowE(yA))) ? en : 0.0f;
-            if constexpr (!FAST) {
-                const int kb = __builtin_amdgcn_readfirstlane(evs[yA - ye0][0]);
-                const int ke = __builtin_amdgcn_readfirstlane(evs[yA - ye0][1]);
-                for (int k = kb; k < ke; ++k) {                         // distinct source cells of the row
-                    const int col = a.ev.cell_x[k];
-                    float acc = 0.0f;
-                    for (int q = a.ev.cell_src[k]; q < a.ev.cell_src[k + 1]; ++q)
-                        acc += a.ev.f[s * a.ev.n_src + a.ev.src_list[q]];
-                    if (c == col) en = en + acc;
-                }
-                if (own_row(yA)) {
-                    const int slot = __builtin_amdgcn_readfirstlane(evr[yA - ya]);
-                    if (slot >= 0 && own)
-                        a.ev.rec_rows[((int64_t)s * a.ev.n_slots + slot) * nx + c] = en;
-                }
+            if (!FAST && fGA[u] >= 0) {                                  // uniform
+                en = en + fEvA[u];
+                bev.st(own & own_row(yA), en, (uint32_t)(fGA[u] * nx) * 4u + c4, a.es0.out);
             }
 #pragma unroll
             for (int i = 0; i < 2 * P - 1; ++i) ewB[i] = ewB[i + 1];
@@ -421,16 +393,23 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
                     snap_put<SNAP>(bsc1, own & in_x, w, curl);
                 }
             }
-            const float en = fmaf(fCaB[u], ev, fCbB[u] * curl);
-            if constexpr (FAST) b1.stv(en, v_own, L.oE + (uint32_t)yB * rowb);
-            else b1.st(own, en, (uint32_t)(yB * nx) * 4u + c4, L.oE);
+            float en = fmaf(fCaB[u], ev, fCbB[u] * curl);
+            if constexpr (FAST) {
+                b1.stv(en, v_own, L.oE + (uint32_t)yB * rowb);
+            } else {
+                if (fGB[u] >= 0) {                                      // uniform
+                    en = en + fEvB[u];
+                    bev.st(own, en, (uint32_t)(fGB[u] * nx) * 4u + c4, a.es1.out);
+                }
+                b1.st(own, en, (uint32_t)(yB * nx) * 4u + c4, L.oE);
+            }
         }
     };
 
     for (int r0 = r_first;; r0 += UNROLL) {
         // uniform: all rows this block computes and prefetches are steady
         const bool fast = r0 >= f_lo && r0 <= f_hi &&
-                          (r0 + UNROLL - 2 * P < e_lo || r0 - 2 * P + 1 > e_hi);
+                          (r0 + UNROLL + D - 2 * P < e_lo || r0 - 4 * P + 2 > e_hi);
         if (fast) {
 #pragma unroll
             for (int uu = 0; uu < UNROLL; ++uu) {
