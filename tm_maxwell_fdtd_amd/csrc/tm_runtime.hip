@@ -122,6 +122,7 @@ struct Layout {
     uint64_t fwd = 0, fwd_bytes = 0, fset[2] = {0, 0};
     uint64_t adj = 0, adj_bytes = 0, aset[2] = {0, 0};
     uint64_t snapE = 0, snapC = 0, snap_step = 0; // per-step bytes of one snapshot array (all shots)
+    uint64_t snap_stride = 0;                     // bytes per stored step: its Ey then its curl H
     uint64_t snap_shot = 0;                       // ... of one shot
     uint64_t ckpt = 0, ckpt_slot = 0;
     uint64_t ev_row = 0;                          // bytes of one step's event rows [NS][nx]
@@ -253,8 +254,9 @@ bool make_layout(tm_plan* p)
     L.snap_step = align_up(S * L.snap_shot);
     const uint64_t dev_steps = p->storage == TM_STORE_HOST ? (uint64_t)HOST_RING
                              : p->K > 0 ? (uint64_t)p->seg_steps : (uint64_t)p->n_store;
-    L.snapE = take(L.snap_step * dev_steps);
-    L.snapC = take(L.snap_step * dev_steps);
+    L.snap_stride = 2 * L.snap_step;
+    L.snapE = take(L.snap_stride * dev_steps);
+    L.snapC = L.snapE + L.snap_step;
     L.ckpt_slot = L.set_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
     L.ev_row = (uint64_t)p->NS * (uint64_t)g.nx * 4;
@@ -474,24 +476,15 @@ tm_status slot_copy(tm_plan* p, const Ptrs& q, int i, int64_t j, bool to_host)
     hipStream_t cs = p->copy_stream;
     if (p->slot_kernel_pending[i]) HIPCHK(hipStreamWaitEvent(cs, p->slot_done[i], 0));
     p->slot_kernel_pending[i] = false;
-    char* he = p->host_store + (uint64_t)j * 2 * n;
-    char* de = q.snapE + (uint64_t)i * n;
-    char* dc = q.snapC + (uint64_t)i * n;
-    if (to_host) {
-        HIPCHK(hipMemcpyAsync(he, de, n, hipMemcpyDeviceToHost, cs));
-        HIPCHK(hipMemcpyAsync(he + n, dc, n, hipMemcpyDeviceToHost, cs));
-    } else {
-        HIPCHK(hipMemcpyAsync(de, he, n, hipMemcpyHostToDevice, cs));
-        HIPCHK(hipMemcpyAsync(dc, he + n, n, hipMemcpyHostToDevice, cs));
-    }
+    char* he = p->host_store + (uint64_t)j * 2 * n;      // [E | C] of stored step j
+    char* de = q.snapE + (uint64_t)i * p->lay.snap_stride; // the slot: E then C
+    if (to_host) HIPCHK(hipMemcpyAsync(he, de, 2 * n, hipMemcpyDeviceToHost, cs));
+    else HIPCHK(hipMemcpyAsync(de, he, 2 * n, hipMemcpyHostToDevice, cs));
     HIPCHK(hipEventRecord(p->slot_copied[i], cs));
     p->slot_copy_pending[i] = true;
     return TM_OK;
 }
 
-// One forward step t (set cur -> 1-cur): H and E updates, the step's
-// sources and receivers and the snapshot epilogue (se/sc non-null) in one
-// kernel.
 // Event-row view of the forward (adjoint = false) or adjoint buffers: the
 // add rows [EB][NS][nx] followed by the out rows.
 EventRows event_rows(const tm_plan* p, const Ptrs& q, bool adjoint)
@@ -513,6 +506,9 @@ EventStep event_step(const tm_plan* p, bool adjoint, int64_t t)
     return EventStep{(uint32_t)row, (uint32_t)(o - a + row)};
 }
 
+// One forward step t (set cur -> 1-cur): H and E updates, the step's
+// sources and receivers and the snapshot epilogue (se/sc non-null) in one
+// kernel.
 template <int P>
 void fwd_step(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap, char* se, char* sc,
               hipStream_t st)
@@ -771,8 +767,8 @@ tm_status run_forward(tm_plan* p, void* ws, const float* f, float* r, int64_t t0
     const bool host = snap != SNAP_NONE && p->storage == TM_STORE_HOST;
     if (host && (v = host_setup(p)) != TM_OK) return v;
     auto at = [&](int64_t t, char*& se, char*& sc) {
-        se = q.snapE + dev_slot(p, t) * p->lay.snap_step;
-        sc = q.snapC + dev_slot(p, t) * p->lay.snap_step;
+        se = q.snapE + dev_slot(p, t) * p->lay.snap_stride;
+        sc = q.snapC + dev_slot(p, t) * p->lay.snap_stride;
     };
     return forward_range<P>(p, q, &p->fwd_cur, f, r, t0, t1, snap, at, store && !full, host, st);
 }
@@ -812,7 +808,7 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             const bool use = want_grad && t % p->R == 0;
             const int64_t slot = use ? dev_slot(p, t) : 0;
             if (use && host && (v = slot_acquire(p, (int)slot, st)) != TM_OK) return v;
-            const uint64_t so = (uint64_t)slot * p->lay.snap_step;
+            const uint64_t so = (uint64_t)slot * p->lay.snap_stride;
             if ((v = events(t)) != TM_OK) return v;
             adj_step<P>(p, q, t, k, use ? snap : SNAP_NONE, use ? q.snapE + so : nullptr,
                         use ? q.snapC + so : nullptr, gca, gcb, st);
@@ -835,15 +831,15 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             }
             int cur = 0;
             auto at = [&](int64_t t, char*& se, char*& sc) {
-                se = q.snapE + (t - ta) * p->lay.snap_step;
-                sc = q.snapC + (t - ta) * p->lay.snap_step;
+                se = q.snapE + (t - ta) * p->lay.snap_stride;
+                sc = q.snapC + (t - ta) * p->lay.snap_stride;
             };
             v = forward_range<P>(p, q, &cur, f, nullptr, ta, tb, snap, at, false, false, st);
             if (v != TM_OK) return v;
             for (int64_t t = tb - 1; t >= ta; --t, ++k) {
                 if ((v = events(t)) != TM_OK) return v;
-                adj_step<P>(p, q, t, k, snap, q.snapE + (t - ta) * p->lay.snap_step,
-                            q.snapC + (t - ta) * p->lay.snap_step, gca, gcb, st);
+                adj_step<P>(p, q, t, k, snap, q.snapE + (t - ta) * p->lay.snap_stride,
+                            q.snapC + (t - ta) * p->lay.snap_stride, gca, gcb, st);
             }
         }
     }

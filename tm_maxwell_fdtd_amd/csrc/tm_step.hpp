@@ -144,6 +144,10 @@ struct RBuf {
     __device__ __forceinline__ RBuf(const void* p, uint32_t bytes)
         : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000))
     {
+        // one opaque value: the compiler keeps the descriptor in its own
+        // aligned register quad instead of sharing equal words between
+        // descriptors and copying them together before every access
+        asm volatile("" : "+s"(r));
     }
     // byte offset `off` (per lane) within the sub-array at byte `base` (uniform)
     __device__ __forceinline__ float ld(bool ok, uint32_t off, uint32_t base) const
@@ -175,6 +179,14 @@ struct RBuf {
     {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, (int)soff, 0);
     }
+    __device__ __forceinline__ float ldv_bf16(int voff, uint32_t soff) const
+    {
+        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff, (int)soff, 0));
+    }
+    __device__ __forceinline__ float ldv_fp8(int voff, uint32_t soff) const
+    {
+        return e4m3_to_f32(__builtin_amdgcn_raw_buffer_load_b8(r, voff, (int)soff, 0));
+    }
     __device__ __forceinline__ float ld_fp8(bool ok, uint32_t off) const
     {
         return e4m3_to_f32(__builtin_amdgcn_raw_buffer_load_b8(r, ok ? (int)off : OOB, 0, 0));
@@ -202,6 +214,16 @@ __device__ __forceinline__ float snap_get(const RBuf& b, bool ok, uint32_t w)
     if constexpr (SNAP == SNAP_F32) return b.ld(ok, w * 4u, 0u);
     else if constexpr (SNAP == SNAP_BF16) return b.ld_bf16(ok, w * 2u);
     else if constexpr (SNAP == SNAP_FP8) return b.ld_fp8(ok, w);
+    else return 0.0f;
+}
+// Load with a precomputed lane offset (bytes, out of range where masked) and
+// a uniform row offset.
+template <int SNAP>
+__device__ __forceinline__ float snap_getv(const RBuf& b, int voff, uint32_t soff)
+{
+    if constexpr (SNAP == SNAP_F32) return b.ldv(voff, soff);
+    else if constexpr (SNAP == SNAP_BF16) return b.ldv_bf16(voff, soff);
+    else if constexpr (SNAP == SNAP_FP8) return b.ldv_fp8(voff, soff);
     else return 0.0f;
 }
 // Store with a precomputed lane offset (bytes, out of range where masked)
@@ -565,6 +587,7 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf bm(a.m.base, a.m.bytes);
+    constexpr uint32_t ESZ = snap_bytes<SNAP>();
     const uint32_t ssb = SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u;
     const RBuf bse(a.snap_e + (int64_t)s * a.snap_shot_bytes, ssb);
     const RBuf bsc(a.snap_c + (int64_t)s * a.snap_shot_bytes, ssb);
@@ -573,6 +596,22 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
     const RBuf bev(a.ev.base, a.ev.bytes);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
+    const uint32_t rowb = (uint32_t)nx * 4u, brow = (uint32_t)g.bx * 4u;
+
+    // Addressing: the lane part of an offset is loop-invariant and already
+    // out of range where the lane never touches that array; a row's
+    // conditions OR in a uniform mask (0, or out of range); the row part is
+    // a uniform offset of the row clamped into the array, so that a masked
+    // offset plus the row offset never wraps back into range.
+    const int v_e = lane_off(e_col, c4), v_own = lane_off(own, c4);
+    const int v_hz = lane_off(hz_col, c4), v_ownhz = lane_off(own && hz_col, c4);
+    const int v_xe = lane_off(fx_e, bx4), v_ownxe = lane_off(own && fx_e, bx4);
+    const int v_hzxh = lane_off(hz_col && fx_h, bx4), v_ownhzxh = lane_off(own && hz_col && fx_h, bx4);
+    const int v_g = lane_off(grad, c4), v_gs = lane_off(grad, (uint32_t)(c - g.x0) * ESZ);
+    auto msk = [](bool ok) { return ok ? 0 : RBuf::OOB; };
+    auto grow = [&](int y) { return (uint32_t)min(max(y, 0), ny - 1); };                // grid row
+    auto brw = [&](int y) { return (uint32_t)min(max(band_y(g, y), 0), g.by - 1); };    // y-band row
+    auto srw = [&](int y) { return (uint32_t)min(max(y - g.y0, 0), g.nyi - 1) * (uint32_t)g.nxi * ESZ; };
     // slot of window row r, or -1 (uniform)
     auto slot_of = [&](int r) {
         return (r >= e_lo && r <= e_hi) ? __builtin_amdgcn_readfirstlane(evs[r - ya + T0]) : -1;
@@ -584,30 +623,29 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     int fG[D];
     auto issue = [&](int u, int r, bool live) {
         const int h = r - P, y = r - 2 * P + 1;
-        const uint32_t orr = (uint32_t)(r * nx) * 4u + c4, oh = (uint32_t)(h * nx) * 4u + c4;
-        const bool e_do = live && e_col && e_row(r);
+        const int me = msk(live && e_row(r));
+        const uint32_t orr = grow(r) * rowb, oh = grow(h) * rowb;
         const int gs = slot_of(r);
         fG[u] = gs;
         fEv[u] = 0.0f;
-        if (gs >= 0) fEv[u] = bev.ld(e_do, (uint32_t)(gs * nx) * 4u + c4, a.es.add);   // uniform
-        fE[u] = b0.ld(e_do, orr, L.oE);
-        fCb[u] = bm.ld(e_do, orr, a.m.oCb);
-        fMxe[u] = b0.ld(e_do && fx_e, (uint32_t)(r * g.bx) * 4u + bx4, L.oMxe);
-        fMye[u] = b0.ld(e_do && fy_e(r), (uint32_t)(band_y(g, r) * nx) * 4u + c4, L.oMye);
-        const bool g_do = live && grad && r >= ya && r < yb && r >= g.y0 && r < g.y1;
-        const uint32_t wi = (uint32_t)((r - g.y0) * g.nxi + (c - g.x0));
-        fSe[u] = snap_get<SNAP>(bse, g_do, wi);
-        fSc[u] = snap_get<SNAP>(bsc, g_do, wi);
-        fGa[u] = bga.ld(g_do, orr, 0u);
-        fGb[u] = bgb.ld(g_do, orr, 0u);
-        const bool hx_do = live && own && hx_row(h);
-        fHx[u] = b0.ld(hx_do, oh, L.oHx);
-        fMyh[u] = b0.ld(hx_do && fy_h(h), (uint32_t)(band_y(g, h) * nx) * 4u + c4, L.oMyh);
-        fQ[u] = bm.ld(live && e_col && (hx_row(h) || h_own(h)), oh, a.m.oCq);
-        const bool hz_do = live && hz_col && hz_row(h);
-        fHz[u] = b0.ld(hz_do, oh, L.oHz);
-        fMxh[u] = b0.ld(hz_do && fx_h, (uint32_t)(h * g.bx) * 4u + bx4, L.oMxh);
-        fCa[u] = bm.ld(live && own && y >= ya && y < yb, (uint32_t)(y * nx) * 4u + c4, a.m.oCa);
+        if (gs >= 0) fEv[u] = bev.ldv(v_e | me, (uint32_t)gs * rowb + a.es.add);   // uniform
+        fE[u] = b0.ldv(v_e | me, L.oE + orr);
+        fCb[u] = bm.ldv(v_e | me, a.m.oCb + orr);
+        fMxe[u] = b0.ldv(v_xe | me, L.oMxe + grow(r) * brow);
+        fMye[u] = b0.ldv(v_e | me | msk(fy_e(r)), L.oMye + brw(r) * rowb);
+        const int mg = msk(live && r >= ya && r < yb && r >= g.y0 && r < g.y1);
+        fSe[u] = snap_getv<SNAP>(bse, v_gs | mg, srw(r));
+        fSc[u] = snap_getv<SNAP>(bsc, v_gs | mg, srw(r));
+        fGa[u] = bga.ldv(v_g | mg, orr);
+        fGb[u] = bgb.ldv(v_g | mg, orr);
+        const int mh = msk(live && hx_row(h));
+        fHx[u] = b0.ldv(v_own | mh, L.oHx + oh);
+        fMyh[u] = b0.ldv(v_own | mh | msk(fy_h(h)), L.oMyh + brw(h) * rowb);
+        fQ[u] = bm.ldv(v_e | msk(live && (hx_row(h) || h_own(h))), a.m.oCq + oh);
+        const int mz = msk(live && hz_row(h));
+        fHz[u] = b0.ldv(v_hz | mz, L.oHz + oh);
+        fMxh[u] = b0.ldv(v_hzxh | mz, L.oMxh + grow(h) * brow);
+        fCa[u] = bm.ldv(v_own | msk(live && y >= ya && y < yb), a.m.oCa + grow(y) * rowb);
     };
 
     float ed[2 * P];      // lambda_E^{n+1} rows r-2P+1 .. r
@@ -625,28 +663,27 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     auto inject = [&](int r, int gs, float ev, float e) {
         if (gs >= 0) {                                  // uniform
             e = e + ev;
-            bev.st(own && r >= ya && r < yb, e, (uint32_t)(gs * nx) * 4u + c4, a.es.out);
+            bev.stv(e, v_own | msk(r >= ya && r < yb), (uint32_t)gs * rowb + a.es.out);
         }
         return e;
     };
     // u, w of the E-set cell (r, c) for input row r (0 off the E-set); the
     // filter memories are written back on owned cells.
     auto front = [&](int r, float e, float cbv, float mx, float my, float& u, float& w) {
-        const bool r_own = own && r >= ya && r < yb;
+        const int ms = msk(r >= ya && r < yb && e_row(r));    // owned E-set rows
         const float hv = cbv * e;
-        const bool st_m = r_own && e_col && e_row(r);
         u = hv;
         if (xband) {
             float m = mx;
             u = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, hv);
-            b1.st(st_m && fx_e, m, (uint32_t)(r * g.bx) * 4u + bx4, L.oMxe);
+            b1.stv(m, v_ownxe | ms, L.oMxe + grow(r) * brow);
         }
         w = hv;
         if (fy_e(r)) {
             const float* ct = cyt[r - ya + T0];
             float m = my;
             w = cpml_step(m, ct[3], ct[4], ct[5], hv);
-            b1.st(st_m, m, (uint32_t)(band_y(g, r) * nx) * 4u + c4, L.oMye);
+            b1.stv(m, v_own | ms, L.oMye + brw(r) * rowb);
         }
     };
     auto push = [&](float e, float u, float w) {
@@ -662,13 +699,14 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     // prologue: rows ya-2P+1 .. ya-1 (front only, no gradient)
     for (int i = 1; i < 2 * P; ++i) {
         const int r = ya - 2 * P + i;
-        const bool e_do = e_col && e_row(r);
-        const uint32_t orr = (uint32_t)(r * nx) * 4u + c4;
+        const int me = msk(e_row(r));
+        const uint32_t orr = grow(r) * rowb;
         const int gs = slot_of(r);
-        const float ev = bev.ld(e_do && gs >= 0, (uint32_t)(gs * nx) * 4u + c4, a.es.add);
-        const float e0 = inject(r, gs, ev, b0.ld(e_do, orr, L.oE)), cbv = bm.ld(e_do, orr, a.m.oCb);
-        const float mx = b0.ld(e_do && fx_e, (uint32_t)(r * g.bx) * 4u + bx4, L.oMxe);
-        const float my = b0.ld(e_do && fy_e(r), (uint32_t)(band_y(g, r) * nx) * 4u + c4, L.oMye);
+        float ev = 0.0f;
+        if (gs >= 0) ev = bev.ldv(v_e | me, (uint32_t)gs * rowb + a.es.add);   // uniform
+        const float e0 = inject(r, gs, ev, b0.ldv(v_e | me, L.oE + orr)), cbv = bm.ldv(v_e | me, a.m.oCb + orr);
+        const float mx = b0.ldv(v_xe | me, L.oMxe + grow(r) * brow);
+        const float my = b0.ldv(v_e | me | msk(fy_e(r)), L.oMye + brw(r) * rowb);
         float u, w;
         front(r, e0, cbv, mx, my, u, w);
         push(e0, u, w);
@@ -689,16 +727,15 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
                 front(r, e, fCb[u], fMxe[u], fMye[u], uv, wv);
                 if constexpr (SNAP != SNAP_NONE) {
                     if (r < yb && r >= g.y0 && r < g.y1) {  // uniform
-                        const uint32_t orr = (uint32_t)(r * nx) * 4u + c4;
-                        bga.st(grad, fmaf(e, fSe[u] * a.ratio, fGa[u]), orr, 0u);
-                        bgb.st(grad, fmaf(e, fSc[u] * a.ratio, fGb[u]), orr, 0u);
+                        const uint32_t orr = (uint32_t)r * rowb;
+                        bga.stv(fmaf(e, fSe[u] * a.ratio, fGa[u]), v_g, orr);
+                        bgb.stv(fmaf(e, fSc[u] * a.ratio, fGb[u]), v_g, orr);
                     }
                 }
                 push(e, uv, wv);
             }
             const int h = r - P;
             const int y = r - 2 * P + 1;
-            const uint32_t oh = (uint32_t)(h * nx) * 4u + c4;
             const float q = fQ[u];
 
             // --- lambda_Hx(h, c) and its filtered Cq product, own columns
@@ -707,13 +744,14 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
                 const float acc = stencil<P>([&](int k) { return ww[P - 1 + k]; },
                                              [&](int k) { return ww[P - k]; });
                 const float lhx = fmaf(g.rdy, acc, fHx[u]);
-                b1.st(do_h && h_own(h), lhx, oh, L.oHx);
+                const int mho = msk(hx_row(h) && h_own(h));
+                b1.stv(lhx, v_own | mho, L.oHx + grow(h) * rowb);
                 float txv = q * lhx;
                 if (fy_h(h)) {                          // uniform
                     const float* ct = cyt[h - ya + T0];
                     float m = fMyh[u];
                     txv = cpml_step(m, ct[0], ct[1], ct[2], txv);
-                    b1.st(do_h && h_own(h), m, (uint32_t)(band_y(g, h) * nx) * 4u + c4, L.oMyh);
+                    b1.stv(m, v_own | mho, L.oMyh + brw(h) * rowb);
                 }
 #pragma unroll
                 for (int i = 0; i < 2 * P - 1; ++i) tw[i] = tw[i + 1];
@@ -727,12 +765,12 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
                 const float acc = stencil<P>([&](int k) { return rowU[th + k]; },
                                              [&](int k) { return rowU[th - k + 1]; });
                 const float lhz = fmaf(-g.rdx, acc, fHz[u]);
-                b1.st(own && hz_col, lhz, oh, L.oHz);
+                b1.stv(lhz, v_ownhz, L.oHz + (uint32_t)h * rowb);
                 float tz = q * lhz;
                 if (xband) {
                     float m = fMxh[u];
                     tz = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, tz);
-                    b1.st(own && hz_col && fx_h, m, (uint32_t)(h * g.bx) * 4u + bx4, L.oMxh);
+                    b1.stv(m, v_ownhzxh, L.oMxh + (uint32_t)h * brow);
                 }
                 ring[h % P][tid] = hz_col ? tz : 0.0f;
             }
@@ -745,8 +783,7 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
                                             [&](int k) { return tzr[te - k]; });
                 const float ay = stencil<P>([&](int k) { return tw[P - 1 + k]; },
                                             [&](int k) { return tw[P - k]; });
-                b1.st(own, fmaf(fCa[u], ed[0], fmaf(-az, g.rdx, ay * g.rdy)),
-                      (uint32_t)(y * nx) * 4u + c4, L.oE);
+                b1.stv(fmaf(fCa[u], ed[0], fmaf(-az, g.rdx, ay * g.rdy)), v_own, L.oE + (uint32_t)y * rowb);
             }
             issue(u, r + D, r + D <= r_end);
         }
