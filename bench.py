@@ -86,9 +86,9 @@ def kernel_bytes(name, wl, store, snap_bytes):
     same 16 B per band cell and axis for the four adjoint memories, and on
     interior cells the two snapshot reads plus the read-modify-write of the
     two per-shot gradients (16 B).
-    k_fwd_step2 advances two time steps per launch: twice the bytes of
-    k_fwd_step (the per-cell-update figure times the cell-updates of the
-    launch), although the state crosses HBM only once.
+    k_fwd_step2 / k_adj_step2 advance two time steps per launch: twice the
+    bytes of k_fwd_step / k_adj_step (the per-cell-update figure times the
+    cell-updates of the launch), although the state crosses HBM only once.
     """
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
@@ -100,6 +100,8 @@ def kernel_bytes(name, wl, store, snap_bytes):
     if name == "k_adj_step":
         grads = (2 * snap_bytes + 16) * interior if store else 0
         return S * (36 * cells + 16 * (band_y + band_x) + grads)
+    if name == "k_adj_step2":
+        return 2 * kernel_bytes("k_adj_step", wl, store, snap_bytes)
     return None
 
 
@@ -171,6 +173,8 @@ def main():
     ap.add_argument("--nt", type=int, default=0,
                     help="override the number of time steps (profiling runs only; "
                          "the bench line then names the reduced workload)")
+    ap.add_argument("--time-block", type=int, default=0, choices=(0, 1, 2),
+                    help="time steps per launch of the forward and the adjoint (0: the default, 2)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for calibrating HBM byte counters)")
@@ -207,7 +211,7 @@ def main():
     log(f"building workload config{args.config}")
     over = {"nt": args.nt} if args.nt > 0 else {}
     wl = inputs.as_f32(inputs.make_config(args.config, **over))
-    prop = native.Propagator(wl, device=dev)
+    prop = native.Propagator(wl, device=dev, time_block=args.time_block)
     log(f"workspace {prop.ws_bytes / 2**30:.1f} GiB, grid {wl.ny}x{wl.nx}, S={wl.n_shots}, nt={wl.nt}")
     S, ny, nx = wl.n_shots, wl.ny, wl.nx
     f32 = dict(dtype=torch.float32, device=dev)
@@ -287,7 +291,7 @@ def main():
         if n == 0:
             continue
         avg_ms = ms / n
-        launches = wl.nt // 2 if name == "k_fwd_step2" else wl.nt
+        launches = wl.nt // 2 if name in ("k_fwd_step2", "k_adj_step2") else wl.nt
         if name.startswith("k_fwd") and wl.ckpt_every:
             launches *= 2
         # in a full step the forward stores snapshots and the adjoint accumulates gradients

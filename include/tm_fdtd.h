@@ -91,8 +91,10 @@ typedef struct tm_desc {
     int64_t ckpt_every;     /* 0: store every step; K > 0: checkpoint the state
                                every K steps and replay segments in tm_adjoint  */
     uint64_t hbm_budget;    /* bytes the workspace may use; 0 = unlimited       */
-    int32_t time_block;     /* forward time steps per launch: 1, or 2 (two steps
-                               in one pass over the state); 0 = default (2).
+    int32_t time_block;     /* time steps per launch of the forward and of the
+                               adjoint: 1, or 2 (two steps in one pass over the
+                               state; the adjoint pairs steps only with the
+                               snapshots in device memory); 0 = default (2).
                                Both give bitwise the same results.             */
     int32_t storage;        /* tm_storage: where a storing forward keeps the
                                snapshots (full-store mode only)                */

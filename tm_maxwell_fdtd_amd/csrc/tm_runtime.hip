@@ -36,6 +36,7 @@
 #include "tm_kernels.hpp"
 #include "tm_step.hpp"
 #include "tm_step2.hpp"
+#include "tm_adj2.hpp"
 
 using namespace tmf;
 
@@ -137,8 +138,8 @@ struct Layout {
 constexpr int HOST_RING = 3;
 
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
-enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_COUNT };
-const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2"};
+enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_COUNT };
+const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2"};
 
 struct TimedLaunch {
     int kid;
@@ -150,8 +151,8 @@ struct tm_plan {
     int P = 0;
     Geo g{};
     Tiling tiling_fwd{}, tiling_adj{};   // per device, made at the first device call
-    Tiling tiling_fwd2{};
-    int time_block = 2;                  // forward time steps per launch (1 or 2)
+    Tiling tiling_fwd2{}, tiling_adj2{};
+    int time_block = 2;                  // time steps per launch of the forward and the adjoint (1 or 2)
     int tiling_device = -1;
     std::vector<float> cpml;             // [12][L]
     std::vector<int32_t> tables;         // event-row tables, packed
@@ -571,7 +572,7 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap
 
 // One adjoint step t (residual injection at the receivers, transposed H and
 // E updates, source-wavelet gradient and parameter-gradient accumulation in
-// one kernel); k counts the adjoint steps taken (set k%2 -> (k+1)%2).
+// one kernel); k counts the adjoint launches (set k%2 -> (k+1)%2).
 template <int P>
 void adj_step(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const char* se,
               const char* sc, float* gca, float* gcb, hipStream_t st)
@@ -599,6 +600,41 @@ void adj_step(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const c
         else if (snap == SNAP_BF16) k_adj_step<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
         else if (snap == SNAP_FP8) k_adj_step<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
         else k_adj_step<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
+    });
+}
+
+// Adjoint steps t and t-1 in one launch (set k%2 -> (k+1)%2, k counting
+// launches); seA/scA, seB/scB: the snapshots of steps t and t-1, or null.
+template <int P>
+void adj_step2(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const char* seA, const char* scA,
+               const char* seB, const char* scB, float* gca, float* gcb, hipStream_t st)
+{
+    const Layout& L = p->lay;
+    Adj2Args a;
+    a.g = p->g;
+    a.t = p->tiling_adj2;
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.aset[k & 1];
+    a.set1 = q.base + L.aset[(k + 1) & 1];
+    a.snap_eA = seA;
+    a.snap_cA = scA;
+    a.snap_eB = seB;
+    a.snap_cB = scB;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
+    a.gca = gca;
+    a.gcb = gcb;
+    a.ratio = (float)p->R;
+    a.ev = event_rows(p, q, true);
+    a.esA = event_step(p, true, t);
+    a.esB = event_step(p, true, t - 1);
+    const dim3 grid((unsigned)p->tiling_adj2.nblk), blk(NT);
+    timed(p, KID_ADJ_STEP2, t - 1, st, [&] {             // sampled like the forward pairs (even step)
+        if (snap == SNAP_F32) k_adj_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_BF16) k_adj_step2<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
+        else if (snap == SNAP_FP8) k_adj_step2<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
+        else k_adj_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
     });
 }
 
@@ -654,10 +690,14 @@ tm_status device_tiling(tm_plan* p)
     if (v != TM_OK) return v;
     v = resident(pick(&k_fwd_step2<P, SNAP_F32>, &k_fwd_step2<P, SNAP_BF16>, &k_fwd_step2<P, SNAP_FP8>), &c2);
     if (v != TM_OK) return v;
+    int64_t ca2 = 0;
+    v = resident(pick(&k_adj_step2<P, SNAP_F32>, &k_adj_step2<P, SNAP_BF16>, &k_adj_step2<P, SNAP_FP8>), &ca2);
+    if (v != TM_OK) return v;
     // halo_iters: row iterations of a chunk beyond its owned rows
     p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W, CH_MAX, ncu, 2 * P - 1);
     p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W, CH_MAX, ncu, 4 * P - 3);
     p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W, CH2_MAX, ncu, 6 * P - 3);
+    p->tiling_adj2 = make_tiling(p->d, P, ca2, Strip2<P>::W, CHA2_MAX, ncu, 8 * P - 3);
     p->tiling_device = dev;
     return TM_OK;
 }
@@ -804,12 +844,22 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             for (int64_t j = j_last; j >= 0 && j > j_last - HOST_RING; --j)
                 if ((v = slot_copy(p, q, (int)(j % HOST_RING), j, false)) != TM_OK) return v;
         }
-        for (int64_t t = nt - 1; t >= 0; --t, ++k) {
+        for (int64_t t = nt - 1; t >= 0; ++k) {
+            if ((v = events(t)) != TM_OK) return v;
+            if (p->time_block == 2 && !host && t >= 1 && t - 1 >= ev_a) {   // steps t, t-1 in one launch
+                const bool uA = want_grad && t % p->R == 0, uB = want_grad && (t - 1) % p->R == 0;
+                const uint64_t oA = (uint64_t)(uA ? dev_slot(p, t) : 0) * p->lay.snap_stride;
+                const uint64_t oB = (uint64_t)(uB ? dev_slot(p, t - 1) : 0) * p->lay.snap_stride;
+                adj_step2<P>(p, q, t, k, (uA || uB) ? snap : SNAP_NONE, uA ? q.snapE + oA : nullptr,
+                             uA ? q.snapC + oA : nullptr, uB ? q.snapE + oB : nullptr, uB ? q.snapC + oB : nullptr,
+                             gca, gcb, st);
+                t -= 2;
+                continue;
+            }
             const bool use = want_grad && t % p->R == 0;
             const int64_t slot = use ? dev_slot(p, t) : 0;
             if (use && host && (v = slot_acquire(p, (int)slot, st)) != TM_OK) return v;
             const uint64_t so = (uint64_t)slot * p->lay.snap_stride;
-            if ((v = events(t)) != TM_OK) return v;
             adj_step<P>(p, q, t, k, use ? snap : SNAP_NONE, use ? q.snapE + so : nullptr,
                         use ? q.snapC + so : nullptr, gca, gcb, st);
             if (use && host) {
@@ -817,6 +867,7 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
                 const int64_t jn = t / p->R - HOST_RING;   // the stored step that reuses this slot
                 if (jn >= 0 && (v = slot_copy(p, q, (int)slot, jn, false)) != TM_OK) return v;
             }
+            --t;
         }
     } else {
         for (int64_t seg = p->n_seg - 1; seg >= 0; --seg) {
@@ -836,10 +887,18 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             };
             v = forward_range<P>(p, q, &cur, f, nullptr, ta, tb, snap, at, false, false, st);
             if (v != TM_OK) return v;
-            for (int64_t t = tb - 1; t >= ta; --t, ++k) {
+            for (int64_t t = tb - 1; t >= ta; ++k) {
                 if ((v = events(t)) != TM_OK) return v;
-                adj_step<P>(p, q, t, k, snap, q.snapE + (t - ta) * p->lay.snap_stride,
-                            q.snapC + (t - ta) * p->lay.snap_stride, gca, gcb, st);
+                const char* se = q.snapE + (t - ta) * p->lay.snap_stride;
+                const char* sc = q.snapC + (t - ta) * p->lay.snap_stride;
+                if (p->time_block == 2 && t - 1 >= ta && t - 1 >= ev_a) {
+                    adj_step2<P>(p, q, t, k, snap, se, sc, se - p->lay.snap_stride, sc - p->lay.snap_stride, gca,
+                                 gcb, st);
+                    t -= 2;
+                } else {
+                    adj_step<P>(p, q, t, k, snap, se, sc, gca, gcb, st);
+                    --t;
+                }
             }
         }
     }
@@ -981,6 +1040,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     }
     p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024, NT - 4 * P + 2);
     p->tiling_fwd2 = make_tiling(d, P, 1024, NT - 8 * P + 4, CH2_MAX);
+    p->tiling_adj2 = make_tiling(d, P, 1024, NT - 8 * P + 4, CHA2_MAX);
     if (!make_layout(p)) {
         delete p;
         return TM_EINVAL;
