@@ -398,3 +398,16 @@ def test_step_ratio(orc, ratio, storage):
           f"(subsampled vs full gradient in the oracle: {rel_l2(ref['gca'], full['gca']):.2e})", flush=True)
     assert e_r <= REC_TOL
     assert e_a <= GRAD_TOL["f32"] and e_b <= GRAD_TOL["f32"]
+
+
+@pytest.mark.parametrize("ratio,storage", [(2, 0), (3, 0), (3, 1)])
+def test_step_ratio_two_step_launch_bitwise(ratio, storage):
+    """With a snapshot step ratio a pair of adjoint steps may hold one stored
+    step or none; two steps per launch still give bitwise the results of one
+    step per launch (host storage runs the adjoint one step per launch)."""
+    wl = inputs.as_f32(inputs.random_workload(8, 40, 8, nt=37, n_shots=2, n_src=2, n_rec=5, seed=770 + ratio,
+                                              src_anywhere=True))
+    one = run_gpu(wl, snap="bf16", storage=storage, step_ratio=ratio, time_block=1)
+    two = run_gpu(wl, snap="bf16", storage=storage, step_ratio=ratio, time_block=2)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} R={ratio} storage {storage}")
