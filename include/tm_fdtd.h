@@ -81,7 +81,7 @@ typedef enum tm_storage {
 typedef struct tm_desc {
     int32_t order;          /* spatial order: 2, 4 or 8                         */
     int32_t snap;           /* tm_snap                                          */
-    int64_t n_shots;        /* shots S sharing one model                        */
+    int64_t n_shots;        /* shots S (sharing one model unless model_per_shot) */
     int64_t ny, nx;         /* padded grid; ny * nx < 2^29                      */
     int64_t pml_y0, pml_y1; /* interior window rows [pml_y0, pml_y1)            */
     int64_t pml_x0, pml_x1; /* interior window columns [pml_x0, pml_x1)         */
@@ -102,6 +102,11 @@ typedef struct tm_desc {
                                step_ratio-th step only, weighting each term by
                                step_ratio (an approximation); 0 or 1 = every
                                step.  Full-store mode only.                     */
+    int32_t model_per_shot; /* 0: one model for all shots, the coefficient
+                               arrays are [ny][nx]; 1: one model per shot
+                               (batched models), [S][ny][nx], and each shot's
+                               gradient belongs to its own model              */
+    int32_t reserved;       /* 0                                                */
 } tm_desc;
 
 typedef struct tm_plan tm_plan;
@@ -131,9 +136,10 @@ tm_status tm_workspace_bytes(const tm_plan* plan, uint64_t* bytes);
 
 /*
  * Courant number sqrt(max(Cb*Cq)) * sum|c_k| * sqrt(1/dx^2 + 1/dy^2) of a
- * model; the scheme is stable when it is at most 1.  cb, cq: device
- * float32 [ny][nx].  Uses the workspace's scratch area and synchronises
- * ``stream``.
+ * model (the largest over the shots' models with model_per_shot); the
+ * scheme is stable when it is at most 1.  cb, cq: device float32 [ny][nx]
+ * ([S][ny][nx] with model_per_shot).  Uses the workspace's scratch area and
+ * synchronises ``stream``.
  */
 tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb,
                      const float* cq, void* stream, double* courant);
@@ -142,7 +148,8 @@ tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb
  * Forward propagation of all shots over steps [t0, t1), 0 <= t0 < t1 <= nt.
  * t0 == 0 starts from zero fields; t0 > 0 continues the state a previous
  * call on the same workspace left at step t0 (else TM_ESTATE).
- *   ca, cb, cq: device float32 [ny][nx] update coefficients.
+ *   ca, cb, cq: device float32 [ny][nx] update coefficients ([S][ny][nx],
+ *      shot s's model at s, with model_per_shot).
  *   f: device float32 [nt][S][n_src] source amplitudes, added to Ey after
  *      the E update of step n (required when n_src > 0).
  *   r: device float32 [nt][S][n_rec]; rows t0..t1-1 receive Ey at the
@@ -178,7 +185,8 @@ tm_status tm_adjoint(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca
  * Shot sum of the per-shot gradients (combine_grad): grad[j] = sum_s
  * grad_shot[s][j], shots summed in ascending order (deterministic).
  * grad_ca/grad_cb: device float32 [ny][nx], overwritten.  A NULL pair
- * member is skipped.
+ * member is skipped.  (With model_per_shot each shot's gradient belongs to
+ * its own model and is used as it is; the sum is still computed if asked.)
  */
 tm_status tm_grad(const tm_plan* plan, const float* grad_ca_shot, const float* grad_cb_shot,
                   float* grad_ca, float* grad_cb, void* stream);

@@ -79,7 +79,8 @@ def test_valid_plan_and_workspace_size(wl):
 @pytest.mark.parametrize("field,value", [
     ("order", 3), ("order", 6), ("order", 0), ("n_shots", 0), ("nt", 0), ("n_src", -1),
     ("snap", 3), ("snap", -1), ("ckpt_every", -1), ("ny", 5), ("dx", 0.0), ("dy", float("nan")),
-    ("time_block", 3), ("time_block", -1), ("storage", 2), ("step_ratio", -1),
+    ("time_block", 3), ("time_block", -1), ("storage", 2), ("step_ratio", -1), ("model_per_shot", 2),
+    ("model_per_shot", -1),
     ("pml_y0", 1), ("pml_x1", 10 ** 6), ("pml_y1", 20),
 ])
 def test_invalid_descriptor(wl, field, value):
@@ -187,3 +188,19 @@ def test_storage_options_exclude_checkpoints(wl):
     assert b_host < b_r < b_dev
     for p in (p_dev, p_host, p_r):
         native.tm_plan_destroy(p)
+
+
+def test_per_shot_models_workspace(wl):
+    """One model per shot keeps S model blocks [Ca | Cb | Cq] in the workspace."""
+    st, p1 = native.tm_plan_create(make(wl), wl.cpml, wl.src, wl.rec)
+    st2, pS = native.tm_plan_create(make(wl, model_per_shot=1), wl.cpml, wl.src, wl.rec)
+    assert st == st2 == native.TM_OK
+    b1, bS = native.tm_workspace_bytes(p1)[1], native.tm_workspace_bytes(pS)[1]
+    slab = -(-wl.ny * wl.nx * 4 // 256) * 256
+    assert bS - b1 == (wl.n_shots - 1) * 3 * slab
+    native.tm_plan_destroy(p1)
+    native.tm_plan_destroy(pS)
+    # the Python descriptor follows the shape of the coefficient arrays
+    per = inputs.per_shot_models(wl)
+    assert per.ca.shape == (wl.n_shots, wl.ny, wl.nx)
+    assert native.make_desc(per).model_per_shot == 1 and native.make_desc(wl).model_per_shot == 0

@@ -411,3 +411,83 @@ def test_step_ratio_two_step_launch_bitwise(ratio, storage):
     two = run_gpu(wl, snap="bf16", storage=storage, step_ratio=ratio, time_block=2)
     for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
         np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} R={ratio} storage {storage}")
+
+
+def _shot_workload(wl, s):
+    """Shot s of a workload with one model per shot, as a one-shot workload
+    with that shot's model (shots are independent)."""
+    import dataclasses
+
+    from gpu_util import sub_workload
+
+    return dataclasses.replace(sub_workload(wl, [s]), ca=wl.ca[s].copy(), cb=wl.cb[s].copy(), cq=wl.cq[s].copy())
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_per_shot_models(orc, order):
+    """One model per shot (batched models): every shot's records, per-shot
+    gradients and source gradient against the oracle run on that shot with
+    its own model; one and two steps per launch bitwise equal."""
+    base = inputs.random_workload(order, 40, 8, nt=60, n_shots=3, n_src=2, n_rec=6, seed=780 + order)
+    wl = inputs.as_f32(inputs.per_shot_models(base))
+    assert wl.ca.shape == (3, wl.ny, wl.nx)
+    refs = [orc.misfit_and_gradient(_shot_workload(wl, s)) for s in range(wl.n_shots)]
+    resid = np.concatenate([ref["residual"] for ref in refs], axis=1)
+    got = run_gpu(wl, snap="f32", grad_r=resid)
+    one = run_gpu(wl, snap="f32", grad_r=resid, time_block=1)
+    for s, ref in enumerate(refs):
+        e = {"records": rel_l2(got["records"][:, s], ref["records"][:, 0]),
+             "gca_shot": rel_l2(got["gca_shot"][s], ref["gca_shot"][0]),
+             "gcb_shot": rel_l2(got["gcb_shot"][s], ref["gcb_shot"][0]),
+             "grad_f": rel_l2(got["grad_f"][:, s], ref["grad_f"][:, 0])}
+        print(f"[per-shot models o{order} shot {s}] " + "  ".join(f"{k} {v:.2e}" for k, v in e.items()), flush=True)
+        assert e["records"] <= REC_TOL
+        assert max(e["gca_shot"], e["gcb_shot"], e["grad_f"]) <= GRAD_TOL["f32"]
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=f"{key}: two-step != one-step")
+
+
+def test_per_shot_models_identical_equal_shared_model():
+    """S identical per-shot models give bitwise the results of the shared model."""
+    import dataclasses
+
+    wl = inputs.as_f32(inputs.random_workload(8, 40, 8, nt=40, n_shots=3, n_src=2, n_rec=5, seed=790))
+    rep = dataclasses.replace(wl, ca=np.stack([wl.ca] * 3), cb=np.stack([wl.cb] * 3), cq=np.stack([wl.cq] * 3))
+    a, b = run_gpu(wl, snap="bf16"), run_gpu(rep, snap="bf16")
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(b[key], a[key], err_msg=key)
+
+
+def test_per_shot_models_eps_sigma_and_courant(orc):
+    """The chain rule to eps_r / sigma per shot at each shot's own model, and
+    the Courant check over all shots' models."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    base = inputs.random_workload(4, 30, 8, nt=20, n_shots=3, n_src=1, n_rec=3, seed=795, sig_range=(0.0, 0.04))
+    wl = inputs.as_f32(inputs.per_shot_models(base))
+    prop = native.Propagator(wl)
+    try:
+        rng = np.random.default_rng(5)
+        gca = torch.as_tensor(rng.standard_normal(wl.ca.shape).astype(np.float32), device=prop.device)
+        gcb = torch.as_tensor(rng.standard_normal(wl.ca.shape).astype(np.float32), device=prop.device)
+        geps, gsig = prop.grad_eps_sigma(gca, gcb)
+        c_all = prop.courant()
+        torch.cuda.synchronize()
+        got_e, got_s = geps.cpu().numpy(), gsig.cpu().numpy()
+        g_ca, g_cb = gca.cpu().numpy().astype(np.float64), gcb.cpu().numpy().astype(np.float64)
+    finally:
+        prop.close()
+    S = wl.n_shots
+    for s in range(S):
+        eps_s = base.eps_r * (1.0 + 0.25 * s / (S - 1))
+        ce, cs = orc.eps_sigma_grad(eps_s, base.sigma, wl.dt, g_ca[s], g_cb[s])
+        assert rel_l2(got_e[s], ce) <= 1e-5 and rel_l2(got_s[s], cs) <= 1e-5, s
+    # the fastest model is shot 0's (the smallest eps_r): its Courant number
+    shot0 = native.Propagator(_shot_workload(wl, 0))
+    try:
+        c0 = shot0.courant()
+    finally:
+        shot0.close()
+    assert c_all == pytest.approx(c0, rel=1e-6)

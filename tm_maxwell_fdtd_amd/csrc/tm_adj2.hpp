@@ -125,7 +125,7 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
 
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
-    const RBuf bm(a.m.base, a.m.bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
     const uint32_t sbA = (SNAP != SNAP_NONE && a.snap_eA != nullptr) ? a.snap_shot_bytes : 0u;
     const uint32_t sbB = (SNAP != SNAP_NONE && a.snap_eB != nullptr) ? a.snap_shot_bytes : 0u;
     const int64_t so_s = (int64_t)s * a.snap_shot_bytes;

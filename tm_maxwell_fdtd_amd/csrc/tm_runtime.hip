@@ -116,7 +116,8 @@ EventTables build_events(const int64_t* src, int64_t n_src, const int64_t* rec, 
 
 struct Layout {
     uint64_t cpml = 0, tables = 0, scratch = 0;
-    uint64_t model = 0, model_bytes = 0;          // [Ca | Cb | Cq]
+    uint64_t model = 0, model_bytes = 0;          // [Ca | Cb | Cq] of one model
+    uint64_t model_stride = 0;                    // bytes between the shots' models (0: shared)
     uint64_t slab_b = 0;                          // bytes of one [ny][nx] array, aligned
     StateLayout st{};                             // one shot's block (forward and adjoint alike)
     uint64_t set_bytes = 0;                       // S blocks
@@ -241,7 +242,8 @@ bool make_layout(tm_plan* p)
     L.tables = take(p->tables.size() * 4);
     L.scratch = take(4096);
     L.model_bytes = 3 * L.slab_b;
-    L.model = take(L.model_bytes);
+    L.model_stride = d.model_per_shot ? L.model_bytes : 0;
+    L.model = take(L.model_bytes * (d.model_per_shot ? S : 1));
     L.fwd = o;
     L.fset[0] = take(L.set_bytes);
     L.fset[1] = take(L.set_bytes);
@@ -390,9 +392,16 @@ tm_status stage_model(tm_plan* p, void* ws, const float* ca, const float* cb, co
 {
     const uint64_t n = (uint64_t)p->g.slab * 4;
     char* m = wsp<char>(ws, p->lay.model);
-    HIPCHK(hipMemcpyAsync(m, ca, n, hipMemcpyDeviceToDevice, st));
-    HIPCHK(hipMemcpyAsync(m + p->lay.slab_b, cb, n, hipMemcpyDeviceToDevice, st));
-    HIPCHK(hipMemcpyAsync(m + 2 * p->lay.slab_b, cq, n, hipMemcpyDeviceToDevice, st));
+    if (p->lay.model_stride == 0) {
+        HIPCHK(hipMemcpyAsync(m, ca, n, hipMemcpyDeviceToDevice, st));
+        HIPCHK(hipMemcpyAsync(m + p->lay.slab_b, cb, n, hipMemcpyDeviceToDevice, st));
+        HIPCHK(hipMemcpyAsync(m + 2 * p->lay.slab_b, cq, n, hipMemcpyDeviceToDevice, st));
+    } else {                        // [S][ny][nx] each -> S blocks [Ca | Cb | Cq]
+        const size_t S = (size_t)p->d.n_shots, pitch = (size_t)p->lay.model_stride;
+        HIPCHK(hipMemcpy2DAsync(m, pitch, ca, n, n, S, hipMemcpyDeviceToDevice, st));
+        HIPCHK(hipMemcpy2DAsync(m + p->lay.slab_b, pitch, cb, n, n, S, hipMemcpyDeviceToDevice, st));
+        HIPCHK(hipMemcpy2DAsync(m + 2 * p->lay.slab_b, pitch, cq, n, n, S, hipMemcpyDeviceToDevice, st));
+    }
     return TM_OK;
 }
 
@@ -414,7 +423,7 @@ Ptrs pointers(const tm_plan* p, void* ws)
     q.base = static_cast<char*>(ws);
     q.cp = wsp<float>(ws, L.cpml);
     q.model = Model{wsp<char>(ws, L.model), (uint32_t)L.model_bytes, 0u, (uint32_t)L.slab_b,
-                    (uint32_t)(2 * L.slab_b)};
+                    (uint32_t)(2 * L.slab_b), (int64_t)L.model_stride};
     const int32_t* t = wsp<int32_t>(ws, L.tables);
     q.row_slot = t + p->t_slot; q.colcell = t + p->t_colcell; q.slot_shot = t + p->t_sshot;
     q.cell_src = t + p->t_cs; q.src_list = t + p->t_sl; q.cell_rec = t + p->t_cr; q.rec_list = t + p->t_rl;
@@ -910,7 +919,8 @@ tm_status courant_impl(tm_plan* p, void* ws, const float* cb, const float* cq, h
 {
     const Ptrs q = pointers(p, ws);
     constexpr int NB = 256;
-    k_max_cbcq<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, p->g.slab, q.scratch);
+    const int64_t n = p->g.slab * (p->d.model_per_shot ? p->d.n_shots : 1);   // every shot's model
+    k_max_cbcq<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, n, q.scratch);
     HIPCHK(hipGetLastError());
     float part[NB];
     HIPCHK(hipMemcpyAsync(part, q.scratch, sizeof(part), hipMemcpyDeviceToHost, st));
@@ -959,6 +969,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     if (d.time_block < 0 || d.time_block > 2) return TM_EINVAL;
     if (d.storage != TM_STORE_DEVICE && d.storage != TM_STORE_HOST) return TM_EINVAL;
     if (d.step_ratio < 0) return TM_EINVAL;
+    if (d.model_per_shot != 0 && d.model_per_shot != 1) return TM_EINVAL;
     {
         const bool ckpt = d.ckpt_every > 0 && d.ckpt_every < d.nt;
         if (ckpt && (d.storage == TM_STORE_HOST || d.step_ratio > 1)) return TM_EINVAL;

@@ -244,11 +244,13 @@ struct StateLayout {
     uint32_t oMye, oMxe;             // E-update memories: y bands [by][nx], x bands [ny][bx]
 };
 
-// Model block [Ca | Cb | Cq], each [ny][nx].
+// Model block [Ca | Cb | Cq], each [ny][nx]; with one model per shot, shot
+// s's block starts shot_stride bytes after shot s-1's (0: one shared block).
 struct Model {
     const char* __restrict__ base;
     uint32_t bytes;
     uint32_t oCa, oCb, oCq;
+    int64_t shot_stride;
 };
 
 // Sources and receivers (tide-GPR 0.0.9, maxwell.cu: add_sources_ey and
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
 
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
-    const RBuf bm(a.m.base, a.m.bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
     const RBuf bse(a.snap_e + (int64_t)s * a.snap_shot_bytes, SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u);
     const RBuf bsc(a.snap_c + (int64_t)s * a.snap_shot_bytes, SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u);
     const RBuf bev(a.ev.base, a.ev.bytes);
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
 
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
-    const RBuf bm(a.m.base, a.m.bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
     constexpr uint32_t ESZ = snap_bytes<SNAP>();
     const uint32_t ssb = SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u;
     const RBuf bse(a.snap_e + (int64_t)s * a.snap_shot_bytes, ssb);

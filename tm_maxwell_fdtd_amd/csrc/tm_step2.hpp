@@ -143,7 +143,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
 
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
-    const RBuf bm(a.m.base, a.m.bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
     // a stage whose step is not stored gets null destinations: empty views
     const uint32_t sb0 = (SNAP != SNAP_NONE && a.snap_e0 != nullptr) ? a.snap_shot_bytes : 0u;
     const uint32_t sb1 = (SNAP != SNAP_NONE && a.snap_e1 != nullptr) ? a.snap_shot_bytes : 0u;

@@ -414,6 +414,18 @@ def random_workload(order, n_int, npml, nt, n_shots, n_src, n_rec, seed, h=0.01,
     return wl
 
 
+def per_shot_models(wl: Workload, spread: float = 0.25) -> Workload:
+    """The same problem with one model per shot (batched models): shot s's
+    permittivity is the workload's times 1 + spread * s / (S - 1), which only
+    slows the waves, so the workload's dt stays stable.  ``ca``, ``cb``,
+    ``cq`` become [S][ny][nx]; ``eps_r`` stays the shared base model."""
+    S = wl.n_shots
+    coefs = [update_coefficients(wl.eps_r * (1.0 + spread * s / max(S - 1, 1)), wl.sigma, wl.mu_r, wl.dt)
+             for s in range(S)]
+    ca, cb, cq = (np.stack([c[i] for c in coefs]) for i in range(3))
+    return dataclasses.replace(wl, name=wl.name + "-per-shot-models", ca=ca, cb=cb, cq=cq)
+
+
 def as_f32(wl: Workload) -> Workload:
     """A copy whose float arrays are rounded to float32 and widened back.
 

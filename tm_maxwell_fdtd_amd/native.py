@@ -51,6 +51,8 @@ class tm_desc(ctypes.Structure):
         ("time_block", ctypes.c_int32),
         ("storage", ctypes.c_int32),
         ("step_ratio", ctypes.c_int64),
+        ("model_per_shot", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -219,7 +221,8 @@ def tm_timing_read(plan):
 def make_desc(wl, snap: Optional[str] = None, ckpt_every: Optional[int] = None, hbm_budget: int = 0,
               time_block: int = 0, storage: int = 0, step_ratio: int = 0) -> tm_desc:
     snap = wl.snap if snap is None else snap
-    return tm_desc(order=wl.order, snap=SNAP_KINDS[snap],
+    per_shot = np.ndim(wl.ca) == 3        # [S][ny][nx]: one model per shot
+    return tm_desc(order=wl.order, snap=SNAP_KINDS[snap], model_per_shot=int(per_shot),
                    n_shots=wl.n_shots, ny=wl.ny, nx=wl.nx,
                    pml_y0=wl.pml_y0, pml_y1=wl.pml_y1, pml_x0=wl.pml_x0, pml_x1=wl.pml_x1,
                    dy=wl.dy, dx=wl.dx, nt=wl.nt, n_src=wl.n_src, n_rec=wl.n_rec,
@@ -317,15 +320,21 @@ class Propagator:
     def grad_eps_sigma(self, gca, gcb, dt=None):
         """dJ/deps_r, dJ/dsigma [ny][nx] from dJ/dCa, dJ/dCb [ny][nx] (either
         may be None) at this propagator's coefficients; ``dt`` defaults to the
-        workload's time step."""
+        workload's time step.  With one model per shot the inputs and outputs
+        are the per-shot [S][ny][nx] arrays, each shot at its own model."""
         import torch
 
         wl = self.wl
         dt = wl.dt if dt is None else dt
         f32 = dict(dtype=torch.float32, device=self.device)
-        geps = torch.empty((wl.ny, wl.nx), **f32)
-        gsig = torch.empty((wl.ny, wl.nx), **f32)
-        st = tm_grad_eps_sigma(self.plan, ptr(self.ca), ptr(self.cb), ptr(gca), ptr(gcb), float(dt),
-                               ptr(geps), ptr(gsig), stream_handle())
-        _check(st, "tm_grad_eps_sigma")
+        per_shot = self.desc.model_per_shot == 1
+        shape = (wl.n_shots, wl.ny, wl.nx) if per_shot else (wl.ny, wl.nx)
+        geps = torch.empty(shape, **f32)
+        gsig = torch.empty(shape, **f32)
+        pick = (lambda t, s: None if t is None else t[s]) if per_shot else (lambda t, s: t)
+        for s in range(wl.n_shots if per_shot else 1):
+            st = tm_grad_eps_sigma(self.plan, ptr(pick(self.ca, s)), ptr(pick(self.cb, s)), ptr(pick(gca, s)),
+                                   ptr(pick(gcb, s)), float(dt), ptr(pick(geps, s)), ptr(pick(gsig, s)),
+                                   stream_handle())
+            _check(st, "tm_grad_eps_sigma")
         return geps, gsig
