@@ -48,6 +48,8 @@
 namespace tmf {
 
 constexpr int CH2_MAX = 128;   // largest chunk height of the two-step kernel (LDS tables)
+constexpr int PREFETCH_F2 = 2; // rows of loads in flight ahead
+constexpr int UNROLL_F2 = 4;   // row-loop unroll, a multiple of PREFETCH_F2
 
 template <int P>
 struct Strip2 {
@@ -76,7 +78,8 @@ template <int P, int SNAP>
 __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
 {
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
-    constexpr int D = PREFETCH;
+    constexpr int D = PREFETCH_F2;
+    constexpr int U = UNROLL_F2;
     constexpr int R2 = 2 * P;                       // ring / FIFO depth (a power of two)
     constexpr uint32_t ESZ = snap_bytes<SNAP>();
     __shared__ float rowA[NT];                      // E^n row hA
@@ -166,9 +169,9 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
     const int r_end = yb + 4 * P - 3;
     // Unrolled blocks starting at r0 in [f_lo, f_hi] are fast: every stage
     // active, no band row, rows owned / inside the sets, no event row, for
-    // all rows the block computes and prefetches (r0 .. r0+UNROLL-1+D).
+    // all rows the block computes and prefetches (r0 .. r0+U-1+D).
     const int f_lo = max(ya, g.y0) + 4 * P - 2;
-    const int f_hi = min(yb + 2 * P - 2, g.hy1 + P - 1) - (UNROLL - 1 + D);
+    const int f_hi = min(yb + 2 * P - 2, g.hy1 + P - 1) - (U - 1 + D);
     const int e_lo = ev_lo, e_hi = ev_hi;
     // slot of stage-A E row y (ye0 <= y), or -1 (uniform)
     auto slot_of = [&](int y) {
@@ -406,19 +409,19 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
         }
     };
 
-    for (int r0 = r_first;; r0 += UNROLL) {
+    for (int r0 = r_first;; r0 += U) {
         // uniform: all rows this block computes and prefetches are steady
         const bool fast = r0 >= f_lo && r0 <= f_hi &&
-                          (r0 + UNROLL + D - 2 * P < e_lo || r0 - 4 * P + 2 > e_hi);
+                          (r0 + U + D - 2 * P < e_lo || r0 - 4 * P + 2 > e_hi);
         if (fast) {
 #pragma unroll
-            for (int uu = 0; uu < UNROLL; ++uu) {
+            for (int uu = 0; uu < U; ++uu) {
                 iter(std::true_type{}, r0 + uu, uu % D);
                 issue(std::true_type{}, uu % D, r0 + uu + D, true);
             }
         } else {
 #pragma unroll
-            for (int uu = 0; uu < UNROLL; ++uu) {
+            for (int uu = 0; uu < U; ++uu) {
                 const int r = r0 + uu;
                 if (r > r_end) return;
                 iter(std::false_type{}, r, uu % D);
