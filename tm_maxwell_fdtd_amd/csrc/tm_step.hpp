@@ -319,7 +319,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
 {
     constexpr int W = Strip<P>::W, OFF = Strip<P>::OFF;
     constexpr int D = PREFETCH;
-    __shared__ float rowE[NT];
+    __shared__ float rowE[2][NT];       // by row parity (one barrier per row for P >= 2)
     __shared__ float ring[P][NT];
     __shared__ float cyt[CH_MAX + 2 * P][6];
     __shared__ int evs[CH_MAX];         // slots of the owned rows
@@ -450,13 +450,14 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
                 for (int i = 0; i < 2 * P - 1; ++i) hw[i] = hw[i + 1];
                 hw[2 * P - 1] = hxn;
             }
-            rowE[tid] = ew[P - 1];                     // E^n row h
+            float* const rE = rowE[r & 1];
+            rE[tid] = ew[P - 1];                       // E^n row h
             __syncthreads();
 
             // --- Hz(h, c): the owned rows, owned columns plus P on each side
             if (hz_row(h)) {                            // uniform
-                float d = g.rdx * stencil<P>([&](int k) { return rowE[th + k]; },
-                                             [&](int k) { return rowE[th - k + 1]; });
+                float d = g.rdx * stencil<P>([&](int k) { return rE[th + k]; },
+                                             [&](int k) { return rE[th - k + 1]; });
                 if (xband) {                            // uniform
                     float m = fMxh[u];
                     d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
@@ -466,7 +467,10 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
                 b1.st(own && hz_col, hzn, oh, L.oHz);
                 ring[h % P][tid] = hzn;
             }
-            __syncthreads();
+            // P >= 2: the E row reads the ring row written P-1 rows earlier
+            // (barriers in between), and the row buffer alternates, so one
+            // barrier per row suffices
+            if constexpr (P == 1) __syncthreads();
 
             // --- Ey(y, c): owned cells
             if (y >= ya) {                              // uniform

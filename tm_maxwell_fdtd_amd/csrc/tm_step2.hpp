@@ -75,15 +75,15 @@ struct Fwd2Args {
 };
 
 template <int P, int SNAP>
-__global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
+__global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
 {
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH_F2;
     constexpr int U = UNROLL_F2;
     constexpr int R2 = 2 * P;                       // ring / FIFO depth (a power of two)
     constexpr uint32_t ESZ = snap_bytes<SNAP>();
-    __shared__ float rowA[NT];                      // E^n row hA
-    __shared__ float rowB[NT];                      // E^{n+1} row hB
+    __shared__ float rowA[2][NT];                   // E^n row hA, by row parity
+    __shared__ float rowB[2][NT];                   // E^{n+1} row hB, by row parity
     __shared__ float ringA[R2][NT];                 // Hz^{n+1/2} rows
     __shared__ float ringB[P][NT];                  // Hz^{n+3/2} rows
     __shared__ float mfifo[4][R2][NT];              // stage A's CPML memories, lane-private
@@ -256,8 +256,10 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
 #pragma unroll
         for (int i = 0; i < 2 * P - 1; ++i) ewA[i] = ewA[i + 1];
         ewA[2 * P - 1] = fE[u];
-        rowA[tid] = ewA[P - 1];
-        rowB[tid] = ewB[P];
+        float* const rA = rowA[r & 1];
+        float* const rB = rowB[r & 1];
+        rA[tid] = ewA[P - 1];
+        rB[tid] = ewB[P];
         {
             float d = g.rdy * stencil<P>([&](int k) { return ewA[P - 1 + k]; },
                                          [&](int k) { return ewA[P - k]; });
@@ -277,8 +279,8 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
 
         // ---- (b) Hz of stage A (row hA) and of stage B (row hB)
         if (FAST || (hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2))) {   // uniform
-            float d = g.rdx * stencil<P>([&](int k) { return rowA[th + k]; },
-                                         [&](int k) { return rowA[th - k + 1]; });
+            float d = g.rdx * stencil<P>([&](int k) { return rA[th + k]; },
+                                         [&](int k) { return rA[th - k + 1]; });
             if (xband) {
                 float m = fMxh[u];
                 d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
@@ -287,8 +289,8 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
             ringA[slot2(hA)][tid] = hzA_ok ? fmaf(fQa[u], d, fHz[u]) : 0.0f;
         }
         if (FAST || (hz_row(hB) & own_row(hB))) {                             // uniform
-            float d = g.rdx * stencil<P>([&](int k) { return rowB[th + k]; },
-                                         [&](int k) { return rowB[th - k + 1]; });
+            float d = g.rdx * stencil<P>([&](int k) { return rB[th + k]; },
+                                         [&](int k) { return rB[th - k + 1]; });
             if (xband) {
                 float m = mfifo[1][slot2(hB)][tid];
                 d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
@@ -300,7 +302,9 @@ __global__ __launch_bounds__(NT) void k_fwd_step2(Fwd2Args a)
             else b1.st(own & colHz, hzn, (uint32_t)(hB * nx) * 4u + c4, L.oHz);
             ringB[slot1(hB)][tid] = hzn;
         }
-        __syncthreads();
+        // P >= 2: both E rows read ring rows written P-1 rows earlier and the
+        // row buffers alternate, so one barrier per row suffices
+        if constexpr (P == 1) __syncthreads();
 
         // ---- (c) E of stage A (row yA), with the step-n sources and receivers
         if (FAST || r >= ya) {                                                // uniform
