@@ -200,7 +200,8 @@ tm_status tm_grad(const tm_plan* plan, const float* grad_ca_shot, const float* g
  *   dJ/dsigma  = -dJ/dCa (1 + Ca) Cb / 2 - dJ/dCb Cb^2 / 2,
  * per cell, in float32.  Cq (the magnetic coefficient) is not involved.
  *   ca, cb: device float32 [ny][nx], the coefficients the gradients were
- *      taken at (required).
+ *      taken at (required).  With model_per_shot, call it once per shot
+ *      with that shot's coefficients and gradients.
  *   grad_ca, grad_cb: device float32 [ny][nx] (e.g. tm_grad's outputs); a
  *      NULL input counts as zero.
  *   dt: the time step (seconds) the coefficients were built with; must be

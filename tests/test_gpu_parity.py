@@ -491,3 +491,17 @@ def test_per_shot_models_eps_sigma_and_courant(orc):
     finally:
         shot0.close()
     assert c_all == pytest.approx(c0, rel=1e-6)
+
+
+@pytest.mark.parametrize("mode", ["ckpt", "host"])
+def test_per_shot_models_storage_modes(mode):
+    """One model per shot with checkpoint replay (the replay reads every
+    shot's own model again) or with the pinned-host snapshot store: bitwise
+    the results of the full device store."""
+    base = inputs.random_workload(4, 36, 8, nt=45, n_shots=3, n_src=2, n_rec=5, seed=800)
+    wl = inputs.as_f32(inputs.per_shot_models(base))
+    ref = run_gpu(wl, snap="f32", ckpt_every=0)
+    kw = dict(ckpt_every=9) if mode == "ckpt" else dict(ckpt_every=0, storage=1)
+    got = run_gpu(wl, snap="f32", **kw)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{mode} {key}")
