@@ -505,3 +505,30 @@ def test_per_shot_models_storage_modes(mode):
     got = run_gpu(wl, snap="f32", **kw)
     for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{mode} {key}")
+
+
+@pytest.mark.parametrize("order", [4, 8])
+def test_event_rows_everywhere(orc, order):
+    """A receiver line down a column (an event row on every row of the E set)
+    and sources on many rows: every block runs the general iteration, the
+    event rows span the whole window; against the oracle, and one and two
+    steps per launch bitwise equal."""
+    wl = inputs.random_workload(order, 40, 8, nt=40, n_shots=2, n_src=6, n_rec=8, seed=820 + order,
+                                src_anywhere=True)
+    p = order // 2
+    rows = np.arange(p, wl.ny - p + 1)
+    wl.rec = np.stack([rows * wl.nx + (wl.nx // 2 + s) for s in range(2)]).astype(np.int64)   # [S][n_rec]
+    rng = np.random.default_rng(821)
+    wl.src = np.stack([rng.choice(rows, 6) * wl.nx + (p + 3 * s + 1) for s in range(2)]).astype(np.int64)
+    wl.f = wl.f[:, :, :1].repeat(6, axis=2)
+    wl = inputs.as_f32(wl)
+    ref = run_oracle(orc, wl)
+    got = run_gpu(wl, snap="f32", grad_r=ref["residual"])
+    one = run_gpu(wl, snap="f32", grad_r=ref["residual"], time_block=1)
+    errs = {k: rel_l2(got[k], ref[k]) for k in ("records", "gca_shot", "gcb_shot", "grad_f")}
+    print(f"[events everywhere o{order}] n_rec {wl.n_rec}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()),
+          flush=True)
+    assert errs["records"] <= REC_TOL
+    assert max(errs["gca_shot"], errs["gcb_shot"], errs["grad_f"]) <= GRAD_TOL["f32"]
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=key)
