@@ -141,9 +141,17 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
     // Addressing as in k_adj_step: loop-invariant lane offsets (out of range
     // where the lane never touches the array), per-row masks, clamped rows.
     const int v_e = lane_off(colE, c4), v_own = lane_off(own, c4), v_eA = lane_off(eA_ok, c4);
-    const int v_hz = lane_off(hzA_ok, c4), v_ownhz = lane_off(own & colHz, c4);
-    const int v_xe = lane_off(fx_e, bx4), v_ownxe = lane_off(own & fx_e, bx4);
-    const int v_hzxh = lane_off(hzA_ok & fx_h, bx4), v_ownhzxh = lane_off(own & colHz & fx_h, bx4);
+    const int v_hz = lane_off(hzA_ok, c4), v_hzo = lane_off(colHz, c4);
+    const int v_xe = lane_off(fx_e, bx4);
+    const int v_hzxh = lane_off(hzA_ok & fx_h, bx4), v_hzxo = lane_off(colHz & fx_h, bx4);
+    // v | the OOB bit of the non-owned columns, rebuilt at each use (the
+    // empty asm keeps it inside the row loop) so that the owned-column
+    // variants of the offsets take no registers of their own.
+    auto ownv = [&](int v) {
+        int o = v_own;
+        asm volatile("" : "+v"(o));
+        return v | (o & RBuf::OOB);
+    };
     const int v_g = lane_off(grad, c4), v_gs = lane_off(grad, (uint32_t)(c - g.x0) * ESZ);
     auto msk = [](bool ok) { return ok ? 0 : RBuf::OOB; };
     auto grow = [&](int y) { return (uint32_t)min(max(y, 0), ny - 1); };
@@ -161,14 +169,46 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
     float fE[D], fCbA[D], fMxe[D], fMye[D], fHx[D], fMyh[D], fQA[D], fHz[D], fMxh[D], fCaA[D], fEvA[D];
     float fCbB[D], fSeA[D], fScA[D], fSeB[D], fScB[D], fGa[D], fGb[D], fQB[D], fCaB[D], fEvB[D];
     int fGA[D], fGB[D];
-    auto issue = [&](auto fast_t, int u, int r, bool live) {
+    // The loads of a row come in three groups, each issued for the next row
+    // as soon as the current row's iteration has used that group's slots, so
+    // that most loads get nearly a whole iteration of lead: PART 1 (fronts'
+    // inputs and stage A's lambda_Hx inputs) after phase 1, PART 2 (Cq and
+    // the lambda_Hz inputs) after phase 2, PART 3 (Ca, and the gradient
+    // accumulators and snapshots of stage B's front, whose short lead keeps
+    // the registers live across phases 2 and 3 within the budget) after
+    // phase 3.
+    auto issue = [&](auto fast_t, auto part_t, int u, int r, bool live) {
         constexpr bool FAST = decltype(fast_t)::value;
+        constexpr int PART = decltype(part_t)::value;
         auto M = [&](bool ok) { return FAST ? 0 : msk(ok); };
         auto G = [&](int y) { return FAST ? (uint32_t)y : grow(y); };
         const int hA = r - P, yA = r - 2 * P + 1, rB = r - 2 * P, hB = rB - P, yB = rB - 2 * P + 1;
         const bool liveA = live & (r <= r_end - 1);
         const bool liveB = live & (r >= ya + 1);
         const int meA = M(liveA & e_row(r)), meB = M(liveB & e_row(rB));
+        if constexpr (PART == 3) {
+            const uint32_t orB = G(rB) * rowb;
+            const int mg = M(liveB & own_row(rB) & (rB >= g.y0) & (rB < g.y1));
+            const uint32_t sr = FAST ? (uint32_t)(rB - g.y0) * (uint32_t)g.nxi * ESZ : srw(rB);
+            fSeA[u] = snap_getv<SNAP>(bseA, v_gs | mg, sr);
+            fScA[u] = snap_getv<SNAP>(bscA, v_gs | mg, sr);
+            fSeB[u] = snap_getv<SNAP>(bseB, v_gs | mg, sr);
+            fScB[u] = snap_getv<SNAP>(bscB, v_gs | mg, sr);
+            fGa[u] = bga.ldv(v_g | mg, orB);
+            fGb[u] = bgb.ldv(v_g | mg, orB);
+            fCaA[u] = bm.ldv(v_eA | M(liveA & (yA >= Ya) & (yA < Yb) & e_row(yA)), a.m.oCa + G(yA) * rowb);
+            fCaB[u] = bm.ldv(v_own | M(liveB & own_row(yB)), a.m.oCa + G(yB) * rowb);
+            return;
+        }
+        if constexpr (PART == 2) {
+            const uint32_t ohA = G(hA) * rowb;
+            fQA[u] = bm.ldv(v_e | M(liveA & (hx_row(hA) | hzA_row(hA))), a.m.oCq + ohA);
+            const int mzA = M(liveA & hzA_row(hA));
+            fHz[u] = b0.ldv(v_hz | mzA, L.oHz + ohA);
+            fMxh[u] = b0.ldv(xband ? (v_hzxh | mzA) : RBuf::OOB, L.oMxh + G(hA) * brow);
+            fQB[u] = bm.ldv(v_e | M(liveB & (hx_row(hB) | own_row(hB))), a.m.oCq + G(hB) * rowb);
+            return;
+        }
         if constexpr (FAST) {
             fGA[u] = -1;
             fGB[u] = -1;
@@ -192,25 +232,13 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
             fMye[u] = b0.ldv(v_e | meA | msk(fy_e(r)), L.oMye + brw(r) * rowb);
             fMyh[u] = b0.ldv(v_e | mhA | msk(fy_h(hA)), L.oMyh + brw(hA) * rowb);
         }
-        fQA[u] = bm.ldv(v_e | M(liveA & (hx_row(hA) | hzA_row(hA))), a.m.oCq + ohA);
-        const int mzA = M(liveA & hzA_row(hA));
-        fHz[u] = b0.ldv(v_hz | mzA, L.oHz + ohA);
-        fMxh[u] = b0.ldv(xband ? (v_hzxh | mzA) : RBuf::OOB, L.oMxh + G(hA) * brow);
-        fCaA[u] = bm.ldv(v_eA | M(liveA & (yA >= Ya) & (yA < Yb) & e_row(yA)), a.m.oCa + G(yA) * rowb);
         // stage B
         const uint32_t orB = G(rB) * rowb;
         fCbB[u] = bm.ldv(v_e | meB, a.m.oCb + orB);
-        const int mg = M(liveB & own_row(rB) & (rB >= g.y0) & (rB < g.y1));
-        const uint32_t sr = FAST ? (uint32_t)(rB - g.y0) * (uint32_t)g.nxi * ESZ : srw(rB);
-        fSeA[u] = snap_getv<SNAP>(bseA, v_gs | mg, sr);
-        fScA[u] = snap_getv<SNAP>(bscA, v_gs | mg, sr);
-        fSeB[u] = snap_getv<SNAP>(bseB, v_gs | mg, sr);
-        fScB[u] = snap_getv<SNAP>(bscB, v_gs | mg, sr);
-        fGa[u] = bga.ldv(v_g | mg, orB);
-        fGb[u] = bgb.ldv(v_g | mg, orB);
-        fQB[u] = bm.ldv(v_e | M(liveB & (hx_row(hB) | own_row(hB))), a.m.oCq + G(hB) * rowb);
-        fCaB[u] = bm.ldv(v_own | M(liveB & own_row(yB)), a.m.oCa + G(yB) * rowb);
     };
+    using Part1 = std::integral_constant<int, 1>;
+    using Part2 = std::integral_constant<int, 2>;
+    using Part3 = std::integral_constant<int, 3>;
 
     float edA[R2], wwA[R2], twA[R2], udA[P + 1];   // as ed, ww, tw, ud of k_adj_step, stage A
     float edB[R2], wwB[R2], twB[R2], udB[P + 1];   // ... stage B
@@ -273,9 +301,15 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
                b0.ldv(v_xe | me, L.oMxe + grow(r) * brow), b0.ldv(v_e | me | msk(fy_e(r)), L.oMye + brw(r) * rowb));
     }
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue(std::false_type{}, u, Ya + u, Ya + u <= r_end);
+    for (int u = 0; u < D; ++u) {
+        issue(std::false_type{}, Part1{}, u, Ya + u, Ya + u <= r_end);
+        issue(std::false_type{}, Part2{}, u, Ya + u, Ya + u <= r_end);
+        issue(std::false_type{}, Part3{}, u, Ya + u, Ya + u <= r_end);
+    }
 
-    auto iter = [&](auto fast_t, int r, int u) {
+    // nfast_t / rn / live_n: the issue instance, row and liveness of the
+    // next row's loads.
+    auto iter = [&](auto fast_t, auto nfast_t, int r, int u, int rn, bool live_n) {
         constexpr bool FAST = decltype(fast_t)::value;
         auto M = [&](bool ok) { return FAST ? 0 : msk(ok); };
         auto G = [&](int y) { return FAST ? (uint32_t)y : grow(y); };
@@ -309,7 +343,7 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
             if (xband) {
                 float m = mfifo[0][fslot(rB)][tid];
                 uu = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, hv);
-                b1.stv(m, v_ownxe | ms, L.oMxe + G(rB) * brow);
+                b1.stv(m, ownv(v_xe) | ms, L.oMxe + G(rB) * brow);
             }
             if (!FAST && fy_e(rB)) {
                 const float* ct = ctab(rB);
@@ -348,6 +382,7 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
             shift_in(twA, hx_ok ? txv : 0.0f);
             shift_in(hxA, lhx);
         }
+        issue(nfast_t, Part1{}, u, rn, live_n);
         rowUB[tid] = udB[0];                              // u of row hB
         rowUA[tid] = udA[0];                              // u of row hA
         __syncthreads();
@@ -356,12 +391,12 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
         if (fullB && (FAST || hzB_row(hB))) {             // uniform
             const float acc = stencil<P>([&](int k) { return rowUB[th + k]; }, [&](int k) { return rowUB[th - k + 1]; });
             const float lhz = fmaf(-g.rdx, acc, hzA[0]);
-            b1.stv(lhz, v_ownhz, L.oHz + (uint32_t)hB * rowb);
+            b1.stv(lhz, ownv(v_hzo), L.oHz + (uint32_t)hB * rowb);
             float tz = fQB[u] * lhz;
             if (xband) {
                 float m = mfifo[3][fslot(hB)][tid];
                 tz = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, tz);
-                b1.stv(m, v_ownhzxh, L.oMxh + (uint32_t)hB * brow);
+                b1.stv(m, ownv(v_hzxo), L.oMxh + (uint32_t)hB * brow);
             }
             ringB[hB % P][tid] = hzB_ok ? tz : 0.0f;
         }
@@ -380,6 +415,7 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
             }
             shift_in(hzA, hzn);
         }
+        issue(nfast_t, Part2{}, u, rn, live_n);
         __syncthreads();
 
         // ---- phase 3: lambda_E of both stages
@@ -396,6 +432,7 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
             const float en = fmaf(fCaA[u], edA[0], fmaf(-az, g.rdx, ay * g.rdy));
             eAprev = (eA_ok & (FAST || e_row(yA))) ? en : 0.0f;
         }
+        issue(nfast_t, Part3{}, u, rn, live_n);
     };
 
     // Unrolled blocks starting at r0 in [f_lo, f_hi] without event rows are
@@ -411,16 +448,14 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
         if (fast) {
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
-                iter(std::true_type{}, r0 + uu, uu % D);
-                issue(std::true_type{}, uu % D, r0 + uu + D, true);
+                iter(std::true_type{}, std::true_type{}, r0 + uu, uu % D, r0 + uu + D, true);
             }
         } else {
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 const int r = r0 + uu;
                 if (r > r_end) return;
-                iter(std::false_type{}, r, uu % D);
-                issue(std::false_type{}, uu % D, r + D, r + D <= r_end);
+                iter(std::false_type{}, std::false_type{}, r, uu % D, r + D, r + D <= r_end);
             }
         }
     }
