@@ -48,7 +48,7 @@
 namespace tmf {
 
 constexpr int CH2_MAX = 128;   // largest chunk height of the two-step kernel (LDS tables)
-constexpr int PREFETCH_F2 = 2; // rows of loads in flight ahead
+constexpr int PREFETCH_F2 = 1; // rows of loads in flight ahead
 constexpr int UNROLL_F2 = 4;   // row-loop unroll, a multiple of PREFETCH_F2
 
 template <int P>
@@ -183,54 +183,78 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
     float fE[D], fQa[D], fHx[D], fHz[D], fMyh[D], fMxh[D], fCa[D], fCb[D], fMxe[D], fMye[D];
     float fQb[D], fCaB[D], fCbB[D], fEvA[D], fEvB[D];
     int fGA[D], fGB[D];                             // slots of rows yA / yB, or -1
-    auto issue = [&](auto fast_t, int u, int r, bool live) {
+    // The loads of a row come in five groups, each issued for row r + D
+    // right after the part of row r's iteration that last reads the group's
+    // slot: K1 (E, Hx, Myh) after (a), K2 (Cq, Hz, Mxh of stage A) after
+    // (b), K3 (stage A's E inputs and events) after (c), K4 (stage B's Cq)
+    // after stage B's Hx, K5 (stage B's E inputs and events) at the end.
+    auto issue = [&](auto fast_t, auto part_t, int u, int r, bool live) {
         constexpr bool FAST = decltype(fast_t)::value;
+        constexpr int K = decltype(part_t)::value;
         const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
         if constexpr (FAST) {
-            fGA[u] = -1;
-            fGB[u] = -1;
             const uint32_t rA = (uint32_t)hA * rowb, eA = (uint32_t)yA * rowb;
-            fE[u] = b0.ldv(v_in, L.oE + (uint32_t)r * rowb);
-            fQa[u] = bm.ldv(v_in, a.m.oCq + rA);
-            fHx[u] = b0.ldv(v_e, L.oHx + rA);
-            fHz[u] = b0.ldv(v_hz, L.oHz + rA);
-            fMxh[u] = b0.ldv(xband ? v_mxh : RBuf::OOB, L.oMxh + (uint32_t)hA * brow);
-            fCa[u] = bm.ldv(v_e, a.m.oCa + eA);
-            fCb[u] = bm.ldv(v_e, a.m.oCb + eA);
-            fMxe[u] = b0.ldv(xband ? v_mxe : RBuf::OOB, L.oMxe + (uint32_t)yA * brow);
-            fQb[u] = bm.ldv(v_in, a.m.oCq + (uint32_t)hB * rowb);
-            fCaB[u] = bm.ldv(v_own, a.m.oCa + (uint32_t)yB * rowb);
-            fCbB[u] = bm.ldv(v_own, a.m.oCb + (uint32_t)yB * rowb);
+            if constexpr (K == 1) {
+                fE[u] = b0.ldv(v_in, L.oE + (uint32_t)r * rowb);
+                fHx[u] = b0.ldv(v_e, L.oHx + rA);
+            } else if constexpr (K == 2) {
+                fQa[u] = bm.ldv(v_in, a.m.oCq + rA);
+                fHz[u] = b0.ldv(v_hz, L.oHz + rA);
+                fMxh[u] = b0.ldv(xband ? v_mxh : RBuf::OOB, L.oMxh + (uint32_t)hA * brow);
+            } else if constexpr (K == 3) {
+                fGA[u] = -1;
+                fCa[u] = bm.ldv(v_e, a.m.oCa + eA);
+                fCb[u] = bm.ldv(v_e, a.m.oCb + eA);
+                fMxe[u] = b0.ldv(xband ? v_mxe : RBuf::OOB, L.oMxe + (uint32_t)yA * brow);
+            } else if constexpr (K == 4) {
+                fQb[u] = bm.ldv(v_in, a.m.oCq + (uint32_t)hB * rowb);
+            } else {
+                fGB[u] = -1;
+                fCaB[u] = bm.ldv(v_own, a.m.oCa + (uint32_t)yB * rowb);
+                fCbB[u] = bm.ldv(v_own, a.m.oCb + (uint32_t)yB * rowb);
+            }
         } else {
             const uint32_t ohA = (uint32_t)(hA * nx) * 4u + c4, oyA = (uint32_t)(yA * nx) * 4u + c4;
             const uint32_t ohB = (uint32_t)(hB * nx) * 4u + c4, oyB = (uint32_t)(yB * nx) * 4u + c4;
-            // event rows first (uniform branches), then the loads every row has
-            const bool eb_do = live & own & own_row(yB);
-            const int gA = slot_of(yA), gB = slot_of(yB);
-            fGA[u] = gA;
-            fGB[u] = gB;
-            fEvA[u] = 0.0f;
-            fEvB[u] = 0.0f;
-            if (gA >= 0) fEvA[u] = bev.ld(live & incol, (uint32_t)(gA * nx) * 4u + c4, a.es0.add);
-            if (gB >= 0) fEvB[u] = bev.ld(eb_do, (uint32_t)(gB * nx) * 4u + c4, a.es1.add);
-            fE[u] = b0.ld(live & in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
-            fQa[u] = bm.ld(live & in_rows(hA) & incol, ohA, a.m.oCq);
-            const bool hx_do = live & colE & hx_row(hA);
-            fHx[u] = b0.ld(hx_do, ohA, L.oHx);
-            fMyh[u] = b0.ld(hx_do & fy_h(hA), (uint32_t)(band_y(g, hA) * nx) * 4u + c4, L.oMyh);
-            const bool hz_do = live & colHz & hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2);
-            fHz[u] = b0.ld(hz_do, ohA, L.oHz);
-            fMxh[u] = b0.ld(hz_do & fx_h, (uint32_t)(hA * g.bx) * 4u + bx4, L.oMxh);
-            const bool e_do = live & colE & rowE(yA) & (yA >= ye0);
-            fCa[u] = bm.ld(e_do, oyA, a.m.oCa);
-            fCb[u] = bm.ld(e_do, oyA, a.m.oCb);
-            fMxe[u] = b0.ld(e_do & fx_e, (uint32_t)(yA * g.bx) * 4u + bx4, L.oMxe);
-            fMye[u] = b0.ld(e_do & fy_e(yA), (uint32_t)(band_y(g, yA) * nx) * 4u + c4, L.oMye);
-            fQb[u] = bm.ld(live & in_rows(hB) & incol & (hB >= ya - P), ohB, a.m.oCq);
-            fCaB[u] = bm.ld(eb_do, oyB, a.m.oCa);
-            fCbB[u] = bm.ld(eb_do, oyB, a.m.oCb);
+            if constexpr (K == 1) {
+                fE[u] = b0.ld(live & in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
+                const bool hx_do = live & colE & hx_row(hA);
+                fHx[u] = b0.ld(hx_do, ohA, L.oHx);
+                fMyh[u] = b0.ld(hx_do & fy_h(hA), (uint32_t)(band_y(g, hA) * nx) * 4u + c4, L.oMyh);
+            } else if constexpr (K == 2) {
+                fQa[u] = bm.ld(live & in_rows(hA) & incol, ohA, a.m.oCq);
+                const bool hz_do = live & colHz & hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2);
+                fHz[u] = b0.ld(hz_do, ohA, L.oHz);
+                fMxh[u] = b0.ld(hz_do & fx_h, (uint32_t)(hA * g.bx) * 4u + bx4, L.oMxh);
+            } else if constexpr (K == 3) {
+                // event row first (uniform branch), then the loads every row has
+                const int gA = slot_of(yA);
+                fGA[u] = gA;
+                fEvA[u] = 0.0f;
+                if (gA >= 0) fEvA[u] = bev.ld(live & incol, (uint32_t)(gA * nx) * 4u + c4, a.es0.add);
+                const bool e_do = live & colE & rowE(yA) & (yA >= ye0);
+                fCa[u] = bm.ld(e_do, oyA, a.m.oCa);
+                fCb[u] = bm.ld(e_do, oyA, a.m.oCb);
+                fMxe[u] = b0.ld(e_do & fx_e, (uint32_t)(yA * g.bx) * 4u + bx4, L.oMxe);
+                fMye[u] = b0.ld(e_do & fy_e(yA), (uint32_t)(band_y(g, yA) * nx) * 4u + c4, L.oMye);
+            } else if constexpr (K == 4) {
+                fQb[u] = bm.ld(live & in_rows(hB) & incol & (hB >= ya - P), ohB, a.m.oCq);
+            } else {
+                const bool eb_do = live & own & own_row(yB);
+                const int gB = slot_of(yB);
+                fGB[u] = gB;
+                fEvB[u] = 0.0f;
+                if (gB >= 0) fEvB[u] = bev.ld(eb_do, (uint32_t)(gB * nx) * 4u + c4, a.es1.add);
+                fCaB[u] = bm.ld(eb_do, oyB, a.m.oCa);
+                fCbB[u] = bm.ld(eb_do, oyB, a.m.oCb);
+            }
         }
     };
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    using K3 = std::integral_constant<int, 3>;
+    using K4 = std::integral_constant<int, 4>;
+    using K5 = std::integral_constant<int, 5>;
 
     float ewA[2 * P];    // E^n rows r-2P+1 .. r
     float hwA[2 * P];    // Hx^{n+1/2} rows hA-2P+1 .. hA
@@ -244,11 +268,19 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
         ewA[i] = b0.ld(in_rows(r) & incol, (uint32_t)(r * nx) * 4u + c4, L.oE);
     }
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue(std::false_type{}, u, r_first + u, r_first + u <= r_end);
+    for (int u = 0; u < D; ++u) {
+        const int r = r_first + u;
+        issue(std::false_type{}, K1{}, u, r, r <= r_end);
+        issue(std::false_type{}, K2{}, u, r, r <= r_end);
+        issue(std::false_type{}, K3{}, u, r, r <= r_end);
+        issue(std::false_type{}, K4{}, u, r, r <= r_end);
+        issue(std::false_type{}, K5{}, u, r, r <= r_end);
+    }
 
     // One iteration (row r, prefetch slot u).  FAST: the block is fast (all
-    // row predicates true / false as described above).
-    auto iter = [&](auto fast_t, int r, int u) {
+    // row predicates true / false as described above).  The loads of row
+    // rn = r + D (liveness live_n) go into slot u as the iteration frees it.
+    auto iter = [&](auto fast_t, int r, int u, int rn, bool live_n) {
         constexpr bool FAST = decltype(fast_t)::value;
         const int hA = r - P, yA = r - 2 * P + 1, hB = r - 3 * P + 1, yB = r - 4 * P + 2;
 
@@ -275,6 +307,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             for (int i = 0; i < 2 * P - 1; ++i) hwA[i] = hwA[i + 1];
             hwA[2 * P - 1] = hxn;
         }
+        issue(fast_t, K1{}, u, rn, live_n);
         __syncthreads();
 
         // ---- (b) Hz of stage A (row hA) and of stage B (row hB)
@@ -302,6 +335,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             else b1.st(own & colHz, hzn, (uint32_t)(hB * nx) * 4u + c4, L.oHz);
             ringB[slot1(hB)][tid] = hzn;
         }
+        issue(fast_t, K2{}, u, rn, live_n);
         // P >= 2: both E rows read ring rows written P-1 rows earlier and the
         // row buffers alternate, so one barrier per row suffices
         if constexpr (P == 1) __syncthreads();
@@ -347,6 +381,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             for (int i = 0; i < 2 * P - 1; ++i) ewB[i] = ewB[i + 1];
             ewB[2 * P - 1] = en;
         }
+        issue(fast_t, K3{}, u, rn, live_n);
 
         // ---- Hx of stage B (row hB)
         if (FAST || r >= ya + 2 * P - 1) {                                    // uniform
@@ -367,6 +402,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             for (int i = 0; i < 2 * P - 1; ++i) hwB[i] = hwB[i + 1];
             hwB[2 * P - 1] = hxn;
         }
+        issue(fast_t, K4{}, u, rn, live_n);
 
         // ---- E of stage B (row yB): the owned output row
         if (FAST || r >= ya + 4 * P - 2) {                                    // uniform
@@ -411,6 +447,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                 b1.st(own, en, (uint32_t)(yB * nx) * 4u + c4, L.oE);
             }
         }
+        issue(fast_t, K5{}, u, rn, live_n);
     };
 
     for (int r0 = r_first;; r0 += U) {
@@ -420,16 +457,14 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
         if (fast) {
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
-                iter(std::true_type{}, r0 + uu, uu % D);
-                issue(std::true_type{}, uu % D, r0 + uu + D, true);
+                iter(std::true_type{}, r0 + uu, uu % D, r0 + uu + D, true);
             }
         } else {
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 const int r = r0 + uu;
                 if (r > r_end) return;
-                iter(std::false_type{}, r, uu % D);
-                issue(std::false_type{}, uu % D, r + D, r + D <= r_end);
+                iter(std::false_type{}, r, uu % D, r + D, r + D <= r_end);
             }
         }
     }
