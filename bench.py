@@ -9,6 +9,10 @@ the order-8 workload: 1024x1024 interior + 32-cell CPML per side, 16 shots,
 2000 time steps, bfloat16 snapshots.  The misfit is J = 1/2 |r|^2, so the
 adjoint source is the records themselves.
 
+tm_forward is called with TM_FWD_CHECK (Courant check, which also finds
+whether Cq holds one value: mu_r = 1 in these workloads, so the forward
+kernels read no Cq array), inside the timed region.
+
 value = cell-updates / time of one step (Gcell-updates/s), where
 cell-updates = shots x (interior + CPML cells) x time steps.  The forward
 pass alone (no storage) is timed as well and reported as ``fwd_value``.
@@ -89,14 +93,19 @@ def kernel_bytes(name, wl, store, snap_bytes):
     k_fwd_step2 / k_adj_step2 advance two time steps per launch: twice the
     bytes of k_fwd_step / k_adj_step (the per-cell-update figure times the
     cell-updates of the launch), although the state crosses HBM only once.
+    k_fwd_step2_uq is k_fwd_step2 where Cq holds one value and is not read:
+    32 B per cell instead of 36.
     """
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
-    if name == "k_fwd_step":
+    if name in ("k_fwd_step", "k_fwd_step_uq"):
         snaps = 2 * snap_bytes * interior if store else 0
-        return S * (36 * cells + 16 * (band_y + band_x) + snaps)
+        per_cell = 32 if name.endswith("_uq") else 36
+        return S * (per_cell * cells + 16 * (band_y + band_x) + snaps)
     if name == "k_fwd_step2":
         return 2 * kernel_bytes("k_fwd_step", wl, store, snap_bytes)
+    if name == "k_fwd_step2_uq":
+        return 2 * kernel_bytes("k_fwd_step_uq", wl, store, snap_bytes)
     if name == "k_adj_step":
         grads = (2 * snap_bytes + 16) * interior if store else 0
         return S * (36 * cells + 16 * (band_y + band_x) + grads)
@@ -231,7 +240,8 @@ def main():
         return native.stream_handle()
 
     def step():
-        st = native.tm_forward(prop.plan, ws, wsb, ca, cb, cq, f, P(r), 0, wl.nt, native.TM_FWD_STORE, stream())
+        st = native.tm_forward(prop.plan, ws, wsb, ca, cb, cq, f, P(r), 0, wl.nt,
+                               native.TM_FWD_STORE | native.TM_FWD_CHECK, stream())
         assert st == 0, native.status_string(st)
         # J = 1/2 |r|^2: dJ/dr = r
         st = native.tm_adjoint(prop.plan, ws, wsb, ca, cb, cq, f, P(r), P(grad_f), P(gca_s), P(gcb_s), stream())
@@ -240,7 +250,7 @@ def main():
         assert st == 0, native.status_string(st)
 
     def fwd_only():
-        st = native.tm_forward(prop.plan, ws, wsb, ca, cb, cq, f, P(r), 0, wl.nt, 0, stream())
+        st = native.tm_forward(prop.plan, ws, wsb, ca, cb, cq, f, P(r), 0, wl.nt, native.TM_FWD_CHECK, stream())
         assert st == 0, native.status_string(st)
 
     cell_updates = wl.cell_updates()
@@ -287,13 +297,15 @@ def main():
     p = wl.order // 2
     launches_fwd = wl.nt
     kernels = {}
+    uq = results["step"][1].get("k_fwd_step2_uq", (0, 0))[1] > 0   # tm_forward read one Cq value
     for name, (ms, n) in results["step"][1].items():
         if n == 0:
             continue
         avg_ms = ms / n
-        launches = wl.nt // 2 if name in ("k_fwd_step2", "k_adj_step2") else wl.nt
-        if name.startswith("k_fwd") and wl.ckpt_every:
-            launches *= 2
+        launches = wl.nt // 2 if name.startswith(("k_fwd_step2", "k_adj_step2")) else wl.nt
+        if name in ("k_fwd_step", "k_fwd_step2"):
+            # tm_forward (unless it ran the _uq instances) and the replays of the adjoint
+            launches *= (0 if uq else 1) + (1 if wl.ckpt_every else 0)
         # in a full step the forward stores snapshots and the adjoint accumulates gradients
         nbytes = kernel_bytes(name, wl, store=True, snap_bytes=snap_bytes)
         kernels[name] = dict(avg_us=avg_ms * 1e3, samples=n, est_total_s=avg_ms * launches / 1e3,

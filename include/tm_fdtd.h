@@ -157,7 +157,10 @@ tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb
  *      index).  May be NULL.
  *   flags: TM_FWD_STORE keeps what tm_adjoint needs (every chunk from
  *      t0 = 0 to nt must pass it); TM_FWD_CHECK returns TM_EUNSTABLE before
- *      stepping when the Courant number exceeds 1.
+ *      stepping when the Courant number exceeds 1.  The same check finds
+ *      whether every value of cq (all shots' models) has the bits of cq[0]
+ *      (mu_r uniform); the call then runs forward kernels that use that
+ *      value instead of reading the array, with bitwise the same results.
  */
 tm_status tm_forward(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca,
                      const float* cb, const float* cq, const float* f, float* r,
@@ -245,7 +248,9 @@ tm_status tm_timing_enable(tm_plan* plan, int32_t every);
 tm_status tm_timing_read(tm_plan* plan, double* total_ms, int64_t* count);
 
 /* Number of timed kernels, and the name of kernel ``k`` (the prefix of its
- * symbol name as profilers print it; NULL when k is out of range). */
+ * symbol name as profilers print it, with "_uq" for the two-step forward
+ * instances that read one Cq value instead of the array; NULL when k is out
+ * of range). */
 int32_t tm_kernel_count(void);
 const char* tm_kernel_name(int32_t k);
 

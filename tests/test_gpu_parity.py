@@ -203,6 +203,91 @@ def test_two_step_launch_bitwise_equals_single_steps(order, snap, ckpt):
         np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} order {order} {snap} K={ckpt}")
 
 
+@pytest.mark.parametrize("order", inputs.ORDERS)
+@pytest.mark.parametrize("snap,ckpt", [("f32", 0), ("bf16", 0), ("f32", 7)])
+def test_uniform_cq_two_step_bitwise_equals_single_steps(order, snap, ckpt):
+    """mu_r one value everywhere: the two-step kernels read no Cq bytes and
+    use the value instead, the one-step kernels read the array; both give
+    bitwise the same records and gradients."""
+    wl = inputs.as_f32(inputs.random_workload(order, 70, 9, nt=101, n_shots=3, n_src=3, n_rec=7,
+                                              seed=830 + order, src_anywhere=True, mu_range=(1.0, 1.0)))
+    assert np.all(wl.cq == wl.cq.flat[0])
+    one = run_gpu(wl, snap=snap, ckpt_every=ckpt, time_block=1)
+    two = run_gpu(wl, snap=snap, ckpt_every=ckpt, time_block=2)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} order {order} {snap} K={ckpt}")
+
+
+def test_uniform_cq_selects_the_cq_free_forward():
+    """With TM_FWD_CHECK a forward over a uniform Cq runs the instances that
+    read no Cq (timed as k_fwd_step2_uq); without the check, with a
+    non-uniform Cq, and in the adjoint's replays the array instances run."""
+    from tm_maxwell_fdtd_amd import native
+
+    def counts(wl, check, ckpt_every=0):
+        prop = native.Propagator(wl, ckpt_every=ckpt_every)
+        try:
+            native.tm_timing_enable(prop.plan, 1)
+            r = prop.forward(store=True, check=check)
+            _, fwd = native.tm_timing_read(prop.plan)
+            prop.adjoint(r)
+            _, adj = native.tm_timing_read(prop.plan)
+            native.tm_timing_enable(prop.plan, 0)
+        finally:
+            prop.close()
+        return ({k: n for k, (_, n) in fwd.items() if n}, {k: n for k, (_, n) in adj.items() if n})
+
+    uni = inputs.as_f32(inputs.random_workload(8, 40, 8, nt=40, n_shots=2, n_src=1, n_rec=4, seed=840,
+                                               mu_range=(1.0, 1.0)))
+    het = inputs.as_f32(inputs.random_workload(8, 40, 8, nt=40, n_shots=2, n_src=1, n_rec=4, seed=840))
+    fwd, _ = counts(uni, check=True)
+    assert fwd.get("k_fwd_step2_uq", 0) > 0 and "k_fwd_step2" not in fwd, fwd
+    fwd, _ = counts(uni, check=False)
+    assert fwd.get("k_fwd_step2", 0) > 0 and "k_fwd_step2_uq" not in fwd, fwd
+    fwd, _ = counts(het, check=True)
+    assert fwd.get("k_fwd_step2", 0) > 0 and "k_fwd_step2_uq" not in fwd, fwd
+    fwd, adj = counts(uni, check=True, ckpt_every=8)
+    assert fwd.get("k_fwd_step2_uq", 0) > 0 and "k_fwd_step2" not in fwd, fwd
+    assert adj.get("k_fwd_step2", 0) > 0 and "k_fwd_step2_uq" not in adj, adj
+
+
+@pytest.mark.parametrize("where", ["first", "interior", "last-used"])
+def test_cq_one_differing_cell_is_not_uniform(orc, where):
+    """Cq uniform except at one cell: the first cell (a halo cell the step
+    never reads, but the reference value of the uniformity test), an
+    interior cell, or the last cell any update reads.  The result must be
+    that of the array, against the oracle and bitwise across launch shapes."""
+    order = 4
+    wl = inputs.as_f32(inputs.random_workload(order, 48, 8, nt=80, n_shots=2, n_src=2, n_rec=6,
+                                              seed=850, mu_range=(1.0, 1.0)))
+    p = order // 2
+    cell = {"first": (0, 0), "interior": (wl.ny // 2 + 3, wl.nx // 2 - 5),
+            "last-used": (wl.ny - p - 1, wl.nx - p - 1)}[where]
+    wl.cq = wl.cq.copy()
+    wl.cq[cell] = np.float64(np.float32(wl.cq[cell] * 1.5))
+    got, _ = check(orc, wl, snap="f32", label=f"Cq differs at {where} {cell}")
+    one = run_gpu(wl, snap="f32", grad_r=got["residual"], time_block=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=f"{key}: two-step != one-step ({where})")
+
+
+def test_per_shot_models_uniform_cq_except_one_shot(orc):
+    """Per-shot models, mu_r = 1 in every shot but one cell of the last
+    shot's Cq: every shot against the oracle on its own model."""
+    base = inputs.random_workload(4, 36, 8, nt=50, n_shots=3, n_src=2, n_rec=5, seed=860, mu_range=(1.0, 1.0))
+    wl = inputs.as_f32(inputs.per_shot_models(base))
+    wl.cq = wl.cq.copy()
+    wl.cq[2, wl.ny // 2, wl.nx // 2] = np.float64(np.float32(wl.cq[2, wl.ny // 2, wl.nx // 2] * 0.75))
+    refs = [orc.misfit_and_gradient(_shot_workload(wl, s)) for s in range(wl.n_shots)]
+    resid = np.concatenate([ref["residual"] for ref in refs], axis=1)
+    got = run_gpu(wl, snap="f32", grad_r=resid)
+    for s, ref in enumerate(refs):
+        e_r = rel_l2(got["records"][:, s], ref["records"][:, 0])
+        e_g = max(rel_l2(got["gca_shot"][s], ref["gca_shot"][0]), rel_l2(got["gcb_shot"][s], ref["gcb_shot"][0]))
+        print(f"[per-shot uniform Cq but one cell, shot {s}] records {e_r:.2e}  grads {e_g:.2e}", flush=True)
+        assert e_r <= REC_TOL and e_g <= GRAD_TOL["f32"]
+
+
 @pytest.mark.parametrize("steps,ckpt,chunks", [(1, 0, None), (3, 0, None), (8, 0, [5, 50]), (3, 7, None),
                                                (5, 0, [33])])
 def test_event_blocks_bitwise(monkeypatch, steps, ckpt, chunks):

@@ -124,6 +124,21 @@ __global__ __launch_bounds__(256) void k_zero(float* __restrict__ p, int64_t n)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
+// Whether q[0, n) holds one value: info[0] must be 0 on entry and becomes
+// nonzero if the bits of any value differ from those of q[0]; info[1] gets
+// q[0]'s bits.  Every lane that finds a difference stores the same word.
+__global__ __launch_bounds__(256) void k_cq_uniform(const float* __restrict__ q, int64_t n,
+                                                    uint32_t* __restrict__ info)
+{
+    const uint32_t ref = __float_as_uint(q[0]);
+    bool diff = false;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step)
+        diff |= __float_as_uint(q[i]) != ref;
+    if (diff) info[0] = 1u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) info[1] = ref;
+}
+
 // Max of cb*cq over [0, n): per-block maxima into part[blockIdx.x].
 __global__ __launch_bounds__(256) void k_max_cbcq(const float* __restrict__ cb,
                                                   const float* __restrict__ cq, int64_t n,

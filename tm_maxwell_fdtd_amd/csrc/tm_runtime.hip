@@ -139,8 +139,9 @@ struct Layout {
 constexpr int HOST_RING = 3;
 
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
-enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_COUNT };
-const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2"};
+enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_COUNT };
+const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2",
+                                             "k_fwd_step2_uq"};
 
 struct TimedLaunch {
     int kid;
@@ -183,6 +184,10 @@ struct tm_plan {
     int fwd_cur = 0;                     // forward set holding the state at fwd_next
     bool stored_ok = false;
     bool fwd_complete = false;
+    // during a tm_forward call whose Courant check found Cq to hold one
+    // value: that value, read by the two-step forward instead of the array
+    bool cq_uniform = false;
+    float cq_value = 0.0f;
     // sampled kernel timing
     int timing_every = 0;
     std::vector<hipEvent_t> ev_free;
@@ -570,12 +575,20 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap
     a.ev = event_rows(p, q, false);
     a.es0 = event_step(p, false, t);
     a.es1 = event_step(p, false, t + 1);
+    a.cq = p->cq_value;
     const dim3 grid((unsigned)p->tiling_fwd2.nblk), blk(NT);
-    timed(p, KID_FWD_STEP2, t, st, [&] {
-        if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
-        else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
-        else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
-        else k_fwd_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
+    timed(p, p->cq_uniform ? KID_FWD_STEP2_UQ : KID_FWD_STEP2, t, st, [&] {
+        if (p->cq_uniform) {
+            if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32, true><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16, true><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8, true><<<grid, blk, 0, st>>>(a);
+            else k_fwd_step2<P, SNAP_NONE, true><<<grid, blk, 0, st>>>(a);
+        } else {
+            if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32, false><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16, false><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8, false><<<grid, blk, 0, st>>>(a);
+            else k_fwd_step2<P, SNAP_NONE, false><<<grid, blk, 0, st>>>(a);
+        }
     });
 }
 
@@ -697,7 +710,8 @@ tm_status device_tiling(tm_plan* p)
     if (v != TM_OK) return v;
     v = resident(pick(&k_adj_step<P, SNAP_F32>, &k_adj_step<P, SNAP_BF16>, &k_adj_step<P, SNAP_FP8>), &ca);
     if (v != TM_OK) return v;
-    v = resident(pick(&k_fwd_step2<P, SNAP_F32>, &k_fwd_step2<P, SNAP_BF16>, &k_fwd_step2<P, SNAP_FP8>), &c2);
+    v = resident(pick(&k_fwd_step2<P, SNAP_F32, false>, &k_fwd_step2<P, SNAP_BF16, false>,
+                      &k_fwd_step2<P, SNAP_FP8, false>), &c2);
     if (v != TM_OK) return v;
     int64_t ca2 = 0;
     v = resident(pick(&k_adj_step2<P, SNAP_F32>, &k_adj_step2<P, SNAP_BF16>, &k_adj_step2<P, SNAP_FP8>), &ca2);
@@ -915,14 +929,21 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
 
-tm_status courant_impl(tm_plan* p, void* ws, const float* cb, const float* cq, hipStream_t st, double* out)
+tm_status courant_impl(tm_plan* p, void* ws, const float* cb, const float* cq, hipStream_t st, double* out,
+                       bool* cq_one = nullptr, float* cq_val = nullptr)
 {
     const Ptrs q = pointers(p, ws);
     constexpr int NB = 256;
     const int64_t n = p->g.slab * (p->d.model_per_shot ? p->d.n_shots : 1);   // every shot's model
     k_max_cbcq<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, n, q.scratch);
     HIPCHK(hipGetLastError());
-    float part[NB];
+    // whether Cq holds one value (two words after the NB partial maxima)
+    uint32_t* info = reinterpret_cast<uint32_t*>(q.scratch + NB);
+    k_zero<<<dim3(1), dim3(64), 0, st>>>(q.scratch + NB, 2);
+    HIPCHK(hipGetLastError());
+    k_cq_uniform<<<dim3(NB), dim3(256), 0, st>>>(cq, n, info);
+    HIPCHK(hipGetLastError());
+    float part[NB + 2];
     HIPCHK(hipMemcpyAsync(part, q.scratch, sizeof(part), hipMemcpyDeviceToHost, st));
     HIPCHK(hipStreamSynchronize(st));
     double m = 0.0;
@@ -930,6 +951,10 @@ tm_status courant_impl(tm_plan* p, void* ws, const float* cb, const float* cq, h
         if (part[i] != part[i]) { m = NAN; break; }
         m = std::max(m, (double)part[i]);
     }
+    uint32_t w[2];
+    std::memcpy(w, part + NB, sizeof(w));
+    if (cq_one != nullptr) *cq_one = w[0] == 0u;
+    if (cq_val != nullptr) std::memcpy(cq_val, &w[1], sizeof(float));
     const double rdx = 1.0 / p->d.dx, rdy = 1.0 / p->d.dy;
     *out = std::sqrt(m) * abs_coef_sum(p->d.order) * std::sqrt(rdx * rdx + rdy * rdy);
     return TM_OK;
@@ -1153,9 +1178,11 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     if (t0 > 0 && (ws != p->ws_last || p->fwd_next != t0)) return TM_ESTATE;
     hipStream_t st = as_stream(stream);
     const bool store = (flags & TM_FWD_STORE) != 0;
+    bool cq_one = false;
+    float cq_val = 0.0f;
     if (flags & TM_FWD_CHECK) {
         double c = 0.0;
-        v = courant_impl(p, ws, cb, cq, st, &c);
+        v = courant_impl(p, ws, cb, cq, st, &c, &cq_one, &cq_val);
         if (v != TM_OK) return v;
         if (!(c <= 1.0)) return TM_EUNSTABLE;
     }
@@ -1172,11 +1199,14 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     }
     p->ws_last = ws;
     p->fwd_next = -1;
+    p->cq_uniform = cq_one;
+    p->cq_value = cq_val;
     switch (p->P) {
     case 1: v = run_forward<1>(p, ws, f, r, t0, t1, store, st); break;
     case 2: v = run_forward<2>(p, ws, f, r, t0, t1, store, st); break;
     default: v = run_forward<4>(p, ws, f, r, t0, t1, store, st); break;
     }
+    p->cq_uniform = false;            // the adjoint's replays read the array
     if (v != TM_OK) return v;
     p->fwd_next = t1;
     p->fwd_complete = (t1 == p->d.nt) && p->stored_ok;

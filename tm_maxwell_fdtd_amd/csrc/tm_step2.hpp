@@ -72,9 +72,14 @@ struct Fwd2Args {
     uint32_t snap_shot_bytes;
     EventRows ev;                      // sources (add) and receivers (out)
     EventStep es0, es1;                // ... of steps n and n+1
+    float cq;                          // Cq where it holds one value (UQ instances)
 };
 
-template <int P, int SNAP>
+// UQ: Cq holds one value in every cell (mu_r uniform, non-magnetic media),
+// so no Cq bytes are read: each Cq load becomes that value on the lanes and
+// rows where the load would have read a cell and 0 elsewhere, and the step
+// computes bitwise what it computes with the array.
+template <int P, int SNAP, bool UQ>
 __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
 {
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
@@ -178,6 +183,17 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
         return (y >= e_lo && y <= e_hi) ? __builtin_amdgcn_readfirstlane(evs[y - ye0]) : -1;
     };
 
+    // Cq of an H row: per-lane offset (negative where masked) + row offset,
+    // or a predicate + lane offset (general blocks)
+    auto cq_v = [&](int voff, uint32_t soff) {
+        if constexpr (UQ) return voff < 0 ? 0.0f : a.cq;
+        else return bm.ldv(voff, soff);
+    };
+    auto cq_p = [&](bool ok, uint32_t off) {
+        if constexpr (UQ) return ok ? a.cq : 0.0f;
+        else return bm.ld(ok, off, a.m.oCq);
+    };
+
     // Prefetch ring: the loads of iteration r are issued at iteration r - D
     // into slot (r - r_first) % D.
     float fE[D], fQa[D], fHx[D], fHz[D], fMyh[D], fMxh[D], fCa[D], fCb[D], fMxe[D], fMye[D];
@@ -198,7 +214,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                 fE[u] = b0.ldv(v_in, L.oE + (uint32_t)r * rowb);
                 fHx[u] = b0.ldv(v_e, L.oHx + rA);
             } else if constexpr (K == 2) {
-                fQa[u] = bm.ldv(v_in, a.m.oCq + rA);
+                fQa[u] = cq_v(v_in, a.m.oCq + rA);
                 fHz[u] = b0.ldv(v_hz, L.oHz + rA);
                 fMxh[u] = b0.ldv(xband ? v_mxh : RBuf::OOB, L.oMxh + (uint32_t)hA * brow);
             } else if constexpr (K == 3) {
@@ -207,7 +223,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                 fCb[u] = bm.ldv(v_e, a.m.oCb + eA);
                 fMxe[u] = b0.ldv(xband ? v_mxe : RBuf::OOB, L.oMxe + (uint32_t)yA * brow);
             } else if constexpr (K == 4) {
-                fQb[u] = bm.ldv(v_in, a.m.oCq + (uint32_t)hB * rowb);
+                fQb[u] = cq_v(v_in, a.m.oCq + (uint32_t)hB * rowb);
             } else {
                 fGB[u] = -1;
                 fCaB[u] = bm.ldv(v_own, a.m.oCa + (uint32_t)yB * rowb);
@@ -222,7 +238,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                 fHx[u] = b0.ld(hx_do, ohA, L.oHx);
                 fMyh[u] = b0.ld(hx_do & fy_h(hA), (uint32_t)(band_y(g, hA) * nx) * 4u + c4, L.oMyh);
             } else if constexpr (K == 2) {
-                fQa[u] = bm.ld(live & in_rows(hA) & incol, ohA, a.m.oCq);
+                fQa[u] = cq_p(live & in_rows(hA) & incol, ohA);
                 const bool hz_do = live & colHz & hz_row(hA) & (hA >= ye0) & (hA <= yb + 2 * P - 2);
                 fHz[u] = b0.ld(hz_do, ohA, L.oHz);
                 fMxh[u] = b0.ld(hz_do & fx_h, (uint32_t)(hA * g.bx) * 4u + bx4, L.oMxh);
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                 fMxe[u] = b0.ld(e_do & fx_e, (uint32_t)(yA * g.bx) * 4u + bx4, L.oMxe);
                 fMye[u] = b0.ld(e_do & fy_e(yA), (uint32_t)(band_y(g, yA) * nx) * 4u + c4, L.oMye);
             } else if constexpr (K == 4) {
-                fQb[u] = bm.ld(live & in_rows(hB) & incol & (hB >= ya - P), ohB, a.m.oCq);
+                fQb[u] = cq_p(live & in_rows(hB) & incol & (hB >= ya - P), ohB);
             } else {
                 const bool eb_do = live & own & own_row(yB);
                 const int gB = slot_of(yB);

@@ -383,19 +383,20 @@ def make_config(cfg: int, **over) -> Workload:
 
 def random_workload(order, n_int, npml, nt, n_shots, n_src, n_rec, seed, h=0.01,
                     freq=700e6, eps_range=(1.5, 9.0), sig_range=(0.0, 0.02),
-                    identity_pml=False, src_anywhere=False, nx_int=None):
+                    identity_pml=False, src_anywhere=False, nx_int=None, mu_range=(1.0, 2.0)):
     """A small heterogeneous workload for property tests.
 
     Models are random per cell (not smooth), several sources per shot at
     random interior cells (duplicates allowed), receivers at random cells,
     and random source amplitudes instead of a wavelet, so that every path
-    through the kernels is exercised.
+    through the kernels is exercised.  ``mu_range`` = (m, m) gives a
+    uniform mu_r = m (non-magnetic media for m = 1).
     """
     rng = np.random.default_rng(seed)
     shape = (n_int, n_int if nx_int is None else nx_int)   # rows x columns of the interior
     eps = rng.uniform(*eps_range, size=shape)
     sig = rng.uniform(*sig_range, size=shape)
-    mu = rng.uniform(1.0, 2.0, size=shape)
+    mu = rng.uniform(*mu_range, size=shape)
     wl = assemble(f"random{seed}", order, eps, sig, npml, h, nt, n_shots, n_rec, freq,
                   mu_int=mu)
     p = order // 2
