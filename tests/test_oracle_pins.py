@@ -364,6 +364,44 @@ def test_eps_sigma_partials_match_coefficient_differences(orc):
     assert np.all(dca_de[:4] == 0.0)
 
 
+def _golden(name):
+    import os
+
+    vals = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].split()
+            if len(line) == 2:
+                vals[line[0]] = float(line[1])
+    return vals
+
+
+def test_eps_sigma_partials_match_the_page_closed_forms(orc):
+    """The oracle's chain rule (written from eps = eps0 eps_r and
+    D = eps + sigma dt / 2) against the partials the page states in terms of
+    the coefficients themselves (tide-GPR 0.0.9, maxwell.cu,
+    convert_grad_ca_cb_to_eps_sigma): dCa/deps = (1 - Ca) Cb / dt,
+    dCb/deps = -Cb^2 / dt, dCa/dsigma = -(1 + Ca) Cb / 2,
+    dCb/dsigma = -Cb^2 / 2, with dJ/deps_r = eps0 dJ/deps and eps0 the
+    page's printed value (tests/golden/vacuum_permittivity.txt)."""
+    eps0 = _golden("vacuum_permittivity.txt")["eps0"]
+    assert inputs.EP0 == eps0
+    rng = np.random.default_rng(11)
+    n = 200
+    eps_r = rng.uniform(1.0, 30.0, n)
+    sigma = rng.uniform(0.0, 0.05, n)
+    sigma[:5] = 0.0
+    dt = 4.1e-12
+    ca, cb, _ = inputs.update_coefficients(eps_r, sigma, np.ones(n), dt)
+    ga = rng.standard_normal(n)
+    gb = rng.standard_normal(n)
+    ge, gs = orc.eps_sigma_grad(eps_r, sigma, dt, ga, gb)
+    page_e = eps0 * (ga * (1.0 - ca) * cb / dt - gb * cb * cb / dt)
+    page_s = ga * (-0.5 * (1.0 + ca) * cb) + gb * (-0.5 * cb * cb)
+    np.testing.assert_allclose(ge, page_e, rtol=1e-10, atol=1e-12 * np.abs(page_e).max())
+    np.testing.assert_allclose(gs, page_s, rtol=1e-10, atol=1e-12 * np.abs(page_s).max())
+
+
 @pytest.mark.parametrize("order", inputs.ORDERS)
 def test_eps_sigma_gradient_matches_central_differences(orc, order):
     """dJ/deps_r and dJ/dsigma of the full misfit against central differences
