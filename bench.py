@@ -93,8 +93,8 @@ def kernel_bytes(name, wl, store, snap_bytes):
     k_fwd_step2 / k_adj_step2 advance two time steps per launch: twice the
     bytes of k_fwd_step / k_adj_step (the per-cell-update figure times the
     cell-updates of the launch), although the state crosses HBM only once.
-    k_fwd_step2_uq is k_fwd_step2 where Cq holds one value and is not read:
-    32 B per cell instead of 36.
+    k_fwd_step2_uq / k_adj_step2_uq are the instances where Cq holds one
+    value and is not read: 32 B per cell instead of 36.
     """
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
@@ -106,11 +106,14 @@ def kernel_bytes(name, wl, store, snap_bytes):
         return 2 * kernel_bytes("k_fwd_step", wl, store, snap_bytes)
     if name == "k_fwd_step2_uq":
         return 2 * kernel_bytes("k_fwd_step_uq", wl, store, snap_bytes)
-    if name == "k_adj_step":
+    if name in ("k_adj_step", "k_adj_step_uq"):
         grads = (2 * snap_bytes + 16) * interior if store else 0
-        return S * (36 * cells + 16 * (band_y + band_x) + grads)
+        per_cell = 32 if name.endswith("_uq") else 36
+        return S * (per_cell * cells + 16 * (band_y + band_x) + grads)
     if name == "k_adj_step2":
         return 2 * kernel_bytes("k_adj_step", wl, store, snap_bytes)
+    if name == "k_adj_step2_uq":
+        return 2 * kernel_bytes("k_adj_step_uq", wl, store, snap_bytes)
     return None
 
 
@@ -297,15 +300,15 @@ def main():
     p = wl.order // 2
     launches_fwd = wl.nt
     kernels = {}
-    uq = results["step"][1].get("k_fwd_step2_uq", (0, 0))[1] > 0   # tm_forward read one Cq value
     for name, (ms, n) in results["step"][1].items():
         if n == 0:
             continue
         avg_ms = ms / n
         launches = wl.nt // 2 if name.startswith(("k_fwd_step2", "k_adj_step2")) else wl.nt
-        if name in ("k_fwd_step", "k_fwd_step2"):
-            # tm_forward (unless it ran the _uq instances) and the replays of the adjoint
-            launches *= (0 if uq else 1) + (1 if wl.ckpt_every else 0)
+        if name.startswith("k_fwd") and wl.ckpt_every:
+            # tm_forward and the replays of the adjoint (the samples mix both;
+            # the bytes below count the replays' snapshot stores for all)
+            launches *= 2
         # in a full step the forward stores snapshots and the adjoint accumulates gradients
         nbytes = kernel_bytes(name, wl, store=True, snap_bytes=snap_bytes)
         kernels[name] = dict(avg_us=avg_ms * 1e3, samples=n, est_total_s=avg_ms * launches / 1e3,

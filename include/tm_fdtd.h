@@ -171,7 +171,10 @@ tm_status tm_forward(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca
  * included) over all nt steps, after a storing tm_forward that reached nt on
  * the same workspace (else TM_ESTATE).  May be called repeatedly.
  *   ca, cb, cq, f: the same arrays as the forward (f is re-read by the
- *      segment replay of checkpoint mode).
+ *      segment replay of checkpoint mode; when the forward's TM_FWD_CHECK
+ *      found cq to hold one value and cq is the same pointer, the adjoint
+ *      steps and the replays use that value instead of reading the array,
+ *      with bitwise the same results).
  *   grad_r: device float32 [nt][S][n_rec], dJ/dr (required when n_rec > 0).
  *   grad_f: device float32 [nt][S][n_src], receives dJ/df (adjoint field at
  *      the sources); may be NULL.
@@ -248,9 +251,9 @@ tm_status tm_timing_enable(tm_plan* plan, int32_t every);
 tm_status tm_timing_read(tm_plan* plan, double* total_ms, int64_t* count);
 
 /* Number of timed kernels, and the name of kernel ``k`` (the prefix of its
- * symbol name as profilers print it, with "_uq" for the two-step forward
- * instances that read one Cq value instead of the array; NULL when k is out
- * of range). */
+ * symbol name as profilers print it, with "_uq" for the two-step instances
+ * that use one Cq value instead of reading the array; NULL when k is out of
+ * range). */
 int32_t tm_kernel_count(void);
 const char* tm_kernel_name(int32_t k);
 

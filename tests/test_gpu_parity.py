@@ -218,19 +218,26 @@ def test_uniform_cq_two_step_bitwise_equals_single_steps(order, snap, ckpt):
         np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} order {order} {snap} K={ckpt}")
 
 
-def test_uniform_cq_selects_the_cq_free_forward():
+def test_uniform_cq_selects_the_cq_free_instances():
     """With TM_FWD_CHECK a forward over a uniform Cq runs the instances that
-    read no Cq (timed as k_fwd_step2_uq); without the check, with a
-    non-uniform Cq, and in the adjoint's replays the array instances run."""
+    read no Cq (timed as k_fwd_step2_uq), and so do the adjoint
+    (k_adj_step2_uq) and its checkpoint replays given the same cq pointer;
+    without the check, with a non-uniform Cq, or with another cq pointer
+    (same values) for the adjoint, the array instances run."""
+    import torch
+
     from tm_maxwell_fdtd_amd import native
 
-    def counts(wl, check, ckpt_every=0):
+    def counts(wl, check, ckpt_every=0, other_cq=False):
         prop = native.Propagator(wl, ckpt_every=ckpt_every)
         try:
             native.tm_timing_enable(prop.plan, 1)
             r = prop.forward(store=True, check=check)
             _, fwd = native.tm_timing_read(prop.plan)
+            if other_cq:
+                prop.cq = prop.cq.clone()
             prop.adjoint(r)
+            torch.cuda.synchronize()
             _, adj = native.tm_timing_read(prop.plan)
             native.tm_timing_enable(prop.plan, 0)
         finally:
@@ -248,7 +255,16 @@ def test_uniform_cq_selects_the_cq_free_forward():
     assert fwd.get("k_fwd_step2", 0) > 0 and "k_fwd_step2_uq" not in fwd, fwd
     fwd, adj = counts(uni, check=True, ckpt_every=8)
     assert fwd.get("k_fwd_step2_uq", 0) > 0 and "k_fwd_step2" not in fwd, fwd
-    assert adj.get("k_fwd_step2", 0) > 0 and "k_fwd_step2_uq" not in adj, adj
+    assert adj.get("k_fwd_step2_uq", 0) > 0 and "k_fwd_step2" not in adj, adj
+    assert adj.get("k_adj_step2_uq", 0) > 0 and "k_adj_step2" not in adj, adj
+    _, adj = counts(uni, check=True)
+    assert adj.get("k_adj_step2_uq", 0) > 0 and "k_adj_step2" not in adj, adj
+    for kw in (dict(check=True, other_cq=True), dict(check=False)):
+        _, adj = counts(uni, ckpt_every=8, **kw)
+        assert adj.get("k_fwd_step2", 0) > 0 and "k_fwd_step2_uq" not in adj, (kw, adj)
+        assert adj.get("k_adj_step2", 0) > 0 and "k_adj_step2_uq" not in adj, (kw, adj)
+    _, adj = counts(het, check=True)
+    assert adj.get("k_adj_step2", 0) > 0 and "k_adj_step2_uq" not in adj, adj
 
 
 @pytest.mark.parametrize("where", ["first", "interior", "last-used"])

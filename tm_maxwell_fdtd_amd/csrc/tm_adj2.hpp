@@ -54,9 +54,13 @@ struct Adj2Args {
     float ratio;                       // weight of a stored step's gradient term
     EventRows ev;                      // residual at the receivers (add), sources (out)
     EventStep esA, esB;                // ... of steps n and n-1
+    float cq;                          // Cq where it holds one value (UQ instances)
 };
 
-template <int P, int SNAP>
+// UQ: Cq holds one value (mu_r uniform), passed as cq: no Cq bytes are read,
+// and each Cq load becomes that value where the load would have read a cell
+// (0 where it is masked), bitwise what the array gives.
+template <int P, int SNAP, bool UQ>
 __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
 {
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
@@ -162,6 +166,12 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
     };
     auto ctab = [&](int y) { return cyt[y - yt]; };
 
+    // Cq of an H row: lane offset (negative where masked) + row offset
+    auto cq_v = [&](int voff, uint32_t soff) {
+        if constexpr (UQ) return voff < 0 ? 0.0f : a.cq;
+        else return bm.ldv(voff, soff);
+    };
+
     // Prefetch ring: the loads of iteration r are issued at iteration r - D.
     // FAST: every row the iteration touches is active, owned, inside the
     // index sets, off the y bands and free of events (see the block test
@@ -202,11 +212,11 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
         }
         if constexpr (PART == 2) {
             const uint32_t ohA = G(hA) * rowb;
-            fQA[u] = bm.ldv(v_e | M(liveA & (hx_row(hA) | hzA_row(hA))), a.m.oCq + ohA);
+            fQA[u] = cq_v(v_e | M(liveA & (hx_row(hA) | hzA_row(hA))), a.m.oCq + ohA);
             const int mzA = M(liveA & hzA_row(hA));
             fHz[u] = b0.ldv(v_hz | mzA, L.oHz + ohA);
             fMxh[u] = b0.ldv(xband ? (v_hzxh | mzA) : RBuf::OOB, L.oMxh + G(hA) * brow);
-            fQB[u] = bm.ldv(v_e | M(liveB & (hx_row(hB) | own_row(hB))), a.m.oCq + G(hB) * rowb);
+            fQB[u] = cq_v(v_e | M(liveB & (hx_row(hB) | own_row(hB))), a.m.oCq + G(hB) * rowb);
             return;
         }
         if constexpr (FAST) {

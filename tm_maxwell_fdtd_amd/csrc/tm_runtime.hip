@@ -139,9 +139,11 @@ struct Layout {
 constexpr int HOST_RING = 3;
 
 // Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
-enum KernelId { KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_COUNT };
+enum KernelId {
+    KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_ADJ_STEP2_UQ, KID_COUNT
+};
 const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2",
-                                             "k_fwd_step2_uq"};
+                                             "k_fwd_step2_uq", "k_adj_step2_uq"};
 
 struct TimedLaunch {
     int kid;
@@ -188,6 +190,12 @@ struct tm_plan {
     // value: that value, read by the two-step forward instead of the array
     bool cq_uniform = false;
     float cq_value = 0.0f;
+    // what the checks of the storing forward found: every chunk's Cq held
+    // the one value fwd_cq_val, at the pointer fwd_cq (the replays of the
+    // adjoint, which take the same arrays, then read no Cq either)
+    const float* fwd_cq = nullptr;
+    bool fwd_cq_one = false;
+    float fwd_cq_val = 0.0f;
     // sampled kernel timing
     int timing_every = 0;
     std::vector<hipEvent_t> ev_free;
@@ -651,12 +659,21 @@ void adj_step2(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const 
     a.ev = event_rows(p, q, true);
     a.esA = event_step(p, true, t);
     a.esB = event_step(p, true, t - 1);
+    a.cq = p->cq_value;
     const dim3 grid((unsigned)p->tiling_adj2.nblk), blk(NT);
-    timed(p, KID_ADJ_STEP2, t - 1, st, [&] {             // sampled like the forward pairs (even step)
-        if (snap == SNAP_F32) k_adj_step2<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
-        else if (snap == SNAP_BF16) k_adj_step2<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
-        else if (snap == SNAP_FP8) k_adj_step2<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
-        else k_adj_step2<P, SNAP_NONE><<<grid, blk, 0, st>>>(a);
+    // sampled like the forward pairs (even step)
+    timed(p, p->cq_uniform ? KID_ADJ_STEP2_UQ : KID_ADJ_STEP2, t - 1, st, [&] {
+        if (p->cq_uniform) {
+            if (snap == SNAP_F32) k_adj_step2<P, SNAP_F32, true><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_BF16) k_adj_step2<P, SNAP_BF16, true><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_FP8) k_adj_step2<P, SNAP_FP8, true><<<grid, blk, 0, st>>>(a);
+            else k_adj_step2<P, SNAP_NONE, true><<<grid, blk, 0, st>>>(a);
+        } else {
+            if (snap == SNAP_F32) k_adj_step2<P, SNAP_F32, false><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_BF16) k_adj_step2<P, SNAP_BF16, false><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_FP8) k_adj_step2<P, SNAP_FP8, false><<<grid, blk, 0, st>>>(a);
+            else k_adj_step2<P, SNAP_NONE, false><<<grid, blk, 0, st>>>(a);
+        }
     });
 }
 
@@ -714,7 +731,8 @@ tm_status device_tiling(tm_plan* p)
                       &k_fwd_step2<P, SNAP_FP8, false>), &c2);
     if (v != TM_OK) return v;
     int64_t ca2 = 0;
-    v = resident(pick(&k_adj_step2<P, SNAP_F32>, &k_adj_step2<P, SNAP_BF16>, &k_adj_step2<P, SNAP_FP8>), &ca2);
+    v = resident(pick(&k_adj_step2<P, SNAP_F32, false>, &k_adj_step2<P, SNAP_BF16, false>,
+                      &k_adj_step2<P, SNAP_FP8, false>), &ca2);
     if (v != TM_OK) return v;
     // halo_iters: row iterations of a chunk beyond its owned rows
     p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W, CH_MAX, ncu, 2 * P - 1);
@@ -1199,6 +1217,14 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     }
     p->ws_last = ws;
     p->fwd_next = -1;
+    if (t0 == 0) {
+        p->fwd_cq = cq;
+        p->fwd_cq_one = cq_one;
+        p->fwd_cq_val = cq_val;
+    } else {
+        p->fwd_cq_one = p->fwd_cq_one && cq_one && cq == p->fwd_cq &&
+                        std::memcmp(&cq_val, &p->fwd_cq_val, sizeof(float)) == 0;
+    }
     p->cq_uniform = cq_one;
     p->cq_value = cq_val;
     switch (p->P) {
@@ -1234,11 +1260,16 @@ TM_API tm_status tm_adjoint(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     const uint64_t gbytes = (uint64_t)p->d.n_shots * (uint64_t)p->g.slab * 4;
     if (grad_ca_shot && (v = zero(grad_ca_shot, gbytes, st)) != TM_OK) return v;
     if (grad_cb_shot && (v = zero(grad_cb_shot, gbytes, st)) != TM_OK) return v;
+    // the adjoint steps and the checkpoint replays take the arrays of the
+    // storing forward: its check's finding holds for them
+    p->cq_uniform = p->fwd_cq_one && cq == p->fwd_cq;
+    p->cq_value = p->fwd_cq_val;
     switch (p->P) {
     case 1: v = run_adjoint<1>(p, ws, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
     case 2: v = run_adjoint<2>(p, ws, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
     default: v = run_adjoint<4>(p, ws, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
     }
+    p->cq_uniform = false;
     if (v != TM_OK) return v;
     if (p->K > 0 && want_grad) p->fwd_next = -1;   // the replay overwrote the forward state
     return TM_OK;
