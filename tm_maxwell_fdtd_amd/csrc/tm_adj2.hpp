@@ -166,12 +166,6 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
     };
     auto ctab = [&](int y) { return cyt[y - yt]; };
 
-    // Cq of an H row: lane offset (negative where masked) + row offset
-    auto cq_v = [&](int voff, uint32_t soff) {
-        if constexpr (UQ) return voff < 0 ? 0.0f : a.cq;
-        else return bm.ldv(voff, soff);
-    };
-
     // Prefetch ring: the loads of iteration r are issued at iteration r - D.
     // FAST: every row the iteration touches is active, owned, inside the
     // index sets, off the y bands and free of events (see the block test
@@ -212,11 +206,21 @@ __global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
         }
         if constexpr (PART == 2) {
             const uint32_t ohA = G(hA) * rowb;
-            fQA[u] = cq_v(v_e | M(liveA & (hx_row(hA) | hzA_row(hA))), a.m.oCq + ohA);
+            if constexpr (UQ) {
+                const int qo = v_e | M(liveA & (hx_row(hA) | hzA_row(hA)));
+                fQA[u] = qo < 0 ? 0.0f : a.cq;
+            } else {
+                fQA[u] = bm.ldv(v_e | M(liveA & (hx_row(hA) | hzA_row(hA))), a.m.oCq + ohA);
+            }
             const int mzA = M(liveA & hzA_row(hA));
             fHz[u] = b0.ldv(v_hz | mzA, L.oHz + ohA);
             fMxh[u] = b0.ldv(xband ? (v_hzxh | mzA) : RBuf::OOB, L.oMxh + G(hA) * brow);
-            fQB[u] = cq_v(v_e | M(liveB & (hx_row(hB) | own_row(hB))), a.m.oCq + G(hB) * rowb);
+            if constexpr (UQ) {
+                const int qo = v_e | M(liveB & (hx_row(hB) | own_row(hB)));
+                fQB[u] = qo < 0 ? 0.0f : a.cq;
+            } else {
+                fQB[u] = bm.ldv(v_e | M(liveB & (hx_row(hB) | own_row(hB))), a.m.oCq + G(hB) * rowb);
+            }
             return;
         }
         if constexpr (FAST) {
