@@ -61,7 +61,7 @@ struct Adj2Args {
 // and each Cq load becomes that value where the load would have read a cell
 // (0 where it is masked), bitwise what the array gives.
 template <int P, int SNAP, bool UQ>
-__global__ __launch_bounds__(NT, 3) void k_adj_step2(Adj2Args a)
+__global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
 {
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH_A2;
