@@ -44,11 +44,9 @@ struct Adj2Args {
     const float* __restrict__ cp;
     const char* __restrict__ set0;     // adjoint state after step n+1
     char* __restrict__ set1;           // adjoint state after step n-1
-    const char* __restrict__ snap_eA;  // Ey^n, curl H^n [S][nyi][nxi], or null (step n not stored)
-    const char* __restrict__ snap_cA;
-    const char* __restrict__ snap_eB;  // Ey^{n-1}, curl H^{n-1}, or null
-    const char* __restrict__ snap_cB;
-    uint32_t snap_shot_bytes;
+    const char* __restrict__ snapA;    // (Ey^n, curl H^n) pairs [S][nyi][nxi][2], or null (step n not stored)
+    const char* __restrict__ snapB;    // (Ey^{n-1}, curl H^{n-1}) pairs, or null
+    uint32_t snap_shot_bytes;          // bytes of one shot's pairs
     float* __restrict__ gca;           // per-shot gradients [S][ny][nx], or null
     float* __restrict__ gcb;
     float ratio;                       // weight of a stored step's gradient term
@@ -130,11 +128,10 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
-    const uint32_t sbA = (SNAP != SNAP_NONE && a.snap_eA != nullptr) ? a.snap_shot_bytes : 0u;
-    const uint32_t sbB = (SNAP != SNAP_NONE && a.snap_eB != nullptr) ? a.snap_shot_bytes : 0u;
+    const uint32_t sbA = (SNAP != SNAP_NONE && a.snapA != nullptr) ? a.snap_shot_bytes : 0u;
+    const uint32_t sbB = (SNAP != SNAP_NONE && a.snapB != nullptr) ? a.snap_shot_bytes : 0u;
     const int64_t so_s = (int64_t)s * a.snap_shot_bytes;
-    const RBuf bseA(sbA ? a.snap_eA + so_s : nullptr, sbA), bscA(sbA ? a.snap_cA + so_s : nullptr, sbA);
-    const RBuf bseB(sbB ? a.snap_eB + so_s : nullptr, sbB), bscB(sbB ? a.snap_cB + so_s : nullptr, sbB);
+    const RBuf bspA(sbA ? a.snapA + so_s : nullptr, sbA), bspB(sbB ? a.snapB + so_s : nullptr, sbB);
     const uint32_t slab_b = (uint32_t)(g.slab * 4);
     const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
     const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
@@ -156,11 +153,11 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
         asm volatile("" : "+v"(o));
         return v | (o & RBuf::OOB);
     };
-    const int v_g = lane_off(grad, c4), v_gs = lane_off(grad, (uint32_t)(c - g.x0) * ESZ);
+    const int v_g = lane_off(grad, c4), v_gs = lane_off(grad, (uint32_t)(c - g.x0) * 2u * ESZ);
     auto msk = [](bool ok) { return ok ? 0 : RBuf::OOB; };
     auto grow = [&](int y) { return (uint32_t)min(max(y, 0), ny - 1); };
     auto brw = [&](int y) { return (uint32_t)min(max(band_y(g, y), 0), g.by - 1); };
-    auto srw = [&](int y) { return (uint32_t)min(max(y - g.y0, 0), g.nyi - 1) * (uint32_t)g.nxi * ESZ; };
+    auto srw = [&](int y) { return (uint32_t)min(max(y - g.y0, 0), g.nyi - 1) * (uint32_t)g.nxi * 2u * ESZ; };
     auto slot_of = [&](int y) {
         return (y >= e_lo && y <= e_hi) ? __builtin_amdgcn_readfirstlane(evs[y - yt]) : -1;
     };
@@ -193,11 +190,13 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
         if constexpr (PART == 3) {
             const uint32_t orB = G(rB) * rowb;
             const int mg = M(liveB & own_row(rB) & (rB >= g.y0) & (rB < g.y1));
-            const uint32_t sr = FAST ? (uint32_t)(rB - g.y0) * (uint32_t)g.nxi * ESZ : srw(rB);
-            fSeA[u] = snap_getv<SNAP>(bseA, v_gs | mg, sr);
-            fScA[u] = snap_getv<SNAP>(bscA, v_gs | mg, sr);
-            fSeB[u] = snap_getv<SNAP>(bseB, v_gs | mg, sr);
-            fScB[u] = snap_getv<SNAP>(bscB, v_gs | mg, sr);
+            const uint32_t sr = FAST ? (uint32_t)(rB - g.y0) * (uint32_t)g.nxi * 2u * ESZ : srw(rB);
+            const SnapPair pA = snap_get2v<SNAP>(bspA, v_gs | mg, sr);
+            const SnapPair pB = snap_get2v<SNAP>(bspB, v_gs | mg, sr);
+            fSeA[u] = pA.e;
+            fScA[u] = pA.c;
+            fSeB[u] = pB.e;
+            fScB[u] = pB.c;
             fGa[u] = bga.ldv(v_g | mg, orB);
             fGb[u] = bgb.ldv(v_g | mg, orB);
             fCaA[u] = bm.ldv(v_eA | M(liveA & (yA >= Ya) & (yA < Yb) & e_row(yA)), a.m.oCa + G(yA) * rowb);

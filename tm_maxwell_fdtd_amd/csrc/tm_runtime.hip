@@ -123,8 +123,8 @@ struct Layout {
     uint64_t set_bytes = 0;                       // S blocks
     uint64_t fwd = 0, fwd_bytes = 0, fset[2] = {0, 0};
     uint64_t adj = 0, adj_bytes = 0, aset[2] = {0, 0};
-    uint64_t snapE = 0, snapC = 0, snap_step = 0; // per-step bytes of one snapshot array (all shots)
-    uint64_t snap_stride = 0;                     // bytes per stored step: its Ey then its curl H
+    uint64_t snap = 0;                            // stored steps: (Ey, curl H) pairs [S][nyi][nxi][2] each
+    uint64_t snap_stride = 0;                     // bytes per stored step (all shots)
     uint64_t snap_shot = 0;                       // ... of one shot
     uint64_t ckpt = 0, ckpt_slot = 0;
     uint64_t ev_row = 0;                          // bytes of one step's event rows [NS][nx]
@@ -170,7 +170,7 @@ struct tm_plan {
     // a pinned host store reached through a ring of device slots
     int64_t R = 1, n_store = 0;
     int storage = TM_STORE_DEVICE;
-    char* host_store = nullptr;          // pinned [n_store][E | C][S][nyi][nxi]
+    char* host_store = nullptr;          // pinned [n_store][S][nyi][nxi][2] (Ey, curl H pairs)
     uint64_t host_bytes = 0;
     hipStream_t copy_stream = nullptr;
     hipEvent_t slot_copied[HOST_RING] = {};   // last copy into / out of the slot finished
@@ -266,13 +266,11 @@ bool make_layout(tm_plan* p)
     L.aset[1] = take(L.set_bytes);
     L.adj_bytes = o - L.adj;
     const uint64_t esz = d.snap == TM_SNAP_BF16 ? 2 : d.snap == TM_SNAP_FP8 ? 1 : 4;
-    L.snap_shot = (uint64_t)g.nyi * (uint64_t)g.nxi * esz;
-    L.snap_step = align_up(S * L.snap_shot);
+    L.snap_shot = (uint64_t)g.nyi * (uint64_t)g.nxi * 2 * esz;
     const uint64_t dev_steps = p->storage == TM_STORE_HOST ? (uint64_t)HOST_RING
                              : p->K > 0 ? (uint64_t)p->seg_steps : (uint64_t)p->n_store;
-    L.snap_stride = 2 * L.snap_step;
-    L.snapE = take(L.snap_stride * dev_steps);
-    L.snapC = L.snapE + L.snap_step;
+    L.snap_stride = align_up(S * L.snap_shot);
+    L.snap = take(L.snap_stride * dev_steps);
     L.ckpt_slot = L.set_bytes;
     L.ckpt = take(L.ckpt_slot * (uint64_t)p->n_ckpt);
     L.ev_row = (uint64_t)p->NS * (uint64_t)g.nx * 4;
@@ -425,7 +423,7 @@ struct Ptrs {
     Model model;
     const int32_t *row_slot, *colcell, *slot_shot, *cell_src, *src_list, *cell_rec, *rec_list, *src_pos, *rec_pos;
     float *ev_fadd, *ev_fout, *ev_aadd, *ev_aout;
-    char *snapE, *snapC, *ckpt;
+    char *snap, *ckpt;
     float* scratch;
 };
 
@@ -443,8 +441,7 @@ Ptrs pointers(const tm_plan* p, void* ws)
     q.src_pos = t + p->t_spos; q.rec_pos = t + p->t_rpos;
     q.ev_fadd = wsp<float>(ws, L.ev_fadd); q.ev_fout = wsp<float>(ws, L.ev_fout);
     q.ev_aadd = wsp<float>(ws, L.ev_aadd); q.ev_aout = wsp<float>(ws, L.ev_aout);
-    q.snapE = wsp<char>(ws, L.snapE);
-    q.snapC = wsp<char>(ws, L.snapC);
+    q.snap = wsp<char>(ws, L.snap);
     q.ckpt = wsp<char>(ws, L.ckpt);
     q.scratch = wsp<float>(ws, L.scratch);
     return q;
@@ -495,14 +492,14 @@ tm_status slot_release(tm_plan* p, int i, hipStream_t st)
 // slot's last kernel; the next kernel using the slot waits for it.
 tm_status slot_copy(tm_plan* p, const Ptrs& q, int i, int64_t j, bool to_host)
 {
-    const uint64_t n = p->lay.snap_step;
+    const uint64_t n = p->lay.snap_stride;
     hipStream_t cs = p->copy_stream;
     if (p->slot_kernel_pending[i]) HIPCHK(hipStreamWaitEvent(cs, p->slot_done[i], 0));
     p->slot_kernel_pending[i] = false;
-    char* he = p->host_store + (uint64_t)j * 2 * n;      // [E | C] of stored step j
-    char* de = q.snapE + (uint64_t)i * p->lay.snap_stride; // the slot: E then C
-    if (to_host) HIPCHK(hipMemcpyAsync(he, de, 2 * n, hipMemcpyDeviceToHost, cs));
-    else HIPCHK(hipMemcpyAsync(de, he, 2 * n, hipMemcpyHostToDevice, cs));
+    char* he = p->host_store + (uint64_t)j * n;          // the pairs of stored step j
+    char* de = q.snap + (uint64_t)i * n;                 // the slot
+    if (to_host) HIPCHK(hipMemcpyAsync(he, de, n, hipMemcpyDeviceToHost, cs));
+    else HIPCHK(hipMemcpyAsync(de, he, n, hipMemcpyHostToDevice, cs));
     HIPCHK(hipEventRecord(p->slot_copied[i], cs));
     p->slot_copy_pending[i] = true;
     return TM_OK;
@@ -533,8 +530,7 @@ EventStep event_step(const tm_plan* p, bool adjoint, int64_t t)
 // sources and receivers and the snapshot epilogue (se/sc non-null) in one
 // kernel.
 template <int P>
-void fwd_step(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap, char* se, char* sc,
-              hipStream_t st)
+void fwd_step(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap, char* sp, hipStream_t st)
 {
     const Layout& L = p->lay;
     FwdArgs a;
@@ -545,8 +541,7 @@ void fwd_step(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap,
     a.cp = q.cp;
     a.set0 = q.base + L.fset[cur];
     a.set1 = q.base + L.fset[1 - cur];
-    a.snap_e = se;
-    a.snap_c = sc;
+    a.snap = sp;
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
     a.ev = event_rows(p, q, false);
     a.es = event_step(p, false, t);
@@ -560,11 +555,11 @@ void fwd_step(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap,
 }
 
 // Forward steps t and t+1 in one launch (set cur -> 1-cur), with the
-// sources and receivers of both.  se0/sc0, se1/sc1: snapshot destinations
-// of steps t and t+1, or null.
+// sources and receivers of both.  sp0, sp1: snapshot destinations of
+// steps t and t+1, or null.
 template <int P>
-void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap, char* se0, char* sc0,
-               char* se1, char* sc1, hipStream_t st)
+void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap, char* sp0, char* sp1,
+               hipStream_t st)
 {
     const Layout& L = p->lay;
     Fwd2Args a;
@@ -575,10 +570,8 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap
     a.cp = q.cp;
     a.set0 = q.base + L.fset[cur];
     a.set1 = q.base + L.fset[1 - cur];
-    a.snap_e0 = se0;
-    a.snap_c0 = sc0;
-    a.snap_e1 = se1;
-    a.snap_c1 = sc1;
+    a.snap0 = sp0;
+    a.snap1 = sp1;
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
     a.ev = event_rows(p, q, false);
     a.es0 = event_step(p, false, t);
@@ -604,8 +597,8 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap
 // E updates, source-wavelet gradient and parameter-gradient accumulation in
 // one kernel); k counts the adjoint launches (set k%2 -> (k+1)%2).
 template <int P>
-void adj_step(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const char* se,
-              const char* sc, float* gca, float* gcb, hipStream_t st)
+void adj_step(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const char* sp, float* gca,
+              float* gcb, hipStream_t st)
 {
     const Layout& L = p->lay;
     AdjArgs a;
@@ -616,8 +609,7 @@ void adj_step(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const c
     a.cp = q.cp;
     a.set0 = q.base + L.aset[k & 1];
     a.set1 = q.base + L.aset[(k + 1) & 1];
-    a.snap_e = se;
-    a.snap_c = sc;
+    a.snap = sp;
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
     a.gca = gca;
     a.gcb = gcb;
@@ -634,10 +626,10 @@ void adj_step(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const c
 }
 
 // Adjoint steps t and t-1 in one launch (set k%2 -> (k+1)%2, k counting
-// launches); seA/scA, seB/scB: the snapshots of steps t and t-1, or null.
+// launches); spA, spB: the snapshots of steps t and t-1, or null.
 template <int P>
-void adj_step2(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const char* seA, const char* scA,
-               const char* seB, const char* scB, float* gca, float* gcb, hipStream_t st)
+void adj_step2(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const char* spA, const char* spB,
+               float* gca, float* gcb, hipStream_t st)
 {
     const Layout& L = p->lay;
     Adj2Args a;
@@ -648,10 +640,8 @@ void adj_step2(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const 
     a.cp = q.cp;
     a.set0 = q.base + L.aset[k & 1];
     a.set1 = q.base + L.aset[(k + 1) & 1];
-    a.snap_eA = seA;
-    a.snap_cA = scA;
-    a.snap_eB = seB;
-    a.snap_cB = scB;
+    a.snapA = spA;
+    a.snapB = spB;
     a.snap_shot_bytes = (uint32_t)L.snap_shot;
     a.gca = gca;
     a.gcb = gcb;
@@ -778,7 +768,7 @@ tm_status events_gather(const tm_plan* p, const Ptrs& q, bool adjoint, float* ou
 
 // Forward steps [t0, t1) from set *cur (updated).  snap: SNAP_* kind of the
 // stored steps (the multiples of R), whose device destinations
-// snap_at(t, se, sc) gives; host: copy every stored step to the host store
+// snap_at(t) gives; host: copy every stored step to the host store
 // through its ring slot; ckpt: save the state at every multiple of K into
 // the checkpoint slots.
 template <int P, typename SnapAt>
@@ -803,11 +793,11 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
         // two steps per launch unless step t+1 starts a checkpoint interval
         const bool pair = p->time_block == 2 && t + 1 < ev_b && !(ckpt && (t + 1) % p->K == 0);
         const int nstep = pair ? 2 : 1;
-        char *se[2] = {nullptr, nullptr}, *sc[2] = {nullptr, nullptr};
+        char* sp[2] = {nullptr, nullptr};
         bool any = false;
         for (int i = 0; i < nstep; ++i) {
             if (!stored(t + i)) continue;
-            snap_at(t + i, se[i], sc[i]);
+            sp[i] = snap_at(t + i);
             if (host) {
                 tm_status v = slot_acquire(p, (int)dev_slot(p, t + i), st);
                 if (v != TM_OK) return v;
@@ -815,8 +805,8 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
             any = true;
         }
         const int kind = any ? snap : SNAP_NONE;
-        if (pair) fwd_step2<P>(p, q, *cur, r, t, kind, se[0], sc[0], se[1], sc[1], st);
-        else fwd_step<P>(p, q, *cur, r, t, kind, se[0], sc[0], st);
+        if (pair) fwd_step2<P>(p, q, *cur, r, t, kind, sp[0], sp[1], st);
+        else fwd_step<P>(p, q, *cur, r, t, kind, sp[0], st);
         for (int i = 0; host && i < nstep; ++i) {
             if (!stored(t + i)) continue;
             const int slot = (int)dev_slot(p, t + i);
@@ -847,10 +837,7 @@ tm_status run_forward(tm_plan* p, void* ws, const float* f, float* r, int64_t t0
     const int snap = (store && full) ? snap_kind(p) : SNAP_NONE;
     const bool host = snap != SNAP_NONE && p->storage == TM_STORE_HOST;
     if (host && (v = host_setup(p)) != TM_OK) return v;
-    auto at = [&](int64_t t, char*& se, char*& sc) {
-        se = q.snapE + dev_slot(p, t) * p->lay.snap_stride;
-        sc = q.snapC + dev_slot(p, t) * p->lay.snap_stride;
-    };
+    auto at = [&](int64_t t) { return q.snap + dev_slot(p, t) * p->lay.snap_stride; };
     return forward_range<P>(p, q, &p->fwd_cur, f, r, t0, t1, snap, at, store && !full, host, st);
 }
 
@@ -891,9 +878,8 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
                 const bool uA = want_grad && t % p->R == 0, uB = want_grad && (t - 1) % p->R == 0;
                 const uint64_t oA = (uint64_t)(uA ? dev_slot(p, t) : 0) * p->lay.snap_stride;
                 const uint64_t oB = (uint64_t)(uB ? dev_slot(p, t - 1) : 0) * p->lay.snap_stride;
-                adj_step2<P>(p, q, t, k, (uA || uB) ? snap : SNAP_NONE, uA ? q.snapE + oA : nullptr,
-                             uA ? q.snapC + oA : nullptr, uB ? q.snapE + oB : nullptr, uB ? q.snapC + oB : nullptr,
-                             gca, gcb, st);
+                adj_step2<P>(p, q, t, k, (uA || uB) ? snap : SNAP_NONE, uA ? q.snap + oA : nullptr,
+                             uB ? q.snap + oB : nullptr, gca, gcb, st);
                 t -= 2;
                 continue;
             }
@@ -901,8 +887,7 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             const int64_t slot = use ? dev_slot(p, t) : 0;
             if (use && host && (v = slot_acquire(p, (int)slot, st)) != TM_OK) return v;
             const uint64_t so = (uint64_t)slot * p->lay.snap_stride;
-            adj_step<P>(p, q, t, k, use ? snap : SNAP_NONE, use ? q.snapE + so : nullptr,
-                        use ? q.snapC + so : nullptr, gca, gcb, st);
+            adj_step<P>(p, q, t, k, use ? snap : SNAP_NONE, use ? q.snap + so : nullptr, gca, gcb, st);
             if (use && host) {
                 if ((v = slot_release(p, (int)slot, st)) != TM_OK) return v;
                 const int64_t jn = t / p->R - HOST_RING;   // the stored step that reuses this slot
@@ -922,22 +907,17 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
                                       p->lay.ckpt_slot, hipMemcpyDeviceToDevice, st));
             }
             int cur = 0;
-            auto at = [&](int64_t t, char*& se, char*& sc) {
-                se = q.snapE + (t - ta) * p->lay.snap_stride;
-                sc = q.snapC + (t - ta) * p->lay.snap_stride;
-            };
+            auto at = [&](int64_t t) { return q.snap + (t - ta) * p->lay.snap_stride; };
             v = forward_range<P>(p, q, &cur, f, nullptr, ta, tb, snap, at, false, false, st);
             if (v != TM_OK) return v;
             for (int64_t t = tb - 1; t >= ta; ++k) {
                 if ((v = events(t)) != TM_OK) return v;
-                const char* se = q.snapE + (t - ta) * p->lay.snap_stride;
-                const char* sc = q.snapC + (t - ta) * p->lay.snap_stride;
+                const char* sp = q.snap + (t - ta) * p->lay.snap_stride;
                 if (p->time_block == 2 && t - 1 >= ta && t - 1 >= ev_a) {
-                    adj_step2<P>(p, q, t, k, snap, se, sc, se - p->lay.snap_stride, sc - p->lay.snap_stride, gca,
-                                 gcb, st);
+                    adj_step2<P>(p, q, t, k, snap, sp, sp - p->lay.snap_stride, gca, gcb, st);
                     t -= 2;
                 } else {
-                    adj_step<P>(p, q, t, k, snap, se, sc, gca, gcb, st);
+                    adj_step<P>(p, q, t, k, snap, sp, gca, gcb, st);
                     --t;
                 }
             }
@@ -1099,7 +1079,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         delete p;
         return TM_EINVAL;
     }
-    if (p->storage == TM_STORE_HOST) p->host_bytes = (uint64_t)p->n_store * 2 * p->lay.snap_step;
+    if (p->storage == TM_STORE_HOST) p->host_bytes = (uint64_t)p->n_store * p->lay.snap_stride;
     if (d.hbm_budget > 0 && p->lay.total > d.hbm_budget) {
         delete p;
         return TM_ENOMEM;

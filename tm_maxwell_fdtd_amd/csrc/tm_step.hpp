@@ -158,14 +158,6 @@ struct RBuf {
     {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, ok ? (int)off : OOB, (int)base, 0);
     }
-    __device__ __forceinline__ float ld_bf16(bool ok, uint32_t off) const
-    {
-        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, ok ? (int)off : OOB, 0, 0));
-    }
-    __device__ __forceinline__ void st_bf16(bool ok, float v, uint32_t off) const
-    {
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, ok ? (int)off : OOB, 0, 0);
-    }
     // per-lane offset `voff` (already OOB where masked), uniform offset `soff`
     __device__ __forceinline__ float ldv(int voff, uint32_t soff) const
     {
@@ -175,65 +167,66 @@ struct RBuf {
     {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, (int)soff, 0);
     }
-    __device__ __forceinline__ void stv_bf16(float v, int voff, uint32_t soff) const
-    {
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, (int)soff, 0);
-    }
-    __device__ __forceinline__ float ldv_bf16(int voff, uint32_t soff) const
-    {
-        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff, (int)soff, 0));
-    }
-    __device__ __forceinline__ float ldv_fp8(int voff, uint32_t soff) const
-    {
-        return e4m3_to_f32(__builtin_amdgcn_raw_buffer_load_b8(r, voff, (int)soff, 0));
-    }
-    __device__ __forceinline__ float ld_fp8(bool ok, uint32_t off) const
-    {
-        return e4m3_to_f32(__builtin_amdgcn_raw_buffer_load_b8(r, ok ? (int)off : OOB, 0, 0));
-    }
-    __device__ __forceinline__ void stv_fp8(float v, int voff, uint32_t soff) const
-    {
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)f32_to_e4m3(v), r, voff, (int)soff, 0);
-    }
 };
 
 // Lane offset, or the out-of-range offset where the lane is masked.
 __device__ __forceinline__ int lane_off(bool ok, uint32_t off) { return ok ? (int)off : RBuf::OOB; }
 
-// Snapshot element access (f32 or bf16), element index w.
+// Snapshot pairs.  A stored step keeps Ey^n and curl H^n of each interior
+// cell side by side ([Ey, curl H] per cell, twice the element size), so one
+// access of 2, 4 or 8 bytes moves both values of a cell: [S][nyi][nxi][2]
+// per stored step.  Masked lanes (offset out of range) store nothing and
+// read (0, 0).
+struct SnapPair {
+    float e, c;
+};
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
 template <int SNAP>
-__device__ __forceinline__ void snap_put(const RBuf& b, bool ok, uint32_t w, float v)
+constexpr uint32_t pair_bytes() { return 2u * snap_bytes<SNAP>(); }
+
+// Store with a lane offset (bytes, out of range where masked) and a uniform
+// row offset.
+template <int SNAP>
+__device__ __forceinline__ void snap_put2v(const RBuf& b, float e, float c, int voff, uint32_t soff)
 {
-    if constexpr (SNAP == SNAP_F32) b.st(ok, v, w * 4u, 0u);
-    else if constexpr (SNAP == SNAP_BF16) b.st_bf16(ok, v, w * 2u);
-    else if constexpr (SNAP == SNAP_FP8) b.stv_fp8(v, lane_off(ok, w), 0u);
+    if constexpr (SNAP == SNAP_F32) {
+        const u32x2_t v = {__float_as_uint(e), __float_as_uint(c)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, b.r, voff, (int)soff, 0);
+    } else if constexpr (SNAP == SNAP_BF16) {
+        const uint32_t v = (uint32_t)f32_to_bf16(e) | ((uint32_t)f32_to_bf16(c) << 16);
+        __builtin_amdgcn_raw_buffer_store_b32(v, b.r, voff, (int)soff, 0);
+    } else if constexpr (SNAP == SNAP_FP8) {
+        const uint32_t v = f32_to_e4m3(e) | (f32_to_e4m3(c) << 8);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, b.r, voff, (int)soff, 0);
+    }
 }
 template <int SNAP>
-__device__ __forceinline__ float snap_get(const RBuf& b, bool ok, uint32_t w)
+__device__ __forceinline__ SnapPair snap_get2v(const RBuf& b, int voff, uint32_t soff)
 {
-    if constexpr (SNAP == SNAP_F32) return b.ld(ok, w * 4u, 0u);
-    else if constexpr (SNAP == SNAP_BF16) return b.ld_bf16(ok, w * 2u);
-    else if constexpr (SNAP == SNAP_FP8) return b.ld_fp8(ok, w);
-    else return 0.0f;
+    if constexpr (SNAP == SNAP_F32) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(b.r, voff, (int)soff, 0);
+        return SnapPair{__uint_as_float(v.x), __uint_as_float(v.y)};
+    } else if constexpr (SNAP == SNAP_BF16) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(b.r, voff, (int)soff, 0);
+        return SnapPair{__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u)};
+    } else if constexpr (SNAP == SNAP_FP8) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(b.r, voff, (int)soff, 0);
+        return SnapPair{e4m3_to_f32(v & 0xffu), e4m3_to_f32(v >> 8)};
+    } else {
+        return SnapPair{0.0f, 0.0f};
+    }
 }
-// Load with a precomputed lane offset (bytes, out of range where masked) and
-// a uniform row offset.
+// ... with a predicate and the pair index w of the cell
 template <int SNAP>
-__device__ __forceinline__ float snap_getv(const RBuf& b, int voff, uint32_t soff)
+__device__ __forceinline__ void snap_put2(const RBuf& b, bool ok, uint32_t w, float e, float c)
 {
-    if constexpr (SNAP == SNAP_F32) return b.ldv(voff, soff);
-    else if constexpr (SNAP == SNAP_BF16) return b.ldv_bf16(voff, soff);
-    else if constexpr (SNAP == SNAP_FP8) return b.ldv_fp8(voff, soff);
-    else return 0.0f;
+    snap_put2v<SNAP>(b, e, c, lane_off(ok, w * pair_bytes<SNAP>()), 0u);
 }
-// Store with a precomputed lane offset (bytes, out of range where masked)
-// and a uniform row offset.
 template <int SNAP>
-__device__ __forceinline__ void snap_putv(const RBuf& b, float v, int voff, uint32_t soff)
+__device__ __forceinline__ SnapPair snap_get2(const RBuf& b, bool ok, uint32_t w)
 {
-    if constexpr (SNAP == SNAP_F32) b.stv(v, voff, soff);
-    else if constexpr (SNAP == SNAP_BF16) b.stv_bf16(v, voff, soff);
-    else if constexpr (SNAP == SNAP_FP8) b.stv_fp8(v, voff, soff);
+    return snap_get2v<SNAP>(b, lane_off(ok, w * pair_bytes<SNAP>()), 0u);
 }
 
 // Layout of one shot's state block (byte offsets of the sub-arrays).
@@ -307,9 +300,8 @@ struct FwdArgs {
     const float* __restrict__ cp;      // CPML table [12][L]
     const char* __restrict__ set0;     // state at step n, shot-major blocks
     char* __restrict__ set1;           // state at step n+1
-    char* __restrict__ snap_e;         // Ey^n on the interior window [S][nyi][nxi], or null
-    char* __restrict__ snap_c;         // curl H^n
-    uint32_t snap_shot_bytes;
+    char* __restrict__ snap;           // (Ey^n, curl H^n) pairs on the interior window [S][nyi][nxi][2], or null
+    uint32_t snap_shot_bytes;          // bytes of one shot's pairs
     EventRows ev;                      // sources (add) and receivers (out)
     EventStep es;                      // ... of this step
 };
@@ -371,8 +363,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
     const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
-    const RBuf bse(a.snap_e + (int64_t)s * a.snap_shot_bytes, SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u);
-    const RBuf bsc(a.snap_c + (int64_t)s * a.snap_shot_bytes, SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u);
+    const RBuf bsp(a.snap + (int64_t)s * a.snap_shot_bytes, SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u);
     const RBuf bev(a.ev.base, a.ev.bytes);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
 
@@ -495,8 +486,7 @@ __global__ __launch_bounds__(NT) void k_fwd_step(FwdArgs a)
                 if constexpr (SNAP != SNAP_NONE) {
                     if (y >= g.y0 && y < g.y1) {
                         const uint32_t w = (uint32_t)((y - g.y0) * g.nxi + (c - g.x0));
-                        snap_put<SNAP>(bse, own && in_x, w, ev);
-                        snap_put<SNAP>(bsc, own && in_x, w, curl);
+                        snap_put2<SNAP>(bsp, own && in_x, w, ev, curl);
                     }
                 }
                 float en = fmaf(fCa[u], ev, fCb[u] * curl);
@@ -523,9 +513,8 @@ struct AdjArgs {
     const float* __restrict__ cp;
     const char* __restrict__ set0;     // adjoint state after step n+1
     char* __restrict__ set1;           // adjoint state after step n
-    const char* __restrict__ snap_e;   // Ey^n, curl H^n of this step [S][nyi][nxi], or null
-    const char* __restrict__ snap_c;
-    uint32_t snap_shot_bytes;
+    const char* __restrict__ snap;     // (Ey^n, curl H^n) pairs of this step [S][nyi][nxi][2], or null
+    uint32_t snap_shot_bytes;          // bytes of one shot's pairs
     float* __restrict__ gca;           // per-shot gradients [S][ny][nx], or null
     float* __restrict__ gcb;
     float ratio;                       // weight of this step's gradient term (the snapshot step ratio)
@@ -595,8 +584,7 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
     constexpr uint32_t ESZ = snap_bytes<SNAP>();
     const uint32_t ssb = SNAP != SNAP_NONE ? a.snap_shot_bytes : 0u;
-    const RBuf bse(a.snap_e + (int64_t)s * a.snap_shot_bytes, ssb);
-    const RBuf bsc(a.snap_c + (int64_t)s * a.snap_shot_bytes, ssb);
+    const RBuf bsp(a.snap + (int64_t)s * a.snap_shot_bytes, ssb);
     const uint32_t slab_b = (uint32_t)(g.slab * 4);
     const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
     const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
@@ -613,11 +601,11 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
     const int v_hz = lane_off(hz_col, c4), v_ownhz = lane_off(own && hz_col, c4);
     const int v_xe = lane_off(fx_e, bx4), v_ownxe = lane_off(own && fx_e, bx4);
     const int v_hzxh = lane_off(hz_col && fx_h, bx4), v_ownhzxh = lane_off(own && hz_col && fx_h, bx4);
-    const int v_g = lane_off(grad, c4), v_gs = lane_off(grad, (uint32_t)(c - g.x0) * ESZ);
+    const int v_g = lane_off(grad, c4), v_gs = lane_off(grad, (uint32_t)(c - g.x0) * 2u * ESZ);
     auto msk = [](bool ok) { return ok ? 0 : RBuf::OOB; };
     auto grow = [&](int y) { return (uint32_t)min(max(y, 0), ny - 1); };                // grid row
     auto brw = [&](int y) { return (uint32_t)min(max(band_y(g, y), 0), g.by - 1); };    // y-band row
-    auto srw = [&](int y) { return (uint32_t)min(max(y - g.y0, 0), g.nyi - 1) * (uint32_t)g.nxi * ESZ; };
+    auto srw = [&](int y) { return (uint32_t)min(max(y - g.y0, 0), g.nyi - 1) * (uint32_t)g.nxi * 2u * ESZ; };
     // slot of window row r, or -1 (uniform)
     auto slot_of = [&](int r) {
         return (r >= e_lo && r <= e_hi) ? __builtin_amdgcn_readfirstlane(evs[r - ya + T0]) : -1;
@@ -640,8 +628,9 @@ __global__ __launch_bounds__(NT) void k_adj_step(AdjArgs a)
         fMxe[u] = b0.ldv(v_xe | me, L.oMxe + grow(r) * brow);
         fMye[u] = b0.ldv(v_e | me | msk(fy_e(r)), L.oMye + brw(r) * rowb);
         const int mg = msk(live && r >= ya && r < yb && r >= g.y0 && r < g.y1);
-        fSe[u] = snap_getv<SNAP>(bse, v_gs | mg, srw(r));
-        fSc[u] = snap_getv<SNAP>(bsc, v_gs | mg, srw(r));
+        const SnapPair sp = snap_get2v<SNAP>(bsp, v_gs | mg, srw(r));
+        fSe[u] = sp.e;
+        fSc[u] = sp.c;
         fGa[u] = bga.ldv(v_g | mg, orr);
         fGb[u] = bgb.ldv(v_g | mg, orr);
         const int mh = msk(live && hx_row(h));

@@ -65,11 +65,9 @@ struct Fwd2Args {
     const float* __restrict__ cp;      // CPML table [12][L]
     const char* __restrict__ set0;     // state at step n
     char* __restrict__ set1;           // state at step n+2
-    char* __restrict__ snap_e0;        // Ey^n, curl H^n [S][nyi][nxi], or null (step n not stored)
-    char* __restrict__ snap_c0;
-    char* __restrict__ snap_e1;        // Ey^{n+1}, curl H^{n+1}, or null
-    char* __restrict__ snap_c1;
-    uint32_t snap_shot_bytes;
+    char* __restrict__ snap0;          // (Ey^n, curl H^n) pairs [S][nyi][nxi][2], or null (step n not stored)
+    char* __restrict__ snap1;          // (Ey^{n+1}, curl H^{n+1}) pairs, or null
+    uint32_t snap_shot_bytes;          // bytes of one shot's pairs
     EventRows ev;                      // sources (add) and receivers (out)
     EventStep es0, es1;                // ... of steps n and n+1
     float cq;                          // Cq where it holds one value (UQ instances)
@@ -153,13 +151,11 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
     const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
     const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
     // a stage whose step is not stored gets null destinations: empty views
-    const uint32_t sb0 = (SNAP != SNAP_NONE && a.snap_e0 != nullptr) ? a.snap_shot_bytes : 0u;
-    const uint32_t sb1 = (SNAP != SNAP_NONE && a.snap_e1 != nullptr) ? a.snap_shot_bytes : 0u;
+    const uint32_t sb0 = (SNAP != SNAP_NONE && a.snap0 != nullptr) ? a.snap_shot_bytes : 0u;
+    const uint32_t sb1 = (SNAP != SNAP_NONE && a.snap1 != nullptr) ? a.snap_shot_bytes : 0u;
     const int64_t so_s = (int64_t)s * a.snap_shot_bytes;
-    const RBuf bse0(sb0 ? a.snap_e0 + so_s : nullptr, sb0);
-    const RBuf bsc0(sb0 ? a.snap_c0 + so_s : nullptr, sb0);
-    const RBuf bse1(sb1 ? a.snap_e1 + so_s : nullptr, sb1);
-    const RBuf bsc1(sb1 ? a.snap_c1 + so_s : nullptr, sb1);
+    const RBuf bsp0(sb0 ? a.snap0 + so_s : nullptr, sb0);
+    const RBuf bsp1(sb1 ? a.snap1 + so_s : nullptr, sb1);
     const RBuf bev(a.ev.base, a.ev.bytes);
     const uint32_t c4 = (uint32_t)c * 4u, bx4 = (uint32_t)bxc * 4u;
     const uint32_t rowb = (uint32_t)nx * 4u, brow = (uint32_t)g.bx * 4u;
@@ -168,7 +164,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
     const int v_in = lane_off(incol, c4), v_e = lane_off(colE, c4), v_hz = lane_off(colHz, c4);
     const int v_own = lane_off(own, c4), v_ownhz = lane_off(own & colHz, c4);
     const int v_mxh = lane_off(colHz & fx_h, bx4), v_mxe = lane_off(colE & fx_e, bx4);
-    const int v_snap = lane_off(own & in_x, (uint32_t)(c - g.x0) * ESZ);
+    const int v_snap = lane_off(own & in_x, (uint32_t)(c - g.x0) * 2u * ESZ);
 
     const int r_first = ya - 2 * P + 1;
     const int r_end = yb + 4 * P - 3;
@@ -378,13 +374,11 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             const float ev = ewA[0];
             if constexpr (SNAP != SNAP_NONE) {
                 if constexpr (FAST) {
-                    const uint32_t so = (uint32_t)((yA - g.y0) * g.nxi) * ESZ;
-                    snap_putv<SNAP>(bse0, ev, v_snap, so);
-                    snap_putv<SNAP>(bsc0, curl, v_snap, so);
+                    const uint32_t so = (uint32_t)((yA - g.y0) * g.nxi) * 2u * ESZ;
+                    snap_put2v<SNAP>(bsp0, ev, curl, v_snap, so);
                 } else if ((yA >= g.y0) & (yA < g.y1) & own_row(yA)) {
                     const uint32_t w = (uint32_t)((yA - g.y0) * g.nxi + (c - g.x0));
-                    snap_put<SNAP>(bse0, own & in_x, w, ev);
-                    snap_put<SNAP>(bsc0, own & in_x, w, curl);
+                    snap_put2<SNAP>(bsp0, own & in_x, w, ev, curl);
                 }
             }
             float en = fmaf(fCa[u], ev, fCb[u] * curl);
@@ -443,13 +437,11 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             const float ev = ewB[0];
             if constexpr (SNAP != SNAP_NONE) {
                 if constexpr (FAST) {
-                    const uint32_t so = (uint32_t)((yB - g.y0) * g.nxi) * ESZ;
-                    snap_putv<SNAP>(bse1, ev, v_snap, so);
-                    snap_putv<SNAP>(bsc1, curl, v_snap, so);
+                    const uint32_t so = (uint32_t)((yB - g.y0) * g.nxi) * 2u * ESZ;
+                    snap_put2v<SNAP>(bsp1, ev, curl, v_snap, so);
                 } else if ((yB >= g.y0) & (yB < g.y1)) {
                     const uint32_t w = (uint32_t)((yB - g.y0) * g.nxi + (c - g.x0));
-                    snap_put<SNAP>(bse1, own & in_x, w, ev);
-                    snap_put<SNAP>(bsc1, own & in_x, w, curl);
+                    snap_put2<SNAP>(bsp1, own & in_x, w, ev, curl);
                 }
             }
             float en = fmaf(fCaB[u], ev, fCbB[u] * curl);
