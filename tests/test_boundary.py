@@ -42,6 +42,14 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_timed_kernel_names():
+    """The timing ids name the step kernels; _uq marks the instances that
+    use one Cq value instead of reading the array."""
+    names = [native.tm_kernel_name(k) for k in range(native.tm_kernel_count())]
+    assert names == ["k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2", "k_fwd_step2_uq", "k_adj_step2_uq"]
+    assert native.tm_kernel_name(-1) is None and native.tm_kernel_name(len(names)) is None
+
+
 def test_status_strings_distinct():
     s = [native.status_string(i) for i in range(7)]
     assert len(set(s)) == 7 and all(s)
