@@ -131,3 +131,20 @@ def run_gpu_window(wl, t_window=None):
         del prop
         torch.cuda.empty_cache()
     return out
+
+
+def shot_block_bytes(n, npml, order):
+    """Bytes of one shot's state block on an n x n padded grid: Ey, Hx, Hz
+    and the y- and x-band memories of both updates, each 256-byte aligned."""
+    al = lambda v: (v + 255) // 256 * 256
+    p = order // 2
+    band = (p + npml) + (n - (n - p - npml) + 1)      # rows below y0 and from y1-1 on
+    return 3 * al(n * n * 4) + 2 * al(band * n * 4) + 2 * al(n * band * 4)
+
+
+def largest_square_grid(order, npml):
+    """The largest n whose shot block fits one buffer view (2^31 - 256 bytes)."""
+    n = 1024
+    while shot_block_bytes(n + 1, npml, order) <= (1 << 31) - 256:
+        n += 1
+    return n

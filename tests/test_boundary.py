@@ -9,6 +9,8 @@ import pytest
 
 from tm_maxwell_fdtd_amd import inputs, native
 
+from gpu_util import largest_square_grid
+
 FAKE_WS = 1 << 20          # an aligned address never dereferenced by these calls
 
 
@@ -140,6 +142,20 @@ def test_memory_budget(wl):
     native.tm_plan_destroy(plan)
     assert create(wl, hbm_budget=need) == native.TM_OK
     assert create(wl, hbm_budget=need - 1) == native.TM_ENOMEM
+
+
+def test_largest_grid_one_buffer_view():
+    """A shot's state block must fit one buffer view (2^31 - 256 bytes): the
+    largest square grid is accepted, one more row and column is not."""
+    order, npml = 4, 8
+    n = largest_square_grid(order, npml)
+    for size, want in ((n, native.TM_OK), (n + 1, native.TM_EINVAL)):
+        w = inputs.homogeneous_workload(order, size, size, npml, 2, (size // 2, size // 2), [(size // 2, size // 2 + 3)],
+                                        seed=1)
+        st, plan = native.tm_plan_create(native.make_desc(w), w.cpml, w.src, w.rec)
+        if plan:
+            native.tm_plan_destroy(plan)
+        assert st == want, (size, st)
 
 
 def test_null_arguments():

@@ -112,3 +112,58 @@ def test_checkpoint_intervals(orc, k):
         np.testing.assert_array_equal(ck[key], full[key], err_msg=f"K={k} {key}")
     ref = run_oracle(orc, wl)
     assert rel_l2(ck["gca_shot"], ref["gca_shot"]) <= GRAD_TOL
+
+
+def _run_windowed(wl, grad_r, centre, half):
+    """Records, and the per-shot gradients on the window centre +- half
+    together with their nonzero counts over the whole grid (so nothing is
+    copied back at full size)."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    prop = native.Propagator(wl)
+    try:
+        r = prop.forward(store=True)
+        resid = torch.as_tensor(np.asarray(grad_r, np.float32), device=prop.device)
+        grad_f, gca, gcb = prop.adjoint(resid)
+        win = (slice(centre[0] - half, centre[0] + half + 1), slice(centre[1] - half, centre[1] + half + 1))
+        out = dict(records=r.cpu().numpy(), grad_f=grad_f.cpu().numpy(),
+                   gca=gca[0][win].cpu().numpy(), gcb=gcb[0][win].cpu().numpy(),
+                   nnz_a=int(torch.count_nonzero(gca[0])), nnz_b=int(torch.count_nonzero(gcb[0])))
+        torch.cuda.synchronize()
+    finally:
+        prop.close()
+    return out
+
+
+def test_largest_grid_matches_a_small_one(orc):
+    """The largest square grid one buffer view allows (order 4), with the
+    source 40 cells from its far corner: in a homogeneous lossless medium
+    the records and gradients of 6 steps equal bitwise those of the same
+    source and receivers on an 80 x 80 grid (the fields reach at most 24
+    cells), which match the oracle; the gradients are zero outside the
+    window.  This runs every offset and buffer view at its largest."""
+    from gpu_util import largest_square_grid
+
+    order, npml, nt, half = 4, 8, 6, 30
+    n = largest_square_grid(order, npml)
+    offs = [(0, 4), (-3, 0), (5, -2), (2, 7), (-6, -6)]
+    big_c, small_c = (n - 40, n - 40), (40, 40)
+    big = inputs.homogeneous_workload(order, n, n, npml, nt, big_c, [(big_c[0] + a, big_c[1] + b) for a, b in offs],
+                                      seed=910)
+    small = inputs.homogeneous_workload(order, 80, 80, npml, nt, small_c,
+                                        [(small_c[0] + a, small_c[1] + b) for a, b in offs], seed=910)
+    print(f"[largest grid] {n} x {n}", flush=True)
+    ref = run_oracle(orc, small)
+    got_s = _run_windowed(small, ref["residual"], small_c, half)
+    got_b = _run_windowed(big, ref["residual"], big_c, half)
+    e_r = rel_l2(got_b["records"], ref["records"])
+    e_a = rel_l2(got_b["gca"], ref["gca_shot"][0][10:71, 10:71])
+    e_b = rel_l2(got_b["gcb"], ref["gcb_shot"][0][10:71, 10:71])
+    print(f"[largest grid] records {e_r:.2e}  gCa {e_a:.2e}  gCb {e_b:.2e}", flush=True)
+    assert e_r <= REC_TOL and e_a <= GRAD_TOL and e_b <= GRAD_TOL
+    for key in ("records", "grad_f", "gca", "gcb"):
+        np.testing.assert_array_equal(got_b[key], got_s[key], err_msg=key)
+    assert got_b["nnz_a"] == np.count_nonzero(got_b["gca"]) > 0
+    assert got_b["nnz_b"] == np.count_nonzero(got_b["gcb"]) > 0

@@ -415,6 +415,33 @@ def random_workload(order, n_int, npml, nt, n_shots, n_src, n_rec, seed, h=0.01,
     return wl
 
 
+def homogeneous_workload(order, ny, nx, npml, nt, src_yx, rec_yx, seed, eps_r=4.0, h=0.01):
+    """One shot in a homogeneous lossless medium with an identity CPML
+    profile, sized ny x nx (padded), with one source at ``src_yx`` and
+    receivers at the cells ``rec_yx``, random source amplitudes.
+
+    The coefficient arrays are float32 (float32-exact values), so grids
+    close to the largest allowed size stay cheap to build; ``eps_r``,
+    ``sigma`` and ``mu_r`` are 1x1 placeholders.  Its field after nt steps
+    is a translate of the same problem on any grid that keeps the source
+    and receivers more than 2 * P * nt cells from the halo.
+    """
+    rng = np.random.default_rng(seed)
+    p = order // 2
+    dt = stable_dt(eps_r, 1.0, h, h, order)
+    ca, cb, cq = update_coefficients(np.array([eps_r]), np.array([0.0]), np.array([1.0]), dt)
+    full = lambda v: np.full((ny, nx), np.float32(v[0]), dtype=np.float32)
+    f = rng.standard_normal((nt, 1, 1)).astype(np.float32).astype(np.float64)
+    src = np.array([[src_yx[0] * nx + src_yx[1]]], dtype=np.int64)
+    rec = np.array([[y * nx + x for (y, x) in rec_yx]], dtype=np.int64)
+    one = np.ones((1, 1))
+    return Workload(name=f"homogeneous{ny}x{nx}", order=order, n_shots=1, ny=ny, nx=nx,
+                    pml_y0=p + npml, pml_y1=ny - p - npml, pml_x0=p + npml, pml_x1=nx - p - npml,
+                    dy=h, dx=h, dt=dt, nt=nt, eps_r=one * eps_r, sigma=one * 0.0, mu_r=one,
+                    ca=full(ca), cb=full(cb), cq=full(cq), cpml=identity_cpml(ny, nx), f=f, src=src, rec=rec,
+                    freq=0.0)
+
+
 def per_shot_models(wl: Workload, spread: float = 0.25) -> Workload:
     """The same problem with one model per shot (batched models): shot s's
     permittivity is the workload's times 1 + spread * s / (S - 1), which only
