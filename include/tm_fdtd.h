@@ -32,6 +32,10 @@
  * memories, the snapshot store (or checkpoints and a replay segment) and
  * small tables.  A plan owns host memory only.  Every call is asynchronous
  * on ``stream`` (a hipStream_t; NULL = the null stream) unless stated.
+ * A plan also holds the state of a forward/adjoint sequence (the step the
+ * forward reached, which workspace it used, what its checks found), so
+ * calls on one plan must not run concurrently from several host threads;
+ * separate plans are independent.
  *
  * Errors: argument errors are detected on the host before any launch and
  * returned as a tm_status; nothing is printed and nothing aborts.
