@@ -218,6 +218,23 @@ def test_uniform_cq_two_step_bitwise_equals_single_steps(order, snap, ckpt):
         np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} order {order} {snap} K={ckpt}")
 
 
+@pytest.mark.parametrize("snap", ["f32", "bf16"])
+def test_uniform_cq_host_storage_and_step_ratio_bitwise(snap):
+    """mu_r one value: the Cq-free instances with snapshots in pinned host
+    memory equal the device store bitwise, and with a snapshot step ratio of
+    2 two steps per launch equal one step per launch bitwise."""
+    wl = inputs.as_f32(inputs.random_workload(8, 48, 8, nt=41, n_shots=2, n_src=2, n_rec=5, seed=870,
+                                              src_anywhere=True, mu_range=(1.0, 1.0)))
+    dev = run_gpu(wl, snap=snap)
+    host = run_gpu(wl, snap=snap, storage=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(host[key], dev[key], err_msg=f"host store {snap} {key}")
+    one = run_gpu(wl, snap=snap, step_ratio=2, time_block=1)
+    two = run_gpu(wl, snap=snap, step_ratio=2, time_block=2)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(two[key], one[key], err_msg=f"step ratio 2 {snap} {key}")
+
+
 def test_uniform_cq_selects_the_cq_free_instances():
     """With TM_FWD_CHECK a forward over a uniform Cq runs the instances that
     read no Cq (timed as k_fwd_step2_uq), and so do the adjoint
