@@ -321,6 +321,23 @@ def test_per_shot_models_uniform_cq_except_one_shot(orc):
         assert e_r <= REC_TOL and e_g <= GRAD_TOL["f32"]
 
 
+@pytest.mark.parametrize("npml,n_int", [(9, 300), (30, 60), (9, 40)])
+def test_order8_forward_fifo_layouts_bitwise(npml, n_int):
+    """Order 8: the two-step forward keeps stage A's x-band memories in
+    compact FIFOs when every strip has at most 56 x-band lanes (one band of
+    13 lanes per strip at 9 CPML cells and 316 columns; both bands, 26 lanes,
+    in one strip at 40 interior columns) and in full FIFOs otherwise (both
+    bands, 69 lanes, at 30 CPML cells and 128 columns).  Both give bitwise
+    the results of one step per launch."""
+    wl = inputs.as_f32(inputs.random_workload(8, 40, npml, nt=37, n_shots=2, n_src=2, n_rec=5, seed=880 + npml,
+                                              src_anywhere=True, nx_int=n_int, mu_range=(1.0, 1.0)))
+    for snap in ("bf16", "f32"):
+        one = run_gpu(wl, snap=snap, time_block=1)
+        two = run_gpu(wl, snap=snap, time_block=2)
+        for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+            np.testing.assert_array_equal(two[key], one[key], err_msg=f"{key} npml {npml} nx_int {n_int} {snap}")
+
+
 @pytest.mark.parametrize("steps,ckpt,chunks", [(1, 0, None), (3, 0, None), (8, 0, [5, 50]), (3, 7, None),
                                                (5, 0, [33])])
 def test_event_blocks_bitwise(monkeypatch, steps, ckpt, chunks):

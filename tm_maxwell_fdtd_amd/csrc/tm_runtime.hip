@@ -190,6 +190,9 @@ struct tm_plan {
     // value: that value, read by the two-step forward instead of the array
     bool cq_uniform = false;
     float cq_value = 0.0f;
+    // order 8: every strip's x-band lanes fit the compact FIFOs of the
+    // two-step forward (then its four-workgroup instances run)
+    bool fwd_cx = false;
     // what the checks of the storing forward found: every chunk's Cq held
     // the one value fwd_cq_val, at the pointer fwd_cq (the replays of the
     // adjoint, which take the same arrays, then read no Cq either)
@@ -579,17 +582,24 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap
     a.cq = p->cq_value;
     const dim3 grid((unsigned)p->tiling_fwd2.nblk), blk(NT);
     timed(p, p->cq_uniform ? KID_FWD_STEP2_UQ : KID_FWD_STEP2, t, st, [&] {
-        if (p->cq_uniform) {
-            if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32, true><<<grid, blk, 0, st>>>(a);
-            else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16, true><<<grid, blk, 0, st>>>(a);
-            else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8, true><<<grid, blk, 0, st>>>(a);
-            else k_fwd_step2<P, SNAP_NONE, true><<<grid, blk, 0, st>>>(a);
-        } else {
-            if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32, false><<<grid, blk, 0, st>>>(a);
-            else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16, false><<<grid, blk, 0, st>>>(a);
-            else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8, false><<<grid, blk, 0, st>>>(a);
-            else k_fwd_step2<P, SNAP_NONE, false><<<grid, blk, 0, st>>>(a);
+        auto launch = [&](auto uq_t, auto cx_t) {
+            constexpr bool UQ = decltype(uq_t)::value, CX = decltype(cx_t)::value;
+            if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32, UQ, CX><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_BF16) k_fwd_step2<P, SNAP_BF16, UQ, CX><<<grid, blk, 0, st>>>(a);
+            else if (snap == SNAP_FP8) k_fwd_step2<P, SNAP_FP8, UQ, CX><<<grid, blk, 0, st>>>(a);
+            else k_fwd_step2<P, SNAP_NONE, UQ, CX><<<grid, blk, 0, st>>>(a);
+        };
+        using T = std::true_type;
+        using F = std::false_type;
+        if constexpr (P == 4) {
+            if (p->fwd_cx) {
+                if (p->cq_uniform) launch(T{}, T{});
+                else launch(F{}, T{});
+                return;
+            }
         }
+        if (p->cq_uniform) launch(T{}, F{});
+        else launch(F{}, F{});
     });
 }
 
@@ -698,6 +708,21 @@ tm_status resident(const void* fn, int64_t* cap, int64_t* ncu_out = nullptr)
     return TM_OK;
 }
 
+// Whether the x-band lanes of every strip of the two-step forward (strip
+// width W) fit its compact FIFOs: the lanes with c < x0 or c >= hx1 inside
+// the grid, counted as the kernel numbers them.
+bool compact_xfifo_fits(const Geo& g, int P, int W, int nstrip)
+{
+    for (int st = 0; st < nstrip; ++st) {
+        const int c0 = P + st * W - (4 * P - 2);
+        const int cl = std::max(c0, 0), cr = std::max(g.hx1, c0);
+        const int nl = std::max(0, std::min(g.x0, c0 + NT) - cl);
+        const int nr = std::max(0, std::min(g.nx, c0 + NT) - cr);
+        if (nl + nr > XFIFO_W) return false;
+    }
+    return true;
+}
+
 // Make the tilings for the current device (once per device).
 template <int P>
 tm_status device_tiling(tm_plan* p)
@@ -717,8 +742,17 @@ tm_status device_tiling(tm_plan* p)
     if (v != TM_OK) return v;
     v = resident(pick(&k_adj_step<P, SNAP_F32>, &k_adj_step<P, SNAP_BF16>, &k_adj_step<P, SNAP_FP8>), &ca);
     if (v != TM_OK) return v;
-    v = resident(pick(&k_fwd_step2<P, SNAP_F32, false>, &k_fwd_step2<P, SNAP_BF16, false>,
-                      &k_fwd_step2<P, SNAP_FP8, false>), &c2);
+    if constexpr (P == 4) {
+        if (p->fwd_cx)
+            v = resident(pick(&k_fwd_step2<P, SNAP_F32, false, true>, &k_fwd_step2<P, SNAP_BF16, false, true>,
+                              &k_fwd_step2<P, SNAP_FP8, false, true>), &c2);
+        else
+            v = resident(pick(&k_fwd_step2<P, SNAP_F32, false, false>, &k_fwd_step2<P, SNAP_BF16, false, false>,
+                              &k_fwd_step2<P, SNAP_FP8, false, false>), &c2);
+    } else {
+        v = resident(pick(&k_fwd_step2<P, SNAP_F32, false, false>, &k_fwd_step2<P, SNAP_BF16, false, false>,
+                          &k_fwd_step2<P, SNAP_FP8, false, false>), &c2);
+    }
     if (v != TM_OK) return v;
     int64_t ca2 = 0;
     v = resident(pick(&k_adj_step2<P, SNAP_F32, false>, &k_adj_step2<P, SNAP_BF16, false>,
@@ -1074,6 +1108,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     }
     p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024, NT - 4 * P + 2);
     p->tiling_fwd2 = make_tiling(d, P, 1024, NT - 8 * P + 4, CH2_MAX);
+    p->fwd_cx = P == 4 && compact_xfifo_fits(p->g, P, NT - 8 * P + 4, p->tiling_fwd2.nstrip);
     p->tiling_adj2 = make_tiling(d, P, 1024, NT - 8 * P + 4, CHA2_MAX);
     if (!make_layout(p)) {
         delete p;

@@ -50,6 +50,8 @@ namespace tmf {
 constexpr int CH2_MAX = 128;   // largest chunk height of the two-step kernel (LDS tables)
 constexpr int PREFETCH_F2 = 1; // rows of loads in flight ahead
 constexpr int UNROLL_F2 = 4;   // row-loop unroll, a multiple of PREFETCH_F2
+constexpr int UNROLL_F2_CX = 2; // ... of the compact-FIFO instances (order 8, four workgroups per CU)
+constexpr int XFIFO_W = 56;     // x-band lanes per strip the compact FIFOs hold
 
 template <int P>
 struct Strip2 {
@@ -77,19 +79,28 @@ struct Fwd2Args {
 // so no Cq bytes are read: each Cq load becomes that value on the lanes and
 // rows where the load would have read a cell and 0 elsewhere, and the step
 // computes bitwise what it computes with the array.
-template <int P, int SNAP, bool UQ>
-__global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
+// CX (order 8): the FIFOs of stage A's x-band memories hold only the
+// strip's x-band lanes (at most XFIFO_W, which the plan checks); the other
+// lanes' memory is 0, which is what they hold in the full FIFOs (their
+// CPML coefficients are a = b = 0).  With an unroll of two this fits the
+// kernel into 128 VGPRs and 40 KB of LDS, four workgroups per CU.
+template <int P, int SNAP, bool UQ, bool CX>
+__global__ __launch_bounds__(NT, CX ? 4 : 3) void k_fwd_step2(Fwd2Args a)
 {
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH_F2;
-    constexpr int U = UNROLL_F2;
+    constexpr int U = CX ? UNROLL_F2_CX : UNROLL_F2;
+    constexpr int XW = XFIFO_W;                     // x-band slots of the compact FIFOs
     constexpr int R2 = 2 * P;                       // ring / FIFO depth (a power of two)
     constexpr uint32_t ESZ = snap_bytes<SNAP>();
     __shared__ float rowA[2][NT];                   // E^n row hA, by row parity
     __shared__ float rowB[2][NT];                   // E^{n+1} row hB, by row parity
     __shared__ float ringA[R2][NT];                 // Hz^{n+1/2} rows
     __shared__ float ringB[P][NT];                  // Hz^{n+3/2} rows
-    __shared__ float mfifo[4][R2][NT];              // stage A's CPML memories, lane-private
+    // stage A's CPML memories for stage B, each [R2] rows: full layout
+    // [Myh | Mxh | Mxe | Mye] of NT lanes; CX: [Myh | Mye] of NT lanes, then
+    // [Mxh | Mxe] of XW x-band slots
+    __shared__ float fifo[CX ? 2 * R2 * (NT + XW) : 4 * R2 * NT];
     __shared__ float cyt[CH2_MAX + 6 * P - 3][6];   // per-row CPML coefficients
     __shared__ int evs[CH2_MAX + 4 * P - 2];        // slot of each stage-A E row
     __shared__ int ev_lo, ev_hi;                    // first / last stage-A E row with events
@@ -129,6 +140,33 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
     const bool in_x = (c >= g.x0) & (c < g.x1);
     const int c0 = xs - OFF;
     const bool xband = c0 < g.x0 || c0 + NT - 1 >= g.hx1;   // uniform
+    // x-band FIFO slot: the lane itself, or (CX) the lane's index among the
+    // strip's x-band lanes, -1 off the band
+    int xi = tid;
+    if constexpr (CX) {
+        const int cl = max(c0, 0), cr = max(g.hx1, c0);
+        const int nl = max(0, min(g.x0, c0 + NT) - cl);
+        xi = !fx_h ? -1 : (c < g.x0 ? c - cl : nl + (c - cr));
+    }
+    // k = 0: the H-update memory, 1: the E-update memory
+    auto yref = [&](int k, int slot) -> float& {
+        return fifo[((CX ? k : 3 * k) * R2 + slot) * NT + tid];
+    };
+    auto xput = [&](int k, int slot, float m) {
+        if constexpr (CX) {
+            if (xi >= 0) fifo[2 * R2 * NT + (k * R2 + slot) * XW + xi] = m;
+        } else {
+            fifo[((1 + k) * R2 + slot) * NT + tid] = m;
+        }
+    };
+    auto xget = [&](int k, int slot) {
+        if constexpr (CX) {
+            const float m = fifo[2 * R2 * NT + (k * R2 + slot) * XW + max(xi, 0)];
+            return xi < 0 ? 0.0f : m;
+        } else {
+            return fifo[((1 + k) * R2 + slot) * NT + tid];
+        }
+    };
     const int bxc = band_x(g, incol ? c : 0);
     const int th = min(max(tid, P - 1), NT - P - 1);
     const int te = min(max(tid, P), NT - P);
@@ -311,7 +349,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                 const float* ct = cyt[hA - yc0];
                 float m = fMyh[u];
                 d = cpml_step(m, ct[0], ct[1], ct[2], d);
-                mfifo[0][slot2(hA)][tid] = m;
+                yref(0, slot2(hA)) = m;
             }
             const bool hx_ok = FAST ? colE : (colE & hx_row(hA));
             const float hxn = hx_ok ? fmaf(-fQa[u], d, fHx[u]) : 0.0f;
@@ -329,7 +367,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             if (xband) {
                 float m = fMxh[u];
                 d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
-                mfifo[1][slot2(hA)][tid] = m;
+                xput(0, slot2(hA), m);
             }
             ringA[slot2(hA)][tid] = hzA_ok ? fmaf(fQa[u], d, fHz[u]) : 0.0f;
         }
@@ -337,7 +375,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             float d = g.rdx * stencil<P>([&](int k) { return rB[th + k]; },
                                          [&](int k) { return rB[th - k + 1]; });
             if (xband) {
-                float m = mfifo[1][slot2(hB)][tid];
+                float m = xget(0, slot2(hB));
                 d = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, d);
                 if constexpr (FAST) b1.stv(m, lane_off(own & colHz & fx_h, bx4), L.oMxh + (uint32_t)hB * brow);
                 else b1.st(own & colHz & fx_h, m, (uint32_t)(hB * g.bx) * 4u + bx4, L.oMxh);
@@ -360,7 +398,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             if (xband) {
                 float m = fMxe[u];
                 uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
-                mfifo[2][slot2(yA)][tid] = m;
+                xput(1, slot2(yA), m);
             }
             float v = g.rdy * stencil<P>([&](int k) { return hwA[P - 1 + k]; },
                                          [&](int k) { return hwA[P - k]; });
@@ -368,7 +406,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                 const float* ct = cyt[yA - yc0];
                 float m = fMye[u];
                 v = cpml_step(m, ct[3], ct[4], ct[5], v);
-                mfifo[3][slot2(yA)][tid] = m;
+                yref(1, slot2(yA)) = m;
             }
             const float curl = uu_ - v;
             const float ev = ewA[0];
@@ -400,7 +438,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             const bool st_h = FAST ? own : (own & hx_row(hB) & own_row(hB));
             if (!FAST && fy_h(hB)) {
                 const float* ct = cyt[hB - yc0];
-                float m = mfifo[0][slot2(hB)][tid];
+                float m = yref(0, slot2(hB));
                 d = cpml_step(m, ct[0], ct[1], ct[2], d);
                 b1.st(st_h, m, (uint32_t)(band_y(g, hB) * nx) * 4u + c4, L.oMyh);
             }
@@ -420,7 +458,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
             float uu_ = g.rdx * stencil<P>([&](int k) { return hzr[te + k - 1]; },
                                            [&](int k) { return hzr[te - k]; });
             if (xband) {
-                float m = mfifo[2][slot2(yB)][tid];
+                float m = xget(1, slot2(yB));
                 uu_ = cpml_step(m, cx_e.a, cx_e.b, cx_e.ik, uu_);
                 if constexpr (FAST) b1.stv(m, lane_off(own & fx_e, bx4), L.oMxe + (uint32_t)yB * brow);
                 else b1.st(own & fx_e, m, (uint32_t)(yB * g.bx) * 4u + bx4, L.oMxe);
@@ -429,7 +467,7 @@ __global__ __launch_bounds__(NT, 3) void k_fwd_step2(Fwd2Args a)
                                          [&](int k) { return hwB[P - k]; });
             if (!FAST && fy_e(yB)) {
                 const float* ct = cyt[yB - yc0];
-                float m = mfifo[3][slot2(yB)][tid];
+                float m = yref(1, slot2(yB));
                 v = cpml_step(m, ct[3], ct[4], ct[5], v);
                 b1.st(own, m, (uint32_t)(band_y(g, yB) * nx) * 4u + c4, L.oMye);
             }
