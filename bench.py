@@ -142,7 +142,7 @@ def load_traffic(kernel, cfg):
 
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, steps, min_seconds=10.0, max_runs=8):
+def cpu_baseline(wl, steps, min_seconds=10.0, max_runs=24):
     """fp64 oracle on one shot of the workload for ``steps`` time steps.
 
     The sample (forward with storage, then the exact adjoint) is repeated
