@@ -65,6 +65,7 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
     constexpr int D = PREFETCH_A2;
     constexpr int R2 = 2 * P;                       // window / FIFO depth (a power of two)
     constexpr uint32_t ESZ = snap_bytes<SNAP>();
+    constexpr int GRAD_PART = P == 4 ? 1 : 3;       // load group of stage B's gradients and snapshots
     __shared__ float rowUA[NT], rowUB[NT];          // u of rows hA / hB (x-stencils of lambda_Hz)
     __shared__ float ringA[P][NT], ringB[P][NT];    // filtered Cq lambda_Hz rows of each stage
     __shared__ float mfifo[4][R2][NT];              // stage A's Mxe, Mye, Myh, Mxh, lane-private
@@ -174,10 +175,11 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
     // as soon as the current row's iteration has used that group's slots, so
     // that most loads get nearly a whole iteration of lead: PART 1 (fronts'
     // inputs and stage A's lambda_Hx inputs) after phase 1, PART 2 (Cq and
-    // the lambda_Hz inputs) after phase 2, PART 3 (Ca, and the gradient
-    // accumulators and snapshots of stage B's front, whose short lead keeps
-    // the registers live across phases 2 and 3 within the budget) after
-    // phase 3.
+    // the lambda_Hz inputs) after phase 2, PART 3 (Ca) after phase 3.  The
+    // gradient accumulators and snapshots of stage B's front, read in phase
+    // 1, go with PART 1 at order 8 (a whole iteration of lead within the
+    // register budget) and with PART 3 at lower orders (a short lead, which
+    // keeps their registers free across phases 2 and 3).
     auto issue = [&](auto fast_t, auto part_t, int u, int r, bool live) {
         constexpr bool FAST = decltype(fast_t)::value;
         constexpr int PART = decltype(part_t)::value;
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
         const bool liveA = live & (r <= r_end - 1);
         const bool liveB = live & (r >= ya + 1);
         const int meA = M(liveA & e_row(r)), meB = M(liveB & e_row(rB));
-        if constexpr (PART == 3) {
+        if constexpr (PART == GRAD_PART) {
             const uint32_t orB = G(rB) * rowb;
             const int mg = M(liveB & own_row(rB) & (rB >= g.y0) & (rB < g.y1));
             const uint32_t sr = FAST ? (uint32_t)(rB - g.y0) * (uint32_t)g.nxi * 2u * ESZ : srw(rB);
@@ -199,6 +201,8 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
             fScB[u] = pB.c;
             fGa[u] = bga.ldv(v_g | mg, orB);
             fGb[u] = bgb.ldv(v_g | mg, orB);
+        }
+        if constexpr (PART == 3) {
             fCaA[u] = bm.ldv(v_eA | M(liveA & (yA >= Ya) & (yA < Yb) & e_row(yA)), a.m.oCa + G(yA) * rowb);
             fCaB[u] = bm.ldv(v_own | M(liveB & own_row(yB)), a.m.oCa + G(yB) * rowb);
             return;
