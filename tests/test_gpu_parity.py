@@ -204,11 +204,12 @@ def test_two_step_launch_bitwise_equals_single_steps(order, snap, ckpt):
 
 
 @pytest.mark.parametrize("order", inputs.ORDERS)
-@pytest.mark.parametrize("snap,ckpt", [("f32", 0), ("bf16", 0), ("f32", 7)])
+@pytest.mark.parametrize("snap,ckpt", [("f32", 0), ("bf16", 0), ("fp8", 0), ("f32", 7)])
 def test_uniform_cq_two_step_bitwise_equals_single_steps(order, snap, ckpt):
     """mu_r one value everywhere: the two-step kernels read no Cq bytes and
     use the value instead, the one-step kernels read the array; both give
-    bitwise the same records and gradients."""
+    bitwise the same records and gradients (the one-step kernels' FP8
+    snapshots are checked against the oracle elsewhere)."""
     wl = inputs.as_f32(inputs.random_workload(order, 70, 9, nt=101, n_shots=3, n_src=3, n_rec=7,
                                               seed=830 + order, src_anywhere=True, mu_range=(1.0, 1.0)))
     assert np.all(wl.cq == wl.cq.flat[0])
