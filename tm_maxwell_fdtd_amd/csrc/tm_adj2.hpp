@@ -156,6 +156,14 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
     };
     const int v_g = lane_off(grad, c4), v_gs = lane_off(grad, (uint32_t)(c - g.x0) * 2u * ESZ);
     auto msk = [](bool ok) { return ok ? 0 : RBuf::OOB; };
+    // ring slot of a row; at order 4 the slot is the row's parity, fixed in
+    // each unrolled iteration, and the empty asm makes the compiler rebuild
+    // the slot's LDS address at each use instead of holding (or spilling)
+    // one address per slot
+    auto rslot = [](int s) {
+        if constexpr (P == 2) asm volatile("" : "+s"(s));
+        return s;
+    };
     auto grow = [&](int y) { return (uint32_t)min(max(y, 0), ny - 1); };
     auto brw = [&](int y) { return (uint32_t)min(max(band_y(g, y), 0), g.by - 1); };
     auto srw = [&](int y) { return (uint32_t)min(max(y - g.y0, 0), g.nyi - 1) * (uint32_t)g.nxi * 2u * ESZ; };
@@ -415,7 +423,7 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
                 tz = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, tz);
                 b1.stv(m, ownv(v_hzxo), L.oMxh + (uint32_t)hB * brow);
             }
-            ringB[hB % P][tid] = hzB_ok ? tz : 0.0f;
+            ringB[rslot(hB % P)][tid] = hzB_ok ? tz : 0.0f;
         }
         if (actA) {
             float hzn = 0.0f;
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
                     tz = cpml_step(m, cx_h.a, cx_h.b, cx_h.ik, tz);
                     mfifo[3][fslot(hA)][tid] = m;
                 }
-                ringA[(hA + 4 * P) % P][tid] = hzA_ok ? tz : 0.0f;
+                ringA[rslot((hA + 4 * P) % P)][tid] = hzA_ok ? tz : 0.0f;
             }
             shift_in(hzA, hzn);
         }
