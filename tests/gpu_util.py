@@ -15,6 +15,70 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
 
 
+def seam_columns(wl, halo=None):
+    """Columns within ``halo`` cells of a strip edge of the step kernels:
+    one-step strips are 256 - 4P + 2 columns wide, two-step strips
+    256 - 8P + 4, both starting at column P."""
+    p = wl.order // 2
+    halo = 4 * p if halo is None else halo
+    cols = set()
+    for w in (256 - 4 * p + 2, 256 - 8 * p + 4):
+        for c0 in range(p, wl.nx, w):
+            cols.update(range(max(0, c0 - halo), min(wl.nx, c0 + halo)))
+    return np.array(sorted(cols), dtype=np.int64)
+
+
+def grid_regions(wl):
+    """Boolean [ny][nx] masks of the places where a localized kernel error
+    would hide in a global norm: the interior rows and columns next to the
+    CPML bands (2P deep) and the strip seams inside the interior window."""
+    p = wl.order // 2
+    y0, y1, x0, x1 = wl.pml_y0, wl.pml_y1, wl.pml_x0, wl.pml_x1
+    inside = np.zeros((wl.ny, wl.nx), bool)
+    inside[y0:y1, x0:x1] = True
+    regions = {}
+    m = np.zeros_like(inside)
+    m[y0:y0 + 2 * p] = True
+    m[y1 - 2 * p:y1] = True
+    regions["band rows"] = m & inside
+    m = np.zeros_like(inside)
+    m[:, x0:x0 + 2 * p] = True
+    m[:, x1 - 2 * p:x1] = True
+    regions["band cols"] = m & inside
+    m = np.zeros_like(inside)
+    m[:, seam_columns(wl)] = True
+    regions["strip seams"] = m & inside
+    return regions
+
+
+def compare(name, got, ref, tol, regions=None, elem_factor=10.0):
+    """Relative L2 of ``got`` against ``ref``, plus two local bounds:
+    every element within elem_factor * tol * max|ref|, and the relative L2
+    of each region (masks over the last two axes) within tol.  Returns the
+    global relative L2; raises AssertionError naming the failing bound."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    e = rel_l2(got, ref)
+    assert e <= tol, f"{name}: relative L2 {e:.3e} > {tol:.1e}"
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    if ref.size:
+        worst = float(np.abs(got - ref).max())
+        assert worst <= elem_factor * tol * scale + 1e-30, \
+            f"{name}: max element error {worst:.3e} > {elem_factor:g} x {tol:.1e} x max|ref| ({scale:.3e})"
+    for rname, mask in (regions or {}).items():
+        if not mask.any():
+            continue
+        g, r = got[..., mask], ref[..., mask]
+        nr = np.linalg.norm(r)
+        if nr == 0.0:
+            assert not np.any(g), f"{name} [{rname}]: nonzero where the reference is 0"
+            continue
+        er = float(np.linalg.norm(g - r) / nr)
+        assert er <= tol, f"{name} [{rname}]: relative L2 {er:.3e} > {tol:.1e}"
+    return e
+
+
 def observed_records_oracle(orc, wl):
     """Observed data of a workload with an anomaly model (oracle side)."""
     obs = inputs.observed_coefficients(wl)

@@ -27,6 +27,8 @@ import pytest
 
 from tm_maxwell_fdtd_amd import inputs
 
+import cpml_probe
+
 
 def taylor_staggered(order):
     """c_1..c_P solving sum_k c_k (2k-1)^(2m+1) = [m == 0], m = 0..P-1."""
@@ -499,3 +501,87 @@ def test_subsampled_gradient_is_the_sum_of_kept_step_terms(orc):
     # the records and grad_f do not depend on the snapshots
     np.testing.assert_array_equal(sub["records"], full["records"])
     np.testing.assert_array_equal(sub["grad_f"], full["grad_f"])
+
+
+# ---------------------------------------------------------------------------
+# CPML filter and band flags, site by site (tests/cpml_probe.py)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+@pytest.mark.parametrize("site,where", cpml_probe.CASES)
+@pytest.mark.parametrize("kappa", [1.7, 4.0])
+def test_cpml_filter_closed_form_and_band_flags(orc, order, site, where, kappa):
+    """One filter site at one index against the closed-form solution of its
+    recursion, out_n = d_n / kappa + sum_{k<=n} b^(n-k) a d_k, over 6 steps.
+
+    The index runs over lo-1, lo, hi-2, hi-1 and hi of the window on the
+    site's axis: H derivatives are filtered at lo-1, hi-1 and hi, E
+    derivatives at lo-1 and hi only (the page's forward_kernel_h /
+    forward_kernel_e bounds).  A profile that multiplied by kappa, a filter
+    at the wrong rows, swapped profile arrays or a wrong c_1 each change the
+    records by far more than the tolerance (checked on the alternatives)."""
+    wl, info = cpml_probe.workload(order, site, where, kappa, seed=900 + order)
+    r, _, _ = orc.forward(wl)
+    c1 = float(taylor_staggered(order)[0])
+    exp = cpml_probe.expected_records(wl, info, c1)
+    got = r[:, 0, 0]
+    scale = np.abs(exp).max()
+    assert scale > 0
+    err = np.abs(got - exp).max() / scale
+    assert err <= 1e-6, (info, err)
+    # the pin has power: the other flag decision and d * kappa differ
+    alt_flag = cpml_probe.expected_records(wl, info, c1, filtered=not info["filtered"])
+    assert np.abs(alt_flag - exp).max() > 1e-2 * scale
+    if info["filtered"]:
+        alt_kappa = cpml_probe.expected_records(wl, info, c1, kappa_power=1)
+        assert np.abs(alt_kappa - exp).max() > 1e-2 * scale
+
+
+def test_cpml_probe_flags_match_the_page_bounds():
+    """The flag decisions the probe expects at the five indices."""
+    lo, hi = 10, 20
+    h = [cpml_probe.band_flag("hy", p, lo, hi) for p in (lo - 1, lo, hi - 2, hi - 1, hi)]
+    e = [cpml_probe.band_flag("ey", p, lo, hi) for p in (lo - 1, lo, hi - 2, hi - 1, hi)]
+    assert h == [True, False, False, True, True]
+    assert e == [True, False, False, False, True]
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+def test_adjoint_dot_test_stretched_cpml(orc, order):
+    """The dot test with kappa rising to 5 in the bands (every band cell
+    has kappa != 1, so the adjoint's d / kappa terms are all exercised)."""
+    wl = inputs.random_workload(order, 20, 6, nt=120, n_shots=2, n_src=3, n_rec=5, seed=37,
+                                src_anywhere=True, kappa_max=5.0)
+    p = order // 2
+    ky = wl.cpml[2, :wl.ny]
+    assert np.all(ky[p:wl.pml_y0] > 1.0) and ky[wl.pml_y0] == 1.0
+    r, _, _ = orc.forward(wl)
+    d = np.random.default_rng(6).standard_normal(r.shape)
+    grad_f, _, _ = orc.adjoint(wl, d)
+    lhs = float(np.sum(r * d))
+    rhs = float(np.sum(wl.f * grad_f))
+    assert abs(lhs - rhs) <= 1e-10 * abs(lhs), (lhs, rhs)
+
+
+@pytest.mark.parametrize("order", [2, 8])
+def test_gradient_central_differences_stretched_cpml(orc, order):
+    """dJ/dCa and dJ/dCb against central differences with kappa_max = 5,
+    at cells next to the bands."""
+    wl = inputs.random_workload(order, 16, 8, nt=150, n_shots=1, n_src=2, n_rec=6, seed=41,
+                                kappa_max=5.0)
+    ref = orc.misfit_and_gradient(wl)
+    cells = [(wl.pml_y0, wl.pml_x0 + 3), (wl.pml_y1 - 1, wl.pml_x0 + 7), (wl.pml_y0 + 5, wl.pml_x1 - 1),
+             (wl.pml_y0 + 8, wl.pml_x0)]
+    for name, key in (("ca", "gca"), ("cb", "gcb")):
+        for (y, x) in cells:
+            base = getattr(wl, name)
+            h = 1e-6 * abs(base[y, x])
+            js = []
+            for sgn in (1.0, -1.0):
+                arr = base.copy()
+                arr[y, x] += sgn * h
+                r, _, _ = orc.forward(wl, **{name: arr})
+                js.append(0.5 * float(np.sum(r * r)))
+            fd = (js[0] - js[1]) / (2 * h)
+            g = ref[key][y, x]
+            assert abs(fd - g) <= 1e-5 * abs(g) + 1e-12 * abs(ref["J"]) / abs(base[y, x]), (name, y, x, fd, g)

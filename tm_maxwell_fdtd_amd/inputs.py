@@ -18,7 +18,8 @@ layer that builds these arrays is not):
   Cq = dt / (mu0 mu_r) is the plain Yee reading.  The 1/dx factors are
   applied inside the stencils (the ``rdx``/``rdy`` constants of the kernels).
 * CPML profile: standard convolutional PML with a quadratic damping profile,
-  alpha decreasing linearly into the band and kappa = 1; integer-grid arrays
+  alpha decreasing linearly into the band and kappa = 1 by default (or
+  kappa rising quadratically from 1 to ``kappa_max``); integer-grid arrays
   (ax, bx, kx) serve the E-update derivatives and half-grid arrays (axh, ...)
   the H-update derivatives, as in ``forward_kernel_h``/``forward_kernel_e``.
 * Ricker wavelet of unit amplitude, delayed by 1.5 periods.
@@ -141,14 +142,15 @@ def stable_dt(eps_r_min, mu_r_min, dy, dx, order, fraction=0.9):
     return fraction / (vmax * _ABS_COEF_SUM[order] * math.sqrt(1.0 / dx ** 2 + 1.0 / dy ** 2))
 
 
-def cpml_axis(n, lo, hi, npml, h, dt, vmax, freq, r_coef=1e-3):
+def cpml_axis(n, lo, hi, npml, h, dt, vmax, freq, r_coef=1e-3, kappa_max=1.0):
     """CPML profile arrays for one axis of ``n`` points.
 
     ``lo`` is the first interior index and ``hi`` one past the last one.
     Returns (a, b, k, ah, bh, kh), each of length n, for integer points
     (x) and half points (x + 1/2 stored at x).  Outside the band the
-    damping is zero (a = 0), so a kernel that ignored its band flag would
-    still not damp there.
+    damping is zero (a = 0) and kappa = 1, so a kernel that ignored its band
+    flag would still not damp there.  Inside the band kappa grows as
+    1 + (kappa_max - 1) xi^2 with the normalised depth xi, like the damping.
     """
     if npml <= 0:
         z = np.zeros(n)
@@ -167,7 +169,7 @@ def cpml_axis(n, lo, hi, npml, h, dt, vmax, freq, r_coef=1e-3):
         xi = np.clip(xi, 0.0, None)
         d = d0 * xi ** 2
         alpha = alpha0 * np.clip(1.0 - xi, 0.0, None)
-        kappa = np.ones_like(pos)
+        kappa = 1.0 + (kappa_max - 1.0) * xi ** 2
         b = np.exp(-(d / kappa + alpha) * dt)
         denom = kappa * (d + kappa * alpha)
         a = np.where(d > 0.0, d * (b - 1.0) / np.where(denom > 0.0, denom, 1.0), 0.0)
@@ -271,7 +273,7 @@ def paint_ellipses(rng, eps, sig, count, ax_lo, ax_hi, eps_lo, eps_hi, sig_lo, s
 
 def assemble(name, order, eps_int, sig_int, npml, h, nt, n_shots, n_rec, freq,
              src_row=2, rec_row=5, dt=None, snap="f32", ckpt_every=0,
-             obs_eps_int=None, src_cols=None, mu_int=None, cfl_fraction=0.9):
+             obs_eps_int=None, src_cols=None, mu_int=None, cfl_fraction=0.9, kappa_max=1.0):
     """Build a Workload from an interior model and acquisition parameters."""
     p = order // 2
     ny_int, nx_int = eps_int.shape                  # the interior may be rectangular
@@ -288,8 +290,8 @@ def assemble(name, order, eps_int, sig_int, npml, h, nt, n_shots, n_rec, freq,
         dt = stable_dt(eps_min, float(mu_r.min()), h, h, order, cfl_fraction)
     ca, cb, cq = update_coefficients(eps_r, sigma, mu_r, dt)
     vmax = C0 / math.sqrt(eps_min * float(mu_r.min()))
-    ycoefs = cpml_axis(ny, y0, y1, npml, h, dt, vmax, freq)
-    xcoefs = cpml_axis(nx, x0, x1, npml, h, dt, vmax, freq)
+    ycoefs = cpml_axis(ny, y0, y1, npml, h, dt, vmax, freq, kappa_max=kappa_max)
+    xcoefs = cpml_axis(nx, x0, x1, npml, h, dt, vmax, freq, kappa_max=kappa_max)
     cpml = pack_cpml(ny, nx, ycoefs, xcoefs)
     wav = ricker(freq, nt, dt)
     f = np.repeat(wav[:, None, None], n_shots, axis=1)          # [nt][S][1]
@@ -344,10 +346,11 @@ def make_config(cfg: int, **over) -> Workload:
     """Workload ``cfg`` (1..5), optionally reduced via keyword overrides.
 
     Recognised overrides: n_int, npml, nt, n_shots, n_rec, order, snap,
-    ckpt_every, seed.
+    ckpt_every, seed, kappa_max (CPML stretching, 1 = none).
     """
     p = dict(CONFIG_DEFAULTS[cfg])
     seed = over.pop("seed", 20260 + cfg)
+    kappa_max = over.pop("kappa_max", 1.0)
     p.update(over)
     rng = np.random.default_rng(seed)
     n = p["n_int"]
@@ -377,20 +380,22 @@ def make_config(cfg: int, **over) -> Workload:
     return assemble(
         f"config{cfg}", p["order"], eps, sig, p["npml"], p["h"], p["nt"], p["n_shots"],
         p["n_rec"], p["freq"], snap=p["snap"], ckpt_every=p["ckpt_every"],
-        obs_eps_int=obs, src_cols=src_cols,
+        obs_eps_int=obs, src_cols=src_cols, kappa_max=kappa_max,
     )
 
 
 def random_workload(order, n_int, npml, nt, n_shots, n_src, n_rec, seed, h=0.01,
                     freq=700e6, eps_range=(1.5, 9.0), sig_range=(0.0, 0.02),
-                    identity_pml=False, src_anywhere=False, nx_int=None, mu_range=(1.0, 2.0)):
+                    identity_pml=False, src_anywhere=False, nx_int=None, mu_range=(1.0, 2.0),
+                    kappa_max=1.0):
     """A small heterogeneous workload for property tests.
 
     Models are random per cell (not smooth), several sources per shot at
     random interior cells (duplicates allowed), receivers at random cells,
     and random source amplitudes instead of a wavelet, so that every path
     through the kernels is exercised.  ``mu_range`` = (m, m) gives a
-    uniform mu_r = m (non-magnetic media for m = 1).
+    uniform mu_r = m (non-magnetic media for m = 1); ``kappa_max`` > 1
+    stretches the CPML coordinates (kappa from 1 to kappa_max into the band).
     """
     rng = np.random.default_rng(seed)
     shape = (n_int, n_int if nx_int is None else nx_int)   # rows x columns of the interior
@@ -398,7 +403,7 @@ def random_workload(order, n_int, npml, nt, n_shots, n_src, n_rec, seed, h=0.01,
     sig = rng.uniform(*sig_range, size=shape)
     mu = rng.uniform(*mu_range, size=shape)
     wl = assemble(f"random{seed}", order, eps, sig, npml, h, nt, n_shots, n_rec, freq,
-                  mu_int=mu)
+                  mu_int=mu, kappa_max=kappa_max)
     p = order // 2
     lo = p if src_anywhere else wl.pml_y0
     hi_y = (wl.ny - p) if src_anywhere else wl.pml_y1 - 1
