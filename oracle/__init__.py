@@ -63,7 +63,10 @@ def lib():
         L = ctypes.CDLL(_LIB)
         L.orc_forward.restype = ctypes.c_int
         L.orc_forward.argtypes = [ctypes.POINTER(Geom), _dp, _dp, _dp, _dp, _ll, _dp, _lp, _lp,
-                                  _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ll, _ll]
+                                  _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ll, _ll, _ll]
+        L.orc_adjoint_range.restype = ctypes.c_int
+        L.orc_adjoint_range.argtypes = [ctypes.POINTER(Geom), _dp, _dp, _dp, _dp, _ll, _lp, _lp, _dp, _dp,
+                                        _dp, _dp, _ll, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ll, _ll]
         L.orc_adjoint.restype = ctypes.c_int
         L.orc_adjoint.argtypes = [ctypes.POINTER(Geom), _dp, _dp, _dp, _dp, _ll, _lp, _lp, _ll,
                                   _dp, _dp, _dp, _dp, _dp, _dp]
@@ -141,21 +144,27 @@ class State:
 
 
 def forward(wl, t0: int = 0, t1: Optional[int] = None, state: Optional[State] = None,
-            store: bool = False, periodic: bool = False, ca=None, cb=None, cq=None, f=None):
+            store: bool = False, periodic: bool = False, ca=None, cb=None, cq=None, f=None,
+            segment: bool = False, records: Optional[np.ndarray] = None):
     """Run forward steps t0..t1-1.  Returns (records, state, snapshots).
 
-    ``records`` is [nt][S][n_rec] (rows outside [t0, t1) are zero);
-    ``snapshots`` is None or a pair (Ey^n, curlH^n) of [nt][S][ny_i][nx_i].
+    ``records`` is [nt][S][n_rec] (rows outside [t0, t1) are zero, or keep
+    what a passed-in ``records`` array held);
+    ``snapshots`` is None or a pair (Ey^n, curlH^n) of [nt][S][ny_i][nx_i]
+    (with ``segment``: of [t1 - t0][S][ny_i][nx_i], step n at n - t0).
     ``ca``/``cb``/``cq``/``f`` override the workload's arrays.
     """
     t1 = wl.nt if t1 is None else t1
     g = geom(wl, periodic)
     st = State(wl.n_shots, wl.ny, wl.nx) if state is None else state
-    r = np.zeros((wl.nt, wl.n_shots, wl.n_rec))
+    r = np.zeros((wl.nt, wl.n_shots, wl.n_rec)) if records is None else records
+    assert r.shape == (wl.nt, wl.n_shots, wl.n_rec) and r.dtype == np.float64 and r.flags.c_contiguous
     snaps = None
+    snap_t0 = t0 if segment else 0
     if store:
         nyi, nxi = wl.pml_y1 - wl.pml_y0, wl.pml_x1 - wl.pml_x0
-        snaps = (np.zeros((wl.nt, wl.n_shots, nyi, nxi)), np.zeros((wl.nt, wl.n_shots, nyi, nxi)))
+        steps = (t1 - t0) if segment else wl.nt
+        snaps = (np.zeros((steps, wl.n_shots, nyi, nxi)), np.zeros((steps, wl.n_shots, nyi, nxi)))
     ca = _c64(wl.ca if ca is None else ca)
     cb = _c64(wl.cb if cb is None else cb)
     cq = _c64(wl.cq if cq is None else cq)
@@ -167,7 +176,7 @@ def forward(wl, t0: int = 0, t1: Optional[int] = None, state: Optional[State] = 
                            _d(f), _l(src), _l(rec), _d(st.E), _d(st.Hx), _d(st.Hz),
                            _d(st.psi_ez), _d(st.psi_ex), _d(st.psi_hxz), _d(st.psi_hzx),
                            _d(r), _d(snaps[0] if snaps else None), _d(snaps[1] if snaps else None),
-                           t0, t1)
+                           snap_t0, t0, t1)
     if rc != 0:
         raise RuntimeError(f"orc_forward failed ({rc})")
     return r, st, snaps
@@ -195,6 +204,77 @@ def adjoint(wl, grad_r: np.ndarray, snaps=None, ca=None, cb=None, cq=None, want_
     if rc != 0:
         raise RuntimeError(f"orc_adjoint failed ({rc})")
     return grad_f, gca, gcb
+
+
+class AdjointState:
+    """Adjoint state of all shots: lambda_E, lambda_Hx, lambda_Hz and the
+    adjoint memories of the four CPML filters (zero before step nt-1)."""
+
+    NAMES = ("lE", "lHx", "lHz", "m_hzx", "m_hxz", "m_ex", "m_ez")
+
+    def __init__(self, n_shots, ny, nx):
+        for k in self.NAMES:
+            setattr(self, k, np.zeros((n_shots, ny, nx)))
+
+
+def adjoint_range(wl, grad_r: np.ndarray, t0: int, t1: int, state: AdjointState, snaps=None,
+                  snap_t0: int = 0, gca=None, gcb=None, grad_f=None, ca=None, cb=None, cq=None):
+    """Adjoint steps t1-1 .. t0 on ``state`` (updated in place).  ``snaps``
+    holds step n at index n - snap_t0; the per-shot gradients are
+    accumulated into ``gca`` / ``gcb`` ([S][ny][nx] fp64, may be None) and
+    rows t0..t1-1 of ``grad_f`` ([nt][S][n_src], may be None) written."""
+    g = geom(wl)
+    grad_r = _c64(grad_r)
+    assert grad_r.shape == (wl.nt, wl.n_shots, wl.n_rec)
+    ca = _c64(wl.ca if ca is None else ca)
+    cb = _c64(wl.cb if cb is None else cb)
+    cq = _c64(wl.cq if cq is None else cq)
+    cpml = _c64(wl.cpml)
+    src = np.ascontiguousarray(wl.src, dtype=np.int64)
+    rec = np.ascontiguousarray(wl.rec, dtype=np.int64)
+    se = _c64(snaps[0]) if snaps is not None else None
+    sc = _c64(snaps[1]) if snaps is not None else None
+    rc = lib().orc_adjoint_range(ctypes.byref(g), _d(ca), _d(cb), _d(cq), _d(cpml), cpml.shape[1],
+                                 _l(src), _l(rec), _d(grad_r), _d(grad_f), _d(se), _d(sc), snap_t0,
+                                 *(_d(getattr(state, k)) for k in AdjointState.NAMES),
+                                 _d(gca), _d(gcb), t0, t1)
+    if rc != 0:
+        raise RuntimeError(f"orc_adjoint_range failed ({rc})")
+
+
+def gradient_checkpointed(wl, every: int, grad_r=None, residual=None, want_grad_f=True):
+    """Records and the exact adjoint's gradients with bounded memory: the
+    forward keeps its state every ``every`` steps; the adjoint replays each
+    segment from its checkpoint (storing that segment's snapshots only) and
+    runs the segment's reverse steps, last segment first.  The arithmetic is
+    that of forward + adjoint (the replay repeats the same steps), so the
+    results equal the full-storage ones.
+
+    dJ/dr is ``grad_r`` if given, else ``residual(records)``, else the
+    records themselves (J = 1/2 |r|^2).  Returns a dict like
+    ``misfit_and_gradient`` (without J)."""
+    nt, S = wl.nt, wl.n_shots
+    st = State(S, wl.ny, wl.nx)
+    r = np.zeros((nt, S, wl.n_rec))
+    ckpts = {}
+    for ta in range(0, nt, every):
+        ckpts[ta] = st.copy()
+        forward(wl, ta, min(ta + every, nt), state=st, records=r)
+    del st
+    if grad_r is None:
+        grad_r = r if residual is None else residual(r)
+    grad_r = _c64(grad_r)
+    adj = AdjointState(S, wl.ny, wl.nx)
+    gca = np.zeros((S, wl.ny, wl.nx))
+    gcb = np.zeros((S, wl.ny, wl.nx))
+    grad_f = np.zeros((nt, S, wl.n_src)) if want_grad_f else None
+    for ta in sorted(ckpts, reverse=True):
+        tb = min(ta + every, nt)
+        _, _, snaps = forward(wl, ta, tb, state=ckpts.pop(ta), store=True, segment=True)
+        adjoint_range(wl, grad_r, ta, tb, adj, snaps, snap_t0=ta, gca=gca, gcb=gcb, grad_f=grad_f)
+        del snaps
+    return dict(records=r, grad_f=grad_f, gca_shot=gca, gcb_shot=gcb, gca=shot_sum(gca), gcb=shot_sum(gcb),
+                residual=grad_r)
 
 
 def shot_sum(grad_shot: np.ndarray) -> np.ndarray:

@@ -186,15 +186,16 @@ static int setup(ctx_t *k, const orc_geom *g)
  * each [S][ny][nx]), which the caller owns and may carry between calls.
  *   f    [nt][S][n_src]   source amplitudes (indexed by absolute step)
  *   r    [nt][S][n_rec]   records (written for the steps run), may be NULL
- *   snap_e, snap_c  [nt][S][ny_i][nx_i] Ey^n and curlH^n on the interior
- *                   window (written for the steps run), may be NULL
+ *   snap_e, snap_c  [..][S][ny_i][nx_i] Ey^n and curlH^n on the interior
+ *                   window, step n at index n - snap_t0 (written for the
+ *                   steps run), may be NULL
  */
 int orc_forward(const orc_geom *g, const double *ca, const double *cb, const double *cq,
                 const double *cpml_arr, ll cpml_len,
                 const double *f, const ll *src, const ll *rec,
                 double *E, double *Hx, double *Hz,
                 double *psi_ez, double *psi_ex, double *psi_hxz, double *psi_hzx,
-                double *r, double *snap_e, double *snap_c, ll t0, ll t1)
+                double *r, double *snap_e, double *snap_c, ll snap_t0, ll t0, ll t1)
 {
     ctx_t k;
     int rc = setup(&k, g);
@@ -244,7 +245,7 @@ int orc_forward(const orc_geom *g, const double *ca, const double *cb, const dou
                         v = cpml(&phxz[j], CP(AY, y), CP(BY, y), CP(KY, y), v);
                     double curl = u - v;
                     if (!g->periodic && interior(g, y, x)) {
-                        ll w = ((n * S + s) * nyi + (y - g->pml_y0)) * nxi + (x - g->pml_x0);
+                        ll w = (((n - snap_t0) * S + s) * nyi + (y - g->pml_y0)) * nxi + (x - g->pml_x0);
                         if (snap_e) snap_e[w] = e[j];
                         if (snap_c) snap_c[w] = curl;
                     }
@@ -271,21 +272,25 @@ int orc_forward(const orc_geom *g, const double *ca, const double *cb, const dou
 
 /* ---- exact adjoint -------------------------------------------------------- */
 /*
- * Reverse loop n = nt-1 .. 0 of the exact transpose of orc_forward's step,
- * from a zero adjoint state.
- *   grad_r  [nt][S][n_rec]  dJ/dr
- *   grad_f  [nt][S][n_src]  dJ/df (output, may be NULL)
- *   snap_e, snap_c  interior snapshots from orc_forward (may be NULL: no
- *                   gradient is accumulated then)
- *   gca, gcb  [S][ny][nx]  per-shot gradients (output, overwritten; zero
- *                          outside the interior window)
+ * Reverse steps n = t1-1 .. t0 of the exact transpose of orc_forward's step,
+ * on an adjoint state the caller owns and may carry between calls (all
+ * [S][ny][nx]: lambda_E, lambda_Hx, lambda_Hz and the adjoint memories of
+ * the four CPML filters; zero before the last step nt-1).
+ *   grad_r  [nt][S][n_rec]  dJ/dr (indexed by absolute step)
+ *   grad_f  [nt][S][n_src]  dJ/df (rows t0..t1-1 written, may be NULL)
+ *   snap_e, snap_c  interior snapshots from orc_forward, step n at index
+ *                   n - snap_t0 (may be NULL: no gradient is accumulated)
+ *   gca, gcb  [S][ny][nx]  per-shot gradients, accumulated (+=) on the
+ *                          interior window; may be NULL
  */
-int orc_adjoint(const orc_geom *g, const double *ca, const double *cb, const double *cq,
-                const double *cpml_arr, ll cpml_len,
-                const ll *src, const ll *rec, ll nt,
-                const double *grad_r, double *grad_f,
-                const double *snap_e, const double *snap_c,
-                double *gca, double *gcb)
+int orc_adjoint_range(const orc_geom *g, const double *ca, const double *cb, const double *cq,
+                      const double *cpml_arr, ll cpml_len,
+                      const ll *src, const ll *rec,
+                      const double *grad_r, double *grad_f,
+                      const double *snap_e, const double *snap_c, ll snap_t0,
+                      double *lE_all, double *lHx_all, double *lHz_all,
+                      double *m_hzx_all, double *m_hxz_all, double *m_ex_all, double *m_ez_all,
+                      double *gca, double *gcb, ll t0, ll t1)
 {
     ctx_t k;
     int rc = setup(&k, g);
@@ -296,36 +301,25 @@ int orc_adjoint(const orc_geom *g, const double *ca, const double *cb, const dou
     const double *cp = cpml_arr;
 #define CP(row, i) cp[(ll)(row) * cpml_len + (i)]
 
-    double *lE = calloc((size_t)numel, sizeof(double));
-    double *lHx = calloc((size_t)numel, sizeof(double));
-    double *lHz = calloc((size_t)numel, sizeof(double));
-    double *m_hzx = calloc((size_t)numel, sizeof(double)); /* adjoint memory of the E-update x filter */
-    double *m_hxz = calloc((size_t)numel, sizeof(double)); /* ... E-update y filter */
-    double *m_ex = calloc((size_t)numel, sizeof(double));  /* ... Hz-update x filter */
-    double *m_ez = calloc((size_t)numel, sizeof(double));  /* ... Hx-update y filter */
     double *U = calloc((size_t)numel, sizeof(double));     /* filtered Cb*lambda for the Hz transpose */
     double *W = calloc((size_t)numel, sizeof(double));     /* ... for the Hx transpose */
     double *TZ = calloc((size_t)numel, sizeof(double));    /* filtered Cq*lambda_Hz */
     double *TX = calloc((size_t)numel, sizeof(double));    /* filtered Cq*lambda_Hx */
-    if (!lE || !lHx || !lHz || !m_hzx || !m_hxz || !m_ex || !m_ez || !U || !W || !TZ || !TX) {
+    if (!U || !W || !TZ || !TX) {
         rc = -4;
         goto done;
     }
 
     for (ll s = 0; s < S; ++s) {
-        memset(lE, 0, numel * sizeof(double));
-        memset(lHx, 0, numel * sizeof(double));
-        memset(lHz, 0, numel * sizeof(double));
-        memset(m_hzx, 0, numel * sizeof(double));
-        memset(m_hxz, 0, numel * sizeof(double));
-        memset(m_ex, 0, numel * sizeof(double));
-        memset(m_ez, 0, numel * sizeof(double));
+        double *lE = lE_all + s * numel, *lHx = lHx_all + s * numel, *lHz = lHz_all + s * numel;
+        double *m_hzx = m_hzx_all + s * numel; /* adjoint memory of the E-update x filter */
+        double *m_hxz = m_hxz_all + s * numel; /* ... E-update y filter */
+        double *m_ex = m_ex_all + s * numel;   /* ... Hz-update x filter */
+        double *m_ez = m_ez_all + s * numel;   /* ... Hx-update y filter */
         double *ga = gca ? gca + s * numel : NULL;
         double *gb = gcb ? gcb + s * numel : NULL;
-        if (ga) memset(ga, 0, numel * sizeof(double));
-        if (gb) memset(gb, 0, numel * sizeof(double));
 
-        for (ll n = nt - 1; n >= 0; --n) {
+        for (ll n = t1 - 1; n >= t0; --n) {
             /* transpose of the receiver read: inject the residual */
             for (ll i = 0; i < g->n_rec; ++i) {
                 ll c = rec[s * g->n_rec + i];
@@ -347,7 +341,7 @@ int orc_adjoint(const orc_geom *g, const double *ca, const double *cb, const dou
                     if (!in_e(&k, y, x)) { U[j] = 0.0; W[j] = 0.0; continue; }
                     double e = lE[j];
                     if (interior(g, y, x)) {
-                        ll w = ((n * S + s) * nyi + (y - g->pml_y0)) * nxi + (x - g->pml_x0);
+                        ll w = (((n - snap_t0) * S + s) * nyi + (y - g->pml_y0)) * nxi + (x - g->pml_x0);
                         if (ga && snap_e) ga[j] += e * snap_e[w];
                         if (gb && snap_c) gb[j] += e * snap_c[w];
                     }
@@ -404,9 +398,38 @@ int orc_adjoint(const orc_geom *g, const double *ca, const double *cb, const dou
         }
     }
 done:
-    free(lE); free(lHx); free(lHz); free(m_hzx); free(m_hxz); free(m_ex); free(m_ez);
     free(U); free(W); free(TZ); free(TX);
 #undef CP
+    return rc;
+}
+
+/*
+ * The whole reverse loop n = nt-1 .. 0 from a zero adjoint state
+ * (orc_adjoint_range over [0, nt) on a fresh state).
+ *   grad_r  [nt][S][n_rec]  dJ/dr
+ *   grad_f  [nt][S][n_src]  dJ/df (output, may be NULL)
+ *   snap_e, snap_c  [nt][S][ny_i][nx_i] interior snapshots from orc_forward
+ *                   (may be NULL: no gradient is accumulated then)
+ *   gca, gcb  [S][ny][nx]  per-shot gradients (output, overwritten; zero
+ *                          outside the interior window)
+ */
+int orc_adjoint(const orc_geom *g, const double *ca, const double *cb, const double *cq,
+                const double *cpml_arr, ll cpml_len,
+                const ll *src, const ll *rec, ll nt,
+                const double *grad_r, double *grad_f,
+                const double *snap_e, const double *snap_c,
+                double *gca, double *gcb)
+{
+    const ll n = g->n_shots * g->ny * g->nx;
+    if (g->periodic) return -3;
+    double *st = calloc((size_t)(7 * n), sizeof(double));
+    if (!st) return -4;
+    if (gca) memset(gca, 0, (size_t)n * sizeof(double));
+    if (gcb) memset(gcb, 0, (size_t)n * sizeof(double));
+    int rc = orc_adjoint_range(g, ca, cb, cq, cpml_arr, cpml_len, src, rec, grad_r, grad_f, snap_e, snap_c, 0,
+                               st, st + n, st + 2 * n, st + 3 * n, st + 4 * n, st + 5 * n, st + 6 * n,
+                               gca, gcb, 0, nt);
+    free(st);
     return rc;
 }
 

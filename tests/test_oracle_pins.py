@@ -585,3 +585,17 @@ def test_gradient_central_differences_stretched_cpml(orc, order):
             fd = (js[0] - js[1]) / (2 * h)
             g = ref[key][y, x]
             assert abs(fd - g) <= 1e-5 * abs(g) + 1e-12 * abs(ref["J"]) / abs(base[y, x]), (name, y, x, fd, g)
+
+
+@pytest.mark.parametrize("every", [1, 7, 64])
+def test_checkpointed_oracle_equals_full_storage(orc, every):
+    """The oracle's segment-replay adjoint (forward state kept every K steps,
+    each segment replayed before its reverse steps) gives bitwise the
+    records and gradients of the full-storage run: it repeats the same steps
+    in the same arithmetic."""
+    wl = inputs.random_workload(8, 18, 6, nt=41, n_shots=2, n_src=2, n_rec=5, seed=61, src_anywhere=True,
+                                kappa_max=3.0)
+    full = orc.misfit_and_gradient(wl)
+    ck = orc.gradient_checkpointed(wl, every)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f", "gca", "gcb"):
+        np.testing.assert_array_equal(ck[key], full[key], err_msg=key)
