@@ -94,8 +94,12 @@ def kernel_bytes(name, wl, store, snap_bytes):
     bytes of k_fwd_step / k_adj_step (the per-cell-update figure times the
     cell-updates of the launch), although the state crosses HBM only once.
     k_fwd_step2_uq / k_adj_step2_uq are the instances where Cq holds one
-    value and is not read: 32 B per cell instead of 36.
+    value and is not read: 32 B per cell instead of 36.  A "_store" suffix
+    names the forward launches that store snapshots (the library times them
+    apart); ``stores(name)`` gives ``store`` for a timed name.
     """
+    if name.endswith("_store"):
+        name, store = name[:-len("_store")], True
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
     if name in ("k_fwd_step", "k_fwd_step_uq"):
@@ -115,6 +119,12 @@ def kernel_bytes(name, wl, store, snap_bytes):
     if name == "k_adj_step2_uq":
         return 2 * kernel_bytes("k_adj_step_uq", wl, store, snap_bytes)
     return None
+
+
+def stores(name):
+    """Whether launches timed under ``name`` store snapshots (forward) or
+    accumulate gradients (adjoint) in a full forward + adjoint step."""
+    return name.endswith("_store") or name.startswith("k_adj")
 
 
 def kernel_source_sha():
@@ -142,12 +152,43 @@ def load_traffic(kernel, cfg):
 
 # ---------------------------------------------------------------------------
 
+def cpu_info():
+    """CPU model, physical cores and the CPUs this process may run on."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "logical_cpus": os.cpu_count(),
+            "cpus_available": avail}
+
+
 def cpu_baseline(wl, steps, min_seconds=10.0, max_runs=24):
     """fp64 oracle on one shot of the workload for ``steps`` time steps.
 
     The sample (forward with storage, then the exact adjoint) is repeated
     until at least ``min_seconds`` of CPU work has been timed; the rate is
-    total cell-updates over total time.
+    total cell-updates over total time.  The forward alone (no storage) is
+    timed the same way for ``fwd_value``.
     """
     import dataclasses
 
@@ -157,18 +198,29 @@ def cpu_baseline(wl, steps, min_seconds=10.0, max_runs=24):
                               f=wl.f[:steps, :1].copy())
     p = wl.order // 2
     cells = (wl.ny - 2 * p) * (wl.nx - 2 * p) * steps
-    total, runs = 0.0, 0
-    while runs < max_runs and (runs == 0 or total < min_seconds):
-        t0 = time.perf_counter()
+
+    def rate(fn):
+        total, runs = 0.0, 0
+        while runs < max_runs and (runs == 0 or total < min_seconds):
+            t0 = time.perf_counter()
+            fn()
+            total += time.perf_counter() - t0
+            runs += 1
+        return cells * runs / total / 1e9, runs, total
+
+    def fwd_adj():
         r, _, snaps = oracle.forward(one, store=True)
         oracle.adjoint(one, r, snaps)
-        total += time.perf_counter() - t0
-        runs += 1
-        del r, snaps
-    return {"value": cells * runs / total / 1e9, "unit": "Gcell-updates/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"1 of {wl.n_shots} shots, {steps} of {wl.nt} time steps, same grid and model; "
-                      f"forward with storage + exact adjoint in fp64, {runs} run(s), {total:.1f} s"}
+
+    value, runs, total = rate(fwd_adj)
+    fwd_value, fruns, ftotal = rate(lambda: oracle.forward(one))
+    out = {"value": value, "unit": "Gcell-updates/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"1 of {wl.n_shots} shots, {steps} of {wl.nt} time steps, same grid and model; "
+                     f"forward with storage + exact adjoint in fp64, {runs} run(s), {total:.1f} s; "
+                     f"forward alone {fruns} run(s), {ftotal:.1f} s",
+           "fwd_value": fwd_value, "threads": oracle.num_threads()}
+    out.update(cpu_info())
+    return out
 
 
 def main():
@@ -297,20 +349,17 @@ def main():
 
     # roofline of the dominant kernel of the full step
     snap_bytes = 2 if wl.snap == "bf16" else 4
-    p = wl.order // 2
-    launches_fwd = wl.nt
     kernels = {}
     for name, (ms, n) in results["step"][1].items():
         if n == 0:
             continue
         avg_ms = ms / n
-        launches = wl.nt // 2 if name.startswith(("k_fwd_step2", "k_adj_step2")) else wl.nt
-        if name.startswith("k_fwd") and wl.ckpt_every:
-            # tm_forward and the replays of the adjoint (the samples mix both;
-            # the bytes below count the replays' snapshot stores for all)
-            launches *= 2
-        # in a full step the forward stores snapshots and the adjoint accumulates gradients
-        nbytes = kernel_bytes(name, wl, store=True, snap_bytes=snap_bytes)
+        # launches of the sampled steps: every timing_every-th step's launch
+        # (a two-step launch covers two steps)
+        per_launch = 2 if name.startswith(("k_fwd_step2", "k_adj_step2")) else 1
+        launches = n * args.timing_every / per_launch / args.steps
+        # the adjoint accumulates gradients on every launch of a full step
+        nbytes = kernel_bytes(name, wl, store=stores(name), snap_bytes=snap_bytes)
         kernels[name] = dict(avg_us=avg_ms * 1e3, samples=n, est_total_s=avg_ms * launches / 1e3,
                              alg_bytes=nbytes, gbs=nbytes / (avg_ms * 1e-3) / 1e9)
     dom = max(kernels, key=lambda k: kernels[k]["est_total_s"])
@@ -320,17 +369,18 @@ def main():
     traffic_b = load_traffic(dom, args.config)
     traffic = None if traffic_b is None else round(traffic_b / (kd["avg_us"] * 1e-6) / 1e9, 1)
     roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-                "avg_launch_us": round(kd["avg_us"], 2), "alg_bytes_per_launch": kd["alg_bytes"],
+                "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_frac": None if traffic is None else round(traffic / HBM_PEAK_GBS, 4),
+                "kernel": dom, "avg_launch_us": round(kd["avg_us"], 2), "alg_bytes_per_launch": kd["alg_bytes"],
                 "traffic_bytes_per_launch": None if traffic_b is None else int(traffic_b)}
     for name, k in sorted(kernels.items()):
-        log(f"  {name:12s} avg {k['avg_us']:9.2f} us  ({k['samples']} samples)  "
+        log(f"  {name:20s} avg {k['avg_us']:9.2f} us  ({k['samples']} samples)  "
             f"alg {k['alg_bytes'] / 1e6:8.1f} MB  -> {k['gbs']:7.1f} GB/s  est {k['est_total_s']:.3f} s/step")
     fwd_kern = {}
     if "fwd" in results:
         for name, (ms, n) in results["fwd"][1].items():
             if n:
-                nb = kernel_bytes(name, wl, store=False, snap_bytes=snap_bytes)
+                nb = kernel_bytes(name, wl, store=stores(name), snap_bytes=snap_bytes)
                 fwd_kern[name] = dict(avg_us=round(ms / n * 1e3, 2),
                                       gbs=round(nb / (ms / n * 1e-3) / 1e9, 1))
 

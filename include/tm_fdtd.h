@@ -117,6 +117,17 @@ typedef struct tm_plan tm_plan;
 
 /*
  * Validate a problem and build a plan (host only, no HIP call).
+ * Defined by: the set-up part of the page's host launchers forward,
+ * forward_with_storage and backward (grid sizes, 1/dy and 1/dx, the CPML
+ * window pml_y0..pml_x1, sources and receivers per shot, shot-batched or
+ * shared models), which this plan does once instead of per call.
+ * Why the source and receiver cells are plan arguments and not per-call
+ * ones (the page's launchers take them per call): the step kernels inject
+ * and record through host-built per-row tables (event rows: the grid rows
+ * holding sources or receivers, the distinct cells on them, CSR lists of
+ * the entries of each cell), whose size sets part of the workspace layout.
+ * A new acquisition geometry on the same grid is set with
+ * tm_plan_set_indices, without a new plan.
  *   cpml: host float32 [12][max(ny, nx)]: ay, by, ky, ayh, byh, kyh (first
  *         ny entries used) then ax, bx, kx, axh, bxh, kxh (first nx used);
  *         the integer-grid arrays filter E-update derivatives, the half-grid
@@ -138,12 +149,32 @@ tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const int64_t* 
 
 void tm_plan_destroy(tm_plan* plan);
 
+/*
+ * Replace the plan's source and receiver cells (a new acquisition geometry
+ * with the same n_src and n_rec per shot; same conventions as
+ * tm_plan_create: host int64 [S][n_src] and [S][n_rec], negative = none).
+ * Defined by: the src / rec index arguments of the page's launchers
+ * (forward, forward_with_storage, backward) and the kernels that use them
+ * (add_sources_ey, record_receivers_ey, add_adjoint_sources_ey,
+ * record_adjoint_at_sources).
+ * The event-row tables are rebuilt, so the workspace size may change:
+ * query tm_workspace_bytes again (a smaller workspace than it reports is
+ * rejected with TM_ENOMEM by the device calls).  The sequence state is
+ * reset: tm_adjoint needs a new storing tm_forward (else TM_ESTATE).  When
+ * the plan has run on a device, the call waits for that device
+ * (hipDeviceSynchronize) before it frees the plan's pinned staging copy of
+ * the old tables.  Errors (TM_EINVAL: a bad index; TM_ENOMEM: over
+ * hbm_budget; TM_EHIP: the wait failed) leave the plan unchanged.
+ */
+tm_status tm_plan_set_indices(tm_plan* plan, const int64_t* src, const int64_t* rec);
+
 /* Bytes of device workspace the plan needs (host only). */
 tm_status tm_workspace_bytes(const tm_plan* plan, uint64_t* bytes);
 
 /*
  * Courant number sqrt(max(Cb*Cq)) * sum|c_k| * sqrt(1/dx^2 + 1/dy^2) of a
- * model (the largest over the shots' models with model_per_shot); the
+ * model (the stability limit of the staggered leapfrog scheme; the page
+ * gives none, its launchers do not check stability) (the largest over the shots' models with model_per_shot); the
  * scheme is stable when it is at most 1.  cb, cq: device float32 [ny][nx]
  * ([S][ny][nx] with model_per_shot).  Uses the workspace's scratch area and
  * synchronises ``stream``.
@@ -153,6 +184,11 @@ tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb
 
 /*
  * Forward propagation of all shots over steps [t0, t1), 0 <= t0 < t1 <= nt.
+ * Defined by: the page's host launchers forward (without TM_FWD_STORE) and
+ * forward_with_storage (with it), and the per-step order of their loop:
+ * forward_kernel_h, forward_kernel_e / forward_kernel_e_with_storage(_bf16,
+ * _fp8), add_sources_ey, record_receivers_ey; the header comment's forward
+ * equations.  The launchers' start_t / nt chunking is t0 / t1 here.
  * t0 == 0 starts from zero fields; t0 > 0 continues the state a previous
  * call on the same workspace left at step t0 (else TM_ESTATE).
  *   ca, cb, cq: device float32 [ny][nx] update coefficients ([S][ny][nx],
@@ -177,6 +213,15 @@ tm_status tm_forward(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca
  * Exact discrete adjoint (time-reversed transpose of the forward step, CPML
  * included) over all nt steps, after a storing tm_forward that reached nt on
  * the same workspace (else TM_ESTATE).  May be called repeatedly.
+ * Defined by: the page's host launcher backward (its reverse time loop:
+ * add_adjoint_sources_ey, record_adjoint_at_sources, backward_kernel_lambda_h,
+ * backward_kernel_lambda_e_with_grad) and the header comment's adjoint
+ * equations (the forward run backwards in time with transposed operators)
+ * and gradients (dJ/dCa = sum_n lambda^{n+1} Ey^n, dJ/dCb = sum_n
+ * lambda^{n+1} curlH^n).  Unlike the page's kernels, the transpose here is
+ * exact for heterogeneous Cb, Cq and inside the CPML bands (the coefficient
+ * at the source point, then that point's filter run backwards in time,
+ * then the transposed stencil).
  *   ca, cb, cq, f: the same arrays as the forward (f is re-read by the
  *      segment replay of checkpoint mode; when the forward's TM_FWD_CHECK
  *      found cq to hold one value and cq is the same pointer, the adjoint
@@ -195,8 +240,10 @@ tm_status tm_adjoint(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* ca
                      float* grad_f, float* grad_ca_shot, float* grad_cb_shot, void* stream);
 
 /*
- * Shot sum of the per-shot gradients (combine_grad): grad[j] = sum_s
+ * Shot sum of the per-shot gradients: grad[j] = sum_s
  * grad_shot[s][j], shots summed in ascending order (deterministic).
+ * Defined by: the page's kernel combine_grad, launched at the end of
+ * backward over the per-shot gradient workspace.
  * grad_ca/grad_cb: device float32 [ny][nx], overwritten.  A NULL pair
  * member is skipped.  (With model_per_shot each shot's gradient belongs to
  * its own model and is used as it is; the sum is still computed if asked.)
@@ -206,7 +253,8 @@ tm_status tm_grad(const tm_plan* plan, const float* grad_ca_shot, const float* g
 
 /*
  * Gradients in the physical parameters by the chain rule
- * (convert_grad_ca_cb_to_eps_sigma): with eps = EP0 eps_r (EP0 =
+ * (defined by the page's kernel convert_grad_ca_cb_to_eps_sigma: its
+ * closed forms in Ca, Cb and dt, and the EP0 value it defines): with eps = EP0 eps_r (EP0 =
  * 8.8541878128e-12 F/m) and s = sigma dt / (2 eps), the update
  * coefficients are Ca = (1 - s) / (1 + s) and Cb = (dt / eps) / (1 + s), so
  *   dJ/deps_r  = EP0 (dJ/dCa (1 - Ca) Cb / dt - dJ/dCb Cb^2 / dt),
@@ -229,9 +277,10 @@ tm_status tm_grad_eps_sigma(const tm_plan* plan, const float* ca, const float* c
                             float* grad_eps_r, float* grad_sigma, void* stream);
 
 /*
- * The FP8 snapshot encoding (TM_SNAP_FP8; FP8 E4M3 storage of the page's
- * fp8_e4m3_from_float / fp8_e4m3_to_float, its intrinsic path: OCP E4M3
- * with saturation to the largest finite value).  encode: float32 -> one
+ * The FP8 snapshot encoding (TM_SNAP_FP8), defined by the page's
+ * forward_kernel_e_with_storage_fp8 and its conversions fp8_e4m3_from_float /
+ * fp8_e4m3_to_float, their intrinsic path: OCP E4M3 with saturation to the
+ * largest finite value.  encode: float32 -> one
  * byte per element, round to nearest even, |x| > 448 -> +-448, NaN -> NaN;
  * decode: byte -> float32 (exact).  in/out: device arrays of n elements
  * (n >= 0; NULL allowed only for n == 0).  The same conversions are used
@@ -259,8 +308,8 @@ tm_status tm_timing_read(tm_plan* plan, double* total_ms, int64_t* count);
 
 /* Number of timed kernels, and the name of kernel ``k`` (the prefix of its
  * symbol name as profilers print it, with "_uq" for the two-step instances
- * that use one Cq value instead of reading the array; NULL when k is out of
- * range). */
+ * that use one Cq value instead of reading the array and "_store" for the
+ * forward launches that store snapshots; NULL when k is out of range). */
 int32_t tm_kernel_count(void);
 const char* tm_kernel_name(int32_t k);
 

@@ -242,7 +242,7 @@ def adjoint_range(wl, grad_r: np.ndarray, t0: int, t1: int, state: AdjointState,
         raise RuntimeError(f"orc_adjoint_range failed ({rc})")
 
 
-def gradient_checkpointed(wl, every: int, grad_r=None, residual=None, want_grad_f=True):
+def gradient_checkpointed(wl, every: int, grad_r=None, residual=None, want_grad_f=True, progress=None):
     """Records and the exact adjoint's gradients with bounded memory: the
     forward keeps its state every ``every`` steps; the adjoint replays each
     segment from its checkpoint (storing that segment's snapshots only) and
@@ -251,7 +251,8 @@ def gradient_checkpointed(wl, every: int, grad_r=None, residual=None, want_grad_
     results equal the full-storage ones.
 
     dJ/dr is ``grad_r`` if given, else ``residual(records)``, else the
-    records themselves (J = 1/2 |r|^2).  Returns a dict like
+    records themselves (J = 1/2 |r|^2).  ``progress(msg)``, if given, is
+    called after each forward and adjoint segment.  Returns a dict like
     ``misfit_and_gradient`` (without J)."""
     nt, S = wl.nt, wl.n_shots
     st = State(S, wl.ny, wl.nx)
@@ -260,6 +261,8 @@ def gradient_checkpointed(wl, every: int, grad_r=None, residual=None, want_grad_
     for ta in range(0, nt, every):
         ckpts[ta] = st.copy()
         forward(wl, ta, min(ta + every, nt), state=st, records=r)
+        if progress is not None:
+            progress(f"oracle forward {min(ta + every, nt)}/{nt}")
     del st
     if grad_r is None:
         grad_r = r if residual is None else residual(r)
@@ -273,6 +276,8 @@ def gradient_checkpointed(wl, every: int, grad_r=None, residual=None, want_grad_
         _, _, snaps = forward(wl, ta, tb, state=ckpts.pop(ta), store=True, segment=True)
         adjoint_range(wl, grad_r, ta, tb, adj, snaps, snap_t0=ta, gca=gca, gcb=gcb, grad_f=grad_f)
         del snaps
+        if progress is not None:
+            progress(f"oracle adjoint {ta}/{nt}")
     return dict(records=r, grad_f=grad_f, gca_shot=gca, gcb_shot=gcb, gca=shot_sum(gca), gcb=shot_sum(gcb),
                 residual=grad_r)
 

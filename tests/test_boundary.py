@@ -48,7 +48,8 @@ def test_timed_kernel_names():
     """The timing ids name the step kernels; _uq marks the instances that
     use one Cq value instead of reading the array."""
     names = [native.tm_kernel_name(k) for k in range(native.tm_kernel_count())]
-    assert names == ["k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2", "k_fwd_step2_uq", "k_adj_step2_uq"]
+    assert names == ["k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2", "k_fwd_step2_uq", "k_adj_step2_uq",
+                     "k_fwd_step_store", "k_fwd_step2_store", "k_fwd_step2_uq_store"]
     assert native.tm_kernel_name(-1) is None and native.tm_kernel_name(len(names)) is None
 
 
@@ -228,3 +229,72 @@ def test_per_shot_models_workspace(wl):
     per = inputs.per_shot_models(wl)
     assert per.ca.shape == (wl.n_shots, wl.ny, wl.nx)
     assert native.make_desc(per).model_per_shot == 1 and native.make_desc(wl).model_per_shot == 0
+
+
+def test_set_indices_on_the_host(wl):
+    """tm_plan_set_indices: bad indices and a geometry over the memory budget
+    leave the plan unchanged; a valid one sizes the workspace like a fresh
+    plan of that geometry and resets the call sequence."""
+    st, plan = native.tm_plan_create(make(wl), wl.cpml, wl.src, wl.rec)
+    assert st == native.TM_OK
+    try:
+        b0 = native.tm_workspace_bytes(plan)[1]
+        assert native.lib().tm_plan_set_indices(None, None, None) == native.TM_EINVAL
+        bad = wl.src.copy()
+        bad[1, 0] = wl.ny * wl.nx                        # outside the grid
+        assert native.tm_plan_set_indices(plan, bad, wl.rec) == native.TM_EINVAL
+        bad = wl.rec.copy()
+        bad[0, 1] = 0                                    # in the halo, not an E cell
+        assert native.tm_plan_set_indices(plan, wl.src, bad) == native.TM_EINVAL
+        assert native.tm_plan_set_indices(plan, None, wl.rec) == native.TM_EINVAL
+        assert native.tm_workspace_bytes(plan)[1] == b0
+        # receivers spread over many rows: more event rows, a larger workspace
+        rows = wl.pml_y0 + np.arange(wl.n_rec) * 3
+        rec = np.stack([rows * wl.nx + wl.pml_x0 + 2 + s for s in range(wl.n_shots)]).astype(np.int64)
+        assert native.tm_plan_set_indices(plan, wl.src, rec) == native.TM_OK
+        b1 = native.tm_workspace_bytes(plan)[1]
+        st, fresh = native.tm_plan_create(make(wl), wl.cpml, wl.src, rec)
+        assert st == native.TM_OK and native.tm_workspace_bytes(fresh)[1] == b1 > b0
+        native.tm_plan_destroy(fresh)
+        # the state of the old geometry is gone: gradients need a new forward
+        dev = FAKE_WS
+        assert native.tm_adjoint(plan, dev, b1, dev, dev, dev, dev, dev, None, dev, dev, None) == native.TM_ESTATE
+        assert native.tm_forward(plan, dev, b1, dev, dev, dev, dev, None, 3, 5, 0, None) == native.TM_ESTATE
+        # and back to the original geometry
+        assert native.tm_plan_set_indices(plan, wl.src, wl.rec) == native.TM_OK
+        assert native.tm_workspace_bytes(plan)[1] == b0
+    finally:
+        native.tm_plan_destroy(plan)
+    # over the budget: refused, plan unchanged
+    st, plan = native.tm_plan_create(make(wl, hbm_budget=b0), wl.cpml, wl.src, wl.rec)
+    assert st == native.TM_OK
+    try:
+        assert native.tm_plan_set_indices(plan, wl.src, rec) == native.TM_ENOMEM
+        assert native.tm_workspace_bytes(plan)[1] == b0
+        assert native.tm_plan_set_indices(plan, wl.src, wl.rec) == native.TM_OK
+    finally:
+        native.tm_plan_destroy(plan)
+
+
+def test_event_steps_override_is_bounded(monkeypatch):
+    """TM_FDTD_EVENT_STEPS cannot push an event buffer past its size bound:
+    a huge value gives the default block length (same workspace), a small
+    one a smaller workspace."""
+    wl = inputs.make_config(2, n_int=400, nt=30, n_shots=2, n_rec=5)    # 4 event rows of 444 cells
+    st, plan = native.tm_plan_create(make(wl, nt=5000), wl.cpml, wl.src, wl.rec)
+    b_default = native.tm_workspace_bytes(plan)[1]
+    native.tm_plan_destroy(plan)
+    monkeypatch.setenv("TM_FDTD_EVENT_STEPS", str(1 << 40))
+    st, plan = native.tm_plan_create(make(wl, nt=5000), wl.cpml, wl.src, wl.rec)
+    assert st == native.TM_OK
+    # (the default rounds the block down to an even length: at most one
+    # step of the four event buffers apart; unbounded, 5000 steps would
+    # add about 33 MB)
+    one_step = 4 * 4 * wl.nx * 4
+    assert abs(native.tm_workspace_bytes(plan)[1] - b_default) <= one_step + 4 * 256
+    native.tm_plan_destroy(plan)
+    monkeypatch.setenv("TM_FDTD_EVENT_STEPS", "8")
+    st, plan = native.tm_plan_create(make(wl, nt=5000), wl.cpml, wl.src, wl.rec)
+    assert st == native.TM_OK
+    assert native.tm_workspace_bytes(plan)[1] < b_default
+    native.tm_plan_destroy(plan)

@@ -262,7 +262,23 @@ def test_uniform_cq_selects_the_cq_free_instances():
             native.tm_timing_enable(prop.plan, 0)
         finally:
             prop.close()
-        return ({k: n for k, (_, n) in fwd.items() if n}, {k: n for k, (_, n) in adj.items() if n})
+        # storing launches are timed apart ("_store"): full store mode stores
+        # in tm_forward, checkpoint mode in the adjoint's replays only
+        stored_fwd = {k for k, (_, n) in fwd.items() if n and k.endswith("_store")}
+        stored_adj = {k for k, (_, n) in adj.items() if n and k.endswith("_store")}
+        assert (stored_fwd == set()) == (ckpt_every > 0), (ckpt_every, fwd)
+        assert (stored_adj != set()) == (ckpt_every > 0), (ckpt_every, adj)
+        assert all(not k.startswith("k_fwd") or k.endswith("_store")
+                   for k, (_, n) in fwd.items() if n and ckpt_every == 0), fwd
+
+        def merged(d):
+            out = {}
+            for k, (_, n) in d.items():
+                if n:
+                    key = k[:-len("_store")] if k.endswith("_store") else k
+                    out[key] = out.get(key, 0) + n
+            return out
+        return merged(fwd), merged(adj)
 
     uni = inputs.as_f32(inputs.random_workload(8, 40, 8, nt=40, n_shots=2, n_src=1, n_rec=4, seed=840,
                                                mu_range=(1.0, 1.0)))
@@ -723,3 +739,45 @@ def test_cpml_probe_sites_and_flags(orc, order, tb):
             e_o = rel_l2(got[:, 0, 0], ref[:, 0, 0])
             e_c = float(np.abs(got[:, 0, 0] - exp).max() / np.abs(exp).max())
             assert e_o <= REC_TOL and e_c <= 1e-5, (site, where, kappa, e_o, e_c)
+
+
+def test_set_indices_equals_a_fresh_plan(orc):
+    """A plan re-pointed at a new acquisition geometry with
+    tm_plan_set_indices (more event rows: a larger workspace) gives bitwise
+    the results of a plan created with that geometry, and those match the
+    oracle; the adjoint right after the switch is refused (TM_ESTATE)."""
+    import dataclasses
+
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wa = inputs.as_f32(inputs.random_workload(8, 50, 8, nt=60, n_shots=2, n_src=2, n_rec=6, seed=870))
+    rng = np.random.default_rng(871)
+    ys = rng.integers(wa.pml_y0 - 4, wa.pml_y1 + 4, size=(2, 6))
+    xs = rng.integers(wa.pml_x0, wa.pml_x1, size=(2, 6))
+    rec_b = (ys * wa.nx + xs).astype(np.int64)
+    wb = dataclasses.replace(wa, rec=rec_b)
+    fresh = run_gpu(wb, snap="f32")
+    prop = native.Propagator(wa)
+    try:
+        r = prop.forward(store=True)
+        prop.adjoint(r)
+        bytes_a = prop.ws_bytes
+        prop.set_indices(wb.src, wb.rec)
+        assert prop.ws_bytes >= bytes_a
+        with pytest.raises(native.TmError) as ei:
+            prop.adjoint(r)
+        assert ei.value.status == native.TM_ESTATE
+        r = prop.forward(store=True)
+        grad_f, gca, gcb = prop.adjoint(r)
+        torch.cuda.synchronize()
+        got = dict(records=r.cpu().numpy(), grad_f=grad_f.cpu().numpy(), gca_shot=gca.cpu().numpy(),
+                   gcb_shot=gcb.cpu().numpy())
+    finally:
+        prop.close()
+    for key in ("records", "grad_f", "gca_shot", "gcb_shot"):
+        np.testing.assert_array_equal(got[key], fresh[key], err_msg=key)
+    ref = run_oracle(orc, wb)
+    compare("records", got["records"], ref["records"], REC_TOL)
+    compare("gCa/shot", got["gca_shot"], ref["gca_shot"], GRAD_TOL["f32"], grid_regions(wb))

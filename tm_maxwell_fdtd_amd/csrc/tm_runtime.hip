@@ -138,12 +138,16 @@ struct Layout {
 // kernels writing or reading the others).
 constexpr int HOST_RING = 3;
 
-// Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes.
+// Timed stencil kernels (tm_timing_*): ids and symbol-name prefixes; the
+// forward launches that store snapshots are timed apart from the others
+// ("_store"), since they move more bytes.
 enum KernelId {
-    KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_ADJ_STEP2_UQ, KID_COUNT
+    KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_ADJ_STEP2_UQ,
+    KID_FWD_STEP_ST, KID_FWD_STEP2_ST, KID_FWD_STEP2_UQ_ST, KID_COUNT
 };
 const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2",
-                                             "k_fwd_step2_uq", "k_adj_step2_uq"};
+                                             "k_fwd_step2_uq", "k_adj_step2_uq", "k_fwd_step_store",
+                                             "k_fwd_step2_store", "k_fwd_step2_uq_store"};
 
 struct TimedLaunch {
     int kid;
@@ -549,7 +553,7 @@ void fwd_step(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap,
     a.ev = event_rows(p, q, false);
     a.es = event_step(p, false, t);
     const dim3 grid((unsigned)p->tiling_fwd.nblk), blk(NT);
-    timed(p, KID_FWD_STEP, t, st, [&] {
+    timed(p, snap == SNAP_NONE ? KID_FWD_STEP : KID_FWD_STEP_ST, t, st, [&] {
         if (snap == SNAP_F32) k_fwd_step<P, SNAP_F32><<<grid, blk, 0, st>>>(a);
         else if (snap == SNAP_BF16) k_fwd_step<P, SNAP_BF16><<<grid, blk, 0, st>>>(a);
         else if (snap == SNAP_FP8) k_fwd_step<P, SNAP_FP8><<<grid, blk, 0, st>>>(a);
@@ -581,7 +585,9 @@ void fwd_step2(tm_plan* p, const Ptrs& q, int cur, float* r, int64_t t, int snap
     a.es1 = event_step(p, false, t + 1);
     a.cq = p->cq_value;
     const dim3 grid((unsigned)p->tiling_fwd2.nblk), blk(NT);
-    timed(p, p->cq_uniform ? KID_FWD_STEP2_UQ : KID_FWD_STEP2, t, st, [&] {
+    const int kid = p->cq_uniform ? (snap == SNAP_NONE ? KID_FWD_STEP2_UQ : KID_FWD_STEP2_UQ_ST)
+                                  : (snap == SNAP_NONE ? KID_FWD_STEP2 : KID_FWD_STEP2_ST);
+    timed(p, kid, t, st, [&] {
         auto launch = [&](auto uq_t, auto cx_t) {
             constexpr bool UQ = decltype(uq_t)::value, CX = decltype(cx_t)::value;
             if (snap == SNAP_F32) k_fwd_step2<P, SNAP_F32, UQ, CX><<<grid, blk, 0, st>>>(a);
@@ -961,6 +967,38 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
 
+// Event-row tables of the sources and receivers (validated indices) into
+// the plan: the packed table block, the event-row count NS and the steps
+// per event block EB.
+tm_status set_events(tm_plan* p, const int64_t* src, const int64_t* rec)
+{
+    const tm_desc& d = p->d;
+    std::vector<int32_t> tables;
+    auto append = [&](const std::vector<int32_t>& v) {
+        const uint64_t at = tables.size();
+        tables.insert(tables.end(), v.begin(), v.end());
+        return at;
+    };
+    const EventTables et = build_events(src, d.n_src, rec, d.n_rec, d.n_shots, d.ny, d.nx);
+    if ((uint64_t)et.n_slots * (uint64_t)d.nx * 4 > EV_ROW_MAX) return TM_ENOMEM;
+    p->t_slot = append(et.row_slot); p->t_colcell = append(et.colcell); p->t_sshot = append(et.slot_shot);
+    p->t_cs = append(et.cell_src); p->t_sl = append(et.src_list);
+    p->t_cr = append(et.cell_rec); p->t_rl = append(et.rec_list);
+    p->t_spos = append(et.src_pos); p->t_rpos = append(et.rec_pos);
+    p->tables = std::move(tables);
+    p->NS = et.n_slots;
+    // steps per event block: each of the four event buffers stays within
+    // EV_BLOCK_BYTES; even, so that blocks do not split pairs of steps
+    const int64_t eb_max = p->NS > 0 ? std::max<int64_t>(1, (int64_t)(EV_BLOCK_BYTES / (p->NS * d.nx * 4))) : d.nt;
+    p->EB = std::min<int64_t>(d.nt, eb_max);
+    if (p->EB > 1 && p->EB < d.nt) p->EB &= ~int64_t(1);
+    if (const char* env = std::getenv("TM_FDTD_EVENT_STEPS")) {   // forced block length (tests, tuning)
+        const long long v = std::atoll(env);
+        if (v >= 1) p->EB = std::min<int64_t>(std::min<int64_t>(v, d.nt), eb_max);
+    }
+    return TM_OK;
+}
+
 tm_status courant_impl(tm_plan* p, void* ws, const float* cb, const float* cq, hipStream_t st, double* out,
                        bool* cq_one = nullptr, float* cq_val = nullptr)
 {
@@ -1069,27 +1107,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     g.slab = d.ny * d.nx;
     p->cpml.assign(cpml, cpml + 12 * L);
 
-    auto append = [&](const std::vector<int32_t>& v) {
-        const uint64_t at = p->tables.size();
-        p->tables.insert(p->tables.end(), v.begin(), v.end());
-        return at;
-    };
-    const EventTables et = build_events(src, d.n_src, rec, d.n_rec, d.n_shots, d.ny, d.nx);
-    p->t_slot = append(et.row_slot); p->t_colcell = append(et.colcell); p->t_sshot = append(et.slot_shot);
-    p->t_cs = append(et.cell_src); p->t_sl = append(et.src_list);
-    p->t_cr = append(et.cell_rec); p->t_rl = append(et.rec_list);
-    p->t_spos = append(et.src_pos); p->t_rpos = append(et.rec_pos);
-    p->NS = et.n_slots;
-    if ((uint64_t)p->NS * (uint64_t)d.nx * 4 > EV_ROW_MAX) { delete p; return TM_ENOMEM; }
-    // steps per event block: each of the four event buffers stays within
-    // EV_BLOCK_BYTES; even, so that blocks do not split pairs of steps
-    p->EB = p->NS > 0 ? std::max<int64_t>(1, std::min<int64_t>(d.nt, (int64_t)(EV_BLOCK_BYTES / (p->NS * d.nx * 4))))
-                      : d.nt;
-    if (p->EB > 1 && p->EB < d.nt) p->EB &= ~int64_t(1);
-    if (const char* env = std::getenv("TM_FDTD_EVENT_STEPS")) {   // forced block length (tests, tuning)
-        const long long v = std::atoll(env);
-        if (v >= 1) p->EB = std::min<int64_t>(v, d.nt);
-    }
+    if ((v = set_events(p, src, rec)) != TM_OK) { delete p; return v; }
     p->time_block = d.time_block == 0 ? 2 : (int)d.time_block;
     p->R = d.step_ratio > 1 ? d.step_ratio : 1;
     p->n_store = (d.nt + p->R - 1) / p->R;
@@ -1120,6 +1138,54 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
         return TM_ENOMEM;
     }
     *out = p;
+    return TM_OK;
+}
+
+TM_API tm_status tm_plan_set_indices(tm_plan* p, const int64_t* src, const int64_t* rec)
+{
+    if (p == nullptr) return TM_EINVAL;
+    const tm_desc& d = p->d;
+    tm_status v = validate_indices(src, d.n_shots, d.n_src, d.ny, d.nx, p->P);
+    if (v != TM_OK) return v;
+    if ((v = validate_indices(rec, d.n_shots, d.n_rec, d.ny, d.nx, p->P)) != TM_OK) return v;
+    // what the new tables replace, restored when they do not fit
+    struct Saved {
+        std::vector<int32_t> tables;
+        uint64_t off[9];
+        int64_t NS, EB;
+        Layout lay;
+    } old{p->tables, {p->t_slot, p->t_colcell, p->t_sshot, p->t_cs, p->t_sl, p->t_cr, p->t_rl, p->t_spos,
+                      p->t_rpos}, p->NS, p->EB, p->lay};
+    auto restore = [&] {
+        p->tables = std::move(old.tables);
+        p->t_slot = old.off[0]; p->t_colcell = old.off[1]; p->t_sshot = old.off[2]; p->t_cs = old.off[3];
+        p->t_sl = old.off[4]; p->t_cr = old.off[5]; p->t_rl = old.off[6]; p->t_spos = old.off[7];
+        p->t_rpos = old.off[8];
+        p->NS = old.NS;
+        p->EB = old.EB;
+        p->lay = old.lay;
+    };
+    v = set_events(p, src, rec);
+    if (v == TM_OK && !make_layout(p)) v = TM_EINVAL;
+    if (v == TM_OK && d.hbm_budget > 0 && p->lay.total > d.hbm_budget) v = TM_ENOMEM;
+    if (v == TM_OK && p->pinned != nullptr) {
+        // earlier calls may still be copying the old tables from the pinned
+        // staging buffer: wait for the device before freeing it
+        if (hipDeviceSynchronize() != hipSuccess) v = TM_EHIP;
+    }
+    if (v != TM_OK) {
+        restore();
+        return v;
+    }
+    if (p->pinned != nullptr) {
+        (void)hipHostFree(p->pinned);
+        p->pinned = nullptr;            // restaged at the next device call
+    }
+    // the workspace's state belongs to the old geometry
+    p->ws_last = nullptr;
+    p->fwd_next = -1;
+    p->stored_ok = false;
+    p->fwd_complete = false;
     return TM_OK;
 }
 

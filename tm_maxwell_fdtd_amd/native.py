@@ -77,6 +77,8 @@ def lib():
         L.tm_workspace_bytes.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
         L.tm_courant.restype = ctypes.c_int
         L.tm_courant.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_double)]
+        L.tm_plan_set_indices.restype = ctypes.c_int
+        L.tm_plan_set_indices.argtypes = [_vp, _vp, _vp]
         L.tm_forward.restype = ctypes.c_int
         L.tm_forward.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _vp]
@@ -147,6 +149,12 @@ def tm_plan_create(desc: tm_desc, cpml: np.ndarray, src: Optional[np.ndarray], r
     out = _vp()
     st = lib().tm_plan_create(ctypes.byref(desc), ptr(cpml), ptr(src), ptr(rec), ctypes.byref(out))
     return st, out.value
+
+
+def tm_plan_set_indices(plan, src: Optional[np.ndarray], rec: Optional[np.ndarray]) -> int:
+    src = None if src is None else np.ascontiguousarray(src, dtype=np.int64)
+    rec = None if rec is None else np.ascontiguousarray(rec, dtype=np.int64)
+    return lib().tm_plan_set_indices(plan, ptr(src), ptr(rec))
 
 
 def tm_plan_destroy(plan):
@@ -272,6 +280,24 @@ class Propagator:
             self.close()
         except Exception:
             pass
+
+    def set_indices(self, src, rec):
+        """New source / receiver cells ([S][n_src], [S][n_rec] int64) for the
+        same plan; the workspace is reallocated when its size changes."""
+        import torch
+
+        torch.cuda.synchronize(self.device)
+        st = tm_plan_set_indices(self.plan, src, rec)
+        _check(st, "tm_plan_set_indices")
+        st, nbytes = tm_workspace_bytes(self.plan)
+        _check(st, "tm_workspace_bytes")
+        if nbytes != self.ws_bytes:
+            self.ws = None
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self.ws_bytes = nbytes
+        import dataclasses
+
+        self.wl = dataclasses.replace(self.wl, src=np.asarray(src, np.int64), rec=np.asarray(rec, np.int64))
 
     def courant(self):
         st, c = tm_courant(self.plan, ptr(self.ws), self.ws_bytes, ptr(self.cb), ptr(self.cq),
