@@ -183,6 +183,23 @@ tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb
                      const float* cq, void* stream, double* courant);
 
 /*
+ * tm_courant without a workspace, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation) or that check a model before allocating the workspace.
+ * Same result as tm_courant (bitwise; same kernels).  Its scratch (258
+ * floats: 256 partial maxima and two words of the uniform-Cq test) is a
+ * static device array of the library, one per device, held until the
+ * process ends; the scratch size does not depend on the model size, so no
+ * size is refused for it.  Allocates nothing (no hipMalloc / hipFree),
+ * synchronises ``stream``.  Calls that overlap on one device share the
+ * array and race: serialise them.  TM_EINVAL for a NULL argument or a
+ * device ordinal of 64 or more; TM_EHIP when the array's device address
+ * cannot be found.
+ */
+tm_status tm_courant_noalloc(tm_plan* plan, const float* cb, const float* cq, void* stream,
+                             double* courant);
+
+/*
  * Forward propagation of all shots over steps [t0, t1), 0 <= t0 < t1 <= nt.
  * Defined by: the page's host launchers forward (without TM_FWD_STORE) and
  * forward_with_storage (with it), and the per-step order of their loop:

@@ -167,6 +167,8 @@ def test_null_arguments():
     assert L.tm_forward(None, None, 0, None, None, None, None, None, 0, 1, 0, None) == native.TM_EINVAL
     assert L.tm_adjoint(None, None, 0, None, None, None, None, None, None, None, None, None) == native.TM_EINVAL
     assert L.tm_grad(None, None, None, None, None, None) == native.TM_EINVAL
+    c = ctypes.c_double(0.0)
+    assert L.tm_courant_noalloc(None, None, None, None, ctypes.byref(c)) == native.TM_EINVAL
 
 
 def test_call_sequence_checked_before_launch(wl):

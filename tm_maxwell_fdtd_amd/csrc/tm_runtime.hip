@@ -28,6 +28,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -49,6 +50,7 @@ uint64_t align_up(uint64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 constexpr uint64_t BLOCK_MAX = (uint64_t(1) << 31) - ALIGN;   // one buffer view
 constexpr uint64_t EV_BLOCK_BYTES = uint64_t(16) << 20;        // one event-row buffer (a run of steps)
 constexpr uint64_t EV_ROW_MAX = uint64_t(1) << 29;              // one step's event rows (add + out in one view)
+constexpr uint64_t SCRATCH_BYTES = 4096;                        // the workspace's scratch area
 
 double abs_coef_sum(int order)
 {
@@ -260,7 +262,7 @@ bool make_layout(tm_plan* p)
     auto take = [&](uint64_t bytes) { uint64_t at = o; o = align_up(o + bytes); return at; };
     L.cpml = take(12 * (uint64_t)g.L * 4);
     L.tables = take(p->tables.size() * 4);
-    L.scratch = take(4096);
+    L.scratch = take(SCRATCH_BYTES);
     L.model_bytes = 3 * L.slab_b;
     L.model_stride = d.model_per_shot ? L.model_bytes : 0;
     L.model = take(L.model_bytes * (d.model_per_shot ? S : 1));
@@ -999,22 +1001,29 @@ tm_status set_events(tm_plan* p, const int64_t* src, const int64_t* rec)
     return TM_OK;
 }
 
-tm_status courant_impl(tm_plan* p, void* ws, const float* cb, const float* cq, hipStream_t st, double* out,
+// Partial maxima of the Courant reduction, plus two words of the uniform-Cq
+// test: the device scratch the check uses (COURANT_WORDS floats).
+constexpr int COURANT_NB = 256;
+constexpr int COURANT_WORDS = COURANT_NB + 2;
+static_assert(COURANT_WORDS * sizeof(float) <= SCRATCH_BYTES, "Courant scratch exceeds the workspace's area");
+
+// scratch: COURANT_WORDS floats of device memory (the workspace's scratch
+// area, or the static array of tm_courant_noalloc).
+tm_status courant_impl(tm_plan* p, float* scratch, const float* cb, const float* cq, hipStream_t st, double* out,
                        bool* cq_one = nullptr, float* cq_val = nullptr)
 {
-    const Ptrs q = pointers(p, ws);
-    constexpr int NB = 256;
+    constexpr int NB = COURANT_NB;
     const int64_t n = p->g.slab * (p->d.model_per_shot ? p->d.n_shots : 1);   // every shot's model
-    k_max_cbcq<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, n, q.scratch);
+    k_max_cbcq<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, n, scratch);
     HIPCHK(hipGetLastError());
     // whether Cq holds one value (two words after the NB partial maxima)
-    uint32_t* info = reinterpret_cast<uint32_t*>(q.scratch + NB);
-    k_zero<<<dim3(1), dim3(64), 0, st>>>(q.scratch + NB, 2);
+    uint32_t* info = reinterpret_cast<uint32_t*>(scratch + NB);
+    k_zero<<<dim3(1), dim3(64), 0, st>>>(scratch + NB, 2);
     HIPCHK(hipGetLastError());
     k_cq_uniform<<<dim3(NB), dim3(256), 0, st>>>(cq, n, info);
     HIPCHK(hipGetLastError());
-    float part[NB + 2];
-    HIPCHK(hipMemcpyAsync(part, q.scratch, sizeof(part), hipMemcpyDeviceToHost, st));
+    float part[COURANT_WORDS];
+    HIPCHK(hipMemcpyAsync(part, scratch, sizeof(part), hipMemcpyDeviceToHost, st));
     HIPCHK(hipStreamSynchronize(st));
     double m = 0.0;
     for (int i = 0; i < NB; ++i) {
@@ -1261,7 +1270,50 @@ TM_API tm_status tm_courant(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     if (p == nullptr || cb == nullptr || cq == nullptr || courant == nullptr) return TM_EINVAL;
     tm_status v = check_ws(p, ws, ws_bytes);
     if (v != TM_OK) return v;
-    return courant_impl(p, ws, cb, cq, as_stream(stream), courant);
+    return courant_impl(p, pointers(p, ws).scratch, cb, cq, as_stream(stream), courant);
+}
+
+// ---------------------------------------------------------------------------
+// tm_courant_noalloc: the Courant check with its scratch in static device
+// memory, for callers that cannot allocate (and before a workspace exists).
+// Every device the library runs on holds one copy of the array until the
+// process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns on that device (the array's name is a host
+// stand-in).  Calls that overlap on one device share the array and race.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) float noalloc_scratch[COURANT_WORDS];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+float* noalloc_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// The device address of the current device's copy of noalloc_scratch,
+// looked up once per device.
+tm_status noalloc_scratch_ptr(float** out)
+{
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return TM_EINVAL;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (noalloc_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || ptr == nullptr) return TM_EHIP;
+        noalloc_ptr[dev] = static_cast<float*>(ptr);
+    }
+    *out = noalloc_ptr[dev];
+    return TM_OK;
+}
+}  // namespace
+
+TM_API tm_status tm_courant_noalloc(tm_plan* p, const float* cb, const float* cq, void* stream, double* courant)
+{
+    if (p == nullptr || cb == nullptr || cq == nullptr || courant == nullptr) return TM_EINVAL;
+    float* scratch = nullptr;
+    tm_status v = noalloc_scratch_ptr(&scratch);
+    if (v != TM_OK) return v;
+    return courant_impl(p, scratch, cb, cq, as_stream(stream), courant);
 }
 
 TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float* ca, const float* cb,
@@ -1281,7 +1333,7 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     float cq_val = 0.0f;
     if (flags & TM_FWD_CHECK) {
         double c = 0.0;
-        v = courant_impl(p, ws, cb, cq, st, &c, &cq_one, &cq_val);
+        v = courant_impl(p, pointers(p, ws).scratch, cb, cq, st, &c, &cq_one, &cq_val);
         if (v != TM_OK) return v;
         if (!(c <= 1.0)) return TM_EUNSTABLE;
     }

@@ -77,6 +77,8 @@ def lib():
         L.tm_workspace_bytes.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
         L.tm_courant.restype = ctypes.c_int
         L.tm_courant.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_double)]
+        L.tm_courant_noalloc.restype = ctypes.c_int
+        L.tm_courant_noalloc.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_double)]
         L.tm_plan_set_indices.restype = ctypes.c_int
         L.tm_plan_set_indices.argtypes = [_vp, _vp, _vp]
         L.tm_forward.restype = ctypes.c_int
@@ -170,6 +172,12 @@ def tm_workspace_bytes(plan):
 def tm_courant(plan, ws, ws_bytes, cb, cq, stream):
     c = ctypes.c_double(0.0)
     st = lib().tm_courant(plan, ws, ws_bytes, cb, cq, stream, ctypes.byref(c))
+    return st, c.value
+
+
+def tm_courant_noalloc(plan, cb, cq, stream):
+    c = ctypes.c_double(0.0)
+    st = lib().tm_courant_noalloc(plan, cb, cq, stream, ctypes.byref(c))
     return st, c.value
 
 
