@@ -102,6 +102,17 @@ def kernel_bytes(name, wl, store, snap_bytes):
         name, store = name[:-len("_store")], True
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
+    if name in ("k_fwd_small", "k_adj_small"):
+        # resident kernels: one launch runs a whole event block (the whole
+        # run here) on chip; HBM sees the state in and out (fields and band
+        # memories), the model once, and per step the snapshots (and in the
+        # adjoint the gradients once, read and written)
+        p = wl.order // 2
+        full = wl.ny * wl.nx
+        state = 2 * 4 * (3 * full + 2 * (band_y + band_x))
+        snaps = wl.nt * 2 * snap_bytes * interior if store else 0
+        grads = 16 * interior if (store and name == "k_adj_small") else 0
+        return S * (state + 12 * full + snaps + grads)
     if name in ("k_fwd_step", "k_fwd_step_uq"):
         snaps = 2 * snap_bytes * interior if store else 0
         per_cell = 32 if name.endswith("_uq") else 36

@@ -95,11 +95,17 @@ typedef struct tm_desc {
     int64_t ckpt_every;     /* 0: store every step; K > 0: checkpoint the state
                                every K steps and replay segments in tm_adjoint  */
     uint64_t hbm_budget;    /* bytes the workspace may use; 0 = unlimited       */
-    int32_t time_block;     /* time steps per launch of the forward and of the
-                               adjoint: 1, or 2 (two steps in one pass over the
-                               state; the adjoint pairs steps only with the
-                               snapshots in device memory); 0 = default (2).
-                               Both give bitwise the same results.             */
+    int32_t time_block;     /* how the steps are launched: 1 = one step per
+                               launch of the streaming kernels; 2 = two steps
+                               in one pass over the state (the adjoint pairs
+                               steps only with the snapshots in device
+                               memory); 3 = resident kernels wherever the grid
+                               fits one workgroup's LDS (ny * nx < 8192, a
+                               whole run of steps per launch, one workgroup
+                               per shot; snapshots in device memory and no
+                               checkpoints, else 2); 0 = default: 3 with 16
+                               shots or more, else 2.  All give bitwise the
+                               same results.                                   */
     int32_t storage;        /* tm_storage: where a storing forward keeps the
                                snapshots (full-store mode only)                */
     int64_t step_ratio;     /* store snapshots (and accumulate gradients) every

@@ -249,7 +249,7 @@ def test_uniform_cq_selects_the_cq_free_instances():
     from tm_maxwell_fdtd_amd import native
 
     def counts(wl, check, ckpt_every=0, other_cq=False):
-        prop = native.Propagator(wl, ckpt_every=ckpt_every)
+        prop = native.Propagator(wl, ckpt_every=ckpt_every, time_block=2)   # (not the resident kernels)
         try:
             native.tm_timing_enable(prop.plan, 1)
             r = prop.forward(store=True, check=check)
@@ -712,12 +712,12 @@ def test_stretched_cpml(orc, order, snap, ckpt, tb, mu):
 
 
 @pytest.mark.parametrize("order", inputs.ORDERS)
-@pytest.mark.parametrize("tb", [1, 2])
+@pytest.mark.parametrize("tb", [3, 1, 2])
 def test_cpml_probe_sites_and_flags(orc, order, tb):
     """The oracle's closed-form CPML probe (one filter site at one index,
     tests/cpml_probe.py) through the C ABI: every site at lo-1, lo, hi-2,
     hi-1 and hi, kappa 1.7 and 4, records against the oracle and against the
-    closed form."""
+    closed form; time_block 3 runs the resident small-grid kernels."""
     import cpml_probe
 
     from tm_maxwell_fdtd_amd import native
@@ -781,3 +781,115 @@ def test_set_indices_equals_a_fresh_plan(orc):
     ref = run_oracle(orc, wb)
     compare("records", got["records"], ref["records"], REC_TOL)
     compare("gCa/shot", got["gca_shot"], ref["gca_shot"], GRAD_TOL["f32"], grid_regions(wb))
+
+
+# ---------------------------------------------------------------------------
+# Resident kernels for small grids (the whole shot in one workgroup's LDS)
+# ---------------------------------------------------------------------------
+
+def _kernel_counts(wl, **kw):
+    """Run forward (storing) + adjoint with timing on; the kernels that ran."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    prop = native.Propagator(wl, **kw)
+    try:
+        native.tm_timing_enable(prop.plan, 1)
+        r = prop.forward(store=True)
+        prop.adjoint(r)
+        torch.cuda.synchronize()
+        _, kt = native.tm_timing_read(prop.plan)
+        native.tm_timing_enable(prop.plan, 0)
+    finally:
+        prop.close()
+    return {k for k, (_, n) in kt.items() if n}
+
+
+@pytest.mark.parametrize("order", inputs.ORDERS)
+@pytest.mark.parametrize("snap,ratio,kappa", [("f32", 1, 1.0), ("bf16", 1, 4.0), ("fp8", 1, 1.0), ("f32", 3, 4.0)])
+def test_resident_small_grid_bitwise(orc, order, snap, ratio, kappa):
+    """A grid that fits one workgroup's LDS runs the resident kernels with
+    time_block 3: bitwise the records, per-shot gradients and grad_f of one
+    step per launch, and the oracle's within the tolerances.
+    Sources and receivers anywhere (bands, edge rows), duplicates and
+    negative indices, stretched CPML, snapshot kinds and step ratios."""
+    wl = inputs.random_workload(order, 40, 7, nt=57, n_shots=3, n_src=3, n_rec=6, seed=1300 + order,
+                                src_anywhere=True, kappa_max=kappa)
+    wl.src[1, 1] = wl.src[1, 0]
+    wl.src[2, 2] = -1
+    wl.rec[0, 3] = wl.rec[0, 2]
+    wl.rec[2, 0] = -1
+    wl.rec[1, 4] = wl.src[1, 0]
+    wl = inputs.as_f32(wl)
+    assert wl.ny * wl.nx <= 8192
+    ran = _kernel_counts(wl, snap=snap, step_ratio=ratio, time_block=3)
+    assert "k_adj_small" in ran and any(k.startswith("k_fwd_small") for k in ran), ran
+    assert not any(k.startswith(("k_fwd_step", "k_adj_step")) for k in ran), ran
+    got = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=3)
+    one = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=key)
+    if snap == "f32":
+        ref = orc.misfit_and_gradient(wl, step_ratio=ratio)
+        regions = grid_regions(wl)
+        compare("records", got["records"], ref["records"], REC_TOL)
+        compare("gCa/shot", got["gca_shot"], ref["gca_shot"], GRAD_TOL["f32"], regions)
+        compare("gCb/shot", got["gcb_shot"], ref["gcb_shot"], GRAD_TOL["f32"], regions)
+        compare("grad_f", got["grad_f"], ref["grad_f"], GRAD_TOL["f32"])
+
+
+@pytest.mark.parametrize("case", ["chunks", "event-blocks", "per-shot-models", "no-grads", "ckpt-plan"])
+def test_resident_small_grid_modes(monkeypatch, case):
+    """The resident kernels under the other call patterns, bitwise against
+    one step per launch: forward chunks (the state crosses launches), short
+    event blocks (one launch per block), one model per shot, an adjoint
+    without gradients, and a checkpointing plan (its storing forward and
+    replays stream, its gradient-free calls may run resident)."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.random_workload(4, 40, 7, nt=41, n_shots=2, n_src=2, n_rec=5, seed=1320,
+                                              src_anywhere=True, kappa_max=3.0))
+    kw, chunks = {}, None
+    if case == "chunks":
+        chunks = [7, 8, 30]
+    elif case == "event-blocks":
+        monkeypatch.setenv("TM_FDTD_EVENT_STEPS", "6")
+    elif case == "per-shot-models":
+        wl = inputs.as_f32(inputs.per_shot_models(wl))
+    elif case == "ckpt-plan":
+        kw = dict(ckpt_every=9)
+    if case == "no-grads":
+        outs = []
+        for tb in (3, 1):
+            prop = native.Propagator(wl, time_block=tb)
+            try:
+                r = prop.forward(store=False)
+                d = torch.randn(r.shape, generator=torch.Generator().manual_seed(5)).to(prop.device)
+                gf, _, _ = prop.adjoint(d, want_grads=False)
+                torch.cuda.synchronize()
+                outs.append((r.cpu().numpy(), gf.cpu().numpy()))
+            finally:
+                prop.close()
+        np.testing.assert_array_equal(outs[0][0], outs[1][0])
+        np.testing.assert_array_equal(outs[0][1], outs[1][1])
+        return
+    got = run_gpu(wl, snap="f32", chunks=chunks, time_block=3, **kw)
+    one = run_gpu(wl, snap="f32", chunks=chunks, time_block=1, **kw)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=f"{case} {key}")
+
+
+def test_resident_kernels_by_default_from_16_shots():
+    """time_block 0 picks the resident kernels for a grid that fits with 16
+    shots or more, the streaming kernels with fewer; bitwise equal."""
+    wl16 = inputs.as_f32(inputs.make_config(1, n_shots=16, nt=40))
+    wl4 = inputs.as_f32(inputs.make_config(1, n_shots=4, nt=40))
+    assert "k_adj_small" in _kernel_counts(wl16)
+    assert "k_adj_small" not in _kernel_counts(wl4)
+    got = run_gpu(wl16)
+    two = run_gpu(wl16, time_block=2)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], two[key], err_msg=key)

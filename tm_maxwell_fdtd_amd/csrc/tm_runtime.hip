@@ -38,6 +38,7 @@
 #include "tm_step.hpp"
 #include "tm_step2.hpp"
 #include "tm_adj2.hpp"
+#include "tm_small.hpp"
 
 using namespace tmf;
 
@@ -145,11 +146,13 @@ constexpr int HOST_RING = 3;
 // ("_store"), since they move more bytes.
 enum KernelId {
     KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_ADJ_STEP2_UQ,
-    KID_FWD_STEP_ST, KID_FWD_STEP2_ST, KID_FWD_STEP2_UQ_ST, KID_COUNT
+    KID_FWD_STEP_ST, KID_FWD_STEP2_ST, KID_FWD_STEP2_UQ_ST, KID_FWD_SMALL, KID_FWD_SMALL_ST, KID_ADJ_SMALL,
+    KID_COUNT
 };
 const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2",
                                              "k_fwd_step2_uq", "k_adj_step2_uq", "k_fwd_step_store",
-                                             "k_fwd_step2_store", "k_fwd_step2_uq_store"};
+                                             "k_fwd_step2_store", "k_fwd_step2_uq_store", "k_fwd_small",
+                                             "k_fwd_small_store", "k_adj_small"};
 
 struct TimedLaunch {
     int kid;
@@ -162,7 +165,10 @@ struct tm_plan {
     Geo g{};
     Tiling tiling_fwd{}, tiling_adj{};   // per device, made at the first device call
     Tiling tiling_fwd2{}, tiling_adj2{};
-    int time_block = 2;                  // time steps per launch of the forward and the adjoint (1 or 2)
+    int time_block = 2;                  // time steps per launch of the streaming kernels (1 or 2)
+    int resident = 0;                    // resident kernels: 0 never, 1 where they fit and the shots are
+                                         // many (time_block 0), 2 wherever they fit (time_block 3)
+    bool small = false;                  // the resident kernels run (per device, with the tilings)
     int tiling_device = -1;
     std::vector<float> cpml;             // [12][L]
     std::vector<int32_t> tables;         // event-row tables, packed
@@ -685,6 +691,79 @@ void adj_step2(tm_plan* p, const Ptrs& q, int64_t t, int64_t k, int snap, const 
     });
 }
 
+// Forward steps [ta, tb) of one event block with the resident kernel (set
+// cur -> 1-cur); stored steps go to the device store.
+template <int P>
+void fwd_small(tm_plan* p, const Ptrs& q, int cur, int64_t ta, int64_t tb, int snap, hipStream_t st)
+{
+    const Layout& L = p->lay;
+    SmallArgs a{};
+    a.g = p->g;
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.fset[cur];
+    a.set1 = q.base + L.fset[1 - cur];
+    a.snap = snap != SNAP_NONE ? q.snap : nullptr;
+    a.snap_stride = L.snap_stride;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
+    a.R = (int)p->R;
+    a.ratio = (float)p->R;
+    a.t0 = (int)ta;
+    a.t1 = (int)tb;
+    a.ev = event_rows(p, q, false);
+    const EventStep e0 = event_step(p, false, ta);
+    a.ev_add0 = e0.add;
+    a.ev_out0 = e0.out;
+    a.ev_row = (uint32_t)L.ev_row;
+    const uint32_t lds = small_lds_bytes(p->g, false);
+    const dim3 grid((unsigned)p->d.n_shots), blk(NTS);
+    timed(p, snap == SNAP_NONE ? KID_FWD_SMALL : KID_FWD_SMALL_ST, ta, st, [&] {
+        if (snap == SNAP_F32) k_fwd_small<P, SNAP_F32><<<grid, blk, lds, st>>>(a);
+        else if (snap == SNAP_BF16) k_fwd_small<P, SNAP_BF16><<<grid, blk, lds, st>>>(a);
+        else if (snap == SNAP_FP8) k_fwd_small<P, SNAP_FP8><<<grid, blk, lds, st>>>(a);
+        else k_fwd_small<P, SNAP_NONE><<<grid, blk, lds, st>>>(a);
+    });
+}
+
+// Adjoint steps tb-1 .. ta of one event block with the resident kernel (set
+// k%2 -> (k+1)%2); snapshots from the device store when snap is set.
+template <int P>
+void adj_small(tm_plan* p, const Ptrs& q, int64_t ta, int64_t tb, int64_t k, int snap, float* gca, float* gcb,
+               hipStream_t st)
+{
+    const Layout& L = p->lay;
+    SmallArgs a{};
+    a.g = p->g;
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.aset[k & 1];
+    a.set1 = q.base + L.aset[(k + 1) & 1];
+    a.snap = snap != SNAP_NONE ? q.snap : nullptr;
+    a.snap_stride = L.snap_stride;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
+    a.R = (int)p->R;
+    a.ratio = (float)p->R;
+    a.t0 = (int)ta;
+    a.t1 = (int)tb;
+    a.ev = event_rows(p, q, true);
+    const EventStep e0 = event_step(p, true, ta);
+    a.ev_add0 = e0.add;
+    a.ev_out0 = e0.out;
+    a.ev_row = (uint32_t)L.ev_row;
+    a.gca = gca;
+    a.gcb = gcb;
+    const uint32_t lds = small_lds_bytes(p->g, true);
+    const dim3 grid((unsigned)p->d.n_shots), blk(NTS);
+    timed(p, KID_ADJ_SMALL, ta, st, [&] {
+        if (snap == SNAP_F32) k_adj_small<P, SNAP_F32><<<grid, blk, lds, st>>>(a);
+        else if (snap == SNAP_BF16) k_adj_small<P, SNAP_BF16><<<grid, blk, lds, st>>>(a);
+        else if (snap == SNAP_FP8) k_adj_small<P, SNAP_FP8><<<grid, blk, lds, st>>>(a);
+        else k_adj_small<P, SNAP_NONE><<<grid, blk, lds, st>>>(a);
+    });
+}
+
 int snap_kind(const tm_plan* p)
 {
     return p->d.snap == TM_SNAP_BF16 ? SNAP_BF16 : p->d.snap == TM_SNAP_FP8 ? SNAP_FP8 : SNAP_F32;
@@ -771,6 +850,17 @@ tm_status device_tiling(tm_plan* p)
     p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W, CH_MAX, ncu, 4 * P - 3);
     p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W, CH2_MAX, ncu, 6 * P - 3);
     p->tiling_adj2 = make_tiling(p->d, P, ca2, Strip2<P>::W, CHA2_MAX, ncu, 8 * P - 3);
+    // resident kernels: the whole shot in one workgroup's LDS
+    int lds_max = 0;
+    HIPCHK(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+    // (by default only with many shots: one workgroup, one CU, per shot is
+    // slower than the streaming kernels spread over the device for a few
+    // shots; measured on the 86^2 order-2 grid, the resident kernels win
+    // from about 16 shots on)
+    const bool fits = p->g.slab <= SMALL_CELLS && p->g.ny < 2048 && p->d.nt < (int64_t(1) << 30) &&
+                      small_lds_bytes(p->g, false) <= (uint32_t)lds_max &&
+                      small_lds_bytes(p->g, true) <= (uint32_t)lds_max;
+    p->small = fits && (p->resident == 2 || (p->resident == 1 && p->d.n_shots >= SMALL_MIN_SHOTS));
     p->tiling_device = dev;
     return TM_OK;
 }
@@ -818,6 +908,10 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
                         int snap, SnapAt snap_at, bool ckpt, bool host, hipStream_t st)
 {
     auto stored = [&](int64_t t) { return snap != SNAP_NONE && t % p->R == 0; };
+    // the resident kernel runs each event block in one launch: snapshots in
+    // the device store of full-store mode (not a replay's segment buffer),
+    // or none; no checkpoints, no host store
+    const bool small = p->small && !ckpt && !host && (p->K == 0 || snap == SNAP_NONE);
     int64_t ev_a = t0, ev_b = t0;        // event block of the current steps: [ev_a, ev_b)
     tm_status v = TM_OK;
     for (int64_t t = t0; t < t1;) {
@@ -826,6 +920,12 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
             ev_a = t;
             ev_b = std::min(t1, (t / p->EB + 1) * p->EB);
             if ((v = events_add(p, q, false, f, ev_a, ev_b, st)) != TM_OK) return v;
+        }
+        if (small) {
+            fwd_small<P>(p, q, *cur, t, ev_b, snap, st);
+            *cur = 1 - *cur;
+            t = ev_b;
+            continue;
         }
         if (ckpt && t > 0 && t % p->K == 0) {
             const int64_t slot = t / p->K - 1;
@@ -916,6 +1016,11 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
         }
         for (int64_t t = nt - 1; t >= 0; ++k) {
             if ((v = events(t)) != TM_OK) return v;
+            if (p->small && !host) {                                           // the event block in one launch
+                adj_small<P>(p, q, ev_a, t + 1, k, snap, gca, gcb, st);
+                t = ev_a - 1;
+                continue;
+            }
             if (p->time_block == 2 && !host && t >= 1 && t - 1 >= ev_a) {   // steps t, t-1 in one launch
                 const bool uA = want_grad && t % p->R == 0, uB = want_grad && (t - 1) % p->R == 0;
                 const uint64_t oA = (uint64_t)(uA ? dev_slot(p, t) : 0) * p->lay.snap_stride;
@@ -1070,7 +1175,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16 && d.snap != TM_SNAP_FP8) return TM_EINVAL;
-    if (d.time_block < 0 || d.time_block > 2) return TM_EINVAL;
+    if (d.time_block < 0 || d.time_block > 3) return TM_EINVAL;
     if (d.storage != TM_STORE_DEVICE && d.storage != TM_STORE_HOST) return TM_EINVAL;
     if (d.step_ratio < 0) return TM_EINVAL;
     if (d.model_per_shot != 0 && d.model_per_shot != 1) return TM_EINVAL;
@@ -1117,7 +1222,8 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     p->cpml.assign(cpml, cpml + 12 * L);
 
     if ((v = set_events(p, src, rec)) != TM_OK) { delete p; return v; }
-    p->time_block = d.time_block == 0 ? 2 : (int)d.time_block;
+    p->time_block = (d.time_block == 0 || d.time_block == 3) ? 2 : (int)d.time_block;
+    p->resident = d.time_block == 0 ? 1 : d.time_block == 3 ? 2 : 0;
     p->R = d.step_ratio > 1 ? d.step_ratio : 1;
     p->n_store = (d.nt + p->R - 1) / p->R;
     p->storage = (int)d.storage;
