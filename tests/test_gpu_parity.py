@@ -163,6 +163,28 @@ def test_deterministic_and_chunked():
         prop.close()
 
 
+@pytest.mark.parametrize("order,n_int,nx_int,npml,shots", [
+    (8, 40, 200, 240, 2),      # x bands wider than a strip: two band strips on the left
+    (4, 60, 700, 20, 3),       # band strips at both edges, two interior strips
+    (2, 50, 1000, 12, 1),      # three interior strips
+])
+def test_balanced_tiling_bitwise(monkeypatch, order, n_int, nx_int, npml, shots):
+    """The cost-balanced cut of the two-step kernels' strips into chunks
+    (more, shorter chunks for band strips, chunk edges at weighted row
+    quantiles; forced on these small grids with TM_FDTD_BALANCE=2) gives
+    bitwise the records, per-shot gradients and grad_f of the uniform cut."""
+    wl = inputs.as_f32(inputs.random_workload(order, n_int, npml, nt=40, n_shots=shots, n_src=2, n_rec=6,
+                                              seed=611 + order, nx_int=nx_int))
+    wl.rec = np.concatenate([wl.src, wl.src + 1, wl.src + wl.nx], axis=1)   # receivers by the sources
+    monkeypatch.setenv("TM_FDTD_BALANCE", "0")
+    uni = run_gpu(wl, snap="f32", time_block=2)
+    monkeypatch.setenv("TM_FDTD_BALANCE", "2")
+    bal = run_gpu(wl, snap="f32", time_block=2)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(bal[key], uni[key], err_msg=f"order {order} {key}")
+    assert np.abs(uni["records"]).max() > 0
+
+
 def test_checkpoint_replay_bitwise_equals_full_store():
     wl = inputs.as_f32(inputs.random_workload(4, 64, 8, nt=150, n_shots=2, n_src=1, n_rec=6, seed=501))
     full = run_gpu(wl, snap="f32", ckpt_every=0)

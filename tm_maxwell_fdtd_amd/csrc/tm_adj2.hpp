@@ -32,7 +32,7 @@
 
 namespace tmf {
 
-constexpr int CHA2_MAX = 128;   // largest chunk height of the two-step adjoint (LDS tables)
+constexpr int CHA2_MAX = 160;   // largest chunk height of the two-step adjoint (LDS tables)
 constexpr int PREFETCH_A2 = 1;  // rows of loads in flight ahead (one iteration covers both stages)
 constexpr int UNROLL_A2 = 2;    // row-loop unroll
 
@@ -75,14 +75,12 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
 
     const Geo& g = a.g;
     const StateLayout& L = a.L;
-    int s, strip, chunk;
-    tile_of(a.t, s, strip, chunk);
+    int s, strip, ya, yb;
+    tile2_of(a.t, g.ny, P, s, strip, ya, yb);
     const int tid = threadIdx.x;
     const int nx = g.nx, ny = g.ny;
     const int xs = P + strip * W;
     const int xe = min(xs + W, nx - P + 1);
-    const int ya = P + chunk * a.t.CH;
-    const int yb = min(ya + a.t.CH, ny - P + 1);
     const int Ya = ya - 2 * P + 1, Yb = yb + 2 * P - 1;   // stage A's output rows [Ya, Yb)
     const int yt = ya - 4 * P + 2;                  // first row of the tables (stage A's first input row)
     const int r_end = yb + 4 * P - 2;               // last iteration (stage B's last input row + 2P)

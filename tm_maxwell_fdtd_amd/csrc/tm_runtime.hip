@@ -26,6 +26,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -298,15 +299,16 @@ bool make_layout(tm_plan* p)
     return true;
 }
 
-// Tiling of the step kernels over one device.  Strips are Strip<P>::W
-// columns wide; every (strip, shot) pair of the R = ny - 2P + 1 computed rows
-// is cut into m chunks so that the grid is just below a whole number of
-// "rounds" of the device's resident workgroups (cap), chunks stay between
-// 16 and CH_MAX rows, and no round runs half empty.  TM_FDTD_CHUNK_ROWS
-// (environment, read when the tiling is made) forces the chunk height, for
-// tuning.
+// Tiling of the step kernels over one device.  Strips are W columns wide;
+// every (strip, shot) pair of the R = ny - 2P + 1 computed rows is cut into
+// m chunks so that the grid is just below a whole number of "rounds" of the
+// device's resident workgroups (cap) and chunks stay between 16 and chmax
+// rows.  Small problems (fewer than two workgroups per CU) take short chunks
+// instead (see below).  TM_FDTD_CHUNK_ROWS (environment, read when the
+// tiling is made) forces the chunk height, for tuning.  ``small`` reports
+// whether the small-problem rule chose the height.
 Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_MAX, int64_t ncu = 256,
-                   int halo_iters = 0)
+                   int halo_iters = 0, bool* small = nullptr, bool allow_small = true)
 {
     Tiling t{};
     const int R = (int)d.ny - 2 * P + 1, nx_e = (int)d.nx - 2 * P + 1;
@@ -326,7 +328,8 @@ Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_M
     // then each workgroup's time is its row count (owned rows plus the
     // halo_iters rows of its halo), so take the chunk height that minimises
     // (rows per workgroup) x (workgroups per pair of CUs, at least 1).
-    if (U * ((R + ch - 1) / ch) < 2 * ncu) {
+    const bool sm = allow_small && U * ((R + ch - 1) / ch) < 2 * ncu;
+    if (sm) {
         double best = 1e300;
         for (int c = std::min(ch, chmax); c >= 1; --c) {
             const int64_t nblk = U * ((R + c - 1) / c);
@@ -334,14 +337,136 @@ Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_M
             if (score < best) { best = score; ch = c; }
         }
     }
-    if (const char* env = std::getenv("TM_FDTD_CHUNK_ROWS")) {
-        const int v = std::atoi(env);
-        if (v >= 1) ch = std::min(v, chmax);
-    }
+    const char* env = std::getenv("TM_FDTD_CHUNK_ROWS");
+    if (env != nullptr && std::atoi(env) >= 1) ch = std::min(std::atoi(env), chmax);
+    if (small != nullptr) *small = sm || (env != nullptr && std::atoi(env) >= 1);
     t.CH = ch;
     t.nchunk = (R + ch - 1) / ch;
     t.nblk = (int)(U * t.nchunk);
+    // the same cut in the two-step representation: equal weights, every
+    // strip nchunk chunks of at most CH rows
+    t.nbl = t.nbr = 0;
+    t.nb_ch = t.ni_ch = t.nchunk;
+    t.per_shot = t.nstrip * t.nchunk;
+    t.wy0 = P;
+    t.wy1 = P + R;
+    t.wi = t.wb = 1;
     return t;
+}
+
+// Largest and smallest chunk height of a two-step cut into n chunks.
+void chunk_heights(const Tiling& t, int ny, int P, int n, int& hmin, int& hmax)
+{
+    hmin = INT32_MAX;
+    hmax = 0;
+    int y = chunk_row(t, ny, P, 0, n);
+    for (int k = 1; k <= n; ++k) {
+        const int z = chunk_row(t, ny, P, k, n);
+        hmin = std::min(hmin, z - y);
+        hmax = std::max(hmax, z - y);
+        y = z;
+    }
+}
+
+// Tiling of the two-step kernels.  Large problems run a launch as a few
+// rounds of resident workgroups, each of which streams its tile row by row
+// at a rate set by memory latency; a launch ends with its slowest
+// workgroups.  Rows on and near the y bands (CPML memories, predicated row
+// blocks) cost about 1 + beta interior rows, and a strip with x-band lanes
+// about mx times an interior strip.  Keeping the uniform tiling's rounds,
+// this cut gives the band strips more, shorter chunks from the workgroups
+// the uniform cut leaves unused, and cuts every strip at weighted row
+// quantiles, so that band rows are spread over more tiles.
+// TM_FDTD_BALANCE=0 keeps the uniform cut, =2 applies this one to small
+// problems too (for tests).
+Tiling make_tiling2(const tm_desc& d, const Geo& g, int P, int64_t cap, int W, int chmax, int64_t ncu,
+                    int halo_iters, double beta, double mx, const char* tiles_env)
+{
+    const char* env = std::getenv("TM_FDTD_BALANCE");
+    const int mode = env != nullptr ? std::atoi(env) : 1;
+    bool small = false;
+    Tiling t = make_tiling(d, P, cap, W, chmax, ncu, halo_iters, &small, mode != 2);
+    if (mode == 0 || small) return t;
+    const int ny = (int)d.ny, R = ny - 2 * P + 1, S = (int)d.n_shots;
+    const int64_t rounds = std::max<int64_t>(1, (t.nblk + cap - 1) / cap);
+    const int64_t budget = rounds * cap / S;                     // tiles per shot
+    if (budget < t.nstrip || budget > (int64_t)1 << 24) return t;
+    // strips with x-band lanes (as the kernels decide it), from the edges in
+    const int OFF = 4 * P - 2;
+    auto band = [&](int st) {
+        const int c0 = P + st * W - OFF;
+        return c0 < g.x0 || c0 + NT - 1 >= g.hx1;
+    };
+    Tiling b = t;
+    b.nbl = 0;
+    while (b.nbl < t.nstrip && band(b.nbl)) ++b.nbl;
+    b.nbr = 0;
+    while (b.nbr < t.nstrip - b.nbl && band(t.nstrip - 1 - b.nbr)) ++b.nbr;
+    const int nI = t.nstrip - b.nbl - b.nbr, nB = b.nbl + b.nbr;
+    b.wi = 16;
+    b.wb = 16 + (int)std::lround(16.0 * std::max(0.0, beta));
+    b.wy0 = std::min(std::max(g.y0, P), P + R);
+    b.wy1 = std::min(std::max(g.y1, b.wy0), P + R);
+    const double tot = ((double)(b.wy0 - P) * b.wb + (double)(b.wy1 - b.wy0) * b.wi +
+                        (double)(P + R - b.wy1) * b.wb) / b.wi;   // in interior rows
+    auto cost = [&](int n, double m) { return m * (tot / n + halo_iters); };
+    auto fits = [&](int n) {
+        if (n < 1 || n > R) return false;
+        int hmin = 0, hmax = 0;
+        chunk_heights(b, ny, P, n, hmin, hmax);
+        return hmin >= 1 && hmax <= chmax;
+    };
+    // Interior strips keep the uniform cut's chunk count (or the next one
+    // whose weighted chunks fit); band strips take the count that brings
+    // their tiles down to the interior tiles' cost, within the budget and
+    // never fewer than the interior strips.  (Searching both counts by the
+    // cost model alone chose fewer, longer interior chunks, which measured
+    // slower.)
+    int best_i = 0, best_b = 0;
+    int64_t best_tiles = 0;
+    int ni = nI > 0 ? std::max(1, t.nchunk) : 1;
+    while (nI > 0 && ni <= R && (int64_t)nI * ni < budget && !fits(ni)) ++ni;
+    if (nI == 0 || ((int64_t)nI * ni < budget && fits(ni))) {
+        const double ci = nI > 0 ? cost(ni, 1.0) : 0.0;
+        const int64_t left = budget - (int64_t)nI * ni;
+        const int nb_max = nB > 0 ? (int)std::min<int64_t>(R, left / nB) : 1;
+        int nb = 1;
+        if (nB > 0) {
+            const double room = ci / mx - halo_iters;
+            nb = room > 0.0 ? (int)std::ceil(tot / room - 1e-9) : nb_max;
+            nb = std::min(std::max(nb, nI > 0 ? ni : 1), nb_max);
+            while (nb <= nb_max && !fits(nb)) ++nb;
+        }
+        if (nb >= 1 && nb <= nb_max && (nI == 0 || nb >= ni)) {
+            best_i = ni;
+            best_b = nb;
+            best_tiles = (int64_t)nI * ni + (int64_t)nB * nb;
+        }
+    }
+    // tiles_env = "ni,nb[,wb]" forces the chunk counts (and the band row
+    // weight in 16ths), for tuning; ignored unless every chunk fits
+    if (const char* e = std::getenv(tiles_env)) {
+        int fi = 0, fb = 0, fw = b.wb;
+        if (std::sscanf(e, "%d,%d,%d", &fi, &fb, &fw) >= 2 && fw >= 1) {
+            Tiling f = b;
+            f.wb = fw;
+            int h0 = 0, h1 = 0, k0 = 0, k1 = 0;
+            chunk_heights(f, ny, P, std::max(fi, 1), h0, h1);
+            chunk_heights(f, ny, P, std::max(fb, 1), k0, k1);
+            if (fi >= 1 && fb >= 1 && h0 >= 1 && h1 <= chmax && k0 >= 1 && k1 <= chmax) {
+                b.wb = fw;
+                best_i = fi;
+                best_b = fb;
+                best_tiles = (int64_t)nI * fi + (int64_t)nB * fb;
+            }
+        }
+    }
+    if (best_tiles == 0) return t;
+    b.ni_ch = nI > 0 ? best_i : 1;
+    b.nb_ch = nB > 0 ? best_b : 1;
+    b.per_shot = (int)best_tiles;
+    b.nblk = (int)(best_tiles * S);
+    return b;
 }
 
 template <typename T>
@@ -810,6 +935,14 @@ bool compact_xfifo_fits(const Geo& g, int P, int W, int nstrip)
     return true;
 }
 
+// Relative cost of a y-band row (1 + beta interior rows: the rows near the
+// bands also leave the unrolled fast blocks) and of a strip with x-band
+// lanes (mx interior strips) in the two-step kernels.  From per-workgroup
+// timings and sweeps of the chunk counts and band weights on the order-8
+// 1096^2 workload (16 shots), checked on the 4184^2 and order-4 428^2 ones.
+constexpr double FWD2_BETA = 1.0, FWD2_MX = 1.14;
+constexpr double ADJ2_BETA = 1.125, ADJ2_MX = 1.22;
+
 // Make the tilings for the current device (once per device).
 template <int P>
 tm_status device_tiling(tm_plan* p)
@@ -848,8 +981,10 @@ tm_status device_tiling(tm_plan* p)
     // halo_iters: row iterations of a chunk beyond its owned rows
     p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W, CH_MAX, ncu, 2 * P - 1);
     p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W, CH_MAX, ncu, 4 * P - 3);
-    p->tiling_fwd2 = make_tiling(p->d, P, c2, Strip2<P>::W, CH2_MAX, ncu, 6 * P - 3);
-    p->tiling_adj2 = make_tiling(p->d, P, ca2, Strip2<P>::W, CHA2_MAX, ncu, 8 * P - 3);
+    p->tiling_fwd2 = make_tiling2(p->d, p->g, P, c2, Strip2<P>::W, CH2_MAX, ncu, 6 * P - 3, FWD2_BETA, FWD2_MX,
+                                   "TM_FDTD_FWD2_TILES");
+    p->tiling_adj2 = make_tiling2(p->d, p->g, P, ca2, Strip2<P>::W, CHA2_MAX, ncu, 8 * P - 3, ADJ2_BETA, ADJ2_MX,
+                                   "TM_FDTD_ADJ2_TILES");
     // resident kernels: the whole shot in one workgroup's LDS
     int lds_max = 0;
     HIPCHK(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));

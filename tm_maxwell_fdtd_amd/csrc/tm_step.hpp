@@ -64,26 +64,80 @@ struct Strip {
 };
 
 // Launch geometry of the step kernels.
+//
+// One-step kernels: every strip is cut into nchunk chunks of CH rows.
+// Two-step kernels: the nbl leftmost and nbr rightmost strips (those with
+// x-band lanes) are cut into nb_ch chunks each, the others into ni_ch, and
+// chunk k of n spans the rows between the k/n and (k+1)/n quantiles of a
+// row weight (wb outside the rows [wy0, wy1), wi inside), so that the
+// slower band rows and band strips get smaller tiles.  Any such cut covers
+// every row of every strip exactly once, so the results do not depend on it.
 struct Tiling {
-    int W, CH;            // owned columns per strip, owned rows per chunk
-    int nstrip, nchunk;   // strips per row, chunks per column
-    int nblk;             // nstrip * nchunk * S
+    int W, CH;            // owned columns per strip, owned rows per chunk (one-step)
+    int nstrip, nchunk;   // strips per row, chunks per column (one-step)
+    int nblk;             // workgroups of a launch
+    int per_shot;         // two-step: tiles per shot
+    int nbl, nbr;         // two-step: band strips at the left / right edge
+    int nb_ch, ni_ch;     // two-step: chunks per band strip / per other strip
+    int wy0, wy1, wi, wb; // two-step: row weights
 };
 
-// Workgroup id -> (shot, strip, chunk).  Workgroups are dealt round-robin to
-// the 8 XCDs; the remap gives each XCD a contiguous range of logical ids, so
-// vertically adjacent chunks (which share 2P-1 halo rows) run on the same
-// XCD and meet in its L2.
-__device__ __forceinline__ void tile_of(const Tiling& t, int& s, int& strip, int& chunk)
+// Workgroup id -> logical tile id.  Workgroups are dealt round-robin to the
+// 8 XCDs; the remap gives each XCD a contiguous range of logical ids, so
+// vertically adjacent chunks (which share halo rows) run on the same XCD
+// and meet in its L2.
+__device__ __forceinline__ int xcd_logical(int nblk)
 {
     const int L = blockIdx.x;
-    const int q = t.nblk >> 3, rem = t.nblk & 7;
+    const int q = nblk >> 3, rem = nblk & 7;
     const int xcd = L & 7, j = L >> 3;
-    const int logical = xcd * q + (xcd < rem ? xcd : rem) + j;
+    return xcd * q + (xcd < rem ? xcd : rem) + j;
+}
+
+// Workgroup id -> (shot, strip, chunk) of the one-step kernels.
+__device__ __forceinline__ void tile_of(const Tiling& t, int& s, int& strip, int& chunk)
+{
+    const int logical = xcd_logical(t.nblk);
     chunk = logical % t.nchunk;
     const int rest = logical / t.nchunk;
     strip = rest % t.nstrip;
     s = rest / t.nstrip;
+}
+
+// First row of chunk k of n (two-step tiling): the smallest row y of
+// [P, ny - P + 1] whose summed row weight over [P, y) reaches
+// ceil(k * total / n); k = 0 gives P and k = n gives ny - P + 1.
+__host__ __device__ inline int chunk_row(const Tiling& t, int ny, int P, int k, int n)
+{
+    const int y_end = ny - P + 1;
+    const int64_t A = (int64_t)(t.wy0 - P) * t.wb, M = (int64_t)(t.wy1 - t.wy0) * t.wi;
+    const int64_t B = (int64_t)(y_end - t.wy1) * t.wb;
+    const int64_t T = ((int64_t)k * (A + M + B) + n - 1) / n;
+    if (T <= A) return P + (int)((T + t.wb - 1) / t.wb);
+    if (T <= A + M) return t.wy0 + (int)((T - A + t.wi - 1) / t.wi);
+    return t.wy1 + (int)((T - A - M + t.wb - 1) / t.wb);
+}
+
+// Workgroup id -> (shot, strip, owned rows [ya, yb)) of the two-step kernels.
+__device__ __forceinline__ void tile2_of(const Tiling& t, int ny, int P, int& s, int& strip, int& ya, int& yb)
+{
+    const int logical = xcd_logical(t.nblk);
+    s = logical / t.per_shot;
+    int k = logical - s * t.per_shot;
+    const int nb = t.nbl * t.nb_ch, ni = (t.nstrip - t.nbl - t.nbr) * t.ni_ch;
+    int n = t.nb_ch, first = 0;
+    if (k >= nb + ni) {
+        k -= nb + ni;
+        first = t.nstrip - t.nbr;
+    } else if (k >= nb) {
+        k -= nb;
+        n = t.ni_ch;
+        first = t.nbl;
+    }
+    const int q = k / n;
+    strip = first + q;
+    ya = chunk_row(t, ny, P, k - q * n, n);
+    yb = chunk_row(t, ny, P, k - q * n + 1, n);
 }
 
 // CPML recursion on one point: memory m <- b m + a d; returns d / kappa + m.

@@ -85,7 +85,7 @@ struct Fwd2Args {
 // CPML coefficients are a = b = 0).  With an unroll of two this fits the
 // kernel into 128 VGPRs and 40 KB of LDS, four workgroups per CU.
 template <int P, int SNAP, bool UQ, bool CX>
-__global__ __launch_bounds__(NT, CX ? 4 : 3) void k_fwd_step2(Fwd2Args a)
+__global__ __launch_bounds__(NT, (CX || P <= 2) ? 4 : 3) void k_fwd_step2(Fwd2Args a)
 {
     constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH_F2;
@@ -107,14 +107,12 @@ __global__ __launch_bounds__(NT, CX ? 4 : 3) void k_fwd_step2(Fwd2Args a)
 
     const Geo& g = a.g;
     const StateLayout& L = a.L;
-    int s, strip, chunk;
-    tile_of(a.t, s, strip, chunk);
+    int s, strip, ya, yb;
+    tile2_of(a.t, g.ny, P, s, strip, ya, yb);
     const int tid = threadIdx.x;
     const int nx = g.nx, ny = g.ny;
     const int xs = P + strip * W;
     const int xe = min(xs + W, nx - P + 1);
-    const int ya = P + chunk * a.t.CH;
-    const int yb = min(ya + a.t.CH, ny - P + 1);
     const int yc0 = ya - 3 * P + 1;                 // first row of the CPML table
     const int ye0 = ya - 2 * P + 1;                 // first stage-A E row
     if (tid == 0) {
