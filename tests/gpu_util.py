@@ -17,12 +17,16 @@ def rel_l2(a, b):
 
 def seam_columns(wl, halo=None):
     """Columns within ``halo`` cells of a strip edge of the step kernels:
-    one-step strips are 256 - 4P + 2 columns wide, two-step strips
-    256 - 8P + 4, both starting at column P."""
+    one-step strips are 256 - 4P + 2 columns wide; the two-step kernels
+    cut the columns into as many strips of at most 256 - 8P + 4 as needed,
+    of equal widths; both start at column P."""
     p = wl.order // 2
     halo = 4 * p if halo is None else halo
+    nx_e = wl.nx - 2 * p + 1
+    w0 = 256 - 8 * p + 4
+    n2 = -(-nx_e // w0)
     cols = set()
-    for w in (256 - 4 * p + 2, 256 - 8 * p + 4):
+    for w in (256 - 4 * p + 2, -(-nx_e // n2)):
         for c0 in range(p, wl.nx, w):
             cols.update(range(max(0, c0 - halo), min(wl.nx, c0 + halo)))
     return np.array(sorted(cols), dtype=np.int64)

@@ -165,7 +165,7 @@ def test_deterministic_and_chunked():
 
 @pytest.mark.parametrize("order,n_int,nx_int,npml,shots", [
     (8, 40, 200, 240, 2),      # x bands wider than a strip: two band strips on the left
-    (4, 60, 700, 20, 3),       # band strips at both edges, two interior strips
+    (4, 60, 500, 130, 3),      # two band strips on the right, one on the left
     (2, 50, 1000, 12, 1),      # three interior strips
 ])
 def test_balanced_tiling_bitwise(monkeypatch, order, n_int, nx_int, npml, shots):

@@ -20,7 +20,8 @@
 // barriers of the iteration.  The gradients of row rB use lambda_E^{n+1}(rB)
 // still in stage A's register window and stage B's input lambda_E^n(rB).
 //
-// A strip of 256 lanes owns W = 256 - 8P + 4 columns: stage A's lambda_E is
+// A strip of 256 lanes owns up to W = 256 - 8P + 4 columns (the strips of
+// a grid are cut to equal widths, Tiling::W): stage A's lambda_E is
 // valid 2P-1 lanes in from the edges, stage B's another 2P-1; a chunk of CH
 // owned rows reads 4P-2 rows above and 4P-1 below.  Stage A's values
 // outside the fields' index sets are forced to 0, as the cells the single
@@ -61,7 +62,7 @@ struct Adj2Args {
 template <int P, int SNAP, bool UQ>
 __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
 {
-    constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
+    constexpr int OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH_A2;
     constexpr int R2 = 2 * P;                       // window / FIFO depth (a power of two)
     constexpr uint32_t ESZ = snap_bytes<SNAP>();
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(NT, P == 2 ? 4 : 3) void k_adj_step2(Adj2Args a)
     tile2_of(a.t, g.ny, P, s, strip, ya, yb);
     const int tid = threadIdx.x;
     const int nx = g.nx, ny = g.ny;
-    const int xs = P + strip * W;
-    const int xe = min(xs + W, nx - P + 1);
+    const int xs = P + strip * a.t.W;               // a.t.W <= Strip2<P>::W
+    const int xe = min(xs + a.t.W, nx - P + 1);
     const int Ya = ya - 2 * P + 1, Yb = yb + 2 * P - 1;   // stage A's output rows [Ya, Yb)
     const int yt = ya - 4 * P + 2;                  // first row of the tables (stage A's first input row)
     const int r_end = yb + 4 * P - 2;               // last iteration (stage B's last input row + 2P)

@@ -354,6 +354,16 @@ Tiling make_tiling(const tm_desc& d, int P, int64_t cap, int W, int chmax = CH_M
     return t;
 }
 
+// Owned columns per strip of the two-step kernels: as many strips as
+// columns of at most Strip2<P>::W need, cut to equal widths (so that no
+// strip is a narrow, cheap remainder while the others set the time).
+int strip2_width(int64_t nx, int P)
+{
+    const int nx_e = (int)nx - 2 * P + 1, w0 = NT - 8 * P + 4;
+    const int n = (nx_e + w0 - 1) / w0;
+    return (nx_e + n - 1) / n;
+}
+
 // Largest and smallest chunk height of a two-step cut into n chunks.
 void chunk_heights(const Tiling& t, int ny, int P, int n, int& hmin, int& hmax)
 {
@@ -386,6 +396,8 @@ Tiling make_tiling2(const tm_desc& d, const Geo& g, int P, int64_t cap, int W, i
     const int mode = env != nullptr ? std::atoi(env) : 1;
     bool small = false;
     Tiling t = make_tiling(d, P, cap, W, chmax, ncu, halo_iters, &small, mode != 2);
+    t.W = strip2_width(d.nx, P);
+    W = t.W;
     if (mode == 0 || small) return t;
     const int ny = (int)d.ny, R = ny - 2 * P + 1, S = (int)d.n_shots;
     const int64_t rounds = std::max<int64_t>(1, (t.nblk + cap - 1) / cap);
@@ -1376,8 +1388,10 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     }
     p->tiling_fwd = p->tiling_adj = make_tiling(d, P, 1024, NT - 4 * P + 2);
     p->tiling_fwd2 = make_tiling(d, P, 1024, NT - 8 * P + 4, CH2_MAX);
-    p->fwd_cx = P == 4 && compact_xfifo_fits(p->g, P, NT - 8 * P + 4, p->tiling_fwd2.nstrip);
+    p->tiling_fwd2.W = strip2_width(d.nx, P);
+    p->fwd_cx = P == 4 && compact_xfifo_fits(p->g, P, p->tiling_fwd2.W, p->tiling_fwd2.nstrip);
     p->tiling_adj2 = make_tiling(d, P, 1024, NT - 8 * P + 4, CHA2_MAX);
+    p->tiling_adj2.W = strip2_width(d.nx, P);
     if (!make_layout(p)) {
         delete p;
         return TM_EINVAL;

@@ -17,7 +17,8 @@
 // coefficients of stage B's rows are loaded again (they were read 2P-1 rows
 // earlier by the same workgroup and are served by the caches).
 //
-// A strip of 256 lanes owns W = 256 - 8P + 4 columns: stage A's values are
+// A strip of 256 lanes owns up to W = 256 - 8P + 4 columns (the strips of
+// a grid are cut to equal widths, Tiling::W): stage A's values are
 // valid 2P-1 lanes further in from the edges than the loaded E^n, stage B's
 // another 2P-1.  A chunk of CH owned rows reads 4P-2 rows above and below.
 // Values of stage A outside the field's index set are forced to 0 exactly
@@ -55,7 +56,7 @@ constexpr int XFIFO_W = 56;     // x-band lanes per strip the compact FIFOs hold
 
 template <int P>
 struct Strip2 {
-    static constexpr int W = NT - 8 * P + 4;   // owned columns per strip
+    static constexpr int W = NT - 8 * P + 4;   // most owned columns per strip
     static constexpr int OFF = 4 * P - 2;      // lane of the first owned column
 };
 
@@ -87,7 +88,7 @@ struct Fwd2Args {
 template <int P, int SNAP, bool UQ, bool CX>
 __global__ __launch_bounds__(NT, (CX || P <= 2) ? 4 : 3) void k_fwd_step2(Fwd2Args a)
 {
-    constexpr int W = Strip2<P>::W, OFF = Strip2<P>::OFF;
+    constexpr int OFF = Strip2<P>::OFF;
     constexpr int D = PREFETCH_F2;
     constexpr int U = CX ? UNROLL_F2_CX : UNROLL_F2;
     constexpr int XW = XFIFO_W;                     // x-band slots of the compact FIFOs
@@ -111,8 +112,8 @@ __global__ __launch_bounds__(NT, (CX || P <= 2) ? 4 : 3) void k_fwd_step2(Fwd2Ar
     tile2_of(a.t, g.ny, P, s, strip, ya, yb);
     const int tid = threadIdx.x;
     const int nx = g.nx, ny = g.ny;
-    const int xs = P + strip * W;
-    const int xe = min(xs + W, nx - P + 1);
+    const int xs = P + strip * a.t.W;               // a.t.W <= Strip2<P>::W
+    const int xe = min(xs + a.t.W, nx - P + 1);
     const int yc0 = ya - 3 * P + 1;                 // first row of the CPML table
     const int ye0 = ya - 2 * P + 1;                 // first stage-A E row
     if (tid == 0) {
