@@ -102,7 +102,7 @@ def kernel_bytes(name, wl, store, snap_bytes):
         name, store = name[:-len("_store")], True
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
-    if name in ("k_fwd_small", "k_adj_small"):
+    if name in ("k_fwd_small", "k_adj_small", "k_fwd_band", "k_adj_band"):
         # resident kernels: one launch runs a whole event block (the whole
         # run here) on chip; HBM sees the state in and out (fields and band
         # memories), the model once, and per step the snapshots (and in the
@@ -111,7 +111,7 @@ def kernel_bytes(name, wl, store, snap_bytes):
         full = wl.ny * wl.nx
         state = 2 * 4 * (3 * full + 2 * (band_y + band_x))
         snaps = wl.nt * 2 * snap_bytes * interior if store else 0
-        grads = 16 * interior if (store and name == "k_adj_small") else 0
+        grads = 16 * interior if (store and name.startswith("k_adj")) else 0
         return S * (state + 12 * full + snaps + grads)
     if name in ("k_fwd_step", "k_fwd_step_uq"):
         snaps = 2 * snap_bytes * interior if store else 0
@@ -248,7 +248,7 @@ def main():
     ap.add_argument("--nt", type=int, default=0,
                     help="override the number of time steps (profiling runs only; "
                          "the bench line then names the reduced workload)")
-    ap.add_argument("--time-block", type=int, default=0, choices=(0, 1, 2),
+    ap.add_argument("--time-block", type=int, default=0, choices=(0, 1, 2, 3, 4),
                     help="time steps per launch of the forward and the adjoint (0: the default, 2)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "

@@ -904,6 +904,117 @@ def test_resident_small_grid_modes(monkeypatch, case):
         np.testing.assert_array_equal(got[key], one[key], err_msg=f"{case} {key}")
 
 
+@pytest.mark.parametrize("order", inputs.ORDERS)
+@pytest.mark.parametrize("snap,ratio,kappa", [("f32", 1, 1.0), ("bf16", 1, 4.0), ("fp8", 1, 1.0), ("f32", 3, 4.0)])
+def test_banded_small_grid_bitwise(order, snap, ratio, kappa):
+    """The banded resident kernels (time_block 4: several workgroups per
+    shot, rows exchanged between neighbouring bands every step) give bitwise
+    the records, per-shot gradients and grad_f of the single-workgroup
+    resident kernels and of one step per launch.  Sources and receivers
+    anywhere (bands, edge rows, duplicates, negative indices), stretched
+    CPML, snapshot kinds and step ratios."""
+    wl = inputs.random_workload(order, 40, 7, nt=57, n_shots=3, n_src=3, n_rec=6, seed=1400 + order,
+                                src_anywhere=True, kappa_max=kappa)
+    wl.src[1, 1] = wl.src[1, 0]
+    wl.src[2, 2] = -1
+    wl.rec[0, 3] = wl.rec[0, 2]
+    wl.rec[2, 0] = -1
+    wl.rec[1, 4] = wl.src[1, 0]
+    wl = inputs.as_f32(wl)
+    ran = _kernel_counts(wl, snap=snap, step_ratio=ratio, time_block=4)
+    assert "k_adj_band" in ran and any(k.startswith("k_fwd_band") for k in ran), ran
+    assert not any(k.startswith(("k_fwd_step", "k_adj_step", "k_fwd_small", "k_adj_small")) for k in ran), ran
+    got = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=4)
+    res = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=3)
+    one = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], res[key], err_msg=f"resident {key}")
+        np.testing.assert_array_equal(got[key], one[key], err_msg=f"one step {key}")
+    assert np.abs(got["records"]).max() > 0
+
+
+@pytest.mark.parametrize("order,n_int,nx_int,shots", [(2, 150, 90, 1), (4, 120, 200, 2), (8, 60, 150, 4)])
+def test_banded_larger_grid(orc, order, n_int, nx_int, shots):
+    """Grids too large for one workgroup's LDS, in bands: against one step
+    per launch (bitwise) and the oracle (within the tolerances)."""
+    wl = inputs.as_f32(inputs.random_workload(order, n_int, 8, nt=45, n_shots=shots, n_src=2, n_rec=8,
+                                              seed=1420 + order, nx_int=nx_int))
+    assert wl.ny * wl.nx > 8192
+    ran = _kernel_counts(wl, time_block=4)
+    assert "k_adj_band" in ran, ran
+    got = run_gpu(wl, snap="f32", time_block=4)
+    one = run_gpu(wl, snap="f32", time_block=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=key)
+    # (no per-region bounds: in 45 steps the fields reach some of the band
+    # columns only as fp64 underflow-size values, which fp32 rounds to 0)
+    ref = orc.misfit_and_gradient(wl)
+    compare("records", got["records"], ref["records"], REC_TOL)
+    compare("gCa/shot", got["gca_shot"], ref["gca_shot"], GRAD_TOL["f32"])
+    compare("gCb/shot", got["gcb_shot"], ref["gcb_shot"], GRAD_TOL["f32"])
+    compare("grad_f", got["grad_f"], ref["grad_f"], GRAD_TOL["f32"])
+
+
+@pytest.mark.parametrize("case", ["chunks", "event-blocks", "per-shot-models", "no-grads", "ckpt-plan"])
+def test_banded_modes(monkeypatch, case):
+    """The banded kernels under the other call patterns, bitwise against
+    one step per launch: forward chunks, short event blocks (one launch per
+    block), one model per shot, an adjoint without gradients, and a
+    checkpointing plan (its storing forward and replays stream)."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.random_workload(4, 60, 7, nt=41, n_shots=2, n_src=2, n_rec=5, seed=1440,
+                                              src_anywhere=True, kappa_max=3.0))
+    kw, chunks = {}, None
+    if case == "chunks":
+        chunks = [7, 8, 30]
+    elif case == "event-blocks":
+        monkeypatch.setenv("TM_FDTD_EVENT_STEPS", "6")
+    elif case == "per-shot-models":
+        wl = inputs.as_f32(inputs.per_shot_models(wl))
+    elif case == "ckpt-plan":
+        kw = dict(ckpt_every=9)
+    if case == "no-grads":
+        outs = []
+        for tb in (4, 1):
+            prop = native.Propagator(wl, time_block=tb)
+            try:
+                r = prop.forward(store=False)
+                d = torch.randn(r.shape, generator=torch.Generator().manual_seed(5)).to(prop.device)
+                gf, _, _ = prop.adjoint(d, want_grads=False)
+                torch.cuda.synchronize()
+                outs.append((r.cpu().numpy(), gf.cpu().numpy()))
+            finally:
+                prop.close()
+        np.testing.assert_array_equal(outs[0][0], outs[1][0])
+        np.testing.assert_array_equal(outs[0][1], outs[1][1])
+        return
+    got = run_gpu(wl, snap="f32", chunks=chunks, time_block=4, **kw)
+    one = run_gpu(wl, snap="f32", chunks=chunks, time_block=1, **kw)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=f"{case} {key}")
+
+
+def test_banded_kernels_by_default_for_small_problems():
+    """time_block 0 runs the banded kernels on the small workloads (the
+    order-2 86^2 grid with one shot, the order-4 300^2 grid with four) and
+    the streaming kernels on a large one; bitwise equal to two steps per
+    launch."""
+    wl1 = inputs.as_f32(inputs.make_config(1, nt=30))
+    wl2 = inputs.as_f32(inputs.make_config(2, nt=20))
+    wl3 = inputs.as_f32(inputs.make_config(3, n_shots=1, nt=6))
+    assert "k_adj_band" in _kernel_counts(wl1)
+    assert "k_adj_band" in _kernel_counts(wl2)
+    assert "k_adj_band" not in _kernel_counts(wl3)
+    for wl in (wl1, wl2):
+        got = run_gpu(wl)
+        two = run_gpu(wl, time_block=2)
+        for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+            np.testing.assert_array_equal(got[key], two[key], err_msg=key)
+
+
 def test_resident_kernels_by_default_from_16_shots():
     """time_block 0 picks the resident kernels for a grid that fits with 16
     shots or more, the streaming kernels with fewer; bitwise equal."""

@@ -1,0 +1,541 @@
+// Banded resident kernels for small grids with few shots (gfx950, wave64).
+//
+// The single-workgroup resident kernels (tm_small.hpp) run a whole shot on
+// one CU; with one or a few shots that leaves most of the device idle, and
+// the streaming kernels instead pay a few microseconds of launch and
+// pipeline-fill time per launch, for a few microseconds of work.  Here each
+// shot is cut into bands of consecutive rows, one workgroup per band, and
+// every workgroup keeps its band (plus P halo rows above and below) in LDS
+// for a whole run of time steps.  After each phase whose output a
+// neighbour reads through a y-stencil, the workgroup publishes its first
+// and last P rows of that array to a global exchange buffer, raises its
+// counter, waits for the two neighbours' counters and copies their rows
+// into its halo: two exchanges per step (forward: Hx after the H half-step,
+// Ey after the E step; adjoint: the filtered w after the transposed E step,
+// the filtered Cq lambda_Hx after the transposed H step).  Arrays read only
+// through x-stencils need no halo.
+//
+// Every cell update is the operation sequence of the single-workgroup
+// resident kernels, so results are bitwise theirs (and those of the
+// streaming kernels up to the sign of a zero).
+//
+// The workgroups of a launch wait on each other, so the runtime launches
+// them cooperatively (all resident at once, or the launch fails); every
+// wait is bounded: a wait that runs past spin_max polls, or sees another
+// workgroup's failure, marks the launch failed (err) and every workgroup
+// leaves its time loop, so the grid always drains.  Exchange rows have a
+// buffer per kind and step parity: a workgroup rewrites a buffer two steps
+// later, after both neighbours have published that kind for the step in
+// between, which they do only after reading it.
+#pragma once
+
+#include "tm_small.hpp"
+
+namespace tmf {
+
+constexpr int CPTB = 4;                     // cells per thread of a band (bands are small)
+
+struct BandArgs {
+    SmallArgs a;               // the run (as for the single-workgroup kernels)
+    int rb;                    // owned rows per band (the last band: the rest, at least P)
+    int nband;                 // bands per shot; workgroup w = shot * nband + band
+    uint64_t* __restrict__ xbuf;  // exchange rows [workgroup][kind][parity][side: first, last][P][nx]:
+                                  // (step tag << 32) | value bits; cleared before each launch
+    int* __restrict__ err;        // set to 1 when a wait fails
+    int spin_max;              // polls before a wait fails
+};
+
+// LDS carve-up (float offsets): `ncell` cell arrays of rb + 2P rows (P halo
+// rows above and below the band) with pad = P*nx + P floats of zeros before
+// and after; the band memories of the own rows ([rb][nx] y-band memories,
+// [rb][bx] x-band memories, each with one spare slot); the CPML tables
+// [6][ny] and [6][nx]; the event-row slots [ny].
+struct BandLayout {
+    uint32_t pad, stride;              // padding, and floats per padded cell array
+    uint32_t myh, mye, mxh, mxe;       // band memories of the own rows
+    uint32_t ty, tx, slot;             // tables
+    uint32_t floats;                   // total
+};
+
+__host__ __device__ inline BandLayout band_layout(const Geo& g, int rb, int ncell)
+{
+    BandLayout s;
+    s.pad = (uint32_t)(g.P * g.nx + g.P);
+    s.stride = (uint32_t)((rb + 2 * g.P) * g.nx) + 2u * s.pad;
+    uint32_t o = (uint32_t)ncell * s.stride;
+    const uint32_t yn = (uint32_t)(rb * g.nx) + 1u, xn = (uint32_t)(rb * g.bx) + 1u;
+    s.myh = o; o += yn;
+    s.mye = o; o += yn;
+    s.mxh = o; o += xn;
+    s.mxe = o; o += xn;
+    s.ty = o; o += 6u * (uint32_t)g.ny;
+    s.tx = o; o += 6u * (uint32_t)g.nx;
+    s.slot = o; o += (uint32_t)g.ny;
+    s.floats = o;
+    return s;
+}
+
+__host__ __device__ inline uint32_t band_lds_bytes(const Geo& g, int rb, bool adjoint)
+{
+    return 4u * band_layout(g, rb, adjoint ? 4 : 3).floats;
+}
+
+// Whether a band height fits the packed cell word (14-bit local index, the
+// trailing pad included) and the thread count (CPTB cells per thread).
+__host__ __device__ inline bool band_rows_ok(const Geo& g, int rb)
+{
+    return rb >= g.P && (rb + 3 * g.P) * g.nx + g.P < (1 << 14) && rb * g.nx <= NTS * CPTB && g.ny < 2048;
+}
+
+// One own cell of a band, packed as in tm_small.hpp, with j the index in
+// the band's cell arrays (own row y -> array row y - ya + P) and y the
+// global row.  Unused slots pack the first word of the trailing padding
+// with every flag clear.
+template <int P>
+__device__ __forceinline__ int pack_band_cell(int jo, int nrow, int ya, int rb, const Geo& g)
+{
+    const int nx = g.nx;
+    const bool ok = jo < nrow * nx;
+    const int r = ok ? jo / nx : 0;
+    const int y = ya + r, x = ok ? jo - r * nx : P;
+    const bool ecol = x >= P && x <= nx - P, erow = y >= P && y <= g.ny - P;
+    const bool e = ok && ecol && erow;
+    const bool hx = ok && ecol && y >= P && y <= g.ny - P - 1;
+    const bool hz = ok && erow && x >= P && x <= nx - P - 1;
+    const bool fhy = hx && (y < g.y0 || y >= g.hy1), fhx = hz && (x < g.x0 || x >= g.hx1);
+    const bool fey = e && (y < g.y0 || y >= g.y1), fex = e && (x < g.x0 || x >= g.x1);
+    const int j = ok ? jo + P * nx : (rb + 2 * P) * nx;
+    return j | (y << 14) | ((int)e << CB_E) | ((int)hx << CB_HX) | ((int)hz << CB_HZ) | ((int)fhy << CB_FHY) |
+           ((int)fhx << CB_FHX) | ((int)fey << CB_FEY) | ((int)fex << CB_FEX);
+}
+
+// Per-workgroup context of a band: its rows, buffers and the exchange.
+struct Band {
+    int s, b, w;                       // shot, band, workgroup
+    int ya, yb, nrow;                  // own rows [ya, yb)
+};
+
+__device__ __forceinline__ Band band_of(const BandArgs& ba)
+{
+    Band t;
+    t.w = blockIdx.x;
+    t.s = t.w / ba.nband;
+    t.b = t.w - t.s * ba.nband;
+    t.ya = t.b * ba.rb;
+    t.yb = min(t.ya + ba.rb, ba.a.g.ny);
+    t.nrow = t.yb - t.ya;
+    return t;
+}
+
+// Stage the band memories of the own rows and the tables into LDS.
+__device__ __forceinline__ void band_stage(float* lds, const BandLayout& bl, const RBuf& b0, const StateLayout& L,
+                                           const Geo& g, const float* __restrict__ cp, const EventRows& ev,
+                                           const Band& t)
+{
+    const int nx = g.nx;
+    for (int i = threadIdx.x; i < t.nrow * nx; i += NTS) {
+        const int r = i / nx, x = i - r * nx, y = t.ya + r;
+        const bool on = y < g.y0 || y >= g.hy1;                      // a row of the y-band arrays
+        const uint32_t o = (uint32_t)((on ? band_y(g, y) : 0) * nx + x) * 4u;
+        lds[bl.myh + i] = b0.ld(on, o, L.oMyh);
+        lds[bl.mye + i] = b0.ld(on, o, L.oMye);
+    }
+    for (int i = threadIdx.x; i < t.nrow * g.bx; i += NTS) {
+        const uint32_t o = (uint32_t)(t.ya * g.bx + i) * 4u;
+        lds[bl.mxh + i] = b0.ld(true, o, L.oMxh);
+        lds[bl.mxe + i] = b0.ld(true, o, L.oMxe);
+    }
+    for (int i = threadIdx.x; i < 6 * g.ny; i += NTS) {
+        const int k = i / g.ny, y = i - k * g.ny;
+        const int row = (k < 3 ? AYH : AY) + (k < 3 ? k : k - 3);
+        const float v = cp[row * g.L + y];
+        lds[bl.ty + i] = (k == 2 || k == 5) ? 1.0f / v : v;
+    }
+    for (int i = threadIdx.x; i < 6 * nx; i += NTS) {
+        const int k = i / nx, x = i - k * nx;
+        const int row = (k < 3 ? AXH : AX) + (k < 3 ? k : k - 3);
+        const float v = cp[row * g.L + x];
+        lds[bl.tx + i] = (k == 2 || k == 5) ? 1.0f / v : v;
+    }
+    int* slot = reinterpret_cast<int*>(lds + bl.slot);
+    for (int y = threadIdx.x; y < g.ny; y += NTS) slot[y] = ev.row_slot[t.s * g.ny + y];
+}
+
+// Write the band memories of the own rows back into set b1.
+__device__ __forceinline__ void band_unstage(const float* lds, const BandLayout& bl, const RBuf& b1,
+                                             const StateLayout& L, const Geo& g, const Band& t)
+{
+    const int nx = g.nx;
+    for (int i = threadIdx.x; i < t.nrow * nx; i += NTS) {
+        const int r = i / nx, x = i - r * nx, y = t.ya + r;
+        const bool on = y < g.y0 || y >= g.hy1;
+        const uint32_t o = (uint32_t)((on ? band_y(g, y) : 0) * nx + x) * 4u;
+        b1.st(on, lds[bl.myh + i], o, L.oMyh);
+        b1.st(on, lds[bl.mye + i], o, L.oMye);
+    }
+    for (int i = threadIdx.x; i < t.nrow * g.bx; i += NTS) {
+        const uint32_t o = (uint32_t)(t.ya * g.bx + i) * 4u;
+        b1.st(true, lds[bl.mxh + i], o, L.oMxh);
+        b1.st(true, lds[bl.mxe + i], o, L.oMxe);
+    }
+}
+
+// Exchange n of kind `kind` (0 or 1) of array A: publish the own first and
+// last P rows, then copy the two neighbours' rows into the halo rows.  Each
+// published word carries its step tag n + 1 next to the value (one 64-bit
+// device-coherent store, which bypasses the non-coherent caches; the
+// buffers are cleared before every launch), and a reader polls each word
+// until it carries the tag, so the rows need no separate counter, fence or
+// barrier.  Returns false (in every thread) when the launch has failed.
+template <int P>
+__device__ __forceinline__ bool band_exchange(const BandArgs& ba, const Band& t, float* A, int kind, int n,
+                                              int* quit)
+{
+    const int nx = ba.a.g.nx, tid = threadIdx.x, pn = P * nx;
+    const uint64_t tag = (uint64_t)(uint32_t)(n + 1) << 32;
+    __syncthreads();                                          // the phase's writes to A are done
+    uint64_t* ob = ba.xbuf + (size_t)(((t.w * 2 + kind) * 2 + (n & 1)) * 2) * pn;
+    for (int i = tid; i < 2 * pn; i += NTS) {
+        const int side = i >= pn, k = i - side * pn;          // k = r * nx + x
+        const float v = A[(side ? t.nrow : P) * nx + k];      // own rows [0, P) or [nrow - P, nrow)
+        __hip_atomic_store(&ob[i], tag | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bool bad = false;
+    for (int i = tid; i < 2 * pn; i += NTS) {
+        const int side = i >= pn, k = i - side * pn;
+        const int nb = side ? t.b + 1 : t.b - 1;
+        if (nb < 0 || nb >= ba.nband) continue;               // beyond the grid: the halo stays 0
+        // above: the neighbour's last rows -> halo rows [0, P); below: its
+        // first rows -> halo rows [P + nrow, 2P + nrow)
+        const uint64_t* ib =
+            ba.xbuf + (size_t)(((((t.s * ba.nband + nb) * 2 + kind) * 2 + (n & 1)) * 2) + (side ? 0 : 1)) * pn;
+        uint64_t w = __hip_atomic_load(&ib[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int it = 1; (w & 0xffffffff00000000ull) != tag; ++it) {
+            if (it >= ba.spin_max ||
+                ((it & 63) == 0 && __hip_atomic_load(ba.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                bad = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            w = __hip_atomic_load(&ib[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (bad) break;
+        A[(side ? P + t.nrow : 0) * nx + k] = __uint_as_float((uint32_t)w);
+    }
+    if (bad) {
+        __hip_atomic_store(ba.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *quit = 1;                                            // any thread may set it; all read it below
+    }
+    __syncthreads();
+    return *quit == 0;
+}
+
+// ---------------------------------------------------------------------------
+// Forward: steps t0 .. t1-1, workgroup = (shot, band)
+// ---------------------------------------------------------------------------
+template <int P, int SNAP>
+__global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
+{
+    extern __shared__ float lds[];
+    __shared__ int quit;
+    const SmallArgs& a = ba.a;
+    const Geo& g = a.g;
+    const StateLayout& L = a.L;
+    const Band t = band_of(ba);
+    const int s = t.s, tid = threadIdx.x;
+    const int ny = g.ny, nx = g.nx;
+    const BandLayout bl = band_layout(g, ba.rb, 3);
+    float* const sE = lds + bl.pad;
+    float* const sHx = sE + bl.stride;
+    float* const sHz = sHx + bl.stride;
+    float* const myh = lds + bl.myh;
+    float* const mye = lds + bl.mye;
+    float* const mxh = lds + bl.mxh;
+    float* const mxe = lds + bl.mxe;
+    const float* const ty = lds + bl.ty;
+    const float* const tx = lds + bl.tx;
+    const int* const slot = reinterpret_cast<const int*>(lds + bl.slot);
+    const int y_arr = t.ya - P;                    // global row of array row 0
+
+    const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
+    const RBuf bev(a.ev.base, a.ev.bytes);
+
+    // fields of the array rows (own and halo; 0 off the grid) and padding
+    const int arr = (ba.rb + 2 * P) * nx;
+    for (int i = tid - (int)bl.pad; i < arr + (int)bl.pad; i += NTS) {
+        const int gj = y_arr * nx + i;
+        const bool in = i >= 0 && i < arr && gj >= 0 && gj < ny * nx;
+        const uint32_t o = (uint32_t)(in ? gj : 0) * 4u;
+        sE[i] = b0.ld(in, o, L.oE);
+        sHx[i] = b0.ld(in, o, L.oHx);
+        sHz[i] = b0.ld(in, o, L.oHz);
+    }
+    band_stage(lds, bl, b0, L, g, a.cp, a.ev, t);
+    if (tid == 0) quit = 0;
+
+    int pk[CPTB];
+    float ca[CPTB], cb[CPTB], cq[CPTB];
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const int jo = tid + i * NTS;
+        const bool ok = jo < t.nrow * nx;
+        pk[i] = pack_band_cell<P>(jo, t.nrow, t.ya, ba.rb, g);
+        const uint32_t o = (uint32_t)(ok ? t.ya * nx + jo : 0) * 4u;
+        ca[i] = bm.ld(ok, o, a.m.oCa);
+        cb[i] = bm.ld(ok, o, a.m.oCb);
+        cq[i] = bm.ld(ok, o, a.m.oCq);
+    }
+    __syncthreads();
+
+    auto xof = [&](const Cell& c) { return c.j() - (c.y() - y_arr) * nx; };
+    float add[CPTB];
+    auto load_add = [&](int tt, float (&dst)[CPTB]) {
+        const bool live = tt < a.t1;
+        const uint32_t off = a.ev_add0 + (uint32_t)(live ? tt - a.t0 : 0) * a.ev_row;
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            const Cell c = cell(pk[i]);
+            const int y = c.y(), gs = slot[y];
+            dst[i] = bev.ld(live && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + xof(c)) * 4u, off);
+        }
+    };
+    load_add(a.t0, add);
+
+    for (int tt = a.t0; tt < a.t1; ++tt) {
+        float add_n[CPTB];
+        load_add(tt + 1, add_n);
+
+        // ---- H half-step (reads Ey^n, own rows and halo)
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            const Cell c = cell(pk[i]);
+            const int j = c.j();
+            float dy = g.rdy * stencil<P>([&](int k) { return sE[j + k * nx]; },
+                                          [&](int k) { return sE[j - (k - 1) * nx]; });
+            float dx = g.rdx * stencil<P>([&](int k) { return sE[j + k]; }, [&](int k) { return sE[j - k + 1]; });
+            dy = site(c.bit(CB_FHY), myh, [&] { return (c.y() - t.ya) * nx + xof(c); }, ty + c.y(), ny, dy);
+            dx = site(c.bit(CB_FHX), mxh, [&] { return (c.y() - t.ya) * g.bx + band_x(g, xof(c)); },
+                      tx + xof(c), nx, dx);
+            const float hx = sHx[j], hz = sHz[j];
+            sHx[j] = c.bit(CB_HX) ? fmaf(-cq[i], dy, hx) : hx;
+            sHz[j] = c.bit(CB_HZ) ? fmaf(cq[i], dx, hz) : hz;
+        }
+        if (!band_exchange<P>(ba, t, sHx, 0, tt - a.t0, &quit)) break;
+
+        // ---- E step (reads H^{n+1/2}), snapshots, sources, receivers
+        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+                              : nullptr,
+                       stored ? a.snap_shot_bytes : 0u);
+        const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            const Cell c = cell(pk[i]);
+            const int j = c.j();
+            float uu = g.rdx * stencil<P>([&](int k) { return sHz[j + k - 1]; }, [&](int k) { return sHz[j - k]; });
+            float v = g.rdy * stencil<P>([&](int k) { return sHx[j + (k - 1) * nx]; },
+                                         [&](int k) { return sHx[j - k * nx]; });
+            uu = site(c.bit(CB_FEX), mxe, [&] { return (c.y() - t.ya) * g.bx + band_x(g, xof(c)); },
+                      tx + 3 * nx + xof(c), nx, uu);
+            v = site(c.bit(CB_FEY), mye, [&] { return (c.y() - t.ya) * nx + xof(c); }, ty + 3 * ny + c.y(), ny, v);
+            const float curl = uu - v;
+            const float ev = sE[j];
+            const int y = c.y(), x = xof(c);
+            if constexpr (SNAP != SNAP_NONE) {
+                const bool in_w = c.bit(CB_E) && y >= g.y0 && y < g.y1 && x >= g.x0 && x < g.x1;
+                snap_put2<SNAP>(bsp, stored && in_w, (uint32_t)((y - g.y0) * g.nxi + (x - g.x0)), ev, curl);
+            }
+            float en = fmaf(ca[i], ev, cb[i] * curl);
+            const int gs = slot[y];
+            const bool evr = c.bit(CB_E) && gs >= 0;
+            en = evr ? en + add[i] : en;
+            bev.st(evr, en, (uint32_t)(gs * nx + x) * 4u, out_off);
+            sE[j] = c.bit(CB_E) ? en : ev;
+        }
+        if (!band_exchange<P>(ba, t, sE, 1, tt - a.t0, &quit)) break;
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) add[i] = add_n[i];
+    }
+
+    // own rows back
+    for (int i = tid; i < t.nrow * nx; i += NTS) {
+        const uint32_t o = (uint32_t)(t.ya * nx + i) * 4u;
+        b1.st(true, sE[P * nx + i], o, L.oE);
+        b1.st(true, sHx[P * nx + i], o, L.oHx);
+        b1.st(true, sHz[P * nx + i], o, L.oHz);
+    }
+    band_unstage(lds, bl, b1, L, g, t);
+}
+
+// ---------------------------------------------------------------------------
+// Exact adjoint: steps t1-1 down to t0, workgroup = (shot, band)
+// ---------------------------------------------------------------------------
+template <int P, int SNAP>
+__global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
+{
+    extern __shared__ float lds[];
+    __shared__ int quit;
+    const SmallArgs& a = ba.a;
+    const Geo& g = a.g;
+    const StateLayout& L = a.L;
+    const Band t = band_of(ba);
+    const int s = t.s, tid = threadIdx.x;
+    const int ny = g.ny, nx = g.nx;
+    const BandLayout bl = band_layout(g, ba.rb, 4);
+    float* const sU = lds + bl.pad;     // filtered Cb lambda_E for the Hz transpose (0 off the E set)
+    float* const sW = sU + bl.stride;   // ... for the Hx transpose (exchanged)
+    float* const sTZ = sW + bl.stride;  // filtered Cq lambda_Hz (0 off the Hz set)
+    float* const sTX = sTZ + bl.stride; // filtered Cq lambda_Hx (0 off the Hx set; exchanged)
+    float* const myh = lds + bl.myh;
+    float* const mye = lds + bl.mye;
+    float* const mxh = lds + bl.mxh;
+    float* const mxe = lds + bl.mxe;
+    const float* const ty = lds + bl.ty;
+    const float* const tx = lds + bl.tx;
+    const int* const slot = reinterpret_cast<const int*>(lds + bl.slot);
+    const int y_arr = t.ya - P;
+
+    const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
+    const RBuf bev(a.ev.base, a.ev.bytes);
+    const uint32_t slab_b = (uint32_t)(g.slab * 4);
+    const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
+    const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
+
+    for (int i = tid; i < 4 * (int)bl.stride; i += NTS) lds[i] = 0.0f;
+    band_stage(lds, bl, b0, L, g, a.cp, a.ev, t);
+    if (tid == 0) quit = 0;
+
+    auto xof = [&](const Cell& c) { return c.j() - (c.y() - y_arr) * nx; };
+    auto in_window = [&](const Cell& c) {
+        const int y = c.y(), x = xof(c);
+        return c.bit(CB_E) && y >= g.y0 && y < g.y1 && x >= g.x0 && x < g.x1;
+    };
+    int pk[CPTB];
+    float ca[CPTB], cb[CPTB], cq[CPTB], lE[CPTB], lHx[CPTB], lHz[CPTB], ga[CPTB], gb[CPTB];
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const int jo = tid + i * NTS;
+        const bool ok = jo < t.nrow * nx;
+        pk[i] = pack_band_cell<P>(jo, t.nrow, t.ya, ba.rb, g);
+        const uint32_t o = (uint32_t)(ok ? t.ya * nx + jo : 0) * 4u;
+        ca[i] = bm.ld(ok, o, a.m.oCa);
+        cb[i] = bm.ld(ok, o, a.m.oCb);
+        cq[i] = bm.ld(ok, o, a.m.oCq);
+        lE[i] = b0.ld(ok, o, L.oE);
+        lHx[i] = b0.ld(ok, o, L.oHx);
+        lHz[i] = b0.ld(ok, o, L.oHz);
+        const bool gw = SNAP != SNAP_NONE && in_window(Cell{pk[i]});
+        ga[i] = bga.ld(gw, o, 0u);
+        gb[i] = bgb.ld(gw, o, 0u);
+    }
+
+    float add[CPTB], se[CPTB], sc[CPTB];
+    auto load_step = [&](int tt) {
+        const bool live = tt >= a.t0;
+        const uint32_t off = a.ev_add0 + (uint32_t)(live ? tt - a.t0 : 0) * a.ev_row;
+        const bool stored = SNAP != SNAP_NONE && live && tt % a.R == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+                              : nullptr,
+                       stored ? a.snap_shot_bytes : 0u);
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            const Cell c = cell(pk[i]);
+            const int y = c.y(), x = xof(c), gs = slot[y];
+            add[i] = bev.ld(live && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + x) * 4u, off);
+            const SnapPair sp = snap_get2<SNAP>(bsp, stored && in_window(c),
+                                                (uint32_t)((y - g.y0) * g.nxi + (x - g.x0)));
+            se[i] = sp.e;
+            sc[i] = sp.c;
+        }
+    };
+    __syncthreads();
+    load_step(a.t1 - 1);
+
+    for (int tt = a.t1 - 1; tt >= a.t0; --tt) {
+        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
+        const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
+        const int n = a.t1 - 1 - tt;
+
+        // ---- phase 1, transpose of the E step: residual, gradient, Cb, E-update filters
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            const Cell c = cell(pk[i]);
+            const int j = c.j(), y = c.y(), x = xof(c);
+            const bool on = c.bit(CB_E);
+            const int gs = slot[y];
+            const bool evr = on && gs >= 0;
+            const float e = evr ? lE[i] + add[i] : lE[i];
+            bev.st(evr, e, (uint32_t)(gs * nx + x) * 4u, out_off);
+            if (SNAP != SNAP_NONE && stored) {
+                const bool in_w = in_window(c);
+                const float na = fmaf(e, se[i] * a.ratio, ga[i]), nb = fmaf(e, sc[i] * a.ratio, gb[i]);
+                ga[i] = in_w ? na : ga[i];
+                gb[i] = in_w ? nb : gb[i];
+            }
+            const float hv = cb[i] * e;
+            const float u = site(c.bit(CB_FEX), mxe, [&] { return (y - t.ya) * g.bx + band_x(g, x); },
+                                 tx + 3 * nx + x, nx, hv);
+            const float w = site(c.bit(CB_FEY), mye, [&] { return (y - t.ya) * nx + x; }, ty + 3 * ny + y, ny, hv);
+            sU[j] = on ? u : 0.0f;
+            sW[j] = on ? w : 0.0f;
+            lE[i] = e;
+        }
+        load_step(tt - 1);
+        if (!band_exchange<P>(ba, t, sW, 0, n, &quit)) break;
+
+        // ---- phase 2, transposed curl, then Cq and the H-update filters
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            const Cell c = cell(pk[i]);
+            const int j = c.j();
+            const float accx = stencil<P>([&](int k) { return sW[j + k * nx]; },
+                                          [&](int k) { return sW[j - (k - 1) * nx]; });
+            const float accz = stencil<P>([&](int k) { return sU[j + k]; }, [&](int k) { return sU[j - k + 1]; });
+            const float lhx = fmaf(g.rdy, accx, lHx[i]);
+            const float lhz = fmaf(-g.rdx, accz, lHz[i]);
+            const int y = c.y(), x = xof(c);
+            const float txv = site(c.bit(CB_FHY), myh, [&] { return (y - t.ya) * nx + x; }, ty + y, ny, cq[i] * lhx);
+            const float tz = site(c.bit(CB_FHX), mxh, [&] { return (y - t.ya) * g.bx + band_x(g, x); }, tx + x, nx,
+                                  cq[i] * lhz);
+            const bool hx = c.bit(CB_HX), hz = c.bit(CB_HZ);
+            lHx[i] = hx ? lhx : lHx[i];
+            lHz[i] = hz ? lhz : lHz[i];
+            sTX[j] = hx ? txv : 0.0f;
+            sTZ[j] = hz ? tz : 0.0f;
+        }
+        if (!band_exchange<P>(ba, t, sTX, 1, n, &quit)) break;
+
+        // ---- phase 3, lambda_E = Ca e - Dx[t_z] + Dz[t_x]
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            const Cell c = cell(pk[i]);
+            const int j = c.j();
+            const float az = stencil<P>([&](int k) { return sTZ[j + k - 1]; }, [&](int k) { return sTZ[j - k]; });
+            const float ay = stencil<P>([&](int k) { return sTX[j + (k - 1) * nx]; },
+                                        [&](int k) { return sTX[j - k * nx]; });
+            const float en = fmaf(ca[i], lE[i], fmaf(-az, g.rdx, ay * g.rdy));
+            lE[i] = c.bit(CB_E) ? en : lE[i];
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const int jo = tid + i * NTS;
+        const bool ok = jo < t.nrow * nx;
+        const uint32_t o = (uint32_t)(ok ? t.ya * nx + jo : 0) * 4u;
+        b1.st(ok, lE[i], o, L.oE);
+        b1.st(ok, lHx[i], o, L.oHx);
+        b1.st(ok, lHz[i], o, L.oHz);
+        const bool gw = SNAP != SNAP_NONE && in_window(Cell{pk[i]});
+        bga.st(gw, ga[i], o, 0u);
+        bgb.st(gw, gb[i], o, 0u);
+    }
+    __syncthreads();
+    band_unstage(lds, bl, b1, L, g, t);
+}
+
+}  // namespace tmf

@@ -40,6 +40,7 @@
 #include "tm_step2.hpp"
 #include "tm_adj2.hpp"
 #include "tm_small.hpp"
+#include "tm_band.hpp"
 
 using namespace tmf;
 
@@ -133,6 +134,7 @@ struct Layout {
     uint64_t ckpt = 0, ckpt_slot = 0;
     uint64_t ev_row = 0;                          // bytes of one step's event rows [NS][nx]
     uint64_t ev_fadd = 0, ev_fout = 0, ev_aadd = 0, ev_aout = 0;   // [EB][NS][nx] each
+    uint64_t band_x = 0, band_x_bytes = 0, band_err = 0;   // banded kernels: exchange rows, failure word
     uint64_t total = 0;
 };
 
@@ -148,12 +150,13 @@ constexpr int HOST_RING = 3;
 enum KernelId {
     KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_ADJ_STEP2_UQ,
     KID_FWD_STEP_ST, KID_FWD_STEP2_ST, KID_FWD_STEP2_UQ_ST, KID_FWD_SMALL, KID_FWD_SMALL_ST, KID_ADJ_SMALL,
-    KID_COUNT
+    KID_FWD_BAND, KID_FWD_BAND_ST, KID_ADJ_BAND, KID_COUNT
 };
 const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2",
                                              "k_fwd_step2_uq", "k_adj_step2_uq", "k_fwd_step_store",
                                              "k_fwd_step2_store", "k_fwd_step2_uq_store", "k_fwd_small",
-                                             "k_fwd_small_store", "k_adj_small"};
+                                             "k_fwd_small_store", "k_adj_small", "k_fwd_band",
+                                             "k_fwd_band_store", "k_adj_band"};
 
 struct TimedLaunch {
     int kid;
@@ -170,6 +173,11 @@ struct tm_plan {
     int resident = 0;                    // resident kernels: 0 never, 1 where they fit and the shots are
                                          // many (time_block 0), 2 wherever they fit (time_block 3)
     bool small = false;                  // the resident kernels run (per device, with the tilings)
+    int band = 0;                        // banded resident kernels: 0 never, 1 for small problems with
+                                         // few shots (time_block 0), 2 wherever they fit (time_block 4)
+    int band_rb = 0, band_n = 0;         // their band height and bands per shot (0: the grid does not fit)
+    bool banded = false;                 // the banded kernels run (per device)
+    bool band_ran = false;               // a banded launch ran in the current call (its failure word is read)
     int tiling_device = -1;
     std::vector<float> cpml;             // [12][L]
     std::vector<int32_t> tables;         // event-row tables, packed
@@ -242,6 +250,31 @@ bool finite_all(const float* p, int64_t n)
     return true;
 }
 
+// Band height and bands per shot of the banded resident kernels (0: they
+// do not apply): as many bands as one workgroup per CU of the device allows
+// (256 CUs; the device check repeats it with the real count), each of at
+// least max(2P, 4) rows, the last of at least P, within the packed cell
+// word and the LDS of a CU.
+void band_plan(tm_plan* p)
+{
+    p->band_rb = p->band_n = 0;
+    if (p->band == 0) return;
+    const Geo& g = p->g;
+    const int64_t S = p->d.n_shots;
+    constexpr int64_t WG_MAX = 256;
+    if (S > WG_MAX || g.ny >= 2048) return;
+    const int rb_min = std::max(2 * g.P, 4);
+    for (int64_t nb = std::min<int64_t>(WG_MAX / S, g.ny / rb_min); nb >= 2; --nb) {
+        const int rb = (int)((g.ny + nb - 1) / nb);
+        const int n = (g.ny + rb - 1) / rb;
+        if (g.ny - (n - 1) * rb < g.P || !band_rows_ok(g, rb)) continue;
+        if (band_lds_bytes(g, rb, true) > 160u * 1024u) continue;
+        p->band_rb = rb;
+        p->band_n = n;
+        return;
+    }
+}
+
 // Returns false when a per-shot block or the model block exceeds one
 // buffer view.
 bool make_layout(tm_plan* p)
@@ -295,6 +328,12 @@ bool make_layout(tm_plan* p)
     L.ev_fout = take(evb);
     L.ev_aadd = take(evb);
     L.ev_aout = take(evb);
+    if (p->band_n > 0) {
+        const uint64_t nw = (uint64_t)d.n_shots * (uint64_t)p->band_n;
+        L.band_x_bytes = nw * 8 * (uint64_t)g.P * (uint64_t)g.nx * 8;   // [kind][parity][side][P][nx] words
+        L.band_x = take(L.band_x_bytes);
+        L.band_err = take(4);
+    }
     L.total = o;
     return true;
 }
@@ -390,12 +429,13 @@ void chunk_heights(const Tiling& t, int ny, int P, int n, int& hmin, int& hmax)
 // TM_FDTD_BALANCE=0 keeps the uniform cut, =2 applies this one to small
 // problems too (for tests).
 Tiling make_tiling2(const tm_desc& d, const Geo& g, int P, int64_t cap, int W, int chmax, int64_t ncu,
-                    int halo_iters, double beta, double mx, const char* tiles_env)
+                    int halo_iters, double beta, double mx, const char* tiles_env, bool* small_out = nullptr)
 {
     const char* env = std::getenv("TM_FDTD_BALANCE");
     const int mode = env != nullptr ? std::atoi(env) : 1;
     bool small = false;
     Tiling t = make_tiling(d, P, cap, W, chmax, ncu, halo_iters, &small, mode != 2);
+    if (small_out != nullptr) *small_out = small;
     t.W = strip2_width(d.nx, P);
     W = t.W;
     if (mode == 0 || small) return t;
@@ -577,6 +617,8 @@ struct Ptrs {
     float *ev_fadd, *ev_fout, *ev_aadd, *ev_aout;
     char *snap, *ckpt;
     float* scratch;
+    uint64_t* band_x;                    // banded kernels: exchange rows
+    int* band_err;                       // ... failure word
 };
 
 Ptrs pointers(const tm_plan* p, void* ws)
@@ -596,6 +638,8 @@ Ptrs pointers(const tm_plan* p, void* ws)
     q.snap = wsp<char>(ws, L.snap);
     q.ckpt = wsp<char>(ws, L.ckpt);
     q.scratch = wsp<float>(ws, L.scratch);
+    q.band_x = wsp<uint64_t>(ws, L.band_x);
+    q.band_err = wsp<int>(ws, L.band_err);
     return q;
 }
 
@@ -901,6 +945,126 @@ void adj_small(tm_plan* p, const Ptrs& q, int64_t ta, int64_t tb, int64_t k, int
     });
 }
 
+// Polls of one exchange wait before a banded launch counts as failed
+// (about 0.2 s; a normal wait is a few microseconds).
+constexpr int BAND_SPIN_MAX = 200000;
+
+// The banded kernels' arguments for the run [ta, tb) on sets s0 -> s1.
+BandArgs band_args(const tm_plan* p, const Ptrs& q, const SmallArgs& a)
+{
+    BandArgs b{};
+    b.a = a;
+    b.rb = p->band_rb;
+    b.nband = p->band_n;
+    b.xbuf = q.band_x;
+    b.err = q.band_err;
+    b.spin_max = BAND_SPIN_MAX;
+    return b;
+}
+
+// Launch a banded kernel cooperatively (all its workgroups resident at
+// once), its exchange rows cleared first (their step tags restart at every
+// launch); the failure word is cleared by the first banded launch of a call
+// and read at the call's end.
+tm_status band_launch(tm_plan* p, const Ptrs& q, const void* fn, BandArgs& b, bool adjoint, int kid, int64_t t,
+                      hipStream_t st)
+{
+    const int nw = (int)(p->d.n_shots * p->band_n);
+    tm_status v = zero(reinterpret_cast<float*>(q.band_x), p->lay.band_x_bytes, st);
+    if (v == TM_OK && !p->band_ran) v = zero(reinterpret_cast<float*>(q.band_err), 4, st);
+    if (v != TM_OK) return v;
+    p->band_ran = true;
+    void* args[] = {&b};
+    const uint32_t lds = band_lds_bytes(p->g, p->band_rb, adjoint);
+    hipError_t e = hipSuccess;
+    timed(p, kid, t, st, [&] {
+        e = hipLaunchCooperativeKernel(fn, dim3((unsigned)nw), dim3(NTS), args, lds, st);
+    });
+    return e == hipSuccess ? TM_OK : TM_EHIP;
+}
+
+// Whether the banded launches of this call completed every exchange (read
+// back, so it waits for the stream; skipped while the stream is captured).
+tm_status band_check(tm_plan* p, const Ptrs& q, hipStream_t st)
+{
+    if (!p->band_ran) return TM_OK;
+    p->band_ran = false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIPCHK(hipStreamIsCapturing(st, &cs));
+    if (cs != hipStreamCaptureStatusNone) return TM_OK;
+    int failed = 0;
+    HIPCHK(hipMemcpyAsync(&failed, q.band_err, sizeof(int), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    return failed ? TM_EHIP : TM_OK;
+}
+
+// Forward steps [ta, tb) of one event block with the banded kernels.
+template <int P>
+tm_status fwd_band(tm_plan* p, const Ptrs& q, int cur, int64_t ta, int64_t tb, int snap, hipStream_t st)
+{
+    const Layout& L = p->lay;
+    SmallArgs a{};
+    a.g = p->g;
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.fset[cur];
+    a.set1 = q.base + L.fset[1 - cur];
+    a.snap = snap != SNAP_NONE ? q.snap : nullptr;
+    a.snap_stride = L.snap_stride;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
+    a.R = (int)p->R;
+    a.ratio = (float)p->R;
+    a.t0 = (int)ta;
+    a.t1 = (int)tb;
+    a.ev = event_rows(p, q, false);
+    const EventStep e0 = event_step(p, false, ta);
+    a.ev_add0 = e0.add;
+    a.ev_out0 = e0.out;
+    a.ev_row = (uint32_t)L.ev_row;
+    BandArgs b = band_args(p, q, a);
+    const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>)
+                   : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_BF16>)
+                   : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_FP8>)
+                                         : reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_NONE>);
+    return band_launch(p, q, fn, b, false, snap == SNAP_NONE ? KID_FWD_BAND : KID_FWD_BAND_ST, ta, st);
+}
+
+// Adjoint steps tb-1 .. ta of one event block with the banded kernels.
+template <int P>
+tm_status adj_band(tm_plan* p, const Ptrs& q, int64_t ta, int64_t tb, int64_t k, int snap, float* gca, float* gcb,
+                   hipStream_t st)
+{
+    const Layout& L = p->lay;
+    SmallArgs a{};
+    a.g = p->g;
+    a.L = L.st;
+    a.m = q.model;
+    a.cp = q.cp;
+    a.set0 = q.base + L.aset[k & 1];
+    a.set1 = q.base + L.aset[(k + 1) & 1];
+    a.snap = snap != SNAP_NONE ? q.snap : nullptr;
+    a.snap_stride = L.snap_stride;
+    a.snap_shot_bytes = (uint32_t)L.snap_shot;
+    a.R = (int)p->R;
+    a.ratio = (float)p->R;
+    a.t0 = (int)ta;
+    a.t1 = (int)tb;
+    a.ev = event_rows(p, q, true);
+    const EventStep e0 = event_step(p, true, ta);
+    a.ev_add0 = e0.add;
+    a.ev_out0 = e0.out;
+    a.ev_row = (uint32_t)L.ev_row;
+    a.gca = gca;
+    a.gcb = gcb;
+    BandArgs b = band_args(p, q, a);
+    const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>)
+                   : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_BF16>)
+                   : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_FP8>)
+                                         : reinterpret_cast<const void*>(&k_adj_band<P, SNAP_NONE>);
+    return band_launch(p, q, fn, b, true, KID_ADJ_BAND, ta, st);
+}
+
 int snap_kind(const tm_plan* p)
 {
     return p->d.snap == TM_SNAP_BF16 ? SNAP_BF16 : p->d.snap == TM_SNAP_FP8 ? SNAP_FP8 : SNAP_F32;
@@ -993,8 +1157,9 @@ tm_status device_tiling(tm_plan* p)
     // halo_iters: row iterations of a chunk beyond its owned rows
     p->tiling_fwd = make_tiling(p->d, P, cf, Strip<P>::W, CH_MAX, ncu, 2 * P - 1);
     p->tiling_adj = make_tiling(p->d, P, ca, Strip<P>::W, CH_MAX, ncu, 4 * P - 3);
+    bool stream_small = false;
     p->tiling_fwd2 = make_tiling2(p->d, p->g, P, c2, Strip2<P>::W, CH2_MAX, ncu, 6 * P - 3, FWD2_BETA, FWD2_MX,
-                                   "TM_FDTD_FWD2_TILES");
+                                   "TM_FDTD_FWD2_TILES", &stream_small);
     p->tiling_adj2 = make_tiling2(p->d, p->g, P, ca2, Strip2<P>::W, CHA2_MAX, ncu, 8 * P - 3, ADJ2_BETA, ADJ2_MX,
                                    "TM_FDTD_ADJ2_TILES");
     // resident kernels: the whole shot in one workgroup's LDS
@@ -1008,6 +1173,21 @@ tm_status device_tiling(tm_plan* p)
                       small_lds_bytes(p->g, false) <= (uint32_t)lds_max &&
                       small_lds_bytes(p->g, true) <= (uint32_t)lds_max;
     p->small = fits && (p->resident == 2 || (p->resident == 1 && p->d.n_shots >= SMALL_MIN_SHOTS));
+    // banded resident kernels: where the streaming kernels would run a small
+    // problem (few workgroups per CU) and every band's workgroup can be
+    // resident at once
+    p->banded = false;
+    if (p->band_n > 0 && !p->small && (p->band == 2 || (p->band == 1 && stream_small))) {
+        const uint32_t lf = band_lds_bytes(p->g, p->band_rb, false), la = band_lds_bytes(p->g, p->band_rb, true);
+        if (lf <= (uint32_t)lds_max && la <= (uint32_t)lds_max) {
+            int of = 0, oa = 0;
+            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &of, reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>), NTS, lf));
+            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &oa, reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>), NTS, la));
+            p->banded = p->d.n_shots * p->band_n <= (int64_t)std::min(of, oa) * ncu;
+        }
+    }
     p->tiling_device = dev;
     return TM_OK;
 }
@@ -1059,6 +1239,7 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
     // the device store of full-store mode (not a replay's segment buffer),
     // or none; no checkpoints, no host store
     const bool small = p->small && !ckpt && !host && (p->K == 0 || snap == SNAP_NONE);
+    const bool band = !small && p->banded && !ckpt && !host && (p->K == 0 || snap == SNAP_NONE);
     int64_t ev_a = t0, ev_b = t0;        // event block of the current steps: [ev_a, ev_b)
     tm_status v = TM_OK;
     for (int64_t t = t0; t < t1;) {
@@ -1070,6 +1251,12 @@ tm_status forward_range(tm_plan* p, const Ptrs& q, int* cur, const float* f, flo
         }
         if (small) {
             fwd_small<P>(p, q, *cur, t, ev_b, snap, st);
+            *cur = 1 - *cur;
+            t = ev_b;
+            continue;
+        }
+        if (band) {
+            if ((v = fwd_band<P>(p, q, *cur, t, ev_b, snap, st)) != TM_OK) return v;
             *cur = 1 - *cur;
             t = ev_b;
             continue;
@@ -1165,6 +1352,11 @@ tm_status run_adjoint(tm_plan* p, void* ws, const float* f, const float* grad_r,
             if ((v = events(t)) != TM_OK) return v;
             if (p->small && !host) {                                           // the event block in one launch
                 adj_small<P>(p, q, ev_a, t + 1, k, snap, gca, gcb, st);
+                t = ev_a - 1;
+                continue;
+            }
+            if (p->banded && !host) {                                          // ... with the banded kernels
+                if ((v = adj_band<P>(p, q, ev_a, t + 1, k, snap, gca, gcb, st)) != TM_OK) return v;
                 t = ev_a - 1;
                 continue;
             }
@@ -1322,7 +1514,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16 && d.snap != TM_SNAP_FP8) return TM_EINVAL;
-    if (d.time_block < 0 || d.time_block > 3) return TM_EINVAL;
+    if (d.time_block < 0 || d.time_block > 4) return TM_EINVAL;
     if (d.storage != TM_STORE_DEVICE && d.storage != TM_STORE_HOST) return TM_EINVAL;
     if (d.step_ratio < 0) return TM_EINVAL;
     if (d.model_per_shot != 0 && d.model_per_shot != 1) return TM_EINVAL;
@@ -1369,8 +1561,10 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     p->cpml.assign(cpml, cpml + 12 * L);
 
     if ((v = set_events(p, src, rec)) != TM_OK) { delete p; return v; }
-    p->time_block = (d.time_block == 0 || d.time_block == 3) ? 2 : (int)d.time_block;
+    p->time_block = (d.time_block == 0 || d.time_block >= 3) ? 2 : (int)d.time_block;
     p->resident = d.time_block == 0 ? 1 : d.time_block == 3 ? 2 : 0;
+    p->band = d.time_block == 0 ? 1 : d.time_block == 4 ? 2 : 0;
+    band_plan(p);
     p->R = d.step_ratio > 1 ? d.step_ratio : 1;
     p->n_store = (d.nt + p->R - 1) / p->R;
     p->storage = (int)d.storage;
@@ -1621,6 +1815,8 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     default: v = run_forward<4>(p, ws, f, r, t0, t1, store, st); break;
     }
     p->cq_uniform = false;            // the adjoint's replays read the array
+    if (v == TM_OK) v = band_check(p, pointers(p, ws), st);
+    p->band_ran = false;
     if (v != TM_OK) return v;
     p->fwd_next = t1;
     p->fwd_complete = (t1 == p->d.nt) && p->stored_ok;
@@ -1658,6 +1854,8 @@ TM_API tm_status tm_adjoint(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     default: v = run_adjoint<4>(p, ws, f, grad_r, grad_f, grad_ca_shot, grad_cb_shot, st); break;
     }
     p->cq_uniform = false;
+    if (v == TM_OK) v = band_check(p, pointers(p, ws), st);
+    p->band_ran = false;
     if (v != TM_OK) return v;
     if (p->K > 0 && want_grad) p->fwd_next = -1;   // the replay overwrote the forward state
     return TM_OK;
