@@ -79,7 +79,7 @@ def _counts(wl):
     return cells, interior, band_y, band_x
 
 
-def kernel_bytes(name, wl, store, snap_bytes):
+def kernel_bytes(name, wl, store, snap_bytes, run_steps=None):
     """Algorithmic HBM bytes of one launch of kernel ``name`` (all shots).
 
     k_fwd_step: read E, Hx, Hz, Ca, Cb, Cq and write E, Hx, Hz (36 B per
@@ -103,14 +103,16 @@ def kernel_bytes(name, wl, store, snap_bytes):
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
     if name in ("k_fwd_small", "k_adj_small", "k_fwd_band", "k_adj_band"):
-        # resident kernels: one launch runs a whole event block (the whole
-        # run here) on chip; HBM sees the state in and out (fields and band
-        # memories), the model once, and per step the snapshots (and in the
-        # adjoint the gradients once, read and written)
+        # resident kernels: one launch runs a whole event block (run_steps
+        # steps, the whole run if not given) on chip; HBM sees the state in
+        # and out (fields and band memories), the model once, and per step
+        # the snapshots (and in the adjoint the gradients once, read and
+        # written)
         p = wl.order // 2
         full = wl.ny * wl.nx
         state = 2 * 4 * (3 * full + 2 * (band_y + band_x))
-        snaps = wl.nt * 2 * snap_bytes * interior if store else 0
+        steps = wl.nt if run_steps is None else run_steps
+        snaps = steps * 2 * snap_bytes * interior if store else 0
         grads = 16 * interior if (store and name.startswith("k_adj")) else 0
         return S * (state + 12 * full + snaps + grads)
     if name in ("k_fwd_step", "k_fwd_step_uq"):
@@ -240,8 +242,10 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
-    ap.add_argument("--timing-every", type=int, default=8,
-                    help="sample every k-th time step's stencil kernels with HIP events")
+    ap.add_argument("--timing-every", type=int, default=0,
+                    help="sample the stencil launches starting at every k-th time step with HIP events "
+                         "(0: 8, and 1 for configs 1 and 2, whose resident kernels run a block of "
+                         "steps per launch)")
     ap.add_argument("--cpu-steps", type=int, default=200, help="time steps of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only timing")
@@ -254,6 +258,8 @@ def main():
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
+    if args.timing_every <= 0:
+        args.timing_every = 1 if args.config in (1, 2) else 8
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -369,8 +375,14 @@ def main():
         # (a two-step launch covers two steps)
         per_launch = 2 if name.startswith(("k_fwd_step2", "k_adj_step2")) else 1
         launches = n * args.timing_every / per_launch / args.steps
+        # resident kernels: one launch per event block, all sampled at
+        # timing_every 1; their steps per launch from the launch count
+        resident = name.startswith(("k_fwd_small", "k_adj_small", "k_fwd_band", "k_adj_band"))
+        if resident:
+            launches = n / args.steps if args.timing_every == 1 else launches
+        run_steps = wl.nt / launches if resident and launches > 0 else None
         # the adjoint accumulates gradients on every launch of a full step
-        nbytes = kernel_bytes(name, wl, store=stores(name), snap_bytes=snap_bytes)
+        nbytes = kernel_bytes(name, wl, store=stores(name), snap_bytes=snap_bytes, run_steps=run_steps)
         kernels[name] = dict(avg_us=avg_ms * 1e3, samples=n, est_total_s=avg_ms * launches / 1e3,
                              alg_bytes=nbytes, gbs=nbytes / (avg_ms * 1e-3) / 1e9)
     dom = max(kernels, key=lambda k: kernels[k]["est_total_s"])
@@ -391,7 +403,10 @@ def main():
     if "fwd" in results:
         for name, (ms, n) in results["fwd"][1].items():
             if n:
-                nb = kernel_bytes(name, wl, store=stores(name), snap_bytes=snap_bytes)
+                rs = None
+                if name.startswith(("k_fwd_small", "k_fwd_band")) and args.timing_every == 1:
+                    rs = wl.nt / (n / args.steps)
+                nb = kernel_bytes(name, wl, store=stores(name), snap_bytes=snap_bytes, run_steps=rs)
                 fwd_kern[name] = dict(avg_us=round(ms / n * 1e3, 2),
                                       gbs=round(nb / (ms / n * 1e-3) / 1e9, 1))
 

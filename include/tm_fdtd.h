@@ -103,9 +103,19 @@ typedef struct tm_desc {
                                fits one workgroup's LDS (ny * nx < 8192, a
                                whole run of steps per launch, one workgroup
                                per shot; snapshots in device memory and no
-                               checkpoints, else 2); 0 = default: 3 with 16
-                               shots or more, else 2.  All give bitwise the
-                               same results.                                   */
+                               checkpoints, else 2); 4 = banded resident
+                               kernels wherever they fit (each shot in bands
+                               of rows, one workgroup per band, a whole run
+                               of steps per launch, neighbouring bands
+                               exchanging halo rows every step; ny < 2048,
+                               every band's workgroup resident at once, same
+                               conditions as 3, else 2); 0 = default: 3 with
+                               16 shots or more, else 4 where the streaming
+                               kernels would leave most of the device idle,
+                               else 2.  All give bitwise the same results.
+                               A banded launch whose exchange wait fails
+                               makes the call return TM_EHIP (never
+                               expected; its outputs are then undefined).    */
     int32_t storage;        /* tm_storage: where a storing forward keeps the
                                snapshots (full-store mode only)                */
     int64_t step_ratio;     /* store snapshots (and accumulate gradients) every

@@ -1015,6 +1015,30 @@ def test_banded_kernels_by_default_for_small_problems():
             np.testing.assert_array_equal(got[key], two[key], err_msg=key)
 
 
+def test_banded_failed_wait_is_reported(monkeypatch):
+    """A banded launch whose exchange wait fails (forced from the host with
+    a poll limit of 0: every workgroup gives up at its first wait and leaves
+    its time loop) makes tm_forward and tm_adjoint return TM_EHIP instead of
+    hanging; the device stays usable and a plan without the forced failure
+    gives the one-step-per-launch results."""
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.random_workload(2, 60, 7, nt=20, n_shots=2, n_src=2, n_rec=4, seed=1460))
+    monkeypatch.setenv("TM_FDTD_BAND_SPIN", "0")
+    prop = native.Propagator(wl, time_block=4)
+    try:
+        with pytest.raises(native.TmError) as e:
+            prop.forward(store=True)
+        assert e.value.status == native.TM_EHIP
+    finally:
+        prop.close()
+    monkeypatch.delenv("TM_FDTD_BAND_SPIN")
+    got = run_gpu(wl, snap="f32", time_block=4)
+    one = run_gpu(wl, snap="f32", time_block=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=key)
+
+
 def test_resident_kernels_by_default_from_16_shots():
     """time_block 0 picks the resident kernels for a grid that fits with 16
     shots or more, the streaming kernels with fewer; bitwise equal."""

@@ -42,7 +42,7 @@ struct BandArgs {
     uint64_t* __restrict__ xbuf;  // exchange rows [workgroup][kind][parity][side: first, last][P][nx]:
                                   // (step tag << 32) | value bits; cleared before each launch
     int* __restrict__ err;        // set to 1 when a wait fails
-    int spin_max;              // polls before a wait fails
+    int spin_max;                 // polls before a wait fails (<= 0: the first wait fails)
 };
 
 // LDS carve-up (float offsets): `ncell` cell arrays of rb + 2P rows (P halo
@@ -200,8 +200,8 @@ __device__ __forceinline__ bool band_exchange(const BandArgs& ba, const Band& t,
         const float v = A[(side ? t.nrow : P) * nx + k];      // own rows [0, P) or [nrow - P, nrow)
         __hip_atomic_store(&ob[i], tag | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    bool bad = false;
-    for (int i = tid; i < 2 * pn; i += NTS) {
+    bool bad = ba.spin_max <= 0;                              // (a host-forced failure, for tests)
+    for (int i = tid; i < 2 * pn && !bad; i += NTS) {
         const int side = i >= pn, k = i - side * pn;
         const int nb = side ? t.b + 1 : t.b - 1;
         if (nb < 0 || nb >= ba.nband) continue;               // beyond the grid: the halo stays 0
