@@ -1039,6 +1039,47 @@ def test_banded_failed_wait_is_reported(monkeypatch):
         np.testing.assert_array_equal(got[key], one[key], err_msg=key)
 
 
+@pytest.mark.parametrize("time_block", [2, 3])
+def test_hip_graph_replays_bitwise(time_block):
+    """The C-ABI calls of a forward with storage and an adjoint can be
+    captured in a HIP graph (no host synchronisation, no memset nodes):
+    every replay, with eager work on the stream between replays, gives
+    bitwise the eager records, per-shot gradients and grad_f (streaming
+    and single-workgroup resident kernels)."""
+    import torch
+
+    from tm_maxwell_fdtd_amd import native
+
+    wl = inputs.as_f32(inputs.random_workload(4, 40, 7, nt=33, n_shots=2, n_src=2, n_rec=5, seed=1480))
+    prop = native.Propagator(wl, time_block=time_block)
+    try:
+        r = torch.zeros((wl.nt, wl.n_shots, wl.n_rec), dtype=torch.float32, device=prop.device)
+        prop.forward(r=r, store=True, check=False)
+        ref = [x.clone() for x in (r, *prop.adjoint(r))]
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):                   # warm-up on the capture stream
+            prop.forward(r=r, store=True, check=False)
+            prop.adjoint(r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            prop.forward(r=r, store=True, check=False)
+            out = prop.adjoint(r)
+        for i in range(3):
+            junk = torch.randn(1 << 16, device=prop.device) * 3.0   # eager work between replays
+            r.fill_(7.0)
+            g.replay()
+            torch.cuda.synchronize()
+            for a, b, name in zip((r, *out), ref, ("records", "grad_f", "gca_shot", "gcb_shot")):
+                assert torch.equal(a, b), f"replay {i}: {name}"
+            del junk
+    finally:
+        prop.close()
+
+
 def test_resident_kernels_by_default_from_16_shots():
     """time_block 0 picks the resident kernels for a grid that fits with 16
     shots or more, the streaming kernels with fewer; bitwise equal."""
