@@ -115,7 +115,9 @@ typedef struct tm_desc {
                                else 2.  All give bitwise the same results.
                                A banded launch whose exchange wait fails
                                makes the call return TM_EHIP (never
-                               expected; its outputs are then undefined).    */
+                               expected; its outputs are then undefined;
+                               not detected in calls captured in a HIP
+                               graph, which the calls otherwise support).    */
     int32_t storage;        /* tm_storage: where a storing forward keeps the
                                snapshots (full-store mode only)                */
     int64_t step_ratio;     /* store snapshots (and accumulate gradients) every

@@ -1039,7 +1039,7 @@ def test_banded_failed_wait_is_reported(monkeypatch):
         np.testing.assert_array_equal(got[key], one[key], err_msg=key)
 
 
-@pytest.mark.parametrize("time_block", [2, 3])
+@pytest.mark.parametrize("time_block", [2, 3, 4])
 def test_hip_graph_replays_bitwise(time_block):
     """The C-ABI calls of a forward with storage and an adjoint can be
     captured in a HIP graph (no host synchronisation, no memset nodes):
