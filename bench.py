@@ -102,7 +102,7 @@ def kernel_bytes(name, wl, store, snap_bytes, run_steps=None):
         name, store = name[:-len("_store")], True
     cells, interior, band_y, band_x = _counts(wl)
     S = wl.n_shots
-    if name in ("k_fwd_small", "k_adj_small", "k_fwd_band", "k_adj_band"):
+    if name in ("k_fwd_small", "k_adj_small", "k_fwd_band", "k_adj_band", "k_fwd_bandk", "k_adj_bandk"):
         # resident kernels: one launch runs a whole event block (run_steps
         # steps, the whole run if not given) on chip; HBM sees the state in
         # and out (fields and band memories), the model once, and per step

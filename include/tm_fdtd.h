@@ -109,10 +109,16 @@ typedef struct tm_desc {
                                of steps per launch, neighbouring bands
                                exchanging halo rows every step; ny < 2048,
                                every band's workgroup resident at once, same
-                               conditions as 3, else 2); 0 = default: 3 with
-                               16 shots or more, else 4 where the streaming
+                               conditions as 3, else 2); 5 = as 4, with
+                               blocked banded kernels where they fit (every
+                               band also steps the 2(2P-1) rows next to it
+                               on each side, so that neighbouring bands
+                               exchange their whole state only every second
+                               step), else as 4; 0 = default: 3 with 16
+                               shots or more, else, where the streaming
                                kernels would leave most of the device idle,
-                               else 2.  All give bitwise the same results.
+                               5 at order 2 and 4 at orders 4 and 8, else 2.
+                               All give bitwise the same results.
                                A banded launch whose exchange wait fails
                                makes the call return TM_EHIP (never
                                expected; its outputs are then undefined;

@@ -50,7 +50,8 @@ def test_timed_kernel_names():
     names = [native.tm_kernel_name(k) for k in range(native.tm_kernel_count())]
     assert names == ["k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2", "k_fwd_step2_uq", "k_adj_step2_uq",
                      "k_fwd_step_store", "k_fwd_step2_store", "k_fwd_step2_uq_store", "k_fwd_small",
-                     "k_fwd_small_store", "k_adj_small", "k_fwd_band", "k_fwd_band_store", "k_adj_band"]
+                     "k_fwd_small_store", "k_adj_small", "k_fwd_band", "k_fwd_band_store", "k_adj_band",
+                     "k_fwd_bandk", "k_fwd_bandk_store", "k_adj_bandk"]
     assert native.tm_kernel_name(-1) is None and native.tm_kernel_name(len(names)) is None
 
 
@@ -91,7 +92,7 @@ def test_valid_plan_and_workspace_size(wl):
 @pytest.mark.parametrize("field,value", [
     ("order", 3), ("order", 6), ("order", 0), ("n_shots", 0), ("nt", 0), ("n_src", -1),
     ("snap", 3), ("snap", -1), ("ckpt_every", -1), ("ny", 5), ("dx", 0.0), ("dy", float("nan")),
-    ("time_block", 5), ("time_block", -1), ("storage", 2), ("step_ratio", -1), ("model_per_shot", 2),
+    ("time_block", 6), ("time_block", -1), ("storage", 2), ("step_ratio", -1), ("model_per_shot", 2),
     ("model_per_shot", -1),
     ("pml_y0", 1), ("pml_x1", 10 ** 6), ("pml_y1", 20),
 ])

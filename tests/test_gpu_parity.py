@@ -904,15 +904,21 @@ def test_resident_small_grid_modes(monkeypatch, case):
         np.testing.assert_array_equal(got[key], one[key], err_msg=f"{case} {key}")
 
 
+BAND_KERNELS = {4: "k_adj_band", 5: "k_adj_bandk"}
+
+
+@pytest.mark.parametrize("tb", [4, 5])
 @pytest.mark.parametrize("order", inputs.ORDERS)
 @pytest.mark.parametrize("snap,ratio,kappa", [("f32", 1, 1.0), ("bf16", 1, 4.0), ("fp8", 1, 1.0), ("f32", 3, 4.0)])
-def test_banded_small_grid_bitwise(order, snap, ratio, kappa):
+def test_banded_small_grid_bitwise(order, snap, ratio, kappa, tb):
     """The banded resident kernels (time_block 4: several workgroups per
-    shot, rows exchanged between neighbouring bands every step) give bitwise
-    the records, per-shot gradients and grad_f of the single-workgroup
-    resident kernels and of one step per launch.  Sources and receivers
-    anywhere (bands, edge rows, duplicates, negative indices), stretched
-    CPML, snapshot kinds and step ratios."""
+    shot, rows exchanged between neighbouring bands every step; time_block
+    5: each band also steps 2(2P-1) rows of its neighbours and the bands
+    exchange their whole state every second step) give bitwise the records,
+    per-shot gradients and grad_f of the single-workgroup resident kernels
+    and of one step per launch.  Sources and receivers anywhere (bands, edge
+    rows, duplicates, negative indices), stretched CPML, snapshot kinds and
+    step ratios."""
     wl = inputs.random_workload(order, 40, 7, nt=57, n_shots=3, n_src=3, n_rec=6, seed=1400 + order,
                                 src_anywhere=True, kappa_max=kappa)
     wl.src[1, 1] = wl.src[1, 0]
@@ -921,10 +927,10 @@ def test_banded_small_grid_bitwise(order, snap, ratio, kappa):
     wl.rec[2, 0] = -1
     wl.rec[1, 4] = wl.src[1, 0]
     wl = inputs.as_f32(wl)
-    ran = _kernel_counts(wl, snap=snap, step_ratio=ratio, time_block=4)
-    assert "k_adj_band" in ran and any(k.startswith("k_fwd_band") for k in ran), ran
+    ran = _kernel_counts(wl, snap=snap, step_ratio=ratio, time_block=tb)
+    assert BAND_KERNELS[tb] in ran and any(k.startswith("k_fwd_band") for k in ran), ran
     assert not any(k.startswith(("k_fwd_step", "k_adj_step", "k_fwd_small", "k_adj_small")) for k in ran), ran
-    got = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=4)
+    got = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=tb)
     res = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=3)
     one = run_gpu(wl, snap=snap, step_ratio=ratio, time_block=1)
     for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
@@ -933,16 +939,19 @@ def test_banded_small_grid_bitwise(order, snap, ratio, kappa):
     assert np.abs(got["records"]).max() > 0
 
 
+@pytest.mark.parametrize("tb", [4, 5])
 @pytest.mark.parametrize("order,n_int,nx_int,shots", [(2, 150, 90, 1), (4, 120, 200, 2), (8, 60, 150, 4)])
-def test_banded_larger_grid(orc, order, n_int, nx_int, shots):
+def test_banded_larger_grid(orc, order, n_int, nx_int, shots, tb):
     """Grids too large for one workgroup's LDS, in bands: against one step
     per launch (bitwise) and the oracle (within the tolerances)."""
     wl = inputs.as_f32(inputs.random_workload(order, n_int, 8, nt=45, n_shots=shots, n_src=2, n_rec=8,
                                               seed=1420 + order, nx_int=nx_int))
     assert wl.ny * wl.nx > 8192
-    ran = _kernel_counts(wl, time_block=4)
-    assert "k_adj_band" in ran, ran
-    got = run_gpu(wl, snap="f32", time_block=4)
+    ran = _kernel_counts(wl, time_block=tb)
+    # (time_block 5 at order 8: 2 x 14 extended rows of 174 cells exceed a
+    # band's cells, so the bands exchange every step)
+    assert BAND_KERNELS[4 if order == 8 else tb] in ran, ran
+    got = run_gpu(wl, snap="f32", time_block=tb)
     one = run_gpu(wl, snap="f32", time_block=1)
     for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
         np.testing.assert_array_equal(got[key], one[key], err_msg=key)
@@ -955,8 +964,9 @@ def test_banded_larger_grid(orc, order, n_int, nx_int, shots):
     compare("grad_f", got["grad_f"], ref["grad_f"], GRAD_TOL["f32"])
 
 
+@pytest.mark.parametrize("tb", [4, 5])
 @pytest.mark.parametrize("case", ["chunks", "event-blocks", "per-shot-models", "no-grads", "ckpt-plan"])
-def test_banded_modes(monkeypatch, case):
+def test_banded_modes(monkeypatch, case, tb):
     """The banded kernels under the other call patterns, bitwise against
     one step per launch: forward chunks, short event blocks (one launch per
     block), one model per shot, an adjoint without gradients, and a
@@ -978,8 +988,8 @@ def test_banded_modes(monkeypatch, case):
         kw = dict(ckpt_every=9)
     if case == "no-grads":
         outs = []
-        for tb in (4, 1):
-            prop = native.Propagator(wl, time_block=tb)
+        for b in (tb, 1):
+            prop = native.Propagator(wl, time_block=b)
             try:
                 r = prop.forward(store=False)
                 d = torch.randn(r.shape, generator=torch.Generator().manual_seed(5)).to(prop.device)
@@ -991,7 +1001,7 @@ def test_banded_modes(monkeypatch, case):
         np.testing.assert_array_equal(outs[0][0], outs[1][0])
         np.testing.assert_array_equal(outs[0][1], outs[1][1])
         return
-    got = run_gpu(wl, snap="f32", chunks=chunks, time_block=4, **kw)
+    got = run_gpu(wl, snap="f32", chunks=chunks, time_block=tb, **kw)
     one = run_gpu(wl, snap="f32", chunks=chunks, time_block=1, **kw)
     for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
         np.testing.assert_array_equal(got[key], one[key], err_msg=f"{case} {key}")
@@ -999,15 +1009,15 @@ def test_banded_modes(monkeypatch, case):
 
 def test_banded_kernels_by_default_for_small_problems():
     """time_block 0 runs the banded kernels on the small workloads (the
-    order-2 86^2 grid with one shot, the order-4 300^2 grid with four) and
-    the streaming kernels on a large one; bitwise equal to two steps per
-    launch."""
+    order-2 86^2 grid with one shot: the blocked ones; the order-4 300^2
+    grid with four: those exchanging every step) and the streaming kernels
+    on a large one; bitwise equal to two steps per launch."""
     wl1 = inputs.as_f32(inputs.make_config(1, nt=30))
     wl2 = inputs.as_f32(inputs.make_config(2, nt=20))
     wl3 = inputs.as_f32(inputs.make_config(3, n_shots=1, nt=6))
-    assert "k_adj_band" in _kernel_counts(wl1)
+    assert "k_adj_bandk" in _kernel_counts(wl1)
     assert "k_adj_band" in _kernel_counts(wl2)
-    assert "k_adj_band" not in _kernel_counts(wl3)
+    assert not any(k.startswith("k_adj_band") for k in _kernel_counts(wl3))
     for wl in (wl1, wl2):
         got = run_gpu(wl)
         two = run_gpu(wl, time_block=2)
@@ -1015,7 +1025,27 @@ def test_banded_kernels_by_default_for_small_problems():
             np.testing.assert_array_equal(got[key], two[key], err_msg=key)
 
 
-def test_banded_failed_wait_is_reported(monkeypatch):
+@pytest.mark.parametrize("order,kx", [(2, 1), (2, 3), (2, 4), (4, 1), (8, 1)])
+def test_blocked_banded_exchange_intervals(monkeypatch, order, kx):
+    """The blocked banded kernels with other numbers of steps between
+    exchanges (TM_FDTD_BAND_KX; the band heights follow), with an odd step
+    count, so that the last run of steps between exchanges is short:
+    bitwise one step per launch."""
+    wl = inputs.random_workload(order, 70, 7, nt=47, n_shots=2, n_src=2, n_rec=6, seed=1470 + order + kx,
+                                src_anywhere=True, kappa_max=3.0)
+    wl = inputs.as_f32(wl)
+    monkeypatch.setenv("TM_FDTD_BAND_KX", str(kx))
+    ran = _kernel_counts(wl, time_block=5)
+    assert "k_adj_bandk" in ran, ran
+    got = run_gpu(wl, snap="bf16", step_ratio=2, time_block=5)
+    monkeypatch.delenv("TM_FDTD_BAND_KX")
+    one = run_gpu(wl, snap="bf16", step_ratio=2, time_block=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=key)
+
+
+@pytest.mark.parametrize("tb", [4, 5])
+def test_banded_failed_wait_is_reported(monkeypatch, tb):
     """A banded launch whose exchange wait fails (forced from the host with
     a poll limit of 0: every workgroup gives up at its first wait and leaves
     its time loop) makes tm_forward and tm_adjoint return TM_EHIP instead of
@@ -1025,7 +1055,7 @@ def test_banded_failed_wait_is_reported(monkeypatch):
 
     wl = inputs.as_f32(inputs.random_workload(2, 60, 7, nt=20, n_shots=2, n_src=2, n_rec=4, seed=1460))
     monkeypatch.setenv("TM_FDTD_BAND_SPIN", "0")
-    prop = native.Propagator(wl, time_block=4)
+    prop = native.Propagator(wl, time_block=tb)
     try:
         with pytest.raises(native.TmError) as e:
             prop.forward(store=True)
@@ -1033,19 +1063,19 @@ def test_banded_failed_wait_is_reported(monkeypatch):
     finally:
         prop.close()
     monkeypatch.delenv("TM_FDTD_BAND_SPIN")
-    got = run_gpu(wl, snap="f32", time_block=4)
+    got = run_gpu(wl, snap="f32", time_block=tb)
     one = run_gpu(wl, snap="f32", time_block=1)
     for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
         np.testing.assert_array_equal(got[key], one[key], err_msg=key)
 
 
-@pytest.mark.parametrize("time_block", [2, 3, 4])
+@pytest.mark.parametrize("time_block", [2, 3, 4, 5])
 def test_hip_graph_replays_bitwise(time_block):
     """The C-ABI calls of a forward with storage and an adjoint can be
     captured in a HIP graph (no host synchronisation, no memset nodes):
     every replay, with eager work on the stream between replays, gives
-    bitwise the eager records, per-shot gradients and grad_f (streaming
-    and single-workgroup resident kernels)."""
+    bitwise the eager records, per-shot gradients and grad_f (streaming,
+    single-workgroup resident, banded and blocked banded kernels)."""
     import torch
 
     from tm_maxwell_fdtd_amd import native

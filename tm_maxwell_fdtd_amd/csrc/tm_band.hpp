@@ -539,3 +539,619 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
 }
 
 }  // namespace tmf
+
+namespace tmf {
+
+// ---------------------------------------------------------------------------
+// Blocked variant: one exchange per kx steps.
+//
+// Each workgroup computes every step on its band widened by hd = kx (2P-1)
+// rows on each side (its "extended" rows), as if the extended rows were the
+// whole grid.  A row's value after a step depends on rows at most 2P-1 away
+// before it, so after kx steps the own rows are exact although the outer
+// extended rows were computed from rows the workgroup does not hold; then
+// the whole state of the extended rows outside the band (fields and band
+// memories, seven words per cell) is replaced by the neighbours' own rows,
+// which are exact.  Sources and receiver residuals are injected on every
+// extended row, so the rows that matter are computed exactly; records,
+// snapshots, source gradients and model gradients are written for the own
+// rows only.  The band memories live in the cells' registers.  Exchange
+// words are tagged with the exchange number, as above.
+// ---------------------------------------------------------------------------
+
+constexpr int BK_NW = 7;                    // exchanged words per cell
+
+struct BandKArgs {
+    SmallArgs a;
+    int rb, nband;                          // owned rows per band (each band at least hd), bands per shot
+    int hd, kx;                             // extended rows on each side, steps between exchanges
+    uint64_t* __restrict__ xbuf;            // [workgroup][parity][side][BK_NW][hd][nx] tagged words
+    int* __restrict__ err;
+    int spin_max;
+};
+
+struct BandKLayout {
+    uint32_t pad, stride;                   // padding, and floats per padded cell array
+    uint32_t ty, tx, slot;                  // tables
+    uint32_t floats;
+};
+
+__host__ __device__ inline BandKLayout bandk_layout(const Geo& g, int rb, int hd, int ncell)
+{
+    BandKLayout s;
+    s.pad = (uint32_t)(g.P * g.nx + g.P);
+    s.stride = (uint32_t)((rb + 2 * hd) * g.nx) + 2u * s.pad;
+    uint32_t o = (uint32_t)ncell * s.stride;
+    s.ty = o; o += 6u * (uint32_t)g.ny;
+    s.tx = o; o += 6u * (uint32_t)g.nx;
+    s.slot = o; o += (uint32_t)g.ny;
+    s.floats = o;
+    return s;
+}
+
+__host__ __device__ inline uint32_t bandk_lds_bytes(const Geo& g, int rb, int hd, bool adjoint)
+{
+    return 4u * bandk_layout(g, rb, hd, adjoint ? 4 : 3).floats;
+}
+
+__host__ __device__ inline bool bandk_rows_ok(const Geo& g, int rb, int hd)
+{
+    return rb >= hd && hd >= 2 * g.P - 1 && (rb + 2 * hd + g.P) * g.nx + g.P < (1 << 14) &&
+           (rb + 2 * hd) * g.nx <= NTS * CPTB && g.ny < 2048;
+}
+
+struct BandK {
+    int s, b, w;
+    int ya, yb, nrow;                       // own rows [ya, yb)
+    int ea, eb;                             // extended rows in the grid [ea, eb)
+    int y_arr;                              // global row of array row 0 (ya - hd)
+};
+
+__device__ __forceinline__ BandK bandk_of(const BandKArgs& ba)
+{
+    BandK t;
+    t.w = blockIdx.x;
+    t.s = t.w / ba.nband;
+    t.b = t.w - t.s * ba.nband;
+    t.ya = t.b * ba.rb;
+    t.yb = min(t.ya + ba.rb, ba.a.g.ny);
+    t.nrow = t.yb - t.ya;
+    t.ea = max(t.ya - ba.hd, 0);
+    t.eb = min(t.yb + ba.hd, ba.a.g.ny);
+    t.y_arr = t.ya - ba.hd;
+    return t;
+}
+
+// One cell of the extended rows (index je from row ea), packed as in
+// tm_small.hpp with j its index in the cell arrays (array row y - y_arr).
+template <int P>
+__device__ __forceinline__ int pack_bandk_cell(int je, const BandK& t, int rows, const Geo& g)
+{
+    const int nx = g.nx;
+    const bool ok = je < (t.eb - t.ea) * nx;
+    const int r = ok ? je / nx : 0;
+    const int y = t.ea + r, x = ok ? je - r * nx : P;
+    const bool ecol = x >= P && x <= nx - P, erow = y >= P && y <= g.ny - P;
+    const bool e = ok && ecol && erow;
+    const bool hx = ok && ecol && y >= P && y <= g.ny - P - 1;
+    const bool hz = ok && erow && x >= P && x <= nx - P - 1;
+    const bool fhy = hx && (y < g.y0 || y >= g.hy1), fhx = hz && (x < g.x0 || x >= g.hx1);
+    const bool fey = e && (y < g.y0 || y >= g.y1), fex = e && (x < g.x0 || x >= g.x1);
+    const int j = ok ? (y - t.y_arr) * nx + x : rows * nx;
+    return j | (y << 14) | ((int)e << CB_E) | ((int)hx << CB_HX) | ((int)hz << CB_HZ) | ((int)fhy << CB_FHY) |
+           ((int)fhx << CB_FHX) | ((int)fey << CB_FEY) | ((int)fex << CB_FEX);
+}
+
+// The CPML tables and event-row slots into LDS.
+__device__ __forceinline__ void bandk_tables(float* lds, const BandKLayout& bl, const Geo& g,
+                                             const float* __restrict__ cp, const EventRows& ev, int s)
+{
+    for (int i = threadIdx.x; i < 6 * g.ny; i += NTS) {
+        const int k = i / g.ny, y = i - k * g.ny;
+        const int row = (k < 3 ? AYH : AY) + (k < 3 ? k : k - 3);
+        const float v = cp[row * g.L + y];
+        lds[bl.ty + i] = (k == 2 || k == 5) ? 1.0f / v : v;
+    }
+    for (int i = threadIdx.x; i < 6 * g.nx; i += NTS) {
+        const int k = i / g.nx, x = i - k * g.nx;
+        const int row = (k < 3 ? AXH : AX) + (k < 3 ? k : k - 3);
+        const float v = cp[row * g.L + x];
+        lds[bl.tx + i] = (k == 2 || k == 5) ? 1.0f / v : v;
+    }
+    int* slot = reinterpret_cast<int*>(lds + bl.slot);
+    for (int y = threadIdx.x; y < g.ny; y += NTS) slot[y] = ev.row_slot[s * g.ny + y];
+}
+
+// The band memories of a cell, from / to set b: every cell of a row of the
+// y-band arrays has a y-memory word, every cell of a column of the x-band
+// arrays an x-memory word (also where no filter site applies: those words
+// pass through unchanged); 0 elsewhere.
+struct CellMem {
+    float yh, xh, ye, xe;
+};
+
+__device__ __forceinline__ CellMem bandk_mem_load(const RBuf& b, const StateLayout& L, const Geo& g, int y, int x,
+                                                  bool ok)
+{
+    const bool ry = ok && flag_hy(g, y), rx = ok && flag_hx(g, x);
+    const uint32_t oy = (uint32_t)((ry ? band_y(g, y) : 0) * g.nx + x) * 4u;
+    const uint32_t ox = (uint32_t)(y * g.bx + (rx ? band_x(g, x) : 0)) * 4u;
+    CellMem m;
+    m.yh = b.ld(ry, oy, L.oMyh);
+    m.ye = b.ld(ry, oy, L.oMye);
+    m.xh = b.ld(rx, ox, L.oMxh);
+    m.xe = b.ld(rx, ox, L.oMxe);
+    return m;
+}
+
+__device__ __forceinline__ void bandk_mem_store(const RBuf& b, const StateLayout& L, const Geo& g, int y, int x,
+                                                bool own, const CellMem& m)
+{
+    const bool ry = own && flag_hy(g, y), rx = own && flag_hx(g, x);
+    const uint32_t oy = (uint32_t)((ry ? band_y(g, y) : 0) * g.nx + x) * 4u;
+    const uint32_t ox = (uint32_t)(y * g.bx + (rx ? band_x(g, x) : 0)) * 4u;
+    b.st(ry, m.yh, oy, L.oMyh);
+    b.st(ry, m.ye, oy, L.oMye);
+    b.st(rx, m.xh, ox, L.oMxh);
+    b.st(rx, m.xe, ox, L.oMxe);
+}
+
+// A filter on a register memory: the recursion where the site applies,
+// the identity elsewhere.
+__device__ __forceinline__ float rsite(bool on, float& m, const float* tab, int n, float d)
+{
+    if (on) d = cpml_step(m, tab[0], tab[n], tab[2 * n], d);
+    return d;
+}
+
+// Exchange number n: publish the words of the cells on the first and last
+// hd own rows (w[0..6] of each cell, read by get(i, k)), then replace the
+// words of the cells on the extended rows outside the band with the
+// neighbours' (put(i, k, v)).  Returns false (in every thread) when the
+// launch has failed.
+template <int P, typename Get, typename Put>
+__device__ __forceinline__ bool bandk_exchange(const BandKArgs& ba, const BandK& t, const int (&pk)[CPTB], int n,
+                                               int* quit, Get get, Put put)
+{
+    const int nx = ba.a.g.nx, hd = ba.hd;
+    const size_t plane = (size_t)hd * nx, side_w = plane * BK_NW;   // one word of every cell of a side
+    const uint64_t tag = (uint64_t)(uint32_t)(n + 1) << 32;
+    __syncthreads();                                          // the step's LDS writes are done
+    uint64_t* ob = ba.xbuf + (size_t)((t.w * 2 + (n & 1)) * 2) * side_w;
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const Cell c = cell(pk[i]);
+        const int y = c.y(), x = c.j() - (y - t.y_arr) * nx;
+        const bool valid = c.j() < (t.eb - t.y_arr) * nx && y >= t.ya && y < t.yb;
+        if (!valid) continue;
+        if (y < t.ya + hd) {                                  // side 0: first hd own rows
+            uint64_t* o = ob + (size_t)(y - t.ya) * nx + x;
+#pragma unroll
+            for (int k = 0; k < BK_NW; ++k)
+                __hip_atomic_store(&o[k * plane], tag | __float_as_uint(get(i, k)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (y >= t.yb - hd) {                                 // side 1: last hd own rows
+            uint64_t* o = ob + side_w + (size_t)(y - (t.yb - hd)) * nx + x;
+#pragma unroll
+            for (int k = 0; k < BK_NW; ++k)
+                __hip_atomic_store(&o[k * plane], tag | __float_as_uint(get(i, k)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    bool bad = ba.spin_max <= 0;                              // (a host-forced failure, for tests)
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const Cell c = cell(pk[i]);
+        const int y = c.y(), x = c.j() - (y - t.y_arr) * nx;
+        const bool valid = c.j() < (t.eb - t.y_arr) * nx;
+        if (!valid || bad || (y >= t.ya && y < t.yb)) continue;
+        // above the band: the band above's last rows [ya - hd, ya); below:
+        // the band below's first rows [yb, yb + hd)
+        const bool above = y < t.ya;
+        const int nb = above ? t.b - 1 : t.b + 1;
+        const int r = above ? y - (t.ya - hd) : y - t.yb;
+        const uint64_t* ib = ba.xbuf + (size_t)(((t.s * ba.nband + nb) * 2 + (n & 1)) * 2 + (above ? 1 : 0)) * side_w +
+                             (size_t)r * nx + x;
+        uint64_t w[BK_NW];
+        for (int it = 0;; ++it) {
+            bool all = true;
+#pragma unroll
+            for (int k = 0; k < BK_NW; ++k) {
+                w[k] = __hip_atomic_load(&ib[k * plane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                all = all && (w[k] & 0xffffffff00000000ull) == tag;
+            }
+            if (all) break;
+            if (it >= ba.spin_max ||
+                ((it & 63) == 63 && __hip_atomic_load(ba.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                bad = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (bad) continue;
+#pragma unroll
+        for (int k = 0; k < BK_NW; ++k) put(i, k, __uint_as_float((uint32_t)w[k]));
+    }
+    if (bad) {
+        __hip_atomic_store(ba.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *quit = 1;
+    }
+    __syncthreads();
+    return *quit == 0;
+}
+
+// Forward, blocked: steps t0 .. t1-1, workgroup = (shot, band).
+template <int P, int SNAP>
+__global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
+{
+    extern __shared__ float lds[];
+    __shared__ int quit;
+    const SmallArgs& a = ba.a;
+    const Geo& g = a.g;
+    const StateLayout& L = a.L;
+    const BandK t = bandk_of(ba);
+    const int s = t.s, tid = threadIdx.x;
+    const int ny = g.ny, nx = g.nx;
+    const int rows = ba.rb + 2 * ba.hd;
+    const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 3);
+    float* const sE = lds + bl.pad;
+    float* const sHx = sE + bl.stride;
+    float* const sHz = sHx + bl.stride;
+    const float* const ty = lds + bl.ty;
+    const float* const tx = lds + bl.tx;
+    const int* const slot = reinterpret_cast<const int*>(lds + bl.slot);
+
+    const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
+    const RBuf bev(a.ev.base, a.ev.bytes);
+
+    // fields of the array rows (0 off the grid) and the padding
+    const int arr = rows * nx;
+    for (int i = tid - (int)bl.pad; i < arr + (int)bl.pad; i += NTS) {
+        const int gj = t.y_arr * nx + i;
+        const bool in = i >= 0 && i < arr && gj >= 0 && gj < ny * nx;
+        const uint32_t o = (uint32_t)(in ? gj : 0) * 4u;
+        sE[i] = b0.ld(in, o, L.oE);
+        sHx[i] = b0.ld(in, o, L.oHx);
+        sHz[i] = b0.ld(in, o, L.oHz);
+    }
+    bandk_tables(lds, bl, g, a.cp, a.ev, s);
+    if (tid == 0) quit = 0;
+
+    auto xof = [&](const Cell& c) { return c.j() - (c.y() - t.y_arr) * nx; };
+    // iteration i of the cell loops has work in this wave
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = (t.eb - t.ea) * nx;
+    auto live = [&](int i) { return i * NTS + wbase < ncel; };
+    int pk[CPTB];
+    float ca[CPTB], cb[CPTB], cq[CPTB];
+    CellMem mm[CPTB];
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const int je = tid + i * NTS;
+        const bool ok = je < (t.eb - t.ea) * nx;
+        pk[i] = pack_bandk_cell<P>(je, t, rows, g);
+        const uint32_t o = (uint32_t)(ok ? t.ea * nx + je : 0) * 4u;
+        ca[i] = bm.ld(ok, o, a.m.oCa);
+        cb[i] = bm.ld(ok, o, a.m.oCb);
+        cq[i] = bm.ld(ok, o, a.m.oCq);
+        const Cell c{pk[i]};
+        mm[i] = bandk_mem_load(b0, L, g, c.y(), xof(c), ok);
+    }
+    __syncthreads();
+
+    // event-row offsets of the cells (RBuf::OOB off the event rows), and
+    // the iterations in which this wave has any
+    int evo[CPTB], evmask = 0;
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const Cell c{pk[i]};
+        const int gs = slot[c.y()];
+        evo[i] = c.bit(CB_E) && gs >= 0 ? (gs * nx + xof(c)) * 4 : RBuf::OOB;
+        if (__builtin_amdgcn_ballot_w64(evo[i] != RBuf::OOB) != 0) evmask |= 1 << i;
+    }
+    evmask = __builtin_amdgcn_readfirstlane(evmask);
+
+    float add[CPTB];
+    auto load_add = [&](int tt, float (&dst)[CPTB]) {
+        const bool in_run = tt < a.t1;
+        const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            dst[i] = 0.0f;
+            if (((evmask >> i) & 1) == 0) continue;
+            dst[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
+        }
+    };
+    load_add(a.t0, add);
+    auto get = [&](int i, int k) -> float {
+        const int j = Cell{pk[i]}.j();
+        return k == 0 ? sE[j] : k == 1 ? sHx[j] : k == 2 ? sHz[j] : k == 3 ? mm[i].yh : k == 4 ? mm[i].xh
+             : k == 5 ? mm[i].ye : mm[i].xe;
+    };
+    auto put = [&](int i, int k, float v) {
+        const int j = Cell{pk[i]}.j();
+        if (k == 0) sE[j] = v;
+        else if (k == 1) sHx[j] = v;
+        else if (k == 2) sHz[j] = v;
+        else if (k == 3) mm[i].yh = v;
+        else if (k == 4) mm[i].xh = v;
+        else if (k == 5) mm[i].ye = v;
+        else mm[i].xe = v;
+    };
+
+    int nex = 0;
+    for (int tt = a.t0; tt < a.t1; ++tt) {
+        float add_n[CPTB];
+        load_add(tt + 1, add_n);
+
+        // ---- H half-step on every extended row
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            if (!live(i)) continue;
+            const Cell c = cell(pk[i]);
+            const int j = c.j(), x = xof(c);
+            const float hx = sHx[j], hz = sHz[j];
+            float dy = g.rdy * stencil<P>([&](int k) { return sE[j + k * nx]; },
+                                          [&](int k) { return sE[j - (k - 1) * nx]; });
+            float dx = g.rdx * stencil<P>([&](int k) { return sE[j + k]; }, [&](int k) { return sE[j - k + 1]; });
+            dy = rsite(c.bit(CB_FHY), mm[i].yh, ty + c.y(), ny, dy);
+            dx = rsite(c.bit(CB_FHX), mm[i].xh, tx + x, nx, dx);
+            sHx[j] = c.bit(CB_HX) ? fmaf(-cq[i], dy, hx) : hx;
+            sHz[j] = c.bit(CB_HZ) ? fmaf(cq[i], dx, hz) : hz;
+        }
+        __syncthreads();
+
+        // ---- E step on every extended row; outputs of the own rows
+        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+                              : nullptr,
+                       stored ? a.snap_shot_bytes : 0u);
+        const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            if (!live(i)) continue;
+            const Cell c = cell(pk[i]);
+            const int j = c.j(), y = c.y(), x = xof(c);
+            const float ev = sE[j];
+            float uu = g.rdx * stencil<P>([&](int k) { return sHz[j + k - 1]; }, [&](int k) { return sHz[j - k]; });
+            float v = g.rdy * stencil<P>([&](int k) { return sHx[j + (k - 1) * nx]; },
+                                         [&](int k) { return sHx[j - k * nx]; });
+            uu = rsite(c.bit(CB_FEX), mm[i].xe, tx + 3 * nx + x, nx, uu);
+            v = rsite(c.bit(CB_FEY), mm[i].ye, ty + 3 * ny + y, ny, v);
+            const float curl = uu - v;
+            const bool own = y >= t.ya && y < t.yb;
+            if constexpr (SNAP != SNAP_NONE) {
+                const bool in_w = own && c.bit(CB_E) && y >= g.y0 && y < g.y1 && x >= g.x0 && x < g.x1;
+                snap_put2<SNAP>(bsp, stored && in_w, (uint32_t)((y - g.y0) * g.nxi + (x - g.x0)), ev, curl);
+            }
+            float en = fmaf(ca[i], ev, cb[i] * curl);
+            en = evo[i] != RBuf::OOB ? en + add[i] : en;
+            if ((evmask >> i) & 1) bev.stv(en, own ? evo[i] : RBuf::OOB, out_off);
+            sE[j] = c.bit(CB_E) ? en : ev;
+        }
+        if (tt + 1 < a.t1 && (tt + 1 - a.t0) % ba.kx == 0) {
+            if (!bandk_exchange<P>(ba, t, pk, nex++, &quit, get, put)) break;
+        } else {
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) add[i] = add_n[i];
+    }
+
+    // own rows back
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const Cell c{pk[i]};
+        const int y = c.y(), x = xof(c);
+        const bool own = c.j() < (t.eb - t.y_arr) * nx && y >= t.ya && y < t.yb;
+        const uint32_t o = (uint32_t)(own ? y * nx + x : 0) * 4u;
+        b1.st(own, sE[c.j()], o, L.oE);
+        b1.st(own, sHx[c.j()], o, L.oHx);
+        b1.st(own, sHz[c.j()], o, L.oHz);
+        bandk_mem_store(b1, L, g, y, x, own, mm[i]);
+    }
+}
+
+// Exact adjoint, blocked: steps t1-1 down to t0, workgroup = (shot, band).
+template <int P, int SNAP>
+__global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
+{
+    extern __shared__ float lds[];
+    __shared__ int quit;
+    const SmallArgs& a = ba.a;
+    const Geo& g = a.g;
+    const StateLayout& L = a.L;
+    const BandK t = bandk_of(ba);
+    const int s = t.s, tid = threadIdx.x;
+    const int ny = g.ny, nx = g.nx;
+    const int rows = ba.rb + 2 * ba.hd;
+    const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 4);
+    float* const sU = lds + bl.pad;
+    float* const sW = sU + bl.stride;
+    float* const sTZ = sW + bl.stride;
+    float* const sTX = sTZ + bl.stride;
+    const float* const ty = lds + bl.ty;
+    const float* const tx = lds + bl.tx;
+    const int* const slot = reinterpret_cast<const int*>(lds + bl.slot);
+
+    const RBuf b0(a.set0 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf b1(a.set1 + (int64_t)s * L.shot_bytes, L.shot_bytes);
+    const RBuf bm(a.m.base + (int64_t)s * a.m.shot_stride, a.m.bytes);
+    const RBuf bev(a.ev.base, a.ev.bytes);
+    const uint32_t slab_b = (uint32_t)(g.slab * 4);
+    const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
+    const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
+
+    for (int i = tid; i < 4 * (int)bl.stride; i += NTS) lds[i] = 0.0f;
+    bandk_tables(lds, bl, g, a.cp, a.ev, s);
+    if (tid == 0) quit = 0;
+
+    auto xof = [&](const Cell& c) { return c.j() - (c.y() - t.y_arr) * nx; };
+    auto own_of = [&](const Cell& c) {
+        const int y = c.y();
+        return c.j() < (t.eb - t.y_arr) * nx && y >= t.ya && y < t.yb;
+    };
+    auto in_window = [&](const Cell& c) {
+        const int y = c.y(), x = xof(c);
+        return own_of(c) && c.bit(CB_E) && y >= g.y0 && y < g.y1 && x >= g.x0 && x < g.x1;
+    };
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = (t.eb - t.ea) * nx;
+    auto live = [&](int i) { return i * NTS + wbase < ncel; };
+    int pk[CPTB];
+    float ca[CPTB], cb[CPTB], cq[CPTB], lE[CPTB], lHx[CPTB], lHz[CPTB], ga[CPTB], gb[CPTB];
+    CellMem mm[CPTB];
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const int je = tid + i * NTS;
+        const bool ok = je < (t.eb - t.ea) * nx;
+        pk[i] = pack_bandk_cell<P>(je, t, rows, g);
+        const uint32_t o = (uint32_t)(ok ? t.ea * nx + je : 0) * 4u;
+        ca[i] = bm.ld(ok, o, a.m.oCa);
+        cb[i] = bm.ld(ok, o, a.m.oCb);
+        cq[i] = bm.ld(ok, o, a.m.oCq);
+        lE[i] = b0.ld(ok, o, L.oE);
+        lHx[i] = b0.ld(ok, o, L.oHx);
+        lHz[i] = b0.ld(ok, o, L.oHz);
+        const Cell c{pk[i]};
+        const bool gw = SNAP != SNAP_NONE && in_window(c);
+        ga[i] = bga.ld(gw, o, 0u);
+        gb[i] = bgb.ld(gw, o, 0u);
+        mm[i] = bandk_mem_load(b0, L, g, c.y(), xof(c), ok);
+    }
+
+    __syncthreads();
+    int evo[CPTB], evmask = 0;
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const Cell c{pk[i]};
+        const int gs = slot[c.y()];
+        evo[i] = c.bit(CB_E) && gs >= 0 ? (gs * nx + xof(c)) * 4 : RBuf::OOB;
+        if (__builtin_amdgcn_ballot_w64(evo[i] != RBuf::OOB) != 0) evmask |= 1 << i;
+    }
+    evmask = __builtin_amdgcn_readfirstlane(evmask);
+
+    float add[CPTB], se[CPTB], sc[CPTB];
+    auto load_step = [&](int tt) {
+        const bool in_run = tt >= a.t0;
+        const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
+        const bool stored = SNAP != SNAP_NONE && in_run && tt % a.R == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+                              : nullptr,
+                       stored ? a.snap_shot_bytes : 0u);
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            add[i] = se[i] = sc[i] = 0.0f;
+            if (!live(i)) continue;
+            const Cell c = cell(pk[i]);
+            const int y = c.y(), x = xof(c);
+            if ((evmask >> i) & 1) add[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
+            const SnapPair sp = snap_get2<SNAP>(bsp, stored && in_window(c),
+                                                (uint32_t)((y - g.y0) * g.nxi + (x - g.x0)));
+            se[i] = sp.e;
+            sc[i] = sp.c;
+        }
+    };
+    auto get = [&](int i, int k) -> float {
+        return k == 0 ? lE[i] : k == 1 ? lHx[i] : k == 2 ? lHz[i] : k == 3 ? mm[i].yh : k == 4 ? mm[i].xh
+             : k == 5 ? mm[i].ye : mm[i].xe;
+    };
+    auto put = [&](int i, int k, float v) {
+        if (k == 0) lE[i] = v;
+        else if (k == 1) lHx[i] = v;
+        else if (k == 2) lHz[i] = v;
+        else if (k == 3) mm[i].yh = v;
+        else if (k == 4) mm[i].xh = v;
+        else if (k == 5) mm[i].ye = v;
+        else mm[i].xe = v;
+    };
+    __syncthreads();
+    load_step(a.t1 - 1);
+
+    int nex = 0;
+    for (int tt = a.t1 - 1; tt >= a.t0; --tt) {
+        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
+        const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
+
+        // ---- phase 1 on every extended row: residual, gradient (own), Cb, E-update filters
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            if (!live(i)) continue;
+            const Cell c = cell(pk[i]);
+            const int j = c.j(), y = c.y(), x = xof(c);
+            const bool on = c.bit(CB_E);
+            const float e = evo[i] != RBuf::OOB ? lE[i] + add[i] : lE[i];
+            if ((evmask >> i) & 1) bev.stv(e, own_of(c) ? evo[i] : RBuf::OOB, out_off);
+            if (SNAP != SNAP_NONE && stored) {
+                const bool in_w = in_window(c);
+                const float na = fmaf(e, se[i] * a.ratio, ga[i]), nb = fmaf(e, sc[i] * a.ratio, gb[i]);
+                ga[i] = in_w ? na : ga[i];
+                gb[i] = in_w ? nb : gb[i];
+            }
+            const float hv = cb[i] * e;
+            const float u = rsite(c.bit(CB_FEX), mm[i].xe, tx + 3 * nx + x, nx, hv);
+            const float w = rsite(c.bit(CB_FEY), mm[i].ye, ty + 3 * ny + y, ny, hv);
+            sU[j] = on ? u : 0.0f;
+            sW[j] = on ? w : 0.0f;
+            lE[i] = e;
+        }
+        load_step(tt - 1);
+        __syncthreads();
+
+        // ---- phase 2 on every extended row: transposed curl, Cq, H-update filters
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            if (!live(i)) continue;
+            const Cell c = cell(pk[i]);
+            const int j = c.j();
+            const float accx = stencil<P>([&](int k) { return sW[j + k * nx]; },
+                                          [&](int k) { return sW[j - (k - 1) * nx]; });
+            const float accz = stencil<P>([&](int k) { return sU[j + k]; }, [&](int k) { return sU[j - k + 1]; });
+            const float lhx = fmaf(g.rdy, accx, lHx[i]);
+            const float lhz = fmaf(-g.rdx, accz, lHz[i]);
+            const int y = c.y(), x = xof(c);
+            const float txv = rsite(c.bit(CB_FHY), mm[i].yh, ty + y, ny, cq[i] * lhx);
+            const float tz = rsite(c.bit(CB_FHX), mm[i].xh, tx + x, nx, cq[i] * lhz);
+            const bool hx = c.bit(CB_HX), hz = c.bit(CB_HZ);
+            lHx[i] = hx ? lhx : lHx[i];
+            lHz[i] = hz ? lhz : lHz[i];
+            sTX[j] = hx ? txv : 0.0f;
+            sTZ[j] = hz ? tz : 0.0f;
+        }
+        __syncthreads();
+
+        // ---- phase 3 on every extended row: lambda_E = Ca e - Dx[t_z] + Dz[t_x]
+#pragma unroll
+        for (int i = 0; i < CPTB; ++i) {
+            if (!live(i)) continue;
+            const Cell c = cell(pk[i]);
+            const int j = c.j();
+            const float az = stencil<P>([&](int k) { return sTZ[j + k - 1]; }, [&](int k) { return sTZ[j - k]; });
+            const float ay = stencil<P>([&](int k) { return sTX[j + (k - 1) * nx]; },
+                                        [&](int k) { return sTX[j - k * nx]; });
+            const float en = fmaf(ca[i], lE[i], fmaf(-az, g.rdx, ay * g.rdy));
+            lE[i] = c.bit(CB_E) ? en : lE[i];
+        }
+        if (tt > a.t0 && (a.t1 - tt) % ba.kx == 0) {
+            if (!bandk_exchange<P>(ba, t, pk, nex++, &quit, get, put)) break;
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const Cell c{pk[i]};
+        const int y = c.y(), x = xof(c);
+        const bool own = own_of(c);
+        const uint32_t o = (uint32_t)(own ? y * nx + x : 0) * 4u;
+        b1.st(own, lE[i], o, L.oE);
+        b1.st(own, lHx[i], o, L.oHx);
+        b1.st(own, lHz[i], o, L.oHz);
+        const bool gw = SNAP != SNAP_NONE && in_window(c);
+        bga.st(gw, ga[i], o, 0u);
+        bgb.st(gw, gb[i], o, 0u);
+        bandk_mem_store(b1, L, g, y, x, own, mm[i]);
+    }
+}
+
+}  // namespace tmf

@@ -150,13 +150,14 @@ constexpr int HOST_RING = 3;
 enum KernelId {
     KID_FWD_STEP = 0, KID_ADJ_STEP, KID_FWD_STEP2, KID_ADJ_STEP2, KID_FWD_STEP2_UQ, KID_ADJ_STEP2_UQ,
     KID_FWD_STEP_ST, KID_FWD_STEP2_ST, KID_FWD_STEP2_UQ_ST, KID_FWD_SMALL, KID_FWD_SMALL_ST, KID_ADJ_SMALL,
-    KID_FWD_BAND, KID_FWD_BAND_ST, KID_ADJ_BAND, KID_COUNT
+    KID_FWD_BAND, KID_FWD_BAND_ST, KID_ADJ_BAND, KID_FWD_BANDK, KID_FWD_BANDK_ST, KID_ADJ_BANDK, KID_COUNT
 };
 const char* const KERNEL_NAMES[KID_COUNT] = {"k_fwd_step", "k_adj_step", "k_fwd_step2", "k_adj_step2",
                                              "k_fwd_step2_uq", "k_adj_step2_uq", "k_fwd_step_store",
                                              "k_fwd_step2_store", "k_fwd_step2_uq_store", "k_fwd_small",
                                              "k_fwd_small_store", "k_adj_small", "k_fwd_band",
-                                             "k_fwd_band_store", "k_adj_band"};
+                                             "k_fwd_band_store", "k_adj_band", "k_fwd_bandk",
+                                             "k_fwd_bandk_store", "k_adj_bandk"};
 
 struct TimedLaunch {
     int kid;
@@ -176,6 +177,8 @@ struct tm_plan {
     int band = 0;                        // banded resident kernels: 0 never, 1 for small problems with
                                          // few shots (time_block 0), 2 wherever they fit (time_block 4)
     int band_rb = 0, band_n = 0;         // their band height and bands per shot (0: the grid does not fit)
+    int band_kx = 0, band_hd = 0;        // blocked banded kernels: steps per exchange and extended rows
+                                         // per side (0: the kernels exchanging twice per step)
     bool banded = false;                 // the banded kernels run (per device)
     bool band_ran = false;               // a banded launch ran in the current call (its failure word is read)
     int tiling_device = -1;
@@ -250,19 +253,40 @@ bool finite_all(const float* p, int64_t n)
     return true;
 }
 
+// Steps between exchanges of the blocked banded kernels (measured on the
+// order-2 86^2 grid with one shot: 2 and 3 alike, 1 and 4 slower).
+constexpr int BANDK_STEPS = 2;
+
 // Band height and bands per shot of the banded resident kernels (0: they
 // do not apply): as many bands as one workgroup per CU of the device allows
-// (256 CUs; the device check repeats it with the real count), each of at
-// least max(2P, 4) rows, the last of at least P, within the packed cell
-// word and the LDS of a CU.
-void band_plan(tm_plan* p)
+// (256 CUs; the device check repeats it with the real count).  Blocked
+// kernels (kx > 0 steps between exchanges): every band but the last owns
+// at least hd = kx (2P - 1) rows, and the extended rows fit the packed cell
+// word, the threads and the LDS of a CU; where they do not, the kernels
+// exchanging every step, with bands of at least max(2P, 4) rows, the last of
+// at least P, within the packed cell word and the LDS of a CU.
+void band_plan(tm_plan* p, int kx)
 {
-    p->band_rb = p->band_n = 0;
+    p->band_rb = p->band_n = p->band_kx = p->band_hd = 0;
     if (p->band == 0) return;
     const Geo& g = p->g;
     const int64_t S = p->d.n_shots;
     constexpr int64_t WG_MAX = 256;
     if (S > WG_MAX || g.ny >= 2048) return;
+    if (kx > 0) {
+        // blocked: every band but the last owns at least hd rows
+        const int hd = kx * (2 * g.P - 1);
+        for (int64_t nb = std::min<int64_t>(WG_MAX / S, (g.ny + hd - 1) / hd); nb >= 2; --nb) {
+            const int rb = (int)((g.ny + nb - 1) / nb);
+            const int n = (g.ny + rb - 1) / rb;
+            if (!bandk_rows_ok(g, rb, hd) || bandk_lds_bytes(g, rb, hd, true) > 160u * 1024u) continue;
+            p->band_rb = rb;
+            p->band_n = n;
+            p->band_kx = kx;
+            p->band_hd = hd;
+            return;
+        }
+    }
     const int rb_min = std::max(2 * g.P, 4);
     for (int64_t nb = std::min<int64_t>(WG_MAX / S, g.ny / rb_min); nb >= 2; --nb) {
         const int rb = (int)((g.ny + nb - 1) / nb);
@@ -330,7 +354,9 @@ bool make_layout(tm_plan* p)
     L.ev_aout = take(evb);
     if (p->band_n > 0) {
         const uint64_t nw = (uint64_t)d.n_shots * (uint64_t)p->band_n;
-        L.band_x_bytes = nw * 8 * (uint64_t)g.P * (uint64_t)g.nx * 8;   // [kind][parity][side][P][nx] words
+        L.band_x_bytes = p->band_kx > 0
+                             ? nw * 4 * (uint64_t)p->band_hd * (uint64_t)g.nx * BK_NW * 8   // [parity][side][7][hd][nx]
+                             : nw * 8 * (uint64_t)g.P * (uint64_t)g.nx * 8;   // [kind][parity][side][P][nx] words
         L.band_x = take(L.band_x_bytes);
         L.band_err = take(4);
     }
@@ -963,11 +989,27 @@ BandArgs band_args(const tm_plan* p, const Ptrs& q, const SmallArgs& a)
     return b;
 }
 
+// ... of the blocked banded kernels.
+BandKArgs bandk_args(const tm_plan* p, const Ptrs& q, const SmallArgs& a)
+{
+    const BandArgs b = band_args(p, q, a);
+    BandKArgs k{};
+    k.a = a;
+    k.rb = b.rb;
+    k.nband = b.nband;
+    k.hd = p->band_hd;
+    k.kx = p->band_kx;
+    k.xbuf = b.xbuf;
+    k.err = b.err;
+    k.spin_max = b.spin_max;
+    return k;
+}
+
 // Launch a banded kernel cooperatively (all its workgroups resident at
 // once), its exchange rows cleared first (their step tags restart at every
 // launch); the failure word is cleared by the first banded launch of a call
 // and read at the call's end.
-tm_status band_launch(tm_plan* p, const Ptrs& q, const void* fn, BandArgs& b, bool adjoint, int kid, int64_t t,
+tm_status band_launch(tm_plan* p, const Ptrs& q, const void* fn, void* argp, uint32_t lds, int kid, int64_t t,
                       hipStream_t st)
 {
     const int nw = (int)(p->d.n_shots * p->band_n);
@@ -975,8 +1017,7 @@ tm_status band_launch(tm_plan* p, const Ptrs& q, const void* fn, BandArgs& b, bo
     if (v == TM_OK && !p->band_ran) v = zero(reinterpret_cast<float*>(q.band_err), 4, st);
     if (v != TM_OK) return v;
     p->band_ran = true;
-    void* args[] = {&b};
-    const uint32_t lds = band_lds_bytes(p->g, p->band_rb, adjoint);
+    void* args[] = {argp};
     hipError_t e = hipSuccess;
     timed(p, kid, t, st, [&] {
         e = hipLaunchCooperativeKernel(fn, dim3((unsigned)nw), dim3(NTS), args, lds, st);
@@ -1023,12 +1064,22 @@ tm_status fwd_band(tm_plan* p, const Ptrs& q, int cur, int64_t ta, int64_t tb, i
     a.ev_add0 = e0.add;
     a.ev_out0 = e0.out;
     a.ev_row = (uint32_t)L.ev_row;
+    if (p->band_kx > 0) {
+        BandKArgs b = bandk_args(p, q, a);
+        const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_F32>)
+                       : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_BF16>)
+                       : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_FP8>)
+                                             : reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_NONE>);
+        return band_launch(p, q, fn, &b, bandk_lds_bytes(p->g, p->band_rb, p->band_hd, false),
+                           snap == SNAP_NONE ? KID_FWD_BANDK : KID_FWD_BANDK_ST, ta, st);
+    }
     BandArgs b = band_args(p, q, a);
     const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>)
                    : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_BF16>)
                    : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_FP8>)
                                          : reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_NONE>);
-    return band_launch(p, q, fn, b, false, snap == SNAP_NONE ? KID_FWD_BAND : KID_FWD_BAND_ST, ta, st);
+    return band_launch(p, q, fn, &b, band_lds_bytes(p->g, p->band_rb, false),
+                       snap == SNAP_NONE ? KID_FWD_BAND : KID_FWD_BAND_ST, ta, st);
 }
 
 // Adjoint steps tb-1 .. ta of one event block with the banded kernels.
@@ -1058,12 +1109,21 @@ tm_status adj_band(tm_plan* p, const Ptrs& q, int64_t ta, int64_t tb, int64_t k,
     a.ev_row = (uint32_t)L.ev_row;
     a.gca = gca;
     a.gcb = gcb;
+    if (p->band_kx > 0) {
+        BandKArgs b = bandk_args(p, q, a);
+        const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_F32>)
+                       : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_BF16>)
+                       : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_FP8>)
+                                             : reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_NONE>);
+        return band_launch(p, q, fn, &b, bandk_lds_bytes(p->g, p->band_rb, p->band_hd, true), KID_ADJ_BANDK, ta,
+                           st);
+    }
     BandArgs b = band_args(p, q, a);
     const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>)
                    : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_BF16>)
                    : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_FP8>)
                                          : reinterpret_cast<const void*>(&k_adj_band<P, SNAP_NONE>);
-    return band_launch(p, q, fn, b, true, KID_ADJ_BAND, ta, st);
+    return band_launch(p, q, fn, &b, band_lds_bytes(p->g, p->band_rb, true), KID_ADJ_BAND, ta, st);
 }
 
 int snap_kind(const tm_plan* p)
@@ -1179,13 +1239,19 @@ tm_status device_tiling(tm_plan* p)
     // resident at once
     p->banded = false;
     if (p->band_n > 0 && !p->small && (p->band == 2 || (p->band == 1 && stream_small))) {
-        const uint32_t lf = band_lds_bytes(p->g, p->band_rb, false), la = band_lds_bytes(p->g, p->band_rb, true);
+        const bool kb = p->band_kx > 0;
+        const uint32_t lf = kb ? bandk_lds_bytes(p->g, p->band_rb, p->band_hd, false)
+                               : band_lds_bytes(p->g, p->band_rb, false);
+        const uint32_t la = kb ? bandk_lds_bytes(p->g, p->band_rb, p->band_hd, true)
+                               : band_lds_bytes(p->g, p->band_rb, true);
         if (lf <= (uint32_t)lds_max && la <= (uint32_t)lds_max) {
             int of = 0, oa = 0;
-            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &of, reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>), NTS, lf));
-            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &oa, reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>), NTS, la));
+            const void* ff = kb ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_F32>)
+                                : reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>);
+            const void* fa = kb ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_F32>)
+                                : reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>);
+            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&of, ff, NTS, lf));
+            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&oa, fa, NTS, la));
             p->banded = p->d.n_shots * p->band_n <= (int64_t)std::min(of, oa) * ncu;
         }
     }
@@ -1515,7 +1581,7 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     const int P = d.order / 2;
     if (d.n_shots < 1 || d.nt < 1 || d.n_src < 0 || d.n_rec < 0 || d.ckpt_every < 0) return TM_EINVAL;
     if (d.snap != TM_SNAP_F32 && d.snap != TM_SNAP_BF16 && d.snap != TM_SNAP_FP8) return TM_EINVAL;
-    if (d.time_block < 0 || d.time_block > 4) return TM_EINVAL;
+    if (d.time_block < 0 || d.time_block > 5) return TM_EINVAL;
     if (d.storage != TM_STORE_DEVICE && d.storage != TM_STORE_HOST) return TM_EINVAL;
     if (d.step_ratio < 0) return TM_EINVAL;
     if (d.model_per_shot != 0 && d.model_per_shot != 1) return TM_EINVAL;
@@ -1564,8 +1630,14 @@ TM_API tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const in
     if ((v = set_events(p, src, rec)) != TM_OK) { delete p; return v; }
     p->time_block = (d.time_block == 0 || d.time_block >= 3) ? 2 : (int)d.time_block;
     p->resident = d.time_block == 0 ? 1 : d.time_block == 3 ? 2 : 0;
-    p->band = d.time_block == 0 ? 1 : d.time_block == 4 ? 2 : 0;
-    band_plan(p);
+    p->band = d.time_block == 0 ? 1 : (d.time_block == 4 || d.time_block == 5) ? 2 : 0;
+    {
+        // blocked banded kernels: asked for (time_block 5), and by default
+        // at order 2, where the halo of a step is one row
+        int kx = d.time_block == 5 || (d.time_block == 0 && P == 1) ? BANDK_STEPS : 0;
+        if (const char* e = std::getenv("TM_FDTD_BAND_KX")) kx = std::max(0, std::atoi(e));   // tuning, tests
+        band_plan(p, kx);
+    }
     p->R = d.step_ratio > 1 ? d.step_ratio : 1;
     p->n_store = (d.nt + p->R - 1) / p->R;
     p->storage = (int)d.storage;
