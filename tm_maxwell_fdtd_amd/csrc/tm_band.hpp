@@ -591,7 +591,7 @@ __host__ __device__ inline BandKLayout bandk_layout(const Geo& g, int rb, int hd
 
 __host__ __device__ inline uint32_t bandk_lds_bytes(const Geo& g, int rb, int hd, bool adjoint)
 {
-    return 4u * bandk_layout(g, rb, hd, adjoint ? 4 : 3).floats;
+    return 4u * bandk_layout(g, rb, hd, adjoint ? 6 : 3).floats;
 }
 
 __host__ __device__ inline bool bandk_rows_ok(const Geo& g, int rb, int hd)
@@ -853,7 +853,9 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
     }
     evmask = __builtin_amdgcn_readfirstlane(evmask);
 
-    float add[CPTB];
+    // source amplitudes of the cells on event rows: two steps ahead, in two
+    // sets (steps of even and odd offset from t0), each reloaded right
+    // after its step has used it
     auto load_add = [&](int tt, float (&dst)[CPTB]) {
         const bool in_run = tt < a.t1;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
@@ -864,7 +866,9 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
             dst[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
         }
     };
-    load_add(a.t0, add);
+    float add0[CPTB], add1[CPTB];
+    load_add(a.t0, add0);
+    load_add(a.t0 + 1, add1);
     auto get = [&](int i, int k) -> float {
         const int j = Cell{pk[i]}.j();
         return k == 0 ? sE[j] : k == 1 ? sHx[j] : k == 2 ? sHz[j] : k == 3 ? mm[i].yh : k == 4 ? mm[i].xh
@@ -882,10 +886,8 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
     };
 
     int nex = 0;
-    for (int tt = a.t0; tt < a.t1; ++tt) {
-        float add_n[CPTB];
-        load_add(tt + 1, add_n);
-
+    // one step; false when the launch has failed
+    auto step = [&](int tt, float (&add)[CPTB]) -> bool {
         // ---- H half-step on every extended row
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
@@ -909,6 +911,8 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
+        const bool next_in = tt + 2 < a.t1;
+        const uint32_t next_off = a.ev_add0 + (uint32_t)(next_in ? tt + 2 - a.t0 : 0) * a.ev_row;
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
             if (!live(i)) continue;
@@ -928,16 +932,19 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
             }
             float en = fmaf(ca[i], ev, cb[i] * curl);
             en = evo[i] != RBuf::OOB ? en + add[i] : en;
-            if ((evmask >> i) & 1) bev.stv(en, own ? evo[i] : RBuf::OOB, out_off);
+            if ((evmask >> i) & 1) {
+                bev.stv(en, own ? evo[i] : RBuf::OOB, out_off);
+                add[i] = bev.ldv(next_in ? evo[i] : RBuf::OOB, next_off);   // step tt + 2
+            }
             sE[j] = c.bit(CB_E) ? en : ev;
         }
-        if (tt + 1 < a.t1 && (tt + 1 - a.t0) % ba.kx == 0) {
-            if (!bandk_exchange<P>(ba, t, pk, nex++, &quit, get, put)) break;
-        } else {
-            __syncthreads();
-        }
-#pragma unroll
-        for (int i = 0; i < CPTB; ++i) add[i] = add_n[i];
+        if (tt + 1 < a.t1 && (tt + 1 - a.t0) % ba.kx == 0) return bandk_exchange<P>(ba, t, pk, nex++, &quit, get, put);
+        __syncthreads();
+        return true;
+    };
+    for (int tt = a.t0; tt < a.t1; tt += 2) {
+        if (!step(tt, add0)) break;
+        if (tt + 1 < a.t1 && !step(tt + 1, add1)) break;
     }
 
     // own rows back
@@ -967,11 +974,13 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const int s = t.s, tid = threadIdx.x;
     const int ny = g.ny, nx = g.nx;
     const int rows = ba.rb + 2 * ba.hd;
-    const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 4);
+    const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 6);
     float* const sU = lds + bl.pad;
     float* const sW = sU + bl.stride;
     float* const sTZ = sW + bl.stride;
     float* const sTX = sTZ + bl.stride;
+    float* const sGA = sTX + bl.stride;          // per-shot gradients of the own window cells
+    float* const sGB = sGA + bl.stride;
     const float* const ty = lds + bl.ty;
     const float* const tx = lds + bl.tx;
     const int* const slot = reinterpret_cast<const int*>(lds + bl.slot);
@@ -984,7 +993,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
     const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
 
-    for (int i = tid; i < 4 * (int)bl.stride; i += NTS) lds[i] = 0.0f;
+    for (int i = tid; i < 6 * (int)bl.stride; i += NTS) lds[i] = 0.0f;
     bandk_tables(lds, bl, g, a.cp, a.ev, s);
     if (tid == 0) quit = 0;
 
@@ -1000,7 +1009,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = (t.eb - t.ea) * nx;
     auto live = [&](int i) { return i * NTS + wbase < ncel; };
     int pk[CPTB];
-    float ca[CPTB], cb[CPTB], cq[CPTB], lE[CPTB], lHx[CPTB], lHz[CPTB], ga[CPTB], gb[CPTB];
+    float ca[CPTB], cb[CPTB], cq[CPTB], lE[CPTB], lHx[CPTB], lHz[CPTB], ga[CPTB], gb[CPTB];   // (ga, gb: loads only)
     CellMem mm[CPTB];
 #pragma unroll
     for (int i = 0; i < CPTB; ++i) {
@@ -1021,17 +1030,6 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         mm[i] = bandk_mem_load(b0, L, g, c.y(), xof(c), ok);
     }
 
-    __syncthreads();
-    int evo[CPTB], evmask = 0;
-#pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
-        const Cell c{pk[i]};
-        const int gs = slot[c.y()];
-        evo[i] = c.bit(CB_E) && gs >= 0 ? (gs * nx + xof(c)) * 4 : RBuf::OOB;
-        if (__builtin_amdgcn_ballot_w64(evo[i] != RBuf::OOB) != 0) evmask |= 1 << i;
-    }
-    evmask = __builtin_amdgcn_readfirstlane(evmask);
-
     float add[CPTB], se[CPTB], sc[CPTB];
     auto load_step = [&](int tt) {
         const bool in_run = tt >= a.t0;
@@ -1045,8 +1043,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             add[i] = se[i] = sc[i] = 0.0f;
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
-            const int y = c.y(), x = xof(c);
-            if ((evmask >> i) & 1) add[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
+            const int y = c.y(), x = xof(c), gs = slot[y];
+            add[i] = bev.ld(in_run && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + x) * 4u, off);
             const SnapPair sp = snap_get2<SNAP>(bsp, stored && in_window(c),
                                                 (uint32_t)((y - g.y0) * g.nxi + (x - g.x0)));
             se[i] = sp.e;
@@ -1067,6 +1065,14 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         else mm[i].xe = v;
     };
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const int j = Cell{pk[i]}.j();
+        if (SNAP != SNAP_NONE && in_window(Cell{pk[i]})) {
+            sGA[j] = ga[i];
+            sGB[j] = gb[i];
+        }
+    }
     load_step(a.t1 - 1);
 
     int nex = 0;
@@ -1081,13 +1087,16 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             const Cell c = cell(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
             const bool on = c.bit(CB_E);
-            const float e = evo[i] != RBuf::OOB ? lE[i] + add[i] : lE[i];
-            if ((evmask >> i) & 1) bev.stv(e, own_of(c) ? evo[i] : RBuf::OOB, out_off);
+            const int gs = slot[y];
+            const bool evr = on && gs >= 0;
+            const float e = evr ? lE[i] + add[i] : lE[i];
+            bev.st(evr && own_of(c), e, (uint32_t)(gs * nx + x) * 4u, out_off);
             if (SNAP != SNAP_NONE && stored) {
                 const bool in_w = in_window(c);
-                const float na = fmaf(e, se[i] * a.ratio, ga[i]), nb = fmaf(e, sc[i] * a.ratio, gb[i]);
-                ga[i] = in_w ? na : ga[i];
-                gb[i] = in_w ? nb : gb[i];
+                if (in_w) {
+                    sGA[j] = fmaf(e, se[i] * a.ratio, sGA[j]);
+                    sGB[j] = fmaf(e, sc[i] * a.ratio, sGB[j]);
+                }
             }
             const float hv = cb[i] * e;
             const float u = rsite(c.bit(CB_FEX), mm[i].xe, tx + 3 * nx + x, nx, hv);
@@ -1148,8 +1157,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         b1.st(own, lHx[i], o, L.oHx);
         b1.st(own, lHz[i], o, L.oHz);
         const bool gw = SNAP != SNAP_NONE && in_window(c);
-        bga.st(gw, ga[i], o, 0u);
-        bgb.st(gw, gb[i], o, 0u);
+        bga.st(gw, sGA[c.j()], o, 0u);
+        bgb.st(gw, sGB[c.j()], o, 0u);
         bandk_mem_store(b1, L, g, y, x, own, mm[i]);
     }
 }
