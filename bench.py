@@ -252,7 +252,7 @@ def main():
     ap.add_argument("--nt", type=int, default=0,
                     help="override the number of time steps (profiling runs only; "
                          "the bench line then names the reduced workload)")
-    ap.add_argument("--time-block", type=int, default=0, choices=(0, 1, 2, 3, 4),
+    ap.add_argument("--time-block", type=int, default=0, choices=(0, 1, 2, 3, 4, 5),
                     help="time steps per launch of the forward and the adjoint (0: the default, 2)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "

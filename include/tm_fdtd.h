@@ -210,10 +210,11 @@ tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb
  * tm_courant without a workspace, for callers that cannot allocate device
  * memory (code under stream capture, tight serving loops, harnesses that
  * forbid allocation) or that check a model before allocating the workspace.
- * Same result as tm_courant (bitwise; same kernels).  Its scratch (258
- * floats: 256 partial maxima and two words of the uniform-Cq test) is a
- * static device array of the library, one per device, held until the
- * process ends; the scratch size does not depend on the model size, so no
+ * Same result as tm_courant (bitwise; same kernel).  Its scratch (513
+ * floats: 256 per-block maxima, 256 per-block flags of the uniform-Cq test
+ * and cq[0]) is a static device array of the library, one per device, held
+ * until the process ends; the scratch size does not depend on the model
+ * size, so no
  * size is refused for it.  Allocates nothing (no hipMalloc / hipFree),
  * synchronises ``stream``.  Calls that overlap on one device share the
  * array and race: serialise them.  TM_EINVAL for a NULL argument or a

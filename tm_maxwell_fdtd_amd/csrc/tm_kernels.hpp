@@ -124,33 +124,29 @@ __global__ __launch_bounds__(256) void k_zero(float* __restrict__ p, int64_t n)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
-// Whether q[0, n) holds one value: info[0] must be 0 on entry and becomes
-// nonzero if the bits of any value differ from those of q[0]; info[1] gets
-// q[0]'s bits.  Every lane that finds a difference stores the same word.
-__global__ __launch_bounds__(256) void k_cq_uniform(const float* __restrict__ q, int64_t n,
-                                                    uint32_t* __restrict__ info)
-{
-    const uint32_t ref = __float_as_uint(q[0]);
-    bool diff = false;
-    const int64_t step = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step)
-        diff |= __float_as_uint(q[i]) != ref;
-    if (diff) info[0] = 1u;
-    if (blockIdx.x == 0 && threadIdx.x == 0) info[1] = ref;
-}
-
-// Max of cb*cq over [0, n): per-block maxima into part[blockIdx.x].
-__global__ __launch_bounds__(256) void k_max_cbcq(const float* __restrict__ cb,
-                                                  const float* __restrict__ cq, int64_t n,
-                                                  float* __restrict__ part)
+// The scan of the Courant check over [0, n), one pass: block b writes the
+// largest cb*cq it saw into part[b] (a NaN wins), and into part[nb + b]
+// 1.0f if any cq value it saw differs in its bits from q[0], else 0.0f;
+// block 0 also writes q[0]'s bits into part[2 nb].
+__global__ __launch_bounds__(256) void k_courant_scan(const float* __restrict__ cb,
+                                                      const float* __restrict__ cq, int64_t n,
+                                                      float* __restrict__ part)
 {
     __shared__ float red[256];
+    __shared__ int diff_any;
+    if (threadIdx.x == 0) diff_any = 0;
+    __syncthreads();
+    const uint32_t ref = __float_as_uint(cq[0]);
     float m = 0.0f;
+    bool diff = false;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const float v = cb[i] * cq[i];
+        const float q = cq[i];
+        const float v = cb[i] * q;
         m = (v > m || v != v) ? v : m;     // NaN propagates
+        diff |= __float_as_uint(q) != ref;
     }
+    if (diff) diff_any = 1;                // every writer stores the same value
     red[threadIdx.x] = m;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -160,7 +156,35 @@ __global__ __launch_bounds__(256) void k_max_cbcq(const float* __restrict__ cb,
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+    if (threadIdx.x == 0) {
+        part[blockIdx.x] = red[0];
+        part[gridDim.x + blockIdx.x] = diff_any ? 1.0f : 0.0f;
+        if (blockIdx.x == 0) part[2 * gridDim.x] = __uint_as_float(ref);
+    }
+}
+
+// Up to FILL_JOBS copies and zero fills in one launch: job j (blockIdx.y)
+// copies n[j] floats from src[j] to dst[j], or writes n[j] zeros where
+// src[j] is null.
+constexpr int FILL_JOBS = 8;
+struct FillJobs {
+    float* dst[FILL_JOBS];
+    const float* src[FILL_JOBS];
+    int64_t n[FILL_JOBS];
+};
+
+__global__ __launch_bounds__(256) void k_fill(FillJobs jobs)
+{
+    const int j = blockIdx.y;
+    float* __restrict__ d = jobs.dst[j];
+    const float* __restrict__ s = jobs.src[j];
+    const int64_t n = jobs.n[j];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if (s != nullptr) {
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) d[i] = s[i];
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) d[i] = 0.0f;
+    }
 }
 
 }  // namespace tmf

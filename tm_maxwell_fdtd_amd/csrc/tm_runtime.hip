@@ -591,6 +591,44 @@ void timed(tm_plan* p, int kid, int64_t t, hipStream_t st, F&& body)
     p->ev_used.push_back(TimedLaunch{kid, a, b});
 }
 
+// Copies and zero fills gathered into k_fill launches (one per FILL_JOBS
+// jobs), so that the small set-up work of a call costs one launch.
+struct Fills {
+    FillJobs j{};
+    int count = 0;
+    int64_t maxn = 0;
+    tm_status launch(hipStream_t st)
+    {
+        if (count == 0) return TM_OK;
+        for (int k = count; k < FILL_JOBS; ++k) {
+            j.dst[k] = nullptr;
+            j.src[k] = nullptr;
+            j.n[k] = 0;
+        }
+        const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((maxn + 255) / 256, 8192));
+        k_fill<<<dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, st>>>(j);
+        count = 0;
+        maxn = 0;
+        return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
+    }
+    // copy `bytes` from src (or zeros where src is null) to dst
+    tm_status add(float* dst, const float* src, uint64_t bytes, hipStream_t st)
+    {
+        const int64_t n = (int64_t)(bytes / 4);
+        if (n == 0) return TM_OK;
+        if (count == FILL_JOBS) {
+            const tm_status v = launch(st);
+            if (v != TM_OK) return v;
+        }
+        j.dst[count] = dst;
+        j.src[count] = src;
+        j.n[count] = n;
+        ++count;
+        maxn = std::max(maxn, n);
+        return TM_OK;
+    }
+};
+
 tm_status zero(float* ptr, uint64_t bytes, hipStream_t st)
 {
     const int64_t n = (int64_t)(bytes / 4);
@@ -602,29 +640,32 @@ tm_status zero(float* ptr, uint64_t bytes, hipStream_t st)
 
 tm_status upload_tables(tm_plan* p, void* ws, hipStream_t st)
 {
+    // the staging buffer mirrors the workspace from the CPML table to the
+    // end of the event tables (which follow it), so one copy moves both
     const uint64_t cb = p->cpml.size() * 4, tb = p->tables.size() * 4;
+    const uint64_t to = p->lay.tables - p->lay.cpml;
     if (p->pinned == nullptr) {
-        p->pinned_bytes = cb + tb;
+        p->pinned_bytes = to + tb;
         HIPCHK(hipHostMalloc(&p->pinned, p->pinned_bytes, hipHostMallocDefault));
+        std::memset(p->pinned, 0, p->pinned_bytes);
         std::memcpy(p->pinned, p->cpml.data(), cb);
-        if (tb) std::memcpy(static_cast<char*>(p->pinned) + cb, p->tables.data(), tb);
+        if (tb) std::memcpy(static_cast<char*>(p->pinned) + to, p->tables.data(), tb);
     }
-    HIPCHK(hipMemcpyAsync(wsp<char>(ws, p->lay.cpml), p->pinned, cb, hipMemcpyHostToDevice, st));
-    if (tb)
-        HIPCHK(hipMemcpyAsync(wsp<char>(ws, p->lay.tables), static_cast<char*>(p->pinned) + cb, tb,
-                              hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(wsp<char>(ws, p->lay.cpml), p->pinned, p->pinned_bytes, hipMemcpyHostToDevice, st));
     return TM_OK;
 }
 
 // Copy the caller's model arrays into the workspace's model block.
-tm_status stage_model(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq, hipStream_t st)
+tm_status stage_model(tm_plan* p, void* ws, const float* ca, const float* cb, const float* cq, hipStream_t st,
+                      Fills& fills)
 {
     const uint64_t n = (uint64_t)p->g.slab * 4;
     char* m = wsp<char>(ws, p->lay.model);
     if (p->lay.model_stride == 0) {
-        HIPCHK(hipMemcpyAsync(m, ca, n, hipMemcpyDeviceToDevice, st));
-        HIPCHK(hipMemcpyAsync(m + p->lay.slab_b, cb, n, hipMemcpyDeviceToDevice, st));
-        HIPCHK(hipMemcpyAsync(m + 2 * p->lay.slab_b, cq, n, hipMemcpyDeviceToDevice, st));
+        tm_status v = fills.add(reinterpret_cast<float*>(m), ca, n, st);
+        if (v == TM_OK) v = fills.add(reinterpret_cast<float*>(m + p->lay.slab_b), cb, n, st);
+        if (v == TM_OK) v = fills.add(reinterpret_cast<float*>(m + 2 * p->lay.slab_b), cq, n, st);
+        return v;
     } else {                        // [S][ny][nx] each -> S blocks [Ca | Cb | Cq]
         const size_t S = (size_t)p->d.n_shots, pitch = (size_t)p->lay.model_stride;
         HIPCHK(hipMemcpy2DAsync(m, pitch, ca, n, n, S, hipMemcpyDeviceToDevice, st));
@@ -1013,8 +1054,10 @@ tm_status band_launch(tm_plan* p, const Ptrs& q, const void* fn, void* argp, uin
                       hipStream_t st)
 {
     const int nw = (int)(p->d.n_shots * p->band_n);
-    tm_status v = zero(reinterpret_cast<float*>(q.band_x), p->lay.band_x_bytes, st);
-    if (v == TM_OK && !p->band_ran) v = zero(reinterpret_cast<float*>(q.band_err), 4, st);
+    Fills fills;
+    tm_status v = fills.add(reinterpret_cast<float*>(q.band_x), nullptr, p->lay.band_x_bytes, st);
+    if (v == TM_OK && !p->band_ran) v = fills.add(reinterpret_cast<float*>(q.band_err), nullptr, 4, st);
+    if (v == TM_OK) v = fills.launch(st);
     if (v != TM_OK) return v;
     p->band_ran = true;
     void* args[] = {argp};
@@ -1512,10 +1555,11 @@ tm_status set_events(tm_plan* p, const int64_t* src, const int64_t* rec)
     return TM_OK;
 }
 
-// Partial maxima of the Courant reduction, plus two words of the uniform-Cq
-// test: the device scratch the check uses (COURANT_WORDS floats).
+// Per-block maxima of the Courant reduction and per-block flags of the
+// uniform-Cq test, then cq[0]: the device scratch the check uses
+// (COURANT_WORDS floats).
 constexpr int COURANT_NB = 256;
-constexpr int COURANT_WORDS = COURANT_NB + 2;
+constexpr int COURANT_WORDS = 2 * COURANT_NB + 1;
 static_assert(COURANT_WORDS * sizeof(float) <= SCRATCH_BYTES, "Courant scratch exceeds the workspace's area");
 
 // scratch: COURANT_WORDS floats of device memory (the workspace's scratch
@@ -1525,26 +1569,21 @@ tm_status courant_impl(tm_plan* p, float* scratch, const float* cb, const float*
 {
     constexpr int NB = COURANT_NB;
     const int64_t n = p->g.slab * (p->d.model_per_shot ? p->d.n_shots : 1);   // every shot's model
-    k_max_cbcq<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, n, scratch);
-    HIPCHK(hipGetLastError());
-    // whether Cq holds one value (two words after the NB partial maxima)
-    uint32_t* info = reinterpret_cast<uint32_t*>(scratch + NB);
-    k_zero<<<dim3(1), dim3(64), 0, st>>>(scratch + NB, 2);
-    HIPCHK(hipGetLastError());
-    k_cq_uniform<<<dim3(NB), dim3(256), 0, st>>>(cq, n, info);
+    // per block: the largest cb*cq, whether Cq differs from cq[0]; cq[0]
+    k_courant_scan<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, n, scratch);
     HIPCHK(hipGetLastError());
     float part[COURANT_WORDS];
     HIPCHK(hipMemcpyAsync(part, scratch, sizeof(part), hipMemcpyDeviceToHost, st));
     HIPCHK(hipStreamSynchronize(st));
     double m = 0.0;
+    bool one = true;
     for (int i = 0; i < NB; ++i) {
-        if (part[i] != part[i]) { m = NAN; break; }
-        m = std::max(m, (double)part[i]);
+        if (part[i] != part[i]) m = NAN;
+        else if (m == m) m = std::max(m, (double)part[i]);
+        one = one && part[NB + i] == 0.0f;
     }
-    uint32_t w[2];
-    std::memcpy(w, part + NB, sizeof(w));
-    if (cq_one != nullptr) *cq_one = w[0] == 0u;
-    if (cq_val != nullptr) std::memcpy(cq_val, &w[1], sizeof(float));
+    if (cq_one != nullptr) *cq_one = one;
+    if (cq_val != nullptr) std::memcpy(cq_val, &part[2 * NB], sizeof(float));
     const double rdx = 1.0 / p->d.dx, rdy = 1.0 / p->d.dy;
     *out = std::sqrt(m) * abs_coef_sum(p->d.order) * std::sqrt(rdx * rdx + rdy * rdy);
     return TM_OK;
@@ -1860,11 +1899,12 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
         if (!(c <= 1.0)) return TM_EUNSTABLE;
     }
     if ((v = upload_tables(p, ws, st)) != TM_OK) return v;
-    if ((v = stage_model(p, ws, ca, cb, cq, st)) != TM_OK) return v;
+    Fills fills;
+    if ((v = stage_model(p, ws, ca, cb, cq, st, fills)) != TM_OK) return v;
+    if (t0 == 0 && (v = fills.add(wsp<float>(ws, p->lay.fwd), nullptr, p->lay.fwd_bytes, st)) != TM_OK) return v;
+    if ((v = fills.launch(st)) != TM_OK) return v;
     if (t0 == 0) {
         p->fwd_complete = false;
-        v = zero(wsp<float>(ws, p->lay.fwd), p->lay.fwd_bytes, st);
-        if (v != TM_OK) return v;
         p->fwd_cur = 0;
         p->stored_ok = store;
     } else {
@@ -1911,12 +1951,13 @@ TM_API tm_status tm_adjoint(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     }
     hipStream_t st = as_stream(stream);
     if ((v = upload_tables(p, ws, st)) != TM_OK) return v;
-    if ((v = stage_model(p, ws, ca, cb, cq, st)) != TM_OK) return v;
-    v = zero(wsp<float>(ws, p->lay.adj), p->lay.adj_bytes, st);
-    if (v != TM_OK) return v;
+    Fills fills;
+    if ((v = stage_model(p, ws, ca, cb, cq, st, fills)) != TM_OK) return v;
+    if ((v = fills.add(wsp<float>(ws, p->lay.adj), nullptr, p->lay.adj_bytes, st)) != TM_OK) return v;
     const uint64_t gbytes = (uint64_t)p->d.n_shots * (uint64_t)p->g.slab * 4;
-    if (grad_ca_shot && (v = zero(grad_ca_shot, gbytes, st)) != TM_OK) return v;
-    if (grad_cb_shot && (v = zero(grad_cb_shot, gbytes, st)) != TM_OK) return v;
+    if (grad_ca_shot && (v = fills.add(grad_ca_shot, nullptr, gbytes, st)) != TM_OK) return v;
+    if (grad_cb_shot && (v = fills.add(grad_cb_shot, nullptr, gbytes, st)) != TM_OK) return v;
+    if ((v = fills.launch(st)) != TM_OK) return v;
     // the adjoint steps and the checkpoint replays take the arrays of the
     // storing forward: its check's finding holds for them
     p->cq_uniform = p->fwd_cq_one && cq == p->fwd_cq;
