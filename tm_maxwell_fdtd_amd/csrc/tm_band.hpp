@@ -560,6 +560,7 @@ namespace tmf {
 // ---------------------------------------------------------------------------
 
 constexpr int BK_NW = 7;                    // exchanged words per cell
+constexpr int CPTK = 2;                     // cells per thread (a band's extended rows: at most 2048 cells)
 
 struct BandKArgs {
     SmallArgs a;
@@ -591,13 +592,13 @@ __host__ __device__ inline BandKLayout bandk_layout(const Geo& g, int rb, int hd
 
 __host__ __device__ inline uint32_t bandk_lds_bytes(const Geo& g, int rb, int hd, bool adjoint)
 {
-    return 4u * bandk_layout(g, rb, hd, adjoint ? 6 : 3).floats;
+    return 4u * bandk_layout(g, rb, hd, adjoint ? 4 : 3).floats;
 }
 
 __host__ __device__ inline bool bandk_rows_ok(const Geo& g, int rb, int hd)
 {
     return rb >= hd && hd >= 2 * g.P - 1 && (rb + 2 * hd + g.P) * g.nx + g.P < (1 << 14) &&
-           (rb + 2 * hd) * g.nx <= NTS * CPTB && g.ny < 2048;
+           (rb + 2 * hd) * g.nx <= NTS * CPTK && g.ny < 2048;
 }
 
 struct BandK {
@@ -704,22 +705,20 @@ __device__ __forceinline__ float rsite(bool on, float& m, const float* tab, int 
     return d;
 }
 
-// Exchange number n: publish the words of the cells on the first and last
-// hd own rows (w[0..6] of each cell, read by get(i, k)), then replace the
-// words of the cells on the extended rows outside the band with the
-// neighbours' (put(i, k, v)).  Returns false (in every thread) when the
-// launch has failed.
-template <int P, typename Get, typename Put>
-__device__ __forceinline__ bool bandk_exchange(const BandKArgs& ba, const BandK& t, const int (&pk)[CPTB], int n,
-                                               int* quit, Get get, Put put)
+// Exchange number n, in two halves that need no barrier of their own.
+// Publish: the words of the cells on the first and last hd own rows (w[0..6]
+// of each cell, read by get(i, k); each thread publishes its own cells,
+// whose values it wrote itself).
+template <int P, typename Get>
+__device__ __forceinline__ void bandk_publish(const BandKArgs& ba, const BandK& t, const int (&pk)[CPTK], int n,
+                                              Get get)
 {
     const int nx = ba.a.g.nx, hd = ba.hd;
     const size_t plane = (size_t)hd * nx, side_w = plane * BK_NW;   // one word of every cell of a side
     const uint64_t tag = (uint64_t)(uint32_t)(n + 1) << 32;
-    __syncthreads();                                          // the step's LDS writes are done
     uint64_t* ob = ba.xbuf + (size_t)((t.w * 2 + (n & 1)) * 2) * side_w;
 #pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
+    for (int i = 0; i < CPTK; ++i) {
         const Cell c = cell(pk[i]);
         const int y = c.y(), x = c.j() - (y - t.y_arr) * nx;
         const bool valid = c.j() < (t.eb - t.y_arr) * nx && y >= t.ya && y < t.yb;
@@ -739,9 +738,21 @@ __device__ __forceinline__ bool bandk_exchange(const BandKArgs& ba, const BandK&
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// Poll: wait for the neighbours' words of exchange n for the cells on the
+// extended rows outside the band and hand them to put(i, k, v).  Returns
+// false when this thread's wait failed or the launch has failed (err is
+// then set); the caller tells the other threads at its next barrier.
+template <int P, typename Put>
+__device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, const int (&pk)[CPTK], int n, Put put)
+{
+    const int nx = ba.a.g.nx, hd = ba.hd;
+    const size_t plane = (size_t)hd * nx, side_w = plane * BK_NW;
+    const uint64_t tag = (uint64_t)(uint32_t)(n + 1) << 32;
     bool bad = ba.spin_max <= 0;                              // (a host-forced failure, for tests)
 #pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
+    for (int i = 0; i < CPTK; ++i) {
         const Cell c = cell(pk[i]);
         const int y = c.y(), x = c.j() - (y - t.y_arr) * nx;
         const bool valid = c.j() < (t.eb - t.y_arr) * nx;
@@ -773,12 +784,8 @@ __device__ __forceinline__ bool bandk_exchange(const BandKArgs& ba, const BandK&
 #pragma unroll
         for (int k = 0; k < BK_NW; ++k) put(i, k, __uint_as_float((uint32_t)w[k]));
     }
-    if (bad) {
-        __hip_atomic_store(ba.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *quit = 1;
-    }
-    __syncthreads();
-    return *quit == 0;
+    if (bad) __hip_atomic_store(ba.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return !bad;
 }
 
 // Forward, blocked: steps t0 .. t1-1, workgroup = (shot, band).
@@ -824,11 +831,11 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
     // iteration i of the cell loops has work in this wave
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = (t.eb - t.ea) * nx;
     auto live = [&](int i) { return i * NTS + wbase < ncel; };
-    int pk[CPTB];
-    float ca[CPTB], cb[CPTB], cq[CPTB];
-    CellMem mm[CPTB];
+    int pk[CPTK];
+    float ca[CPTK], cb[CPTK], cq[CPTK];
+    CellMem mm[CPTK];
 #pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
+    for (int i = 0; i < CPTK; ++i) {
         const int je = tid + i * NTS;
         const bool ok = je < (t.eb - t.ea) * nx;
         pk[i] = pack_bandk_cell<P>(je, t, rows, g);
@@ -843,9 +850,9 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     // event-row offsets of the cells (RBuf::OOB off the event rows), and
     // the iterations in which this wave has any
-    int evo[CPTB], evmask = 0;
+    int evo[CPTK], evmask = 0;
 #pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
+    for (int i = 0; i < CPTK; ++i) {
         const Cell c{pk[i]};
         const int gs = slot[c.y()];
         evo[i] = c.bit(CB_E) && gs >= 0 ? (gs * nx + xof(c)) * 4 : RBuf::OOB;
@@ -856,17 +863,17 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
     // source amplitudes of the cells on event rows: two steps ahead, in two
     // sets (steps of even and odd offset from t0), each reloaded right
     // after its step has used it
-    auto load_add = [&](int tt, float (&dst)[CPTB]) {
+    auto load_add = [&](int tt, float (&dst)[CPTK]) {
         const bool in_run = tt < a.t1;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
 #pragma unroll
-        for (int i = 0; i < CPTB; ++i) {
+        for (int i = 0; i < CPTK; ++i) {
             dst[i] = 0.0f;
             if (((evmask >> i) & 1) == 0) continue;
             dst[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
         }
     };
-    float add0[CPTB], add1[CPTB];
+    float add0[CPTK], add1[CPTK];
     load_add(a.t0, add0);
     load_add(a.t0 + 1, add1);
     auto get = [&](int i, int k) -> float {
@@ -887,10 +894,10 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     int nex = 0;
     // one step; false when the launch has failed
-    auto step = [&](int tt, float (&add)[CPTB]) -> bool {
+    auto step = [&](int tt, float (&add)[CPTK]) -> bool {
         // ---- H half-step on every extended row
 #pragma unroll
-        for (int i = 0; i < CPTB; ++i) {
+        for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j(), x = xof(c);
@@ -914,7 +921,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
         const bool next_in = tt + 2 < a.t1;
         const uint32_t next_off = a.ev_add0 + (uint32_t)(next_in ? tt + 2 - a.t0 : 0) * a.ev_row;
 #pragma unroll
-        for (int i = 0; i < CPTB; ++i) {
+        for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
@@ -938,9 +945,21 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
             }
             sE[j] = c.bit(CB_E) ? en : ev;
         }
-        if (tt + 1 < a.t1 && (tt + 1 - a.t0) % ba.kx == 0) return bandk_exchange<P>(ba, t, pk, nex++, &quit, get, put);
+        if (tt + 1 < a.t1 && (tt + 1 - a.t0) % ba.kx == 0) {
+            // Own cells' values are final (each thread wrote its own), so
+            // publish and poll at once.  The neighbours' fields go straight
+            // into the outer rows while other threads may still run this
+            // step's E update: of the rows written, that update reads only
+            // Hx on the P rows next to the band (for own cells), whose values
+            // here are already exact, so the stores do not change them; the
+            // other reads are for outer-row cells, whose results the
+            // exchange replaces.  The next reads follow the barrier below.
+            bandk_publish<P>(ba, t, pk, nex, get);
+            if (!bandk_poll<P>(ba, t, pk, nex, put)) quit = 1;
+            ++nex;
+        }
         __syncthreads();
-        return true;
+        return quit == 0;
     };
     for (int tt = a.t0; tt < a.t1; tt += 2) {
         if (!step(tt, add0)) break;
@@ -949,7 +968,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     // own rows back
 #pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
+    for (int i = 0; i < CPTK; ++i) {
         const Cell c{pk[i]};
         const int y = c.y(), x = xof(c);
         const bool own = c.j() < (t.eb - t.y_arr) * nx && y >= t.ya && y < t.yb;
@@ -974,13 +993,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const int s = t.s, tid = threadIdx.x;
     const int ny = g.ny, nx = g.nx;
     const int rows = ba.rb + 2 * ba.hd;
-    const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 6);
+    const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 4);
     float* const sU = lds + bl.pad;
     float* const sW = sU + bl.stride;
     float* const sTZ = sW + bl.stride;
     float* const sTX = sTZ + bl.stride;
-    float* const sGA = sTX + bl.stride;          // per-shot gradients of the own window cells
-    float* const sGB = sGA + bl.stride;
     const float* const ty = lds + bl.ty;
     const float* const tx = lds + bl.tx;
     const int* const slot = reinterpret_cast<const int*>(lds + bl.slot);
@@ -993,7 +1010,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
     const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
 
-    for (int i = tid; i < 6 * (int)bl.stride; i += NTS) lds[i] = 0.0f;
+    for (int i = tid; i < 4 * (int)bl.stride; i += NTS) lds[i] = 0.0f;
     bandk_tables(lds, bl, g, a.cp, a.ev, s);
     if (tid == 0) quit = 0;
 
@@ -1008,11 +1025,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     };
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = (t.eb - t.ea) * nx;
     auto live = [&](int i) { return i * NTS + wbase < ncel; };
-    int pk[CPTB];
-    float ca[CPTB], cb[CPTB], cq[CPTB], lE[CPTB], lHx[CPTB], lHz[CPTB], ga[CPTB], gb[CPTB];   // (ga, gb: loads only)
-    CellMem mm[CPTB];
+    int pk[CPTK];
+    float ca[CPTK], cb[CPTK], cq[CPTK], lE[CPTK], lHx[CPTK], lHz[CPTK], ga[CPTK], gb[CPTK];
+    CellMem mm[CPTK];
 #pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
+    for (int i = 0; i < CPTK; ++i) {
         const int je = tid + i * NTS;
         const bool ok = je < (t.eb - t.ea) * nx;
         pk[i] = pack_bandk_cell<P>(je, t, rows, g);
@@ -1030,7 +1047,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         mm[i] = bandk_mem_load(b0, L, g, c.y(), xof(c), ok);
     }
 
-    float add[CPTB], se[CPTB], sc[CPTB];
+    float add[CPTK], se[CPTK], sc[CPTK];
     auto load_step = [&](int tt) {
         const bool in_run = tt >= a.t0;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
@@ -1039,7 +1056,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
 #pragma unroll
-        for (int i = 0; i < CPTB; ++i) {
+        for (int i = 0; i < CPTK; ++i) {
             add[i] = se[i] = sc[i] = 0.0f;
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
@@ -1065,14 +1082,6 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         else mm[i].xe = v;
     };
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
-        const int j = Cell{pk[i]}.j();
-        if (SNAP != SNAP_NONE && in_window(Cell{pk[i]})) {
-            sGA[j] = ga[i];
-            sGB[j] = gb[i];
-        }
-    }
     load_step(a.t1 - 1);
 
     int nex = 0;
@@ -1082,7 +1091,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 
         // ---- phase 1 on every extended row: residual, gradient (own), Cb, E-update filters
 #pragma unroll
-        for (int i = 0; i < CPTB; ++i) {
+        for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
@@ -1093,10 +1102,9 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             bev.st(evr && own_of(c), e, (uint32_t)(gs * nx + x) * 4u, out_off);
             if (SNAP != SNAP_NONE && stored) {
                 const bool in_w = in_window(c);
-                if (in_w) {
-                    sGA[j] = fmaf(e, se[i] * a.ratio, sGA[j]);
-                    sGB[j] = fmaf(e, sc[i] * a.ratio, sGB[j]);
-                }
+                const float na = fmaf(e, se[i] * a.ratio, ga[i]), nb = fmaf(e, sc[i] * a.ratio, gb[i]);
+                ga[i] = in_w ? na : ga[i];
+                gb[i] = in_w ? nb : gb[i];
             }
             const float hv = cb[i] * e;
             const float u = rsite(c.bit(CB_FEX), mm[i].xe, tx + 3 * nx + x, nx, hv);
@@ -1107,10 +1115,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         }
         load_step(tt - 1);
         __syncthreads();
+        if (quit) break;                        // an exchange wait failed (set before this barrier)
 
         // ---- phase 2 on every extended row: transposed curl, Cq, H-update filters
 #pragma unroll
-        for (int i = 0; i < CPTB; ++i) {
+        for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
@@ -1132,7 +1141,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 
         // ---- phase 3 on every extended row: lambda_E = Ca e - Dx[t_z] + Dz[t_x]
 #pragma unroll
-        for (int i = 0; i < CPTB; ++i) {
+        for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
@@ -1143,12 +1152,16 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             lE[i] = c.bit(CB_E) ? en : lE[i];
         }
         if (tt > a.t0 && (a.t1 - tt) % ba.kx == 0) {
-            if (!bandk_exchange<P>(ba, t, pk, nex++, &quit, get, put)) break;
+            // the state lives in the cells' registers: no barrier (the next
+            // one, after phase 1, reports a failed wait to every thread)
+            bandk_publish<P>(ba, t, pk, nex, get);
+            if (!bandk_poll<P>(ba, t, pk, nex, put)) quit = 1;
+            ++nex;
         }
     }
 
 #pragma unroll
-    for (int i = 0; i < CPTB; ++i) {
+    for (int i = 0; i < CPTK; ++i) {
         const Cell c{pk[i]};
         const int y = c.y(), x = xof(c);
         const bool own = own_of(c);
@@ -1157,8 +1170,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         b1.st(own, lHx[i], o, L.oHx);
         b1.st(own, lHz[i], o, L.oHz);
         const bool gw = SNAP != SNAP_NONE && in_window(c);
-        bga.st(gw, sGA[c.j()], o, 0u);
-        bgb.st(gw, sGB[c.j()], o, 0u);
+        bga.st(gw, ga[i], o, 0u);
+        bgb.st(gw, gb[i], o, 0u);
         bandk_mem_store(b1, L, g, y, x, own, mm[i]);
     }
 }
