@@ -186,19 +186,28 @@ __device__ __forceinline__ void band_unstage(const float* lds, const BandLayout&
 // device-coherent store, which bypasses the non-coherent caches; the
 // buffers are cleared before every launch), and a reader polls each word
 // until it carries the tag, so the rows need no separate counter, fence or
-// barrier.  Returns false (in every thread) when the launch has failed.
+// barrier.  Every thread publishes its own cells (pk), whose values in A
+// it wrote itself in the phase just done, so publishing needs no barrier
+// either; nobody reads A's halo rows between the previous exchange's
+// barrier and the one that ends this exchange.  Returns false (in every
+// thread) when the launch has failed.
 template <int P>
 __device__ __forceinline__ bool band_exchange(const BandArgs& ba, const Band& t, float* A, int kind, int n,
-                                              int* quit)
+                                              int* quit, const int (&pk)[CPTB])
 {
     const int nx = ba.a.g.nx, tid = threadIdx.x, pn = P * nx;
     const uint64_t tag = (uint64_t)(uint32_t)(n + 1) << 32;
-    __syncthreads();                                          // the phase's writes to A are done
     uint64_t* ob = ba.xbuf + (size_t)(((t.w * 2 + kind) * 2 + (n & 1)) * 2) * pn;
-    for (int i = tid; i < 2 * pn; i += NTS) {
-        const int side = i >= pn, k = i - side * pn;          // k = r * nx + x
-        const float v = A[(side ? t.nrow : P) * nx + k];      // own rows [0, P) or [nrow - P, nrow)
-        __hip_atomic_store(&ob[i], tag | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < CPTB; ++i) {
+        const Cell c = cell(pk[i]);
+        const int j = c.j();
+        if (j >= (P + t.nrow) * nx) continue;                 // an unused slot
+        const int r = c.y() - t.ya, x = j - (r + P) * nx;     // own row r, column x
+        const uint64_t w = tag | __float_as_uint(A[j]);
+        if (r < P) __hip_atomic_store(&ob[r * nx + x], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (r >= t.nrow - P)
+            __hip_atomic_store(&ob[pn + (r - (t.nrow - P)) * nx + x], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     bool bad = ba.spin_max <= 0;                              // (a host-forced failure, for tests)
     for (int i = tid; i < 2 * pn && !bad; i += NTS) {
@@ -322,7 +331,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
             sHx[j] = c.bit(CB_HX) ? fmaf(-cq[i], dy, hx) : hx;
             sHz[j] = c.bit(CB_HZ) ? fmaf(cq[i], dx, hz) : hz;
         }
-        if (!band_exchange<P>(ba, t, sHx, 0, tt - a.t0, &quit)) break;
+        if (!band_exchange<P>(ba, t, sHx, 0, tt - a.t0, &quit, pk)) break;
 
         // ---- E step (reads H^{n+1/2}), snapshots, sources, receivers
         const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
             bev.st(evr, en, (uint32_t)(gs * nx + x) * 4u, out_off);
             sE[j] = c.bit(CB_E) ? en : ev;
         }
-        if (!band_exchange<P>(ba, t, sE, 1, tt - a.t0, &quit)) break;
+        if (!band_exchange<P>(ba, t, sE, 1, tt - a.t0, &quit, pk)) break;
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) add[i] = add_n[i];
     }
@@ -485,7 +494,7 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
             lE[i] = e;
         }
         load_step(tt - 1);
-        if (!band_exchange<P>(ba, t, sW, 0, n, &quit)) break;
+        if (!band_exchange<P>(ba, t, sW, 0, n, &quit, pk)) break;
 
         // ---- phase 2, transposed curl, then Cq and the H-update filters
 #pragma unroll
@@ -507,7 +516,7 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
             sTX[j] = hx ? txv : 0.0f;
             sTZ[j] = hz ? tz : 0.0f;
         }
-        if (!band_exchange<P>(ba, t, sTX, 1, n, &quit)) break;
+        if (!band_exchange<P>(ba, t, sTX, 1, n, &quit, pk)) break;
 
         // ---- phase 3, lambda_E = Ca e - Dx[t_z] + Dz[t_x]
 #pragma unroll
