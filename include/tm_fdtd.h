@@ -112,9 +112,10 @@ typedef struct tm_desc {
                                conditions as 3, else 2); 5 = as 4, with
                                blocked banded kernels where they fit (every
                                band also steps the 2(2P-1) rows next to it
-                               on each side, so that neighbouring bands
-                               exchange their whole state only every second
-                               step), else as 4; 0 = default: 3 with 16
+                               on each side, at most 2048 cells in all, so
+                               that neighbouring bands exchange their whole
+                               state only every second step), else as 4;
+                               0 = default: 3 with 16
                                shots or more, else, where the streaming
                                kernels would leave most of the device idle,
                                5 at order 2 and 4 at orders 4 and 8, else 2.
