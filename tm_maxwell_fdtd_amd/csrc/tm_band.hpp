@@ -1056,8 +1056,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         mm[i] = bandk_mem_load(b0, L, g, c.y(), xof(c), ok);
     }
 
-    float add[CPTK], se[CPTK], sc[CPTK];
-    auto load_step = [&](int tt) {
+    int evo[CPTK];   // event-row offsets of the cells, set once the tables are in LDS
+    // residuals at the receivers and snapshots of a step: two steps ahead,
+    // in two sets (steps of even and odd offset from t1 - 1), each reloaded
+    // right after its step's phase 1 has used it
+    auto load_step = [&](int tt, float (&add)[CPTK], float (&se)[CPTK], float (&sc)[CPTK]) {
         const bool in_run = tt >= a.t0;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
         const bool stored = SNAP != SNAP_NONE && in_run && tt % a.R == 0;
@@ -1069,8 +1072,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             add[i] = se[i] = sc[i] = 0.0f;
             if (!live(i)) continue;
             const Cell c = cell(pk[i]);
-            const int y = c.y(), x = xof(c), gs = slot[y];
-            add[i] = bev.ld(in_run && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + x) * 4u, off);
+            const int y = c.y(), x = xof(c);
+            add[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
             const SnapPair sp = snap_get2<SNAP>(bsp, stored && in_window(c),
                                                 (uint32_t)((y - g.y0) * g.nxi + (x - g.x0)));
             se[i] = sp.e;
@@ -1091,10 +1094,20 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         else mm[i].xe = v;
     };
     __syncthreads();
-    load_step(a.t1 - 1);
+    // event-row offsets of the cells (RBuf::OOB off the event rows)
+#pragma unroll
+    for (int i = 0; i < CPTK; ++i) {
+        const Cell c{pk[i]};
+        const int gs = slot[c.y()];
+        evo[i] = c.bit(CB_E) && gs >= 0 ? (gs * nx + xof(c)) * 4 : RBuf::OOB;
+    }
+    float add0[CPTK], se0[CPTK], sc0[CPTK], add1[CPTK], se1[CPTK], sc1[CPTK];
+    load_step(a.t1 - 1, add0, se0, sc0);
+    load_step(a.t1 - 2, add1, se1, sc1);
 
     int nex = 0;
-    for (int tt = a.t1 - 1; tt >= a.t0; --tt) {
+    // one step; false when the launch has failed
+    auto step = [&](int tt, float (&add)[CPTK], float (&se)[CPTK], float (&sc)[CPTK]) -> bool {
         const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
 
@@ -1105,10 +1118,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             const Cell c = cell(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
             const bool on = c.bit(CB_E);
-            const int gs = slot[y];
-            const bool evr = on && gs >= 0;
-            const float e = evr ? lE[i] + add[i] : lE[i];
-            bev.st(evr && own_of(c), e, (uint32_t)(gs * nx + x) * 4u, out_off);
+            const float e = evo[i] != RBuf::OOB ? lE[i] + add[i] : lE[i];
+            bev.stv(e, own_of(c) ? evo[i] : RBuf::OOB, out_off);
             if (SNAP != SNAP_NONE && stored) {
                 const bool in_w = in_window(c);
                 const float na = fmaf(e, se[i] * a.ratio, ga[i]), nb = fmaf(e, sc[i] * a.ratio, gb[i]);
@@ -1122,9 +1133,9 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             sW[j] = on ? w : 0.0f;
             lE[i] = e;
         }
-        load_step(tt - 1);
+        load_step(tt - 2, add, se, sc);
         __syncthreads();
-        if (quit) break;                        // an exchange wait failed (set before this barrier)
+        if (quit) return false;                 // an exchange wait failed (set before this barrier)
 
         // ---- phase 2 on every extended row: transposed curl, Cq, H-update filters
 #pragma unroll
@@ -1167,6 +1178,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             if (!bandk_poll<P>(ba, t, pk, nex, put)) quit = 1;
             ++nex;
         }
+        return true;
+    };
+    for (int tt = a.t1 - 1; tt >= a.t0; tt -= 2) {
+        if (!step(tt, add0, se0, sc0)) break;
+        if (tt - 1 >= a.t0 && !step(tt - 1, add1, se1, sc1)) break;
     }
 
 #pragma unroll
