@@ -57,9 +57,12 @@ __global__ __launch_bounds__(256) void k_event_gather(float* __restrict__ out, i
 // Shot sum (combine_grad): grad[j] = sum_s grad_shot[s][j], ascending s.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_shot_sum(int64_t slab, int n_shots,
-                                                  const float* __restrict__ gs,
-                                                  float* __restrict__ out)
+                                                  const float* __restrict__ gs0, float* __restrict__ out0,
+                                                  const float* __restrict__ gs1, float* __restrict__ out1)
 {
+    // blockIdx.y picks the pair (the Ca and the Cb gradients in one launch)
+    const float* __restrict__ gs = blockIdx.y ? gs1 : gs0;
+    float* __restrict__ out = blockIdx.y ? out1 : out0;
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= slab) return;
     float acc = 0.0f;

@@ -1950,7 +1950,9 @@ TM_API tm_status tm_adjoint(tm_plan* p, void* ws, uint64_t ws_bytes, const float
         if (p->K > 0 && p->d.n_src > 0 && f == nullptr) return TM_EINVAL;
     }
     hipStream_t st = as_stream(stream);
-    if ((v = upload_tables(p, ws, st)) != TM_OK) return v;
+    // after the storing forward on this workspace (whose snapshots the
+    // gradients read) the tables it uploaded are still there
+    if (!want_grad && (v = upload_tables(p, ws, st)) != TM_OK) return v;
     Fills fills;
     if ((v = stage_model(p, ws, ca, cb, cq, st, fills)) != TM_OK) return v;
     if ((v = fills.add(wsp<float>(ws, p->lay.adj), nullptr, p->lay.adj_bytes, st)) != TM_OK) return v;
@@ -1983,9 +1985,15 @@ TM_API tm_status tm_grad(const tm_plan* p, const float* grad_ca_shot, const floa
     if ((grad_cb == nullptr) != (grad_cb_shot == nullptr)) return TM_EINVAL;
     hipStream_t st = as_stream(stream);
     const int64_t slab = p->g.slab;
-    const dim3 grid((unsigned)((slab + 255) / 256)), blk(256);
-    if (grad_ca) k_shot_sum<<<grid, blk, 0, st>>>(slab, (int)p->d.n_shots, grad_ca_shot, grad_ca);
-    if (grad_cb) k_shot_sum<<<grid, blk, 0, st>>>(slab, (int)p->d.n_shots, grad_cb_shot, grad_cb);
+    // the requested sums in one launch: pair 0 the first requested, pair 1 the other
+    const float* gs[2] = {nullptr, nullptr};
+    float* out[2] = {nullptr, nullptr};
+    int n = 0;
+    if (grad_ca) { gs[n] = grad_ca_shot; out[n] = grad_ca; ++n; }
+    if (grad_cb) { gs[n] = grad_cb_shot; out[n] = grad_cb; ++n; }
+    if (n == 0) return TM_OK;
+    const dim3 grid((unsigned)((slab + 255) / 256), (unsigned)n), blk(256);
+    k_shot_sum<<<grid, blk, 0, st>>>(slab, (int)p->d.n_shots, gs[0], out[0], gs[1], out[1]);
     return hipGetLastError() == hipSuccess ? TM_OK : TM_EHIP;
 }
 
