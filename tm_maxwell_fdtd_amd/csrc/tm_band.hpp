@@ -284,6 +284,9 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
     band_stage(lds, bl, b0, L, g, a.cp, a.ev, t);
     if (tid == 0) quit = 0;
 
+    // iteration i of the cell loops has work in this wave
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = t.nrow * nx;
+    auto cell_live = [&](int i) { return i * NTS + wbase < ncel; };
     int pk[CPTB];
     float ca[CPTB], cb[CPTB], cq[CPTB];
 #pragma unroll
@@ -301,13 +304,15 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
     auto xof = [&](const Cell& c) { return c.j() - (c.y() - y_arr) * nx; };
     float add[CPTB];
     auto load_add = [&](int tt, float (&dst)[CPTB]) {
-        const bool live = tt < a.t1;
-        const uint32_t off = a.ev_add0 + (uint32_t)(live ? tt - a.t0 : 0) * a.ev_row;
+        const bool in_run = tt < a.t1;
+        const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
+            dst[i] = 0.0f;
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int y = c.y(), gs = slot[y];
-            dst[i] = bev.ld(live && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + xof(c)) * 4u, off);
+            dst[i] = bev.ld(in_run && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + xof(c)) * 4u, off);
         }
     };
     load_add(a.t0, add);
@@ -319,6 +324,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
         // ---- H half-step (reads Ey^n, own rows and halo)
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
             float dy = g.rdy * stencil<P>([&](int k) { return sE[j + k * nx]; },
@@ -341,6 +347,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
             float uu = g.rdx * stencil<P>([&](int k) { return sHz[j + k - 1]; }, [&](int k) { return sHz[j - k]; });
@@ -423,6 +430,9 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
         const int y = c.y(), x = xof(c);
         return c.bit(CB_E) && y >= g.y0 && y < g.y1 && x >= g.x0 && x < g.x1;
     };
+    // iteration i of the cell loops has work in this wave
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = t.nrow * nx;
+    auto cell_live = [&](int i) { return i * NTS + wbase < ncel; };
     int pk[CPTB];
     float ca[CPTB], cb[CPTB], cq[CPTB], lE[CPTB], lHx[CPTB], lHz[CPTB], ga[CPTB], gb[CPTB];
 #pragma unroll
@@ -444,17 +454,19 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
 
     float add[CPTB], se[CPTB], sc[CPTB];
     auto load_step = [&](int tt) {
-        const bool live = tt >= a.t0;
-        const uint32_t off = a.ev_add0 + (uint32_t)(live ? tt - a.t0 : 0) * a.ev_row;
-        const bool stored = SNAP != SNAP_NONE && live && tt % a.R == 0;
+        const bool in_run = tt >= a.t0;
+        const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
+        const bool stored = SNAP != SNAP_NONE && in_run && tt % a.R == 0;
         const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
+            add[i] = se[i] = sc[i] = 0.0f;
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int y = c.y(), x = xof(c), gs = slot[y];
-            add[i] = bev.ld(live && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + x) * 4u, off);
+            add[i] = bev.ld(in_run && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + x) * 4u, off);
             const SnapPair sp = snap_get2<SNAP>(bsp, stored && in_window(c),
                                                 (uint32_t)((y - g.y0) * g.nxi + (x - g.x0)));
             se[i] = sp.e;
@@ -472,6 +484,7 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
         // ---- phase 1, transpose of the E step: residual, gradient, Cb, E-update filters
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
             const bool on = c.bit(CB_E);
@@ -499,6 +512,7 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
         // ---- phase 2, transposed curl, then Cq and the H-update filters
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
             const float accx = stencil<P>([&](int k) { return sW[j + k * nx]; },
@@ -521,6 +535,7 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
         // ---- phase 3, lambda_E = Ca e - Dx[t_z] + Dz[t_x]
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
             const float az = stencil<P>([&](int k) { return sTZ[j + k - 1]; }, [&](int k) { return sTZ[j - k]; });
