@@ -302,7 +302,9 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
     __syncthreads();
 
     auto xof = [&](const Cell& c) { return c.j() - (c.y() - y_arr) * nx; };
-    float add[CPTB];
+    // source amplitudes of the cells on event rows: two steps ahead, in two
+    // sets (steps of even and odd offset from t0), each reloaded right after
+    // its step has used it
     auto load_add = [&](int tt, float (&dst)[CPTB]) {
         const bool in_run = tt < a.t1;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
@@ -315,12 +317,12 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
             dst[i] = bev.ld(in_run && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + xof(c)) * 4u, off);
         }
     };
-    load_add(a.t0, add);
+    float add0[CPTB], add1[CPTB];
+    load_add(a.t0, add0);
+    load_add(a.t0 + 1, add1);
 
-    for (int tt = a.t0; tt < a.t1; ++tt) {
-        float add_n[CPTB];
-        load_add(tt + 1, add_n);
-
+    // one step; false when the launch has failed
+    auto step = [&](int tt, float (&add)[CPTB]) -> bool {
         // ---- H half-step (reads Ey^n, own rows and halo)
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
             sHx[j] = c.bit(CB_HX) ? fmaf(-cq[i], dy, hx) : hx;
             sHz[j] = c.bit(CB_HZ) ? fmaf(cq[i], dx, hz) : hz;
         }
-        if (!band_exchange<P>(ba, t, sHx, 0, tt - a.t0, &quit, pk)) break;
+        if (!band_exchange<P>(ba, t, sHx, 0, tt - a.t0, &quit, pk)) return false;
 
         // ---- E step (reads H^{n+1/2}), snapshots, sources, receivers
         const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
@@ -345,6 +347,8 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
+        const bool next_in = tt + 2 < a.t1;
+        const uint32_t next_off = a.ev_add0 + (uint32_t)(next_in ? tt + 2 - a.t0 : 0) * a.ev_row;
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
             if (!cell_live(i)) continue;
@@ -368,12 +372,16 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
             const bool evr = c.bit(CB_E) && gs >= 0;
             en = evr ? en + add[i] : en;
             bev.st(evr, en, (uint32_t)(gs * nx + x) * 4u, out_off);
+            add[i] = bev.ld(next_in && evr, (uint32_t)(gs * nx + x) * 4u, next_off);   // step tt + 2
             sE[j] = c.bit(CB_E) ? en : ev;
         }
-        if (!band_exchange<P>(ba, t, sE, 1, tt - a.t0, &quit, pk)) break;
-#pragma unroll
-        for (int i = 0; i < CPTB; ++i) add[i] = add_n[i];
+        return band_exchange<P>(ba, t, sE, 1, tt - a.t0, &quit, pk);
+    };
+    for (int tt = a.t0; tt < a.t1; tt += 2) {
+        if (!step(tt, add0)) break;
+        if (tt + 1 < a.t1 && !step(tt + 1, add1)) break;
     }
+
 
     // own rows back
     for (int i = tid; i < t.nrow * nx; i += NTS) {
