@@ -34,6 +34,8 @@
 namespace tmf {
 
 constexpr int CPTB = 4;                     // cells per thread of a band (bands are small)
+constexpr int BX_WORDS = 8;                 // exchange words per thread and exchange (2 P nx <= 8 NTS)
+constexpr int BX_BATCH = 2;                 // ... polled together
 
 struct BandArgs {
     SmallArgs a;               // the run (as for the single-workgroup kernels)
@@ -84,7 +86,8 @@ __host__ __device__ inline uint32_t band_lds_bytes(const Geo& g, int rb, bool ad
 // trailing pad included) and the thread count (CPTB cells per thread).
 __host__ __device__ inline bool band_rows_ok(const Geo& g, int rb)
 {
-    return rb >= g.P && (rb + 3 * g.P) * g.nx + g.P < (1 << 14) && rb * g.nx <= NTS * CPTB && g.ny < 2048;
+    return rb >= g.P && (rb + 3 * g.P) * g.nx + g.P < (1 << 14) && rb * g.nx <= NTS * CPTB && g.ny < 2048 &&
+           2 * g.P * g.nx <= BX_WORDS * NTS;
 }
 
 // One own cell of a band, packed as in tm_small.hpp, with j the index in
@@ -209,27 +212,52 @@ __device__ __forceinline__ bool band_exchange(const BandArgs& ba, const Band& t,
         if (r >= t.nrow - P)
             __hip_atomic_store(&ob[pn + (r - (t.nrow - P)) * nx + x], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // poll: a thread's words (at most BX_WORDS: 2P rows of at most 4096 / P
+    // cells) are taken BX_BATCH at a time and the words of a batch are
+    // loaded together in every round, so a thread with two words waits one
+    // round trip, not two
     bool bad = ba.spin_max <= 0;                              // (a host-forced failure, for tests)
-    for (int i = tid; i < 2 * pn && !bad; i += NTS) {
-        const int side = i >= pn, k = i - side * pn;
-        const int nb = side ? t.b + 1 : t.b - 1;
-        if (nb < 0 || nb >= ba.nband) continue;               // beyond the grid: the halo stays 0
-        // above: the neighbour's last rows -> halo rows [0, P); below: its
-        // first rows -> halo rows [P + nrow, 2P + nrow)
-        const uint64_t* ib =
-            ba.xbuf + (size_t)(((((t.s * ba.nband + nb) * 2 + kind) * 2 + (n & 1)) * 2) + (side ? 0 : 1)) * pn;
-        uint64_t w = __hip_atomic_load(&ib[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int it = 1; (w & 0xffffffff00000000ull) != tag; ++it) {
+    const size_t nbase = (size_t)(t.s * ba.nband) * 8 * pn;  // the shot's first workgroup
+#pragma unroll 1
+    for (int q0 = 0; q0 < BX_WORDS && tid + q0 * NTS < 2 * pn && !bad; q0 += BX_BATCH) {
+        uint32_t pending = 0;
+#pragma unroll
+        for (int q = 0; q < BX_BATCH; ++q) {
+            const int i = tid + (q0 + q) * NTS;
+            const int side = i >= pn, nb = side ? t.b + 1 : t.b - 1;
+            if (i < 2 * pn && nb >= 0 && nb < ba.nband) pending |= 1u << q;   // beyond the grid: the halo stays 0
+        }
+#pragma unroll 1
+        for (int it = 0; pending != 0; ++it) {
+            uint64_t w[BX_BATCH];
+#pragma unroll
+            for (int q = 0; q < BX_BATCH; ++q) {
+                if (!((pending >> q) & 1u)) continue;
+                const int i = tid + (q0 + q) * NTS;
+                const int side = i >= pn, k = i - side * pn;
+                const int nb = side ? t.b + 1 : t.b - 1;
+                // above: the neighbour's last rows -> halo rows [0, P); below:
+                // its first rows -> halo rows [P + nrow, 2P + nrow)
+                const uint64_t* ib =
+                    ba.xbuf + nbase + (size_t)((((nb * 2 + kind) * 2 + (n & 1)) * 2) + (side ? 0 : 1)) * pn;
+                w[q] = __hip_atomic_load(&ib[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int q = 0; q < BX_BATCH; ++q) {
+                if (!((pending >> q) & 1u) || (w[q] & 0xffffffff00000000ull) != tag) continue;
+                const int i = tid + (q0 + q) * NTS;
+                const int side = i >= pn, k = i - side * pn;
+                A[(side ? P + t.nrow : 0) * nx + k] = __uint_as_float((uint32_t)w[q]);
+                pending &= ~(1u << q);
+            }
+            if (pending == 0) break;
             if (it >= ba.spin_max ||
-                ((it & 63) == 0 && __hip_atomic_load(ba.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                ((it & 63) == 63 && __hip_atomic_load(ba.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
                 bad = true;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
-            w = __hip_atomic_load(&ib[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (bad) break;
-        A[(side ? P + t.nrow : 0) * nx + k] = __uint_as_float((uint32_t)w);
     }
     if (bad) {
         __hip_atomic_store(ba.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
