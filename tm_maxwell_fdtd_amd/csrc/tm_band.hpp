@@ -8,12 +8,14 @@
 // every workgroup keeps its band (plus P halo rows above and below) in LDS
 // for a whole run of time steps.  After each phase whose output a
 // neighbour reads through a y-stencil, the workgroup publishes its first
-// and last P rows of that array to a global exchange buffer, raises its
-// counter, waits for the two neighbours' counters and copies their rows
-// into its halo: two exchanges per step (forward: Hx after the H half-step,
-// Ey after the E step; adjoint: the filtered w after the transposed E step,
+// and last P rows of that array to a global exchange buffer as tagged words
+// and copies the neighbours' words into its halo rows once they carry the
+// step's tag: two exchanges per step (forward: Hx after the H half-step, Ey
+// after the E step; adjoint: the filtered w after the transposed E step,
 // the filtered Cq lambda_Hx after the transposed H step).  Arrays read only
-// through x-stencils need no halo.
+// through x-stencils need no halo.  The blocked variant at the end of this
+// file steps extra rows of its neighbours instead and exchanges its whole
+// state every few steps.
 //
 // Every cell update is the operation sequence of the single-workgroup
 // resident kernels, so results are bitwise theirs (and those of the
@@ -616,7 +618,9 @@ namespace tmf {
 // extended row, so the rows that matter are computed exactly; records,
 // snapshots, source gradients and model gradients are written for the own
 // rows only.  The band memories live in the cells' registers.  Exchange
-// words are tagged with the exchange number, as above.
+// words are tagged with the exchange number, as above, and laid out so that
+// a wave's lanes store and poll consecutive words; an exchange takes no
+// barrier of its own (the kernels say why).
 // ---------------------------------------------------------------------------
 
 constexpr int BK_NW = 7;                    // exchanged words per cell
