@@ -364,6 +364,10 @@ __global__ __launch_bounds__(NTS) void k_adj_small(SmallArgs a)
         const int y = c.y(), x = c.j() - y * nx;
         return c.bit(CB_E) && y >= g.y0 && y < g.y1 && x >= g.x0 && x < g.x1;
     };
+    // iteration i of the cell loops has work in this wave (skipping the
+    // others also keeps more of the adjoint's state out of scratch)
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
+    auto cell_live = [&](int i) { return i * NTS + wbase < nc; };
     int pk[CPT];
     float ca[CPT], cb[CPT], cq[CPT], lE[CPT], lHx[CPT], lHz[CPT], ga[CPT], gb[CPT];
 #pragma unroll
@@ -395,6 +399,8 @@ __global__ __launch_bounds__(NTS) void k_adj_small(SmallArgs a)
                        stored ? a.snap_shot_bytes : 0u);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
+            add[i] = se[i] = sc[i] = 0.0f;
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int y = c.y(), x = c.j() - y * nx, gs = slot[y];
             add[i] = bev.ld(live && c.bit(CB_E) && gs >= 0, (uint32_t)(gs * nx + x) * 4u, off);
@@ -414,6 +420,7 @@ __global__ __launch_bounds__(NTS) void k_adj_small(SmallArgs a)
         // ---- phase 1, transpose of the E step: residual, gradient, Cb, E-update filters
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j(), y = c.y(), x = j - y * nx;
             const bool on = c.bit(CB_E);
@@ -440,6 +447,7 @@ __global__ __launch_bounds__(NTS) void k_adj_small(SmallArgs a)
         // ---- phase 2, transposed curl, then Cq and the H-update filters
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
             const float accx = stencil<P>([&](int k) { return sW[j + k * nx]; },
@@ -461,6 +469,7 @@ __global__ __launch_bounds__(NTS) void k_adj_small(SmallArgs a)
         // ---- phase 3, lambda_E = Ca e - Dx[t_z] + Dz[t_x]
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
+            if (!cell_live(i)) continue;
             const Cell c = cell(pk[i]);
             const int j = c.j();
             const float az = stencil<P>([&](int k) { return sTZ[j + k - 1]; }, [&](int k) { return sTZ[j - k]; });
