@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -204,6 +205,8 @@ struct tm_plan {
     // pinned staging copy of cpml + tables (allocated on first device call)
     void* pinned = nullptr;
     uint64_t pinned_bytes = 0;
+    float* readback = nullptr;           // pinned words the host reads back (Courant scan, failure word)
+    hipEvent_t readback_done = nullptr;  // ... recorded after their copy
     // sequence state
     void* ws_last = nullptr;
     int64_t fwd_next = -1;
@@ -628,6 +631,36 @@ struct Fills {
         return TM_OK;
     }
 };
+
+// The plan's pinned read-back words and their event, made at first use.
+constexpr int READBACK_WORDS = 1024;
+tm_status ensure_readback(tm_plan* p)
+{
+    if (p->readback != nullptr) return TM_OK;
+    HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&p->readback), READBACK_WORDS * 4, hipHostMallocDefault));
+    HIPCHK(hipEventCreateWithFlags(&p->readback_done, hipEventDisableTiming));
+    return TM_OK;
+}
+
+// Wait for the work queued on st so far (a read-back copy into the pinned
+// words at its end).  The host polls an event for up to SPIN_US
+// microseconds, then blocks: a blocking wait alone wakes the host tens of
+// microseconds after the device finishes, which the small problems (a few
+// milliseconds per call) feel; a long wait does not keep a core busy.
+constexpr int SPIN_US = 200;
+tm_status wait_readback(tm_plan* p, hipStream_t st)
+{
+    HIPCHK(hipEventRecord(p->readback_done, st));
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+        const hipError_t e = hipEventQuery(p->readback_done);
+        if (e == hipSuccess) return TM_OK;
+        if (e != hipErrorNotReady) return TM_EHIP;
+        if (std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(SPIN_US)) break;
+    }
+    HIPCHK(hipEventSynchronize(p->readback_done));
+    return TM_OK;
+}
 
 tm_status zero(float* ptr, uint64_t bytes, hipStream_t st)
 {
@@ -1077,9 +1110,12 @@ tm_status band_check(tm_plan* p, const Ptrs& q, hipStream_t st)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     HIPCHK(hipStreamIsCapturing(st, &cs));
     if (cs != hipStreamCaptureStatusNone) return TM_OK;
+    tm_status v = ensure_readback(p);
+    if (v != TM_OK) return v;
+    HIPCHK(hipMemcpyAsync(p->readback, q.band_err, sizeof(int), hipMemcpyDeviceToHost, st));
+    if ((v = wait_readback(p, st)) != TM_OK) return v;
     int failed = 0;
-    HIPCHK(hipMemcpyAsync(&failed, q.band_err, sizeof(int), hipMemcpyDeviceToHost, st));
-    HIPCHK(hipStreamSynchronize(st));
+    std::memcpy(&failed, p->readback, sizeof(int));
     return failed ? TM_EHIP : TM_OK;
 }
 
@@ -1561,11 +1597,14 @@ tm_status set_events(tm_plan* p, const int64_t* src, const int64_t* rec)
 constexpr int COURANT_NB = 256;
 constexpr int COURANT_WORDS = 2 * COURANT_NB + 1;
 static_assert(COURANT_WORDS * sizeof(float) <= SCRATCH_BYTES, "Courant scratch exceeds the workspace's area");
+static_assert(COURANT_WORDS <= READBACK_WORDS, "Courant read-back exceeds the plan's pinned words");
 
 // scratch: COURANT_WORDS floats of device memory (the workspace's scratch
 // area, or the static array of tm_courant_noalloc).
+// pinned: read back through the plan's pinned words (a polled wait), else
+// into host memory of the call (a blocking one; allocates nothing).
 tm_status courant_impl(tm_plan* p, float* scratch, const float* cb, const float* cq, hipStream_t st, double* out,
-                       bool* cq_one = nullptr, float* cq_val = nullptr)
+                       bool pinned, bool* cq_one = nullptr, float* cq_val = nullptr)
 {
     constexpr int NB = COURANT_NB;
     const int64_t n = p->g.slab * (p->d.model_per_shot ? p->d.n_shots : 1);   // every shot's model
@@ -1573,8 +1612,16 @@ tm_status courant_impl(tm_plan* p, float* scratch, const float* cb, const float*
     k_courant_scan<<<dim3(NB), dim3(256), 0, st>>>(cb, cq, n, scratch);
     HIPCHK(hipGetLastError());
     float part[COURANT_WORDS];
-    HIPCHK(hipMemcpyAsync(part, scratch, sizeof(part), hipMemcpyDeviceToHost, st));
-    HIPCHK(hipStreamSynchronize(st));
+    if (pinned) {
+        tm_status v = ensure_readback(p);
+        if (v != TM_OK) return v;
+        HIPCHK(hipMemcpyAsync(p->readback, scratch, sizeof(part), hipMemcpyDeviceToHost, st));
+        if ((v = wait_readback(p, st)) != TM_OK) return v;
+        std::memcpy(part, p->readback, sizeof(part));
+    } else {
+        HIPCHK(hipMemcpyAsync(part, scratch, sizeof(part), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+    }
     double m = 0.0;
     bool one = true;
     for (int i = 0; i < NB; ++i) {
@@ -1763,6 +1810,9 @@ TM_API void tm_plan_destroy(tm_plan* p)
 {
     if (p == nullptr) return;
     if (p->pinned != nullptr) (void)hipHostFree(p->pinned);
+    if (p->readback_done != nullptr) (void)hipEventSynchronize(p->readback_done);
+    if (p->readback != nullptr) (void)hipHostFree(p->readback);
+    if (p->readback_done != nullptr) (void)hipEventDestroy(p->readback_done);
     if (p->copy_stream != nullptr) (void)hipStreamSynchronize(p->copy_stream);
     if (p->host_store != nullptr) (void)hipHostFree(p->host_store);
     if (p->copy_stream != nullptr) (void)hipStreamDestroy(p->copy_stream);
@@ -1831,7 +1881,7 @@ TM_API tm_status tm_courant(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     if (p == nullptr || cb == nullptr || cq == nullptr || courant == nullptr) return TM_EINVAL;
     tm_status v = check_ws(p, ws, ws_bytes);
     if (v != TM_OK) return v;
-    return courant_impl(p, pointers(p, ws).scratch, cb, cq, as_stream(stream), courant);
+    return courant_impl(p, pointers(p, ws).scratch, cb, cq, as_stream(stream), courant, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -1874,7 +1924,7 @@ TM_API tm_status tm_courant_noalloc(tm_plan* p, const float* cb, const float* cq
     float* scratch = nullptr;
     tm_status v = noalloc_scratch_ptr(&scratch);
     if (v != TM_OK) return v;
-    return courant_impl(p, scratch, cb, cq, as_stream(stream), courant);
+    return courant_impl(p, scratch, cb, cq, as_stream(stream), courant, false);
 }
 
 TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float* ca, const float* cb,
@@ -1894,7 +1944,7 @@ TM_API tm_status tm_forward(tm_plan* p, void* ws, uint64_t ws_bytes, const float
     float cq_val = 0.0f;
     if (flags & TM_FWD_CHECK) {
         double c = 0.0;
-        v = courant_impl(p, pointers(p, ws).scratch, cb, cq, st, &c, &cq_one, &cq_val);
+        v = courant_impl(p, pointers(p, ws).scratch, cb, cq, st, &c, true, &cq_one, &cq_val);
         if (v != TM_OK) return v;
         if (!(c <= 1.0)) return TM_EUNSTABLE;
     }
