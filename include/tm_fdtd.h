@@ -172,6 +172,9 @@ typedef struct tm_plan tm_plan;
 tm_status tm_plan_create(const tm_desc* desc, const float* cpml, const int64_t* src,
                          const int64_t* rec, tm_plan** out);
 
+/* Frees the plan and the host memory it allocated (pinned staging and
+ * read-back buffers, the pinned snapshot store of TM_STORE_HOST), after
+ * waiting for the work that uses it. */
 void tm_plan_destroy(tm_plan* plan);
 
 /*
@@ -202,7 +205,10 @@ tm_status tm_workspace_bytes(const tm_plan* plan, uint64_t* bytes);
  * gives none, its launchers do not check stability) (the largest over the shots' models with model_per_shot); the
  * scheme is stable when it is at most 1.  cb, cq: device float32 [ny][nx]
  * ([S][ny][nx] with model_per_shot).  Uses the workspace's scratch area and
- * synchronises ``stream``.
+ * synchronises ``stream`` (the result comes back through a few KiB of
+ * pinned host memory that the plan allocates at its first read-back and
+ * tm_plan_destroy frees; tm_forward's check and the banded kernels' failure
+ * word use them too).
  */
 tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb,
                      const float* cq, void* stream, double* courant);
@@ -215,9 +221,9 @@ tm_status tm_courant(tm_plan* plan, void* ws, uint64_t ws_bytes, const float* cb
  * floats: 256 per-block maxima, 256 per-block flags of the uniform-Cq test
  * and cq[0]) is a static device array of the library, one per device, held
  * until the process ends; the scratch size does not depend on the model
- * size, so no
- * size is refused for it.  Allocates nothing (no hipMalloc / hipFree),
- * synchronises ``stream``.  Calls that overlap on one device share the
+ * size, so no size is refused for it.  Allocates nothing (no hipMalloc /
+ * hipFree, no pinned host memory: the result is read back into memory of
+ * the call), synchronises ``stream``.  Calls that overlap on one device share the
  * array and race: serialise them.  TM_EINVAL for a NULL argument or a
  * device ordinal of 64 or more; TM_EHIP when the array's device address
  * cannot be found.
