@@ -687,15 +687,34 @@ __device__ __forceinline__ BandK bandk_of(const BandKArgs& ba)
     return t;
 }
 
-// One cell of the extended rows (index je from row ea), packed as in
+// The cells of the extended rows that some update touches: rows [ca, cb)
+// of the grid's rows P .. ny-P, columns P .. nx-P (ncol of them).  The
+// others (the outermost rows and columns) are never written by any update,
+// so the kernels leave them as loaded (0) and neither step nor exchange
+// them: on the 86^2 order-2 grid that brings a band's 6 x 86 cells to 510,
+// eight waves instead of nine.
+struct BandKCells {
+    int ca, cb, ncol, n;
+};
+__device__ __forceinline__ BandKCells bandk_cells(const BandK& t, const Geo& g)
+{
+    BandKCells c;
+    c.ca = max(t.ea, g.P);
+    c.cb = min(t.eb, g.ny - g.P + 1);
+    c.ncol = g.nx - 2 * g.P + 1;
+    c.n = c.cb > c.ca ? (c.cb - c.ca) * c.ncol : 0;
+    return c;
+}
+
+// Cell je of those (row-major from row ca, column P), packed as in
 // tm_small.hpp with j its index in the cell arrays (array row y - y_arr).
 template <int P>
-__device__ __forceinline__ int pack_bandk_cell(int je, const BandK& t, int rows, const Geo& g)
+__device__ __forceinline__ int pack_bandk_cell(int je, const BandK& t, const BandKCells& cs, int rows, const Geo& g)
 {
     const int nx = g.nx;
-    const bool ok = je < (t.eb - t.ea) * nx;
-    const int r = ok ? je / nx : 0;
-    const int y = t.ea + r, x = ok ? je - r * nx : P;
+    const bool ok = je < cs.n;
+    const int r = ok ? je / cs.ncol : 0;
+    const int y = ok ? cs.ca + r : t.ea, x = ok ? P + je - r * cs.ncol : P;
     const bool ecol = x >= P && x <= nx - P, erow = y >= P && y <= g.ny - P;
     const bool e = ok && ecol && erow;
     const bool hx = ok && ecol && y >= P && y <= g.ny - P - 1;
@@ -893,7 +912,8 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     auto xof = [&](const Cell& c) { return c.j() - (c.y() - t.y_arr) * nx; };
     // iteration i of the cell loops has work in this wave
-    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = (t.eb - t.ea) * nx;
+    const BandKCells cs = bandk_cells(t, g);
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = cs.n;
     auto live = [&](int i) { return i * NTS + wbase < ncel; };
     int pk[CPTK];
     float ca[CPTK], cb[CPTK], cq[CPTK];
@@ -901,9 +921,10 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 #pragma unroll
     for (int i = 0; i < CPTK; ++i) {
         const int je = tid + i * NTS;
-        const bool ok = je < (t.eb - t.ea) * nx;
-        pk[i] = pack_bandk_cell<P>(je, t, rows, g);
-        const uint32_t o = (uint32_t)(ok ? t.ea * nx + je : 0) * 4u;
+        const bool ok = je < cs.n;
+        pk[i] = pack_bandk_cell<P>(je, t, cs, rows, g);
+        const Cell c0{pk[i]};
+        const uint32_t o = (uint32_t)(ok ? c0.y() * nx + xof(c0) : 0) * 4u;
         ca[i] = bm.ld(ok, o, a.m.oCa);
         cb[i] = bm.ld(ok, o, a.m.oCb);
         cq[i] = bm.ld(ok, o, a.m.oCq);
@@ -1087,7 +1108,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         const int y = c.y(), x = xof(c);
         return own_of(c) && c.bit(CB_E) && y >= g.y0 && y < g.y1 && x >= g.x0 && x < g.x1;
     };
-    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = (t.eb - t.ea) * nx;
+    const BandKCells cs = bandk_cells(t, g);
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = cs.n;
     auto live = [&](int i) { return i * NTS + wbase < ncel; };
     int pk[CPTK];
     float ca[CPTK], cb[CPTK], cq[CPTK], lE[CPTK], lHx[CPTK], lHz[CPTK], ga[CPTK], gb[CPTK];
@@ -1095,9 +1117,10 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 #pragma unroll
     for (int i = 0; i < CPTK; ++i) {
         const int je = tid + i * NTS;
-        const bool ok = je < (t.eb - t.ea) * nx;
-        pk[i] = pack_bandk_cell<P>(je, t, rows, g);
-        const uint32_t o = (uint32_t)(ok ? t.ea * nx + je : 0) * 4u;
+        const bool ok = je < cs.n;
+        pk[i] = pack_bandk_cell<P>(je, t, cs, rows, g);
+        const Cell c0{pk[i]};
+        const uint32_t o = (uint32_t)(ok ? c0.y() * nx + xof(c0) : 0) * 4u;
         ca[i] = bm.ld(ok, o, a.m.oCa);
         cb[i] = bm.ld(ok, o, a.m.oCb);
         cq[i] = bm.ld(ok, o, a.m.oCq);
