@@ -706,6 +706,17 @@ __device__ __forceinline__ BandKCells bandk_cells(const BandK& t, const Geo& g)
     return c;
 }
 
+// A packed cell in a step loop: at order 2 decoded where the compiler likes
+// (it keeps the decoded fields in registers across the time loop), at
+// higher orders rebuilt at each use (cell(), tm_small.hpp), since their
+// larger stencils leave no registers for that.
+template <int P>
+__device__ __forceinline__ Cell bcell(int packed)
+{
+    if constexpr (P == 1) return Cell{packed};
+    else return cell(packed);
+}
+
 // Cell je of those (row-major from row ca, column P), packed as in
 // tm_small.hpp with j its index in the cell arrays (array row y - y_arr).
 template <int P>
@@ -984,7 +995,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 #pragma unroll
         for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
-            const Cell c = cell(pk[i]);
+            const Cell c = bcell<P>(pk[i]);
             const int j = c.j(), x = xof(c);
             const float hx = sHx[j], hz = sHz[j];
             float dy = g.rdy * stencil<P>([&](int k) { return sE[j + k * nx]; },
@@ -1008,7 +1019,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 #pragma unroll
         for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
-            const Cell c = cell(pk[i]);
+            const Cell c = bcell<P>(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
             const float ev = sE[j];
             float uu = g.rdx * stencil<P>([&](int k) { return sHz[j + k - 1]; }, [&](int k) { return sHz[j - k]; });
@@ -1149,7 +1160,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         for (int i = 0; i < CPTK; ++i) {
             add[i] = se[i] = sc[i] = 0.0f;
             if (!live(i)) continue;
-            const Cell c = cell(pk[i]);
+            const Cell c = bcell<P>(pk[i]);
             const int y = c.y(), x = xof(c);
             add[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
             const SnapPair sp = snap_get2<SNAP>(bsp, stored && in_window(c),
@@ -1193,7 +1204,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 #pragma unroll
         for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
-            const Cell c = cell(pk[i]);
+            const Cell c = bcell<P>(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
             const bool on = c.bit(CB_E);
             const float e = evo[i] != RBuf::OOB ? lE[i] + add[i] : lE[i];
@@ -1219,7 +1230,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 #pragma unroll
         for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
-            const Cell c = cell(pk[i]);
+            const Cell c = bcell<P>(pk[i]);
             const int j = c.j();
             const float accx = stencil<P>([&](int k) { return sW[j + k * nx]; },
                                           [&](int k) { return sW[j - (k - 1) * nx]; });
@@ -1241,7 +1252,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 #pragma unroll
         for (int i = 0; i < CPTK; ++i) {
             if (!live(i)) continue;
-            const Cell c = cell(pk[i]);
+            const Cell c = bcell<P>(pk[i]);
             const int j = c.j();
             const float az = stencil<P>([&](int k) { return sTZ[j + k - 1]; }, [&](int k) { return sTZ[j - k]; });
             const float ay = stencil<P>([&](int k) { return sTX[j + (k - 1) * nx]; },
