@@ -407,6 +407,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
         }
         return band_exchange<P>(ba, t, sE, 1, tt - a.t0, &quit, pk);
     };
+    drain_vmem();
     for (int tt = a.t0; tt < a.t1; tt += 2) {
         if (!step(tt, add0)) break;
         if (tt + 1 < a.t1 && !step(tt + 1, add1)) break;
@@ -514,6 +515,7 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
     __syncthreads();
     load_step(a.t1 - 1);
 
+    drain_vmem();
     for (int tt = a.t1 - 1; tt >= a.t0; --tt) {
         const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
@@ -624,7 +626,7 @@ namespace tmf {
 // ---------------------------------------------------------------------------
 
 constexpr int BK_NW = 7;                    // exchanged words per cell
-constexpr int CPTK = 2;                     // cells per thread (a band's extended rows: at most 2048 cells)
+constexpr int CPTK = 2;                     // most cells per thread (a band's extended rows: at most 2048 cells)
 
 struct BandKArgs {
     SmallArgs a;
@@ -663,6 +665,14 @@ __host__ __device__ inline bool bandk_rows_ok(const Geo& g, int rb, int hd)
 {
     return rb >= hd && hd >= 2 * g.P - 1 && (rb + 2 * hd + g.P) * g.nx + g.P < (1 << 14) &&
            (rb + 2 * hd) * g.nx <= NTS * CPTK && g.ny < 2048;
+}
+
+// Cells per thread of the kernel instance that runs a layout: 1 where the
+// extended rows have at most NTS cells (half the cell registers, which the
+// order-2 adjoint needs to stay out of scratch), else CPTK.
+__host__ __device__ inline int bandk_cells_per_thread(const Geo& g, int rb, int hd)
+{
+    return (rb + 2 * hd) * g.nx <= NTS ? 1 : CPTK;
 }
 
 struct BandK {
@@ -792,19 +802,25 @@ __device__ __forceinline__ void bandk_mem_store(const RBuf& b, const StateLayout
 }
 
 // A filter on a register memory: the recursion where the site applies,
-// the identity elsewhere.
+// the identity elsewhere.  The coefficients are read whether or not the
+// site applies (every row and column has table entries), so the reads
+// leave with the stencil's instead of after it: one LDS round trip less
+// per filtered update.
 __device__ __forceinline__ float rsite(bool on, float& m, const float* tab, int n, float d)
 {
-    if (on) d = cpml_step(m, tab[0], tab[n], tab[2 * n], d);
-    return d;
+    const float a = tab[0], b = tab[n], ik = tab[2 * n];
+    float mn = m;
+    const float r = cpml_step(mn, a, b, ik, d);
+    m = on ? mn : m;
+    return on ? r : d;
 }
 
 // Exchange number n, in two halves that need no barrier of their own.
 // Publish: the words of the cells on the first and last hd own rows (w[0..6]
 // of each cell, read by get(i, k); each thread publishes its own cells,
 // whose values it wrote itself).
-template <int P, typename Get>
-__device__ __forceinline__ void bandk_publish(const BandKArgs& ba, const BandK& t, const int (&pk)[CPTK], int n,
+template <int P, int CK, typename Get>
+__device__ __forceinline__ void bandk_publish(const BandKArgs& ba, const BandK& t, const int (&pk)[CK], int n,
                                               Get get)
 {
     const int nx = ba.a.g.nx, hd = ba.hd;
@@ -812,7 +828,7 @@ __device__ __forceinline__ void bandk_publish(const BandKArgs& ba, const BandK& 
     const uint64_t tag = (uint64_t)(uint32_t)(n + 1) << 32;
     uint64_t* ob = ba.xbuf + (size_t)((t.w * 2 + (n & 1)) * 2) * side_w;
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const Cell c = cell(pk[i]);
         const int y = c.y(), x = c.j() - (y - t.y_arr) * nx;
         const bool valid = c.j() < (t.eb - t.y_arr) * nx && y >= t.ya && y < t.yb;
@@ -838,15 +854,26 @@ __device__ __forceinline__ void bandk_publish(const BandKArgs& ba, const BandK& 
 // extended rows outside the band and hand them to put(i, k, v).  Returns
 // false when this thread's wait failed or the launch has failed (err is
 // then set); the caller tells the other threads at its next barrier.
-template <int P, typename Put>
-__device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, const int (&pk)[CPTK], int n, Put put)
+//
+// The words go through the memory that all the chip's L2s share, so each
+// poll is one memory round trip; neighbours publish at about the same time,
+// and a poll sent at once mostly arrives before their words and costs a
+// second round trip.  A thread with cells to poll therefore sleeps
+// BK_POLL_WAIT units (64 clocks each) before its first poll: on the 86^2 order-2 grid 12
+// units took the forward from 503 to 465 us and the adjoint from 645 to
+// 612 us over 300 steps (8 units: 473 / 615; 24: 499 / 653).
+constexpr int BK_POLL_WAIT = 12;
+
+template <int P, int CK, typename Put>
+__device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, const int (&pk)[CK], int n, Put put)
 {
     const int nx = ba.a.g.nx, hd = ba.hd;
     const size_t plane = (size_t)hd * nx, side_w = plane * BK_NW;
     const uint64_t tag = (uint64_t)(uint32_t)(n + 1) << 32;
     bool bad = ba.spin_max <= 0;                              // (a host-forced failure, for tests)
+    bool waited = false;
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const Cell c = cell(pk[i]);
         const int y = c.y(), x = c.j() - (y - t.y_arr) * nx;
         const bool valid = c.j() < (t.eb - t.y_arr) * nx;
@@ -859,6 +886,8 @@ __device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, 
         const uint64_t* ib = ba.xbuf + (size_t)(((t.s * ba.nband + nb) * 2 + (n & 1)) * 2 + (above ? 1 : 0)) * side_w +
                              (size_t)r * nx + x;
         uint64_t w[BK_NW];
+        if (!waited) __builtin_amdgcn_s_sleep(BK_POLL_WAIT);
+        waited = true;
         for (int it = 0;; ++it) {
             bool all = true;
 #pragma unroll
@@ -883,7 +912,7 @@ __device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, 
 }
 
 // Forward, blocked: steps t0 .. t1-1, workgroup = (shot, band).
-template <int P, int SNAP>
+template <int P, int SNAP, int CK>
 __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 {
     extern __shared__ float lds[];
@@ -926,11 +955,11 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
     const BandKCells cs = bandk_cells(t, g);
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = cs.n;
     auto live = [&](int i) { return i * NTS + wbase < ncel; };
-    int pk[CPTK];
-    float ca[CPTK], cb[CPTK], cq[CPTK];
-    CellMem mm[CPTK];
+    int pk[CK];
+    float ca[CK], cb[CK], cq[CK];
+    CellMem mm[CK];
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const int je = tid + i * NTS;
         const bool ok = je < cs.n;
         pk[i] = pack_bandk_cell<P>(je, t, cs, rows, g);
@@ -946,9 +975,9 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     // event-row offsets of the cells (RBuf::OOB off the event rows), and
     // the iterations in which this wave has any
-    int evo[CPTK], evmask = 0;
+    int evo[CK], evmask = 0;
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const Cell c{pk[i]};
         const int gs = slot[c.y()];
         evo[i] = c.bit(CB_E) && gs >= 0 ? (gs * nx + xof(c)) * 4 : RBuf::OOB;
@@ -959,17 +988,17 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
     // source amplitudes of the cells on event rows: two steps ahead, in two
     // sets (steps of even and odd offset from t0), each reloaded right
     // after its step has used it
-    auto load_add = [&](int tt, float (&dst)[CPTK]) {
+    auto load_add = [&](int tt, float (&dst)[CK]) {
         const bool in_run = tt < a.t1;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
 #pragma unroll
-        for (int i = 0; i < CPTK; ++i) {
+        for (int i = 0; i < CK; ++i) {
             dst[i] = 0.0f;
             if (((evmask >> i) & 1) == 0) continue;
             dst[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
         }
     };
-    float add0[CPTK], add1[CPTK];
+    float add0[CK], add1[CK];
     load_add(a.t0, add0);
     load_add(a.t0 + 1, add1);
     auto get = [&](int i, int k) -> float {
@@ -990,10 +1019,10 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     int nex = 0;
     // one step; false when the launch has failed
-    auto step = [&](int tt, float (&add)[CPTK]) -> bool {
+    auto step = [&](int tt, float (&add)[CK]) -> bool {
         // ---- H half-step on every extended row
 #pragma unroll
-        for (int i = 0; i < CPTK; ++i) {
+        for (int i = 0; i < CK; ++i) {
             if (!live(i)) continue;
             const Cell c = bcell<P>(pk[i]);
             const int j = c.j(), x = xof(c);
@@ -1017,7 +1046,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
         const bool next_in = tt + 2 < a.t1;
         const uint32_t next_off = a.ev_add0 + (uint32_t)(next_in ? tt + 2 - a.t0 : 0) * a.ev_row;
 #pragma unroll
-        for (int i = 0; i < CPTK; ++i) {
+        for (int i = 0; i < CK; ++i) {
             if (!live(i)) continue;
             const Cell c = bcell<P>(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
@@ -1050,13 +1079,14 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
             // here are already exact, so the stores do not change them; the
             // other reads are for outer-row cells, whose results the
             // exchange replaces.  The next reads follow the barrier below.
-            bandk_publish<P>(ba, t, pk, nex, get);
-            if (!bandk_poll<P>(ba, t, pk, nex, put)) quit = 1;
+            bandk_publish<P, CK>(ba, t, pk, nex, get);
+            if (!bandk_poll<P, CK>(ba, t, pk, nex, put)) quit = 1;
             ++nex;
         }
         __syncthreads();
         return quit == 0;
     };
+    drain_vmem();
     for (int tt = a.t0; tt < a.t1; tt += 2) {
         if (!step(tt, add0)) break;
         if (tt + 1 < a.t1 && !step(tt + 1, add1)) break;
@@ -1064,7 +1094,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     // own rows back
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const Cell c{pk[i]};
         const int y = c.y(), x = xof(c);
         const bool own = c.j() < (t.eb - t.y_arr) * nx && y >= t.ya && y < t.yb;
@@ -1077,7 +1107,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 }
 
 // Exact adjoint, blocked: steps t1-1 down to t0, workgroup = (shot, band).
-template <int P, int SNAP>
+template <int P, int SNAP, int CK>
 __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 {
     extern __shared__ float lds[];
@@ -1122,11 +1152,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const BandKCells cs = bandk_cells(t, g);
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = cs.n;
     auto live = [&](int i) { return i * NTS + wbase < ncel; };
-    int pk[CPTK];
-    float ca[CPTK], cb[CPTK], cq[CPTK], lE[CPTK], lHx[CPTK], lHz[CPTK], ga[CPTK], gb[CPTK];
-    CellMem mm[CPTK];
+    int pk[CK];
+    float ca[CK], cb[CK], cq[CK], lE[CK], lHx[CK], lHz[CK], ga[CK], gb[CK];
+    CellMem mm[CK];
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const int je = tid + i * NTS;
         const bool ok = je < cs.n;
         pk[i] = pack_bandk_cell<P>(je, t, cs, rows, g);
@@ -1145,11 +1175,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         mm[i] = bandk_mem_load(b0, L, g, c.y(), xof(c), ok);
     }
 
-    int evo[CPTK];   // event-row offsets of the cells, set once the tables are in LDS
+    int evo[CK];   // event-row offsets of the cells, set once the tables are in LDS
     // residuals at the receivers and snapshots of a step: two steps ahead,
     // in two sets (steps of even and odd offset from t1 - 1), each reloaded
     // right after its step's phase 1 has used it
-    auto load_step = [&](int tt, float (&add)[CPTK], float (&se)[CPTK], float (&sc)[CPTK]) {
+    auto load_step = [&](int tt, float (&add)[CK], float (&se)[CK], float (&sc)[CK]) {
         const bool in_run = tt >= a.t0;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
         const bool stored = SNAP != SNAP_NONE && in_run && tt % a.R == 0;
@@ -1157,7 +1187,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
 #pragma unroll
-        for (int i = 0; i < CPTK; ++i) {
+        for (int i = 0; i < CK; ++i) {
             add[i] = se[i] = sc[i] = 0.0f;
             if (!live(i)) continue;
             const Cell c = bcell<P>(pk[i]);
@@ -1185,24 +1215,24 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     __syncthreads();
     // event-row offsets of the cells (RBuf::OOB off the event rows)
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const Cell c{pk[i]};
         const int gs = slot[c.y()];
         evo[i] = c.bit(CB_E) && gs >= 0 ? (gs * nx + xof(c)) * 4 : RBuf::OOB;
     }
-    float add0[CPTK], se0[CPTK], sc0[CPTK], add1[CPTK], se1[CPTK], sc1[CPTK];
+    float add0[CK], se0[CK], sc0[CK], add1[CK], se1[CK], sc1[CK];
     load_step(a.t1 - 1, add0, se0, sc0);
     load_step(a.t1 - 2, add1, se1, sc1);
 
     int nex = 0;
     // one step; false when the launch has failed
-    auto step = [&](int tt, float (&add)[CPTK], float (&se)[CPTK], float (&sc)[CPTK]) -> bool {
+    auto step = [&](int tt, float (&add)[CK], float (&se)[CK], float (&sc)[CK]) -> bool {
         const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
 
         // ---- phase 1 on every extended row: residual, gradient (own), Cb, E-update filters
 #pragma unroll
-        for (int i = 0; i < CPTK; ++i) {
+        for (int i = 0; i < CK; ++i) {
             if (!live(i)) continue;
             const Cell c = bcell<P>(pk[i]);
             const int j = c.j(), y = c.y(), x = xof(c);
@@ -1228,7 +1258,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 
         // ---- phase 2 on every extended row: transposed curl, Cq, H-update filters
 #pragma unroll
-        for (int i = 0; i < CPTK; ++i) {
+        for (int i = 0; i < CK; ++i) {
             if (!live(i)) continue;
             const Cell c = bcell<P>(pk[i]);
             const int j = c.j();
@@ -1250,7 +1280,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
 
         // ---- phase 3 on every extended row: lambda_E = Ca e - Dx[t_z] + Dz[t_x]
 #pragma unroll
-        for (int i = 0; i < CPTK; ++i) {
+        for (int i = 0; i < CK; ++i) {
             if (!live(i)) continue;
             const Cell c = bcell<P>(pk[i]);
             const int j = c.j();
@@ -1263,19 +1293,20 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         if (tt > a.t0 && (a.t1 - tt) % ba.kx == 0) {
             // the state lives in the cells' registers: no barrier (the next
             // one, after phase 1, reports a failed wait to every thread)
-            bandk_publish<P>(ba, t, pk, nex, get);
-            if (!bandk_poll<P>(ba, t, pk, nex, put)) quit = 1;
+            bandk_publish<P, CK>(ba, t, pk, nex, get);
+            if (!bandk_poll<P, CK>(ba, t, pk, nex, put)) quit = 1;
             ++nex;
         }
         return true;
     };
+    drain_vmem();
     for (int tt = a.t1 - 1; tt >= a.t0; tt -= 2) {
         if (!step(tt, add0, se0, sc0)) break;
         if (tt - 1 >= a.t0 && !step(tt - 1, add1, se1, sc1)) break;
     }
 
 #pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
+    for (int i = 0; i < CK; ++i) {
         const Cell c{pk[i]};
         const int y = c.y(), x = xof(c);
         const bool own = own_of(c);

@@ -48,6 +48,14 @@ __device__ __forceinline__ constexpr float coef<4>(int k)
                   : (float)(-5.0 / 7168.0);
 }
 
+// Wait until every vector memory access this wave has issued is done
+// (vmcnt 0, the other counters left alone).  Resident kernels call it once
+// before their time loop: a value loaded before the loop and carried
+// through it otherwise looks possibly in flight at the loop head, and the
+// compiler then places a wait on it inside the loop, which at every step
+// also waits for that step's prefetches and snapshot stores.
+__device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ int band_x(const Geo& g, int x) { return x < g.x0 ? x : g.bxl + (x - g.hx1); }
 __device__ __forceinline__ int band_y(const Geo& g, int y) { return y < g.y0 ? y : g.byl + (y - g.hy1); }
 

@@ -1079,6 +1079,24 @@ BandKArgs bandk_args(const tm_plan* p, const Ptrs& q, const SmallArgs& a)
     return k;
 }
 
+// The blocked kernel instances of a snapshot format and cells per thread.
+template <int P, int CK>
+const void* fwd_bandk_fn(int snap)
+{
+    return snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_F32, CK>)
+         : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_BF16, CK>)
+         : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_FP8, CK>)
+                               : reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_NONE, CK>);
+}
+template <int P, int CK>
+const void* adj_bandk_fn(int snap)
+{
+    return snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_F32, CK>)
+         : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_BF16, CK>)
+         : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_FP8, CK>)
+                               : reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_NONE, CK>);
+}
+
 // Launch a banded kernel cooperatively (all its workgroups resident at
 // once), its exchange rows cleared first (their step tags restart at every
 // launch); the failure word is cleared by the first banded launch of a call
@@ -1145,10 +1163,8 @@ tm_status fwd_band(tm_plan* p, const Ptrs& q, int cur, int64_t ta, int64_t tb, i
     a.ev_row = (uint32_t)L.ev_row;
     if (p->band_kx > 0) {
         BandKArgs b = bandk_args(p, q, a);
-        const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_F32>)
-                       : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_BF16>)
-                       : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_FP8>)
-                                             : reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_NONE>);
+        const void* fn = bandk_cells_per_thread(p->g, p->band_rb, p->band_hd) == 1 ? fwd_bandk_fn<P, 1>(snap)
+                                                                                  : fwd_bandk_fn<P, CPTK>(snap);
         return band_launch(p, q, fn, &b, bandk_lds_bytes(p->g, p->band_rb, p->band_hd, false),
                            snap == SNAP_NONE ? KID_FWD_BANDK : KID_FWD_BANDK_ST, ta, st);
     }
@@ -1190,10 +1206,8 @@ tm_status adj_band(tm_plan* p, const Ptrs& q, int64_t ta, int64_t tb, int64_t k,
     a.gcb = gcb;
     if (p->band_kx > 0) {
         BandKArgs b = bandk_args(p, q, a);
-        const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_F32>)
-                       : snap == SNAP_BF16   ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_BF16>)
-                       : snap == SNAP_FP8    ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_FP8>)
-                                             : reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_NONE>);
+        const void* fn = bandk_cells_per_thread(p->g, p->band_rb, p->band_hd) == 1 ? adj_bandk_fn<P, 1>(snap)
+                                                                                  : adj_bandk_fn<P, CPTK>(snap);
         return band_launch(p, q, fn, &b, bandk_lds_bytes(p->g, p->band_rb, p->band_hd, true), KID_ADJ_BANDK, ta,
                            st);
     }
@@ -1325,10 +1339,11 @@ tm_status device_tiling(tm_plan* p)
                                : band_lds_bytes(p->g, p->band_rb, true);
         if (lf <= (uint32_t)lds_max && la <= (uint32_t)lds_max) {
             int of = 0, oa = 0;
-            const void* ff = kb ? reinterpret_cast<const void*>(&k_fwd_bandk<P, SNAP_F32>)
-                                : reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>);
-            const void* fa = kb ? reinterpret_cast<const void*>(&k_adj_bandk<P, SNAP_F32>)
-                                : reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>);
+            const bool k1 = kb && bandk_cells_per_thread(p->g, p->band_rb, p->band_hd) == 1;
+            const void* ff = !kb ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>)
+                             : k1 ? fwd_bandk_fn<P, 1>(SNAP_F32) : fwd_bandk_fn<P, CPTK>(SNAP_F32);
+            const void* fa = !kb ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>)
+                             : k1 ? adj_bandk_fn<P, 1>(SNAP_F32) : adj_bandk_fn<P, CPTK>(SNAP_F32);
             HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&of, ff, NTS, lf));
             HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&oa, fa, NTS, la));
             p->banded = p->d.n_shots * p->band_n <= (int64_t)std::min(of, oa) * ncu;

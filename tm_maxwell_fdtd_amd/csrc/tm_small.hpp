@@ -259,6 +259,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_small(SmallArgs a)
     };
     load_add(a.t0, add);
 
+    drain_vmem();
     for (int tt = a.t0; tt < a.t1; ++tt) {
         float add_n[CPT];
         load_add(tt + 1, add_n);
@@ -413,6 +414,7 @@ __global__ __launch_bounds__(NTS) void k_adj_small(SmallArgs a)
     __syncthreads();
     load_step(a.t1 - 1);
 
+    drain_vmem();
     for (int tt = a.t1 - 1; tt >= a.t0; --tt) {
         const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
