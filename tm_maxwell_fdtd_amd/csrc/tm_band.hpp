@@ -1186,10 +1186,11 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
         const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
+        // (every wave loads, off the buffers where it has no cell, so that
+        // the registers are only ever written by loads: no wait for the
+        // previous loads into them)
 #pragma unroll
         for (int i = 0; i < CK; ++i) {
-            add[i] = se[i] = sc[i] = 0.0f;
-            if (!live(i)) continue;
             const Cell c = bcell<P>(pk[i]);
             const int y = c.y(), x = xof(c);
             add[i] = bev.ldv(in_run ? evo[i] : RBuf::OOB, off);
