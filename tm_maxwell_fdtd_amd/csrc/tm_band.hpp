@@ -265,6 +265,10 @@ __device__ __forceinline__ bool band_exchange(const BandArgs& ba, const Band& t,
         __hip_atomic_store(ba.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *quit = 1;                                            // any thread may set it; all read it below
     }
+    // Every poll load has been waited for, but the compiler cannot tell on
+    // all paths and would otherwise wait for all memory accesses at each
+    // later write of those registers (each cell of the next phases).
+    drain_vmem();
     __syncthreads();
     return *quit == 0;
 }
