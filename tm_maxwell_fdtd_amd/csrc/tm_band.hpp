@@ -679,6 +679,17 @@ __host__ __device__ inline int bandk_cells_per_thread(const Geo& g, int rb, int 
     return (rb + 2 * hd) * g.nx <= NTS ? 1 : CPTK;
 }
 
+// Threads of a blocked launch: with one cell per thread, one per cell that
+// some update touches (rounded up to whole waves: a band's extended rows
+// within rows P .. ny-P, columns P .. nx-P), so that no wave only keeps
+// time at the barriers; else NTS.
+__host__ __device__ inline int bandk_threads(const Geo& g, int rb, int hd)
+{
+    if (bandk_cells_per_thread(g, rb, hd) != 1) return NTS;
+    const int n = (rb + 2 * hd) * (g.nx - 2 * g.P + 1);
+    return (n + 63) / 64 * 64;
+}
+
 struct BandK {
     int s, b, w;
     int ya, yb, nrow;                       // own rows [ya, yb)
@@ -753,22 +764,22 @@ __device__ __forceinline__ int pack_bandk_cell(int je, const BandK& t, const Ban
 
 // The CPML tables and event-row slots into LDS.
 __device__ __forceinline__ void bandk_tables(float* lds, const BandKLayout& bl, const Geo& g,
-                                             const float* __restrict__ cp, const EventRows& ev, int s)
+                                             const float* __restrict__ cp, const EventRows& ev, int s, int nth)
 {
-    for (int i = threadIdx.x; i < 6 * g.ny; i += NTS) {
+    for (int i = threadIdx.x; i < 6 * g.ny; i += nth) {
         const int k = i / g.ny, y = i - k * g.ny;
         const int row = (k < 3 ? AYH : AY) + (k < 3 ? k : k - 3);
         const float v = cp[row * g.L + y];
         lds[bl.ty + i] = (k == 2 || k == 5) ? 1.0f / v : v;
     }
-    for (int i = threadIdx.x; i < 6 * g.nx; i += NTS) {
+    for (int i = threadIdx.x; i < 6 * g.nx; i += nth) {
         const int k = i / g.nx, x = i - k * g.nx;
         const int row = (k < 3 ? AXH : AX) + (k < 3 ? k : k - 3);
         const float v = cp[row * g.L + x];
         lds[bl.tx + i] = (k == 2 || k == 5) ? 1.0f / v : v;
     }
     int* slot = reinterpret_cast<int*>(lds + bl.slot);
-    for (int y = threadIdx.x; y < g.ny; y += NTS) slot[y] = ev.row_slot[s * g.ny + y];
+    for (int y = threadIdx.x; y < g.ny; y += nth) slot[y] = ev.row_slot[s * g.ny + y];
 }
 
 // The band memories of a cell, from / to set b: every cell of a row of the
@@ -915,6 +926,31 @@ __device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, 
     return !bad;
 }
 
+// tt % R and tt / R of a step index that moves one step at a time, kept
+// without the scalar divisions (R > 0; used only while tt >= 0).
+struct StepPhase {
+    int ph, idx;
+    __device__ __forceinline__ void init(int tt, int R)
+    {
+        idx = tt / R;
+        ph = tt - idx * R;
+    }
+    __device__ __forceinline__ void next(int R)
+    {
+        if (++ph == R) {
+            ph = 0;
+            ++idx;
+        }
+    }
+    __device__ __forceinline__ void prev(int R)
+    {
+        if (--ph < 0) {
+            ph = R - 1;
+            --idx;
+        }
+    }
+};
+
 // Forward, blocked: steps t0 .. t1-1, workgroup = (shot, band).
 template <int P, int SNAP, int CK>
 __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
@@ -926,6 +962,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
     const StateLayout& L = a.L;
     const BandK t = bandk_of(ba);
     const int s = t.s, tid = threadIdx.x;
+    const int nth = CK == 1 ? (int)blockDim.x : NTS;   // threads (bandk_threads)
     const int ny = g.ny, nx = g.nx;
     const int rows = ba.rb + 2 * ba.hd;
     const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 3);
@@ -943,7 +980,7 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
 
     // fields of the array rows (0 off the grid) and the padding
     const int arr = rows * nx;
-    for (int i = tid - (int)bl.pad; i < arr + (int)bl.pad; i += NTS) {
+    for (int i = tid - (int)bl.pad; i < arr + (int)bl.pad; i += nth) {
         const int gj = t.y_arr * nx + i;
         const bool in = i >= 0 && i < arr && gj >= 0 && gj < ny * nx;
         const uint32_t o = (uint32_t)(in ? gj : 0) * 4u;
@@ -951,20 +988,20 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
         sHx[i] = b0.ld(in, o, L.oHx);
         sHz[i] = b0.ld(in, o, L.oHz);
     }
-    bandk_tables(lds, bl, g, a.cp, a.ev, s);
+    bandk_tables(lds, bl, g, a.cp, a.ev, s, nth);
     if (tid == 0) quit = 0;
 
     auto xof = [&](const Cell& c) { return c.j() - (c.y() - t.y_arr) * nx; };
     // iteration i of the cell loops has work in this wave
     const BandKCells cs = bandk_cells(t, g);
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = cs.n;
-    auto live = [&](int i) { return i * NTS + wbase < ncel; };
+    auto live = [&](int i) { return i * nth + wbase < ncel; };
     int pk[CK];
     float ca[CK], cb[CK], cq[CK];
     CellMem mm[CK];
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
-        const int je = tid + i * NTS;
+        const int je = tid + i * nth;
         const bool ok = je < cs.n;
         pk[i] = pack_bandk_cell<P>(je, t, cs, rows, g);
         const Cell c0{pk[i]};
@@ -1021,7 +1058,9 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
         else mm[i].xe = v;
     };
 
-    int nex = 0;
+    int nex = 0, xc = 0;                    // exchanges done, steps since the last one
+    StepPhase sp;                           // of the step
+    if constexpr (SNAP != SNAP_NONE) sp.init(a.t0, a.R);
     // one step; false when the launch has failed
     auto step = [&](int tt, float (&add)[CK]) -> bool {
         // ---- H half-step on every extended row
@@ -1042,10 +1081,11 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
         __syncthreads();
 
         // ---- E step on every extended row; outputs of the own rows
-        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
-        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+        const bool stored = SNAP != SNAP_NONE && sp.ph == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)sp.idx * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
+        if constexpr (SNAP != SNAP_NONE) sp.next(a.R);
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
         const bool next_in = tt + 2 < a.t1;
         const uint32_t next_off = a.ev_add0 + (uint32_t)(next_in ? tt + 2 - a.t0 : 0) * a.ev_row;
@@ -1074,7 +1114,8 @@ __global__ __launch_bounds__(NTS) void k_fwd_bandk(BandKArgs ba)
             }
             sE[j] = c.bit(CB_E) ? en : ev;
         }
-        if (tt + 1 < a.t1 && (tt + 1 - a.t0) % ba.kx == 0) {
+        if (++xc == ba.kx) xc = 0;
+        if (tt + 1 < a.t1 && xc == 0) {
             // Own cells' values are final (each thread wrote its own), so
             // publish and poll at once.  The neighbours' fields go straight
             // into the outer rows while other threads may still run this
@@ -1121,6 +1162,7 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const StateLayout& L = a.L;
     const BandK t = bandk_of(ba);
     const int s = t.s, tid = threadIdx.x;
+    const int nth = CK == 1 ? (int)blockDim.x : NTS;   // threads (bandk_threads)
     const int ny = g.ny, nx = g.nx;
     const int rows = ba.rb + 2 * ba.hd;
     const BandKLayout bl = bandk_layout(g, ba.rb, ba.hd, 4);
@@ -1140,8 +1182,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     const RBuf bga(a.gca + (int64_t)s * g.slab, a.gca ? slab_b : 0u);
     const RBuf bgb(a.gcb + (int64_t)s * g.slab, a.gcb ? slab_b : 0u);
 
-    for (int i = tid; i < 4 * (int)bl.stride; i += NTS) lds[i] = 0.0f;
-    bandk_tables(lds, bl, g, a.cp, a.ev, s);
+    for (int i = tid; i < 4 * (int)bl.stride; i += nth) lds[i] = 0.0f;
+    bandk_tables(lds, bl, g, a.cp, a.ev, s, nth);
     if (tid == 0) quit = 0;
 
     auto xof = [&](const Cell& c) { return c.j() - (c.y() - t.y_arr) * nx; };
@@ -1155,13 +1197,13 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     };
     const BandKCells cs = bandk_cells(t, g);
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63), ncel = cs.n;
-    auto live = [&](int i) { return i * NTS + wbase < ncel; };
+    auto live = [&](int i) { return i * nth + wbase < ncel; };
     int pk[CK];
     float ca[CK], cb[CK], cq[CK], lE[CK], lHx[CK], lHz[CK], ga[CK], gb[CK];
     CellMem mm[CK];
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
-        const int je = tid + i * NTS;
+        const int je = tid + i * nth;
         const bool ok = je < cs.n;
         pk[i] = pack_bandk_cell<P>(je, t, cs, rows, g);
         const Cell c0{pk[i]};
@@ -1183,13 +1225,16 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     // residuals at the receivers and snapshots of a step: two steps ahead,
     // in two sets (steps of even and odd offset from t1 - 1), each reloaded
     // right after its step's phase 1 has used it
+    StepPhase lp;                           // of the step load_step reads (one lower at each call)
+    if constexpr (SNAP != SNAP_NONE) lp.init(a.t1 - 1, a.R);
     auto load_step = [&](int tt, float (&add)[CK], float (&se)[CK], float (&sc)[CK]) {
         const bool in_run = tt >= a.t0;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
-        const bool stored = SNAP != SNAP_NONE && in_run && tt % a.R == 0;
-        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+        const bool stored = SNAP != SNAP_NONE && in_run && lp.ph == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)lp.idx * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
+        if constexpr (SNAP != SNAP_NONE) lp.prev(a.R);
         // (every wave loads, off the buffers where it has no cell, so that
         // the registers are only ever written by loads: no wait for the
         // previous loads into them)
@@ -1229,10 +1274,13 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
     load_step(a.t1 - 1, add0, se0, sc0);
     load_step(a.t1 - 2, add1, se1, sc1);
 
-    int nex = 0;
+    int nex = 0, xc = 0;                    // exchanges done, steps since the last one
+    StepPhase sp;                           // of the step
+    if constexpr (SNAP != SNAP_NONE) sp.init(a.t1 - 1, a.R);
     // one step; false when the launch has failed
     auto step = [&](int tt, float (&add)[CK], float (&se)[CK], float (&sc)[CK]) -> bool {
-        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
+        const bool stored = SNAP != SNAP_NONE && sp.ph == 0;
+        if constexpr (SNAP != SNAP_NONE) sp.prev(a.R);
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
 
         // ---- phase 1 on every extended row: residual, gradient (own), Cb, E-update filters
@@ -1295,7 +1343,8 @@ __global__ __launch_bounds__(NTS) void k_adj_bandk(BandKArgs ba)
             const float en = fmaf(ca[i], lE[i], fmaf(-az, g.rdx, ay * g.rdy));
             lE[i] = c.bit(CB_E) ? en : lE[i];
         }
-        if (tt > a.t0 && (a.t1 - tt) % ba.kx == 0) {
+        if (++xc == ba.kx) xc = 0;
+        if (tt > a.t0 && xc == 0) {
             // the state lives in the cells' registers: no barrier (the next
             // one, after phase 1, reports a failed wait to every thread)
             bandk_publish<P, CK>(ba, t, pk, nex, get);

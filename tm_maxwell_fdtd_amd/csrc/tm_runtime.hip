@@ -1102,7 +1102,7 @@ const void* adj_bandk_fn(int snap)
 // launch); the failure word is cleared by the first banded launch of a call
 // and read at the call's end.
 tm_status band_launch(tm_plan* p, const Ptrs& q, const void* fn, void* argp, uint32_t lds, int kid, int64_t t,
-                      hipStream_t st)
+                      hipStream_t st, int threads = NTS)
 {
     const int nw = (int)(p->d.n_shots * p->band_n);
     Fills fills;
@@ -1114,7 +1114,7 @@ tm_status band_launch(tm_plan* p, const Ptrs& q, const void* fn, void* argp, uin
     void* args[] = {argp};
     hipError_t e = hipSuccess;
     timed(p, kid, t, st, [&] {
-        e = hipLaunchCooperativeKernel(fn, dim3((unsigned)nw), dim3(NTS), args, lds, st);
+        e = hipLaunchCooperativeKernel(fn, dim3((unsigned)nw), dim3((unsigned)threads), args, lds, st);
     });
     return e == hipSuccess ? TM_OK : TM_EHIP;
 }
@@ -1166,7 +1166,8 @@ tm_status fwd_band(tm_plan* p, const Ptrs& q, int cur, int64_t ta, int64_t tb, i
         const void* fn = bandk_cells_per_thread(p->g, p->band_rb, p->band_hd) == 1 ? fwd_bandk_fn<P, 1>(snap)
                                                                                   : fwd_bandk_fn<P, CPTK>(snap);
         return band_launch(p, q, fn, &b, bandk_lds_bytes(p->g, p->band_rb, p->band_hd, false),
-                           snap == SNAP_NONE ? KID_FWD_BANDK : KID_FWD_BANDK_ST, ta, st);
+                           snap == SNAP_NONE ? KID_FWD_BANDK : KID_FWD_BANDK_ST, ta, st,
+                           bandk_threads(p->g, p->band_rb, p->band_hd));
     }
     BandArgs b = band_args(p, q, a);
     const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_fwd_band<P, SNAP_F32>)
@@ -1209,7 +1210,7 @@ tm_status adj_band(tm_plan* p, const Ptrs& q, int64_t ta, int64_t tb, int64_t k,
         const void* fn = bandk_cells_per_thread(p->g, p->band_rb, p->band_hd) == 1 ? adj_bandk_fn<P, 1>(snap)
                                                                                   : adj_bandk_fn<P, CPTK>(snap);
         return band_launch(p, q, fn, &b, bandk_lds_bytes(p->g, p->band_rb, p->band_hd, true), KID_ADJ_BANDK, ta,
-                           st);
+                           st, bandk_threads(p->g, p->band_rb, p->band_hd));
     }
     BandArgs b = band_args(p, q, a);
     const void* fn = snap == SNAP_F32    ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>)
@@ -1344,8 +1345,9 @@ tm_status device_tiling(tm_plan* p)
                              : k1 ? fwd_bandk_fn<P, 1>(SNAP_F32) : fwd_bandk_fn<P, CPTK>(SNAP_F32);
             const void* fa = !kb ? reinterpret_cast<const void*>(&k_adj_band<P, SNAP_F32>)
                              : k1 ? adj_bandk_fn<P, 1>(SNAP_F32) : adj_bandk_fn<P, CPTK>(SNAP_F32);
-            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&of, ff, NTS, lf));
-            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&oa, fa, NTS, la));
+            const int nth = kb ? bandk_threads(p->g, p->band_rb, p->band_hd) : NTS;
+            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&of, ff, nth, lf));
+            HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&oa, fa, nth, la));
             p->banded = p->d.n_shots * p->band_n <= (int64_t)std::min(of, oa) * ncu;
         }
     }
