@@ -273,6 +273,31 @@ __device__ __forceinline__ bool band_exchange(const BandArgs& ba, const Band& t,
     return *quit == 0;
 }
 
+// tt % R and tt / R of a step index that moves one step at a time, kept
+// without the scalar divisions (R > 0; used only while tt >= 0).
+struct StepPhase {
+    int ph, idx;
+    __device__ __forceinline__ void init(int tt, int R)
+    {
+        idx = tt / R;
+        ph = tt - idx * R;
+    }
+    __device__ __forceinline__ void next(int R)
+    {
+        if (++ph == R) {
+            ph = 0;
+            ++idx;
+        }
+    }
+    __device__ __forceinline__ void prev(int R)
+    {
+        if (--ph < 0) {
+            ph = R - 1;
+            --idx;
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Forward: steps t0 .. t1-1, workgroup = (shot, band)
 // ---------------------------------------------------------------------------
@@ -355,6 +380,8 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
     load_add(a.t0, add0);
     load_add(a.t0 + 1, add1);
 
+    StepPhase sp;                           // of the step
+    if constexpr (SNAP != SNAP_NONE) sp.init(a.t0, a.R);
     // one step; false when the launch has failed
     auto step = [&](int tt, float (&add)[CPTB]) -> bool {
         // ---- H half-step (reads Ey^n, own rows and halo)
@@ -376,10 +403,11 @@ __global__ __launch_bounds__(NTS) void k_fwd_band(BandArgs ba)
         if (!band_exchange<P>(ba, t, sHx, 0, tt - a.t0, &quit, pk)) return false;
 
         // ---- E step (reads H^{n+1/2}), snapshots, sources, receivers
-        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
-        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+        const bool stored = SNAP != SNAP_NONE && sp.ph == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)sp.idx * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
+        if constexpr (SNAP != SNAP_NONE) sp.next(a.R);
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
         const bool next_in = tt + 2 < a.t1;
         const uint32_t next_off = a.ev_add0 + (uint32_t)(next_in ? tt + 2 - a.t0 : 0) * a.ev_row;
@@ -496,13 +524,16 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
     }
 
     float add[CPTB], se[CPTB], sc[CPTB];
+    StepPhase lp;                           // of the step load_step reads (one lower at each call)
+    if constexpr (SNAP != SNAP_NONE) lp.init(a.t1 - 1, a.R);
     auto load_step = [&](int tt) {
         const bool in_run = tt >= a.t0;
         const uint32_t off = a.ev_add0 + (uint32_t)(in_run ? tt - a.t0 : 0) * a.ev_row;
-        const bool stored = SNAP != SNAP_NONE && in_run && tt % a.R == 0;
-        const RBuf bsp(stored ? a.snap + (uint64_t)(tt / a.R) * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
+        const bool stored = SNAP != SNAP_NONE && in_run && lp.ph == 0;
+        const RBuf bsp(stored ? a.snap + (uint64_t)lp.idx * a.snap_stride + (uint64_t)s * a.snap_shot_bytes
                               : nullptr,
                        stored ? a.snap_shot_bytes : 0u);
+        if constexpr (SNAP != SNAP_NONE) lp.prev(a.R);
 #pragma unroll
         for (int i = 0; i < CPTB; ++i) {
             add[i] = se[i] = sc[i] = 0.0f;
@@ -520,8 +551,11 @@ __global__ __launch_bounds__(NTS) void k_adj_band(BandArgs ba)
     load_step(a.t1 - 1);
 
     drain_vmem();
+    StepPhase sp;                           // of the step
+    if constexpr (SNAP != SNAP_NONE) sp.init(a.t1 - 1, a.R);
     for (int tt = a.t1 - 1; tt >= a.t0; --tt) {
-        const bool stored = SNAP != SNAP_NONE && tt % a.R == 0;
+        const bool stored = SNAP != SNAP_NONE && sp.ph == 0;
+        if constexpr (SNAP != SNAP_NONE) sp.prev(a.R);
         const uint32_t out_off = a.ev_out0 + (uint32_t)(tt - a.t0) * a.ev_row;
         const int n = a.t1 - 1 - tt;
 
@@ -925,31 +959,6 @@ __device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, 
     if (bad) __hip_atomic_store(ba.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return !bad;
 }
-
-// tt % R and tt / R of a step index that moves one step at a time, kept
-// without the scalar divisions (R > 0; used only while tt >= 0).
-struct StepPhase {
-    int ph, idx;
-    __device__ __forceinline__ void init(int tt, int R)
-    {
-        idx = tt / R;
-        ph = tt - idx * R;
-    }
-    __device__ __forceinline__ void next(int R)
-    {
-        if (++ph == R) {
-            ph = 0;
-            ++idx;
-        }
-    }
-    __device__ __forceinline__ void prev(int R)
-    {
-        if (--ph < 0) {
-            ph = R - 1;
-            --idx;
-        }
-    }
-};
 
 // Forward, blocked: steps t0 .. t1-1, workgroup = (shot, band).
 template <int P, int SNAP, int CK>
