@@ -908,10 +908,11 @@ __device__ __forceinline__ void bandk_publish(const BandKArgs& ba, const BandK& 
 // poll is one memory round trip; neighbours publish at about the same time,
 // and a poll sent at once mostly arrives before their words and costs a
 // second round trip.  A thread with cells to poll therefore sleeps
-// BK_POLL_WAIT units (64 clocks each) before its first poll: on the 86^2 order-2 grid 12
-// units took the forward from 503 to 465 us and the adjoint from 645 to
-// 612 us over 300 steps (8 units: 473 / 615; 24: 499 / 653).
-constexpr int BK_POLL_WAIT = 12;
+// BK_POLL_WAIT units (64 clocks each) before its first poll: on the 86^2
+// order-2 grid (300 steps, 150 exchanges) 15 units give the forward 393 us
+// and the adjoint 432 us, against 426 / 465 us at 6 units, 407 / 445 at 9,
+// 402 / 442 at 12 and 395 / 435 at 18.
+constexpr int BK_POLL_WAIT = 15;
 
 template <int P, int CK, typename Put>
 __device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, const int (&pk)[CK], int n, Put put)
