@@ -699,10 +699,17 @@ __host__ __device__ inline uint32_t bandk_lds_bytes(const Geo& g, int rb, int hd
     return 4u * bandk_layout(g, rb, hd, adjoint ? 4 : 3).floats;
 }
 
+// Cells of a band's extended rows that some update can touch (columns
+// P .. nx-P; bandk_cells takes the rows too).
+__host__ __device__ inline int bandk_row_cells(const Geo& g, int rb, int hd)
+{
+    return (rb + 2 * hd) * (g.nx - 2 * g.P + 1);
+}
+
 __host__ __device__ inline bool bandk_rows_ok(const Geo& g, int rb, int hd)
 {
     return rb >= hd && hd >= 2 * g.P - 1 && (rb + 2 * hd + g.P) * g.nx + g.P < (1 << 14) &&
-           (rb + 2 * hd) * g.nx <= NTS * CPTK && g.ny < 2048;
+           bandk_row_cells(g, rb, hd) <= NTS * CPTK && g.ny < 2048;
 }
 
 // Cells per thread of the kernel instance that runs a layout: 1 where the
@@ -710,7 +717,7 @@ __host__ __device__ inline bool bandk_rows_ok(const Geo& g, int rb, int hd)
 // order-2 adjoint needs to stay out of scratch), else CPTK.
 __host__ __device__ inline int bandk_cells_per_thread(const Geo& g, int rb, int hd)
 {
-    return (rb + 2 * hd) * g.nx <= NTS ? 1 : CPTK;
+    return bandk_row_cells(g, rb, hd) <= NTS ? 1 : CPTK;
 }
 
 // Threads of a blocked launch: with one cell per thread, one per cell that
@@ -720,8 +727,7 @@ __host__ __device__ inline int bandk_cells_per_thread(const Geo& g, int rb, int 
 __host__ __device__ inline int bandk_threads(const Geo& g, int rb, int hd)
 {
     if (bandk_cells_per_thread(g, rb, hd) != 1) return NTS;
-    const int n = (rb + 2 * hd) * (g.nx - 2 * g.P + 1);
-    return (n + 63) / 64 * 64;
+    return (bandk_row_cells(g, rb, hd) + 63) / 64 * 64;
 }
 
 struct BandK {
@@ -909,10 +915,10 @@ __device__ __forceinline__ void bandk_publish(const BandKArgs& ba, const BandK& 
 // and a poll sent at once mostly arrives before their words and costs a
 // second round trip.  A thread with cells to poll therefore sleeps
 // BK_POLL_WAIT units (64 clocks each) before its first poll: on the 86^2
-// order-2 grid (300 steps, 150 exchanges) 15 units give the forward 393 us
-// and the adjoint 432 us, against 426 / 465 us at 6 units, 407 / 445 at 9,
-// 402 / 442 at 12 and 395 / 435 at 18.
-constexpr int BK_POLL_WAIT = 15;
+// order-2 grid (300 steps, an exchange every third) 20 units give the
+// forward 360 us and the adjoint 419 us, against 380 / 437 us at 10 units,
+// 364 / 424 at 15 and 362 / 421 at 25.
+constexpr int BK_POLL_WAIT = 20;
 
 template <int P, int CK, typename Put>
 __device__ __forceinline__ bool bandk_poll(const BandKArgs& ba, const BandK& t, const int (&pk)[CK], int n, Put put)

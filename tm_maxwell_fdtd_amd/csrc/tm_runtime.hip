@@ -257,13 +257,15 @@ bool finite_all(const float* p, int64_t n)
 }
 
 // Steps between exchanges of the blocked banded kernels (measured on the
-// order-2 86^2 grid with one shot: 2 and 3 alike, 1 and 4 slower).
-constexpr int BANDK_STEPS = 2;
+// order-2 86^2 grid with one shot, forward + adjoint: 3 steps 2.32 Gcell/s,
+// 2 steps 2.23, 4 steps 2.11); where the extended rows of 3 steps do not
+// fit a band, 2.
+constexpr int BANDK_STEPS = 3;
 
 // Band height and bands per shot of the banded resident kernels (0: they
 // do not apply): as many bands as one workgroup per CU of the device allows
 // (256 CUs; the device check repeats it with the real count).  Blocked
-// kernels (kx > 0 steps between exchanges): every band but the last owns
+// kernels (kx > 0 steps between exchanges, else fewer down to 2): every band but the last owns
 // at least hd = kx (2P - 1) rows, and the extended rows fit the packed cell
 // word, the threads and the LDS of a CU; where they do not, the kernels
 // exchanging every step, with bands of at least max(2P, 4) rows, the last of
@@ -276,16 +278,17 @@ void band_plan(tm_plan* p, int kx)
     const int64_t S = p->d.n_shots;
     constexpr int64_t WG_MAX = 256;
     if (S > WG_MAX || g.ny >= 2048) return;
-    if (kx > 0) {
-        // blocked: every band but the last owns at least hd rows
-        const int hd = kx * (2 * g.P - 1);
+    // blocked: every band but the last owns at least hd rows; kx steps
+    // between exchanges, else fewer, down to 2
+    for (int k = kx; k > 0 && k >= std::min(kx, 2); --k) {
+        const int hd = k * (2 * g.P - 1);
         for (int64_t nb = std::min<int64_t>(WG_MAX / S, (g.ny + hd - 1) / hd); nb >= 2; --nb) {
             const int rb = (int)((g.ny + nb - 1) / nb);
             const int n = (g.ny + rb - 1) / rb;
             if (!bandk_rows_ok(g, rb, hd) || bandk_lds_bytes(g, rb, hd, true) > 160u * 1024u) continue;
             p->band_rb = rb;
             p->band_n = n;
-            p->band_kx = kx;
+            p->band_kx = k;
             p->band_hd = hd;
             return;
         }
