@@ -111,10 +111,11 @@ typedef struct tm_desc {
                                every band's workgroup resident at once, same
                                conditions as 3, else 2); 5 = as 4, with
                                blocked banded kernels where they fit (every
-                               band also steps the 2(2P-1) rows next to it
-                               on each side, at most 2048 cells in all, so
-                               that neighbouring bands exchange their whole
-                               state only every second step), else as 4;
+                               band also steps the 3(2P-1) rows next to it
+                               on each side, else 2(2P-1), at most 2048
+                               cells in all, so that neighbouring bands
+                               exchange their whole state only every third,
+                               else every second, step), else as 4;
                                0 = default: 3 with 16
                                shots or more, else, where the streaming
                                kernels would leave most of the device idle,
