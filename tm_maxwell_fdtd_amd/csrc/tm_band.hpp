@@ -38,6 +38,10 @@ namespace tmf {
 constexpr int CPTB = 4;                     // cells per thread of a band (bands are small)
 constexpr int BX_WORDS = 8;                 // exchange words per thread and exchange (2 P nx <= 8 NTS)
 constexpr int BX_BATCH = 2;                 // ... polled together
+// Sleep units (64 clocks each) before a thread's first poll of an exchange:
+// on the 300^2 order-4 4-shot grid 6 units took forward + adjoint from 33.7
+// to 34.7 Gcell/s (2 units: 34.3, 4: 34.6, 8: 34.3).
+constexpr int BX_POLL_WAIT = 6;
 
 struct BandArgs {
     SmallArgs a;               // the run (as for the single-workgroup kernels)
@@ -229,6 +233,9 @@ __device__ __forceinline__ bool band_exchange(const BandArgs& ba, const Band& t,
             const int side = i >= pn, nb = side ? t.b + 1 : t.b - 1;
             if (i < 2 * pn && nb >= 0 && nb < ba.nband) pending |= 1u << q;   // beyond the grid: the halo stays 0
         }
+        // (a short wait before the first poll, as in the blocked kernels:
+        // polls sent at once mostly arrive before the neighbours' words)
+        if (q0 == 0 && pending != 0) __builtin_amdgcn_s_sleep(BX_POLL_WAIT);
 #pragma unroll 1
         for (int it = 0; pending != 0; ++it) {
             uint64_t w[BX_BATCH];
