@@ -1047,6 +1047,21 @@ def test_blocked_banded_exchange_intervals(monkeypatch, order, kx):
         np.testing.assert_array_equal(got[key], one[key], err_msg=key)
 
 
+def test_blocked_banded_fewer_steps_where_three_do_not_fit():
+    """An order-2 grid too wide for the extended rows of three steps between
+    exchanges (9 rows of 265 cells > 2048) but not of two (6 rows): the
+    blocked kernels still run, with two steps, bitwise one step per launch."""
+    wl = inputs.as_f32(inputs.random_workload(2, 40, 8, nt=23, n_shots=1, n_src=2, n_rec=6, seed=1490,
+                                              src_anywhere=True, nx_int=250))
+    assert 9 * (wl.nx - 1) > 2048 >= 6 * (wl.nx - 1), wl.nx
+    ran = _kernel_counts(wl, time_block=5)
+    assert "k_adj_bandk" in ran and "k_adj_band" not in ran, ran
+    got = run_gpu(wl, snap="f32", time_block=5)
+    one = run_gpu(wl, snap="f32", time_block=1)
+    for key in ("records", "gca_shot", "gcb_shot", "grad_f"):
+        np.testing.assert_array_equal(got[key], one[key], err_msg=key)
+
+
 @pytest.mark.parametrize("tb", [4, 5])
 def test_banded_failed_wait_is_reported(monkeypatch, tb):
     """A banded launch whose exchange wait fails (forced from the host with
